@@ -1,0 +1,229 @@
+/*
+ * v4attn.h -- C ABI of libv4attn.so: CSA / HCA hybrid compressed attention
+ * for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * Method sources (cited by tag):
+ *   [Notes] "DeepSeek V4: Towards Highly Efficient Million Token Context
+ *           Intelligence" (reading notes on the technical report):
+ *           §7 CSA, §8 HCA, §9 CSA/HCA other details, §11 KV cache table.
+ *   [HF]    "DeepSeek-V4: a million-token context that agents can actually
+ *           use" (Hugging Face blog), section "Hybrid attention: CSA and HCA".
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every data pointer is a DEVICE pointer owned by the caller; descriptor
+ *    structs (v4a_kv, v4a_idx) are HOST memory holding device pointers.
+ *    The library never allocates device memory: scratch comes in through a
+ *    caller-provided workspace sized by v4attn_workspace_bytes().
+ *  - Calls are asynchronous and stream-ordered: kernels are enqueued on
+ *    `stream` (a hipStream_t; NULL = the null stream) and the call returns
+ *    without synchronising.  Device faults surface at the caller's next sync.
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    error return leaves no side effects.
+ *  - Positions are absolute 0-based token indices.  Compressed block i covers
+ *    tokens [m*i, m*(i+1)).  A query at position p sees the n_vis(p) =
+ *    min(floor((p+1)/m), cap) blocks whose tokens are all at or before p, and
+ *    its window is the raw tokens max(0, p-n_win+1) .. p; p < 0 sees nothing.
+ *  - All arrays are row-major and densely packed in the shapes given.
+ *  - Results are deterministic, and one sequence's results do not depend on
+ *    the batch size B (split counts and reduction orders are fixed by the
+ *    per-query shapes only).
+ *  - The library keeps no mutable global state except the thread-local HIP
+ *    error of the last failed call; it is thread-safe.
+ */
+#ifndef V4ATTN_H
+#define V4ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+typedef int32_t v4a_status;
+#define V4A_OK               0
+#define V4A_ERR_INVALID     (-1)  /* null / inconsistent argument             */
+#define V4A_ERR_UNSUPPORTED (-2)  /* outside the supported shape/format set   */
+#define V4A_ERR_WORKSPACE   (-3)  /* workspace missing or too small           */
+#define V4A_ERR_HIP         (-4)  /* HIP runtime / launch error (see below)   */
+
+/* ---------------------------------------------------------------- formats */
+#define V4A_F32              0  /* fp32                                        */
+#define V4A_BF16             1  /* bf16 (raw 16-bit patterns)                  */
+#define V4A_KV_FP8_BF16ROPE  2  /* attention entry: e4m3fn nope + bf16 RoPE +
+                                   one fp32 scale per entry ([Notes §9]: RoPE
+                                   dims in BF16, every other KV dim in FP8)    */
+#define V4A_IDX_MXFP4        3  /* indexer key: OCP MXFP4, e2m1 elements with
+                                   one e8m0 scale per 32 ([Notes §9]: the
+                                   lightning indexer runs in FP4)              */
+
+/*
+ * Attention entries: a compressed cache, or a ring of raw (uncompressed)
+ * tokens for the sliding-window branch.  `cap` rows per sequence; row r of
+ * sequence b lives at [b][r].  For a window ring, token t lives at row t mod
+ * cap.  Entry value (used as both key and value, [Notes §7] shared-KV MQA):
+ *   V4A_F32:             nope f32 [B][cap][d_nope] ++ rope f32 [B][cap][d_rope]
+ *   V4A_KV_FP8_BF16ROPE: nope u8 e4m3fn [B][cap][d_nope] times scale f32 [B][cap],
+ *                        ++ rope bf16 [B][cap][d_rope]
+ */
+typedef struct {
+  int32_t fmt;      /* V4A_F32 | V4A_KV_FP8_BF16ROPE                          */
+  int32_t d_nope;   /* non-RoPE dims                                           */
+  int32_t d_rope;   /* RoPE dims (the last d_rope dims of the entry)           */
+  int32_t _pad;
+  int64_t cap;      /* rows per sequence                                       */
+  void   *nope;
+  void   *rope;
+  float  *scale;    /* NULL for V4A_F32                                        */
+} v4a_kv;
+
+/*
+ * Compressed lightning-indexer keys, `cap` rows per sequence.
+ *   V4A_F32:       codes f32 [B][cap][d]
+ *   V4A_IDX_MXFP4: codes u8 [B][cap][d/2] (element 2i in the LOW nibble of
+ *                  byte i), scales u8 e8m0 [B][cap][d/32] (value 2^(byte-127))
+ */
+typedef struct {
+  int32_t  fmt;     /* V4A_F32 | V4A_IDX_MXFP4                                */
+  int32_t  d;
+  int64_t  cap;
+  void    *codes;
+  uint8_t *scales;  /* NULL for V4A_F32                                        */
+} v4a_idx;
+
+/* output kinds of v4attn_compress */
+#define V4A_OUT_KV   0      /* `out` points to a v4a_kv  */
+#define V4A_OUT_IDX  1      /* `out` points to a v4a_idx */
+
+/*
+ * v4attn_compress -- softmax-gated token pooling ([Notes §8] HCA compressor
+ * equations; [Notes §7] CSA overlap compressor; [HF] "softmax-gated pooling
+ * with a learned positional bias").  For every complete block i of the call
+ * and every channel c, a softmax over the block's slots of (gate + positional
+ * bias), then the weighted sum of the slots' KV values:
+ *   non-overlap (kv_prev == NULL): m slots, the m tokens of block i;
+ *   overlap: 2m slots = the m previous-role tokens of block i-1 followed by
+ *            the m current-role tokens of block i (block 0 has no previous
+ *            block: only its m current slots count).
+ * The pooled fp32 row is then stored in the cache's format (FP8: scale =
+ * fp32(amax/448) over the d_nope dims, code = e4m3fn(x/scale) with RNE and
+ * saturation; MXFP4: per 32, e = floor(log2 amax) - 2, code = e2m1(x/2^e) RNE
+ * saturating; BF16 RoPE dims RNE).  With m = 1 and no overlap this is a plain
+ * store/quantisation of the token rows (the window ring is filled that way).
+ *
+ *   kv_cur, gate_cur   [B][T][d] tokens t0 .. t0+T-1 (gate_cur NULL = all 0)
+ *   kv_prev, gate_prev [B][T][d] tokens t0-m .. t0+T-m-1, or both NULL (no
+ *                      overlap); with t0 == 0 the first m rows are not read
+ *   pos_bias           f32 [slots][d], slots = 2m (overlap) or m; NULL = 0
+ *   in_dtype           V4A_F32 | V4A_BF16 (for kv_* and gate_*)
+ *   m                  1, 2, 4, ..., 128;  T and t0 multiples of m; t0 >= 0
+ *   out_kind, out      V4A_OUT_KV + v4a_kv* | V4A_OUT_IDX + v4a_idx* (host);
+ *                      rows (t0/m + j) mod cap, j < T/m, of every sequence
+ *                      are written; nothing else is touched.
+ * Supported: d <= 1024; KV out: d == d_nope + d_rope, FP8 needs d_nope%32==0;
+ * IDX out: d == out->d, MXFP4 needs d%32 == 0.
+ */
+v4a_status v4attn_compress(const void *kv_cur, const void *gate_cur,
+                           const void *kv_prev, const void *gate_prev,
+                           const float *pos_bias, int32_t in_dtype,
+                           int32_t B, int32_t T, int32_t d, int32_t m,
+                           int64_t t0, int32_t out_kind, const void *out,
+                           void *stream);
+
+/*
+ * v4attn_index_topk -- lightning indexer + top-k selector ([Notes §7]:
+ * I_{t,s} = sum_h w_{t,h} ReLU(q_{t,h} . K_s), then Top-k over s).
+ * For each query (b, j) at position pos[b][j], scores every visible block
+ * s < n_vis(p) and returns the k' = min(k, n_vis) highest-scoring block ids
+ * (ties: lower id first), listed in ascending order, padded with -1 to k.
+ * With MXFP4 keys the query heads are quantised to MXFP4 (groups of 32) in the
+ * call ([Notes §9]: FP4 indexer QK path); with F32 keys nothing is quantised.
+ * Scores are accumulated and ranked in fp32.
+ *
+ *   q_idx   [B][Q][H_I][d]  dtype q_dtype (V4A_F32 | V4A_BF16)
+ *   w       f32 [B][Q][H_I] head weights (any sign)
+ *   keys    host v4a_idx (device arrays inside), d = keys->d
+ *   pos     int64 [B][Q]
+ *   topk    int32 [B][Q][k] output
+ *   ws      workspace of at least v4attn_workspace_bytes(V4A_OP_INDEX_TOPK, ...)
+ * Supported: MXFP4 keys with d == 128 and H_I in {16,32,48,64}; F32 keys with
+ * d <= 256, H_I <= 64; 1 <= k <= 4096.
+ */
+v4a_status v4attn_index_topk(const void *q_idx, int32_t q_dtype, const float *w,
+                             const v4a_idx *keys, const int64_t *pos,
+                             int32_t B, int32_t Q, int32_t H_I, int32_t m,
+                             int32_t k, int32_t *topk,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * v4attn_csa_attend -- CSA core attention ([Notes §7]: shared key-value MQA
+ * over the selected compressed entries, plus the sliding-window branch over
+ * the most recent n_win uncompressed entries; [Notes §8] table: both sets enter
+ * core attention together, i.e. one joint softmax; [Notes §9]: optional
+ * per-head attention sink logit).  For query (b, j) at p = pos[b][j], head h:
+ *   E = { comp row s : s in topk[b][j][:], 0 <= s < comp->cap }  (ids outside
+ *       [0, cap) are skipped; no de-duplication)  ++  window tokens of p
+ *   l_e = sm_scale * (q_h . v_e);  out_h = sum_e softmax(l, sink_h)_e v_e
+ *   (the sink adds exp(sink_h - M) to the denominator only); empty E -> 0.
+ *
+ *   q      [B][Q][H][D] q_dtype, D = comp->d_nope + comp->d_rope
+ *   comp, win   host v4a_kv (same format and dims)
+ *   topk   int32 [B][Q][k];  n_win >= 0;  pos int64 [B][Q]
+ *   sink   f32 [H] or NULL
+ *   out    [B][Q][H][D] out_dtype (V4A_F32 | V4A_BF16)
+ * Supported: F32 entries with any D <= 512, H <= 128 (q F32 or BF16);
+ * FP8 entries with d_nope == 448, d_rope == 64, q BF16, H % 16 == 0, H <= 128.
+ * win->cap must be >= n_win (the caller keeps every window token of every
+ * query of the call in the ring).
+ */
+v4a_status v4attn_csa_attend(const void *q, int32_t q_dtype, const v4a_kv *comp,
+                             const int32_t *topk, int32_t k,
+                             const v4a_kv *win, int32_t n_win, const int64_t *pos,
+                             const float *sink, float sm_scale,
+                             int32_t B, int32_t Q, int32_t H,
+                             void *out, int32_t out_dtype,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * v4attn_hca_attend -- HCA core attention ([Notes §8]: no top-k; dense over
+ * every visible compressed entry, plus the same window branch).  As
+ * v4attn_csa_attend with E = { comp rows s < n_vis(p) } ++ window tokens of p.
+ */
+v4a_status v4attn_hca_attend(const void *q, int32_t q_dtype, const v4a_kv *comp,
+                             int32_t m, const v4a_kv *win, int32_t n_win,
+                             const int64_t *pos, const float *sink, float sm_scale,
+                             int32_t B, int32_t Q, int32_t H,
+                             void *out, int32_t out_dtype,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- helpers */
+#define V4A_OP_INDEX_TOPK 1
+#define V4A_OP_CSA_ATTEND 2
+#define V4A_OP_HCA_ATTEND 3
+
+/*
+ * Workspace bytes a call needs (0 = none).  Arguments that do not apply to
+ * `op` are ignored:
+ *   INDEX_TOPK: B, Q, H (= H_I), d (= key dim), cap (= keys->cap), k
+ *   CSA_ATTEND: B, Q, H, d (= D), cap (ignored), k, n_win
+ *   HCA_ATTEND: B, Q, H, d (= D), cap (= comp->cap), k (= m), n_win
+ * Returns (size_t)-1 for an invalid combination.
+ */
+size_t v4attn_workspace_bytes(int32_t op, int32_t B, int32_t Q, int32_t H,
+                              int32_t d, int64_t cap, int32_t k, int32_t n_win);
+
+/* Human-readable status text (static storage). */
+const char *v4attn_status_str(v4a_status s);
+
+/* hipError_t behind the calling thread's last V4A_ERR_HIP (0 if none). */
+int32_t v4attn_last_hip_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t v4attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* V4ATTN_H */

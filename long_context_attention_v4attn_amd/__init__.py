@@ -1,0 +1,14 @@
+"""MI355X (gfx950) CSA / HCA hybrid compressed attention.
+
+The compute lives in ``libv4attn.so`` (hand-written HIP kernels behind a C
+ABI, declared in ``include/v4attn.h``); this package is a thin ctypes binding
+that marshals torch tensors (device memory and streams) into those calls.
+There is no CPU or PyTorch fallback: every call fails loudly when the library
+is not built or no GPU is present.
+"""
+
+from .binding import (  # noqa: F401
+    KVCache, IdxCache, V4AttnError, load, library_path,
+    v4attn_compress, v4attn_index_topk, v4attn_csa_attend, v4attn_hca_attend,
+    v4attn_workspace_bytes, v4attn_status_str,
+)

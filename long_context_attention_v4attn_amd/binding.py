@@ -1,0 +1,254 @@
+"""ctypes binding of libv4attn.so (include/v4attn.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback -- a missing library, a missing GPU or a failed call
+raises V4AttnError.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+F32, BF16, KV_FP8_BF16ROPE, IDX_MXFP4 = 0, 1, 2, 3
+OUT_KV, OUT_IDX = 0, 1
+OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND = 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class V4AttnError(RuntimeError):
+    pass
+
+
+def library_path():
+    return os.environ.get("V4ATTN_LIB", os.path.join(_HERE, "libv4attn.so"))
+
+
+class _KV(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("d_nope", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("_pad", ctypes.c_int32),
+                ("cap", ctypes.c_int64), ("nope", ctypes.c_void_p),
+                ("rope", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class _Idx(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("cap", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+
+_SIGS = {
+    "v4attn_compress": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I64, _I32, _P, _P]),
+    "v4attn_index_topk": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "v4attn_csa_attend": (_I32, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32, _I32,
+                                 _P, _I32, _P, _SZ, _P]),
+    "v4attn_hca_attend": (_I32, [_P, _I32, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32, _I32,
+                                 _P, _I32, _P, _SZ, _P]),
+    "v4attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I64, _I32, _I32]),
+    "v4attn_status_str": (ctypes.c_char_p, [_I32]),
+    "v4attn_last_hip_error": (_I32, []),
+    "v4attn_version": (_I32, []),
+}
+
+
+def load():
+    """Load libv4attn.so (idempotent); raises V4AttnError when it is absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise V4AttnError(f"libv4attn.so not built ({path}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def v4attn_status_str(status):
+    return load().v4attn_status_str(int(status)).decode()
+
+
+def _check(status, what):
+    if status != 0:
+        lib = load()
+        msg = lib.v4attn_status_str(status).decode()
+        raise V4AttnError(f"{what}: {msg} (status {status}, hip error {lib.v4attn_last_hip_error()})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise V4AttnError(f"unsupported dtype {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise V4AttnError("tensors must be on the GPU (no host fallback)")
+
+
+@dataclass
+class KVCache:
+    """Attention entries (compressed cache or window ring) in device memory."""
+    fmt: int
+    d_nope: int
+    d_rope: int
+    nope: torch.Tensor          # f32 [B][cap][d_nope] | uint8 e4m3fn [B][cap][d_nope]
+    rope: torch.Tensor          # f32 [B][cap][d_rope] | bf16 [B][cap][d_rope]
+    scale: torch.Tensor = None  # None | f32 [B][cap]
+
+    @staticmethod
+    def empty(B, cap, d_nope, d_rope, fmt, device="cuda"):
+        if fmt == F32:
+            return KVCache(F32, d_nope, d_rope,
+                           torch.zeros(B, cap, d_nope, dtype=torch.float32, device=device),
+                           torch.zeros(B, cap, d_rope, dtype=torch.float32, device=device))
+        return KVCache(KV_FP8_BF16ROPE, d_nope, d_rope,
+                       torch.zeros(B, cap, d_nope, dtype=torch.uint8, device=device),
+                       torch.zeros(B, cap, d_rope, dtype=torch.bfloat16, device=device),
+                       torch.ones(B, cap, dtype=torch.float32, device=device))
+
+    @property
+    def cap(self):
+        return self.nope.shape[1]
+
+    def c_struct(self):
+        _need_cuda(self.nope, self.rope, self.scale)
+        return _KV(self.fmt, self.d_nope, self.d_rope, 0, self.cap, self.nope.data_ptr(),
+                   self.rope.data_ptr(), 0 if self.scale is None else self.scale.data_ptr())
+
+
+@dataclass
+class IdxCache:
+    """Compressed lightning-indexer keys in device memory."""
+    fmt: int
+    d: int
+    codes: torch.Tensor          # f32 [B][cap][d] | uint8 [B][cap][d/2]
+    scales: torch.Tensor = None  # None | uint8 e8m0 [B][cap][d/32]
+
+    @staticmethod
+    def empty(B, cap, d, fmt, device="cuda"):
+        if fmt == F32:
+            return IdxCache(F32, d, torch.zeros(B, cap, d, dtype=torch.float32, device=device))
+        return IdxCache(IDX_MXFP4, d, torch.zeros(B, cap, d // 2, dtype=torch.uint8, device=device),
+                        torch.zeros(B, cap, d // 32, dtype=torch.uint8, device=device))
+
+    @property
+    def cap(self):
+        return self.codes.shape[1]
+
+    def c_struct(self):
+        _need_cuda(self.codes, self.scales)
+        return _Idx(self.fmt, self.d, self.cap, self.codes.data_ptr(),
+                    0 if self.scales is None else self.scales.data_ptr())
+
+
+def v4attn_workspace_bytes(op, B, Q, H, d, cap, k, n_win):
+    n = load().v4attn_workspace_bytes(op, B, Q, H, d, cap, k, n_win)
+    if n == ctypes.c_size_t(-1).value:
+        raise V4AttnError("invalid workspace query")
+    return n
+
+
+def _workspace(ws, nbytes, device):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise V4AttnError("workspace too small")
+    return ws, ws.numel() * ws.element_size()
+
+
+def v4attn_compress(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, m, t0, out, stream=None):
+    """Pool tokens [t0, t0+T) of every sequence into `out` (KVCache | IdxCache)."""
+    lib = load()
+    _need_cuda(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias)
+    B, T, d = kv_cur.shape
+    kind = OUT_KV if isinstance(out, KVCache) else OUT_IDX
+    st = out.c_struct()
+    s = lib.v4attn_compress(_ptr(kv_cur), _ptr(gate_cur), _ptr(kv_prev), _ptr(gate_prev),
+                            _ptr(pos_bias), _dtype_code(kv_cur), B, T, d, m, int(t0), kind,
+                            ctypes.byref(st), _stream(stream))
+    _check(s, "v4attn_compress")
+    return out
+
+
+def v4attn_index_topk(q_idx, w, keys, pos, m, k, topk=None, ws=None, stream=None):
+    lib = load()
+    _need_cuda(q_idx, w, pos)
+    B, Q, H, d = q_idx.shape
+    if topk is None:
+        topk = torch.empty(B, Q, k, dtype=torch.int32, device=q_idx.device)
+    nbytes = v4attn_workspace_bytes(OP_INDEX_TOPK, B, Q, H, d, keys.cap, k, 0)
+    ws, wsb = _workspace(ws, nbytes, q_idx.device)
+    st = keys.c_struct()
+    s = lib.v4attn_index_topk(_ptr(q_idx), _dtype_code(q_idx), _ptr(w), ctypes.byref(st),
+                              _ptr(pos), B, Q, H, m, k, _ptr(topk), _ptr(ws), wsb, _stream(stream))
+    _check(s, "v4attn_index_topk")
+    return topk
+
+
+def _out(q, out, out_dtype):
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    return out
+
+
+def v4attn_csa_attend(q, comp, topk, win, n_win, pos, sink, sm_scale, out=None,
+                      out_dtype=torch.bfloat16, ws=None, stream=None):
+    lib = load()
+    _need_cuda(q, topk, pos, sink)
+    B, Q, H, D = q.shape
+    k = topk.shape[-1]
+    out = _out(q, out, out_dtype)
+    nbytes = v4attn_workspace_bytes(OP_CSA_ATTEND, B, Q, H, D, comp.cap, k, n_win)
+    ws, wsb = _workspace(ws, nbytes, q.device)
+    cs, wst = comp.c_struct(), win.c_struct()
+    s = lib.v4attn_csa_attend(_ptr(q), _dtype_code(q), ctypes.byref(cs), _ptr(topk), k,
+                              ctypes.byref(wst), n_win, _ptr(pos), _ptr(sink), float(sm_scale),
+                              B, Q, H, _ptr(out), _dtype_code(out), _ptr(ws), wsb, _stream(stream))
+    _check(s, "v4attn_csa_attend")
+    return out
+
+
+def v4attn_hca_attend(q, comp, m, win, n_win, pos, sink, sm_scale, out=None,
+                      out_dtype=torch.bfloat16, ws=None, stream=None):
+    lib = load()
+    _need_cuda(q, pos, sink)
+    B, Q, H, D = q.shape
+    out = _out(q, out, out_dtype)
+    nbytes = v4attn_workspace_bytes(OP_HCA_ATTEND, B, Q, H, D, comp.cap, m, n_win)
+    ws, wsb = _workspace(ws, nbytes, q.device)
+    cs, wst = comp.c_struct(), win.c_struct()
+    s = lib.v4attn_hca_attend(_ptr(q), _dtype_code(q), ctypes.byref(cs), m, ctypes.byref(wst),
+                              n_win, _ptr(pos), _ptr(sink), float(sm_scale), B, Q, H,
+                              _ptr(out), _dtype_code(out), _ptr(ws), wsb, _stream(stream))
+    _check(s, "v4attn_hca_attend")
+    return out
