@@ -1,0 +1,266 @@
+// C ABI of libv4attn: argument validation (before anything is enqueued),
+// launch planning, workspace carving and HIP error mapping.  Semantics of each
+// call are documented in include/v4attn.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/v4attn.h"
+#include "kernels.hpp"
+
+using namespace v4a;
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+v4a_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return V4A_OK;
+  g_last_hip = (int32_t)e;
+  return V4A_ERR_HIP;
+}
+
+bool is_pow2_le(int m, int hi) { return m >= 1 && m <= hi && (m & (m - 1)) == 0; }
+
+bool valid_kv(const v4a_kv* kv) {
+  if (!kv || !kv->nope || !kv->rope || kv->cap < 1 || kv->d_nope < 1 || kv->d_rope < 0) return false;
+  if (kv->fmt == V4A_KV_FP8_BF16ROPE && !kv->scale) return false;
+  return kv->fmt == V4A_F32 || kv->fmt == V4A_KV_FP8_BF16ROPE;
+}
+
+// Shared validation of the two attend calls.
+v4a_status check_attend(const void* q, int32_t q_dtype, const v4a_kv* comp, const v4a_kv* win,
+                        int32_t n_win, const int64_t* pos, int32_t B, int32_t Q, int32_t H,
+                        void* out, int32_t out_dtype) {
+  if (!q || !pos || !out || !comp || !win || B < 0 || Q < 0 || H < 1 || n_win < 0)
+    return V4A_ERR_INVALID;
+  if (!valid_kv(comp) || !valid_kv(win)) return V4A_ERR_INVALID;
+  if (comp->fmt != win->fmt || comp->d_nope != win->d_nope || comp->d_rope != win->d_rope)
+    return V4A_ERR_INVALID;
+  if (q_dtype != V4A_F32 && q_dtype != V4A_BF16) return V4A_ERR_INVALID;
+  if (out_dtype != V4A_F32 && out_dtype != V4A_BF16) return V4A_ERR_INVALID;
+  if (win->cap < n_win) return V4A_ERR_INVALID;
+  if (H > 128) return V4A_ERR_UNSUPPORTED;
+  const int D = comp->d_nope + comp->d_rope;
+  if (comp->fmt == V4A_KV_FP8_BF16ROPE) {
+    if (comp->d_nope != 448 || comp->d_rope != 64 || q_dtype != V4A_BF16 || H % 16 != 0)
+      return V4A_ERR_UNSUPPORTED;
+  } else if (D > 512) {
+    return V4A_ERR_UNSUPPORTED;
+  }
+  return V4A_OK;
+}
+
+void fill_attend(AttendArgs& a, const void* q, int32_t q_dtype, const v4a_kv* comp,
+                 const v4a_kv* win, int32_t n_win, const int64_t* pos, const float* sink,
+                 float sm_scale, int32_t B, int32_t Q, int32_t H, void* out, int32_t out_dtype) {
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.q_bf16 = q_dtype == V4A_BF16;
+  a.c_nope = (const uint8_t*)comp->nope;
+  a.c_rope = (const uint16_t*)comp->rope;
+  a.c_scale = comp->scale;
+  a.c_cap = comp->cap;
+  a.w_nope = (const uint8_t*)win->nope;
+  a.w_rope = (const uint16_t*)win->rope;
+  a.w_scale = win->scale;
+  a.w_cap = win->cap;
+  a.n_win = n_win;
+  a.pos = pos;
+  a.sink = sink;
+  a.sm_scale = sm_scale;
+  a.B = B;
+  a.Q = Q;
+  a.H = H;
+  a.d_nope = comp->d_nope;
+  a.d_rope = comp->d_rope;
+  a.out = out;
+  a.out_bf16 = out_dtype == V4A_BF16;
+  a.fp8 = comp->fmt == V4A_KV_FP8_BF16ROPE;
+}
+
+v4a_status run_attend(AttendArgs& a, int64_t n_entries_max, void* ws, size_t ws_bytes,
+                      void* stream) {
+  attend_plan(a, n_entries_max);
+  size_t need = attend_workspace_bytes(a);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return V4A_ERR_WORKSPACE;
+    attend_carve(a, ws);
+  }
+  return hip_status(launch_attend(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+v4a_status v4attn_compress(const void* kv_cur, const void* gate_cur, const void* kv_prev,
+                           const void* gate_prev, const float* pos_bias, int32_t in_dtype,
+                           int32_t B, int32_t T, int32_t d, int32_t m, int64_t t0,
+                           int32_t out_kind, const void* out, void* stream) {
+  if (!kv_cur || !out || B < 0 || T < 0 || d < 1 || t0 < 0) return V4A_ERR_INVALID;
+  if (in_dtype != V4A_F32 && in_dtype != V4A_BF16) return V4A_ERR_INVALID;
+  if (!is_pow2_le(m, 128)) return V4A_ERR_UNSUPPORTED;
+  if (T % m != 0 || t0 % m != 0) return V4A_ERR_INVALID;
+  if (gate_prev && !kv_prev) return V4A_ERR_INVALID;
+  if (d > 1024) return V4A_ERR_UNSUPPORTED;
+  CompressArgs a;
+  memset(&a, 0, sizeof(a));
+  a.kv_cur = kv_cur;
+  a.gate_cur = gate_cur;
+  a.kv_prev = kv_prev;
+  a.gate_prev = gate_prev;
+  a.bias = pos_bias;
+  a.in_bf16 = in_dtype == V4A_BF16;
+  a.B = B;
+  a.T = T;
+  a.d = d;
+  a.m = m;
+  a.t0 = t0;
+  a.out_kind = out_kind;
+  if (out_kind == V4A_OUT_KV) {
+    const v4a_kv* kv = (const v4a_kv*)out;
+    if (!valid_kv(kv) || kv->d_nope + kv->d_rope != d) return V4A_ERR_INVALID;
+    if (kv->fmt == V4A_KV_FP8_BF16ROPE && kv->d_nope % 32 != 0) return V4A_ERR_UNSUPPORTED;
+    a.out_fmt = kv->fmt;
+    a.d_nope = kv->d_nope;
+    a.cap = kv->cap;
+    a.o_a = kv->nope;
+    a.o_b = kv->rope;
+    a.o_scale = kv->scale;
+  } else if (out_kind == V4A_OUT_IDX) {
+    const v4a_idx* ix = (const v4a_idx*)out;
+    if (!ix->codes || ix->cap < 1 || ix->d != d) return V4A_ERR_INVALID;
+    if (ix->fmt == V4A_IDX_MXFP4) {
+      if (!ix->scales) return V4A_ERR_INVALID;
+      if (d % 32 != 0) return V4A_ERR_UNSUPPORTED;
+    } else if (ix->fmt != V4A_F32) {
+      return V4A_ERR_INVALID;
+    }
+    a.out_fmt = ix->fmt;
+    a.cap = ix->cap;
+    a.o_a = ix->codes;
+    a.o_b = ix->scales;
+  } else {
+    return V4A_ERR_INVALID;
+  }
+  if (B == 0 || T == 0) return V4A_OK;
+  return hip_status(launch_compress(a, (hipStream_t)stream));
+}
+
+v4a_status v4attn_index_topk(const void* q_idx, int32_t q_dtype, const float* w,
+                             const v4a_idx* keys, const int64_t* pos, int32_t B, int32_t Q,
+                             int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (!q_idx || !w || !keys || !pos || !topk || B < 0 || Q < 0 || H_I < 1 || k < 1 || m < 1)
+    return V4A_ERR_INVALID;
+  if (q_dtype != V4A_F32 && q_dtype != V4A_BF16) return V4A_ERR_INVALID;
+  if (!keys->codes || keys->cap < 1 || keys->d < 1) return V4A_ERR_INVALID;
+  if (k > 4096 || H_I > 64) return V4A_ERR_UNSUPPORTED;
+  if (keys->cap >= ((int64_t)1 << 31)) return V4A_ERR_UNSUPPORTED;
+  IndexArgs a;
+  memset(&a, 0, sizeof(a));
+  if (keys->fmt == V4A_IDX_MXFP4) {
+    if (!keys->scales) return V4A_ERR_INVALID;
+    if (keys->d != 128 || H_I % 16 != 0) return V4A_ERR_UNSUPPORTED;
+    a.key_mx = 1;
+  } else if (keys->fmt == V4A_F32) {
+    if (keys->d > 256 || (int64_t)keys->d * H_I > 8192) return V4A_ERR_UNSUPPORTED;
+  } else {
+    return V4A_ERR_INVALID;
+  }
+  a.q = q_idx;
+  a.q_bf16 = q_dtype == V4A_BF16;
+  a.w = w;
+  a.codes = keys->codes;
+  a.kscales = keys->scales;
+  a.cap = keys->cap;
+  a.d = keys->d;
+  a.pos = pos;
+  a.B = B;
+  a.Q = Q;
+  a.H = H_I;
+  a.m = m;
+  a.k = k;
+  a.topk = topk;
+  size_t need = index_workspace_bytes(B, Q, H_I, keys->d, keys->cap, a.key_mx);
+  if (!ws || ws_bytes < need) return V4A_ERR_WORKSPACE;
+  index_carve(a, ws);
+  if (B == 0 || Q == 0) return V4A_OK;
+  return hip_status(launch_index_topk(a, (hipStream_t)stream));
+}
+
+v4a_status v4attn_csa_attend(const void* q, int32_t q_dtype, const v4a_kv* comp,
+                             const int32_t* topk, int32_t k, const v4a_kv* win, int32_t n_win,
+                             const int64_t* pos, const float* sink, float sm_scale, int32_t B,
+                             int32_t Q, int32_t H, void* out, int32_t out_dtype, void* ws,
+                             size_t ws_bytes, void* stream) {
+  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype);
+  if (s != V4A_OK) return s;
+  if (k < 0 || (k > 0 && !topk)) return V4A_ERR_INVALID;
+  AttendArgs a;
+  fill_attend(a, q, q_dtype, comp, win, n_win, pos, sink, sm_scale, B, Q, H, out, out_dtype);
+  a.csa = 1;
+  a.topk = topk;
+  a.k = k;
+  a.m = 1;
+  if (B == 0 || Q == 0) return V4A_OK;
+  return run_attend(a, (int64_t)k + n_win, ws, ws_bytes, stream);
+}
+
+v4a_status v4attn_hca_attend(const void* q, int32_t q_dtype, const v4a_kv* comp, int32_t m,
+                             const v4a_kv* win, int32_t n_win, const int64_t* pos,
+                             const float* sink, float sm_scale, int32_t B, int32_t Q, int32_t H,
+                             void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                             void* stream) {
+  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype);
+  if (s != V4A_OK) return s;
+  if (m < 1) return V4A_ERR_INVALID;
+  AttendArgs a;
+  fill_attend(a, q, q_dtype, comp, win, n_win, pos, sink, sm_scale, B, Q, H, out, out_dtype);
+  a.csa = 0;
+  a.topk = nullptr;
+  a.m = m;
+  if (B == 0 || Q == 0) return V4A_OK;
+  return run_attend(a, comp->cap + n_win, ws, ws_bytes, stream);
+}
+
+size_t v4attn_workspace_bytes(int32_t op, int32_t B, int32_t Q, int32_t H, int32_t d, int64_t cap,
+                              int32_t k, int32_t n_win) {
+  if (B < 0 || Q < 0 || H < 1 || d < 1) return (size_t)-1;
+  if (op == V4A_OP_INDEX_TOPK) {
+    if (cap < 1) return (size_t)-1;
+    return index_workspace_bytes(B, Q, H, d, cap, d == 128 && H % 16 == 0 ? 1 : 0);
+  }
+  if (op != V4A_OP_CSA_ATTEND && op != V4A_OP_HCA_ATTEND) return (size_t)-1;
+  if (n_win < 0 || k < 0) return (size_t)-1;
+  AttendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.B = B;
+  a.Q = Q;
+  a.H = H;
+  a.d_nope = d;
+  a.d_rope = 0;
+  a.fp8 = 1;
+  int64_t n = op == V4A_OP_CSA_ATTEND ? (int64_t)k + n_win : cap + n_win;
+  attend_plan(a, n);
+  return attend_workspace_bytes(a);
+}
+
+const char* v4attn_status_str(v4a_status s) {
+  switch (s) {
+    case V4A_OK: return "ok";
+    case V4A_ERR_INVALID: return "invalid argument";
+    case V4A_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case V4A_ERR_WORKSPACE: return "workspace missing or too small";
+    case V4A_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t v4attn_last_hip_error(void) { return g_last_hip; }
+
+int32_t v4attn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Kernel argument blocks and launchers (host-visible; no torch, no ABI types).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace v4a {
+
+// ---------------------------------------------------------------- compress
+struct CompressArgs {
+  const void* kv_cur;
+  const void* gate_cur;      // may be null (zero gates)
+  const void* kv_prev;       // null = no overlap
+  const void* gate_prev;     // may be null (zero gates) when kv_prev is set
+  const float* bias;         // may be null (zero bias); [slots][d]
+  int in_bf16;
+  int B, T, d, m;
+  int64_t t0;
+  int out_kind;              // 0 = KV entries, 1 = indexer keys
+  int out_fmt;               // 0 = f32, 2 = FP8+BF16 RoPE (KV) / 3 = MXFP4 (keys)
+  int d_nope;                // KV: split point
+  int64_t cap;
+  void* o_a;                 // KV: nope (f32 | u8 e4m3);  keys: codes (f32 | u8 packed)
+  void* o_b;                 // KV: rope (f32 | bf16);     keys: e8m0 scales
+  float* o_scale;            // KV FP8: per-entry scale
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- indexer + top-k
+struct IndexArgs {
+  const void* q;             // [R][H][d]
+  int q_bf16;
+  const float* w;            // [R][H]
+  const void* codes;         // keys: f32 [B][cap][d] | u8 [B][cap][d/2]
+  const uint8_t* kscales;    // e8m0 [B][cap][d/32] (MXFP4)
+  int key_mx;
+  int64_t cap;
+  int d;
+  const int64_t* pos;        // [R]
+  int B, Q, H, m, k;
+  int32_t* topk;             // [R][k]
+  // workspace regions
+  uint8_t* qmx;              // [R][H][d/2]
+  uint8_t* qsc;              // [R][H][d/32]
+  float* scores;             // [R][cap]
+};
+size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx);
+void index_carve(IndexArgs& a, void* ws);
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- attend
+struct AttendArgs {
+  const void* q;             // [R][H][D]
+  int q_bf16;
+  const uint8_t* c_nope;     // compressed entries (typed as bytes; f32 in fp32 mode)
+  const uint16_t* c_rope;
+  const float* c_scale;
+  int64_t c_cap;
+  const uint8_t* w_nope;     // window ring
+  const uint16_t* w_rope;
+  const float* w_scale;
+  int64_t w_cap;
+  int csa;                   // 1: compressed part = the k top-k slots; 0: HCA
+  const int32_t* topk;       // CSA: [R][k] (may be null when k == 0)
+  int k;
+  int m;                     // HCA compression rate
+  int n_win;
+  const int64_t* pos;
+  const float* sink;         // [H] or null
+  float sm_scale;
+  int B, Q, H, d_nope, d_rope;
+  void* out;
+  int out_bf16;
+  int fp8;                   // 1 = FP8 MFMA path, 0 = fp32 VALU path
+  int f32_heads;             // heads per workgroup on the fp32 path
+  int n_split, split_size;   // entry-list split (fixed by the per-query shape)
+  float* part_o;             // [R][n_split][H][D]
+  float* part_ml;            // [R][n_split][H][2]
+};
+void attend_plan(AttendArgs& a, int64_t n_entries_max);
+size_t attend_workspace_bytes(const AttendArgs& a);
+void attend_carve(AttendArgs& a, void* ws);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+
+}  // namespace v4a

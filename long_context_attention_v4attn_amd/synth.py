@@ -95,13 +95,15 @@ def workload1_inputs(B=1, ctx=4096, wid=1):
 
 # ---------------------------------------------------------------- decode, cache-direct
 
-def decode_inputs(wid, B=None, n_comp=None, ctx=None, with_index=None, ring=None):
+def decode_inputs(wid, B=None, n_comp=None, ctx=None, with_index=None, ring=None, rows=None):
     """Cache-direct decode inputs for workloads 2-4 (fp32 values, unquantised).
 
     comp [B][n_comp][D], keys [B][n_comp][d_I] (CSA only), win [B][R][D] holding
     raw tokens ctx-R .. ctx-1 at ring rows t mod R, q [B][1][H][D],
     q_idx [B][1][H_I][d_I], w [B][1][H_I], pos [B][1] = ctx-1.
     Sizes may be overridden to build smaller cases with the same statistics.
+    `rows` (optional) lists the batch rows to draw (default: all B); the arrays
+    then hold those rows, in that order.
     """
     c = WORKLOADS[wid]
     B = c["B"] if B is None else B
@@ -111,21 +113,23 @@ def decode_inputs(wid, B=None, n_comp=None, ctx=None, with_index=None, ring=None
     D = c["d_nope"] + c["d_rope"]
     R = c["n_win"] if ring is None else ring
     with_index = (c["kind"] == "csa") if with_index is None else with_index
+    rows = list(range(B)) if rows is None else list(rows)
+    batched_rows = lambda fn: np.stack([fn(b) for b in rows])
     g = {}
-    g["comp"] = batched(lambda b: normal(wid, T_COMP, b, (n_comp, D), D ** -0.5), B)
-    win_tok = batched(lambda b: normal(wid, T_WIN, b, (R, D), D ** -0.5), B)
+    g["comp"] = batched_rows(lambda b: normal(wid, T_COMP, b, (n_comp, D), D ** -0.5))
+    win_tok = batched_rows(lambda b: normal(wid, T_WIN, b, (R, D), D ** -0.5))
     # token ctx-R+i lives at ring row (ctx-R+i) mod R
-    rows = (np.arange(ctx - R, ctx) % R)
+    ring_rows = np.arange(ctx - R, ctx) % R
     win = np.empty_like(win_tok)
-    win[:, rows] = win_tok
+    win[:, ring_rows] = win_tok
     g["win"] = win
-    g["q"] = batched(lambda b: normal(wid, T_Q, b, (1, c["H"], D), D ** -0.5), B)
+    g["q"] = batched_rows(lambda b: normal(wid, T_Q, b, (1, c["H"], D), D ** -0.5))
     if with_index:
         dI = c["d_I"]
-        g["keys"] = batched(lambda b: normal(wid, T_KEYS, b, (n_comp, dI), dI ** -0.5), B)
-        g["q_idx"] = batched(lambda b: normal(wid, T_QI, b, (1, c["H_I"], dI), dI ** -0.5), B)
-        g["w"] = batched(lambda b: uniform(wid, T_W, b, (1, c["H_I"])), B)
-    g["pos"] = np.full((B, 1), ctx - 1, dtype=np.int64)
+        g["keys"] = batched_rows(lambda b: normal(wid, T_KEYS, b, (n_comp, dI), dI ** -0.5))
+        g["q_idx"] = batched_rows(lambda b: normal(wid, T_QI, b, (1, c["H_I"], dI), dI ** -0.5))
+        g["w"] = batched_rows(lambda b: uniform(wid, T_W, b, (1, c["H_I"])))
+    g["pos"] = np.full((len(rows), 1), ctx - 1, dtype=np.int64)
     return g
 
 

@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every function include/v4attn.h declares; helpers answer; invalid arguments are
+rejected on the host before anything is enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "v4attn.h")
+
+
+@pytest.fixture(scope="module")
+def clib():
+    from long_context_attention_v4attn_amd import binding
+    if not os.path.exists(binding.library_path()):
+        from long_context_attention_v4attn_amd import build
+        build.build()
+    return binding.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(v4attn_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("v4attn_compress", "v4attn_index_topk", "v4attn_csa_attend", "v4attn_hca_attend"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(clib):
+    for name in _declared():
+        assert hasattr(clib, name), f"{name} not exported"
+
+
+def test_status_strings_and_version(clib):
+    from long_context_attention_v4attn_amd import binding as B
+    for s in (0, -1, -2, -3, -4):
+        assert B.v4attn_status_str(s)
+    assert clib.v4attn_version() >= 100
+    assert clib.v4attn_last_hip_error() == 0
+
+
+def test_workspace_sizes(clib):
+    from long_context_attention_v4attn_amd import binding as B
+    # scores [R][cap] fp32 plus the quantised queries
+    n = B.v4attn_workspace_bytes(B.OP_INDEX_TOPK, 4, 1, 16, 128, 262144, 2048, 0)
+    assert n >= 4 * 262144 * 4
+    # a short entry list needs no split partials
+    assert B.v4attn_workspace_bytes(B.OP_CSA_ATTEND, 1, 1, 64, 512, 0, 64, 64) == 0
+    # a long one does, and the need does not depend on B per query
+    a = B.v4attn_workspace_bytes(B.OP_HCA_ATTEND, 1, 1, 64, 512, 8192, 128, 128)
+    b = B.v4attn_workspace_bytes(B.OP_HCA_ATTEND, 16, 1, 64, 512, 8192, 128, 128)
+    assert a > 0 and b >= 16 * a - 16 * 512
+    with pytest.raises(B.V4AttnError):
+        B.v4attn_workspace_bytes(99, 1, 1, 1, 1, 1, 1, 1)
+
+
+class _KV(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("_pad", ctypes.c_int32), ("cap", ctypes.c_int64), ("nope", ctypes.c_void_p),
+                ("rope", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class _Idx(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("d", ctypes.c_int32), ("cap", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def test_invalid_arguments_rejected_on_host(clib):
+    kv = _KV(2, 448, 64, 0, 100, 0x1000, 0x2000, 0x3000)
+    r = ctypes.byref
+    # compress: null input, bad m, T not a multiple of m, mismatched dims
+    assert clib.v4attn_compress(None, None, None, None, None, 0, 1, 4, 512, 4, 0, 0, r(kv), None) == -1
+    assert clib.v4attn_compress(FAKE, None, None, None, None, 0, 1, 6, 512, 3, 0, 0, r(kv), None) == -2
+    assert clib.v4attn_compress(FAKE, None, None, None, None, 0, 1, 6, 512, 4, 0, 0, r(kv), None) == -1
+    assert clib.v4attn_compress(FAKE, None, None, None, None, 0, 1, 8, 500, 4, 0, 0, r(kv), None) == -1
+    assert clib.v4attn_compress(FAKE, None, None, FAKE, None, 0, 1, 8, 512, 4, 0, 0, r(kv), None) == -1
+    # index_topk: k = 0, unsupported d, missing workspace
+    ix = _Idx(3, 128, 1000, 0x1000, 0x2000)
+    assert clib.v4attn_index_topk(FAKE, 1, FAKE, r(ix), FAKE, 1, 1, 16, 4, 0, FAKE, FAKE, 1 << 30, None) == -1
+    ix_bad = _Idx(3, 64, 1000, 0x1000, 0x2000)
+    assert clib.v4attn_index_topk(FAKE, 1, FAKE, r(ix_bad), FAKE, 1, 1, 16, 4, 8, FAKE, FAKE, 1 << 30, None) == -2
+    assert clib.v4attn_index_topk(FAKE, 1, FAKE, r(ix), FAKE, 1, 1, 16, 4, 8, FAKE, None, 0, None) == -3
+    # attend: H not a multiple of 16 on the FP8 path, window ring too small, f32 q on FP8
+    win = _KV(2, 448, 64, 0, 64, 0x1000, 0x2000, 0x3000)
+    assert clib.v4attn_hca_attend(FAKE, 1, r(kv), 128, r(kv), 16, FAKE, None, ctypes.c_float(0.1),
+                                  1, 1, 24, FAKE, 1, FAKE, 1 << 30, None) == -2
+    assert clib.v4attn_hca_attend(FAKE, 1, r(kv), 128, r(win), 128, FAKE, None, ctypes.c_float(0.1),
+                                  1, 1, 64, FAKE, 1, FAKE, 1 << 30, None) == -1
+    assert clib.v4attn_csa_attend(FAKE, 0, r(kv), FAKE, 8, r(kv), 16, FAKE, None, ctypes.c_float(0.1),
+                                  1, 1, 64, FAKE, 1, FAKE, 1 << 30, None) == -2
+    # format mismatch between cache and ring
+    kv32 = _KV(0, 448, 64, 0, 100, 0x1000, 0x2000, 0)
+    assert clib.v4attn_csa_attend(FAKE, 1, r(kv), FAKE, 8, r(kv32), 16, FAKE, None, ctypes.c_float(0.1),
+                                  1, 1, 64, FAKE, 1, FAKE, 1 << 30, None) == -1
+    # a long entry list needs split partials: no workspace -> -3
+    big = _KV(2, 448, 64, 0, 10000, 0x1000, 0x2000, 0x3000)
+    assert clib.v4attn_hca_attend(FAKE, 1, r(big), 4, r(kv), 16, FAKE, None, ctypes.c_float(0.1),
+                                  1, 1, 64, FAKE, 1, None, 0, None) == -3
+
+
+def test_binding_refuses_host_tensors():
+    import numpy as np
+    import torch
+    from long_context_attention_v4attn_amd import binding as B
+    try:
+        B.load()
+    except B.V4AttnError:
+        pytest.skip("library not built")
+    x = torch.zeros(1, 4, 512)
+    out = B.KVCache(B.F32, 448, 64, torch.zeros(1, 2, 448), torch.zeros(1, 2, 64))
+    with pytest.raises(B.V4AttnError):
+        B.v4attn_compress(x, None, None, None, None, 4, 0, out)

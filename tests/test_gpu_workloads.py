@@ -1,0 +1,139 @@
+"""GPU parity on the benchmark workloads: the fp32 full CSA pipeline
+(workload 1) end to end, and workloads 2-4 at full size in the launch
+configuration the benchmark times, checked against the oracle on sampled
+batch rows; determinism and batch invariance."""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_v4attn_amd import synth
+from oracle import codecs as C
+from oracle.attend import csa_attend, hca_attend
+from oracle.indexer import index_scores
+from oracle.pipeline import workload1
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def test_workload1_full_pipeline_fp32(lib):
+    print("workload 1: fp32 CSA pipeline", flush=True)
+    g = synth.workload1_inputs()
+    ref = workload1(g)
+    m, T, D, dI, k, n_win = 4, 4096, 128, 64, 64, 128
+    prev = lambda x: np.concatenate([np.zeros_like(x[:, :m]), x[:, :T - m]], axis=1)
+    comp = lib.KVCache.empty(1, T // m, 64, 64, lib.F32)
+    keys = lib.IdxCache.empty(1, T // m, dI, lib.F32)
+    lib.v4attn_compress(P.dev(g["kv_b"]), P.dev(g["z_b"]), P.dev(prev(g["kv_a"])),
+                        P.dev(prev(g["z_a"])), P.dev(g["bias"]), m, 0, comp)
+    lib.v4attn_compress(P.dev(g["ki_b"]), P.dev(g["zi_b"]), P.dev(prev(g["ki_a"])),
+                        P.dev(prev(g["zi_a"])), P.dev(g["bias_i"]), m, 0, keys)
+    # window ring: the last 128 raw tokens, stored with m = 1
+    win = lib.KVCache.empty(1, n_win, 64, 64, lib.F32)
+    lib.v4attn_compress(P.dev(g["kv_b"][:, T - n_win:]), None, None, None, None, 1, T - n_win, win)
+    topk = lib.v4attn_index_topk(P.dev(g["q_idx"]), P.dev(g["w"]), keys, P.dev(g["pos"]), m, k)
+    out = lib.v4attn_csa_attend(P.dev(g["q"]), comp, topk, win, n_win, P.dev(g["pos"]), None,
+                                D ** -0.5, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # compressed caches
+    cb = P.kv_from_dev(comp)
+    P.check_f32_rows(np.concatenate([cb.nope, cb.rope], -1), ref["y"])
+    P.check_f32_rows(keys.codes.cpu().numpy(), ref["yi"])
+    # top-k against the oracle's scores of the oracle's keys
+    P.check_topk_row(topk.cpu().numpy()[0, 0], ref["scores"][0][0], k)
+    P.check_out(out, ref["out_f64"])
+
+
+def _decode_case(lib, wid, B=None, n_comp=None, ctx=None, distinct=None):
+    """Workload inputs quantised by the oracle.  With `distinct` (a list of
+    batch rows), only those rows are drawn and quantised; every other row of
+    the full batch repeats the nearest preceding distinct row's bytes."""
+    c = synth.WORKLOADS[wid]
+    B = c["B"] if B is None else B
+    rows = list(range(B)) if distinct is None else list(distinct)
+    src = [max(i for i, r in enumerate(rows) if r <= b) for b in range(B)]
+    gd = synth.decode_inputs(wid, B=B, n_comp=n_comp, ctx=ctx, rows=rows)
+    tile = lambda a: a[src]
+    g = {k: tile(v) for k, v in gd.items()}
+    cd = C.kv_encode(gd["comp"], "fp8", c["d_nope"])
+    comp = C.KV("fp8", cd.d_nope, cd.d_rope, tile(cd.nope), tile(cd.rope), tile(cd.scale))
+    win = C.kv_encode(g["win"], "fp8", c["d_nope"])
+    case = dict(g=g, comp=comp, win=win, qb=C.bf16_encode(g["q"]), c=c)
+    if c["kind"] == "csa":
+        kd = C.idx_encode(gd["keys"], "mxfp4")
+        case["keys"] = C.Idx("mxfp4", 128, tile(kd.codes), tile(kd.scales))
+        case["qib"] = C.bf16_encode(g["q_idx"])
+    return case
+
+
+def _gpu_csa(lib, case):
+    c, g = case["c"], case["g"]
+    keys = P.idx_to_dev(case["keys"])
+    topk = lib.v4attn_index_topk(P.dev(case["qib"].view(np.int16)).view(torch.bfloat16),
+                                 P.dev(g["w"]), keys, P.dev(g["pos"]), c["m"], c["k"])
+    out = lib.v4attn_csa_attend(P.dev(case["qb"].view(np.int16)).view(torch.bfloat16),
+                                P.kv_to_dev(case["comp"]), topk, P.kv_to_dev(case["win"]),
+                                c["n_win"], P.dev(g["pos"]), None, 512 ** -0.5)
+    torch.cuda.synchronize()
+    return topk.cpu().numpy(), out
+
+
+@pytest.mark.parametrize("wid", [2, 4])
+def test_csa_decode_full_size_sampled_rows(lib, wid):
+    c = synth.WORKLOADS[wid]
+    print(f"workload {wid}: CSA decode B={c['B']} ctx={c['ctx']}", flush=True)
+    last = c["B"] - 1
+    case = _decode_case(lib, wid, distinct=[0, last])
+    topk, out = _gpu_csa(lib, case)
+    g = case["g"]
+    qi = C.bf16_decode(case["qib"]).astype(np.float32)
+    for b in (0, last):                             # sampled rows
+        sc = index_scores(qi[b:b + 1], g["w"][b:b + 1],
+                          C.Idx("mxfp4", 128, case["keys"].codes[b:b + 1], case["keys"].scales[b:b + 1]),
+                          g["pos"][b:b + 1], c["m"])
+        P.check_topk_row(topk[b, 0], sc[0][0], c["k"])
+        sub = lambda kv: C.KV("fp8", kv.d_nope, kv.d_rope, kv.nope[b:b + 1], kv.rope[b:b + 1],
+                              kv.scale[b:b + 1])
+        # attend over the GPU's own selection (identical entry set on both sides)
+        _, ref = csa_attend(case["qb"][b:b + 1], "bf16", sub(case["comp"]), topk[b:b + 1],
+                            sub(case["win"]), c["n_win"], g["pos"][b:b + 1], None, 512 ** -0.5, "bf16")
+        P.check_out(out[b:b + 1], ref, what=f"row {b}")
+
+
+def test_hca_decode_full_size_sampled_rows(lib):
+    c = synth.WORKLOADS[3]
+    print(f"workload 3: HCA decode B={c['B']} ctx={c['ctx']}", flush=True)
+    case = _decode_case(lib, 3)
+    g = case["g"]
+    out = lib.v4attn_hca_attend(P.dev(case["qb"].view(np.int16)).view(torch.bfloat16),
+                                P.kv_to_dev(case["comp"]), c["m"], P.kv_to_dev(case["win"]),
+                                c["n_win"], P.dev(g["pos"]), None, 512 ** -0.5)
+    torch.cuda.synchronize()
+    for b in (0, 7, c["B"] - 1):
+        sub = lambda kv: C.KV("fp8", kv.d_nope, kv.d_rope, kv.nope[b:b + 1], kv.rope[b:b + 1],
+                              kv.scale[b:b + 1])
+        _, ref = hca_attend(case["qb"][b:b + 1], "bf16", sub(case["comp"]), c["m"], sub(case["win"]),
+                            c["n_win"], g["pos"][b:b + 1], None, 512 ** -0.5, "bf16")
+        P.check_out(out[b:b + 1], ref, what=f"row {b}")
+
+
+def test_determinism_and_batch_invariance(lib):
+    print("determinism / batch invariance (workload 2 shapes, 8192 blocks)", flush=True)
+    case = _decode_case(lib, 2, B=4, n_comp=8192, ctx=8192 * 4)
+    t1, o1 = _gpu_csa(lib, case)
+    t2, o2 = _gpu_csa(lib, case)
+    assert np.array_equal(t1, t2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    # row 2 alone (B = 1) gives the same bits
+    one = dict(case)
+    g = {k: (v[2:3] if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == 4 else v)
+         for k, v in case["g"].items()}
+    one["g"] = g
+    sub = lambda kv: C.KV("fp8", kv.d_nope, kv.d_rope, kv.nope[2:3], kv.rope[2:3], kv.scale[2:3])
+    one["comp"], one["win"] = sub(case["comp"]), sub(case["win"])
+    one["keys"] = C.Idx("mxfp4", 128, case["keys"].codes[2:3], case["keys"].scales[2:3])
+    one["qb"], one["qib"] = case["qb"][2:3], case["qib"][2:3]
+    t3, o3 = _gpu_csa(lib, one)
+    assert np.array_equal(t3[0], t1[2])
+    assert torch.equal(o3[0].view(torch.int16), o1[2].view(torch.int16))
