@@ -272,8 +272,12 @@ def test_attend_f32_entries(lib, kind, q_bf16):
     scale = 128 ** -0.5
     qin = C.bf16_encode(q) if q_bf16 else q
     if kind == "csa":
-        topk = np.stack([np.stack([np.sort(rng.choice(min((p + 1) // 4, n_comp), 64, replace=False))
-                                   for p in row]) for row in pos])
+        topk = np.full((Bn, Q, 64), -1, np.int64)
+        for b in range(Bn):
+            for t in range(Q):
+                nv = min((pos[b, t] + 1) // 4, n_comp)
+                kk = min(64, nv)
+                topk[b, t, :kk] = np.sort(rng.choice(nv, kk, replace=False))
         _, ref = csa_attend(qin, "bf16" if q_bf16 else "f32", comp, topk, win, n_win, pos, None,
                             scale, "f32")
         o = _run_attend(lib, "csa", q, q_bf16, comp, win, n_win, pos, None, scale, topk=topk,
