@@ -1,0 +1,354 @@
+"""Benchmark: CSA + HCA decode at 1M-token context on one MI355X.
+
+One step = one decode query per sequence through
+  * a CSA layer  (1M context, 4x pooling -> 262144 blocks, B = 4): the FP4
+    lightning-indexer scan + top-2048 select (v4attn_index_topk), then
+    attention over the selected blocks and the 128-token window
+    (v4attn_csa_attend);
+  * an HCA layer (1M context, 128x pooling -> 8192 entries, B = 16): dense
+    attention over every entry plus the window (v4attn_hca_attend).
+Headline `value` = decode queries per second through a CSA + HCA layer pair:
+1 / (t_csa / 4 + t_hca / 16), each layer at its own batch.
+
+Inputs are synthetic and seeded (long_context_attention_v4attn_amd.synth),
+uploaded once and quantised to the cache formats on the GPU by the library
+(v4attn_compress with m = 1).  `--replicas` address-distinct copies of every
+cache are cycled so that no step re-reads data another recent step left in the
+256 MB Infinity Cache.  Each call is captured in a HIP graph per replica; the
+timed loop replays them with HIP events between calls (torch's current stream,
+which is the stream the library launches on).
+
+The `cpu_baseline` leg times the CPU oracle (test infrastructure) on a bounded
+sample of the same workload: 4 CSA queries over one 1M-context cache row and
+16 HCA queries over one cache row.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0       # dense bf16 MFMA
+FP4_PEAK_TFLOPS = 10100.0       # dense MXFP4 MFMA
+
+CSA_WID, HCA_WID = 4, 3
+
+
+def algorithmic_bytes(c_csa, c_hca):
+    """Bytes the method must move per query (cache reads at storage size,
+    query / output / selection traffic)."""
+    entry = c_csa["d_nope"] + 2 * c_csa["d_rope"] + 4                 # 580 B
+    key = c_csa["d_I"] // 2 + c_csa["d_I"] // 32                       # 68 B
+    D = c_csa["d_nope"] + c_csa["d_rope"]
+    qo = c_csa["H"] * D * 2 * 2                                        # q in + out, bf16
+    n_blocks = c_csa["ctx"] // c_csa["m"]
+    idx = n_blocks * key + c_csa["H_I"] * c_csa["d_I"] * 2 + c_csa["H_I"] * 4 + c_csa["k"] * 4
+    csa = (c_csa["k"] + c_csa["n_win"]) * entry + qo + c_csa["k"] * 4
+    hca = (c_hca["ctx"] // c_hca["m"] + c_hca["n_win"]) * entry + qo
+    return dict(index=idx, csa_attend=csa, hca_attend=hca)
+
+
+def algorithmic_flops(c_csa, c_hca):
+    D = c_csa["d_nope"] + c_csa["d_rope"]
+    idx = (c_csa["ctx"] // c_csa["m"]) * c_csa["H_I"] * c_csa["d_I"] * 2
+    csa = (c_csa["k"] + c_csa["n_win"]) * c_csa["H"] * D * 4
+    hca = (c_hca["ctx"] // c_hca["m"] + c_hca["n_win"]) * c_hca["H"] * D * 4
+    return dict(index=idx, csa_attend=csa, hca_attend=hca)
+
+
+# ---------------------------------------------------------------- GPU setup
+
+class Replica:
+    pass
+
+
+def build_inputs(v4, torch, replicas, log):
+    from long_context_attention_v4attn_amd import synth
+    dev = "cuda"
+    cc, ch = synth.WORKLOADS[CSA_WID], synth.WORKLOADS[HCA_WID]
+    t0 = time.time()
+    gc = synth.decode_inputs(CSA_WID)
+    gh = synth.decode_inputs(HCA_WID)
+    log(f"synthetic inputs drawn in {time.time() - t0:.1f}s")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def quant_kv(x, B, n):
+        kv = v4.KVCache.empty(B, n, 448, 64, v4.KV_FP8_BF16ROPE)
+        xs = up(x)
+        v4.v4attn_compress(xs, None, None, None, None, 1, 0, kv)
+        del xs
+        return kv
+
+    def quant_keys(x, B, n):
+        ix = v4.IdxCache.empty(B, n, 128, v4.IDX_MXFP4)
+        xs = up(x)
+        v4.v4attn_compress(xs, None, None, None, None, 1, 0, ix)
+        del xs
+        return ix
+
+    t0 = time.time()
+    base = Replica()
+    nc = cc["ctx"] // cc["m"]
+    nh = ch["ctx"] // ch["m"]
+    base.c_comp = quant_kv(gc["comp"], cc["B"], nc)
+    base.c_keys = quant_keys(gc["keys"], cc["B"], nc)
+    base.c_win = quant_kv(gc["win"], cc["B"], cc["n_win"])
+    base.h_comp = quant_kv(gh["comp"], ch["B"], nh)
+    base.h_win = quant_kv(gh["win"], ch["B"], ch["n_win"])
+    base.c_q = up(gc["q"]).to(torch.bfloat16)
+    base.c_qi = up(gc["q_idx"]).to(torch.bfloat16)
+    base.c_w = up(gc["w"])
+    base.c_pos = up(gc["pos"])
+    base.h_q = up(gh["q"]).to(torch.bfloat16)
+    base.h_pos = up(gh["pos"])
+    torch.cuda.synchronize()
+    log(f"caches quantised on the GPU in {time.time() - t0:.1f}s")
+
+    def clone_kv(kv):
+        return v4.KVCache(kv.fmt, kv.d_nope, kv.d_rope, kv.nope.clone(), kv.rope.clone(),
+                          None if kv.scale is None else kv.scale.clone())
+
+    reps = [base]
+    for _ in range(replicas - 1):
+        r = Replica()
+        r.c_comp, r.c_win, r.h_comp, r.h_win = (clone_kv(base.c_comp), clone_kv(base.c_win),
+                                                clone_kv(base.h_comp), clone_kv(base.h_win))
+        r.c_keys = v4.IdxCache(base.c_keys.fmt, 128, base.c_keys.codes.clone(),
+                               base.c_keys.scales.clone())
+        for name in ("c_q", "c_qi", "c_w", "c_pos", "h_q", "h_pos"):
+            setattr(r, name, getattr(base, name).clone())
+        reps.append(r)
+    for r in reps:
+        r.c_topk = torch.empty(cc["B"], 1, cc["k"], dtype=torch.int32, device=dev)
+        r.c_out = torch.empty_like(r.c_q)
+        r.h_out = torch.empty_like(r.h_q)
+    torch.cuda.synchronize()
+    return reps, gc, gh
+
+
+def make_calls(v4, torch, r, ws, cc, ch):
+    """The three C-ABI calls of a step on replica r (fixed buffers)."""
+    D = 512
+    sc = D ** -0.5
+
+    def idx():
+        v4.v4attn_index_topk(r.c_qi, r.c_w, r.c_keys, r.c_pos, cc["m"], cc["k"], topk=r.c_topk,
+                             ws=ws["index"])
+
+    def csa():
+        v4.v4attn_csa_attend(r.c_q, r.c_comp, r.c_topk, r.c_win, cc["n_win"], r.c_pos, None, sc,
+                             out=r.c_out, ws=ws["csa"])
+
+    def hca():
+        v4.v4attn_hca_attend(r.h_q, r.h_comp, ch["m"], r.h_win, ch["n_win"], r.h_pos, None, sc,
+                             out=r.h_out, ws=ws["hca"])
+
+    return [idx, csa, hca]
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(gc, gh, log):
+    from oracle import codecs as C
+    from oracle.attend import hca_attend
+    from oracle.pipeline import csa_layer
+    from long_context_attention_v4attn_amd import synth
+    cc, ch = synth.WORKLOADS[CSA_WID], synth.WORKLOADS[HCA_WID]
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.time()
+    # one cache row of each layer, quantised by the oracle (setup, untimed)
+    comp = C.kv_encode(gc["comp"][:1], "fp8", 448)
+    keys = C.idx_encode(gc["keys"][:1], "mxfp4")
+    win = C.kv_encode(gc["win"][:1], "fp8", 448)
+    hcomp = C.kv_encode(gh["comp"][:1], "fp8", 448)
+    hwin = C.kv_encode(gh["win"][:1], "fp8", 448)
+    log(f"oracle setup (quantise one row of each cache) {time.time() - t0:.1f}s")
+    sc = 512 ** -0.5
+    # CSA: every query of the CSA batch against cache row 0
+    t0 = time.time()
+    for b in range(cc["B"]):
+        qb = C.bf16_encode(gc["q"][b:b + 1])
+        qi = C.bf16_decode(C.bf16_encode(gc["q_idx"][b:b + 1])).astype(np.float32)
+        csa_layer(qb, "bf16", qi, gc["w"][b:b + 1], comp, keys, win, cc["n_win"],
+                  gc["pos"][b:b + 1], cc["m"], cc["k"], sc)
+    t_csa = (time.time() - t0) / cc["B"]
+    t0 = time.time()
+    for b in range(ch["B"]):
+        qb = C.bf16_encode(gh["q"][b:b + 1])
+        hca_attend(qb, "bf16", hcomp, ch["m"], hwin, ch["n_win"], gh["pos"][b:b + 1], None, sc, "bf16")
+    t_hca = (time.time() - t0) / ch["B"]
+    value = 1.0 / (t_csa + t_hca)
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": value, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{cc['B']} CSA queries over one 1M-context cache row (index scores over "
+                       f"262144 blocks, top-2048, attend 2176 entries) + {ch['B']} HCA queries over "
+                       f"one 8192-entry row; oracle s/query: csa {t_csa:.3f}, hca {t_hca:.3f}"),
+            "cpu_model": cpu, "s_per_csa_query": t_csa, "s_per_hca_query": t_hca}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    def log(msg):
+        if not args.quiet:
+            print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import long_context_attention_v4attn_amd as v4
+    from long_context_attention_v4attn_amd import synth
+    v4.load()
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cc, ch = synth.WORKLOADS[CSA_WID], synth.WORKLOADS[HCA_WID]
+
+    reps, gc, gh = build_inputs(v4, torch, args.replicas, log)
+    ws = {
+        "index": torch.empty(v4.v4attn_workspace_bytes(v4.OP_INDEX_TOPK, cc["B"], 1, cc["H_I"], 128,
+                                                       cc["ctx"] // cc["m"], cc["k"], 0),
+                             dtype=torch.uint8, device="cuda"),
+        "csa": torch.empty(max(1, v4.v4attn_workspace_bytes(v4.OP_CSA_ATTEND, cc["B"], 1, cc["H"], 512,
+                                                            0, cc["k"], cc["n_win"])),
+                           dtype=torch.uint8, device="cuda"),
+        "hca": torch.empty(max(1, v4.v4attn_workspace_bytes(v4.OP_HCA_ATTEND, ch["B"], 1, ch["H"], 512,
+                                                            ch["ctx"] // ch["m"], ch["m"], ch["n_win"])),
+                           dtype=torch.uint8, device="cuda"),
+    }
+    calls = [make_calls(v4, torch, r, ws, cc, ch) for r in reps]
+    # eager run once per replica (also validates every call)
+    for cs in calls:
+        for f in cs:
+            f()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    if not args.no_graph:
+        graphs = []
+        cap_stream = torch.cuda.Stream()
+        for cs in calls:
+            gl = []
+            for f in cs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap_stream):
+                    f()
+                gl.append(g)
+            graphs.append(gl)
+        torch.cuda.synchronize()
+        runners = [[g.replay for g in gl] for gl in graphs]
+    else:
+        runners = calls
+    R = len(runners)
+
+    for s in range(args.warmup):
+        for f in runners[s % R]:
+            f()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        e = ev[s]
+        fs = runners[s % R]
+        e[0].record(stream)
+        fs[0]()
+        e[1].record(stream)
+        fs[1]()
+        e[2].record(stream)
+        fs[2]()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_parts = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in ev]) * 1e-3  # s
+    t_idx, t_csa_att, t_hca = t_parts.mean(axis=0)
+    t_csa = t_idx + t_csa_att
+    ms_per_step = wall / K * 1e3
+    pair_qps = 1.0 / (t_csa / cc["B"] + t_hca / ch["B"])
+
+    ab = algorithmic_bytes(cc, ch)
+    af = algorithmic_flops(cc, ch)
+    bytes_step = cc["B"] * (ab["index"] + ab["csa_attend"]) + ch["B"] * ab["hca_attend"]
+    gpu_step = t_parts.sum(axis=1).mean()
+    calls_meta = {
+        "index_topk": dict(t_us=t_idx * 1e6, bytes=cc["B"] * ab["index"], flops=cc["B"] * af["index"]),
+        "csa_attend": dict(t_us=t_csa_att * 1e6, bytes=cc["B"] * ab["csa_attend"],
+                           flops=cc["B"] * af["csa_attend"]),
+        "hca_attend": dict(t_us=t_hca * 1e6, bytes=ch["B"] * ab["hca_attend"],
+                           flops=ch["B"] * af["hca_attend"]),
+    }
+    for k_, m_ in calls_meta.items():
+        m_["GBps"] = m_["bytes"] / (m_["t_us"] * 1e-6) / 1e9
+        m_["hbm_frac"] = m_["GBps"] / HBM_PEAK_GBPS
+    dom = max(calls_meta, key=lambda k_: calls_meta[k_]["t_us"])
+    dm = calls_meta[dom]
+    roofline = {"bound": "hbm", "achieved": round(dm["GBps"], 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dm["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": dom}
+
+    result = {
+        "metric": "CSA+HCA decode queries/sec at 1M ctx; achieved HBM GB/s vs peak",
+        "value": round(pair_qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8/fp4 storage, bf16 MFMA, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "csa_decode_1m (B=4, 262144 blocks, top-2048, window 128) + "
+                               "hca_decode_1m (B=16, 8192 entries, window 128); 64 heads x D=512",
+                   "global_batch": cc["B"] + ch["B"], "seq_len": cc["ctx"], "parallelism": "none (1 GPU)"},
+        "achieved_GBps_step": round(bytes_step / gpu_step / 1e9, 1),
+        "hbm_frac_step": round(bytes_step / gpu_step / 1e9 / HBM_PEAK_GBPS, 4),
+        "csa_qps": round(cc["B"] / t_csa, 1),
+        "hca_qps": round(ch["B"] / t_hca, 1),
+        "calls": {k_: {kk: round(vv, 3) for kk, vv in m_.items()} for k_, m_ in calls_meta.items()},
+        "replicas": R,
+        "graph": not args.no_graph,
+        "roofline": roofline,
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(gc, gh, log)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
