@@ -173,7 +173,7 @@ v4a_status v4attn_index_topk(const void *q_idx, int32_t q_dtype, const float *w,
  *   topk   int32 [B][Q][k];  n_win >= 0;  pos int64 [B][Q]
  *   sink   f32 [H] or NULL
  *   out    [B][Q][H][D] out_dtype (V4A_F32 | V4A_BF16)
- * Supported: F32 entries with any D <= 512, H <= 128 (q F32 or BF16);
+ * Supported: F32 entries with D <= 512, D % 8 == 0, H <= 128 (q F32 or BF16);
  * FP8 entries with d_nope == 448, d_rope == 64, q BF16, H % 16 == 0, H <= 128.
  * win->cap must be >= n_win (the caller keeps every window token of every
  * query of the call in the ring).

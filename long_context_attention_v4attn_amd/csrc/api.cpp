@@ -46,7 +46,7 @@ v4a_status check_attend(const void* q, int32_t q_dtype, const v4a_kv* comp, cons
   if (comp->fmt == V4A_KV_FP8_BF16ROPE) {
     if (comp->d_nope != 448 || comp->d_rope != 64 || q_dtype != V4A_BF16 || H % 16 != 0)
       return V4A_ERR_UNSUPPORTED;
-  } else if (D > 512) {
+  } else if (D > 512 || D % 8 != 0) {
     return V4A_ERR_UNSUPPORTED;
   }
   return V4A_OK;
@@ -242,7 +242,7 @@ size_t v4attn_workspace_bytes(int32_t op, int32_t B, int32_t Q, int32_t H, int32
   a.H = H;
   a.d_nope = d;
   a.d_rope = 0;
-  a.fp8 = 1;
+  a.fp8 = 0;                      // fp32 partials: the larger of the two formats
   int64_t n = op == V4A_OP_CSA_ATTEND ? (int64_t)k + n_win : cap + n_win;
   attend_plan(a, n);
   return attend_workspace_bytes(a);

@@ -9,23 +9,28 @@
 // HCA has no top-k); [Notes §9] attention sink, FP8 KV with BF16 RoPE dims.
 //
 // Kernels
-//   k_attend_fp8  gfx950 MFMA path.  A workgroup = 4 waves = 64 query heads of
-//                 one query; wave w owns heads 16w..16w+15.  The entry list is
-//                 walked in tiles of 32 entries staged (raw FP8 codes + BF16
-//                 RoPE + fp32 scale) in LDS once per workgroup and read by all
-//                 four waves:
-//                   S^T = K Q^T  with v_mfma_f32_16x16x32_bf16, K rows read
-//                         with ds_read_b64 and widened e4m3 -> bf16 exactly,
-//                         Q^T held in registers for the whole kernel;
-//                   O^T += V^T P^T, V^T fragments read straight from the
-//                         row-major tile with ds_read_b64_tr_b8 (transpose
-//                         load), P^T taken from the S^T accumulators.
+//   k_attend_fp8  gfx950 MFMA path.  A workgroup = 8 waves = 64 query heads of
+//                 one query.  The entry list is walked in tiles of 32 entries
+//                 staged (raw FP8 codes + BF16 RoPE + fp32 scale) in LDS once
+//                 per workgroup and read by all eight waves:
+//                   S^T = K Q^T  by (16-head group, half of the dims): wave w
+//                         takes group w&3 and dims 256(w>>2) .. +255 with
+//                         v_mfma_f32_16x16x32_bf16; K rows are read with
+//                         ds_read_b64 and widened e4m3 -> bf16 exactly; Q^T
+//                         stays in registers; the two halves add their
+//                         partial logits through LDS;
+//                   O^T += V^T P^T by 64-dim slice: wave w owns dims
+//                         64w .. 64w+63 of all 64 heads; V^T fragments come
+//                         straight from the row-major tile with
+//                         ds_read_b64_tr_b8 / _tr_b16 (transpose loads), are
+//                         widened once and feed one MFMA per head group, with
+//                         P^T of the four groups passed through LDS.
 //                 The per-entry FP8 scale multiplies the non-RoPE logit and
 //                 the non-RoPE probability in fp32, so decoding adds no
 //                 rounding.  Online softmax in base 2 with a lazily updated
 //                 running max (rescale only when the max grows by > 8).
 //   k_attend_f32  fp32 VALU path for unquantised entries (any D <= 512).
-//   k_merge       combines split partials in fixed split order.
+//   k_merge_tiled / k_merge  combine split partials in fixed split order.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -82,8 +87,8 @@ constexpr int kRowBytes = kNope + 2 * kRope; // 576 staged bytes per entry
 constexpr int kRowStride = 592;              // padded LDS row (bank spread)
 constexpr int kChunks = kRowBytes / 16;      // 36 x 16-byte chunks per entry
 constexpr int kTileChunks = kTile * kChunks; // 1152
-constexpr int kThreads = 256;
-constexpr int kChunksPerThread = (kTileChunks + kThreads - 1) / kThreads;  // 5
+constexpr int kThreads = 512;               // 8 waves: 4 head groups x 2 halves
+constexpr int kChunksPerThread = (kTileChunks + kThreads - 1) / kThreads;  // 3
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;             // lazy max-rescale threshold (log2 units)
 
@@ -95,14 +100,12 @@ struct __align__(16) Fp8Tile {
 
 // Widen 8 e4m3 codes (two dwords) to 8 bf16 (exact).
 __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-  bf16x8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float* v) {
@@ -131,248 +134,395 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint8_t* p) {
   return o;
 }
 
-__device__ __forceinline__ void stage_load(const AttendArgs& a, const RowEntries& r, int row,
-                                           int b, int tile_e0, int e_end, u32x4* regs,
-                                           float* sc_reg, int* valid_reg) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < kChunksPerThread; j++) {
-    int c = t + j * kThreads;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (c < kTileChunks) {
-      int e = c / kChunks, part = c % kChunks;
-      int ue = tile_e0 + e;
-      if (ue < e_end) {
-        bool is_win;
-        int64_t src = entry_source(a, r, row, ue, &is_win);
-        if (src >= 0) {
-          const uint8_t* nope = is_win ? a.w_nope : a.c_nope;
-          const uint16_t* rope = is_win ? a.w_rope : a.c_rope;
-          int64_t cap = is_win ? a.w_cap : a.c_cap;
-          int64_t rowi = (int64_t)b * cap + src;
-          if (part < kNope / 16)
-            v = *(const u32x4*)(nope + rowi * kNope + part * 16);
-          else
-            v = *(const u32x4*)((const uint8_t*)(rope + rowi * kRope) + (part - kNope / 16) * 16);
-        }
-      }
-    }
-    regs[j] = v;
-  }
-  if (t < kTile) {
-    int ue = tile_e0 + t;
-    float s = 0.0f;
-    int ok = 0;
-    if (ue < e_end) {
-      bool is_win;
-      int64_t src = entry_source(a, r, row, ue, &is_win);
-      if (src >= 0) {
-        const float* sc = is_win ? a.w_scale : a.c_scale;
-        int64_t cap = is_win ? a.w_cap : a.c_cap;
-        s = sc[(int64_t)b * cap + src];
-        ok = 1;
-      }
-    }
-    *sc_reg = s;
-    *valid_reg = ok;
+// One tile's staging registers: 5 x 16 B chunks per thread plus, for the
+// first 32 threads, one entry's scale and presence flag.
+struct Stage {
+  u32x4 r[kChunksPerThread];
+  float sc;
+  int ok;                                  // bit j: chunk j present; bit 31: the scale's entry
+};
+
+// Source of every entry of this workgroup's split, resolved once into LDS
+// (top-k ids are loaded here, not inside the tile pipeline, so the pipelined
+// chunk loads never wait on another global load): >= 0 compressed row,
+// -2 - r window ring row r, -1 absent.
+constexpr int kMaxSplit = 4096;
+
+__device__ __forceinline__ void resolve_sources(const AttendArgs& a, const RowEntries& r, int row,
+                                                int e_beg, int e_end, int* src) {
+  for (int e = e_beg + threadIdx.x; e < e_end; e += blockDim.x) {
+    bool is_win;
+    int64_t sr = entry_source(a, r, row, e, &is_win);
+    src[e - e_beg] = sr < 0 ? -1 : (is_win ? (int)(-2 - sr) : (int)sr);
   }
 }
 
-__device__ __forceinline__ void stage_store(Fp8Tile* tl, const u32x4* regs, float sc, int ok) {
+// Every load is issued unconditionally (absent entries read row 0 of the
+// sequence's compressed cache, which always exists, and are zeroed), so the
+// number of loads per tile is fixed and the compiler can keep the later
+// tiles' loads in flight when it waits for an earlier one.
+__device__ __forceinline__ void stage_load(const AttendArgs& a, const int* src, int b, int tile_l0,
+                                           int n_local, Stage& st) {
+  const int t = threadIdx.x;
+  int ok = 0;
+#pragma unroll
+  for (int j = 0; j < kChunksPerThread; j++) {
+    const int c = t + j * kThreads;
+    const int e = c / kChunks, part = c % kChunks;
+    const int le = tile_l0 + e;
+    const int sraw = src[le < kMaxSplit ? le : kMaxSplit - 1];   // always in bounds
+    const int s = (c < kTileChunks && le < n_local) ? sraw : -1;
+    const bool is_win = s < -1;
+    const int64_t rr = s >= 0 ? (int64_t)s : (is_win ? (int64_t)(-2 - s) : 0);
+    const int64_t rowi = (int64_t)b * (is_win ? a.w_cap : a.c_cap) + rr;
+    const uint8_t* nope = is_win ? a.w_nope : a.c_nope;
+    const uint8_t* rope = (const uint8_t*)(is_win ? a.w_rope : a.c_rope);
+    const bool in_nope = part < kNope / 16;
+    const uint8_t* gp = in_nope ? nope + rowi * kNope + part * 16
+                                : rope + rowi * (2 * kRope) + (part - kNope / 16) * 16;
+    // the value is masked when stored to LDS, not here: using it now would
+    // make the compiler wait for this load immediately
+    st.r[j] = __builtin_nontemporal_load((const u32x4*)gp);   // streamed once: not kept in L2
+    ok |= (s != -1 ? 1 : 0) << j;
+  }
+  const int le = tile_l0 + (t & (kTile - 1));
+  const int sraw = src[le < kMaxSplit ? le : kMaxSplit - 1];
+  const int s = le < n_local ? sraw : -1;
+  const bool is_win = s < -1;
+  const int64_t rr = s >= 0 ? (int64_t)s : (is_win ? (int64_t)(-2 - s) : 0);
+  st.sc = (is_win ? a.w_scale : a.c_scale)[(int64_t)b * (is_win ? a.w_cap : a.c_cap) + rr];
+  st.ok = ok | (s != -1 ? (1 << 31) : 0);
+}
+
+__device__ __forceinline__ void stage_store(Fp8Tile* tl, const Stage& st) {
   const int t = threadIdx.x;
 #pragma unroll
   for (int j = 0; j < kChunksPerThread; j++) {
     int c = t + j * kThreads;
     if (c < kTileChunks) {
       int e = c / kChunks, part = c % kChunks;
-      *(u32x4*)(tl->rows + e * kRowStride + part * 16) = regs[j];
+      const u32x4 v = (st.ok >> j) & 1 ? st.r[j] : (u32x4){0u, 0u, 0u, 0u};
+      *(u32x4*)(tl->rows + e * kRowStride + part * 16) = v;
     }
   }
   if (t < kTile) {
-    tl->scale[t] = sc;
+    const bool ok = (st.ok >> 31) & 1;
+    tl->scale[t] = ok ? st.sc : 0.0f;
     tl->valid[t] = ok;
   }
 }
 
-__global__ void __launch_bounds__(256, 1) k_attend_fp8(AttendArgs a) {
+// Work split of the 8 waves of a workgroup (64 heads of one query):
+//  * logits and softmax by head group: wave w takes heads 16*(w&3) .. +16 and
+//    half (w>>2) of the 512 dims; the two halves add their partial logits
+//    through LDS (fp32 addition commutes: both hold identical logits) and
+//    run the same online softmax;
+//  * PV by output-dim slice: wave w owns dims 64w .. 64w+63 for all 64 heads,
+//    so each V^T fragment is widened from FP8 once and feeds four MFMAs (one
+//    per head group); P^T of the four head groups comes through LDS.
+struct __align__(16) Shared {
+  float xc[4][2][64][8];                   // partial logits [hg][half][lane][both row blocks]
+  u32x4 pB[4][64];                         // P^T operand (RoPE dims) [hg][lane]
+  u32x4 pnB[4][64];                        // (P * scale)^T operand (FP8 dims)
+  float alpha[64];                         // per-head rescale of this tile (1 = none)
+  float fin[64];                           // per-head output factor (epilogue)
+  int any_rescale;
+};
+
+// Softmax state of a logits wave (its lane's head); both halves agree.
+struct SoftState {
+  float m_run;
+  float l_run;                             // lane-partial denominator
+};
+
+__device__ __forceinline__ void qk_softmax(const Fp8Tile* tl, Shared* sh, const bf16x8* qf,
+                                           SoftState& S, float c2, int hg, int half, int g,
+                                           int li) {
+  const int lane = threadIdx.x & 63;
+  // ---- partial S^T = K Q^T over this half's dims, both row blocks
+  float part[8];
+#pragma unroll
+  for (int rb = 0; rb < 2; rb++) {
+    f32x4 sn = {0.f, 0.f, 0.f, 0.f}, sr = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* kr = tl->rows + (rb * 16 + li) * kRowStride + g * 8 + half * 256;
+    const int nks = half ? 6 : 8;          // FP8 k-steps of 32 dims
+#pragma unroll
+    for (int ks = 0; ks < 8; ks++) {
+      if (ks < nks) {
+        u32x2 w = *(const u32x2*)(kr + ks * 32);
+        sn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(w[0], w[1]), qf[ks], sn, 0, 0, 0);
+      }
+    }
+    if (half) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        u32x4 v = *(const u32x4*)(tl->rows + (rb * 16 + li) * kRowStride + kNope + ks * 64 + g * 16);
+        sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), qf[6 + ks], sr,
+                                                     0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) part[rb * 4 + i] = sn[i] * tl->scale[rb * 16 + g * 4 + i] + sr[i];
+  }
+  f32x4* mine = (f32x4*)sh->xc[hg][half][lane];
+  mine[0] = (f32x4){part[0], part[1], part[2], part[3]};
+  mine[1] = (f32x4){part[4], part[5], part[6], part[7]};
+  __syncthreads();
+  const f32x4* oth = (const f32x4*)sh->xc[hg][half ^ 1][lane];
+  const f32x4 o0 = oth[0], o1 = oth[1];
+  float s2[8], scl[8];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int e = (i >> 2) * 16 + g * 4 + (i & 3);
+    const float v = (part[i] + (i < 4 ? o0[i] : o1[i - 4])) * c2;
+    s2[i] = tl->valid[e] ? v : -INFINITY;
+    scl[i] = tl->scale[e];
+    tmax = fmaxf(tmax, s2[i]);
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  // lazy rescale: the running max moves only when it grows by more than
+  // kRescale (exact: P <= 2^kRescale, and the final normalisation uses the
+  // same max); the factor goes to the PV waves through LDS
+  const bool need = (S.m_run == -INFINITY) ? (tmax > -INFINITY) : (tmax > S.m_run + kRescale);
+  float alpha = 1.0f;
+  if (need) {
+    alpha = (S.m_run == -INFINITY) ? 0.0f : exp2f(S.m_run - tmax);
+    S.l_run *= alpha;
+    S.m_run = tmax;
+  }
+  const float m_use = (S.m_run == -INFINITY) ? 0.0f : S.m_run;
+  float pv[8], pn[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    float p = exp2f(s2[i] - m_use);
+    S.l_run += p;
+    pv[i] = p;
+    pn[i] = p * scl[i];
+  }
+  if (half == 0) {
+    sh->pB[hg][lane] = __builtin_bit_cast(u32x4, pack8(pv));
+    sh->pnB[hg][lane] = __builtin_bit_cast(u32x4, pack8(pn));
+    if (g == 0) sh->alpha[hg * 16 + li] = alpha;
+    if (__builtin_amdgcn_ballot_w64(need) && lane == 0) sh->any_rescale = 1;
+  }
+}
+
+// PV for wave `ds` (dims 64ds .. 64ds+63), all four head groups.  acc[db][ht]:
+// O^T block of dims 64ds + 16db .. +16 x heads 16ht .. +16.
+__device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f32x4 (*acc)[4],
+                                         int ds, int g, int li) {
+  const int lane = threadIdx.x & 63;
+  if (sh->any_rescale) {
+#pragma unroll
+    for (int ht = 0; ht < 4; ht++) {
+      const float al = sh->alpha[ht * 16 + li];
+#pragma unroll
+      for (int db = 0; db < 4; db++) acc[db][ht] *= al;
+    }
+  }
+  // lane group g's k-values are entries {4g..4g+3, 16+4g..16+4g+3}; source
+  // lane s of the group points at the entry k = s/2 (tr8) resp. s/4 (tr16)
+  const int s = li;
+  if (ds < 7) {
+    bf16x8 pnB[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ht++) pnB[ht] = __builtin_bit_cast(bf16x8, sh->pnB[ht][lane]);
+    const int kk8 = s >> 1;
+    const int ent8 = (kk8 < 4) ? (g * 4 + kk8) : (16 + g * 4 + kk8 - 4);
+    const uint8_t* vb8 = tl->rows + ent8 * kRowStride + (s & 1) * 8 + ds * 64;
+#pragma unroll
+    for (int db = 0; db < 4; db++) {
+      u32x2 w = lds_tr8(vb8 + db * 16);
+      const bf16x8 v = widen8(w[0], w[1]);
+#pragma unroll
+      for (int ht = 0; ht < 4; ht++)
+        acc[db][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pnB[ht], acc[db][ht], 0, 0, 0);
+    }
+  } else {
+    bf16x8 pB[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ht++) pB[ht] = __builtin_bit_cast(bf16x8, sh->pB[ht][lane]);
+    const int kk16 = s >> 2;
+    const uint8_t* vlo = tl->rows + (g * 4 + kk16) * kRowStride + kNope + (s & 3) * 8;
+    const uint8_t* vhi = tl->rows + (16 + g * 4 + kk16) * kRowStride + kNope + (s & 3) * 8;
+#pragma unroll
+    for (int db = 0; db < 4; db++) {
+      u32x2 lo = lds_tr16(vlo + db * 32);
+      u32x2 hi = lds_tr16(vhi + db * 32);
+      const bf16x8 v = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+      for (int ht = 0; ht < 4; ht++)
+        acc[db][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pB[ht], acc[db][ht], 0, 0, 0);
+    }
+  }
+}
+
+// Workgroup -> (query row, split, group of 64 heads).  Workgroups are
+// dispatched to the 8 XCDs round-robin; consecutive positions within one XCD
+// take consecutive splits, so the splits of one query share an XCD (its L2).
+__device__ __forceinline__ bool wg_coords(const AttendArgs& a, int* row, int* split, int* hgrp) {
+  const int n_hg = (a.H + 63) / 64;
+  const int64_t N = (int64_t)a.B * a.Q * n_hg * a.n_split;
+  const int64_t per = (N + 7) / 8;
+  const int64_t L = blockIdx.x;
+  const int64_t P = (L % 8) * per + L / 8;
+  if (P >= N) return false;
+  const int64_t grp = P / a.n_split;
+  *split = (int)(P % a.n_split);
+  *row = (int)(grp / n_hg);
+  *hgrp = (int)(grp % n_hg);
+  return true;
+}
+
+// Split partials of the FP8 path live in the workspace in the accumulator
+// layout, so that a wave stores (and the merge loads) whole contiguous
+// 1 KiB runs: the block of (row, split, head group) holds nh x 512 values
+// ordered [dim slice 8][dim block 4][head tile nht][lane 64][4].
+__device__ __forceinline__ int64_t part_block(const AttendArgs& a, int row, int split, int hgrp) {
+  return (((int64_t)row * a.n_split + split) * a.H + hgrp * 64) * (kNope + kRope);
+}
+
+__global__ void __launch_bounds__(kThreads, 1) k_attend_fp8(AttendArgs a) {
   __shared__ Fp8Tile tiles[2];
-  const int row = blockIdx.x;              // b * Q + j
-  const int split = blockIdx.y;
-  const int hg = blockIdx.z;               // group of 64 heads
+  __shared__ Shared sh;
+  __shared__ int src[kMaxSplit];
+  int row, split, hgrp;
+  if (!wg_coords(a, &row, &split, &hgrp)) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int hg = wave & 3;                 // logits: 16-head group within the 64
+  const int half = wave >> 2;              // logits: dims 0..255 or 256..511
   const int b = row / a.Q;
   const int g = lane >> 4;                 // lane group 0..3
   const int li = lane & 15;
-  const int head = hg * 64 + wave * 16 + li;
+  const int head = hgrp * 64 + hg * 16 + li;
   const bool head_ok = head < a.H;
+  const int nht = min(4, (a.H - hgrp * 64) / 16);   // head tiles present (H % 16 == 0)
   const int D = kNope + kRope;
 
-  RowEntries r = row_entries(a, row);
+  const RowEntries r = row_entries(a, row);
   const int n_tot = r.n_c + r.n_w;
   const int e_beg = split * a.split_size;
   const int e_end = min(e_beg + a.split_size, n_tot);
+  const int n_local = e_end > e_beg ? e_end - e_beg : 0;
+  const int n_tiles = (n_local + kTile - 1) / kTile;
 
-  // Q^T fragments: k-step ks covers dims 32ks .. 32ks+31; lane holds dims
-  // 32ks + 8g .. +8 of its head (zero for heads beyond H).
-  bf16x8 qf[16];
+  resolve_sources(a, r, row, e_beg, e_end, src);
+  __syncthreads();
+
+  // two tiles in flight: tile t is staged in set t % 2
+  Stage s0, s1;
+  if (n_tiles > 0) stage_load(a, src, b, 0, n_local, s0);
+  if (n_tiles > 1) stage_load(a, src, b, kTile, n_local, s1);
+
+  // Q^T fragments of this wave's half: k-step ks covers dims
+  // 256*half + 32ks .. +31 (the RoPE dims are k-steps 6, 7 of half 1); the
+  // lane holds dims +8g .. +8 of its head (zero for heads beyond H)
+  bf16x8 qf[8];
   {
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.H + (head_ok ? head : 0)) * D;
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.H + (head_ok ? head : 0)) * D +
+                         half * 256 + g * 8;
 #pragma unroll
-    for (int ks = 0; ks < 16; ks++) {
-      u32x4 v = *(const u32x4*)(qp + ks * 32 + g * 8);
+    for (int ks = 0; ks < 8; ks++) {
+      u32x4 v = *(const u32x4*)(qp + ks * 32);
       if (!head_ok) v = (u32x4){0u, 0u, 0u, 0u};
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
-
-  f32x4 acc[32];                           // O^T blocks: 28 nope + 4 rope, 16 dims each
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 32; i++) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;                 // running max used for P (log2 units)
-  float l_run = 0.0f;                      // lane-partial denominator
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  SoftState S;
+  S.m_run = -INFINITY;
+  S.l_run = 0.0f;
   const float c2 = a.sm_scale * kLog2e;
 
-  const int n_tiles = e_end > e_beg ? (e_end - e_beg + kTile - 1) / kTile : 0;
-  u32x4 regs[kChunksPerThread];
-  float sc_reg = 0.f;
-  int valid_reg = 0;
   if (n_tiles > 0) {
-    stage_load(a, r, row, b, e_beg, e_end, regs, &sc_reg, &valid_reg);
-    stage_store(&tiles[0], regs, sc_reg, valid_reg);
+    stage_store(&tiles[0], s0);
+    if (n_tiles > 2) stage_load(a, src, b, 2 * kTile, n_local, s0);
   }
   __syncthreads();
 
-  for (int it = 0; it < n_tiles; it++) {
-    const Fp8Tile* tl = &tiles[it & 1];
-    const bool more = it + 1 < n_tiles;
-    if (more) stage_load(a, r, row, b, e_beg + (it + 1) * kTile, e_end, regs, &sc_reg, &valid_reg);
+  // step t: logits + softmax of tile t, PV of tile t, move tile t+1 (set
+  // (t+1)%2) into LDS, refill that set with tile t+3
+#define V4A_STEP(T, SET)                                                          \
+  {                                                                               \
+    const int t_ = (T);                                                           \
+    if (t_ >= n_tiles) break;                                                     \
+    if (threadIdx.x == 0) sh.any_rescale = 0;                                     \
+    qk_softmax(&tiles[t_ & 1], &sh, qf, S, c2, hg, half, g, li);                  \
+    __syncthreads();                                                              \
+    pv_slice(&tiles[t_ & 1], &sh, acc, wave, g, li);                              \
+    if (t_ + 1 < n_tiles) {                                                       \
+      stage_store(&tiles[(t_ + 1) & 1], SET);                                     \
+      if (t_ + 3 < n_tiles) stage_load(a, src, b, (t_ + 3) * kTile, n_local, SET); \
+    }                                                                             \
+    __syncthreads();                                                              \
+  }
+  for (int it = 0; it < n_tiles; it += 2) {
+    V4A_STEP(it, s1)
+    V4A_STEP(it + 1, s0)
+  }
+#undef V4A_STEP
 
-    // ---- S^T = K Q^T for the two 16-entry row blocks
-    f32x4 sn[2], sr[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; rb++) {
-      sn[rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      sr[rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      const uint8_t* kr = tl->rows + (rb * 16 + li) * kRowStride + g * 8;
-#pragma unroll
-      for (int ks = 0; ks < 14; ks++) {
-        u32x2 w = *(const u32x2*)(kr + ks * 32);
-        sn[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(w[0], w[1]), qf[ks], sn[rb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
-        u32x4 v = *(const u32x4*)(tl->rows + (rb * 16 + li) * kRowStride + kNope + ks * 64 + g * 16);
-        sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), qf[14 + ks],
-                                                         sr[rb], 0, 0, 0);
-      }
-    }
-
-    // ---- logits (log2 units), masked entries -> -inf
-    float s2[8], scl[8];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int rb = 0; rb < 2; rb++) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        int e = rb * 16 + g * 4 + i;
-        float sc = tl->scale[e];
-        bool ok = tl->valid[e] != 0;
-        float v = (sn[rb][i] * sc + sr[rb][i]) * c2;
-        v = ok ? v : -INFINITY;
-        s2[rb * 4 + i] = v;
-        scl[rb * 4 + i] = sc;
-        tmax = fmaxf(tmax, v);
+  // ---- epilogue: the logits waves of half 0 publish each head's factor
+  float l_tot = S.l_run + __shfl_xor(S.l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (half == 0 && g == 0) {
+    float f;
+    if (a.n_split == 1) {
+      const float z2 = (a.sink && head_ok) ? a.sink[head] * kLog2e : -INFINITY;
+      const float M = fmaxf(S.m_run, z2);
+      const float so = (S.m_run == -INFINITY) ? 0.0f : exp2f(S.m_run - M);
+      const float den = l_tot * so + ((z2 == -INFINITY) ? 0.0f : exp2f(z2 - M));
+      f = den > 0.0f ? so / den : 0.0f;
+    } else {
+      // partial: O / l (zero when the split saw nothing) + (max, denominator)
+      f = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      if (head_ok) {
+        const int64_t pi = ((int64_t)row * a.n_split + split) * a.H + head;
+        a.part_ml[pi * 2 + 0] = l_tot > 0.0f ? S.m_run : -INFINITY;
+        a.part_ml[pi * 2 + 1] = l_tot;
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // lazy rescale: move the running max only when it grows by more than
-    // kRescale (exact: P <= 2^kRescale and the final normalisation uses the
-    // same max)
-    bool need = (m_run == -INFINITY) ? (tmax > -INFINITY) : (tmax > m_run + kRescale);
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      float m_new = need ? tmax : m_run;
-      float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
-      if (need) {
-        l_run *= alpha;
+    sh.fin[hg * 16 + li] = f;
+  }
+  __syncthreads();
+  // PV wave `wave` holds O^T dims 64*wave + 16db + 4g + i of head 16ht + li
+  if (a.n_split == 1) {
 #pragma unroll
-        for (int i = 0; i < 32; i++) acc[i] *= alpha;
-        m_run = m_new;
-      }
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-    float pv[8], pn[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      float p = exp2f(s2[i] - m_use);
-      l_run += p;
-      pv[i] = p;
-      pn[i] = p * scl[i];
-    }
-    const bf16x8 pB = pack8(pv);           // P^T  (RoPE dims)
-    const bf16x8 pnB = pack8(pn);          // (P * scale)^T (FP8 dims)
-
-    // ---- O^T += V^T P^T; lane group g's k-values are entries
-    // {4g..4g+3, 16+4g..16+4g+3}; source lane s of the group points at the
-    // entry k = s/2 (tr8) resp. s/4 (tr16)
-    {
-      const int s = li;
-      const int kk8 = s >> 1;
-      const int ent8 = (kk8 < 4) ? (g * 4 + kk8) : (16 + g * 4 + kk8 - 4);
-      const uint8_t* vb8 = tl->rows + ent8 * kRowStride + (s & 1) * 8;
-#pragma unroll
-      for (int db = 0; db < 28; db++) {
-        u32x2 w = lds_tr8(vb8 + db * 16);
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(w[0], w[1]), pnB, acc[db], 0, 0, 0);
-      }
-      const int kk16 = s >> 2;
-      const uint8_t* vlo = tl->rows + (g * 4 + kk16) * kRowStride + kNope + (s & 3) * 8;
-      const uint8_t* vhi = tl->rows + (16 + g * 4 + kk16) * kRowStride + kNope + (s & 3) * 8;
+    for (int ht = 0; ht < 4; ht++) {
+      if (ht >= nht) break;
+      const float f = sh.fin[ht * 16 + li];
+      const int64_t ob = ((int64_t)row * a.H + hgrp * 64 + ht * 16 + li) * D + wave * 64 + g * 4;
 #pragma unroll
       for (int db = 0; db < 4; db++) {
-        u32x2 lo = lds_tr16(vlo + db * 32);
-        u32x2 hi = lds_tr16(vhi + db * 32);
-        u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
-        acc[28 + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pB,
-                                                               acc[28 + db], 0, 0, 0);
-      }
-    }
-
-    if (more) stage_store(&tiles[(it + 1) & 1], regs, sc_reg, valid_reg);
-    __syncthreads();
-  }
-
-  // ---- epilogue: lane (g, li) holds O^T dims 16db + 4g + i of head `head`
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (!head_ok) return;
-  if (a.n_split == 1) {
-    float z2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
-    float M = fmaxf(m_run, z2);
-    float so = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
-    float den = l_tot * so + ((z2 == -INFINITY) ? 0.0f : exp2f(z2 - M));
-    float f = den > 0.0f ? so / den : 0.0f;
-    int64_t ob = ((int64_t)row * a.H + head) * D;
-#pragma unroll
-    for (int db = 0; db < 32; db++) {
-      int d0 = db * 16 + g * 4;
-      f32x4 o = acc[db] * f;
-      if (a.out_bf16) {
-        uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-        uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-        *(u32x2*)((uint16_t*)a.out + ob + d0) = (u32x2){lo, hi};
-      } else {
-        *(f32x4*)((float*)a.out + ob + d0) = o;
+        const f32x4 o = acc[db][ht] * f;
+        if (a.out_bf16) {
+          const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+          const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+          *(u32x2*)((uint16_t*)a.out + ob + db * 16) = (u32x2){lo, hi};
+        } else {
+          *(f32x4*)((float*)a.out + ob + db * 16) = o;
+        }
       }
     }
   } else {
-    int64_t pi = ((int64_t)row * a.n_split + split) * a.H + head;
+    uint16_t* po = (uint16_t*)a.part_o + part_block(a, row, split, hgrp);
 #pragma unroll
-    for (int db = 0; db < 32; db++) *(f32x4*)(a.part_o + pi * D + db * 16 + g * 4) = acc[db];
-    if (g == 0) {
-      a.part_ml[pi * 2 + 0] = m_run;
-      a.part_ml[pi * 2 + 1] = l_tot;
+    for (int db = 0; db < 4; db++) {
+#pragma unroll
+      for (int ht = 0; ht < 4; ht++) {
+        if (ht >= nht) break;
+        const f32x4 o = acc[db][ht] * sh.fin[ht * 16 + li];
+        const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+        const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+        *(u32x2*)(po + (((int64_t)(wave * 4 + db) * nht + ht) * 64 + lane) * 4) = (u32x2){lo, hi};
+      }
     }
   }
 }
@@ -496,44 +646,109 @@ __global__ void __launch_bounds__(256) k_attend_f32(AttendArgs a) {
       if (a.out_bf16) ((uint16_t*)a.out)[oi] = (uint16_t)f32_to_bf16_bits(v);
       else ((float*)a.out)[oi] = v;
     } else {
+      // partial: O / l in fp32 (zero when the split saw nothing) + (max, denominator)
       int64_t pi = ((int64_t)row * a.n_split + split) * a.H + head;
-      a.part_o[pi * D + d] = o[j];
+      const float l = lrun[h];
+      ((float*)a.part_o)[pi * D + d] = l > 0.f ? o[j] / l : 0.f;
       if (d == 0) {
-        a.part_ml[pi * 2] = mrun[h];
-        a.part_ml[pi * 2 + 1] = lrun[h];
+        a.part_ml[pi * 2] = l > 0.f ? mrun[h] : -INFINITY;
+        a.part_ml[pi * 2 + 1] = l;
       }
     }
   }
 }
 
 // ---------------------------------------------------------------- merge
-// out[row][h][:] = sum_s O_s 2^(m_s - M) / (sum_s l_s 2^(m_s - M) + 2^(z - M)),
-// splits visited in index order (deterministic).
+// Split s carries On_s = O_s / l_s and (m_s, l_s).  With M = max(max_s m_s, z):
+//   out = sum_s w_s On_s / (sum_s w_s + 2^(z - M)),  w_s = l_s 2^(m_s - M),
+// splits visited in index order (deterministic).  fp32 path: row-major fp32
+// partials; one workgroup per (query, 4 heads); each thread owns 8
+// consecutive dims of one head.
+constexpr int kMergeHeads = 4;
+
 __global__ void __launch_bounds__(256) k_merge(AttendArgs a) {
   const int row = blockIdx.x;
-  const int head = blockIdx.y;
   const int D = a.d_nope + a.d_rope;
+  const int per_head = D / 8;                        // threads per head
+  const int hl = threadIdx.x / per_head;
+  const int d0 = (threadIdx.x % per_head) * 8;
+  const int head = blockIdx.y * kMergeHeads + hl;
+  if (hl >= kMergeHeads || head >= a.H) return;
   const float* ml = a.part_ml + ((int64_t)row * a.n_split * a.H) * 2;
-  float z2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
+  const float z2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
   float M = z2;
   for (int s = 0; s < a.n_split; s++) M = fmaxf(M, ml[((int64_t)s * a.H + head) * 2]);
-  float den = (z2 == -INFINITY || M == -INFINITY) ? 0.f : exp2f(z2 - M);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) acc[i] = 0.f;
+  float den = (M == -INFINITY || z2 == -INFINITY) ? 0.f : exp2f(z2 - M);
   for (int s = 0; s < a.n_split; s++) {
-    float m = ml[((int64_t)s * a.H + head) * 2];
-    if (m != -INFINITY) den += ml[((int64_t)s * a.H + head) * 2 + 1] * exp2f(m - M);
+    const float m = ml[((int64_t)s * a.H + head) * 2];
+    if (m == -INFINITY) continue;
+    const float w = ml[((int64_t)s * a.H + head) * 2 + 1] * exp2f(m - M);
+    den += w;
+    const float* p = (const float*)a.part_o + (((int64_t)row * a.n_split + s) * a.H + head) * D + d0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] += w * p[i];
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < a.n_split; s++) {
-      float m = ml[((int64_t)s * a.H + head) * 2];
-      if (m == -INFINITY) continue;
-      acc += a.part_o[(((int64_t)row * a.n_split + s) * a.H + head) * D + d] * exp2f(m - M);
-    }
-    float v = acc * inv;
-    int64_t oi = ((int64_t)row * a.H + head) * D + d;
-    if (a.out_bf16) ((uint16_t*)a.out)[oi] = (uint16_t)f32_to_bf16_bits(v);
-    else ((float*)a.out)[oi] = v;
+  const int64_t oi = ((int64_t)row * a.H + head) * D + d0;
+  if (a.out_bf16) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      v[i] = f32_to_bf16_bits(acc[2 * i] * inv) | (f32_to_bf16_bits(acc[2 * i + 1] * inv) << 16);
+    *(u32x4*)((uint16_t*)a.out + oi) = v;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) ((float*)a.out)[oi + i] = acc[i] * inv;
+  }
+}
+
+// FP8 path: partials in the accumulator layout (bf16).  One workgroup per
+// (query, head group of 64, 1/32 of the block); thread t owns 4
+// consecutive values of the block, i.e. 4 dims of one head.
+__global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
+  const int row = blockIdx.x, hgrp = blockIdx.y;
+  const int D = kNope + kRope;
+  const int nht = min(4, (a.H - hgrp * 64) / 16);
+  const int n_vals = nht * 16 * D;                     // values in the block
+  const int j = (blockIdx.z * 256 + threadIdx.x) * 4;  // first owned value
+  if (j >= n_vals) return;
+  // decode [dim slice][dim block][head tile][lane][4]
+  const int q4 = j >> 2;
+  const int ln = q4 & 63;
+  const int ht = (q4 >> 6) % nht;
+  const int sb = (q4 >> 6) / nht;                      // dim slice * 4 + dim block
+  const int head = hgrp * 64 + ht * 16 + (ln & 15);
+  const int d0 = sb * 16 + (ln >> 4) * 4;
+  const float* ml = a.part_ml + ((int64_t)row * a.n_split * a.H) * 2;
+  const float z2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
+  float M = z2;
+  for (int s = 0; s < a.n_split; s++) M = fmaxf(M, ml[((int64_t)s * a.H + head) * 2]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float den = (M == -INFINITY || z2 == -INFINITY) ? 0.f : exp2f(z2 - M);
+  const uint16_t* po = (const uint16_t*)a.part_o + part_block(a, row, 0, hgrp) + j;
+  const int64_t sstride = (int64_t)a.H * D;
+  for (int s = 0; s < a.n_split; s++) {
+    const float m = ml[((int64_t)s * a.H + head) * 2];
+    if (m == -INFINITY) continue;
+    const float w = ml[((int64_t)s * a.H + head) * 2 + 1] * exp2f(m - M);
+    den += w;
+    const u32x2 v = *(const u32x2*)(po + s * sstride);
+    acc[0] += w * bf16_bits_to_f32(v[0] & 0xFFFFu);
+    acc[1] += w * bf16_bits_to_f32(v[0] >> 16);
+    acc[2] += w * bf16_bits_to_f32(v[1] & 0xFFFFu);
+    acc[3] += w * bf16_bits_to_f32(v[1] >> 16);
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const int64_t oi = ((int64_t)row * a.H + head) * D + d0;
+  if (a.out_bf16) {
+    const uint32_t lo = f32_to_bf16_bits(acc[0] * inv) | (f32_to_bf16_bits(acc[1] * inv) << 16);
+    const uint32_t hi = f32_to_bf16_bits(acc[2] * inv) | (f32_to_bf16_bits(acc[3] * inv) << 16);
+    *(u32x2*)((uint16_t*)a.out + oi) = (u32x2){lo, hi};
+  } else {
+    *(f32x4*)((float*)a.out + oi) = (f32x4){acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
   }
 }
 
@@ -546,27 +761,33 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // any batch size.
 void attend_plan(AttendArgs& a, int64_t n_entries_max) {
   const int D = a.d_nope + a.d_rope;
+  a.part_bf16 = a.fp8;
   a.f32_heads = a.fp8 ? 64 : (a.H < 4096 / D ? a.H : (4096 / D > 0 ? 4096 / D : 1));
   int64_t per = (n_entries_max + 15) / 16;
   if (per < 128) per = 128;
   per = (per + 31) / 32 * 32;
+  if (per > kMaxSplit) per = kMaxSplit;
   a.split_size = (int)per;
   int64_t ns = n_entries_max > 0 ? (n_entries_max + per - 1) / per : 1;
   a.n_split = (int)ns;
 }
 
+// partial O: bf16 on the FP8 path, fp32 on the fp32 path; the workspace
+// query sizes for fp32 (the larger of the two)
+static size_t part_elem(const AttendArgs& a) { return a.part_bf16 ? 2 : 4; }
+
 size_t attend_workspace_bytes(const AttendArgs& a) {
   if (a.n_split <= 1) return 0;
   const size_t R = (size_t)a.B * a.Q, D = a.d_nope + a.d_rope;
-  return align256(R * a.n_split * a.H * D * sizeof(float)) +
+  return align256(R * a.n_split * a.H * D * part_elem(a)) +
          align256(R * a.n_split * a.H * 2 * sizeof(float));
 }
 
 void attend_carve(AttendArgs& a, void* ws) {
   if (a.n_split <= 1) { a.part_o = nullptr; a.part_ml = nullptr; return; }
   const size_t R = (size_t)a.B * a.Q, D = a.d_nope + a.d_rope;
-  a.part_o = (float*)ws;
-  a.part_ml = (float*)((char*)ws + align256(R * a.n_split * a.H * D * sizeof(float)));
+  a.part_o = ws;
+  a.part_ml = (float*)((char*)ws + align256(R * a.n_split * a.H * D * part_elem(a)));
 }
 
 size_t attend_f32_smem(const AttendArgs& a) {
@@ -580,15 +801,23 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   const int rows = a.B * a.Q;
   if (rows == 0) return hipSuccess;
   if (a.fp8) {
-    dim3 grid(rows, a.n_split, (a.H + 63) / 64);
-    hipLaunchKernelGGL(k_attend_fp8, grid, dim3(kThreads), 0, st, a);
+    const int64_t N = (int64_t)rows * a.n_split * ((a.H + 63) / 64);
+    const int64_t per = (N + 7) / 8;
+    hipLaunchKernelGGL(k_attend_fp8, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st, a);
   } else {
     dim3 grid(rows, a.n_split, (a.H + a.f32_heads - 1) / a.f32_heads);
     hipLaunchKernelGGL(k_attend_f32, grid, dim3(256), attend_f32_smem(a), st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  hipLaunchKernelGGL(k_merge, dim3(rows, a.H), dim3(256), 0, st, a);
+  if (a.fp8) {
+    // 64 heads x 512 dims / (256 threads x 4 values) = 32 workgroups per block
+    const int parts = (64 * (kNope + kRope)) / (256 * 4);
+    hipLaunchKernelGGL(k_merge_tiled, dim3(rows, (a.H + 63) / 64, parts), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(k_merge, dim3(rows, (a.H + kMergeHeads - 1) / kMergeHeads), dim3(256), 0, st,
+                       a);
+  }
   return hipGetLastError();
 }
 

@@ -5,21 +5,31 @@
 // [Notes §9] the indexer's QK path runs in FP4 (keys and queries MXFP4), and
 // the selector ranks fp32 scores.
 //
-// Kernels
-//   k_quant_q     query heads -> MXFP4 (e2m1 codes + e8m0 scale per 32).
-//   k_score_mx    FP4 scan: one v_mfma_scale_f32_16x16x128_f8f6f4 per
-//                 (16 heads, 16 blocks); M = index heads, N = blocks, K = 128
-//                 dims; the e8m0 block scales feed the MFMA's scale operands,
-//                 so products are exact.  The ReLU / head-weight sum is an
-//                 fp32 epilogue: in-lane over 4 heads, then across the four
-//                 lane groups.  Keys stream in coalesced 1 KB wave loads.
-//   k_score_f32   fp32 VALU dot products for unquantised keys.
-//   k_select      exact top-k per query: radix select on the 64-bit key
-//                 (order-preserving fp32 score bits, inverted block id) in
-//                 11/11/10-bit digits with LDS histograms; stops as soon as
-//                 the threshold bin holds exactly the remaining count; the
-//                 selected ids are then compacted in ascending order with a
-//                 block scan (so the output is deterministic), -1 padded.
+// Pipeline of one v4attn_index_topk call (four launches):
+//   k_prep       query heads -> MXFP4 (e2m1 codes + e8m0 scale per 32); zero
+//                the per-query histogram and counters.
+//   k_score_mx   FP4 scan: one v_mfma_scale_f32_16x16x128_f8f6f4 per
+//                (16 index heads, 16 blocks): M = heads, N = blocks, K = 128
+//                dims; the e8m0 scales feed the MFMA's scale operands, so the
+//                per-head dots are exact.  fp32 epilogue: ReLU, head weight,
+//                sum over heads (in-lane over 4 heads, then across the four
+//                lane groups).  A wave streams 256 blocks per iteration (16 KB
+//                of keys in coalesced 1 KB loads); the next iteration's loads
+//                are in flight while the current one computes.  The
+//                workgroup histograms the top 11 bits of its scores'
+//                order-preserving keys in LDS and flushes once (global atomics).
+//   k_score_f32  fp32 VALU variant for unquantised keys (same histogram).
+//   k_filter1    per query, many workgroups: the histogram gives the bin b1
+//                (key bits 31..21) that holds the k-th largest score; ids
+//                above b1 are selected outright (wave-aggregated atomics);
+//                ids in b1 are histogrammed on key bits 20..10.
+//   k_filter2    same split: that second histogram gives the bin b2; ids in
+//                b1 and above b2 are selected, ids in (b1, b2) become
+//                candidates.  The last workgroup of the query to finish
+//                resolves the candidates exactly (radix select on the 64-bit
+//                key = score key : inverted id, so ties go to the lower id),
+//                then sorts the k selected ids ascending in LDS and pads with
+//                -1.  The output is deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,27 +37,42 @@ namespace v4a {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kBins = 2048;                // first radix digit: key bits 31..21
+constexpr int kCandCap = 16384;            // candidate slots per query
+constexpr int kFilterChunk = 8192;         // scores per filter workgroup
+constexpr int kCtr = 4;                    // counters per query
+
 size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx) {
   const size_t R = (size_t)B * Q;
   size_t n = 0;
   if (key_mx) n += align256(R * H * (d / 2)) + align256(R * H * (d / 32));
   n += align256(R * (size_t)cap * sizeof(float));
+  n += 2 * align256(R * kBins * sizeof(uint32_t));
+  n += align256(R * kCtr * sizeof(uint32_t));
+  n += align256(R * kCandCap * sizeof(uint64_t));
   return n;
 }
 
 void index_carve(IndexArgs& a, void* ws) {
   const size_t R = (size_t)a.B * a.Q;
   char* p = (char*)ws;
+  a.qmx = nullptr;
+  a.qsc = nullptr;
   if (a.key_mx) {
     a.qmx = (uint8_t*)p;
     p += align256(R * a.H * (a.d / 2));
     a.qsc = (uint8_t*)p;
     p += align256(R * a.H * (a.d / 32));
-  } else {
-    a.qmx = nullptr;
-    a.qsc = nullptr;
   }
   a.scores = (float*)p;
+  p += align256(R * (size_t)a.cap * sizeof(float));
+  a.hist = (uint32_t*)p;
+  p += align256(R * kBins * sizeof(uint32_t));
+  a.hist2 = (uint32_t*)p;
+  p += align256(R * kBins * sizeof(uint32_t));
+  a.ctr = (uint32_t*)p;
+  p += align256(R * kCtr * sizeof(uint32_t));
+  a.cand = (uint64_t*)p;
 }
 
 __device__ __forceinline__ int64_t n_visible(int64_t p, int m, int64_t cap) {
@@ -56,109 +81,188 @@ __device__ __forceinline__ int64_t n_visible(int64_t p, int m, int64_t cap) {
   return nv < cap ? nv : cap;
 }
 
-// ---------------------------------------------------------------- query MXFP4
-// One wave per (row, head): 128 elements, 2 per lane; a group of 32 elements
-// is 16 lanes.
-__global__ void __launch_bounds__(256) k_quant_q(IndexArgs a) {
-  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int lane = threadIdx.x & 63;
+// Order-preserving key of a score; -0 is ranked equal to +0.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  if (f == 0.0f) f = 0.0f;
+  return order_key(f);
+}
+
+// ---------------------------------------------------------------- prep
+__global__ void __launch_bounds__(256) k_prep(IndexArgs a) {
   const int R = a.B * a.Q;
-  if (wave >= R * a.H) return;
-  const size_t base = (size_t)wave * a.d;
-  float x0 = load_as_f32(a.q, a.q_bf16, base + 2 * lane);
-  float x1 = load_as_f32(a.q, a.q_bf16, base + 2 * lane + 1);
-  float am = fmaxf(fabsf(x0), fabsf(x1));
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t nthr = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = tid; i < (size_t)R * kBins; i += nthr) {
+    a.hist[i] = 0u;
+    a.hist2[i] = 0u;
+  }
+  for (size_t i = tid; i < (size_t)R * kCtr; i += nthr) a.ctr[i] = 0u;
+  if (!a.key_mx) return;
+  // one wave per (row, head): 128 elements, 2 per lane; a group of 32 is 16 lanes
+  const int lane = threadIdx.x & 63;
+  for (size_t wave = tid >> 6; wave < (size_t)R * a.H; wave += nthr >> 6) {
+    const size_t base = wave * a.d;
+    float x0 = load_as_f32(a.q, a.q_bf16, base + 2 * lane);
+    float x1 = load_as_f32(a.q, a.q_bf16, base + 2 * lane + 1);
+    float am = fmaxf(fabsf(x0), fabsf(x1));
 #pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-  int e = mx_exponent(am);
-  float inv = ldexpf(1.0f, -e);
-  uint32_t c0 = am > 0.f ? enc_e2m1(x0 * inv) : 0u;
-  uint32_t c1 = am > 0.f ? enc_e2m1(x1 * inv) : 0u;
-  a.qmx[(size_t)wave * (a.d / 2) + lane] = (uint8_t)(c0 | (c1 << 4));
-  if ((lane & 15) == 0) a.qsc[(size_t)wave * (a.d / 32) + (lane >> 4)] = (uint8_t)(e + 127);
+    for (int o = 8; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    int e = mx_exponent(am);
+    float inv = ldexpf(1.0f, -e);
+    uint32_t c0 = am > 0.f ? enc_e2m1(x0 * inv) : 0u;
+    uint32_t c1 = am > 0.f ? enc_e2m1(x1 * inv) : 0u;
+    a.qmx[wave * (a.d / 2) + lane] = (uint8_t)(c0 | (c1 << 4));
+    if ((lane & 15) == 0) a.qsc[wave * (a.d / 32) + (lane >> 4)] = (uint8_t)(e + 127);
+  }
+}
+
+// LDS histogram of the scores' first digit, flushed to the query's global
+// histogram (non-empty bins only).
+__device__ __forceinline__ void hist_flush(uint32_t* lh, uint32_t* gh) {
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) {
+    uint32_t c = lh[i];
+    if (c) atomicAdd(gh + i, c);
+  }
 }
 
 // ---------------------------------------------------------------- FP4 scan
-// Workgroup = 4 waves x 64 blocks = 256 consecutive blocks of one query.
-constexpr int kScoreBlocks = 256;
+constexpr int kWaveTiles = 16;             // 16 tiles x 16 blocks per wave and iteration
+constexpr int kIterBlocks = 4 * kWaveTiles * 16;   // 1024 blocks per workgroup iteration
 
+struct KeyTiles {
+  u32x4 v[kWaveTiles];
+  int sc[kWaveTiles];
+};
+
+__device__ __forceinline__ void load_keys(const uint8_t* kc, const uint8_t* ks, int64_t blk0,
+                                          int64_t nv, int g, int li, KeyTiles& kt) {
+#pragma unroll
+  for (int t = 0; t < kWaveTiles; t++) {
+    const int64_t blk = blk0 + t * 16 + li;
+    kt.v[t] = (u32x4){0u, 0u, 0u, 0u};
+    kt.sc[t] = 127;
+    if (blk < nv) {
+      kt.v[t] = __builtin_nontemporal_load((const u32x4*)(kc + blk * 64 + g * 16));
+      kt.sc[t] = ks[blk * 4 + g];
+    }
+  }
+}
+
+__device__ __forceinline__ void score_tiles(const KeyTiles& kt, const i32x8* qa, const int* qs,
+                                            float (*wv)[4], int HT, int64_t blk0, int64_t nv,
+                                            int g, int li, float* out, uint32_t* lh) {
+#pragma unroll
+  for (int t = 0; t < kWaveTiles; t++) {
+    const int64_t blk = blk0 + t * 16 + li;
+    i32x8 kb = {(int)kt.v[t][0], (int)kt.v[t][1], (int)kt.v[t][2], (int)kt.v[t][3], 0, 0, 0, 0};
+    float part = 0.0f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ht++) {
+      if (ht < HT) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb, acc, 4, 4, 0, qs[ht], 0,
+                                                               kt.sc[t]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) part += wv[ht][i] * fmaxf(acc[i], 0.0f);
+      }
+    }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (g == 0 && blk < nv) {
+      out[blk] = part;
+      atomicAdd(&lh[score_key(part) >> 21], 1u);
+    }
+  }
+}
+
+// Workgroup w of a query covers blocks [w * iters * 1024, (w + 1) * iters * 1024).
 __global__ void __launch_bounds__(256) k_score_mx(IndexArgs a) {
+  __shared__ uint32_t lh[kBins];
   const int row = blockIdx.y;
   const int b = row / a.Q;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
-  const int64_t blk0 = (int64_t)blockIdx.x * kScoreBlocks + wave * 64;
-  if (blk0 >= nv) return;
-  const int HT = a.H / 16;
+  const int64_t wg0 = (int64_t)blockIdx.x * a.score_iters * kIterBlocks;
+  if (wg0 >= nv) return;                   // uniform across the workgroup
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = 0u;
+  int iters = (int)((nv - wg0 + kIterBlocks - 1) / kIterBlocks);
+  if (iters > a.score_iters) iters = a.score_iters;
 
-  // A operands: q heads (ht*16 + li), 32 elements of group g
+  const uint8_t* kc = (const uint8_t*)a.codes + (size_t)b * a.cap * 64;
+  const uint8_t* ks = a.kscales + (size_t)b * a.cap * 4;
+  const int64_t wblk = wg0 + wave * (kWaveTiles * 16);
+  KeyTiles k0, k1;
+  load_keys(kc, ks, wblk, nv, g, li, k0);
+  // A operands: q heads (ht*16 + li), elements 32g .. 32g+31; head weights
+  const int HT = a.H / 16;
   i32x8 qa[4];
   int qs[4];
   float wv[4][4];
-  for (int ht = 0; ht < HT; ht++) {
-    const uint8_t* qp = a.qmx + ((size_t)row * a.H + ht * 16 + li) * 64 + g * 16;
-    u32x4 v = *(const u32x4*)qp;
-    qa[ht] = (i32x8){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-    qs[ht] = a.qsc[((size_t)row * a.H + ht * 16 + li) * 4 + g];
 #pragma unroll
-    for (int i = 0; i < 4; i++) wv[ht][i] = a.w[(size_t)row * a.H + ht * 16 + g * 4 + i];
-  }
-  const uint8_t* kc = (const uint8_t*)a.codes + (size_t)b * a.cap * 64;
-  const uint8_t* ks = a.kscales + (size_t)b * a.cap * 4;
+  for (int ht = 0; ht < 4; ht++) {
+    qa[ht] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+    qs[ht] = 127;
 #pragma unroll
-  for (int t = 0; t < 4; t++) {
-    const int64_t blk = blk0 + t * 16 + li;
-    const bool ok = blk < nv;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    int sc = 127;
-    if (ok) {
-      v = *(const u32x4*)(kc + blk * 64 + g * 16);
-      sc = ks[blk * 4 + g];
+    for (int i = 0; i < 4; i++) wv[ht][i] = 0.0f;
+    if (ht < HT) {
+      const uint8_t* qp = a.qmx + ((size_t)row * a.H + ht * 16 + li) * 64 + g * 16;
+      u32x4 v = *(const u32x4*)qp;
+      qa[ht] = (i32x8){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+      qs[ht] = a.qsc[((size_t)row * a.H + ht * 16 + li) * 4 + g];
+#pragma unroll
+      for (int i = 0; i < 4; i++) wv[ht][i] = a.w[(size_t)row * a.H + ht * 16 + g * 4 + i];
     }
-    i32x8 kb = {(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-    float part = 0.0f;
-    for (int ht = 0; ht < HT; ht++) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb, acc, 4, 4, 0, qs[ht], 0, sc);
-#pragma unroll
-      for (int i = 0; i < 4; i++) part += wv[ht][i] * fmaxf(acc[i], 0.0f);
-    }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    if (g == 0 && ok) a.scores[(size_t)row * a.cap + blk] = part;
   }
+  __syncthreads();                         // lh zeroed
+  float* out = a.scores + (size_t)row * a.cap;
+  for (int it = 0; it < iters; it += 2) {
+    const int64_t b0 = wblk + (int64_t)it * kIterBlocks;
+    if (it + 1 < iters) load_keys(kc, ks, b0 + kIterBlocks, nv, g, li, k1);
+    score_tiles(k0, qa, qs, wv, HT, b0, nv, g, li, out, lh);
+    if (it + 1 >= iters) break;
+    if (it + 2 < iters) load_keys(kc, ks, b0 + 2 * kIterBlocks, nv, g, li, k0);
+    score_tiles(k1, qa, qs, wv, HT, b0 + kIterBlocks, nv, g, li, out, lh);
+  }
+  hist_flush(lh, a.hist + (size_t)row * kBins);
 }
 
 // ---------------------------------------------------------------- fp32 scan
 __global__ void __launch_bounds__(256) k_score_f32(IndexArgs a) {
-  extern __shared__ float qsm[];          // [H][d] then w[H]
+  extern __shared__ float qsm[];          // [H][d], w[H], then the histogram
   const int row = blockIdx.y;
   const int b = row / a.Q;
   const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
-  const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t wg0 = (int64_t)blockIdx.x * blockDim.x;
+  if (wg0 >= nv) return;
+  const int64_t blk = wg0 + threadIdx.x;
   float* wsm = qsm + a.H * a.d;
+  uint32_t* lh = (uint32_t*)(wsm + a.H);
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = 0u;
   for (int i = threadIdx.x; i < a.H * a.d; i += blockDim.x)
     qsm[i] = load_as_f32(a.q, a.q_bf16, (size_t)row * a.H * a.d + i);
   for (int i = threadIdx.x; i < a.H; i += blockDim.x) wsm[i] = a.w[(size_t)row * a.H + i];
   __syncthreads();
-  if (blk >= nv) return;
-  const float* kr = (const float*)a.codes + ((size_t)b * a.cap + blk) * a.d;
-  float s = 0.0f;
-  for (int h = 0; h < a.H; h++) {
-    float dot = 0.0f;
-    for (int c = 0; c < a.d; c++) dot += qsm[h * a.d + c] * kr[c];
-    s += wsm[h] * fmaxf(dot, 0.0f);
+  if (blk < nv) {
+    const float* kr = (const float*)a.codes + ((size_t)b * a.cap + blk) * a.d;
+    float s = 0.0f;
+    for (int h = 0; h < a.H; h++) {
+      float dot = 0.0f;
+      for (int c = 0; c < a.d; c++) dot += qsm[h * a.d + c] * kr[c];
+      s += wsm[h] * fmaxf(dot, 0.0f);
+    }
+    a.scores[(size_t)row * a.cap + blk] = s;
+    atomicAdd(&lh[score_key(s) >> 21], 1u);
   }
-  a.scores[(size_t)row * a.cap + blk] = s;
+  hist_flush(lh, a.hist + (size_t)row * kBins);
 }
 
-// ---------------------------------------------------------------- select
-constexpr int kSelThreads = 512;
-constexpr int kBins = 2048;
+// ---------------------------------------------------------------- filter + final select
+constexpr int kFThreads = 256;
 
-// Inclusive block scan of one value per thread (kSelThreads threads).
+// Inclusive block scan of one value per thread.
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -174,116 +278,330 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
   return v + add;
 }
 
-// 64-bit selection key of element i: higher = better (score desc, id asc).
-__device__ __forceinline__ uint64_t sel_key(const float* sc, int64_t i) {
-  float f = sc[i];
-  if (f == 0.0f) f = 0.0f;                 // -0 ranks equal to +0
-  return ((uint64_t)order_key(f) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-}
-
-__global__ void __launch_bounds__(kSelThreads) k_select(IndexArgs a) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t tmp[kSelThreads / 64];
-  __shared__ uint64_t s_prefix, s_mask;
-  __shared__ uint32_t s_need, s_tot;
-  __shared__ int s_done;
-  const int row = blockIdx.x;
-  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
-  const int k = a.k;
-  const int64_t kk = nv < k ? nv : k;
-  const float* sc = a.scores + (size_t)row * a.cap;
-  int32_t* out = a.topk + (size_t)row * k;
-
-  if (kk == nv) {                          // everything visible is selected
-    for (int64_t i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < nv ? (int32_t)i : -1;
-    return;
-  }
-  if (threadIdx.x == 0) {
-    s_prefix = 0;
-    s_mask = 0;
-    s_need = (uint32_t)kk;
-    s_done = 0;
+// Find the bin (scanning from the top) where the cumulative count reaches
+// `need` (1 <= need <= total); writes (bin, count strictly above) to shared
+// memory.  All threads must call it; nb is a multiple of kFThreads.
+__device__ void find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* tmp,
+                         int* s_bin, uint32_t* s_above) {
+  const int per = nb / kFThreads;
+  uint32_t cnt = 0;
+  for (int j = 0; j < per; j++) cnt += h[nb - 1 - (threadIdx.x * per + j)];
+  uint32_t incl = block_incl_scan(cnt, tmp);
+  uint32_t excl = incl - cnt;
+  if (excl < need && incl >= need) {
+    uint32_t above = excl;
+    for (int j = 0; j < per; j++) {
+      int bin = nb - 1 - (threadIdx.x * per + j);
+      if (above + h[bin] >= need) {
+        *s_bin = bin;
+        *s_above = above;
+        break;
+      }
+      above += h[bin];
+    }
   }
   __syncthreads();
+}
 
-  // digits (shift, width) over the 64-bit key, most significant first
-  const int shifts[6] = {53, 42, 32, 21, 10, 0};
-  const int widths[6] = {11, 11, 10, 11, 11, 10};
-  for (int pass = 0; pass < 6; pass++) {
+// Candidates of the final select: the compact buffer, or (when it overflowed)
+// the query's scores filtered by the first digit.
+struct CandSrc {
+  const uint64_t* cand;
+  uint32_t n;
+  const float* sc;
+  int64_t nv;
+  uint32_t b12;                            // key bits 31..10 of the candidates
+  bool compact;
+  __device__ __forceinline__ int64_t size() const { return compact ? (int64_t)n : nv; }
+  __device__ __forceinline__ bool get(int64_t i, uint64_t* key) const {
+    if (compact) {
+      *key = cand[i];
+      return true;
+    }
+    uint32_t k32 = score_key(sc[i]);
+    *key = ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+    return (k32 >> 10) == b12;
+  }
+};
+
+__device__ void final_select(const IndexArgs& a, int row, int64_t nv, int kk, uint32_t b12,
+                             uint32_t* lh, uint32_t* tmp, int32_t* lsort) {
+  __shared__ uint64_t s_prefix, s_mask;
+  __shared__ uint32_t s_need, s_above, s_cnt;
+  __shared__ int s_bin, s_done;
+  int32_t* out = a.topk + (size_t)row * a.k;
+  uint32_t* ctr = a.ctr + (size_t)row * kCtr;
+  const uint32_t n_sel = __hip_atomic_load(ctr + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t n_cand = __hip_atomic_load(ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const CandSrc src{a.cand + (size_t)row * kCandCap, n_cand, a.scores + (size_t)row * a.cap, nv, b12,
+                    n_cand <= (uint32_t)kCandCap};
+  if (threadIdx.x == 0) {
+    s_prefix = (uint64_t)b12 << 42;
+    s_mask = (uint64_t)0x3FFFFF << 42;
+    s_need = (uint32_t)kk - n_sel;
+    s_done = 0;
+    s_cnt = 0;
+  }
+  __syncthreads();
+  const int shifts[4] = {32, 21, 10, 0};
+  const int widths[4] = {10, 11, 11, 10};
+  const int64_t n = src.size();
+  for (int pass = 0; pass < 4; pass++) {
     if (s_done) break;
     const int sh = shifts[pass], wd = widths[pass];
     const uint32_t nb = 1u << wd;
-    for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
+    for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = 0u;
     __syncthreads();
     const uint64_t pm = s_mask, pp = s_prefix;
-    for (int64_t i = threadIdx.x; i < nv; i += blockDim.x) {
-      uint64_t key = sel_key(sc, i);
-      if ((key & pm) == pp) atomicAdd(&hist[(uint32_t)(key >> sh) & (nb - 1)], 1u);
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+      uint64_t key;
+      if (src.get(i, &key) && (key & pm) == pp) atomicAdd(&lh[(uint32_t)(key >> sh) & (nb - 1)], 1u);
     }
     __syncthreads();
-    // suffix counts from the top bin: thread t owns bins nb-1-4t .. nb-4-4t
-    const int per = (int)(nb + kSelThreads - 1) / kSelThreads;   // 4 or 2
-    uint32_t cnt = 0;
-    for (int j = 0; j < per; j++) {
-      int bin = (int)nb - 1 - (threadIdx.x * per + j);
-      if (bin >= 0) cnt += hist[bin];
+    find_bin(lh, (int)nb, s_need, tmp, &s_bin, &s_above);
+    if (threadIdx.x == 0) {
+      uint32_t rem = s_need - s_above;
+      s_prefix = pp | ((uint64_t)s_bin << sh);
+      s_mask = pm | ((uint64_t)(nb - 1) << sh);
+      if (lh[s_bin] == rem) s_done = 1;
+      s_need = rem;
     }
-    uint32_t incl = block_incl_scan(cnt, tmp);
-    uint32_t excl = incl - cnt;
-    const uint32_t need = s_need;
-    if (excl < need && incl >= need) {     // exactly one thread
-      uint32_t above = excl;
-      for (int j = 0; j < per; j++) {
-        int bin = (int)nb - 1 - (threadIdx.x * per + j);
-        uint32_t h = hist[bin];
-        if (above + h >= need) {
-          uint32_t rem = need - above;
-          s_prefix = pp | ((uint64_t)bin << sh);
-          s_mask = pm | ((uint64_t)(nb - 1) << sh);
-          s_need = rem;
-          if (h == rem) s_done = 1;
-          break;
-        }
-        above += h;
+    __syncthreads();
+  }
+  // candidates at or above the threshold join the ids selected by the filter
+  {
+    const uint64_t pm = s_mask, pp = s_prefix;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+      uint64_t key;
+      if (src.get(i, &key) && (key & pm) >= pp) {
+        uint32_t dst = n_sel + atomicAdd(&s_cnt, 1u);
+        if (dst < (uint32_t)kk) out[dst] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
       }
     }
-    __syncthreads();
   }
-  // a fully resolved 64-bit key is unique, so (key & mask) >= prefix selects
-  // exactly kk elements; compact them in ascending id order
-  const uint64_t pm = s_mask, pp = s_prefix;
-  uint32_t base = 0;
-  for (int64_t c0 = 0; c0 < nv; c0 += blockDim.x) {
-    int64_t i = c0 + threadIdx.x;
-    uint32_t f = (i < nv && (sel_key(sc, i) & pm) >= pp) ? 1u : 0u;
-    uint32_t incl = block_incl_scan(f, tmp);
-    if (f && base + incl - 1 < (uint32_t)kk) out[base + incl - 1] = (int32_t)i;
-    if (threadIdx.x == blockDim.x - 1) s_tot = incl;
-    __syncthreads();
-    base += s_tot;
-    __syncthreads();
+  __threadfence_block();
+  __syncthreads();
+  // ascending sort of the kk selected ids (bitonic, in LDS)
+  int np = 1;
+  while (np < kk) np <<= 1;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) lsort[i] = i < kk ? out[i] : 0x7FFFFFFF;
+  __syncthreads();
+  for (int size = 2; size <= np; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < np / 2; i += blockDim.x) {
+        int lo = 2 * i - (i & (stride - 1));
+        int hi = lo + stride;
+        bool up = (lo & size) == 0;
+        int x = lsort[lo], y = lsort[hi];
+        if ((x > y) == up) {
+          lsort[lo] = y;
+          lsort[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
   }
-  for (int64_t i = kk + threadIdx.x; i < k; i += blockDim.x) out[i] = -1;
+  for (int i = threadIdx.x; i < a.k; i += blockDim.x) out[i] = i < kk ? lsort[i] : -1;
+}
+
+// Common head of both filter passes: the query's visible count, its k', and
+// the first-digit threshold bin from the score histogram.
+struct FilterRow {
+  int64_t nv;
+  int kk;
+  uint32_t b1, above1;
+};
+
+__device__ __forceinline__ bool filter_head(const IndexArgs& a, int row, uint32_t* lh,
+                                            uint32_t* tmp, FilterRow* fr) {
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above;
+  fr->nv = n_visible(a.pos[row], a.m, a.cap);
+  fr->kk = (int)(fr->nv < a.k ? fr->nv : a.k);
+  if (fr->kk == fr->nv) return false;
+  const uint32_t* gh = a.hist + (size_t)row * kBins;
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = gh[i];
+  __syncthreads();
+  find_bin(lh, kBins, (uint32_t)fr->kk, tmp, &s_bin, &s_above);
+  fr->b1 = (uint32_t)s_bin;
+  fr->above1 = s_above;
+  return true;
+}
+
+// Appends go to an LDS buffer first (wave-aggregated LDS atomics); the
+// workgroup then reserves its range in the query's global list with a single
+// atomic.  Lanes that find the LDS buffer full append to the global list
+// directly.
+template <typename T>
+struct LdsList {
+  T* buf;
+  uint32_t* count;                         // LDS counter
+  uint32_t cap;
+
+  __device__ __forceinline__ void append(bool flag, T value, uint32_t* gcount, T* gbuf,
+                                         uint32_t gcap) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint64_t mask = __builtin_amdgcn_ballot_w64(flag);
+    if (!mask) return;
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(count, (uint32_t)__builtin_popcountll(mask));
+    base = __shfl(base, 0, 64);
+    uint32_t slot = base + (uint32_t)__builtin_popcountll(mask & below);
+    bool spill = flag && slot >= cap;
+    if (flag && !spill) buf[slot] = value;
+    uint64_t ms = __builtin_amdgcn_ballot_w64(spill);
+    if (!ms) return;
+    uint32_t gb = 0;
+    if (lane == 0) gb = atomicAdd(gcount, (uint32_t)__builtin_popcountll(ms));
+    gb = __shfl(gb, 0, 64);
+    if (spill) {
+      uint32_t gs = gb + (uint32_t)__builtin_popcountll(ms & below);
+      if (gs < gcap) gbuf[gs] = value;
+    }
+  }
+
+  // all threads; copies the buffered entries to the global list
+  __device__ __forceinline__ void flush(uint32_t* gcount, T* gbuf, uint32_t gcap, uint32_t* s_base) {
+    __syncthreads();
+    uint32_t n = *count < cap ? *count : cap;
+    if (threadIdx.x == 0) *s_base = n ? atomicAdd(gcount, n) : 0u;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x)
+      if (*s_base + i < gcap) gbuf[*s_base + i] = buf[i];
+  }
+};
+
+constexpr int kSelLds = 4096;              // >= any query's k': one buffer holds a chunk's share
+constexpr int kCandLds = 1024;
+
+__global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
+  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t tmp[kFThreads / 64];
+  __shared__ int32_t sel_buf[kSelLds];
+  __shared__ uint32_t sel_n, s_base;
+  const int row = blockIdx.y;
+  FilterRow fr;
+  if (!filter_head(a, row, lh, tmp, &fr)) {
+    if (blockIdx.x == 0) {                 // everything visible is selected
+      int32_t* out = a.topk + (size_t)row * a.k;
+      for (int64_t i = threadIdx.x; i < a.k; i += blockDim.x) out[i] = i < fr.nv ? (int32_t)i : -1;
+    }
+    return;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = 0u;
+  if (threadIdx.x == 0) sel_n = 0;
+  __syncthreads();
+  const float* sc = a.scores + (size_t)row * a.cap;
+  int32_t* out = a.topk + (size_t)row * a.k;
+  uint32_t* ctr = a.ctr + (size_t)row * kCtr;
+  LdsList<int32_t> sel{sel_buf, &sel_n, (uint32_t)kSelLds};
+  const int64_t c0 = (int64_t)blockIdx.x * kFilterChunk;
+  const int64_t c1 = c0 + kFilterChunk < fr.nv ? c0 + kFilterChunk : fr.nv;
+  for (int64_t base = c0; base < c1; base += blockDim.x) {
+    const int64_t i = base + threadIdx.x;
+    const bool in = i < c1;
+    const uint32_t k32 = in ? score_key(sc[i]) : 0u;
+    const uint32_t d1 = k32 >> 21;
+    sel.append(in && d1 > fr.b1, (int32_t)i, ctr + 0, out, (uint32_t)fr.kk);
+    if (in && d1 == fr.b1) atomicAdd(&lh[(k32 >> 10) & (kBins - 1)], 1u);
+  }
+  sel.flush(ctr + 0, out, (uint32_t)fr.kk, &s_base);
+  hist_flush(lh, a.hist2 + (size_t)row * kBins);
+}
+
+__global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
+  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t tmp[kFThreads / 64];
+  __shared__ int32_t lsort[kSelLds];       // selected ids during the scan, sort buffer after
+  __shared__ uint64_t cand_buf[kCandLds];
+  __shared__ int s_bin, s_last;
+  __shared__ uint32_t s_above, sel_n, cand_n, s_base;
+  const int row = blockIdx.y;
+  FilterRow fr;
+  if (!filter_head(a, row, lh, tmp, &fr)) return;
+  __syncthreads();
+  const uint32_t* gh2 = a.hist2 + (size_t)row * kBins;
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = gh2[i];
+  if (threadIdx.x == 0) {
+    sel_n = 0;
+    cand_n = 0;
+  }
+  __syncthreads();
+  find_bin(lh, kBins, (uint32_t)fr.kk - fr.above1, tmp, &s_bin, &s_above);
+  const uint32_t b12 = (fr.b1 << 11) | (uint32_t)s_bin;   // key bits 31..10
+  const float* sc = a.scores + (size_t)row * a.cap;
+  int32_t* out = a.topk + (size_t)row * a.k;
+  uint32_t* ctr = a.ctr + (size_t)row * kCtr;
+  uint64_t* cand = a.cand + (size_t)row * kCandCap;
+  LdsList<int32_t> sel{lsort, &sel_n, (uint32_t)kSelLds};
+  LdsList<uint64_t> cnd{cand_buf, &cand_n, (uint32_t)kCandLds};
+  const int64_t c0 = (int64_t)blockIdx.x * kFilterChunk;
+  const int64_t c1 = c0 + kFilterChunk < fr.nv ? c0 + kFilterChunk : fr.nv;
+  for (int64_t base = c0; base < c1; base += blockDim.x) {
+    const int64_t i = base + threadIdx.x;
+    const bool in = i < c1;
+    const uint32_t k32 = in ? score_key(sc[i]) : 0u;
+    const bool same1 = in && (k32 >> 21) == fr.b1;
+    const uint32_t d12 = k32 >> 10;
+    sel.append(same1 && d12 > b12, (int32_t)i, ctr + 0, out, (uint32_t)fr.kk);
+    cnd.append(same1 && d12 == b12, ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i),
+               ctr + 1, cand, (uint32_t)kCandCap);
+  }
+  sel.flush(ctr + 0, out, (uint32_t)fr.kk, &s_base);
+  cnd.flush(ctr + 1, cand, (uint32_t)kCandCap, &s_base);
+  // the last workgroup of this query finishes the selection
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t prev = atomicAdd(ctr + 2, 1u);
+    s_last = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  final_select(a, row, fr.nv, fr.kk, b12, lh, tmp, lsort);
 }
 
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st) {
   const int R = a.B * a.Q;
   if (R == 0) return hipSuccess;
-  if (a.key_mx) {
-    const int waves = R * a.H;
-    hipLaunchKernelGGL(k_quant_q, dim3((waves + 3) / 4), dim3(256), 0, st, a);
+  {
+    size_t work = (size_t)R * kBins;
+    if (a.key_mx) {
+      size_t qthreads = (size_t)R * a.H * 64;
+      if (qthreads > work) work = qthreads;
+    }
+    size_t blocks = (work + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_prep, dim3((unsigned)blocks), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)((a.cap + kScoreBlocks - 1) / kScoreBlocks), R);
-    hipLaunchKernelGGL(k_score_mx, grid, dim3(256), 0, st, a);
+  }
+  if (a.key_mx) {
+    // about 512 workgroups in all (two per CU), each walking score_iters
+    // iterations of 1024 blocks: fewer histogram flushes per query
+    IndexArgs b = a;
+    const int64_t it_total = (a.cap + kIterBlocks - 1) / kIterBlocks;
+    int64_t iters = (it_total * R + 511) / 512;
+    if (iters < 1) iters = 1;
+    if (iters > it_total) iters = it_total;
+    b.score_iters = (int)iters;
+    dim3 grid((unsigned)((it_total + iters - 1) / iters), R);
+    hipLaunchKernelGGL(k_score_mx, grid, dim3(256), 0, st, b);
   } else {
     dim3 grid((unsigned)((a.cap + 255) / 256), R);
-    size_t smem = sizeof(float) * ((size_t)a.H * a.d + a.H);
+    size_t smem = sizeof(float) * ((size_t)a.H * a.d + a.H) + sizeof(uint32_t) * kBins;
     hipLaunchKernelGGL(k_score_f32, grid, dim3(256), smem, st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_select, dim3(R), dim3(kSelThreads), 0, st, a);
+  dim3 fgrid((unsigned)((a.cap + kFilterChunk - 1) / kFilterChunk), R);
+  hipLaunchKernelGGL(k_filter1, fgrid, dim3(kFThreads), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_filter2, fgrid, dim3(kFThreads), 0, st, a);
   return hipGetLastError();
 }
 

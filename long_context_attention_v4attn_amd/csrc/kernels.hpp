@@ -39,11 +39,16 @@ struct IndexArgs {
   int d;
   const int64_t* pos;        // [R]
   int B, Q, H, m, k;
+  int score_iters;           // 1024-block iterations per scan workgroup
   int32_t* topk;             // [R][k]
   // workspace regions
   uint8_t* qmx;              // [R][H][d/2]
   uint8_t* qsc;              // [R][H][d/32]
   float* scores;             // [R][cap]
+  uint32_t* hist;            // [R][2048] first-digit histogram (key bits 31..21)
+  uint32_t* hist2;           // [R][2048] second digit (key bits 20..10) within the first
+  uint32_t* ctr;             // [R][4] selected / candidate / finished-workgroup counters
+  uint64_t* cand;            // [R][16384] candidate keys (score key : inverted id)
 };
 size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx);
 void index_carve(IndexArgs& a, void* ws);
@@ -75,8 +80,9 @@ struct AttendArgs {
   int fp8;                   // 1 = FP8 MFMA path, 0 = fp32 VALU path
   int f32_heads;             // heads per workgroup on the fp32 path
   int n_split, split_size;   // entry-list split (fixed by the per-query shape)
-  float* part_o;             // [R][n_split][H][D]
-  float* part_ml;            // [R][n_split][H][2]
+  int part_bf16;             // split partials stored in bf16 (FP8 path) or fp32
+  void* part_o;              // [R][n_split][H][D] O / l
+  float* part_ml;            // [R][n_split][H][2] (max, denominator)
 };
 void attend_plan(AttendArgs& a, int64_t n_entries_max);
 size_t attend_workspace_bytes(const AttendArgs& a);
