@@ -121,7 +121,9 @@ typedef struct {
  *   m                  1, 2, 4, ..., 128;  T and t0 multiples of m; t0 >= 0
  *   out_kind, out      V4A_OUT_KV + v4a_kv* | V4A_OUT_IDX + v4a_idx* (host);
  *                      rows (t0/m + j) mod cap, j < T/m, of every sequence
- *                      are written; nothing else is touched.
+ *                      are written; nothing else is touched.  When T/m > cap
+ *                      only the last cap blocks are written (the ring keeps
+ *                      the newest entries).
  * Supported: d <= 1024; KV out: d == d_nope + d_rope, FP8 needs d_nope%32==0;
  * IDX out: d == out->d, MXFP4 needs d%32 == 0.
  */

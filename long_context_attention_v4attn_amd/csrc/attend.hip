@@ -722,24 +722,30 @@ __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
   const int sb = (q4 >> 6) / nht;                      // dim slice * 4 + dim block
   const int head = hgrp * 64 + ht * 16 + (ln & 15);
   const int d0 = sb * 16 + (ln >> 4) * 4;
-  const float* ml = a.part_ml + ((int64_t)row * a.n_split * a.H) * 2;
+  // (m, l) of every split for this head: independent loads, issued together
+  const f32x2* ml = (const f32x2*)a.part_ml + (int64_t)row * a.n_split * a.H + head;
   const float z2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
   float M = z2;
-  for (int s = 0; s < a.n_split; s++) M = fmaxf(M, ml[((int64_t)s * a.H + head) * 2]);
+#pragma unroll 8
+  for (int s = 0; s < a.n_split; s++) M = fmaxf(M, ml[(int64_t)s * a.H][0]);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  float den = (M == -INFINITY || z2 == -INFINITY) ? 0.f : exp2f(z2 - M);
-  const uint16_t* po = (const uint16_t*)a.part_o + part_block(a, row, 0, hgrp) + j;
-  const int64_t sstride = (int64_t)a.H * D;
-  for (int s = 0; s < a.n_split; s++) {
-    const float m = ml[((int64_t)s * a.H + head) * 2];
-    if (m == -INFINITY) continue;
-    const float w = ml[((int64_t)s * a.H + head) * 2 + 1] * exp2f(m - M);
-    den += w;
-    const u32x2 v = *(const u32x2*)(po + s * sstride);
-    acc[0] += w * bf16_bits_to_f32(v[0] & 0xFFFFu);
-    acc[1] += w * bf16_bits_to_f32(v[0] >> 16);
-    acc[2] += w * bf16_bits_to_f32(v[1] & 0xFFFFu);
-    acc[3] += w * bf16_bits_to_f32(v[1] >> 16);
+  float den = 0.f;
+  if (M != -INFINITY) {
+    den = z2 == -INFINITY ? 0.f : exp2f(z2 - M);
+    const uint16_t* po = (const uint16_t*)a.part_o + part_block(a, row, 0, hgrp) + j;
+    const int64_t sstride = (int64_t)a.H * D;
+    // an empty split has m = -inf, hence weight 0, and zero partials
+#pragma unroll 4
+    for (int s = 0; s < a.n_split; s++) {
+      const f32x2 v_ml = ml[(int64_t)s * a.H];
+      const u32x2 v = *(const u32x2*)(po + s * sstride);
+      const float w = v_ml[1] * exp2f(v_ml[0] - M);
+      den += w;
+      acc[0] += w * bf16_bits_to_f32(v[0] & 0xFFFFu);
+      acc[1] += w * bf16_bits_to_f32(v[0] >> 16);
+      acc[2] += w * bf16_bits_to_f32(v[1] & 0xFFFFu);
+      acc[3] += w * bf16_bits_to_f32(v[1] >> 16);
+    }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   const int64_t oi = ((int64_t)row * a.H + head) * D + d0;

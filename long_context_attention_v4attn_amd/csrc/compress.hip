@@ -37,6 +37,10 @@ __global__ void __launch_bounds__(kCompThreads) k_compress(CompressArgs a) {
   const int d = a.d;
   const bool overlap = a.kv_prev != nullptr;
   const int64_t gblk = a.t0 / m + j;       // global block index
+  // a call that produces more than cap entries keeps the last cap of them:
+  // an earlier block whose ring row a later block of this call also writes
+  // is skipped (concurrent writes to one row would race)
+  if ((int64_t)(a.T / m) - j > a.cap) return;
   const bool has_prev = overlap && gblk > 0;
   const int64_t rbase = ((int64_t)b * a.T + (int64_t)j * m) * d;   // row m*j of this call
 

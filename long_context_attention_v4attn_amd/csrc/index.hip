@@ -5,7 +5,7 @@
 // [Notes §9] the indexer's QK path runs in FP4 (keys and queries MXFP4), and
 // the selector ranks fp32 scores.
 //
-// Pipeline of one v4attn_index_topk call (four launches):
+// Pipeline of one v4attn_index_topk call (five launches):
 //   k_prep       query heads -> MXFP4 (e2m1 codes + e8m0 scale per 32); zero
 //                the per-query histogram and counters.
 //   k_score_mx   FP4 scan: one v_mfma_scale_f32_16x16x128_f8f6f4 per
@@ -19,17 +19,20 @@
 //                workgroup histograms the top 11 bits of its scores'
 //                order-preserving keys in LDS and flushes once (global atomics).
 //   k_score_f32  fp32 VALU variant for unquantised keys (same histogram).
-//   k_filter1    per query, many workgroups: the histogram gives the bin b1
-//                (key bits 31..21) that holds the k-th largest score; ids
-//                above b1 are selected outright (wave-aggregated atomics);
-//                ids in b1 are histogrammed on key bits 20..10.
-//   k_filter2    same split: that second histogram gives the bin b2; ids in
-//                b1 and above b2 are selected, ids in (b1, b2) become
-//                candidates.  The last workgroup of the query to finish
-//                resolves the candidates exactly (radix select on the 64-bit
-//                key = score key : inverted id, so ties go to the lower id),
-//                then sorts the k selected ids ascending in LDS and pads with
-//                -1.  The output is deterministic.
+//   k_filter1    per query, many workgroups (4096 scores each): the
+//                histogram gives the bin b1 (key bits 31..21) that holds the
+//                k-th largest score; ids in b1 are histogrammed on bits 20..10.
+//   k_filter2    same split: the second histogram gives the bin b2; each
+//                workgroup counts its ids above (b1, b2) and appends the ids
+//                in (b1, b2) as candidates.
+//   k_emit       same split: every workgroup resolves the exact threshold T
+//                among the (few) candidates (radix select on the 64-bit key =
+//                score key : inverted id, so ties go to the lower id), then
+//                writes every id of its chunk whose key is >= T at the
+//                chunk's offset plus its rank within the chunk: the k ids
+//                come out ascending with no sort; the tail is -1.  No
+//                workgroup waits for another, and the output is
+//                deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,17 +42,22 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kBins = 2048;                // first radix digit: key bits 31..21
 constexpr int kCandCap = 16384;            // candidate slots per query
-constexpr int kFilterChunk = 8192;         // scores per filter workgroup
-constexpr int kCtr = 4;                    // counters per query
+constexpr int kFThreads = 256;
+constexpr int kPer = 16;                   // consecutive scores per filter thread
+constexpr int kFilterChunk = kFThreads * kPer;   // scores per filter workgroup
+constexpr int kCtr = 8;                    // counters per query
+__host__ __device__ inline int64_t score_ld(int64_t cap) { return (cap + 63) / 64 * 64; }
+__host__ __device__ inline int64_t n_chunks(int64_t cap) { return (cap + kFilterChunk - 1) / kFilterChunk; }
 
 size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx) {
   const size_t R = (size_t)B * Q;
   size_t n = 0;
   if (key_mx) n += align256(R * H * (d / 2)) + align256(R * H * (d / 32));
-  n += align256(R * (size_t)cap * sizeof(float));
+  n += align256(R * (size_t)score_ld(cap) * sizeof(float));
   n += 2 * align256(R * kBins * sizeof(uint32_t));
   n += align256(R * kCtr * sizeof(uint32_t));
   n += align256(R * kCandCap * sizeof(uint64_t));
+  n += align256(R * (size_t)n_chunks(cap) * sizeof(uint32_t));
   return n;
 }
 
@@ -64,8 +72,9 @@ void index_carve(IndexArgs& a, void* ws) {
     a.qsc = (uint8_t*)p;
     p += align256(R * a.H * (a.d / 32));
   }
+  a.sc_ld = score_ld(a.cap);
   a.scores = (float*)p;
-  p += align256(R * (size_t)a.cap * sizeof(float));
+  p += align256(R * (size_t)a.sc_ld * sizeof(float));
   a.hist = (uint32_t*)p;
   p += align256(R * kBins * sizeof(uint32_t));
   a.hist2 = (uint32_t*)p;
@@ -73,6 +82,8 @@ void index_carve(IndexArgs& a, void* ws) {
   a.ctr = (uint32_t*)p;
   p += align256(R * kCtr * sizeof(uint32_t));
   a.cand = (uint64_t*)p;
+  p += align256(R * kCandCap * sizeof(uint64_t));
+  a.chunk = (uint32_t*)p;
 }
 
 __device__ __forceinline__ int64_t n_visible(int64_t p, int m, int64_t cap) {
@@ -217,7 +228,7 @@ __global__ void __launch_bounds__(256) k_score_mx(IndexArgs a) {
     }
   }
   __syncthreads();                         // lh zeroed
-  float* out = a.scores + (size_t)row * a.cap;
+  float* out = a.scores + (size_t)row * a.sc_ld;
   for (int it = 0; it < iters; it += 2) {
     const int64_t b0 = wblk + (int64_t)it * kIterBlocks;
     if (it + 1 < iters) load_keys(kc, ks, b0 + kIterBlocks, nv, g, li, k1);
@@ -253,14 +264,13 @@ __global__ void __launch_bounds__(256) k_score_f32(IndexArgs a) {
       for (int c = 0; c < a.d; c++) dot += qsm[h * a.d + c] * kr[c];
       s += wsm[h] * fmaxf(dot, 0.0f);
     }
-    a.scores[(size_t)row * a.cap + blk] = s;
+    a.scores[(size_t)row * a.sc_ld + blk] = s;
     atomicAdd(&lh[score_key(s) >> 21], 1u);
   }
   hist_flush(lh, a.hist + (size_t)row * kBins);
 }
 
-// ---------------------------------------------------------------- filter + final select
-constexpr int kFThreads = 256;
+// ---------------------------------------------------------------- filter + select
 
 // Inclusive block scan of one value per thread.
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
@@ -303,8 +313,126 @@ __device__ void find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* tmp
   __syncthreads();
 }
 
-// Candidates of the final select: the compact buffer, or (when it overflowed)
-// the query's scores filtered by the first digit.
+// The 64-bit selection key of id i: score key above, inverted id below, so
+// that of two equal scores the lower id ranks higher.
+__device__ __forceinline__ uint64_t sel_key(uint32_t k32, int64_t i) {
+  return ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+// This thread's kPer consecutive scores of filter chunk `chunk` as keys; the
+// loads are issued together (the score rows are padded to 64 floats, and a
+// thread whose group starts past nv reads its row's first group instead).
+// Returns the number of the group's ids below nv.
+__device__ __forceinline__ int load_group(const IndexArgs& a, int row, int64_t nv, int chunk,
+                                          uint32_t* k32, int64_t* i0) {
+  const int64_t g0 = (int64_t)chunk * kFilterChunk + threadIdx.x * kPer;
+  *i0 = g0;
+  const int64_t rem = nv - g0;
+  const int n_in = rem <= 0 ? 0 : (rem >= kPer ? kPer : (int)rem);
+  const float* sc = a.scores + (size_t)row * a.sc_ld + (n_in ? g0 : 0);
+  f32x4 v[kPer / 4];
+#pragma unroll
+  for (int j = 0; j < kPer / 4; j++) v[j] = *(const f32x4*)(sc + 4 * j);
+#pragma unroll
+  for (int j = 0; j < kPer; j++) k32[j] = score_key(v[j / 4][j % 4]);
+  return n_in;
+}
+
+// Common head of the filter kernels: the query's visible count, its k', and
+// the first-digit threshold bin from the score histogram.
+struct FilterRow {
+  int64_t nv;
+  int kk;
+  uint32_t b1, above1;
+};
+
+__device__ __forceinline__ bool filter_head(const IndexArgs& a, int row, uint32_t* lh,
+                                            uint32_t* tmp, FilterRow* fr) {
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above;
+  fr->nv = n_visible(a.pos[row], a.m, a.cap);
+  fr->kk = (int)(fr->nv < a.k ? fr->nv : a.k);
+  if (fr->kk == fr->nv) return false;
+  if ((int64_t)blockIdx.x * kFilterChunk >= fr->nv) return false;
+  const uint32_t* gh = a.hist + (size_t)row * kBins;
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = gh[i];
+  __syncthreads();
+  find_bin(lh, kBins, (uint32_t)fr->kk, tmp, &s_bin, &s_above);
+  fr->b1 = (uint32_t)s_bin;
+  fr->above1 = s_above;
+  return true;
+}
+
+__global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
+  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t tmp[kFThreads / 64];
+  const int row = blockIdx.y;
+  FilterRow fr;
+  if (!filter_head(a, row, lh, tmp, &fr)) {
+    const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
+    if (blockIdx.x == 0 && nv <= a.k) {    // everything visible is selected
+      int32_t* out = a.topk + (size_t)row * a.k;
+      for (int64_t i = threadIdx.x; i < a.k; i += blockDim.x) out[i] = i < nv ? (int32_t)i : -1;
+    }
+    return;
+  }
+  uint32_t k32[kPer];
+  int64_t i0;
+  const int n_in = load_group(a, row, fr.nv, blockIdx.x, k32, &i0);
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; j++)
+    if (j < n_in && (k32[j] >> 21) == fr.b1) atomicAdd(&lh[(k32[j] >> 10) & (kBins - 1)], 1u);
+  hist_flush(lh, a.hist2 + (size_t)row * kBins);
+}
+
+// Candidate appends go to an LDS buffer first (wave-aggregated LDS atomics);
+// the workgroup then reserves its range in the query's global list with a
+// single atomic.  Lanes that find the LDS buffer full append to the global
+// list directly.
+constexpr int kCandLds = 1024;
+
+struct CandList {
+  uint64_t* buf;
+  uint32_t* count;                         // LDS counter
+
+  __device__ __forceinline__ void append(bool flag, uint64_t value, uint32_t* gcount,
+                                         uint64_t* gbuf) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint64_t mask = __builtin_amdgcn_ballot_w64(flag);
+    if (!mask) return;
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(count, (uint32_t)__builtin_popcountll(mask));
+    base = __shfl(base, 0, 64);
+    uint32_t slot = base + (uint32_t)__builtin_popcountll(mask & below);
+    bool spill = flag && slot >= (uint32_t)kCandLds;
+    if (flag && !spill) buf[slot] = value;
+    uint64_t ms = __builtin_amdgcn_ballot_w64(spill);
+    if (!ms) return;
+    uint32_t gb = 0;
+    if (lane == 0) gb = atomicAdd(gcount, (uint32_t)__builtin_popcountll(ms));
+    gb = __shfl(gb, 0, 64);
+    if (spill) {
+      uint32_t gs = gb + (uint32_t)__builtin_popcountll(ms & below);
+      if (gs < (uint32_t)kCandCap) gbuf[gs] = value;
+    }
+  }
+
+  // all threads; copies the buffered entries to the global list
+  __device__ __forceinline__ void flush(uint32_t* gcount, uint64_t* gbuf, uint32_t* s_base) {
+    __syncthreads();
+    uint32_t n = *count < (uint32_t)kCandLds ? *count : (uint32_t)kCandLds;
+    if (threadIdx.x == 0) *s_base = n ? atomicAdd(gcount, n) : 0u;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x)
+      if (*s_base + i < (uint32_t)kCandCap) gbuf[*s_base + i] = buf[i];
+  }
+};
+
+// Candidates of the threshold search: the compact list, or (when it
+// overflowed) the query's scores filtered by the first two digits.
 struct CandSrc {
   const uint64_t* cand;
   uint32_t n;
@@ -319,30 +447,40 @@ struct CandSrc {
       return true;
     }
     uint32_t k32 = score_key(sc[i]);
-    *key = ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+    *key = sel_key(k32, i);
     return (k32 >> 10) == b12;
   }
 };
 
-__device__ void final_select(const IndexArgs& a, int row, int64_t nv, int kk, uint32_t b12,
-                             uint32_t* lh, uint32_t* tmp, int32_t* lsort) {
+// Sum of one value per thread over the workgroup.
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* tmp) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int w = 0; w < kFThreads / 64; w++) t += tmp[w];
+  __syncthreads();
+  return t;
+}
+
+// The exact 64-bit threshold T: the need-th largest key among the
+// candidates (radix select on the bits below the candidates' common 22-bit
+// prefix).  Exactly `need` candidates have keys >= T.
+__device__ uint64_t resolve_threshold(const CandSrc& src, uint32_t need, uint32_t* lh,
+                                      uint32_t* tmp) {
   __shared__ uint64_t s_prefix, s_mask;
-  __shared__ uint32_t s_need, s_above, s_cnt;
+  __shared__ uint32_t s_need, s_above;
   __shared__ int s_bin, s_done;
-  int32_t* out = a.topk + (size_t)row * a.k;
-  uint32_t* ctr = a.ctr + (size_t)row * kCtr;
-  const uint32_t n_sel = __hip_atomic_load(ctr + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t n_cand = __hip_atomic_load(ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const CandSrc src{a.cand + (size_t)row * kCandCap, n_cand, a.scores + (size_t)row * a.cap, nv, b12,
-                    n_cand <= (uint32_t)kCandCap};
   if (threadIdx.x == 0) {
-    s_prefix = (uint64_t)b12 << 42;
+    s_prefix = (uint64_t)src.b12 << 42;
     s_mask = (uint64_t)0x3FFFFF << 42;
-    s_need = (uint32_t)kk - n_sel;
+    s_need = need;
     s_done = 0;
-    s_cnt = 0;
   }
   __syncthreads();
+  // remaining digits: score key bits 9..0, then the inverted id
   const int shifts[4] = {32, 21, 10, 0};
   const int widths[4] = {10, 11, 11, 10};
   const int64_t n = src.size();
@@ -360,208 +498,120 @@ __device__ void final_select(const IndexArgs& a, int row, int64_t nv, int kk, ui
     __syncthreads();
     find_bin(lh, (int)nb, s_need, tmp, &s_bin, &s_above);
     if (threadIdx.x == 0) {
-      uint32_t rem = s_need - s_above;
+      const uint32_t rem = s_need - s_above;
       s_prefix = pp | ((uint64_t)s_bin << sh);
       s_mask = pm | ((uint64_t)(nb - 1) << sh);
+      // the whole bin is taken: the prefix with the remaining bits zero is
+      // a threshold every key of the bin meets
       if (lh[s_bin] == rem) s_done = 1;
       s_need = rem;
     }
     __syncthreads();
   }
-  // candidates at or above the threshold join the ids selected by the filter
-  {
-    const uint64_t pm = s_mask, pp = s_prefix;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-      uint64_t key;
-      if (src.get(i, &key) && (key & pm) >= pp) {
-        uint32_t dst = n_sel + atomicAdd(&s_cnt, 1u);
-        if (dst < (uint32_t)kk) out[dst] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
-      }
-    }
-  }
-  __threadfence_block();
+  const uint64_t T = s_prefix;
   __syncthreads();
-  // ascending sort of the kk selected ids (bitonic, in LDS)
-  int np = 1;
-  while (np < kk) np <<= 1;
-  for (int i = threadIdx.x; i < np; i += blockDim.x) lsort[i] = i < kk ? out[i] : 0x7FFFFFFF;
-  __syncthreads();
-  for (int size = 2; size <= np; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < np / 2; i += blockDim.x) {
-        int lo = 2 * i - (i & (stride - 1));
-        int hi = lo + stride;
-        bool up = (lo & size) == 0;
-        int x = lsort[lo], y = lsort[hi];
-        if ((x > y) == up) {
-          lsort[lo] = y;
-          lsort[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = threadIdx.x; i < a.k; i += blockDim.x) out[i] = i < kk ? lsort[i] : -1;
-}
-
-// Common head of both filter passes: the query's visible count, its k', and
-// the first-digit threshold bin from the score histogram.
-struct FilterRow {
-  int64_t nv;
-  int kk;
-  uint32_t b1, above1;
-};
-
-__device__ __forceinline__ bool filter_head(const IndexArgs& a, int row, uint32_t* lh,
-                                            uint32_t* tmp, FilterRow* fr) {
-  __shared__ int s_bin;
-  __shared__ uint32_t s_above;
-  fr->nv = n_visible(a.pos[row], a.m, a.cap);
-  fr->kk = (int)(fr->nv < a.k ? fr->nv : a.k);
-  if (fr->kk == fr->nv) return false;
-  const uint32_t* gh = a.hist + (size_t)row * kBins;
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = gh[i];
-  __syncthreads();
-  find_bin(lh, kBins, (uint32_t)fr->kk, tmp, &s_bin, &s_above);
-  fr->b1 = (uint32_t)s_bin;
-  fr->above1 = s_above;
-  return true;
-}
-
-// Appends go to an LDS buffer first (wave-aggregated LDS atomics); the
-// workgroup then reserves its range in the query's global list with a single
-// atomic.  Lanes that find the LDS buffer full append to the global list
-// directly.
-template <typename T>
-struct LdsList {
-  T* buf;
-  uint32_t* count;                         // LDS counter
-  uint32_t cap;
-
-  __device__ __forceinline__ void append(bool flag, T value, uint32_t* gcount, T* gbuf,
-                                         uint32_t gcap) {
-    const int lane = threadIdx.x & 63;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    uint64_t mask = __builtin_amdgcn_ballot_w64(flag);
-    if (!mask) return;
-    uint32_t base = 0;
-    if (lane == 0) base = atomicAdd(count, (uint32_t)__builtin_popcountll(mask));
-    base = __shfl(base, 0, 64);
-    uint32_t slot = base + (uint32_t)__builtin_popcountll(mask & below);
-    bool spill = flag && slot >= cap;
-    if (flag && !spill) buf[slot] = value;
-    uint64_t ms = __builtin_amdgcn_ballot_w64(spill);
-    if (!ms) return;
-    uint32_t gb = 0;
-    if (lane == 0) gb = atomicAdd(gcount, (uint32_t)__builtin_popcountll(ms));
-    gb = __shfl(gb, 0, 64);
-    if (spill) {
-      uint32_t gs = gb + (uint32_t)__builtin_popcountll(ms & below);
-      if (gs < gcap) gbuf[gs] = value;
-    }
-  }
-
-  // all threads; copies the buffered entries to the global list
-  __device__ __forceinline__ void flush(uint32_t* gcount, T* gbuf, uint32_t gcap, uint32_t* s_base) {
-    __syncthreads();
-    uint32_t n = *count < cap ? *count : cap;
-    if (threadIdx.x == 0) *s_base = n ? atomicAdd(gcount, n) : 0u;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x)
-      if (*s_base + i < gcap) gbuf[*s_base + i] = buf[i];
-  }
-};
-
-constexpr int kSelLds = 4096;              // >= any query's k': one buffer holds a chunk's share
-constexpr int kCandLds = 1024;
-
-__global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
-  __shared__ uint32_t lh[kBins];
-  __shared__ uint32_t tmp[kFThreads / 64];
-  __shared__ int32_t sel_buf[kSelLds];
-  __shared__ uint32_t sel_n, s_base;
-  const int row = blockIdx.y;
-  FilterRow fr;
-  if (!filter_head(a, row, lh, tmp, &fr)) {
-    if (blockIdx.x == 0) {                 // everything visible is selected
-      int32_t* out = a.topk + (size_t)row * a.k;
-      for (int64_t i = threadIdx.x; i < a.k; i += blockDim.x) out[i] = i < fr.nv ? (int32_t)i : -1;
-    }
-    return;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = 0u;
-  if (threadIdx.x == 0) sel_n = 0;
-  __syncthreads();
-  const float* sc = a.scores + (size_t)row * a.cap;
-  int32_t* out = a.topk + (size_t)row * a.k;
-  uint32_t* ctr = a.ctr + (size_t)row * kCtr;
-  LdsList<int32_t> sel{sel_buf, &sel_n, (uint32_t)kSelLds};
-  const int64_t c0 = (int64_t)blockIdx.x * kFilterChunk;
-  const int64_t c1 = c0 + kFilterChunk < fr.nv ? c0 + kFilterChunk : fr.nv;
-  for (int64_t base = c0; base < c1; base += blockDim.x) {
-    const int64_t i = base + threadIdx.x;
-    const bool in = i < c1;
-    const uint32_t k32 = in ? score_key(sc[i]) : 0u;
-    const uint32_t d1 = k32 >> 21;
-    sel.append(in && d1 > fr.b1, (int32_t)i, ctr + 0, out, (uint32_t)fr.kk);
-    if (in && d1 == fr.b1) atomicAdd(&lh[(k32 >> 10) & (kBins - 1)], 1u);
-  }
-  sel.flush(ctr + 0, out, (uint32_t)fr.kk, &s_base);
-  hist_flush(lh, a.hist2 + (size_t)row * kBins);
+  return T;
 }
 
 __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   __shared__ uint32_t lh[kBins];
   __shared__ uint32_t tmp[kFThreads / 64];
-  __shared__ int32_t lsort[kSelLds];       // selected ids during the scan, sort buffer after
   __shared__ uint64_t cand_buf[kCandLds];
-  __shared__ int s_bin, s_last;
-  __shared__ uint32_t s_above, sel_n, cand_n, s_base;
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above, cand_n, s_base;
   const int row = blockIdx.y;
   FilterRow fr;
   if (!filter_head(a, row, lh, tmp, &fr)) return;
-  __syncthreads();
+  uint32_t k32[kPer];
+  int64_t i0;
+  const int n_in = load_group(a, row, fr.nv, blockIdx.x, k32, &i0);
   const uint32_t* gh2 = a.hist2 + (size_t)row * kBins;
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = gh2[i];
-  if (threadIdx.x == 0) {
-    sel_n = 0;
-    cand_n = 0;
-  }
+  if (threadIdx.x == 0) cand_n = 0;
   __syncthreads();
   find_bin(lh, kBins, (uint32_t)fr.kk - fr.above1, tmp, &s_bin, &s_above);
   const uint32_t b12 = (fr.b1 << 11) | (uint32_t)s_bin;   // key bits 31..10
-  const float* sc = a.scores + (size_t)row * a.cap;
-  int32_t* out = a.topk + (size_t)row * a.k;
   uint32_t* ctr = a.ctr + (size_t)row * kCtr;
   uint64_t* cand = a.cand + (size_t)row * kCandCap;
-  LdsList<int32_t> sel{lsort, &sel_n, (uint32_t)kSelLds};
-  LdsList<uint64_t> cnd{cand_buf, &cand_n, (uint32_t)kCandLds};
-  const int64_t c0 = (int64_t)blockIdx.x * kFilterChunk;
-  const int64_t c1 = c0 + kFilterChunk < fr.nv ? c0 + kFilterChunk : fr.nv;
-  for (int64_t base = c0; base < c1; base += blockDim.x) {
-    const int64_t i = base + threadIdx.x;
-    const bool in = i < c1;
-    const uint32_t k32 = in ? score_key(sc[i]) : 0u;
-    const bool same1 = in && (k32 >> 21) == fr.b1;
-    const uint32_t d12 = k32 >> 10;
-    sel.append(same1 && d12 > b12, (int32_t)i, ctr + 0, out, (uint32_t)fr.kk);
-    cnd.append(same1 && d12 == b12, ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i),
-               ctr + 1, cand, (uint32_t)kCandCap);
+  CandList cnd{cand_buf, &cand_n};
+  uint32_t above = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const bool in = j < n_in;
+    const uint32_t d12 = k32[j] >> 10;
+    above += (in && d12 > b12) ? 1u : 0u;
+    cnd.append(in && d12 == b12, sel_key(k32[j], i0 + j), ctr + 0, cand);
   }
-  sel.flush(ctr + 0, out, (uint32_t)fr.kk, &s_base);
-  cnd.flush(ctr + 1, cand, (uint32_t)kCandCap, &s_base);
-  // the last workgroup of this query finishes the selection
-  __threadfence();
-  __syncthreads();
+  cnd.flush(ctr + 0, cand, &s_base);
+  // the chunk's count of ids above the candidates' bin; the threshold digits
+  above = block_sum(above, tmp);
   if (threadIdx.x == 0) {
-    uint32_t prev = atomicAdd(ctr + 2, 1u);
-    s_last = prev == gridDim.x - 1;
+    a.chunk[(size_t)row * n_chunks(a.cap) + blockIdx.x] = above;
+    if (blockIdx.x == 0) {
+      ctr[2] = b12;
+      ctr[3] = (uint32_t)fr.kk - fr.above1 - s_above;   // candidates to take
+    }
   }
+}
+
+constexpr int kEmitCand = 4096;            // candidates resolved from LDS
+
+// Every workgroup of a query resolves the threshold T from the candidates
+// (few: they share the top 22 key bits with the k-th largest score), finds
+// its chunk's output offset, and writes its chunk's selected ids in order.
+__global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
+  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t tmp[kFThreads / 64];
+  __shared__ uint64_t cl[kEmitCand];
+  const int row = blockIdx.y;
+  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
+  const int kk = (int)(nv < a.k ? nv : a.k);
+  if (kk == nv) return;                    // written by k_filter1
+  int32_t* out = a.topk + (size_t)row * a.k;
+  if (blockIdx.x == 0)
+    for (int i = kk + threadIdx.x; i < a.k; i += blockDim.x) out[i] = -1;
+  if ((int64_t)blockIdx.x * kFilterChunk >= nv) return;
+  uint32_t k32[kPer];
+  int64_t i0;
+  const int n_in = load_group(a, row, nv, blockIdx.x, k32, &i0);
+  const uint32_t* ctr = a.ctr + (size_t)row * kCtr;
+  const uint32_t n_cand = ctr[0], b12 = ctr[2], need = ctr[3];
+  const uint64_t* gc = a.cand + (size_t)row * kCandCap;
+  const bool in_lds = n_cand <= (uint32_t)kEmitCand;
+  if (in_lds)
+    for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) cl[i] = gc[i];
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  final_select(a, row, fr.nv, fr.kk, b12, lh, tmp, lsort);
+  const CandSrc src{in_lds ? cl : gc, n_cand, a.scores + (size_t)row * a.sc_ld, nv, b12,
+                    n_cand <= (uint32_t)kCandCap};
+  const uint64_t T = resolve_threshold(src, need, lh, tmp);
+  // offset of this chunk: ids above the bin in earlier chunks, plus the
+  // candidates >= T with lower ids
+  const int64_t c0 = (int64_t)blockIdx.x * kFilterChunk;
+  uint32_t before = 0;
+  const uint32_t* cc = a.chunk + (size_t)row * n_chunks(a.cap);
+  for (int c = threadIdx.x; c < (int)blockIdx.x; c += blockDim.x) before += cc[c];
+  const int64_t n = src.size();
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    uint64_t key;
+    if (src.get(i, &key) && key >= T) {
+      const int64_t id = (int64_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+      before += id < c0 ? 1u : 0u;
+    }
+  }
+  const uint32_t base = block_sum(before, tmp);
+  uint32_t sel = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; j++)
+    if (j < n_in && sel_key(k32[j], i0 + j) >= T) sel |= 1u << j;
+  const uint32_t cnt = (uint32_t)__builtin_popcount(sel);
+  uint32_t pos = base + block_incl_scan(cnt, tmp) - cnt;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    if ((sel >> j) & 1u) {
+      if (pos < (uint32_t)kk) out[pos] = (int32_t)(i0 + j);
+      pos++;
+    }
+  }
 }
 
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st) {
@@ -597,11 +647,14 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 fgrid((unsigned)((a.cap + kFilterChunk - 1) / kFilterChunk), R);
+  dim3 fgrid((unsigned)n_chunks(a.cap), R);
   hipLaunchKernelGGL(k_filter1, fgrid, dim3(kFThreads), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_filter2, fgrid, dim3(kFThreads), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_emit, fgrid, dim3(kFThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -44,11 +44,13 @@ struct IndexArgs {
   // workspace regions
   uint8_t* qmx;              // [R][H][d/2]
   uint8_t* qsc;              // [R][H][d/32]
-  float* scores;             // [R][cap]
+  float* scores;             // [R][sc_ld]
+  int64_t sc_ld;             // score row stride (cap rounded up to 64)
   uint32_t* hist;            // [R][2048] first-digit histogram (key bits 31..21)
   uint32_t* hist2;           // [R][2048] second digit (key bits 20..10) within the first
-  uint32_t* ctr;             // [R][4] selected / candidate / finished-workgroup counters
+  uint32_t* ctr;             // [R][8] candidate / finished-workgroup counters, threshold
   uint64_t* cand;            // [R][16384] candidate keys (score key : inverted id)
+  uint32_t* chunk;           // [R][n_chunks] selected per filter chunk, then its output offset
 };
 size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx);
 void index_carve(IndexArgs& a, void* ws);
