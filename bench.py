@@ -14,9 +14,13 @@ Inputs are synthetic and seeded (long_context_attention_v4attn_amd.synth),
 uploaded once and quantised to the cache formats on the GPU by the library
 (v4attn_compress with m = 1).  `--replicas` address-distinct copies of every
 cache are cycled so that no step re-reads data another recent step left in the
-256 MB Infinity Cache.  Each call is captured in a HIP graph per replica; the
-timed loop replays them with HIP events between calls (torch's current stream,
-which is the stream the library launches on).
+256 MB Infinity Cache.  Each layer of a step is one HIP graph per replica; the
+timed loop replays K steps with a HIP event between the two layers of every
+step (torch's current stream, which is the stream the library launches on).
+After the timed loop, each call's graphs are replayed back to back for a
+per-call breakdown, and the dominant kernel of each call is timed live with
+HIP events that the library records immediately around that kernel
+(v4attn_time_next_kernel); the roofline is reported for the slowest of them.
 
 The `cpu_baseline` leg times the CPU oracle (test infrastructure) on a bounded
 sample of the same workload: 4 CSA queries over one 1M-context cache row and
@@ -24,6 +28,8 @@ sample of the same workload: 4 CSA queries over one 1M-context cache row and
 """
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -61,6 +67,48 @@ def algorithmic_flops(c_csa, c_hca):
     csa = (c_csa["k"] + c_csa["n_win"]) * c_csa["H"] * D * 4
     hca = (c_hca["ctx"] // c_hca["m"] + c_hca["n_win"]) * c_hca["H"] * D * 4
     return dict(index=idx, csa_attend=csa, hca_attend=hca)
+
+
+def kernel_bytes(c_csa, c_hca):
+    """Algorithmic bytes per launch of each call's dominant kernel: the index
+    scan reads every visible key (68 B per block), q^I and w; the attention
+    kernel reads every entry it attends (580 B), q and (CSA) the top-k ids.
+    The outputs are written by the split merge, not counted here."""
+    entry = c_csa["d_nope"] + 2 * c_csa["d_rope"] + 4
+    key = c_csa["d_I"] // 2 + c_csa["d_I"] // 32
+    D = c_csa["d_nope"] + c_csa["d_rope"]
+    q = c_csa["H"] * D * 2
+    n_blocks = c_csa["ctx"] // c_csa["m"]
+    return {
+        "k_score_mx [index_topk]": c_csa["B"] * (n_blocks * key + c_csa["H_I"] * c_csa["d_I"] * 2
+                                                  + c_csa["H_I"] * 4),
+        "k_attend_fp8 [csa_attend]": c_csa["B"] * ((c_csa["k"] + c_csa["n_win"]) * entry + q
+                                                    + c_csa["k"] * 4),
+        "k_attend_fp8 [hca_attend]": c_hca["B"] * ((c_hca["ctx"] // c_hca["m"] + c_hca["n_win"])
+                                                    * entry + q),
+    }
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
+    None when the summary does not exist or was taken on a different kernel
+    source (its recorded sha256 differs from the current file's)."""
+    path = os.path.join(ROOT, "profiles", "attend_hca_decode_1m_counters.md")
+    src = os.path.join(ROOT, "long_context_attention_v4attn_amd", "csrc", "attend.hip")
+    if not kernel.startswith("k_attend_fp8") or not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    rec = {}
+    for line in open(path):
+        if line.startswith("traffic:"):
+            for kv in line[len("traffic:"):].split():
+                k_, _, v_ = kv.partition("=")
+                rec[k_] = v_
+    tag = "hca" if "hca" in kernel else "csa"
+    if rec.get("source_sha256") != sha or f"{tag}_bytes" not in rec:
+        return None
+    return int(rec[f"{tag}_bytes"])
 
 
 # ---------------------------------------------------------------- GPU setup
@@ -255,69 +303,123 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    # one graph per replica and layer: the CSA layer (index_topk + csa_attend)
+    # and the HCA layer (hca_attend); also per-call graphs for the breakdown
     if not args.no_graph:
-        graphs = []
         cap_stream = torch.cuda.Stream()
-        for cs in calls:
-            gl = []
-            for f in cs:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=cap_stream):
+
+        def capture(fns):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_stream):
+                for f in fns:
                     f()
-                gl.append(g)
-            graphs.append(gl)
+            return g.replay
+
+        layer = [(capture(cs[:2]), capture(cs[2:])) for cs in calls]
+        single = [[capture([f]) for f in cs] for cs in calls]
         torch.cuda.synchronize()
-        runners = [[g.replay for g in gl] for gl in graphs]
     else:
-        runners = calls
-    R = len(runners)
+        layer = [((lambda cs=cs: (cs[0](), cs[1]())), cs[2]) for cs in calls]
+        single = calls
+    R = len(layer)
 
     for s in range(args.warmup):
-        for f in runners[s % R]:
-            f()
+        layer[s % R][0]()
+        layer[s % R][1]()
     torch.cuda.synchronize()
 
+    # ---- the timed region: K steps (CSA layer, then HCA layer), events
+    # between the two layers of every step
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
-        e = ev[s]
-        fs = runners[s % R]
-        e[0].record(stream)
-        fs[0]()
-        e[1].record(stream)
-        fs[1]()
-        e[2].record(stream)
-        fs[2]()
-        e[3].record(stream)
+        ev[s][0].record(stream)
+        layer[s % R][0]()
+        ev[s][1].record(stream)
+        layer[s % R][1]()
+    ev[K][0].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_parts = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in ev]) * 1e-3  # s
-    t_idx, t_csa_att, t_hca = t_parts.mean(axis=0)
-    t_csa = t_idx + t_csa_att
-    ms_per_step = wall / K * 1e3
+    t_csa = sum(ev[s][0].elapsed_time(ev[s][1]) for s in range(K)) / K * 1e-3     # s
+    t_hca = sum(ev[s][1].elapsed_time(ev[s + 1][0]) for s in range(K)) / K * 1e-3
+    t_gpu = ev[0][0].elapsed_time(ev[K][0]) / K * 1e-3
+    ms_per_step = max(wall / K, t_gpu) * 1e3
     pair_qps = 1.0 / (t_csa / cc["B"] + t_hca / ch["B"])
+
+    # ---- per-call breakdown (each call's graphs replayed back to back)
+    def per_call(i, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(n):
+            single[s % R][i]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    n_call = max(20, K // 4)
+    t_idx, t_csa_att, t_hca_call = (per_call(i, n_call) for i in range(3))
+
+    # ---- dominant kernels, timed live with HIP events recorded by the
+    # library immediately around each kernel (eager launches)
+    hip = ctypes.CDLL("libamdhip64.so")
+
+    def kernel_time(i, n):
+        evs = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e)
+        torch.cuda.synchronize()
+        for s in range(n):
+            v4.v4attn_time_next_kernel(evs[2 * s].value, evs[2 * s + 1].value)
+            calls[s % R][i]()
+        torch.cuda.synchronize()
+        tot = 0.0
+        ms = ctypes.c_float()
+        for s in range(n):
+            if hip.hipEventElapsedTime(ctypes.byref(ms), evs[2 * s], evs[2 * s + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            tot += ms.value
+        for e in evs:
+            hip.hipEventDestroy(e)
+        return tot / n * 1e-3
+
+    n_k = max(20, K // 8)
+    kern = {
+        "k_score_mx [index_topk]": kernel_time(0, n_k),
+        "k_attend_fp8 [csa_attend]": kernel_time(1, n_k),
+        "k_attend_fp8 [hca_attend]": kernel_time(2, n_k),
+    }
 
     ab = algorithmic_bytes(cc, ch)
     af = algorithmic_flops(cc, ch)
+    kb = kernel_bytes(cc, ch)
     bytes_step = cc["B"] * (ab["index"] + ab["csa_attend"]) + ch["B"] * ab["hca_attend"]
-    gpu_step = t_parts.sum(axis=1).mean()
     calls_meta = {
         "index_topk": dict(t_us=t_idx * 1e6, bytes=cc["B"] * ab["index"], flops=cc["B"] * af["index"]),
         "csa_attend": dict(t_us=t_csa_att * 1e6, bytes=cc["B"] * ab["csa_attend"],
                            flops=cc["B"] * af["csa_attend"]),
-        "hca_attend": dict(t_us=t_hca * 1e6, bytes=ch["B"] * ab["hca_attend"],
+        "hca_attend": dict(t_us=t_hca_call * 1e6, bytes=ch["B"] * ab["hca_attend"],
                            flops=ch["B"] * af["hca_attend"]),
     }
     for k_, m_ in calls_meta.items():
         m_["GBps"] = m_["bytes"] / (m_["t_us"] * 1e-6) / 1e9
         m_["hbm_frac"] = m_["GBps"] / HBM_PEAK_GBPS
-    dom = max(calls_meta, key=lambda k_: calls_meta[k_]["t_us"])
-    dm = calls_meta[dom]
-    roofline = {"bound": "hbm", "achieved": round(dm["GBps"], 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(dm["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": dom}
+    kernels_meta = {}
+    for name, t in kern.items():
+        b_ = kb[name]
+        kernels_meta[name] = {"t_us": round(t * 1e6, 3), "bytes": b_,
+                              "GBps": round(b_ / t / 1e9, 1)}
+    dom = max(kern, key=lambda n_: kern[n_])
+    dm = kernels_meta[dom]
+    roofline = {"bound": "hbm", "achieved": dm["GBps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dm["GBps"] / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(dom), "kernel": dom, "t_us": dm["t_us"],
+                "algorithmic_bytes": dm["bytes"]}
 
     result = {
         "metric": "CSA+HCA decode queries/sec at 1M ctx; achieved HBM GB/s vs peak",
@@ -330,16 +432,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8/fp4 storage, bf16 MFMA, fp32 accumulate",
+        "dtype": "bf16",
+        "arith": "attention: bf16 MFMA on exactly widened FP8 entries, fp32 accumulate and softmax; "
+                 "indexer: MXFP4 MFMA, fp32 scores",
         "data": "synthetic",
         "config": {"workload": "csa_decode_1m (B=4, 262144 blocks, top-2048, window 128) + "
                                "hca_decode_1m (B=16, 8192 entries, window 128); 64 heads x D=512",
                    "global_batch": cc["B"] + ch["B"], "seq_len": cc["ctx"], "parallelism": "none (1 GPU)"},
-        "achieved_GBps_step": round(bytes_step / gpu_step / 1e9, 1),
-        "hbm_frac_step": round(bytes_step / gpu_step / 1e9 / HBM_PEAK_GBPS, 4),
+        "achieved_GBps_step": round(bytes_step / (t_csa + t_hca) / 1e9, 1),
+        "hbm_frac_step": round(bytes_step / (t_csa + t_hca) / 1e9 / HBM_PEAK_GBPS, 4),
+        "t_csa_layer_us": round(t_csa * 1e6, 3),
+        "t_hca_layer_us": round(t_hca * 1e6, 3),
         "csa_qps": round(cc["B"] / t_csa, 1),
         "hca_qps": round(ch["B"] / t_hca, 1),
         "calls": {k_: {kk: round(vv, 3) for kk, vv in m_.items()} for k_, m_ in calls_meta.items()},
+        "kernels": kernels_meta,
         "replicas": R,
         "graph": not args.no_graph,
         "roofline": roofline,

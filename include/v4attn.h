@@ -222,6 +222,18 @@ const char *v4attn_status_str(v4a_status s);
 /* hipError_t behind the calling thread's last V4A_ERR_HIP (0 if none). */
 int32_t v4attn_last_hip_error(void);
 
+/*
+ * Kernel timing (measurement helper).  The calling thread's next call of
+ * v4attn_index_topk, v4attn_csa_attend or v4attn_hca_attend records `start`
+ * and `stop` (hipEvent_t handles created by the caller) on the call's stream
+ * immediately before and after its dominant kernel -- the index scan, resp.
+ * the attention kernel (not the split merge) -- so hipEventElapsedTime gives
+ * that kernel's duration.  The events are consumed by that one call; NULL
+ * clears them.  Calls that fail validation consume nothing.  Meant for eager
+ * launches, not for stream capture.
+ */
+void v4attn_time_next_kernel(void *start, void *stop);
+
 /* Library version: major * 10000 + minor * 100 + patch. */
 int32_t v4attn_version(void);
 

@@ -58,6 +58,7 @@ _SIGS = {
     "v4attn_status_str": (ctypes.c_char_p, [_I32]),
     "v4attn_last_hip_error": (_I32, []),
     "v4attn_version": (_I32, []),
+    "v4attn_time_next_kernel": (None, [_P, _P]),
 }
 
 
@@ -76,6 +77,12 @@ def load():
         fn.argtypes = args
     _LIB = lib
     return lib
+
+
+def v4attn_time_next_kernel(start, stop):
+    """Record the raw hipEvent_t handles `start` / `stop` (ints) around the
+    dominant kernel of this thread's next index / attend call."""
+    load().v4attn_time_next_kernel(ctypes.c_void_p(start), ctypes.c_void_p(stop))
 
 
 def v4attn_status_str(status):

@@ -14,6 +14,16 @@ using namespace v4a;
 namespace {
 
 thread_local int32_t g_last_hip = 0;
+// events for the calling thread's next index / attend call (kernel timing)
+thread_local KernelEvents g_time_next = {nullptr, nullptr};
+
+// Takes the pending timing events, if any (one call consumes them).
+const KernelEvents* take_events(KernelEvents* slot) {
+  if (!g_time_next.start || !g_time_next.stop) return nullptr;
+  *slot = g_time_next;
+  g_time_next = {nullptr, nullptr};
+  return slot;
+}
 
 v4a_status hip_status(hipError_t e) {
   if (e == hipSuccess) return V4A_OK;
@@ -88,7 +98,8 @@ v4a_status run_attend(AttendArgs& a, int64_t n_entries_max, void* ws, size_t ws_
     if (!ws || ws_bytes < need) return V4A_ERR_WORKSPACE;
     attend_carve(a, ws);
   }
-  return hip_status(launch_attend(a, (hipStream_t)stream));
+  KernelEvents ev;
+  return hip_status(launch_attend(a, (hipStream_t)stream, take_events(&ev)));
 }
 
 }  // namespace
@@ -188,7 +199,8 @@ v4a_status v4attn_index_topk(const void* q_idx, int32_t q_dtype, const float* w,
   if (!ws || ws_bytes < need) return V4A_ERR_WORKSPACE;
   index_carve(a, ws);
   if (B == 0 || Q == 0) return V4A_OK;
-  return hip_status(launch_index_topk(a, (hipStream_t)stream));
+  KernelEvents ev;
+  return hip_status(launch_index_topk(a, (hipStream_t)stream, take_events(&ev)));
 }
 
 v4a_status v4attn_csa_attend(const void* q, int32_t q_dtype, const v4a_kv* comp,
@@ -260,6 +272,10 @@ const char* v4attn_status_str(v4a_status s) {
 }
 
 int32_t v4attn_last_hip_error(void) { return g_last_hip; }
+
+void v4attn_time_next_kernel(void* start, void* stop) {
+  g_time_next = {(hipEvent_t)start, (hipEvent_t)stop};
+}
 
 int32_t v4attn_version(void) { return 100; }
 

@@ -85,17 +85,14 @@ constexpr int kNope = 448;                   // FP8 dims
 constexpr int kRope = 64;                    // BF16 dims
 constexpr int kRowBytes = kNope + 2 * kRope; // 576 staged bytes per entry
 constexpr int kRowStride = 592;              // padded LDS row (bank spread)
-constexpr int kChunks = kRowBytes / 16;      // 36 x 16-byte chunks per entry
-constexpr int kTileChunks = kTile * kChunks; // 1152
 constexpr int kThreads = 512;               // 8 waves: 4 head groups x 2 halves
-constexpr int kChunksPerThread = (kTileChunks + kThreads - 1) / kThreads;  // 3
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;             // lazy max-rescale threshold (log2 units)
 
 struct __align__(16) Fp8Tile {
   uint8_t rows[kTile * kRowStride];
-  float scale[kTile];
-  int valid[kTile];
+  float scale[kTile];                      // FP8 scale of the entry (0 if absent)
+  float bias[kTile];                       // 0, or -inf for an absent entry
 };
 
 // Widen 8 e4m3 codes (two dwords) to 8 bf16 (exact).
@@ -134,12 +131,14 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint8_t* p) {
   return o;
 }
 
-// One tile's staging registers: 5 x 16 B chunks per thread plus, for the
-// first 32 threads, one entry's scale and presence flag.
+// Staging: the 16 threads t = 16e .. 16e+15 move entry e of the tile, so a
+// thread resolves one entry's row per tile.  Thread q = t & 15 moves the
+// 16-byte chunks q, 16 + q and 32 + (q & 3) of the 576-byte staged row
+// (chunks 0..27: FP8 codes, 28..35: BF16 RoPE dims) and the entry's scale.
 struct Stage {
-  u32x4 r[kChunksPerThread];
+  u32x4 r[3];
   float sc;
-  int ok;                                  // bit j: chunk j present; bit 31: the scale's entry
+  int ok;                                  // the entry is present
 };
 
 // Source of every entry of this workgroup's split, resolved once into LDS
@@ -157,59 +156,45 @@ __device__ __forceinline__ void resolve_sources(const AttendArgs& a, const RowEn
   }
 }
 
-// Every load is issued unconditionally (absent entries read row 0 of the
-// sequence's compressed cache, which always exists, and are zeroed), so the
-// number of loads per tile is fixed and the compiler can keep the later
-// tiles' loads in flight when it waits for an earlier one.
+// Every load is issued unconditionally (an absent entry reads row 0 of the
+// sequence's compressed cache, which always exists, and is zeroed when
+// stored), so the number of loads per tile is fixed and the compiler can keep
+// later tiles' loads in flight when it waits for an earlier one.
 __device__ __forceinline__ void stage_load(const AttendArgs& a, const int* src, int b, int tile_l0,
                                            int n_local, Stage& st) {
   const int t = threadIdx.x;
-  int ok = 0;
-#pragma unroll
-  for (int j = 0; j < kChunksPerThread; j++) {
-    const int c = t + j * kThreads;
-    const int e = c / kChunks, part = c % kChunks;
-    const int le = tile_l0 + e;
-    const int sraw = src[le < kMaxSplit ? le : kMaxSplit - 1];   // always in bounds
-    const int s = (c < kTileChunks && le < n_local) ? sraw : -1;
-    const bool is_win = s < -1;
-    const int64_t rr = s >= 0 ? (int64_t)s : (is_win ? (int64_t)(-2 - s) : 0);
-    const int64_t rowi = (int64_t)b * (is_win ? a.w_cap : a.c_cap) + rr;
-    const uint8_t* nope = is_win ? a.w_nope : a.c_nope;
-    const uint8_t* rope = (const uint8_t*)(is_win ? a.w_rope : a.c_rope);
-    const bool in_nope = part < kNope / 16;
-    const uint8_t* gp = in_nope ? nope + rowi * kNope + part * 16
-                                : rope + rowi * (2 * kRope) + (part - kNope / 16) * 16;
-    // the value is masked when stored to LDS, not here: using it now would
-    // make the compiler wait for this load immediately
-    st.r[j] = __builtin_nontemporal_load((const u32x4*)gp);   // streamed once: not kept in L2
-    ok |= (s != -1 ? 1 : 0) << j;
-  }
-  const int le = tile_l0 + (t & (kTile - 1));
-  const int sraw = src[le < kMaxSplit ? le : kMaxSplit - 1];
+  const int q = t & 15;
+  const int le = tile_l0 + (t >> 4);
+  const int sraw = src[le < kMaxSplit ? le : kMaxSplit - 1];   // always in bounds
   const int s = le < n_local ? sraw : -1;
   const bool is_win = s < -1;
   const int64_t rr = s >= 0 ? (int64_t)s : (is_win ? (int64_t)(-2 - s) : 0);
-  st.sc = (is_win ? a.w_scale : a.c_scale)[(int64_t)b * (is_win ? a.w_cap : a.c_cap) + rr];
-  st.ok = ok | (s != -1 ? (1 << 31) : 0);
+  const int64_t rowi = (int64_t)b * (is_win ? a.w_cap : a.c_cap) + rr;
+  const uint8_t* nope = (is_win ? a.w_nope : a.c_nope) + rowi * kNope;
+  const uint8_t* rope = (const uint8_t*)(is_win ? a.w_rope : a.c_rope) + rowi * (2 * kRope);
+  // the values are masked when stored to LDS, not here: using them now would
+  // make the compiler wait for these loads immediately
+  st.r[0] = __builtin_nontemporal_load((const u32x4*)(nope + q * 16));
+  st.r[1] = __builtin_nontemporal_load(
+      (const u32x4*)(q < 12 ? nope + (16 + q) * 16 : rope + (q - 12) * 16));
+  st.r[2] = __builtin_nontemporal_load((const u32x4*)(rope + (4 + (q & 3)) * 16));
+  st.sc = (is_win ? a.w_scale : a.c_scale)[rowi];
+  st.ok = s != -1;
 }
 
 __device__ __forceinline__ void stage_store(Fp8Tile* tl, const Stage& st) {
   const int t = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < kChunksPerThread; j++) {
-    int c = t + j * kThreads;
-    if (c < kTileChunks) {
-      int e = c / kChunks, part = c % kChunks;
-      const u32x4 v = (st.ok >> j) & 1 ? st.r[j] : (u32x4){0u, 0u, 0u, 0u};
-      *(u32x4*)(tl->rows + e * kRowStride + part * 16) = v;
-    }
-  }
-  if (t < kTile) {
-    const bool ok = (st.ok >> 31) & 1;
-    tl->scale[t] = ok ? st.sc : 0.0f;
-    tl->valid[t] = ok;
-  }
+  const int e = t >> 4, q = t & 15;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  uint8_t* dst = tl->rows + e * kRowStride;
+  *(u32x4*)(dst + q * 16) = st.ok ? st.r[0] : z;
+  *(u32x4*)(dst + 256 + q * 16) = st.ok ? st.r[1] : z;
+  // chunks 32..35 and the scale: the entry's threads write identical values
+  // (every value is used unconditionally, so the compiler cannot sink its
+  // load into a branch and wait for it there)
+  *(u32x4*)(dst + 512 + (q & 3) * 16) = st.ok ? st.r[2] : z;
+  tl->scale[e] = st.ok ? st.sc : 0.0f;
+  tl->bias[e] = st.ok ? 0.0f : -INFINITY;
 }
 
 // Work split of the 8 waves of a workgroup (64 heads of one query):
@@ -220,13 +205,20 @@ __device__ __forceinline__ void stage_store(Fp8Tile* tl, const Stage& st) {
 //  * PV by output-dim slice: wave w owns dims 64w .. 64w+63 for all 64 heads,
 //    so each V^T fragment is widened from FP8 once and feeds four MFMAs (one
 //    per head group); P^T of the four head groups comes through LDS.
+// The three phases are software-pipelined over tiles with one barrier per
+// step: step k computes the partial logits of tile k, the softmax of tile
+// k-1 and the PV product of tile k-2, and stages tile k+1.  Four tile
+// buffers and double-buffered exchange / P buffers keep every LDS region of
+// a step either read or written, never both.
+constexpr int kBufs = 4;
+
 struct __align__(16) Shared {
-  float xc[4][2][64][8];                   // partial logits [hg][half][lane][both row blocks]
-  u32x4 pB[4][64];                         // P^T operand (RoPE dims) [hg][lane]
-  u32x4 pnB[4][64];                        // (P * scale)^T operand (FP8 dims)
-  float alpha[64];                         // per-head rescale of this tile (1 = none)
+  float xc[2][4][2][64][8];                // partial logits [k%2][hg][half][lane][both row blocks]
+  u32x4 pB[2][4][64];                      // P^T operand (RoPE dims) [k%2][hg][lane]
+  u32x4 pnB[2][4][64];                     // (P * scale)^T operand (FP8 dims)
+  float alpha[2][64];                      // per-head rescale of the tile (1 = none)
+  int flag[2][4];                          // head group rescaled this tile
   float fin[64];                           // per-head output factor (epilogue)
-  int any_rescale;
 };
 
 // Softmax state of a logits wave (its lane's head); both halves agree.
@@ -235,11 +227,11 @@ struct SoftState {
   float l_run;                             // lane-partial denominator
 };
 
-__device__ __forceinline__ void qk_softmax(const Fp8Tile* tl, Shared* sh, const bf16x8* qf,
-                                           SoftState& S, float c2, int hg, int half, int g,
-                                           int li) {
+// Partial S^T = K Q^T of tile `tl` over this wave's half of the dims, both
+// row blocks, scaled per entry (FP8 part) -> xc slot of this wave.
+__device__ __forceinline__ void qk_partial(const Fp8Tile* tl, float (*xc)[2][64][8],
+                                           const bf16x8* qf, int hg, int half, int g, int li) {
   const int lane = threadIdx.x & 63;
-  // ---- partial S^T = K Q^T over this half's dims, both row blocks
   float part[8];
 #pragma unroll
   for (int rb = 0; rb < 2; rb++) {
@@ -261,23 +253,35 @@ __device__ __forceinline__ void qk_softmax(const Fp8Tile* tl, Shared* sh, const 
                                                      0, 0, 0);
       }
     }
+    const f32x4 sc = *(const f32x4*)&tl->scale[rb * 16 + g * 4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) part[rb * 4 + i] = sn[i] * tl->scale[rb * 16 + g * 4 + i] + sr[i];
+    for (int i = 0; i < 4; i++) part[rb * 4 + i] = sn[i] * sc[i] + sr[i];
   }
-  f32x4* mine = (f32x4*)sh->xc[hg][half][lane];
+  f32x4* mine = (f32x4*)xc[hg][half][lane];
   mine[0] = (f32x4){part[0], part[1], part[2], part[3]};
   mine[1] = (f32x4){part[4], part[5], part[6], part[7]};
-  __syncthreads();
-  const f32x4* oth = (const f32x4*)sh->xc[hg][half ^ 1][lane];
-  const f32x4 o0 = oth[0], o1 = oth[1];
-  float s2[8], scl[8];
+}
+
+// Online softmax of a tile whose partial logits (both halves) are in xc.
+// Half-0 waves publish P^T, (P * scale)^T, the rescale factors and the
+// head group's rescale flag.
+__device__ __forceinline__ void softmax_tile(const Fp8Tile* tl, const float (*xc)[2][64][8],
+                                             Shared* sh, int buf, SoftState& S, float c2, int hg,
+                                             int half, int g, int li) {
+  const int lane = threadIdx.x & 63;
+  const f32x4* p0 = (const f32x4*)xc[hg][0][lane];
+  const f32x4* p1 = (const f32x4*)xc[hg][1][lane];
+  const f32x4 a0 = p0[0], a1 = p0[1], b0 = p1[0], b1 = p1[1];
+  // entries of lane group g: 4g .. 4g+3 and 16+4g .. 16+4g+3
+  const f32x4 sc0 = *(const f32x4*)&tl->scale[g * 4], sc1 = *(const f32x4*)&tl->scale[16 + g * 4];
+  const f32x4 bi0 = *(const f32x4*)&tl->bias[g * 4], bi1 = *(const f32x4*)&tl->bias[16 + g * 4];
+  float s2[8];
   float tmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const int e = (i >> 2) * 16 + g * 4 + (i & 3);
-    const float v = (part[i] + (i < 4 ? o0[i] : o1[i - 4])) * c2;
-    s2[i] = tl->valid[e] ? v : -INFINITY;
-    scl[i] = tl->scale[e];
+    // the same sum in both halves: half 0's partial first
+    const float v = i < 4 ? a0[i] + b0[i] : a1[i - 4] + b1[i - 4];
+    s2[i] = v * c2 + (i < 4 ? bi0[i] : bi1[i - 4]);
     tmax = fmaxf(tmax, s2[i]);
   }
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
@@ -288,7 +292,7 @@ __device__ __forceinline__ void qk_softmax(const Fp8Tile* tl, Shared* sh, const 
   const bool need = (S.m_run == -INFINITY) ? (tmax > -INFINITY) : (tmax > S.m_run + kRescale);
   float alpha = 1.0f;
   if (need) {
-    alpha = (S.m_run == -INFINITY) ? 0.0f : exp2f(S.m_run - tmax);
+    alpha = (S.m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(S.m_run - tmax);
     S.l_run *= alpha;
     S.m_run = tmax;
   }
@@ -296,28 +300,31 @@ __device__ __forceinline__ void qk_softmax(const Fp8Tile* tl, Shared* sh, const 
   float pv[8], pn[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    float p = exp2f(s2[i] - m_use);
+    // 2^(x) for x <= kRescale; an absent entry gives 2^-inf = 0
+    const float p = __builtin_amdgcn_exp2f(s2[i] - m_use);
     S.l_run += p;
     pv[i] = p;
-    pn[i] = p * scl[i];
+    pn[i] = p * (i < 4 ? sc0[i] : sc1[i - 4]);
   }
   if (half == 0) {
-    sh->pB[hg][lane] = __builtin_bit_cast(u32x4, pack8(pv));
-    sh->pnB[hg][lane] = __builtin_bit_cast(u32x4, pack8(pn));
-    if (g == 0) sh->alpha[hg * 16 + li] = alpha;
-    if (__builtin_amdgcn_ballot_w64(need) && lane == 0) sh->any_rescale = 1;
+    sh->pB[buf][hg][lane] = __builtin_bit_cast(u32x4, pack8(pv));
+    sh->pnB[buf][hg][lane] = __builtin_bit_cast(u32x4, pack8(pn));
+    if (g == 0) sh->alpha[buf][hg * 16 + li] = alpha;
+    const int any = __builtin_amdgcn_ballot_w64(need) != 0;
+    if (lane == 0) sh->flag[buf][hg] = any;
   }
 }
 
 // PV for wave `ds` (dims 64ds .. 64ds+63), all four head groups.  acc[db][ht]:
 // O^T block of dims 64ds + 16db .. +16 x heads 16ht .. +16.
-__device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f32x4 (*acc)[4],
-                                         int ds, int g, int li) {
+__device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, int buf,
+                                         f32x4 (*acc)[4], int ds, int g, int li) {
   const int lane = threadIdx.x & 63;
-  if (sh->any_rescale) {
+  const int* fl = sh->flag[buf];
+  if (fl[0] | fl[1] | fl[2] | fl[3]) {
 #pragma unroll
     for (int ht = 0; ht < 4; ht++) {
-      const float al = sh->alpha[ht * 16 + li];
+      const float al = sh->alpha[buf][ht * 16 + li];
 #pragma unroll
       for (int db = 0; db < 4; db++) acc[db][ht] *= al;
     }
@@ -328,7 +335,7 @@ __device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f3
   if (ds < 7) {
     bf16x8 pnB[4];
 #pragma unroll
-    for (int ht = 0; ht < 4; ht++) pnB[ht] = __builtin_bit_cast(bf16x8, sh->pnB[ht][lane]);
+    for (int ht = 0; ht < 4; ht++) pnB[ht] = __builtin_bit_cast(bf16x8, sh->pnB[buf][ht][lane]);
     const int kk8 = s >> 1;
     const int ent8 = (kk8 < 4) ? (g * 4 + kk8) : (16 + g * 4 + kk8 - 4);
     const uint8_t* vb8 = tl->rows + ent8 * kRowStride + (s & 1) * 8 + ds * 64;
@@ -343,7 +350,7 @@ __device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f3
   } else {
     bf16x8 pB[4];
 #pragma unroll
-    for (int ht = 0; ht < 4; ht++) pB[ht] = __builtin_bit_cast(bf16x8, sh->pB[ht][lane]);
+    for (int ht = 0; ht < 4; ht++) pB[ht] = __builtin_bit_cast(bf16x8, sh->pB[buf][ht][lane]);
     const int kk16 = s >> 2;
     const uint8_t* vlo = tl->rows + (g * 4 + kk16) * kRowStride + kNope + (s & 3) * 8;
     const uint8_t* vhi = tl->rows + (16 + g * 4 + kk16) * kRowStride + kNope + (s & 3) * 8;
@@ -385,7 +392,7 @@ __device__ __forceinline__ int64_t part_block(const AttendArgs& a, int row, int 
 }
 
 __global__ void __launch_bounds__(kThreads, 1) k_attend_fp8(AttendArgs a) {
-  __shared__ Fp8Tile tiles[2];
+  __shared__ Fp8Tile tiles[kBufs];
   __shared__ Shared sh;
   __shared__ int src[kMaxSplit];
   int row, split, hgrp;
@@ -406,16 +413,20 @@ __global__ void __launch_bounds__(kThreads, 1) k_attend_fp8(AttendArgs a) {
   const int n_tot = r.n_c + r.n_w;
   const int e_beg = split * a.split_size;
   const int e_end = min(e_beg + a.split_size, n_tot);
-  const int n_local = e_end > e_beg ? e_end - e_beg : 0;
+  // uniform across the workgroup: kept in scalar registers so that the tile
+  // loop's branches are scalar
+  const int n_local = __builtin_amdgcn_readfirstlane(e_end > e_beg ? e_end - e_beg : 0);
   const int n_tiles = (n_local + kTile - 1) / kTile;
 
   resolve_sources(a, r, row, e_beg, e_end, src);
   __syncthreads();
 
-  // two tiles in flight: tile t is staged in set t % 2
+  // every stage_load is unconditional (tiles past the split read valid rows
+  // and are masked), so every path through the loop has the same number of
+  // loads in flight and the compiler's waits stay partial (vmcnt(N), N > 0)
   Stage s0, s1;
-  if (n_tiles > 0) stage_load(a, src, b, 0, n_local, s0);
-  if (n_tiles > 1) stage_load(a, src, b, kTile, n_local, s1);
+  stage_load(a, src, b, 0, n_local, s0);
+  stage_load(a, src, b, kTile, n_local, s1);
 
   // Q^T fragments of this wave's half: k-step ks covers dims
   // 256*half + 32ks .. +31 (the RoPE dims are k-steps 6, 7 of half 1); the
@@ -441,31 +452,32 @@ __global__ void __launch_bounds__(kThreads, 1) k_attend_fp8(AttendArgs a) {
   S.l_run = 0.0f;
   const float c2 = a.sm_scale * kLog2e;
 
-  if (n_tiles > 0) {
-    stage_store(&tiles[0], s0);
-    if (n_tiles > 2) stage_load(a, src, b, 2 * kTile, n_local, s0);
-  }
+  stage_store(&tiles[0], s0);
+  stage_load(a, src, b, 2 * kTile, n_local, s0);
   __syncthreads();
 
-  // step t: logits + softmax of tile t, PV of tile t, move tile t+1 (set
-  // (t+1)%2) into LDS, refill that set with tile t+3
-#define V4A_STEP(T, SET)                                                          \
-  {                                                                               \
-    const int t_ = (T);                                                           \
-    if (t_ >= n_tiles) break;                                                     \
-    if (threadIdx.x == 0) sh.any_rescale = 0;                                     \
-    qk_softmax(&tiles[t_ & 1], &sh, qf, S, c2, hg, half, g, li);                  \
-    __syncthreads();                                                              \
-    pv_slice(&tiles[t_ & 1], &sh, acc, wave, g, li);                              \
-    if (t_ + 1 < n_tiles) {                                                       \
-      stage_store(&tiles[(t_ + 1) & 1], SET);                                     \
-      if (t_ + 3 < n_tiles) stage_load(a, src, b, (t_ + 3) * kTile, n_local, SET); \
-    }                                                                             \
-    __syncthreads();                                                              \
+  // step k: partial logits of tile k, softmax of tile k-1, PV of tile k-2;
+  // tile k+1 (register set (k+1)%2) moves into LDS and that set is refilled
+  // with tile k+3.  Steps go in pairs (fixed register sets); all phase
+  // conditions are uniform scalar branches and every step issues the same
+  // loads.
+#define V4A_STEP(K, SET)                                                              \
+  {                                                                                   \
+    const int k_ = (K);                                                               \
+    if (k_ < n_tiles)                                                                 \
+      qk_partial(&tiles[k_ % kBufs], sh.xc[k_ & 1], qf, hg, half, g, li);             \
+    if (k_ >= 1 && k_ <= n_tiles)                                                     \
+      softmax_tile(&tiles[(k_ - 1) % kBufs], sh.xc[(k_ - 1) & 1], &sh, (k_ - 1) & 1,  \
+                   S, c2, hg, half, g, li);                                           \
+    if (k_ >= 2 && k_ - 2 < n_tiles)                                                  \
+      pv_slice(&tiles[(k_ - 2) % kBufs], &sh, (k_ - 2) & 1, acc, wave, g, li);        \
+    stage_store(&tiles[(k_ + 1) % kBufs], SET);                                       \
+    stage_load(a, src, b, (k_ + 3) * kTile, n_local, SET);                            \
+    __syncthreads();                                                                  \
   }
-  for (int it = 0; it < n_tiles; it += 2) {
-    V4A_STEP(it, s1)
-    V4A_STEP(it + 1, s0)
+  for (int k = 0; k < n_tiles + 2; k += 2) {
+    V4A_STEP(k, s1)
+    V4A_STEP(k + 1, s0)
   }
 #undef V4A_STEP
 
@@ -771,7 +783,7 @@ void attend_plan(AttendArgs& a, int64_t n_entries_max) {
   a.f32_heads = a.fp8 ? 64 : (a.H < 4096 / D ? a.H : (4096 / D > 0 ? 4096 / D : 1));
   int64_t per = (n_entries_max + 15) / 16;
   if (per < 128) per = 128;
-  per = (per + 31) / 32 * 32;
+  per = (per + 63) / 64 * 64;               // whole tile pairs
   if (per > kMaxSplit) per = kMaxSplit;
   a.split_size = (int)per;
   int64_t ns = n_entries_max > 0 ? (n_entries_max + per - 1) / per : 1;
@@ -803,16 +815,24 @@ size_t attend_f32_smem(const AttendArgs& a) {
          sizeof(int) * kF32Chunk;
 }
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st, const KernelEvents* ev) {
   const int rows = a.B * a.Q;
   if (rows == 0) return hipSuccess;
   if (a.fp8) {
     const int64_t N = (int64_t)rows * a.n_split * ((a.H + 63) / 64);
     const int64_t per = (N + 7) / 8;
-    hipLaunchKernelGGL(k_attend_fp8, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st, a);
+    if (ev)
+      hipExtLaunchKernelGGL(k_attend_fp8, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st, ev->start,
+                            ev->stop, 0, a);
+    else
+      hipLaunchKernelGGL(k_attend_fp8, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st, a);
   } else {
     dim3 grid(rows, a.n_split, (a.H + a.f32_heads - 1) / a.f32_heads);
-    hipLaunchKernelGGL(k_attend_f32, grid, dim3(256), attend_f32_smem(a), st, a);
+    if (ev)
+      hipExtLaunchKernelGGL(k_attend_f32, grid, dim3(256), attend_f32_smem(a), st, ev->start,
+                            ev->stop, 0, a);
+    else
+      hipLaunchKernelGGL(k_attend_f32, grid, dim3(256), attend_f32_smem(a), st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;

@@ -614,7 +614,7 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   }
 }
 
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st) {
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEvents* ev) {
   const int R = a.B * a.Q;
   if (R == 0) return hipSuccess;
   {
@@ -639,7 +639,10 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st) {
     if (iters > it_total) iters = it_total;
     b.score_iters = (int)iters;
     dim3 grid((unsigned)((it_total + iters - 1) / iters), R);
-    hipLaunchKernelGGL(k_score_mx, grid, dim3(256), 0, st, b);
+    if (ev)
+      hipExtLaunchKernelGGL(k_score_mx, grid, dim3(256), 0, st, ev->start, ev->stop, 0, b);
+    else
+      hipLaunchKernelGGL(k_score_mx, grid, dim3(256), 0, st, b);
   } else {
     dim3 grid((unsigned)((a.cap + 255) / 256), R);
     size_t smem = sizeof(float) * ((size_t)a.H * a.d + a.H) + sizeof(uint32_t) * kBins;

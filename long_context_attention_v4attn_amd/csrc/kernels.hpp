@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -54,7 +55,12 @@ struct IndexArgs {
 };
 size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx);
 void index_carve(IndexArgs& a, void* ws);
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st);
+// `ev` (may be null): a start / stop event pair recorded around the call's
+// dominant kernel (hipExtLaunchKernelGGL), for kernel-level timing.
+struct KernelEvents {
+  hipEvent_t start, stop;
+};
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEvents* ev);
 
 // ---------------------------------------------------------------- attend
 struct AttendArgs {
@@ -89,6 +95,6 @@ struct AttendArgs {
 void attend_plan(AttendArgs& a, int64_t n_entries_max);
 size_t attend_workspace_bytes(const AttendArgs& a);
 void attend_carve(AttendArgs& a, void* ws);
-hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st, const KernelEvents* ev);
 
 }  // namespace v4a
