@@ -20,8 +20,8 @@
 //                order-preserving keys in LDS and flushes once (global atomics).
 //   k_score_f32  fp32 VALU variant for unquantised keys (same histogram).
 //   k_filter1    per query, many workgroups (4096 scores each): the
-//                histogram gives the bin b1 (key bits 31..21) that holds the
-//                k-th largest score; ids in b1 are histogrammed on bits 20..10.
+//                histogram gives the bin b1 (key bits 31..24) that holds the
+//                k-th largest score; ids in b1 are histogrammed on bits 23..13.
 //   k_filter2    same split: the second histogram gives the bin b2; each
 //                workgroup counts its ids above (b1, b2) and appends the ids
 //                in (b1, b2) as candidates.
@@ -40,7 +40,11 @@ namespace v4a {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr int kBins = 2048;                // first radix digit: key bits 31..21
+constexpr int kBins1 = 256;                // first radix digit: key bits 31..24
+constexpr int kSh1 = 24;
+constexpr int kBins2 = 2048;               // second digit: key bits 23..13
+constexpr int kSh2 = 13;
+constexpr int kBinsMax = 4096;             // widest digit of the final select
 constexpr int kCandCap = 16384;            // candidate slots per query
 constexpr int kFThreads = 256;
 constexpr int kPer = 16;                   // consecutive scores per filter thread
@@ -54,7 +58,7 @@ size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx
   size_t n = 0;
   if (key_mx) n += align256(R * H * (d / 2)) + align256(R * H * (d / 32));
   n += align256(R * (size_t)score_ld(cap) * sizeof(float));
-  n += 2 * align256(R * kBins * sizeof(uint32_t));
+  n += align256(R * kBins1 * sizeof(uint32_t)) + align256(R * kBins2 * sizeof(uint32_t));
   n += align256(R * kCtr * sizeof(uint32_t));
   n += align256(R * kCandCap * sizeof(uint64_t));
   n += align256(R * (size_t)n_chunks(cap) * sizeof(uint32_t));
@@ -76,9 +80,9 @@ void index_carve(IndexArgs& a, void* ws) {
   a.scores = (float*)p;
   p += align256(R * (size_t)a.sc_ld * sizeof(float));
   a.hist = (uint32_t*)p;
-  p += align256(R * kBins * sizeof(uint32_t));
+  p += align256(R * kBins1 * sizeof(uint32_t));
   a.hist2 = (uint32_t*)p;
-  p += align256(R * kBins * sizeof(uint32_t));
+  p += align256(R * kBins2 * sizeof(uint32_t));
   a.ctr = (uint32_t*)p;
   p += align256(R * kCtr * sizeof(uint32_t));
   a.cand = (uint64_t*)p;
@@ -103,10 +107,8 @@ __global__ void __launch_bounds__(256) k_prep(IndexArgs a) {
   const int R = a.B * a.Q;
   const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t nthr = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = tid; i < (size_t)R * kBins; i += nthr) {
-    a.hist[i] = 0u;
-    a.hist2[i] = 0u;
-  }
+  for (size_t i = tid; i < (size_t)R * kBins1; i += nthr) a.hist[i] = 0u;
+  for (size_t i = tid; i < (size_t)R * kBins2; i += nthr) a.hist2[i] = 0u;
   for (size_t i = tid; i < (size_t)R * kCtr; i += nthr) a.ctr[i] = 0u;
   if (!a.key_mx) return;
   // one wave per (row, head): 128 elements, 2 per lane; a group of 32 is 16 lanes
@@ -127,11 +129,11 @@ __global__ void __launch_bounds__(256) k_prep(IndexArgs a) {
   }
 }
 
-// LDS histogram of the scores' first digit, flushed to the query's global
-// histogram (non-empty bins only).
-__device__ __forceinline__ void hist_flush(uint32_t* lh, uint32_t* gh) {
+// LDS histogram of nb bins flushed to the query's global histogram
+// (non-empty bins only).
+__device__ __forceinline__ void hist_flush(uint32_t* lh, uint32_t* gh, int nb) {
   __syncthreads();
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) {
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) {
     uint32_t c = lh[i];
     if (c) atomicAdd(gh + i, c);
   }
@@ -182,14 +184,14 @@ __device__ __forceinline__ void score_tiles(const KeyTiles& kt, const i32x8* qa,
     part += __shfl_xor(part, 32, 64);
     if (g == 0 && blk < nv) {
       out[blk] = part;
-      atomicAdd(&lh[score_key(part) >> 21], 1u);
+      atomicAdd(&lh[score_key(part) >> kSh1], 1u);
     }
   }
 }
 
 // Workgroup w of a query covers blocks [w * iters * 1024, (w + 1) * iters * 1024).
 __global__ void __launch_bounds__(256) k_score_mx(IndexArgs a) {
-  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t lh[kBins1];
   const int row = blockIdx.y;
   const int b = row / a.Q;
   const int lane = threadIdx.x & 63;
@@ -198,7 +200,7 @@ __global__ void __launch_bounds__(256) k_score_mx(IndexArgs a) {
   const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
   const int64_t wg0 = (int64_t)blockIdx.x * a.score_iters * kIterBlocks;
   if (wg0 >= nv) return;                   // uniform across the workgroup
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = 0u;
+  for (int i = threadIdx.x; i < kBins1; i += blockDim.x) lh[i] = 0u;
   int iters = (int)((nv - wg0 + kIterBlocks - 1) / kIterBlocks);
   if (iters > a.score_iters) iters = a.score_iters;
 
@@ -237,7 +239,161 @@ __global__ void __launch_bounds__(256) k_score_mx(IndexArgs a) {
     if (it + 2 < iters) load_keys(kc, ks, b0 + 2 * kIterBlocks, nv, g, li, k0);
     score_tiles(k1, qa, qs, wv, HT, b0 + kIterBlocks, nv, g, li, out, lh);
   }
-  hist_flush(lh, a.hist + (size_t)row * kBins);
+  hist_flush(lh, a.hist + (size_t)row * kBins1, kBins1);
+}
+
+// ---------------------------------------------------------------- FP4 scan, query-tiled
+// Many queries per sequence (prefill chunks): a workgroup takes kQT queries
+// of one sequence and a range of kQRange blocks, so every key fragment loaded
+// feeds kQT MFMAs (one per query).  Wave w takes the 16-block tiles w, w+4,
+// ... of the range; per tile and query one v_mfma_scale_f32_16x16x128_f8f6f4
+// (M = the 16 index heads, N = 16 blocks), ReLU * w over each lane's four
+// heads, then the sum over the four lane groups for all kQT queries at once
+// with two lane-swap steps (v_permlane32_swap, v_permlane16_swap), which
+// leaves lane group g with the totals of queries (g & 1) + 4 (g >> 1) and
+// that + 2.  Per-query first-digit histograms in LDS, flushed once.
+constexpr int kQT = 8;
+constexpr int kQRange = 16384;
+
+// x + y after swapping x's lanes 32..63 with y's lanes 0..31: lanes 0..31
+// hold x summed over lane groups {0, 2} resp. {1, 3}, lanes 32..63 the same
+// for y.
+// (The optimiser of this toolchain folds the two results of a swap into one
+// value when both feed the same add; the empty asm statement -- no
+// instruction, it only marks both registers as read and written -- keeps
+// them apart.)
+__device__ __forceinline__ float swap_add32(float x, float y) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, y), false, false);
+  uint32_t lo = r[0], hi = r[1];
+  __asm__ volatile("" : "+v"(lo), "+v"(hi));
+  return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
+// The same within each half: swaps x's lanes 16..31 (48..63) with y's lanes
+// 0..15 (32..47).
+__device__ __forceinline__ float swap_add16(float x, float y) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, y), false, false);
+  uint32_t lo = r[0], hi = r[1];
+  __asm__ volatile("" : "+v"(lo), "+v"(hi));
+  return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
+struct QFrag {
+  u32x4 v;
+  int sc;
+};
+
+__device__ __forceinline__ void load_qfrag(const uint8_t* kc, const uint8_t* ks, int64_t blk,
+                                           int64_t last, int g, QFrag& f) {
+  const int64_t bb = blk < last ? blk : last;     // clamped: always a real row
+  f.v = __builtin_nontemporal_load((const u32x4*)(kc + bb * 64 + g * 16));
+  f.sc = ks[bb * 4 + g];
+}
+
+__global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
+  __shared__ uint32_t lh[kQT][kBins1];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int qtiles = (a.Q + kQT - 1) / kQT;
+  const int b = blockIdx.x / qtiles;
+  const int t0 = (blockIdx.x % qtiles) * kQT;
+  const int64_t r0 = (int64_t)blockIdx.y * kQRange;
+  int64_t nv_max = 0;
+#pragma unroll
+  for (int q = 0; q < kQT; q++) {
+    const int t = t0 + q;
+    const int64_t nv = t < a.Q ? n_visible(a.pos[(int64_t)b * a.Q + t], a.m, a.cap) : 0;
+    nv_max = nv > nv_max ? nv : nv_max;
+  }
+  if (r0 >= nv_max) return;                // uniform across the workgroup
+  for (int i = threadIdx.x; i < kQT * kBins1; i += blockDim.x) (&lh[0][0])[i] = 0u;
+  // A operands (16 heads x 128 elements of each query), scales, head weights
+  i32x8 qa[kQT];
+  int qs[kQT];
+  float wv[kQT][4];
+#pragma unroll
+  for (int q = 0; q < kQT; q++) {
+    const int t = t0 + q;
+    const int64_t row = (int64_t)b * a.Q + (t < a.Q ? t : a.Q - 1);
+    u32x4 v = *(const u32x4*)(a.qmx + (row * 16 + li) * 64 + g * 16);
+    qa[q] = (i32x8){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+    qs[q] = a.qsc[(row * 16 + li) * 4 + g];
+#pragma unroll
+    for (int i = 0; i < 4; i++) wv[q][i] = t < a.Q ? a.w[row * 16 + g * 4 + i] : 0.0f;
+  }
+  // the two queries this lane stores: (g & 1) + 4 (g >> 1) and that + 2
+  const int qa0 = (g & 1) + 4 * (g >> 1), qa1 = qa0 + 2;
+  int64_t nv0 = 0, nv1 = 0;
+#pragma unroll
+  for (int q = 0; q < kQT; q++) {
+    const int t = t0 + q;
+    const int64_t nv = t < a.Q ? n_visible(a.pos[(int64_t)b * a.Q + t], a.m, a.cap) : 0;
+    if (q == qa0) nv0 = nv;
+    if (q == qa1) nv1 = nv;
+  }
+  float* out0 = a.scores + ((int64_t)b * a.Q + t0 + qa0) * a.sc_ld;
+  float* out1 = a.scores + ((int64_t)b * a.Q + t0 + qa1) * a.sc_ld;
+  __syncthreads();                         // lh zeroed
+
+  const uint8_t* kc = (const uint8_t*)a.codes + (size_t)b * a.cap * 64;
+  const uint8_t* ks = a.kscales + (size_t)b * a.cap * 4;
+  const int64_t r1 = r0 + kQRange < nv_max ? r0 + kQRange : nv_max;
+  const int64_t last = r1 - 1;
+
+  auto tile = [&](const QFrag& f, int64_t blk0) {
+    const i32x8 kb = {(int)f.v[0], (int)f.v[1], (int)f.v[2], (int)f.v[3], 0, 0, 0, 0};
+    float part[kQT];
+#pragma unroll
+    for (int q = 0; q < kQT; q++) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[q], kb, acc, 4, 4, 0, qs[q], 0,
+                                                             f.sc);
+      float p = wv[q][0] * fmaxf(acc[0], 0.0f);
+#pragma unroll
+      for (int i = 1; i < 4; i++) p += wv[q][i] * fmaxf(acc[i], 0.0f);
+      part[q] = p;
+    }
+    // sum over the four lane groups, all queries at once
+    float h[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) h[j] = swap_add32(part[j], part[4 + j]);
+    const float s0 = swap_add16(h[0], h[1]);    // queries 0, 1, 4, 5 by lane group
+    const float s1 = swap_add16(h[2], h[3]);    // queries 2, 3, 6, 7
+    const int64_t blk = blk0 + li;
+    if (blk < nv0 && t0 + qa0 < a.Q) {
+      out0[blk] = s0;
+      atomicAdd(&lh[qa0][score_key(s0) >> kSh1], 1u);
+    }
+    if (blk < nv1 && t0 + qa1 < a.Q) {
+      out1[blk] = s1;
+      atomicAdd(&lh[qa1][score_key(s1) >> kSh1], 1u);
+    }
+  };
+
+  // tiles w, w + 4, ... of 16 blocks; two fragments in flight
+  QFrag fa, fb;
+  int64_t blk0 = r0 + wave * 16;
+  load_qfrag(kc, ks, blk0 + li, last, g, fa);
+  for (; blk0 < r1; blk0 += 128) {
+    load_qfrag(kc, ks, blk0 + 64 + li, last, g, fb);
+    tile(fa, blk0);
+    if (blk0 + 64 >= r1) break;
+    load_qfrag(kc, ks, blk0 + 128 + li, last, g, fa);
+    tile(fb, blk0 + 64);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kQT; q++) {
+    if (t0 + q >= a.Q) break;
+    uint32_t* gh = a.hist + ((int64_t)b * a.Q + t0 + q) * kBins1;
+    for (int i = threadIdx.x; i < kBins1; i += blockDim.x) {
+      const uint32_t c = lh[q][i];
+      if (c) atomicAdd(gh + i, c);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- fp32 scan
@@ -251,7 +407,7 @@ __global__ void __launch_bounds__(256) k_score_f32(IndexArgs a) {
   const int64_t blk = wg0 + threadIdx.x;
   float* wsm = qsm + a.H * a.d;
   uint32_t* lh = (uint32_t*)(wsm + a.H);
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = 0u;
+  for (int i = threadIdx.x; i < kBins1; i += blockDim.x) lh[i] = 0u;
   for (int i = threadIdx.x; i < a.H * a.d; i += blockDim.x)
     qsm[i] = load_as_f32(a.q, a.q_bf16, (size_t)row * a.H * a.d + i);
   for (int i = threadIdx.x; i < a.H; i += blockDim.x) wsm[i] = a.w[(size_t)row * a.H + i];
@@ -265,9 +421,9 @@ __global__ void __launch_bounds__(256) k_score_f32(IndexArgs a) {
       s += wsm[h] * fmaxf(dot, 0.0f);
     }
     a.scores[(size_t)row * a.sc_ld + blk] = s;
-    atomicAdd(&lh[score_key(s) >> 21], 1u);
+    atomicAdd(&lh[score_key(s) >> kSh1], 1u);
   }
-  hist_flush(lh, a.hist + (size_t)row * kBins);
+  hist_flush(lh, a.hist + (size_t)row * kBins1, kBins1);
 }
 
 // ---------------------------------------------------------------- filter + select
@@ -354,17 +510,17 @@ __device__ __forceinline__ bool filter_head(const IndexArgs& a, int row, uint32_
   fr->kk = (int)(fr->nv < a.k ? fr->nv : a.k);
   if (fr->kk == fr->nv) return false;
   if ((int64_t)blockIdx.x * kFilterChunk >= fr->nv) return false;
-  const uint32_t* gh = a.hist + (size_t)row * kBins;
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = gh[i];
+  const uint32_t* gh = a.hist + (size_t)row * kBins1;
+  for (int i = threadIdx.x; i < kBins1; i += blockDim.x) lh[i] = gh[i];
   __syncthreads();
-  find_bin(lh, kBins, (uint32_t)fr->kk, tmp, &s_bin, &s_above);
+  find_bin(lh, kBins1, (uint32_t)fr->kk, tmp, &s_bin, &s_above);
   fr->b1 = (uint32_t)s_bin;
   fr->above1 = s_above;
   return true;
 }
 
 __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
-  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t lh[kBins2];
   __shared__ uint32_t tmp[kFThreads / 64];
   const int row = blockIdx.y;
   FilterRow fr;
@@ -379,12 +535,12 @@ __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
   uint32_t k32[kPer];
   int64_t i0;
   const int n_in = load_group(a, row, fr.nv, blockIdx.x, k32, &i0);
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = 0u;
+  for (int i = threadIdx.x; i < kBins2; i += blockDim.x) lh[i] = 0u;
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kPer; j++)
-    if (j < n_in && (k32[j] >> 21) == fr.b1) atomicAdd(&lh[(k32[j] >> 10) & (kBins - 1)], 1u);
-  hist_flush(lh, a.hist2 + (size_t)row * kBins);
+    if (j < n_in && (k32[j] >> kSh1) == fr.b1) atomicAdd(&lh[(k32[j] >> kSh2) & (kBins2 - 1)], 1u);
+  hist_flush(lh, a.hist2 + (size_t)row * kBins2, kBins2);
 }
 
 // Candidate appends go to an LDS buffer first (wave-aggregated LDS atomics);
@@ -438,7 +594,7 @@ struct CandSrc {
   uint32_t n;
   const float* sc;
   int64_t nv;
-  uint32_t b12;                            // key bits 31..10 of the candidates
+  uint32_t b12;                            // key bits 31..13 of the candidates
   bool compact;
   __device__ __forceinline__ int64_t size() const { return compact ? (int64_t)n : nv; }
   __device__ __forceinline__ bool get(int64_t i, uint64_t* key) const {
@@ -448,7 +604,7 @@ struct CandSrc {
     }
     uint32_t k32 = score_key(sc[i]);
     *key = sel_key(k32, i);
-    return (k32 >> 10) == b12;
+    return (k32 >> kSh2) == b12;
   }
 };
 
@@ -466,7 +622,7 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* tmp) {
 }
 
 // The exact 64-bit threshold T: the need-th largest key among the
-// candidates (radix select on the bits below the candidates' common 22-bit
+// candidates (radix select on the bits below the candidates' common 19-bit
 // prefix).  Exactly `need` candidates have keys >= T.
 __device__ uint64_t resolve_threshold(const CandSrc& src, uint32_t need, uint32_t* lh,
                                       uint32_t* tmp) {
@@ -474,21 +630,21 @@ __device__ uint64_t resolve_threshold(const CandSrc& src, uint32_t need, uint32_
   __shared__ uint32_t s_need, s_above;
   __shared__ int s_bin, s_done;
   if (threadIdx.x == 0) {
-    s_prefix = (uint64_t)src.b12 << 42;
-    s_mask = (uint64_t)0x3FFFFF << 42;
+    s_prefix = (uint64_t)src.b12 << (32 + kSh2);
+    s_mask = (uint64_t)0x7FFFF << (32 + kSh2);
     s_need = need;
     s_done = 0;
   }
   __syncthreads();
-  // remaining digits: score key bits 9..0, then the inverted id
-  const int shifts[4] = {32, 21, 10, 0};
-  const int widths[4] = {10, 11, 11, 10};
+  // remaining digits: score key bits 12..0, then the inverted id
+  const int shifts[4] = {34, 23, 12, 0};
+  const int widths[4] = {11, 11, 11, 12};
   const int64_t n = src.size();
   for (int pass = 0; pass < 4; pass++) {
     if (s_done) break;
     const int sh = shifts[pass], wd = widths[pass];
     const uint32_t nb = 1u << wd;
-    for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = 0u;
+    for (int i = threadIdx.x; i < (int)nb; i += blockDim.x) lh[i] = 0u;
     __syncthreads();
     const uint64_t pm = s_mask, pp = s_prefix;
     for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
@@ -514,7 +670,7 @@ __device__ uint64_t resolve_threshold(const CandSrc& src, uint32_t need, uint32_
 }
 
 __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
-  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t lh[kBins2];
   __shared__ uint32_t tmp[kFThreads / 64];
   __shared__ uint64_t cand_buf[kCandLds];
   __shared__ int s_bin;
@@ -525,12 +681,12 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   uint32_t k32[kPer];
   int64_t i0;
   const int n_in = load_group(a, row, fr.nv, blockIdx.x, k32, &i0);
-  const uint32_t* gh2 = a.hist2 + (size_t)row * kBins;
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) lh[i] = gh2[i];
+  const uint32_t* gh2 = a.hist2 + (size_t)row * kBins2;
+  for (int i = threadIdx.x; i < kBins2; i += blockDim.x) lh[i] = gh2[i];
   if (threadIdx.x == 0) cand_n = 0;
   __syncthreads();
-  find_bin(lh, kBins, (uint32_t)fr.kk - fr.above1, tmp, &s_bin, &s_above);
-  const uint32_t b12 = (fr.b1 << 11) | (uint32_t)s_bin;   // key bits 31..10
+  find_bin(lh, kBins2, (uint32_t)fr.kk - fr.above1, tmp, &s_bin, &s_above);
+  const uint32_t b12 = (fr.b1 << 11) | (uint32_t)s_bin;   // key bits 31..13
   uint32_t* ctr = a.ctr + (size_t)row * kCtr;
   uint64_t* cand = a.cand + (size_t)row * kCandCap;
   CandList cnd{cand_buf, &cand_n};
@@ -538,7 +694,7 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
     const bool in = j < n_in;
-    const uint32_t d12 = k32[j] >> 10;
+    const uint32_t d12 = k32[j] >> kSh2;
     above += (in && d12 > b12) ? 1u : 0u;
     cnd.append(in && d12 == b12, sel_key(k32[j], i0 + j), ctr + 0, cand);
   }
@@ -557,10 +713,10 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
 constexpr int kEmitCand = 4096;            // candidates resolved from LDS
 
 // Every workgroup of a query resolves the threshold T from the candidates
-// (few: they share the top 22 key bits with the k-th largest score), finds
+// (few: they share the top 19 key bits with the k-th largest score), finds
 // its chunk's output offset, and writes its chunk's selected ids in order.
 __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
-  __shared__ uint32_t lh[kBins];
+  __shared__ uint32_t lh[kBinsMax];
   __shared__ uint32_t tmp[kFThreads / 64];
   __shared__ uint64_t cl[kEmitCand];
   const int row = blockIdx.y;
@@ -618,7 +774,7 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEve
   const int R = a.B * a.Q;
   if (R == 0) return hipSuccess;
   {
-    size_t work = (size_t)R * kBins;
+    size_t work = (size_t)R * kBins2;
     if (a.key_mx) {
       size_t qthreads = (size_t)R * a.H * 64;
       if (qthreads > work) work = qthreads;
@@ -629,7 +785,14 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEve
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.key_mx) {
+  if (a.key_mx && a.H == 16 && a.Q >= kQT) {
+    dim3 grid((unsigned)(a.B * ((a.Q + kQT - 1) / kQT)),
+              (unsigned)((a.cap + kQRange - 1) / kQRange));
+    if (ev)
+      hipExtLaunchKernelGGL(k_score_mx_q, grid, dim3(256), 0, st, ev->start, ev->stop, 0, a);
+    else
+      hipLaunchKernelGGL(k_score_mx_q, grid, dim3(256), 0, st, a);
+  } else if (a.key_mx) {
     // about 512 workgroups in all (two per CU), each walking score_iters
     // iterations of 1024 blocks: fewer histogram flushes per query
     IndexArgs b = a;
@@ -645,7 +808,7 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEve
       hipLaunchKernelGGL(k_score_mx, grid, dim3(256), 0, st, b);
   } else {
     dim3 grid((unsigned)((a.cap + 255) / 256), R);
-    size_t smem = sizeof(float) * ((size_t)a.H * a.d + a.H) + sizeof(uint32_t) * kBins;
+    size_t smem = sizeof(float) * ((size_t)a.H * a.d + a.H) + sizeof(uint32_t) * kBins1;
     hipLaunchKernelGGL(k_score_f32, grid, dim3(256), smem, st, a);
   }
   hipError_t e = hipGetLastError();

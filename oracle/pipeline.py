@@ -51,3 +51,46 @@ def workload1(g, k=64, n_win=128, m=4, d_nope=64):
                     g["pos"], m, k, D ** -0.5, None, "f32")
     res.update(comp=comp, keys=keys, win=win, y=y, yi=yi)
     return res
+
+
+def _ring(pre, tokens, t_first, R):
+    """Raw-token ring of R rows: pre holds tokens t_first - len(pre) .. t_first - 1,
+    tokens holds t_first .. t_first + T - 1; token t sits at row t mod R (rows
+    never written stay zero)."""
+    B, _, D = tokens.shape
+    ring = np.zeros((B, R, D), dtype=np.float32)
+    npre = pre.shape[1]
+    for i in range(npre):
+        ring[:, (t_first - npre + i) % R] = pre[:, i]
+    for j in range(tokens.shape[1]):
+        ring[:, (t_first + j) % R] = tokens[:, j]
+    return ring
+
+
+def prefill_caches(g, m_csa=4, m_hca=128, n_win=128, d_nope=448):
+    """Caches of one CSA and one HCA layer after a prefill chunk (workload 5).
+
+    The cached context is cache-direct (entries and keys as given); the chunk
+    [ctx, ctx + T) is pooled by the compressors ([Notes §7] overlap for CSA
+    entries and indexer keys, [Notes §8] non-overlap for HCA) and appended.
+    The raw-token window rings hold tokens ctx - n_win + 1 .. ctx + T - 1 in
+    R = T + n_win rows (row = token mod R), so every query of the chunk finds
+    its whole window.
+    """
+    ctx = int(g["pos"][0, 0])
+    T = g["q"].shape[1]
+    y = compress(g["csa_kv_cur"], g["csa_z_cur"], g["csa_kv_prev"], g["csa_z_prev"],
+                 g["csa_bias"], m_csa, ctx)
+    yi = compress(g["idx_kv_cur"], g["idx_z_cur"], g["idx_kv_prev"], g["idx_z_prev"],
+                  g["idx_bias"], m_csa, ctx)
+    yh = compress(g["hca_kv"], g["hca_z"], None, None, g["hca_bias"], m_hca, ctx)
+    R = T + n_win
+    out = dict(
+        y=y, yi=yi, yh=yh, R=R,
+        comp=kv_encode(np.concatenate([g["csa_comp"], f32(y)], axis=1), "fp8", d_nope),
+        keys=idx_encode(np.concatenate([g["keys"], f32(yi)], axis=1), "mxfp4"),
+        hcomp=kv_encode(np.concatenate([g["hca_comp"], f32(yh)], axis=1), "fp8", d_nope),
+        win=kv_encode(_ring(g["csa_win_pre"], g["csa_kv_cur"], ctx, R), "fp8", d_nope),
+        hwin=kv_encode(_ring(g["hca_win_pre"], g["hca_kv"], ctx, R), "fp8", d_nope),
+    )
+    return out
