@@ -203,6 +203,127 @@ def make_calls(v4, torch, r, ws, cc, ch):
     return [idx, csa, hca]
 
 
+# ---------------------------------------------------------------- prefill chunk
+
+PREFILL_WID = 5
+
+
+def bench_prefill(v4, torch, log, iters=8, warmup=2):
+    """One chunk of 4096 new tokens after a 1M-token context (B = 1): pool the
+    chunk into the CSA entries, indexer keys and HCA entries, then index top-k,
+    CSA attend and HCA attend for every chunk query.  Inputs are random
+    device tensors of the workload's shapes and distributions (the caches
+    quantised by the library); eager launches (each call runs for
+    milliseconds)."""
+    from long_context_attention_v4attn_amd import synth
+    c = synth.WORKLOADS[PREFILL_WID]
+    dev = "cuda"
+    ctx, T, H, HI, dI = c["ctx"], c["chunk"], c["H"], c["H_I"], c["d_I"]
+    D = c["d_nope"] + c["d_rope"]
+    n_csa, n_hca, n_win, k = ctx // c["m_csa"], ctx // c["m_hca"], c["n_win"], c["k"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+
+    def randn(*shape, std=1.0, dtype=torch.float32):
+        return (torch.randn(*shape, device=dev, generator=g) * std).to(dtype)
+
+    def quant_kv(n, rows_src):
+        kv = v4.KVCache.empty(1, n, c["d_nope"], c["d_rope"], v4.KV_FP8_BF16ROPE)
+        v4.v4attn_compress(rows_src, None, None, None, None, 1, 0, kv)
+        return kv
+
+    t0 = time.time()
+    comp = v4.KVCache.empty(1, n_csa + T // 4, c["d_nope"], c["d_rope"], v4.KV_FP8_BF16ROPE)
+    v4.v4attn_compress(randn(1, n_csa, D, std=D ** -0.5), None, None, None, None, 1, 0, comp)
+    keys = v4.IdxCache.empty(1, n_csa + T // 4, dI, v4.IDX_MXFP4)
+    v4.v4attn_compress(randn(1, n_csa, dI, std=dI ** -0.5), None, None, None, None, 1, 0, keys)
+    hcomp = v4.KVCache.empty(1, n_hca + T // 128, c["d_nope"], c["d_rope"], v4.KV_FP8_BF16ROPE)
+    v4.v4attn_compress(randn(1, n_hca, D, std=D ** -0.5), None, None, None, None, 1, 0, hcomp)
+    R = T + n_win
+    win = quant_kv(R, randn(1, R, D, std=D ** -0.5))
+    hwin = quant_kv(R, randn(1, R, D, std=D ** -0.5))
+    bf = torch.bfloat16
+    s_csa = [randn(1, T, D, std=D ** -0.5, dtype=bf), randn(1, T, D, dtype=bf),
+             randn(1, T, D, std=D ** -0.5, dtype=bf), randn(1, T, D, dtype=bf)]
+    s_idx = [randn(1, T, dI, std=dI ** -0.5, dtype=bf), randn(1, T, dI, dtype=bf),
+             randn(1, T, dI, std=dI ** -0.5, dtype=bf), randn(1, T, dI, dtype=bf)]
+    s_hca = [randn(1, T, D, std=D ** -0.5, dtype=bf), randn(1, T, D, dtype=bf)]
+    b_csa, b_idx, b_hca = randn(8, D, std=0.5), randn(8, dI, std=0.5), randn(128, D, std=0.5)
+    q = randn(1, T, H, D, std=D ** -0.5, dtype=bf)
+    qi = randn(1, T, HI, dI, std=dI ** -0.5, dtype=bf)
+    w = torch.rand(1, T, HI, device=dev, generator=g)
+    pos = (ctx + torch.arange(T, device=dev, dtype=torch.int64)).view(1, T)
+    topk = torch.empty(1, T, k, dtype=torch.int32, device=dev)
+    out, hout = torch.empty_like(q), torch.empty_like(q)
+    ws = {
+        "index": torch.empty(v4.v4attn_workspace_bytes(v4.OP_INDEX_TOPK, 1, T, HI, dI, n_csa + T // 4,
+                                                       k, 0), dtype=torch.uint8, device=dev),
+        "csa": torch.empty(max(1, v4.v4attn_workspace_bytes(v4.OP_CSA_ATTEND, 1, T, H, D, 0, k, n_win)),
+                           dtype=torch.uint8, device=dev),
+        "hca": torch.empty(max(1, v4.v4attn_workspace_bytes(v4.OP_HCA_ATTEND, 1, T, H, D,
+                                                            n_hca + T // 128, 128, n_win)),
+                           dtype=torch.uint8, device=dev),
+    }
+    torch.cuda.synchronize()
+    log(f"prefill inputs on the GPU in {time.time() - t0:.1f}s")
+    sc = D ** -0.5
+    calls = [
+        ("compress", lambda: (v4.v4attn_compress(*s_csa, b_csa, 4, ctx, comp),
+                              v4.v4attn_compress(*s_idx, b_idx, 4, ctx, keys),
+                              v4.v4attn_compress(s_hca[0], s_hca[1], None, None, b_hca, 128, ctx,
+                                                 hcomp))),
+        ("index_topk", lambda: v4.v4attn_index_topk(qi, w, keys, pos, 4, k, topk=topk, ws=ws["index"])),
+        ("csa_attend", lambda: v4.v4attn_csa_attend(q, comp, topk, win, n_win, pos, None, sc, out=out,
+                                                    ws=ws["csa"])),
+        ("hca_attend", lambda: v4.v4attn_hca_attend(q, hcomp, 128, hwin, n_win, pos, None, sc,
+                                                    out=hout, ws=ws["hca"])),
+    ]
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+    tot = np.zeros(len(calls))
+    for _ in range(iters):
+        for i, (_, f) in enumerate(calls):
+            ev[i].record(stream)
+            f()
+        ev[-1].record(stream)
+        torch.cuda.synchronize()
+        tot += [ev[i].elapsed_time(ev[i + 1]) for i in range(len(calls))]
+    t_calls = tot / iters * 1e-3
+    # the index scan kernel, timed live
+    hip = ctypes.CDLL("libamdhip64.so")
+    e0, e1, ms = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_float()
+    hip.hipEventCreate(ctypes.byref(e0))
+    hip.hipEventCreate(ctypes.byref(e1))
+    t_scan = 0.0
+    for _ in range(iters):
+        v4.v4attn_time_next_kernel(e0.value, e1.value)
+        calls[1][1]()
+        torch.cuda.synchronize()
+        hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1)
+        t_scan += ms.value * 1e-3
+    hip.hipEventDestroy(e0)
+    hip.hipEventDestroy(e1)
+    t_scan /= iters
+    n_vis = (ctx + np.arange(T) + 1) // c["m_csa"]
+    flops = 2.0 * HI * dI * float(n_vis.sum())
+    t_chunk = float(t_calls.sum())
+    return {
+        "workload": "prefill_pair_1m (B=1, 4096-token chunk after 1048576 cached tokens; CSA top-2048 "
+                    "+ HCA, window 128; 64 heads x D=512; indexer 16 x 128 MXFP4)",
+        "tokens_per_s": round(T / t_chunk, 1),
+        "ms_per_chunk": round(t_chunk * 1e3, 3),
+        "calls_ms": {name: round(t * 1e3, 3) for (name, _), t in zip(calls, t_calls)},
+        "index_scan": {"kernel": "k_score_mx_q", "t_us": round(t_scan * 1e6, 1),
+                       "algorithmic_tflop": round(flops / 1e12, 4),
+                       "achieved_tflops": round(flops / t_scan / 1e12, 1), "peak_tflops": FP4_PEAK_TFLOPS,
+                       "mfma_frac": round(flops / t_scan / 1e12 / FP4_PEAK_TFLOPS, 4)},
+    }
+
+
 # ---------------------------------------------------------------- CPU oracle baseline
 
 def cpu_baseline(gc, gh, log):
@@ -261,6 +382,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk leg")
     args = ap.parse_args()
 
     def log(msg):
@@ -451,6 +573,11 @@ def main():
         "graph": not args.no_graph,
         "roofline": roofline,
     }
+    if not args.no_prefill:
+        del layer, single, calls, reps, ws
+        torch.cuda.empty_cache()
+        log("prefill chunk ...")
+        result["prefill"] = bench_prefill(v4, torch, log)
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(gc, gh, log)
