@@ -83,12 +83,14 @@ __device__ __forceinline__ int64_t entry_source(const AttendArgs& a, const RowEn
 constexpr int kTile = 32;                    // entries per tile
 constexpr int kNope = 448;                   // FP8 dims
 constexpr int kRope = 64;                    // BF16 dims
-constexpr int kRowBytes = kNope + 2 * kRope; // 576 staged bytes per entry
-constexpr int kRowStride = 592;              // padded LDS row (bank spread)
-constexpr int kThreads = 512;               // 8 waves: 4 head groups x 2 halves
+constexpr int kRowStride = 592;              // LDS row: 448 FP8 + 128 B RoPE + pad
+constexpr int kHeads = 32;                   // query heads per workgroup
+constexpr int kThreads = 256;                // 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;             // lazy max-rescale threshold (log2 units)
 
+// A staged tile: raw e4m3 codes (448 B), bf16 RoPE dims (128 B), the FP8
+// scale and an additive mask per entry.
 struct __align__(16) Fp8Tile {
   uint8_t rows[kTile * kRowStride];
   float scale[kTile];                      // FP8 scale of the entry (0 if absent)
@@ -131,12 +133,12 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint8_t* p) {
   return o;
 }
 
-// Staging: the 16 threads t = 16e .. 16e+15 move entry e of the tile, so a
-// thread resolves one entry's row per tile.  Thread q = t & 15 moves the
-// 16-byte chunks q, 16 + q and 32 + (q & 3) of the 576-byte staged row
-// (chunks 0..27: FP8 codes, 28..35: BF16 RoPE dims) and the entry's scale.
+// Staging: the 8 threads t = 8e .. 8e+7 move entry e of the tile, so a thread
+// resolves one entry's row per tile.  Thread q = t & 7 moves the 16-byte
+// chunks q, 8 + q, 16 + q and 24 + q (q < 4) of the FP8 codes, or RoPE chunk
+// q - 4 (q >= 4), plus RoPE chunk 4 + (q & 3) and the entry's scale.
 struct Stage {
-  u32x4 r[3];
+  u32x4 r[5];
   float sc;
   int ok;                                  // the entry is present
 };
@@ -145,7 +147,7 @@ struct Stage {
 // (top-k ids are loaded here, not inside the tile pipeline, so the pipelined
 // chunk loads never wait on another global load): >= 0 compressed row,
 // -2 - r window ring row r, -1 absent.
-constexpr int kMaxSplit = 4096;
+constexpr int kMaxSplit = 2048;
 
 __device__ __forceinline__ void resolve_sources(const AttendArgs& a, const RowEntries& r, int row,
                                                 int e_beg, int e_end, int* src) {
@@ -163,8 +165,8 @@ __device__ __forceinline__ void resolve_sources(const AttendArgs& a, const RowEn
 __device__ __forceinline__ void stage_load(const AttendArgs& a, const int* src, int b, int tile_l0,
                                            int n_local, Stage& st) {
   const int t = threadIdx.x;
-  const int q = t & 15;
-  const int le = tile_l0 + (t >> 4);
+  const int q = t & 7;
+  const int le = tile_l0 + (t >> 3);
   const int sraw = src[le < kMaxSplit ? le : kMaxSplit - 1];   // always in bounds
   const int s = le < n_local ? sraw : -1;
   const bool is_win = s < -1;
@@ -175,63 +177,61 @@ __device__ __forceinline__ void stage_load(const AttendArgs& a, const int* src, 
   // the values are masked when stored to LDS, not here: using them now would
   // make the compiler wait for these loads immediately
   st.r[0] = __builtin_nontemporal_load((const u32x4*)(nope + q * 16));
-  st.r[1] = __builtin_nontemporal_load(
-      (const u32x4*)(q < 12 ? nope + (16 + q) * 16 : rope + (q - 12) * 16));
-  st.r[2] = __builtin_nontemporal_load((const u32x4*)(rope + (4 + (q & 3)) * 16));
+  st.r[1] = __builtin_nontemporal_load((const u32x4*)(nope + (8 + q) * 16));
+  st.r[2] = __builtin_nontemporal_load((const u32x4*)(nope + (16 + q) * 16));
+  st.r[3] = __builtin_nontemporal_load(
+      (const u32x4*)(q < 4 ? nope + (24 + q) * 16 : rope + (q - 4) * 16));
+  st.r[4] = __builtin_nontemporal_load((const u32x4*)(rope + (4 + (q & 3)) * 16));
   st.sc = (is_win ? a.w_scale : a.c_scale)[rowi];
   st.ok = s != -1;
 }
 
+// Every value is stored unconditionally (duplicates write identical values),
+// so the compiler cannot sink a load into a branch and wait for it there.
 __device__ __forceinline__ void stage_store(Fp8Tile* tl, const Stage& st) {
   const int t = threadIdx.x;
-  const int e = t >> 4, q = t & 15;
+  const int e = t >> 3, q = t & 7;
   const u32x4 z = {0u, 0u, 0u, 0u};
   uint8_t* dst = tl->rows + e * kRowStride;
   *(u32x4*)(dst + q * 16) = st.ok ? st.r[0] : z;
-  *(u32x4*)(dst + 256 + q * 16) = st.ok ? st.r[1] : z;
-  // chunks 32..35 and the scale: the entry's threads write identical values
-  // (every value is used unconditionally, so the compiler cannot sink its
-  // load into a branch and wait for it there)
-  *(u32x4*)(dst + 512 + (q & 3) * 16) = st.ok ? st.r[2] : z;
+  *(u32x4*)(dst + (8 + q) * 16) = st.ok ? st.r[1] : z;
+  *(u32x4*)(dst + (16 + q) * 16) = st.ok ? st.r[2] : z;
+  *(u32x4*)(dst + (q < 4 ? (24 + q) * 16 : kNope + (q - 4) * 16)) = st.ok ? st.r[3] : z;
+  *(u32x4*)(dst + kNope + (4 + (q & 3)) * 16) = st.ok ? st.r[4] : z;
   tl->scale[e] = st.ok ? st.sc : 0.0f;
   tl->bias[e] = st.ok ? 0.0f : -INFINITY;
 }
 
-// Work split of the 8 waves of a workgroup (64 heads of one query):
-//  * logits and softmax by head group: wave w takes heads 16*(w&3) .. +16 and
-//    half (w>>2) of the 512 dims; the two halves add their partial logits
-//    through LDS (fp32 addition commutes: both hold identical logits) and
-//    run the same online softmax;
-//  * PV by output-dim slice: wave w owns dims 64w .. 64w+63 for all 64 heads,
-//    so each V^T fragment is widened from FP8 once and feeds four MFMAs (one
-//    per head group); P^T of the four head groups comes through LDS.
-// The three phases are software-pipelined over tiles with one barrier per
-// step: step k computes the partial logits of tile k, the softmax of tile
-// k-1 and the PV product of tile k-2, and stages tile k+1.  Four tile
-// buffers and double-buffered exchange / P buffers keep every LDS region of
-// a step either read or written, never both.
-constexpr int kBufs = 4;
-
+// Work split of the 4 waves of a workgroup (32 heads of one query):
+//  * logits and softmax by head group: wave w takes heads 16*(w&1) .. +16 of
+//    the workgroup's 32 and half (w>>1) of the 512 dims; the two halves add
+//    their partial logits through LDS (fp32 addition commutes: both hold
+//    identical logits) and run the same online softmax;
+//  * PV by output-dim slice: wave w owns dims 128w .. 128w+127 for the 32
+//    heads, so each V^T fragment is widened from FP8 once and feeds two MFMAs
+//    (one per head group); P^T of both head groups comes through LDS.
+// A workgroup is small (4 waves, about 60 KB of LDS) so that two run on
+// every compute unit and each hides the other's barriers and latencies.
 struct __align__(16) Shared {
-  float xc[2][4][2][64][8];                // partial logits [k%2][hg][half][lane][both row blocks]
-  u32x4 pB[2][4][64];                      // P^T operand (RoPE dims) [k%2][hg][lane]
-  u32x4 pnB[2][4][64];                     // (P * scale)^T operand (FP8 dims)
-  float alpha[2][64];                      // per-head rescale of the tile (1 = none)
-  int flag[2][4];                          // head group rescaled this tile
-  float fin[64];                           // per-head output factor (epilogue)
+  float xc[2][2][64][8];                   // partial logits [hg][half][lane][both row blocks]
+  u32x4 pB[2][64];                         // P^T operand (RoPE dims) [hg][lane]
+  u32x4 pnB[2][64];                        // (P * scale)^T operand (FP8 dims)
+  float alpha[kHeads];                     // per-head rescale of the tile (1 = none)
+  int flag[2];                             // head group rescaled this tile
+  float fin[kHeads];                       // per-head output factor (epilogue)
 };
 
-// Softmax state of a logits wave (its lane's head); both halves agree.
+// Online-softmax state of a logits wave (its lane's head); both halves agree.
 struct SoftState {
   float m_run;
   float l_run;                             // lane-partial denominator
 };
 
-// Partial S^T = K Q^T of tile `tl` over this wave's half of the dims, both
-// row blocks, scaled per entry (FP8 part) -> xc slot of this wave.
-__device__ __forceinline__ void qk_partial(const Fp8Tile* tl, float (*xc)[2][64][8],
-                                           const bf16x8* qf, int hg, int half, int g, int li) {
+__device__ __forceinline__ void qk_softmax(const Fp8Tile* tl, Shared* sh, const bf16x8* qf,
+                                           SoftState& S, float c2, int hg, int half, int g,
+                                           int li) {
   const int lane = threadIdx.x & 63;
+  // ---- partial S^T = K Q^T over this half's dims, both row blocks
   float part[8];
 #pragma unroll
   for (int rb = 0; rb < 2; rb++) {
@@ -257,20 +257,12 @@ __device__ __forceinline__ void qk_partial(const Fp8Tile* tl, float (*xc)[2][64]
 #pragma unroll
     for (int i = 0; i < 4; i++) part[rb * 4 + i] = sn[i] * sc[i] + sr[i];
   }
-  f32x4* mine = (f32x4*)xc[hg][half][lane];
+  f32x4* mine = (f32x4*)sh->xc[hg][half][lane];
   mine[0] = (f32x4){part[0], part[1], part[2], part[3]};
   mine[1] = (f32x4){part[4], part[5], part[6], part[7]};
-}
-
-// Online softmax of a tile whose partial logits (both halves) are in xc.
-// Half-0 waves publish P^T, (P * scale)^T, the rescale factors and the
-// head group's rescale flag.
-__device__ __forceinline__ void softmax_tile(const Fp8Tile* tl, const float (*xc)[2][64][8],
-                                             Shared* sh, int buf, SoftState& S, float c2, int hg,
-                                             int half, int g, int li) {
-  const int lane = threadIdx.x & 63;
-  const f32x4* p0 = (const f32x4*)xc[hg][0][lane];
-  const f32x4* p1 = (const f32x4*)xc[hg][1][lane];
+  __syncthreads();
+  const f32x4* p0 = (const f32x4*)sh->xc[hg][0][lane];
+  const f32x4* p1 = (const f32x4*)sh->xc[hg][1][lane];
   const f32x4 a0 = p0[0], a1 = p0[1], b0 = p1[0], b1 = p1[1];
   // entries of lane group g: 4g .. 4g+3 and 16+4g .. 16+4g+3
   const f32x4 sc0 = *(const f32x4*)&tl->scale[g * 4], sc1 = *(const f32x4*)&tl->scale[16 + g * 4];
@@ -307,50 +299,56 @@ __device__ __forceinline__ void softmax_tile(const Fp8Tile* tl, const float (*xc
     pn[i] = p * (i < 4 ? sc0[i] : sc1[i - 4]);
   }
   if (half == 0) {
-    sh->pB[buf][hg][lane] = __builtin_bit_cast(u32x4, pack8(pv));
-    sh->pnB[buf][hg][lane] = __builtin_bit_cast(u32x4, pack8(pn));
-    if (g == 0) sh->alpha[buf][hg * 16 + li] = alpha;
+    sh->pB[hg][lane] = __builtin_bit_cast(u32x4, pack8(pv));
+    sh->pnB[hg][lane] = __builtin_bit_cast(u32x4, pack8(pn));
+    if (g == 0) sh->alpha[hg * 16 + li] = alpha;
     const int any = __builtin_amdgcn_ballot_w64(need) != 0;
-    if (lane == 0) sh->flag[buf][hg] = any;
+    if (lane == 0) sh->flag[hg] = any;
   }
 }
 
-// PV for wave `ds` (dims 64ds .. 64ds+63), all four head groups.  acc[db][ht]:
-// O^T block of dims 64ds + 16db .. +16 x heads 16ht .. +16.
-__device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, int buf,
-                                         f32x4 (*acc)[4], int ds, int g, int li) {
+// PV for wave `ds` (dims 128ds .. 128ds+127), both head groups.  acc[db][ht]:
+// O^T block of dims 128ds + 16db .. +16 x heads 16ht .. +16.  Blocks below
+// dim 448 are FP8 (8-bit transpose reads, widened, times (P * scale)^T);
+// the RoPE blocks (wave 3, blocks 4..7) are bf16 (16-bit transpose reads,
+// times P^T).
+__device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f32x4 (*acc)[2],
+                                         int ds, int g, int li) {
   const int lane = threadIdx.x & 63;
-  const int* fl = sh->flag[buf];
-  if (fl[0] | fl[1] | fl[2] | fl[3]) {
+  if (sh->flag[0] | sh->flag[1]) {
 #pragma unroll
-    for (int ht = 0; ht < 4; ht++) {
-      const float al = sh->alpha[buf][ht * 16 + li];
+    for (int ht = 0; ht < 2; ht++) {
+      const float al = sh->alpha[ht * 16 + li];
 #pragma unroll
-      for (int db = 0; db < 4; db++) acc[db][ht] *= al;
+      for (int db = 0; db < 8; db++) acc[db][ht] *= al;
     }
   }
+  const bf16x8 pn0 = __builtin_bit_cast(bf16x8, sh->pnB[0][lane]);
+  const bf16x8 pn1 = __builtin_bit_cast(bf16x8, sh->pnB[1][lane]);
   // lane group g's k-values are entries {4g..4g+3, 16+4g..16+4g+3}; source
-  // lane s of the group points at the entry k = s/2 (tr8) resp. s/4 (tr16)
+  // lane s of the group points at entry k = s/2 (tr8) resp. s/4 (tr16)
   const int s = li;
-  if (ds < 7) {
-    bf16x8 pnB[4];
+  const int kk8 = s >> 1;
+  const int ent8 = (kk8 < 4) ? (g * 4 + kk8) : (16 + g * 4 + kk8 - 4);
+  const uint8_t* vb8 = tl->rows + ent8 * kRowStride + (s & 1) * 8 + ds * 128;
+  if (ds < 3) {
 #pragma unroll
-    for (int ht = 0; ht < 4; ht++) pnB[ht] = __builtin_bit_cast(bf16x8, sh->pnB[buf][ht][lane]);
-    const int kk8 = s >> 1;
-    const int ent8 = (kk8 < 4) ? (g * 4 + kk8) : (16 + g * 4 + kk8 - 4);
-    const uint8_t* vb8 = tl->rows + ent8 * kRowStride + (s & 1) * 8 + ds * 64;
+    for (int db = 0; db < 8; db++) {
+      u32x2 w = lds_tr8(vb8 + db * 16);
+      const bf16x8 v = widen8(w[0], w[1]);
+      acc[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn0, acc[db][0], 0, 0, 0);
+      acc[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn1, acc[db][1], 0, 0, 0);
+    }
+  } else {
 #pragma unroll
     for (int db = 0; db < 4; db++) {
       u32x2 w = lds_tr8(vb8 + db * 16);
       const bf16x8 v = widen8(w[0], w[1]);
-#pragma unroll
-      for (int ht = 0; ht < 4; ht++)
-        acc[db][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pnB[ht], acc[db][ht], 0, 0, 0);
+      acc[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn0, acc[db][0], 0, 0, 0);
+      acc[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn1, acc[db][1], 0, 0, 0);
     }
-  } else {
-    bf16x8 pB[4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ht++) pB[ht] = __builtin_bit_cast(bf16x8, sh->pB[buf][ht][lane]);
+    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, sh->pB[0][lane]);
+    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, sh->pB[1][lane]);
     const int kk16 = s >> 2;
     const uint8_t* vlo = tl->rows + (g * 4 + kk16) * kRowStride + kNope + (s & 3) * 8;
     const uint8_t* vhi = tl->rows + (16 + g * 4 + kk16) * kRowStride + kNope + (s & 3) * 8;
@@ -359,54 +357,54 @@ __device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, in
       u32x2 lo = lds_tr16(vlo + db * 32);
       u32x2 hi = lds_tr16(vhi + db * 32);
       const bf16x8 v = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-      for (int ht = 0; ht < 4; ht++)
-        acc[db][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pB[ht], acc[db][ht], 0, 0, 0);
+      acc[4 + db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb0, acc[4 + db][0], 0, 0, 0);
+      acc[4 + db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb1, acc[4 + db][1], 0, 0, 0);
     }
   }
 }
 
-// Workgroup -> (query row, split, group of 64 heads).  Workgroups are
+// Workgroup -> (query row, split, group of 32 heads).  Workgroups are
 // dispatched to the 8 XCDs round-robin; consecutive positions within one XCD
-// take consecutive splits, so the splits of one query share an XCD (its L2).
+// take the head groups, then the splits, of one query, so the workgroups
+// that read the same tiles share an XCD (its L2).
 __device__ __forceinline__ bool wg_coords(const AttendArgs& a, int* row, int* split, int* hgrp) {
-  const int n_hg = (a.H + 63) / 64;
+  const int n_hg = (a.H + kHeads - 1) / kHeads;
   const int64_t N = (int64_t)a.B * a.Q * n_hg * a.n_split;
   const int64_t per = (N + 7) / 8;
   const int64_t L = blockIdx.x;
   const int64_t P = (L % 8) * per + L / 8;
   if (P >= N) return false;
-  const int64_t grp = P / a.n_split;
-  *split = (int)(P % a.n_split);
-  *row = (int)(grp / n_hg);
-  *hgrp = (int)(grp % n_hg);
+  *hgrp = (int)(P % n_hg);
+  const int64_t rest = P / n_hg;
+  *split = (int)(rest % a.n_split);
+  *row = (int)(rest / a.n_split);
   return true;
 }
 
 // Split partials of the FP8 path live in the workspace in the accumulator
-// layout, so that a wave stores (and the merge loads) whole contiguous
-// 1 KiB runs: the block of (row, split, head group) holds nh x 512 values
-// ordered [dim slice 8][dim block 4][head tile nht][lane 64][4].
+// layout, so that a wave stores (and the merge loads) whole contiguous runs:
+// the block of (row, split, head group) holds nh x 512 values ordered
+// [dim slice 4][dim block 8][head tile nht][lane 64][4].
 __device__ __forceinline__ int64_t part_block(const AttendArgs& a, int row, int split, int hgrp) {
-  return (((int64_t)row * a.n_split + split) * a.H + hgrp * 64) * (kNope + kRope);
+  return (((int64_t)row * a.n_split + split) * a.H + hgrp * kHeads) * (kNope + kRope);
 }
 
-__global__ void __launch_bounds__(kThreads, 1) k_attend_fp8(AttendArgs a) {
-  __shared__ Fp8Tile tiles[kBufs];
+__global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
+  __shared__ Fp8Tile tiles[2];
   __shared__ Shared sh;
   __shared__ int src[kMaxSplit];
   int row, split, hgrp;
   if (!wg_coords(a, &row, &split, &hgrp)) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int hg = wave & 3;                 // logits: 16-head group within the 64
-  const int half = wave >> 2;              // logits: dims 0..255 or 256..511
+  const int hg = wave & 1;                 // logits: 16-head group within the 32
+  const int half = wave >> 1;              // logits: dims 0..255 or 256..511
   const int b = row / a.Q;
   const int g = lane >> 4;                 // lane group 0..3
   const int li = lane & 15;
-  const int head = hgrp * 64 + hg * 16 + li;
+  const int head = hgrp * kHeads + hg * 16 + li;
   const bool head_ok = head < a.H;
-  const int nht = min(4, (a.H - hgrp * 64) / 16);   // head tiles present (H % 16 == 0)
+  const int nht = min(2, (a.H - hgrp * kHeads) / 16);   // head tiles present (H % 16 == 0)
   const int D = kNope + kRope;
 
   const RowEntries r = row_entries(a, row);
@@ -421,12 +419,11 @@ __global__ void __launch_bounds__(kThreads, 1) k_attend_fp8(AttendArgs a) {
   resolve_sources(a, r, row, e_beg, e_end, src);
   __syncthreads();
 
-  // every stage_load is unconditional (tiles past the split read valid rows
-  // and are masked), so every path through the loop has the same number of
-  // loads in flight and the compiler's waits stay partial (vmcnt(N), N > 0)
-  Stage s0, s1;
-  stage_load(a, src, b, 0, n_local, s0);
-  stage_load(a, src, b, kTile, n_local, s1);
+  // one tile in flight in registers while another is computed; every
+  // stage_load is unconditional (tiles past the split read valid rows and
+  // are masked), so each step issues the same loads
+  Stage st;
+  stage_load(a, src, b, 0, n_local, st);
 
   // Q^T fragments of this wave's half: k-step ks covers dims
   // 256*half + 32ks .. +31 (the RoPE dims are k-steps 6, 7 of half 1); the
@@ -442,44 +439,30 @@ __global__ void __launch_bounds__(kThreads, 1) k_attend_fp8(AttendArgs a) {
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  f32x4 acc[4][4];
+  f32x4 acc[8][2];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < 8; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; j++) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
   SoftState S;
   S.m_run = -INFINITY;
   S.l_run = 0.0f;
   const float c2 = a.sm_scale * kLog2e;
 
-  stage_store(&tiles[0], s0);
-  stage_load(a, src, b, 2 * kTile, n_local, s0);
+  stage_store(&tiles[0], st);
+  stage_load(a, src, b, kTile, n_local, st);
   __syncthreads();
 
-  // step k: partial logits of tile k, softmax of tile k-1, PV of tile k-2;
-  // tile k+1 (register set (k+1)%2) moves into LDS and that set is refilled
-  // with tile k+3.  Steps go in pairs (fixed register sets); all phase
-  // conditions are uniform scalar branches and every step issues the same
-  // loads.
-#define V4A_STEP(K, SET)                                                              \
-  {                                                                                   \
-    const int k_ = (K);                                                               \
-    if (k_ < n_tiles)                                                                 \
-      qk_partial(&tiles[k_ % kBufs], sh.xc[k_ & 1], qf, hg, half, g, li);             \
-    if (k_ >= 1 && k_ <= n_tiles)                                                     \
-      softmax_tile(&tiles[(k_ - 1) % kBufs], sh.xc[(k_ - 1) & 1], &sh, (k_ - 1) & 1,  \
-                   S, c2, hg, half, g, li);                                           \
-    if (k_ >= 2 && k_ - 2 < n_tiles)                                                  \
-      pv_slice(&tiles[(k_ - 2) % kBufs], &sh, (k_ - 2) & 1, acc, wave, g, li);        \
-    stage_store(&tiles[(k_ + 1) % kBufs], SET);                                       \
-    stage_load(a, src, b, (k_ + 3) * kTile, n_local, SET);                            \
-    __syncthreads();                                                                  \
+  // step t: logits + softmax of tile t, PV of tile t, tile t+1 into LDS, the
+  // register set refilled with tile t+2
+  for (int t = 0; t < n_tiles; t++) {
+    qk_softmax(&tiles[t & 1], &sh, qf, S, c2, hg, half, g, li);
+    __syncthreads();
+    pv_slice(&tiles[t & 1], &sh, acc, wave, g, li);
+    stage_store(&tiles[(t + 1) & 1], st);
+    stage_load(a, src, b, (t + 2) * kTile, n_local, st);
+    __syncthreads();
   }
-  for (int k = 0; k < n_tiles + 2; k += 2) {
-    V4A_STEP(k, s1)
-    V4A_STEP(k + 1, s0)
-  }
-#undef V4A_STEP
 
   // ---- epilogue: the logits waves of half 0 publish each head's factor
   float l_tot = S.l_run + __shfl_xor(S.l_run, 16, 64);
@@ -504,15 +487,16 @@ __global__ void __launch_bounds__(kThreads, 1) k_attend_fp8(AttendArgs a) {
     sh.fin[hg * 16 + li] = f;
   }
   __syncthreads();
-  // PV wave `wave` holds O^T dims 64*wave + 16db + 4g + i of head 16ht + li
+  // PV wave `wave` holds O^T dims 128*wave + 16db + 4g + i of head 16ht + li
   if (a.n_split == 1) {
 #pragma unroll
-    for (int ht = 0; ht < 4; ht++) {
+    for (int ht = 0; ht < 2; ht++) {
       if (ht >= nht) break;
       const float f = sh.fin[ht * 16 + li];
-      const int64_t ob = ((int64_t)row * a.H + hgrp * 64 + ht * 16 + li) * D + wave * 64 + g * 4;
+      const int64_t ob =
+          ((int64_t)row * a.H + hgrp * kHeads + ht * 16 + li) * D + wave * 128 + g * 4;
 #pragma unroll
-      for (int db = 0; db < 4; db++) {
+      for (int db = 0; db < 8; db++) {
         const f32x4 o = acc[db][ht] * f;
         if (a.out_bf16) {
           const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
@@ -526,14 +510,14 @@ __global__ void __launch_bounds__(kThreads, 1) k_attend_fp8(AttendArgs a) {
   } else {
     uint16_t* po = (uint16_t*)a.part_o + part_block(a, row, split, hgrp);
 #pragma unroll
-    for (int db = 0; db < 4; db++) {
+    for (int db = 0; db < 8; db++) {
 #pragma unroll
-      for (int ht = 0; ht < 4; ht++) {
+      for (int ht = 0; ht < 2; ht++) {
         if (ht >= nht) break;
         const f32x4 o = acc[db][ht] * sh.fin[ht * 16 + li];
         const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
         const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-        *(u32x2*)(po + (((int64_t)(wave * 4 + db) * nht + ht) * 64 + lane) * 4) = (u32x2){lo, hi};
+        *(u32x2*)(po + (((int64_t)(wave * 8 + db) * nht + ht) * 64 + lane) * 4) = (u32x2){lo, hi};
       }
     }
   }
@@ -718,12 +702,12 @@ __global__ void __launch_bounds__(256) k_merge(AttendArgs a) {
 }
 
 // FP8 path: partials in the accumulator layout (bf16).  One workgroup per
-// (query, head group of 64, 1/32 of the block); thread t owns 4
-// consecutive values of the block, i.e. 4 dims of one head.
+// (query, head group of 32, 1/16 of the block); thread t owns 4 consecutive
+// values of the block, i.e. 4 dims of one head.
 __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
   const int row = blockIdx.x, hgrp = blockIdx.y;
   const int D = kNope + kRope;
-  const int nht = min(4, (a.H - hgrp * 64) / 16);
+  const int nht = min(2, (a.H - hgrp * kHeads) / 16);
   const int n_vals = nht * 16 * D;                     // values in the block
   const int j = (blockIdx.z * 256 + threadIdx.x) * 4;  // first owned value
   if (j >= n_vals) return;
@@ -731,8 +715,8 @@ __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
   const int q4 = j >> 2;
   const int ln = q4 & 63;
   const int ht = (q4 >> 6) % nht;
-  const int sb = (q4 >> 6) / nht;                      // dim slice * 4 + dim block
-  const int head = hgrp * 64 + ht * 16 + (ln & 15);
+  const int sb = (q4 >> 6) / nht;                      // dim slice * 8 + dim block
+  const int head = hgrp * kHeads + ht * 16 + (ln & 15);
   const int d0 = sb * 16 + (ln >> 4) * 4;
   // (m, l) of every split for this head: independent loads, issued together
   const f32x2* ml = (const f32x2*)a.part_ml + (int64_t)row * a.n_split * a.H + head;
@@ -819,7 +803,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st, const KernelEvents
   const int rows = a.B * a.Q;
   if (rows == 0) return hipSuccess;
   if (a.fp8) {
-    const int64_t N = (int64_t)rows * a.n_split * ((a.H + 63) / 64);
+    const int64_t N = (int64_t)rows * a.n_split * ((a.H + kHeads - 1) / kHeads);
     const int64_t per = (N + 7) / 8;
     if (ev)
       hipExtLaunchKernelGGL(k_attend_fp8, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st, ev->start,
@@ -837,9 +821,10 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st, const KernelEvents
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   if (a.fp8) {
-    // 64 heads x 512 dims / (256 threads x 4 values) = 32 workgroups per block
-    const int parts = (64 * (kNope + kRope)) / (256 * 4);
-    hipLaunchKernelGGL(k_merge_tiled, dim3(rows, (a.H + 63) / 64, parts), dim3(256), 0, st, a);
+    // 32 heads x 512 dims / (256 threads x 4 values) = 16 workgroups per block
+    const int parts = (kHeads * (kNope + kRope)) / (256 * 4);
+    hipLaunchKernelGGL(k_merge_tiled, dim3(rows, (a.H + kHeads - 1) / kHeads, parts), dim3(256), 0,
+                       st, a);
   } else {
     hipLaunchKernelGGL(k_merge, dim3(rows, (a.H + kMergeHeads - 1) / kMergeHeads), dim3(256), 0, st,
                        a);
