@@ -383,6 +383,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk leg")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy 10 times (the reference kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
     args = ap.parse_args()
 
     def log(msg):
@@ -396,6 +399,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        x = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(10):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": x.numel() * 4,
+                          "bytes_written": y.numel() * 4, "launches": 10}))
+        return
     import long_context_attention_v4attn_amd as v4
     from long_context_attention_v4attn_amd import synth
     v4.load()
