@@ -702,37 +702,49 @@ __global__ void __launch_bounds__(256) k_merge(AttendArgs a) {
 }
 
 // FP8 path: partials in the accumulator layout (bf16).  One workgroup per
-// (query, head group of 32, 1/16 of the block); thread t owns 4 consecutive
-// values of the block, i.e. 4 dims of one head.
+// (query, head group of 32, 1/64 of the block): 64 groups of 4 consecutive
+// values (4 dims of one head) x 4 split phases; phase p takes the splits
+// s = p, p + 4, ... and the phases combine their maxima, then their weighted
+// sums, through LDS in fixed order (deterministic).
+constexpr int kMergePhases = 4;
+
 __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
+  __shared__ float red[kMergePhases][64][6];
   const int row = blockIdx.x, hgrp = blockIdx.y;
   const int D = kNope + kRope;
   const int nht = min(2, (a.H - hgrp * kHeads) / 16);
   const int n_vals = nht * 16 * D;                     // values in the block
-  const int j = (blockIdx.z * 256 + threadIdx.x) * 4;  // first owned value
-  if (j >= n_vals) return;
+  const int vg = threadIdx.x & 63, ph = threadIdx.x >> 6;
+  const int j = (blockIdx.z * 64 + vg) * 4;            // first owned value
+  const bool active = j < n_vals;
   // decode [dim slice][dim block][head tile][lane][4]
-  const int q4 = j >> 2;
+  const int q4 = (active ? j : 0) >> 2;
   const int ln = q4 & 63;
   const int ht = (q4 >> 6) % nht;
   const int sb = (q4 >> 6) / nht;                      // dim slice * 8 + dim block
   const int head = hgrp * kHeads + ht * 16 + (ln & 15);
   const int d0 = sb * 16 + (ln >> 4) * 4;
-  // (m, l) of every split for this head: independent loads, issued together
   const f32x2* ml = (const f32x2*)a.part_ml + (int64_t)row * a.n_split * a.H + head;
+  // ---- the maximum over all splits (and the sink)
+  float M = -INFINITY;
+#pragma unroll 4
+  for (int s = ph; s < a.n_split; s += kMergePhases) M = fmaxf(M, ml[(int64_t)s * a.H][0]);
+  red[ph][vg][0] = M;
+  __syncthreads();
   const float z2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
-  float M = z2;
-#pragma unroll 8
-  for (int s = 0; s < a.n_split; s++) M = fmaxf(M, ml[(int64_t)s * a.H][0]);
+  M = z2;
+#pragma unroll
+  for (int p = 0; p < kMergePhases; p++) M = fmaxf(M, red[p][vg][0]);
+  // ---- this phase's weighted sums
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   if (M != -INFINITY) {
-    den = z2 == -INFINITY ? 0.f : exp2f(z2 - M);
-    const uint16_t* po = (const uint16_t*)a.part_o + part_block(a, row, 0, hgrp) + j;
+    // (an inactive thread reads the block's first values: always in bounds)
+    const uint16_t* po = (const uint16_t*)a.part_o + part_block(a, row, 0, hgrp) + (active ? j : 0);
     const int64_t sstride = (int64_t)a.H * D;
     // an empty split has m = -inf, hence weight 0, and zero partials
 #pragma unroll 4
-    for (int s = 0; s < a.n_split; s++) {
+    for (int s = ph; s < a.n_split; s += kMergePhases) {
       const f32x2 v_ml = ml[(int64_t)s * a.H];
       const u32x2 v = *(const u32x2*)(po + s * sstride);
       const float w = v_ml[1] * exp2f(v_ml[0] - M);
@@ -743,14 +755,27 @@ __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
       acc[3] += w * bf16_bits_to_f32(v[1] >> 16);
     }
   }
+  red[ph][vg][1] = den;
+#pragma unroll
+  for (int i = 0; i < 4; i++) red[ph][vg][2 + i] = acc[i];
+  __syncthreads();
+  if (ph != 0 || !active) return;
+  den = (M == -INFINITY || z2 == -INFINITY) ? 0.f : exp2f(z2 - M);
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < kMergePhases; p++) {
+    den += red[p][vg][1];
+#pragma unroll
+    for (int i = 0; i < 4; i++) o[i] += red[p][vg][2 + i];
+  }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   const int64_t oi = ((int64_t)row * a.H + head) * D + d0;
   if (a.out_bf16) {
-    const uint32_t lo = f32_to_bf16_bits(acc[0] * inv) | (f32_to_bf16_bits(acc[1] * inv) << 16);
-    const uint32_t hi = f32_to_bf16_bits(acc[2] * inv) | (f32_to_bf16_bits(acc[3] * inv) << 16);
+    const uint32_t lo = f32_to_bf16_bits(o[0] * inv) | (f32_to_bf16_bits(o[1] * inv) << 16);
+    const uint32_t hi = f32_to_bf16_bits(o[2] * inv) | (f32_to_bf16_bits(o[3] * inv) << 16);
     *(u32x2*)((uint16_t*)a.out + oi) = (u32x2){lo, hi};
   } else {
-    *(f32x4*)((float*)a.out + oi) = (f32x4){acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *(f32x4*)((float*)a.out + oi) = (f32x4){o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
   }
 }
 
@@ -765,8 +790,11 @@ void attend_plan(AttendArgs& a, int64_t n_entries_max) {
   const int D = a.d_nope + a.d_rope;
   a.part_bf16 = a.fp8;
   a.f32_heads = a.fp8 ? 64 : (a.H < 4096 / D ? a.H : (4096 / D > 0 ? 4096 / D : 1));
-  int64_t per = (n_entries_max + 15) / 16;
-  if (per < 128) per = 128;
+  // short lists (CSA: k + window) split finer than long ones (HCA), so that
+  // a small batch still spreads over the chip; the size depends on the
+  // per-query bound only
+  int64_t per = n_entries_max <= 4096 ? (n_entries_max + 47) / 48 : (n_entries_max + 15) / 16;
+  if (per < 64) per = 64;
   per = (per + 63) / 64 * 64;               // whole tile pairs
   if (per > kMaxSplit) per = kMaxSplit;
   a.split_size = (int)per;
@@ -821,8 +849,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st, const KernelEvents
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   if (a.fp8) {
-    // 32 heads x 512 dims / (256 threads x 4 values) = 16 workgroups per block
-    const int parts = (kHeads * (kNope + kRope)) / (256 * 4);
+    // 32 heads x 512 dims / (64 value groups x 4 values) = 64 workgroups per block
+    const int parts = (kHeads * (kNope + kRope)) / (64 * 4);
     hipLaunchKernelGGL(k_merge_tiled, dim3(rows, (a.H + kHeads - 1) / kHeads, parts), dim3(256), 0,
                        st, a);
   } else {

@@ -140,6 +140,32 @@ __device__ __forceinline__ void hist_flush(uint32_t* lh, uint32_t* gh, int nb) {
 }
 
 // ---------------------------------------------------------------- FP4 scan
+
+// x + y after swapping x's lanes 32..63 with y's lanes 0..31: lanes 0..31
+// hold x summed over lane groups {0, 2} resp. {1, 3}, lanes 32..63 the same
+// for y.
+// (The optimiser of this toolchain folds the two results of a swap into one
+// value when both feed the same add; the empty asm statement -- no
+// instruction, it only marks both registers as read and written -- keeps
+// them apart.)
+__device__ __forceinline__ float swap_add32(float x, float y) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, y), false, false);
+  uint32_t lo = r[0], hi = r[1];
+  __asm__ volatile("" : "+v"(lo), "+v"(hi));
+  return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
+// The same within each half: swaps x's lanes 16..31 (48..63) with y's lanes
+// 0..15 (32..47).
+__device__ __forceinline__ float swap_add16(float x, float y) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, y), false, false);
+  uint32_t lo = r[0], hi = r[1];
+  __asm__ volatile("" : "+v"(lo), "+v"(hi));
+  return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
 constexpr int kWaveTiles = 16;             // 16 tiles x 16 blocks per wave and iteration
 constexpr int kIterBlocks = 4 * kWaveTiles * 16;   // 1024 blocks per workgroup iteration
 
@@ -162,29 +188,45 @@ __device__ __forceinline__ void load_keys(const uint8_t* kc, const uint8_t* ks, 
   }
 }
 
+// Scores of the wave's kWaveTiles tiles, four tiles at a time: per tile one
+// MFMA per 16 index heads and the lane's ReLU * w partial over its four
+// heads; then the sums over the four lane groups of four tiles at once with
+// two lane-swap steps, which leave lane group g with the total of tile g --
+// so each lane owns one score: blocks blk0 + 16 t4 + lane, stored and
+// histogrammed by all 64 lanes together.
 __device__ __forceinline__ void score_tiles(const KeyTiles& kt, const i32x8* qa, const int* qs,
                                             float (*wv)[4], int HT, int64_t blk0, int64_t nv,
-                                            int g, int li, float* out, uint32_t* lh) {
+                                            int lane, float* out, uint32_t* lh) {
 #pragma unroll
-  for (int t = 0; t < kWaveTiles; t++) {
-    const int64_t blk = blk0 + t * 16 + li;
-    i32x8 kb = {(int)kt.v[t][0], (int)kt.v[t][1], (int)kt.v[t][2], (int)kt.v[t][3], 0, 0, 0, 0};
-    float part = 0.0f;
+  for (int t4 = 0; t4 < kWaveTiles; t4 += 4) {
+    float part[4];
 #pragma unroll
-    for (int ht = 0; ht < 4; ht++) {
-      if (ht < HT) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb, acc, 4, 4, 0, qs[ht], 0,
-                                                               kt.sc[t]);
+    for (int u = 0; u < 4; u++) {
+      const int t = t4 + u;
+      const i32x8 kb = {(int)kt.v[t][0], (int)kt.v[t][1], (int)kt.v[t][2], (int)kt.v[t][3],
+                        0, 0, 0, 0};
+      float p = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; i++) part += wv[ht][i] * fmaxf(acc[i], 0.0f);
+      for (int ht = 0; ht < 4; ht++) {
+        if (ht < HT) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb, acc, 4, 4, 0, qs[ht],
+                                                                 0, kt.sc[t]);
+#pragma unroll
+          for (int i = 0; i < 4; i++) p += wv[ht][i] * fmaxf(acc[i], 0.0f);
+        }
       }
+      part[u] = p;
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    if (g == 0 && blk < nv) {
-      out[blk] = part;
-      atomicAdd(&lh[score_key(part) >> kSh1], 1u);
+    // lanes 0..31 / 32..63: tiles 0, 1 / 2, 3 summed over lane groups {0,2}, {1,3}
+    const float h0 = swap_add32(part[0], part[2]);
+    const float h1 = swap_add32(part[1], part[3]);
+    // lane group g: tile g
+    const float sc = swap_add16(h0, h1);
+    const int64_t blk = blk0 + t4 * 16 + lane;
+    if (blk < nv) {
+      out[blk] = sc;
+      atomicAdd(&lh[score_key(sc) >> kSh1], 1u);
     }
   }
 }
@@ -234,10 +276,10 @@ __global__ void __launch_bounds__(256) k_score_mx(IndexArgs a) {
   for (int it = 0; it < iters; it += 2) {
     const int64_t b0 = wblk + (int64_t)it * kIterBlocks;
     if (it + 1 < iters) load_keys(kc, ks, b0 + kIterBlocks, nv, g, li, k1);
-    score_tiles(k0, qa, qs, wv, HT, b0, nv, g, li, out, lh);
+    score_tiles(k0, qa, qs, wv, HT, b0, nv, lane, out, lh);
     if (it + 1 >= iters) break;
     if (it + 2 < iters) load_keys(kc, ks, b0 + 2 * kIterBlocks, nv, g, li, k0);
-    score_tiles(k1, qa, qs, wv, HT, b0 + kIterBlocks, nv, g, li, out, lh);
+    score_tiles(k1, qa, qs, wv, HT, b0 + kIterBlocks, nv, lane, out, lh);
   }
   hist_flush(lh, a.hist + (size_t)row * kBins1, kBins1);
 }
@@ -254,31 +296,6 @@ __global__ void __launch_bounds__(256) k_score_mx(IndexArgs a) {
 // that + 2.  Per-query first-digit histograms in LDS, flushed once.
 constexpr int kQT = 8;
 constexpr int kQRange = 16384;
-
-// x + y after swapping x's lanes 32..63 with y's lanes 0..31: lanes 0..31
-// hold x summed over lane groups {0, 2} resp. {1, 3}, lanes 32..63 the same
-// for y.
-// (The optimiser of this toolchain folds the two results of a swap into one
-// value when both feed the same add; the empty asm statement -- no
-// instruction, it only marks both registers as read and written -- keeps
-// them apart.)
-__device__ __forceinline__ float swap_add32(float x, float y) {
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                            __builtin_bit_cast(uint32_t, y), false, false);
-  uint32_t lo = r[0], hi = r[1];
-  __asm__ volatile("" : "+v"(lo), "+v"(hi));
-  return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
-}
-
-// The same within each half: swaps x's lanes 16..31 (48..63) with y's lanes
-// 0..15 (32..47).
-__device__ __forceinline__ float swap_add16(float x, float y) {
-  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
-                                            __builtin_bit_cast(uint32_t, y), false, false);
-  uint32_t lo = r[0], hi = r[1];
-  __asm__ volatile("" : "+v"(lo), "+v"(hi));
-  return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
-}
 
 struct QFrag {
   u32x4 v;

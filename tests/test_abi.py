@@ -52,7 +52,7 @@ def test_workspace_sizes(clib):
     n = B.v4attn_workspace_bytes(B.OP_INDEX_TOPK, 4, 1, 16, 128, 262144, 2048, 0)
     assert n >= 4 * 262144 * 4
     # a short entry list needs no split partials
-    assert B.v4attn_workspace_bytes(B.OP_CSA_ATTEND, 1, 1, 64, 512, 0, 64, 64) == 0
+    assert B.v4attn_workspace_bytes(B.OP_CSA_ATTEND, 1, 1, 64, 512, 0, 32, 32) == 0
     # a long one does, and the need does not depend on B per query
     a = B.v4attn_workspace_bytes(B.OP_HCA_ATTEND, 1, 1, 64, 512, 8192, 128, 128)
     b = B.v4attn_workspace_bytes(B.OP_HCA_ATTEND, 16, 1, 64, 512, 8192, 128, 128)
