@@ -49,6 +49,7 @@ constexpr int kCandCap = 16384;            // candidate slots per query
 constexpr int kFThreads = 256;
 constexpr int kPer = 16;                   // consecutive scores per filter thread
 constexpr int kFilterChunk = kFThreads * kPer;   // scores per filter workgroup
+static_assert(kBins1 == kFThreads, "one first-digit bin per filter thread");
 constexpr int kCtr = 8;                    // counters per query
 __host__ __device__ inline int64_t score_ld(int64_t cap) { return (cap + 63) / 64 * 64; }
 __host__ __device__ inline int64_t n_chunks(int64_t cap) { return (cap + kFilterChunk - 1) / kFilterChunk; }
@@ -496,19 +497,29 @@ __device__ __forceinline__ uint64_t sel_key(uint32_t k32, int64_t i) {
 // loads are issued together (the score rows are padded to 64 floats, and a
 // thread whose group starts past nv reads its row's first group instead).
 // Returns the number of the group's ids below nv.
-__device__ __forceinline__ int load_group(const IndexArgs& a, int row, int64_t nv, int chunk,
-                                          uint32_t* k32, int64_t* i0) {
-  const int64_t g0 = (int64_t)chunk * kFilterChunk + threadIdx.x * kPer;
-  *i0 = g0;
-  const int64_t rem = nv - g0;
-  const int n_in = rem <= 0 ? 0 : (rem >= kPer ? kPer : (int)rem);
-  const float* sc = a.scores + (size_t)row * a.sc_ld + (n_in ? g0 : 0);
+
+// This thread's kPer consecutive scores of filter chunk `chunk`, in two
+// halves so that the loads can be issued before anything else the kernel
+// waits for: issue_group needs no visible count (the score rows are padded to
+// 64 floats; a group past the padded row reads the row's first group),
+// finish_group converts them to keys and returns how many are below nv.
+struct Group {
   f32x4 v[kPer / 4];
+  int64_t g0;
+};
+
+__device__ __forceinline__ void issue_group(const IndexArgs& a, int row, int chunk, Group& gr) {
+  gr.g0 = (int64_t)chunk * kFilterChunk + threadIdx.x * kPer;
+  const float* sc = a.scores + (size_t)row * a.sc_ld + (gr.g0 < a.sc_ld ? gr.g0 : 0);
 #pragma unroll
-  for (int j = 0; j < kPer / 4; j++) v[j] = *(const f32x4*)(sc + 4 * j);
+  for (int j = 0; j < kPer / 4; j++) gr.v[j] = *(const f32x4*)(sc + 4 * j);
+}
+
+__device__ __forceinline__ int finish_group(const Group& gr, int64_t nv, uint32_t* k32) {
+  const int64_t rem = nv - gr.g0;
 #pragma unroll
-  for (int j = 0; j < kPer; j++) k32[j] = score_key(v[j / 4][j % 4]);
-  return n_in;
+  for (int j = 0; j < kPer; j++) k32[j] = score_key(gr.v[j / 4][j % 4]);
+  return rem <= 0 ? 0 : (rem >= kPer ? kPer : (int)rem);
 }
 
 // Common head of the filter kernels: the query's visible count, its k', and
@@ -539,24 +550,34 @@ __device__ __forceinline__ bool filter_head(const IndexArgs& a, int row, uint32_
 __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
   __shared__ uint32_t lh[kBins2];
   __shared__ uint32_t tmp[kFThreads / 64];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above;
   const int row = blockIdx.y;
-  FilterRow fr;
-  if (!filter_head(a, row, lh, tmp, &fr)) {
-    const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
-    if (blockIdx.x == 0 && nv <= a.k) {    // everything visible is selected
+  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
+  const int kk = (int)(nv < a.k ? nv : a.k);
+  if (kk == nv) {                          // everything visible is selected
+    if (blockIdx.x == 0) {
       int32_t* out = a.topk + (size_t)row * a.k;
       for (int64_t i = threadIdx.x; i < a.k; i += blockDim.x) out[i] = i < nv ? (int32_t)i : -1;
     }
     return;
   }
-  uint32_t k32[kPer];
-  int64_t i0;
-  const int n_in = load_group(a, row, fr.nv, blockIdx.x, k32, &i0);
+  if ((int64_t)blockIdx.x * kFilterChunk >= nv) return;
+  // all global loads first: the first histogram, then this thread's scores
+  const uint32_t h1 = a.hist[(size_t)row * kBins1 + threadIdx.x];   // kBins1 == kFThreads
+  Group gr;
+  issue_group(a, row, blockIdx.x, gr);
+  lh[threadIdx.x] = h1;
+  __syncthreads();
+  find_bin(lh, kBins1, (uint32_t)kk, tmp, &s_bin, &s_above);
+  const uint32_t b1 = (uint32_t)s_bin;
   for (int i = threadIdx.x; i < kBins2; i += blockDim.x) lh[i] = 0u;
+  uint32_t k32[kPer];
+  const int n_in = finish_group(gr, nv, k32);
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kPer; j++)
-    if (j < n_in && (k32[j] >> kSh1) == fr.b1) atomicAdd(&lh[(k32[j] >> kSh2) & (kBins2 - 1)], 1u);
+    if (j < n_in && (k32[j] >> kSh1) == b1) atomicAdd(&lh[(k32[j] >> kSh2) & (kBins2 - 1)], 1u);
   hist_flush(lh, a.hist2 + (size_t)row * kBins2, kBins2);
 }
 
@@ -693,17 +714,30 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   __shared__ int s_bin;
   __shared__ uint32_t s_above, cand_n, s_base;
   const int row = blockIdx.y;
-  FilterRow fr;
-  if (!filter_head(a, row, lh, tmp, &fr)) return;
-  uint32_t k32[kPer];
-  int64_t i0;
-  const int n_in = load_group(a, row, fr.nv, blockIdx.x, k32, &i0);
-  const uint32_t* gh2 = a.hist2 + (size_t)row * kBins2;
-  for (int i = threadIdx.x; i < kBins2; i += blockDim.x) lh[i] = gh2[i];
+  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
+  const int kk = (int)(nv < a.k ? nv : a.k);
+  if (kk == nv || (int64_t)blockIdx.x * kFilterChunk >= nv) return;
+  // all global loads first: both histograms, then this thread's scores
+  const uint32_t h1 = a.hist[(size_t)row * kBins1 + threadIdx.x];   // kBins1 == kFThreads
+  constexpr int kPer2 = kBins2 / kFThreads;                          // 8
+  const u32x4* gh2 = (const u32x4*)(a.hist2 + (size_t)row * kBins2 + threadIdx.x * kPer2);
+  const u32x4 h2a = gh2[0], h2b = gh2[1];
+  Group gr;
+  issue_group(a, row, blockIdx.x, gr);
+  lh[threadIdx.x] = h1;
   if (threadIdx.x == 0) cand_n = 0;
   __syncthreads();
-  find_bin(lh, kBins2, (uint32_t)fr.kk - fr.above1, tmp, &s_bin, &s_above);
-  const uint32_t b12 = (fr.b1 << 11) | (uint32_t)s_bin;   // key bits 31..13
+  find_bin(lh, kBins1, (uint32_t)kk, tmp, &s_bin, &s_above);
+  const uint32_t b1 = (uint32_t)s_bin, above1 = s_above;
+  *(u32x4*)&lh[threadIdx.x * kPer2] = h2a;
+  *(u32x4*)&lh[threadIdx.x * kPer2 + 4] = h2b;
+  __syncthreads();
+  find_bin(lh, kBins2, (uint32_t)kk - above1, tmp, &s_bin, &s_above);
+  const uint32_t b12 = (b1 << 11) | (uint32_t)s_bin;   // key bits 31..13
+  uint32_t k32[kPer];
+  const int n_in = finish_group(gr, nv, k32);
+  const int64_t i0 = gr.g0;
+  FilterRow fr{nv, kk, b1, above1};
   uint32_t* ctr = a.ctr + (size_t)row * kCtr;
   uint64_t* cand = a.cand + (size_t)row * kCandCap;
   CandList cnd{cand_buf, &cand_n};
@@ -744,15 +778,21 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   if (blockIdx.x == 0)
     for (int i = kk + threadIdx.x; i < a.k; i += blockDim.x) out[i] = -1;
   if ((int64_t)blockIdx.x * kFilterChunk >= nv) return;
-  uint32_t k32[kPer];
-  int64_t i0;
-  const int n_in = load_group(a, row, nv, blockIdx.x, k32, &i0);
+  // all global loads first: counters, the first candidates (speculatively:
+  // the list always has kCandCap slots), the earlier chunks' counts, scores
   const uint32_t* ctr = a.ctr + (size_t)row * kCtr;
   const uint32_t n_cand = ctr[0], b12 = ctr[2], need = ctr[3];
   const uint64_t* gc = a.cand + (size_t)row * kCandCap;
+  const uint64_t c_first = gc[threadIdx.x];
+  const uint32_t* cc = a.chunk + (size_t)row * n_chunks(a.cap);
+  const uint32_t cc_first = (int)threadIdx.x < (int)blockIdx.x ? cc[threadIdx.x] : 0u;
+  Group gr;
+  issue_group(a, row, blockIdx.x, gr);
   const bool in_lds = n_cand <= (uint32_t)kEmitCand;
-  if (in_lds)
-    for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) cl[i] = gc[i];
+  if (in_lds) {
+    if (threadIdx.x < n_cand) cl[threadIdx.x] = c_first;
+    for (uint32_t i = threadIdx.x + blockDim.x; i < n_cand; i += blockDim.x) cl[i] = gc[i];
+  }
   __syncthreads();
   const CandSrc src{in_lds ? cl : gc, n_cand, a.scores + (size_t)row * a.sc_ld, nv, b12,
                     n_cand <= (uint32_t)kCandCap};
@@ -760,9 +800,8 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   // offset of this chunk: ids above the bin in earlier chunks, plus the
   // candidates >= T with lower ids
   const int64_t c0 = (int64_t)blockIdx.x * kFilterChunk;
-  uint32_t before = 0;
-  const uint32_t* cc = a.chunk + (size_t)row * n_chunks(a.cap);
-  for (int c = threadIdx.x; c < (int)blockIdx.x; c += blockDim.x) before += cc[c];
+  uint32_t before = cc_first;
+  for (int c = threadIdx.x + blockDim.x; c < (int)blockIdx.x; c += blockDim.x) before += cc[c];
   const int64_t n = src.size();
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
     uint64_t key;
@@ -771,6 +810,9 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
       before += id < c0 ? 1u : 0u;
     }
   }
+  uint32_t k32[kPer];
+  const int n_in = finish_group(gr, nv, k32);
+  const int64_t i0 = gr.g0;
   const uint32_t base = block_sum(before, tmp);
   uint32_t sel = 0;
 #pragma unroll
