@@ -14,9 +14,10 @@ Inputs are synthetic and seeded (long_context_attention_v4attn_amd.synth),
 uploaded once and quantised to the cache formats on the GPU by the library
 (v4attn_compress with m = 1).  `--replicas` address-distinct copies of every
 cache are cycled so that no step re-reads data another recent step left in the
-256 MB Infinity Cache.  Each layer of a step is one HIP graph per replica; the
+256 MB Infinity Cache.  Each layer is one HIP graph holding that layer's
+calls for all replicas in turn (one graph launch per `--replicas` steps); the
 timed loop replays K steps with a HIP event between the two layers of every
-step (torch's current stream, which is the stream the library launches on).
+round (torch's current stream, which is the stream the library launches on).
 After the timed loop, each call's graphs are replayed back to back for a
 per-call breakdown, and the dominant kernel of each call is timed live with
 HIP events that the library records immediately around that kernel
@@ -378,7 +379,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--quiet", action="store_true")
@@ -437,8 +438,11 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    # one graph per replica and layer: the CSA layer (index_topk + csa_attend)
-    # and the HCA layer (hca_attend); also per-call graphs for the breakdown
+    R = len(calls)
+    # one graph per layer holding that layer's calls for every replica in
+    # turn (R consecutive steps' worth, one graph launch per R steps, as a
+    # serving loop would capture many layers at once); the same per call for
+    # the breakdown
     if not args.no_graph:
         cap_stream = torch.cuda.Stream()
 
@@ -449,51 +453,53 @@ def main():
                     f()
             return g.replay
 
-        layer = [(capture(cs[:2]), capture(cs[2:])) for cs in calls]
-        single = [[capture([f]) for f in cs] for cs in calls]
+        csa_layer = capture([f for cs in calls for f in cs[:2]])
+        hca_layer = capture([cs[2] for cs in calls])
+        per_call_g = [capture([cs[i] for cs in calls]) for i in range(3)]
         torch.cuda.synchronize()
     else:
-        layer = [((lambda cs=cs: (cs[0](), cs[1]())), cs[2]) for cs in calls]
-        single = calls
-    R = len(layer)
+        csa_layer = lambda: [f() for cs in calls for f in cs[:2]]
+        hca_layer = lambda: [cs[2]() for cs in calls]
+        per_call_g = [(lambda i=i: [cs[i]() for cs in calls]) for i in range(3)]
 
-    for s in range(args.warmup):
-        layer[s % R][0]()
-        layer[s % R][1]()
+    for _ in range(max(1, args.warmup // R)):
+        csa_layer()
+        hca_layer()
     torch.cuda.synchronize()
 
-    # ---- the timed region: K steps (CSA layer, then HCA layer), events
-    # between the two layers of every step
-    K = args.steps
+    # ---- the timed region: K steps = K / R rounds of (the CSA layer for the
+    # R replicas, then the HCA layer for the R replicas), events between them
+    K = -(-args.steps // R) * R
+    rounds = K // R
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K + 1)]
+          for _ in range(rounds + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(K):
+    for s in range(rounds):
         ev[s][0].record(stream)
-        layer[s % R][0]()
+        csa_layer()
         ev[s][1].record(stream)
-        layer[s % R][1]()
-    ev[K][0].record(stream)
+        hca_layer()
+    ev[rounds][0].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_csa = sum(ev[s][0].elapsed_time(ev[s][1]) for s in range(K)) / K * 1e-3     # s
-    t_hca = sum(ev[s][1].elapsed_time(ev[s + 1][0]) for s in range(K)) / K * 1e-3
-    t_gpu = ev[0][0].elapsed_time(ev[K][0]) / K * 1e-3
+    t_csa = sum(ev[s][0].elapsed_time(ev[s][1]) for s in range(rounds)) / K * 1e-3     # s per step
+    t_hca = sum(ev[s][1].elapsed_time(ev[s + 1][0]) for s in range(rounds)) / K * 1e-3
+    t_gpu = ev[0][0].elapsed_time(ev[rounds][0]) / K * 1e-3
     ms_per_step = max(wall / K, t_gpu) * 1e3
     pair_qps = 1.0 / (t_csa / cc["B"] + t_hca / ch["B"])
 
-    # ---- per-call breakdown (each call's graphs replayed back to back)
+    # ---- per-call breakdown (each call's graph replayed back to back)
     def per_call(i, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for s in range(n):
-            single[s % R][i]()
+        for _ in range(n):
+            per_call_g[i]()
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n * 1e-3
+        return e0.elapsed_time(e1) / (n * R) * 1e-3
 
-    n_call = max(20, K // 4)
+    n_call = max(4, rounds // 4)
     t_idx, t_csa_att, t_hca_call = (per_call(i, n_call) for i in range(3))
 
     # ---- dominant kernels, timed live with HIP events recorded by the
@@ -586,7 +592,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_prefill:
-        del layer, single, calls, reps, ws
+        del csa_layer, hca_layer, per_call_g, calls, reps, ws
         torch.cuda.empty_cache()
         log("prefill chunk ...")
         result["prefill"] = bench_prefill(v4, torch, log)
