@@ -204,12 +204,14 @@ __device__ __forceinline__ void stage_store(Fp8Tile* tl, const Stage& st) {
 
 // Work split of the 4 waves of a workgroup (32 heads of one query):
 //  * logits and softmax by head group: wave w takes heads 16*(w&1) .. +16 of
-//    the workgroup's 32 and half (w>>1) of the 512 dims; the two halves add
+//    the workgroup's 32 and half (w>>1) of the 512 dims (224 FP8 + 32 RoPE
+//    dims each); the two halves add
 //    their partial logits through LDS (fp32 addition commutes: both hold
 //    identical logits) and run the same online softmax;
-//  * PV by output-dim slice: wave w owns dims 128w .. 128w+127 for the 32
-//    heads, so each V^T fragment is widened from FP8 once and feeds two MFMAs
-//    (one per head group); P^T of both head groups comes through LDS.
+//  * PV by output-dim slice: wave w owns FP8 dims 112w .. 112w+111 and RoPE
+//    dims 448 + 16w .. +15 for the 32 heads, so each V^T fragment is widened
+//    from FP8 once and feeds two MFMAs (one per head group); P^T of both
+//    head groups comes through LDS.
 // A workgroup is small (4 waves, about 60 KB of LDS) so that two run on
 // every compute unit and each hides the other's barriers and latencies.
 struct __align__(16) Shared {
@@ -231,28 +233,25 @@ __device__ __forceinline__ void qk_softmax(const Fp8Tile* tl, Shared* sh, const 
                                            SoftState& S, float c2, int hg, int half, int g,
                                            int li) {
   const int lane = threadIdx.x & 63;
-  // ---- partial S^T = K Q^T over this half's dims, both row blocks
+  // ---- partial S^T = K Q^T over this half's dims, both row blocks.  Half h
+  // takes FP8 dims 224h .. 224h+223 (7 k-steps) and RoPE dims 448 + 32h ..
+  // +31 (1 k-step): the same code for both halves, no branches, so all of a
+  // row block's K reads can be in flight together.
   float part[8];
+  const uint8_t* kbase = tl->rows + half * 224 + g * 8;
+  const uint8_t* rbase = tl->rows + kNope + (half * 32 + g * 8) * 2;
 #pragma unroll
   for (int rb = 0; rb < 2; rb++) {
+    const int er = (rb * 16 + li) * kRowStride;
+    u32x2 kw[7];
+#pragma unroll
+    for (int ks = 0; ks < 7; ks++) kw[ks] = *(const u32x2*)(kbase + er + ks * 32);
+    const u32x4 kr = *(const u32x4*)(rbase + er);
     f32x4 sn = {0.f, 0.f, 0.f, 0.f}, sr = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* kr = tl->rows + (rb * 16 + li) * kRowStride + g * 8 + half * 256;
-    const int nks = half ? 6 : 8;          // FP8 k-steps of 32 dims
 #pragma unroll
-    for (int ks = 0; ks < 8; ks++) {
-      if (ks < nks) {
-        u32x2 w = *(const u32x2*)(kr + ks * 32);
-        sn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(w[0], w[1]), qf[ks], sn, 0, 0, 0);
-      }
-    }
-    if (half) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
-        u32x4 v = *(const u32x4*)(tl->rows + (rb * 16 + li) * kRowStride + kNope + ks * 64 + g * 16);
-        sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), qf[6 + ks], sr,
-                                                     0, 0, 0);
-      }
-    }
+    for (int ks = 0; ks < 7; ks++)
+      sn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(kw[ks][0], kw[ks][1]), qf[ks], sn, 0, 0, 0);
+    sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr), qf[7], sr, 0, 0, 0);
     const f32x4 sc = *(const f32x4*)&tl->scale[rb * 16 + g * 4];
 #pragma unroll
     for (int i = 0; i < 4; i++) part[rb * 4 + i] = sn[i] * sc[i] + sr[i];
@@ -307,14 +306,36 @@ __device__ __forceinline__ void qk_softmax(const Fp8Tile* tl, Shared* sh, const 
   }
 }
 
-// PV for wave `ds` (dims 128ds .. 128ds+127), both head groups.  acc[db][ht]:
-// O^T block of dims 128ds + 16db .. +16 x heads 16ht .. +16.  Blocks below
-// dim 448 are FP8 (8-bit transpose reads, widened, times (P * scale)^T);
-// the RoPE blocks (wave 3, blocks 4..7) are bf16 (16-bit transpose reads,
-// times P^T).
+// Output dims of PV wave w, block db (16 dims): FP8 dims 112w + 16db for
+// db < 7, RoPE dims 448 + 16w for db = 7 -- every wave the same mix, so the
+// PV code has no branches on the wave.
+__device__ __forceinline__ int pv_dim0(int w, int db) { return db < 7 ? 112 * w + 16 * db : kNope + 16 * w; }
+
+// PV for wave `ds`, both head groups: acc[db][ht] = O^T block of dims
+// pv_dim0(ds, db) .. +16 x heads 16ht .. +16.  FP8 blocks: 8-bit transpose
+// reads, widened, times (P * scale)^T; the RoPE block: 16-bit transpose
+// reads times P^T.  All LDS reads are issued before the (rare) rescale.
 __device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f32x4 (*acc)[2],
                                          int ds, int g, int li) {
   const int lane = threadIdx.x & 63;
+  const bf16x8 pn0 = __builtin_bit_cast(bf16x8, sh->pnB[0][lane]);
+  const bf16x8 pn1 = __builtin_bit_cast(bf16x8, sh->pnB[1][lane]);
+  const bf16x8 pb0 = __builtin_bit_cast(bf16x8, sh->pB[0][lane]);
+  const bf16x8 pb1 = __builtin_bit_cast(bf16x8, sh->pB[1][lane]);
+  // lane group g's k-values are entries {4g..4g+3, 16+4g..16+4g+3}; source
+  // lane s of the group points at entry k = s/2 (tr8) resp. s/4 (tr16)
+  const int s = li;
+  const int kk8 = s >> 1;
+  const int ent8 = (kk8 < 4) ? (g * 4 + kk8) : (16 + g * 4 + kk8 - 4);
+  const uint8_t* vb8 = tl->rows + ent8 * kRowStride + (s & 1) * 8 + ds * 112;
+  u32x2 w8[7];
+#pragma unroll
+  for (int db = 0; db < 7; db++) w8[db] = lds_tr8(vb8 + db * 16);
+  const int kk16 = s >> 2;
+  const uint8_t* vlo = tl->rows + (g * 4 + kk16) * kRowStride + kNope + ds * 32 + (s & 3) * 8;
+  const uint8_t* vhi = tl->rows + (16 + g * 4 + kk16) * kRowStride + kNope + ds * 32 + (s & 3) * 8;
+  const u32x2 lo = lds_tr16(vlo);
+  const u32x2 hi = lds_tr16(vhi);
   if (sh->flag[0] | sh->flag[1]) {
 #pragma unroll
     for (int ht = 0; ht < 2; ht++) {
@@ -323,44 +344,15 @@ __device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f3
       for (int db = 0; db < 8; db++) acc[db][ht] *= al;
     }
   }
-  const bf16x8 pn0 = __builtin_bit_cast(bf16x8, sh->pnB[0][lane]);
-  const bf16x8 pn1 = __builtin_bit_cast(bf16x8, sh->pnB[1][lane]);
-  // lane group g's k-values are entries {4g..4g+3, 16+4g..16+4g+3}; source
-  // lane s of the group points at entry k = s/2 (tr8) resp. s/4 (tr16)
-  const int s = li;
-  const int kk8 = s >> 1;
-  const int ent8 = (kk8 < 4) ? (g * 4 + kk8) : (16 + g * 4 + kk8 - 4);
-  const uint8_t* vb8 = tl->rows + ent8 * kRowStride + (s & 1) * 8 + ds * 128;
-  if (ds < 3) {
 #pragma unroll
-    for (int db = 0; db < 8; db++) {
-      u32x2 w = lds_tr8(vb8 + db * 16);
-      const bf16x8 v = widen8(w[0], w[1]);
-      acc[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn0, acc[db][0], 0, 0, 0);
-      acc[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn1, acc[db][1], 0, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int db = 0; db < 4; db++) {
-      u32x2 w = lds_tr8(vb8 + db * 16);
-      const bf16x8 v = widen8(w[0], w[1]);
-      acc[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn0, acc[db][0], 0, 0, 0);
-      acc[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn1, acc[db][1], 0, 0, 0);
-    }
-    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, sh->pB[0][lane]);
-    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, sh->pB[1][lane]);
-    const int kk16 = s >> 2;
-    const uint8_t* vlo = tl->rows + (g * 4 + kk16) * kRowStride + kNope + (s & 3) * 8;
-    const uint8_t* vhi = tl->rows + (16 + g * 4 + kk16) * kRowStride + kNope + (s & 3) * 8;
-#pragma unroll
-    for (int db = 0; db < 4; db++) {
-      u32x2 lo = lds_tr16(vlo + db * 32);
-      u32x2 hi = lds_tr16(vhi + db * 32);
-      const bf16x8 v = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
-      acc[4 + db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb0, acc[4 + db][0], 0, 0, 0);
-      acc[4 + db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb1, acc[4 + db][1], 0, 0, 0);
-    }
+  for (int db = 0; db < 7; db++) {
+    const bf16x8 v = widen8(w8[db][0], w8[db][1]);
+    acc[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn0, acc[db][0], 0, 0, 0);
+    acc[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn1, acc[db][1], 0, 0, 0);
   }
+  const bf16x8 vr = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+  acc[7][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr, pb0, acc[7][0], 0, 0, 0);
+  acc[7][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr, pb1, acc[7][1], 0, 0, 0);
 }
 
 // Workgroup -> (query row, split, group of 32 heads).  Workgroups are
@@ -384,7 +376,7 @@ __device__ __forceinline__ bool wg_coords(const AttendArgs& a, int* row, int* sp
 // Split partials of the FP8 path live in the workspace in the accumulator
 // layout, so that a wave stores (and the merge loads) whole contiguous runs:
 // the block of (row, split, head group) holds nh x 512 values ordered
-// [dim slice 4][dim block 8][head tile nht][lane 64][4].
+// [PV wave 4][dim block 8][head tile nht][lane 64][4] (dims: pv_dim0).
 __device__ __forceinline__ int64_t part_block(const AttendArgs& a, int row, int split, int hgrp) {
   return (((int64_t)row * a.n_split + split) * a.H + hgrp * kHeads) * (kNope + kRope);
 }
@@ -425,16 +417,17 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   Stage st;
   stage_load(a, src, b, 0, n_local, st);
 
-  // Q^T fragments of this wave's half: k-step ks covers dims
-  // 256*half + 32ks .. +31 (the RoPE dims are k-steps 6, 7 of half 1); the
+  // Q^T fragments of this wave's half: k-steps 0..6 cover FP8 dims
+  // 224*half + 32ks .. +31, k-step 7 RoPE dims 448 + 32*half .. +31; the
   // lane holds dims +8g .. +8 of its head (zero for heads beyond H)
   bf16x8 qf[8];
   {
     const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.H + (head_ok ? head : 0)) * D +
-                         half * 256 + g * 8;
+                         g * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ks++) {
-      u32x4 v = *(const u32x4*)(qp + ks * 32);
+      const int d0 = ks < 7 ? half * 224 + ks * 32 : kNope + half * 32;
+      u32x4 v = *(const u32x4*)(qp + d0);
       if (!head_ok) v = (u32x4){0u, 0u, 0u, 0u};
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
@@ -487,23 +480,23 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
     sh.fin[hg * 16 + li] = f;
   }
   __syncthreads();
-  // PV wave `wave` holds O^T dims 128*wave + 16db + 4g + i of head 16ht + li
+  // PV wave `wave` holds O^T dims pv_dim0(wave, db) + 4g + i of head 16ht + li
   if (a.n_split == 1) {
 #pragma unroll
     for (int ht = 0; ht < 2; ht++) {
       if (ht >= nht) break;
       const float f = sh.fin[ht * 16 + li];
-      const int64_t ob =
-          ((int64_t)row * a.H + hgrp * kHeads + ht * 16 + li) * D + wave * 128 + g * 4;
+      const int64_t ob = ((int64_t)row * a.H + hgrp * kHeads + ht * 16 + li) * D + g * 4;
 #pragma unroll
       for (int db = 0; db < 8; db++) {
         const f32x4 o = acc[db][ht] * f;
+        const int64_t oi = ob + pv_dim0(wave, db);
         if (a.out_bf16) {
           const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
           const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-          *(u32x2*)((uint16_t*)a.out + ob + db * 16) = (u32x2){lo, hi};
+          *(u32x2*)((uint16_t*)a.out + oi) = (u32x2){lo, hi};
         } else {
-          *(f32x4*)((float*)a.out + ob + db * 16) = o;
+          *(f32x4*)((float*)a.out + oi) = o;
         }
       }
     }
@@ -721,9 +714,9 @@ __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
   const int q4 = (active ? j : 0) >> 2;
   const int ln = q4 & 63;
   const int ht = (q4 >> 6) % nht;
-  const int sb = (q4 >> 6) / nht;                      // dim slice * 8 + dim block
+  const int sb = (q4 >> 6) / nht;                      // PV wave * 8 + dim block
   const int head = hgrp * kHeads + ht * 16 + (ln & 15);
-  const int d0 = sb * 16 + (ln >> 4) * 4;
+  const int d0 = pv_dim0(sb >> 3, sb & 7) + (ln >> 4) * 4;
   const f32x2* ml = (const f32x2*)a.part_ml + (int64_t)row * a.n_split * a.H + head;
   // ---- the maximum over all splits (and the sink)
   float M = -INFINITY;
