@@ -9,22 +9,21 @@
 // HCA has no top-k); [Notes §9] attention sink, FP8 KV with BF16 RoPE dims.
 //
 // Kernels
-//   k_attend_fp8  gfx950 MFMA path.  A workgroup = 8 waves = 64 query heads of
-//                 one query.  The entry list is walked in tiles of 32 entries
-//                 staged (raw FP8 codes + BF16 RoPE + fp32 scale) in LDS once
-//                 per workgroup and read by all eight waves:
-//                   S^T = K Q^T  by (16-head group, half of the dims): wave w
-//                         takes group w&3 and dims 256(w>>2) .. +255 with
-//                         v_mfma_f32_16x16x32_bf16; K rows are read with
-//                         ds_read_b64 and widened e4m3 -> bf16 exactly; Q^T
-//                         stays in registers; the two halves add their
-//                         partial logits through LDS;
-//                   O^T += V^T P^T by 64-dim slice: wave w owns dims
-//                         64w .. 64w+63 of all 64 heads; V^T fragments come
-//                         straight from the row-major tile with
-//                         ds_read_b64_tr_b8 / _tr_b16 (transpose loads), are
-//                         widened once and feed one MFMA per head group, with
-//                         P^T of the four groups passed through LDS.
+//   k_attend_fp8  gfx950 MFMA path.  A workgroup = 4 waves = 32 query heads of
+//                 one query (two workgroups per compute unit).  The entry
+//                 list is walked in tiles of 32 entries staged (raw FP8 codes
+//                 + BF16 RoPE + fp32 scale) in LDS once per workgroup:
+//                   S = K Q^T   by dim quarter: wave w computes all 32 x 32
+//                         logits over its 112 FP8 + 16 RoPE dims with
+//                         v_mfma_f32_32x32x16_bf16 (K rows read with
+//                         ds_read_b64 and widened e4m3 -> bf16 exactly, Q^T in
+//                         registers); the partials are added through LDS;
+//                   softmax by head: wave w owns heads 8w .. 8w+7;
+//                   O^T += V^T P^T by dim slice: wave w owns the same dims
+//                         for all 32 heads; V^T fragments come straight from
+//                         the row-major tile with ds_read_b64_tr_b8 / _tr_b16
+//                         (transpose loads), are widened once and feed one
+//                         v_mfma_f32_16x16x32_bf16 per 16-head tile.
 //                 The per-entry FP8 scale multiplies the non-RoPE logit and
 //                 the non-RoPE probability in fp32, so decoding adds no
 //                 rounding.  Online softmax in base 2 with a lazily updated
@@ -107,11 +106,11 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-__device__ __forceinline__ bf16x8 pack8(const float* v) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; i++) r[i] = (__bf16)v[i];
-  return r;
+// 4 fp32 -> 4 bf16 (round to nearest even), packed.
+__device__ __forceinline__ u32x2 pack4(const float* v) {
+  const bf16x2 lo = {(__bf16)v[0], (__bf16)v[1]};
+  const bf16x2 hi = {(__bf16)v[2], (__bf16)v[3]};
+  return (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 typedef int v2i_lds __attribute__((ext_vector_type(2)));
@@ -146,44 +145,98 @@ struct Stage {
 // Source of every entry of this workgroup's split, resolved once into LDS
 // (top-k ids are loaded here, not inside the tile pipeline, so the pipelined
 // chunk loads never wait on another global load): >= 0 compressed row,
-// -2 - r window ring row r, -1 absent.
+// -2 - r window ring row r, -1 absent.  Per tile, the kinds of entries it
+// holds (bit set), so that a tile of only compressed (only window) rows takes
+// a branch-free address path.
 constexpr int kMaxSplit = 2048;
+constexpr int kMaxTiles = kMaxSplit / kTile + 2;   // + the two prefetched past the end
+constexpr int kHasComp = 1, kHasWin = 2, kHasAbsent = 4;
+
+// An absent entry (or a slot past the split) reads this zero row: its codes,
+// RoPE dims and scale are all zero, so no loaded value needs masking.
+__device__ __align__(256) uint32_t g_zero_row[(kNope + 2 * kRope + 64) / 4];
 
 __device__ __forceinline__ void resolve_sources(const AttendArgs& a, const RowEntries& r, int row,
-                                                int e_beg, int e_end, int* src) {
+                                                int e_beg, int e_end, int n_local, int n_tiles,
+                                                int* src, int* tbits) {
+  for (int i = threadIdx.x; i < kMaxTiles; i += blockDim.x) tbits[i] = i < n_tiles ? 0 : kHasAbsent;
+  __syncthreads();
   for (int e = e_beg + threadIdx.x; e < e_end; e += blockDim.x) {
     bool is_win;
     int64_t sr = entry_source(a, r, row, e, &is_win);
-    src[e - e_beg] = sr < 0 ? -1 : (is_win ? (int)(-2 - sr) : (int)sr);
+    const int code = sr < 0 ? -1 : (is_win ? (int)(-2 - sr) : (int)sr);
+    src[e - e_beg] = code;
+    atomicOr(&tbits[(e - e_beg) / kTile], code >= 0 ? kHasComp : (code == -1 ? kHasAbsent : kHasWin));
   }
+  if (threadIdx.x == 0 && (n_local % kTile) != 0) atomicOr(&tbits[n_local / kTile], kHasAbsent);
 }
 
-// Every load is issued unconditionally (an absent entry reads row 0 of the
-// sequence's compressed cache, which always exists, and is zeroed when
-// stored), so the number of loads per tile is fixed and the compiler can keep
-// later tiles' loads in flight when it waits for an earlier one.
-__device__ __forceinline__ void stage_load(const AttendArgs& a, const int* src, int b, int tile_l0,
-                                           int n_local, Stage& st) {
+// Per-sequence bases of the compressed cache and the window ring.
+struct Bases {
+  const uint8_t* cn;
+  const uint8_t* cr;
+  const float* cs;
+  const uint8_t* wn;
+  const uint8_t* wr;
+  const float* ws;
+};
+
+// Every load is issued unconditionally (absent entries read the zero row), so
+// the number of loads per tile is fixed and the compiler can keep later
+// tiles' loads in flight when it waits for an earlier one.  The address path
+// branches on the tile's kind, which is uniform across the workgroup.
+__device__ __forceinline__ void stage_load(Bases B, const int* src, const int* tbits,
+                                           int tile, int n_local, Stage& st) {
   const int t = threadIdx.x;
   const int q = t & 7;
-  const int le = tile_l0 + (t >> 3);
-  const int sraw = src[le < kMaxSplit ? le : kMaxSplit - 1];   // always in bounds
-  const int s = le < n_local ? sraw : -1;
-  const bool is_win = s < -1;
-  const int64_t rr = s >= 0 ? (int64_t)s : (is_win ? (int64_t)(-2 - s) : 0);
-  const int64_t rowi = (int64_t)b * (is_win ? a.w_cap : a.c_cap) + rr;
-  const uint8_t* nope = (is_win ? a.w_nope : a.c_nope) + rowi * kNope;
-  const uint8_t* rope = (const uint8_t*)(is_win ? a.w_rope : a.c_rope) + rowi * (2 * kRope);
-  // the values are masked when stored to LDS, not here: using them now would
-  // make the compiler wait for these loads immediately
+  const int le = tile * kTile + (t >> 3);
+  const int bits = __builtin_amdgcn_readfirstlane(tbits[tile]);
+  const uint8_t* nope;
+  const uint8_t* rope;
+  const float* scp;
+  int ok = 1;
+  if (bits == kHasComp) {
+    const int64_t rr = src[le];
+    nope = B.cn + rr * kNope;
+    rope = B.cr + rr * (2 * kRope);
+    scp = B.cs + rr;
+  } else if (bits == kHasWin) {
+    const int64_t rr = -2 - src[le];
+    nope = B.wn + rr * kNope;
+    rope = B.wr + rr * (2 * kRope);
+    scp = B.ws + rr;
+  } else {
+    const int sraw = src[le < kMaxSplit ? le : kMaxSplit - 1];   // always in bounds
+    const int s = le < n_local ? sraw : -1;
+    const bool is_win = s < -1;
+    const int64_t rr = is_win ? (int64_t)(-2 - s) : (int64_t)s;
+    ok = s != -1;
+    const uint8_t* zero = (const uint8_t*)g_zero_row;
+    if (is_win) {
+      nope = B.wn + rr * kNope;
+      rope = B.wr + rr * (2 * kRope);
+      scp = B.ws + rr;
+    } else {
+      nope = B.cn + rr * kNope;
+      rope = B.cr + rr * (2 * kRope);
+      scp = B.cs + rr;
+    }
+    if (!ok) {
+      nope = zero;
+      rope = zero + kNope;
+      scp = (const float*)zero;
+    }
+  }
+  // the values are stored to LDS one step later: using them now would make
+  // the compiler wait for these loads immediately
   st.r[0] = __builtin_nontemporal_load((const u32x4*)(nope + q * 16));
   st.r[1] = __builtin_nontemporal_load((const u32x4*)(nope + (8 + q) * 16));
   st.r[2] = __builtin_nontemporal_load((const u32x4*)(nope + (16 + q) * 16));
   st.r[3] = __builtin_nontemporal_load(
       (const u32x4*)(q < 4 ? nope + (24 + q) * 16 : rope + (q - 4) * 16));
   st.r[4] = __builtin_nontemporal_load((const u32x4*)(rope + (4 + (q & 3)) * 16));
-  st.sc = (is_win ? a.w_scale : a.c_scale)[rowi];
-  st.ok = s != -1;
+  st.sc = *scp;
+  st.ok = ok;
 }
 
 // Every value is stored unconditionally (duplicates write identical values),
@@ -191,90 +244,98 @@ __device__ __forceinline__ void stage_load(const AttendArgs& a, const int* src, 
 __device__ __forceinline__ void stage_store(Fp8Tile* tl, const Stage& st) {
   const int t = threadIdx.x;
   const int e = t >> 3, q = t & 7;
-  const u32x4 z = {0u, 0u, 0u, 0u};
   uint8_t* dst = tl->rows + e * kRowStride;
-  *(u32x4*)(dst + q * 16) = st.ok ? st.r[0] : z;
-  *(u32x4*)(dst + (8 + q) * 16) = st.ok ? st.r[1] : z;
-  *(u32x4*)(dst + (16 + q) * 16) = st.ok ? st.r[2] : z;
-  *(u32x4*)(dst + (q < 4 ? (24 + q) * 16 : kNope + (q - 4) * 16)) = st.ok ? st.r[3] : z;
-  *(u32x4*)(dst + kNope + (4 + (q & 3)) * 16) = st.ok ? st.r[4] : z;
-  tl->scale[e] = st.ok ? st.sc : 0.0f;
+  *(u32x4*)(dst + q * 16) = st.r[0];
+  *(u32x4*)(dst + (8 + q) * 16) = st.r[1];
+  *(u32x4*)(dst + (16 + q) * 16) = st.r[2];
+  *(u32x4*)(dst + (q < 4 ? (24 + q) * 16 : kNope + (q - 4) * 16)) = st.r[3];
+  *(u32x4*)(dst + kNope + (4 + (q & 3)) * 16) = st.r[4];
+  tl->scale[e] = st.sc;
   tl->bias[e] = st.ok ? 0.0f : -INFINITY;
 }
 
 // Work split of the 4 waves of a workgroup (32 heads of one query):
-//  * logits and softmax by head group: wave w takes heads 16*(w&1) .. +16 of
-//    the workgroup's 32 and half (w>>1) of the 512 dims (224 FP8 + 32 RoPE
-//    dims each); the two halves add
-//    their partial logits through LDS (fp32 addition commutes: both hold
-//    identical logits) and run the same online softmax;
+//  * logits by dim quarter: wave w computes the partial S = K Q^T of the
+//    tile's 32 entries x 32 heads over FP8 dims 112w .. +111 and RoPE dims
+//    448 + 16w .. +15 with v_mfma_f32_32x32x16_bf16, so each widened K value
+//    feeds 32 heads; the four partials meet in LDS (added in wave order);
+//  * softmax by head: wave w owns heads 8w .. 8w+7, a lane one head and four
+//    entries (entry group eg = lane / 8);
 //  * PV by output-dim slice: wave w owns FP8 dims 112w .. 112w+111 and RoPE
 //    dims 448 + 16w .. +15 for the 32 heads, so each V^T fragment is widened
-//    from FP8 once and feeds two MFMAs (one per head group); P^T of both
-//    head groups comes through LDS.
-// A workgroup is small (4 waves, about 60 KB of LDS) so that two run on
+//    from FP8 once and feeds two MFMAs (one per 16-head tile); P^T comes
+//    through LDS.
+// A workgroup is small (4 waves, about 64 KB of LDS) so that two run on
 // every compute unit and each hides the other's barriers and latencies.
 struct __align__(16) Shared {
-  float xc[2][2][64][8];                   // partial logits [hg][half][lane][both row blocks]
-  u32x4 pB[2][64];                         // P^T operand (RoPE dims) [hg][lane]
+  f32x4 xp[4][4][64];                      // partial logits [QK wave][softmax wave][lane]
+  u32x4 pB[2][64];                         // P^T operand (RoPE dims) [head tile][lane]
   u32x4 pnB[2][64];                        // (P * scale)^T operand (FP8 dims)
   float alpha[kHeads];                     // per-head rescale of the tile (1 = none)
-  int flag[2];                             // head group rescaled this tile
+  i32x4 flag;                              // softmax wave rescaled this tile
   float fin[kHeads];                       // per-head output factor (epilogue)
+  int tbits[kMaxTiles];                    // entry kinds per tile
 };
 
-// Online-softmax state of a logits wave (its lane's head); both halves agree.
+// Online-softmax state of a softmax lane's head (the 8 lanes of a head agree
+// on the max; the denominator is lane-partial).
 struct SoftState {
   float m_run;
-  float l_run;                             // lane-partial denominator
+  float l_run;
 };
 
-__device__ __forceinline__ void qk_softmax(const Fp8Tile* tl, Shared* sh, const bf16x8* qf,
-                                           SoftState& S, float c2, int hg, int half, int g,
-                                           int li) {
-  const int lane = threadIdx.x & 63;
-  // ---- partial S^T = K Q^T over this half's dims, both row blocks.  Half h
-  // takes FP8 dims 224h .. 224h+223 (7 k-steps) and RoPE dims 448 + 32h ..
-  // +31 (1 k-step): the same code for both halves, no branches, so all of a
-  // row block's K reads can be in flight together.
-  float part[8];
-  const uint8_t* kbase = tl->rows + half * 224 + g * 8;
-  const uint8_t* rbase = tl->rows + kNope + (half * 32 + g * 8) * 2;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Partial logits of QK wave w.  MFMA operands: A = K (lane: entry lane & 31,
+// dims +8 (lane >> 5) .. +8 of the k-step), B = Q^T (lane: head lane & 31,
+// same dims); the accumulator's value v of a lane is entry
+// 8 (v / 4) + 4 (lane >> 5) + v % 4, head lane & 31.  The FP8 part is scaled
+// per entry in fp32 before the RoPE part is added.
+__device__ __forceinline__ void qk_partial(const Fp8Tile* tl, Shared* sh, const bf16x8* qf, int w,
+                                           int lane) {
+  const int kh = lane >> 5;
+  const uint8_t* er = tl->rows + (lane & 31) * kRowStride;
+  const uint8_t* kp = er + 112 * w + 8 * kh;
+  u32x2 kw[7];
 #pragma unroll
-  for (int rb = 0; rb < 2; rb++) {
-    const int er = (rb * 16 + li) * kRowStride;
-    u32x2 kw[7];
+  for (int ks = 0; ks < 7; ks++) kw[ks] = *(const u32x2*)(kp + 16 * ks);
+  const u32x4 kr = *(const u32x4*)(er + kNope + (16 * w + 8 * kh) * 2);
+  f32x16 sn = {}, sr = {};
 #pragma unroll
-    for (int ks = 0; ks < 7; ks++) kw[ks] = *(const u32x2*)(kbase + er + ks * 32);
-    const u32x4 kr = *(const u32x4*)(rbase + er);
-    f32x4 sn = {0.f, 0.f, 0.f, 0.f}, sr = {0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < 7; ks++)
+    sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8(kw[ks][0], kw[ks][1]), qf[ks], sn, 0, 0, 0);
+  sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr), qf[7], sr, 0, 0, 0);
+  const int j = lane & 31;
 #pragma unroll
-    for (int ks = 0; ks < 7; ks++)
-      sn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(kw[ks][0], kw[ks][1]), qf[ks], sn, 0, 0, 0);
-    sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr), qf[7], sr, 0, 0, 0);
-    const f32x4 sc = *(const f32x4*)&tl->scale[rb * 16 + g * 4];
+  for (int qd = 0; qd < 4; qd++) {
+    // entries 8qd + 4kh .. +3 = entry group 2qd + kh
+    const f32x4 sc = *(const f32x4*)&tl->scale[8 * qd + 4 * kh];
+    f32x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; i++) part[rb * 4 + i] = sn[i] * sc[i] + sr[i];
+    for (int i = 0; i < 4; i++) v[i] = sn[4 * qd + i] * sc[i] + sr[4 * qd + i];
+    sh->xp[w][j >> 3][(2 * qd + kh) * 8 + (j & 7)] = v;
   }
-  f32x4* mine = (f32x4*)sh->xc[hg][half][lane];
-  mine[0] = (f32x4){part[0], part[1], part[2], part[3]};
-  mine[1] = (f32x4){part[4], part[5], part[6], part[7]};
-  __syncthreads();
-  const f32x4* p0 = (const f32x4*)sh->xc[hg][0][lane];
-  const f32x4* p1 = (const f32x4*)sh->xc[hg][1][lane];
-  const f32x4 a0 = p0[0], a1 = p0[1], b0 = p1[0], b1 = p1[1];
-  // entries of lane group g: 4g .. 4g+3 and 16+4g .. 16+4g+3
-  const f32x4 sc0 = *(const f32x4*)&tl->scale[g * 4], sc1 = *(const f32x4*)&tl->scale[16 + g * 4];
-  const f32x4 bi0 = *(const f32x4*)&tl->bias[g * 4], bi1 = *(const f32x4*)&tl->bias[16 + g * 4];
-  float s2[8];
+}
+
+// Softmax of wave w's 8 heads: lane = head h (lane & 7) x entry group eg
+// (lane >> 3, entries 4eg .. 4eg+3).  Writes P^T and (P * scale)^T in the
+// PV operand layout: head tile j / 16, lane (j % 16) + 16 (eg % 4), slots
+// 4 (eg / 4) .. +3 (PV's k-slot order: entries 4g .. 4g+3, 16+4g .. +3).
+__device__ __forceinline__ void softmax_tile(const Fp8Tile* tl, Shared* sh, SoftState& S,
+                                             float c2, int w, int lane) {
+  const int h = lane & 7, eg = lane >> 3;
+  const f32x4 a0 = sh->xp[0][w][lane], a1 = sh->xp[1][w][lane];
+  const f32x4 a2 = sh->xp[2][w][lane], a3 = sh->xp[3][w][lane];
+  const f32x4 bi = *(const f32x4*)&tl->bias[4 * eg];
+  const f32x4 sc = *(const f32x4*)&tl->scale[4 * eg];
+  float s2[4];
   float tmax = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    // the same sum in both halves: half 0's partial first
-    const float v = i < 4 ? a0[i] + b0[i] : a1[i - 4] + b1[i - 4];
-    s2[i] = v * c2 + (i < 4 ? bi0[i] : bi1[i - 4]);
+  for (int i = 0; i < 4; i++) {
+    s2[i] = (((a0[i] + a1[i]) + a2[i]) + a3[i]) * c2 + bi[i];
     tmax = fmaxf(tmax, s2[i]);
   }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 8, 64));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
   // lazy rescale: the running max moves only when it grows by more than
@@ -288,22 +349,24 @@ __device__ __forceinline__ void qk_softmax(const Fp8Tile* tl, Shared* sh, const 
     S.m_run = tmax;
   }
   const float m_use = (S.m_run == -INFINITY) ? 0.0f : S.m_run;
-  float pv[8], pn[8];
+  float pv[4], pn[4];
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
+  for (int i = 0; i < 4; i++) {
     // 2^(x) for x <= kRescale; an absent entry gives 2^-inf = 0
     const float p = __builtin_amdgcn_exp2f(s2[i] - m_use);
     S.l_run += p;
     pv[i] = p;
-    pn[i] = p * (i < 4 ? sc0[i] : sc1[i - 4]);
+    pn[i] = p * sc[i];
   }
-  if (half == 0) {
-    sh->pB[hg][lane] = __builtin_bit_cast(u32x4, pack8(pv));
-    sh->pnB[hg][lane] = __builtin_bit_cast(u32x4, pack8(pn));
-    if (g == 0) sh->alpha[hg * 16 + li] = alpha;
-    const int any = __builtin_amdgcn_ballot_w64(need) != 0;
-    if (lane == 0) sh->flag[hg] = any;
-  }
+  const int j = 8 * w + h;
+  const int pl = (j & 15) + 16 * (eg & 3);
+  uint8_t* pb = (uint8_t*)&sh->pB[j >> 4][pl] + 8 * (eg >> 2);
+  uint8_t* pnb = (uint8_t*)&sh->pnB[j >> 4][pl] + 8 * (eg >> 2);
+  *(u32x2*)pb = pack4(pv);
+  *(u32x2*)pnb = pack4(pn);
+  if (eg == 0) sh->alpha[j] = alpha;
+  const int any = __builtin_amdgcn_ballot_w64(need) != 0;
+  if (lane == 0) sh->flag[w] = any;
 }
 
 // Output dims of PV wave w, block db (16 dims): FP8 dims 112w + 16db for
@@ -336,7 +399,8 @@ __device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f3
   const uint8_t* vhi = tl->rows + (16 + g * 4 + kk16) * kRowStride + kNope + ds * 32 + (s & 3) * 8;
   const u32x2 lo = lds_tr16(vlo);
   const u32x2 hi = lds_tr16(vhi);
-  if (sh->flag[0] | sh->flag[1]) {
+  const i32x4 fl = sh->flag;
+  if ((fl[0] | fl[1]) | (fl[2] | fl[3])) {
 #pragma unroll
     for (int ht = 0; ht < 2; ht++) {
       const float al = sh->alpha[ht * 16 + li];
@@ -389,13 +453,9 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   if (!wg_coords(a, &row, &split, &hgrp)) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int hg = wave & 1;                 // logits: 16-head group within the 32
-  const int half = wave >> 1;              // logits: dims 0..255 or 256..511
   const int b = row / a.Q;
-  const int g = lane >> 4;                 // lane group 0..3
+  const int g = lane >> 4;                 // PV: lane group 0..3
   const int li = lane & 15;
-  const int head = hgrp * kHeads + hg * 16 + li;
-  const bool head_ok = head < a.H;
   const int nht = min(2, (a.H - hgrp * kHeads) / 16);   // head tiles present (H % 16 == 0)
   const int D = kNope + kRope;
 
@@ -408,27 +468,37 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   const int n_local = __builtin_amdgcn_readfirstlane(e_end > e_beg ? e_end - e_beg : 0);
   const int n_tiles = (n_local + kTile - 1) / kTile;
 
-  resolve_sources(a, r, row, e_beg, e_end, src);
+  resolve_sources(a, r, row, e_beg, e_end, n_local, n_tiles, src, sh.tbits);
   __syncthreads();
 
-  // one tile in flight in registers while another is computed; every
-  // stage_load is unconditional (tiles past the split read valid rows and
-  // are masked), so each step issues the same loads
-  Stage st;
-  stage_load(a, src, b, 0, n_local, st);
+  Bases B;
+  B.cn = a.c_nope + (int64_t)b * a.c_cap * kNope;
+  B.cr = (const uint8_t*)(a.c_rope + (int64_t)b * a.c_cap * kRope);
+  B.cs = a.c_scale + (int64_t)b * a.c_cap;
+  B.wn = a.w_nope + (int64_t)b * a.w_cap * kNope;
+  B.wr = (const uint8_t*)(a.w_rope + (int64_t)b * a.w_cap * kRope);
+  B.ws = a.w_scale + (int64_t)b * a.w_cap;
 
-  // Q^T fragments of this wave's half: k-steps 0..6 cover FP8 dims
-  // 224*half + 32ks .. +31, k-step 7 RoPE dims 448 + 32*half .. +31; the
-  // lane holds dims +8g .. +8 of its head (zero for heads beyond H)
+  // one tile in flight in registers while another is computed; every
+  // stage_load issues the same loads (tiles past the split read the zero row)
+  Stage st;
+  stage_load(B, src, sh.tbits, 0, n_local, st);
+
+  // Q^T fragments of this wave's dim quarter (MFMA B operand): k-steps 0..6
+  // cover FP8 dims 112 wave + 16 ks .. +15, k-step 7 RoPE dims 448 + 16 wave
+  // .. +15; the lane holds dims +8 (lane >> 5) .. +8 of head lane & 31 (zero
+  // for heads beyond H)
   bf16x8 qf[8];
   {
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.H + (head_ok ? head : 0)) * D +
-                         g * 8;
+    const int qh = hgrp * kHeads + (lane & 31);
+    const bool q_ok = qh < a.H;
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.H + (q_ok ? qh : 0)) * D +
+                         8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < 8; ks++) {
-      const int d0 = ks < 7 ? half * 224 + ks * 32 : kNope + half * 32;
+      const int d0 = ks < 7 ? 112 * wave + 16 * ks : kNope + 16 * wave;
       u32x4 v = *(const u32x4*)(qp + d0);
-      if (!head_ok) v = (u32x4){0u, 0u, 0u, 0u};
+      if (!q_ok) v = (u32x4){0u, 0u, 0u, 0u};
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -443,24 +513,33 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   const float c2 = a.sm_scale * kLog2e;
 
   stage_store(&tiles[0], st);
-  stage_load(a, src, b, kTile, n_local, st);
+  stage_load(B, src, sh.tbits, 1, n_local, st);
   __syncthreads();
 
-  // step t: logits + softmax of tile t, PV of tile t, tile t+1 into LDS, the
-  // register set refilled with tile t+2
+  // step t: partial logits of tile t | softmax of tile t, tile t+1 into LDS,
+  // the register set refilled with tile t+2 | PV of tile t.  Two barriers
+  // per tile: the partial logits and tile t+1 are read only after the
+  // barrier that follows their writes, and every LDS buffer is rewritten
+  // only after a barrier that follows its last read.
   for (int t = 0; t < n_tiles; t++) {
-    qk_softmax(&tiles[t & 1], &sh, qf, S, c2, hg, half, g, li);
+    qk_partial(&tiles[t & 1], &sh, qf, wave, lane);
+    __syncthreads();
+    softmax_tile(&tiles[t & 1], &sh, S, c2, wave, lane);
+    stage_store(&tiles[(t + 1) & 1], st);
+    stage_load(B, src, sh.tbits, t + 2, n_local, st);
     __syncthreads();
     pv_slice(&tiles[t & 1], &sh, acc, wave, g, li);
-    stage_store(&tiles[(t + 1) & 1], st);
-    stage_load(a, src, b, (t + 2) * kTile, n_local, st);
-    __syncthreads();
   }
 
-  // ---- epilogue: the logits waves of half 0 publish each head's factor
-  float l_tot = S.l_run + __shfl_xor(S.l_run, 16, 64);
+  // ---- epilogue: the softmax lanes of entry group 0 publish each head's
+  // factor (the denominator summed over the head's 8 lanes)
+  float l_tot = S.l_run + __shfl_xor(S.l_run, 8, 64);
+  l_tot += __shfl_xor(l_tot, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  if (half == 0 && g == 0) {
+  if (lane < 8) {
+    const int jh = 8 * wave + lane;
+    const int head = hgrp * kHeads + jh;
+    const bool head_ok = head < a.H;
     float f;
     if (a.n_split == 1) {
       const float z2 = (a.sink && head_ok) ? a.sink[head] * kLog2e : -INFINITY;
@@ -477,7 +556,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
         a.part_ml[pi * 2 + 1] = l_tot;
       }
     }
-    sh.fin[hg * 16 + li] = f;
+    sh.fin[jh] = f;
   }
   __syncthreads();
   // PV wave `wave` holds O^T dims pv_dim0(wave, db) + 4g + i of head 16ht + li
