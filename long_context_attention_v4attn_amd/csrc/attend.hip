@@ -149,7 +149,7 @@ struct Stage {
 // holds (bit set), so that a tile of only compressed (only window) rows takes
 // a branch-free address path.
 constexpr int kMaxSplit = 2048;
-constexpr int kMaxTiles = kMaxSplit / kTile + 2;   // + the two prefetched past the end
+constexpr int kMaxTiles = kMaxSplit / kTile + 3;   // + the three prefetched past the end
 constexpr int kHasComp = 1, kHasWin = 2, kHasAbsent = 4;
 
 // An absent entry (or a slot past the split) reads this zero row: its codes,
@@ -479,10 +479,10 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   B.wr = (const uint8_t*)(a.w_rope + (int64_t)b * a.w_cap * kRope);
   B.ws = a.w_scale + (int64_t)b * a.w_cap;
 
-  // one tile in flight in registers while another is computed; every
+  // two tiles in flight in registers while another is computed; every
   // stage_load issues the same loads (tiles past the split read the zero row)
-  Stage st;
-  stage_load(B, src, sh.tbits, 0, n_local, st);
+  Stage st0, st1;
+  stage_load(B, src, sh.tbits, 0, n_local, st0);
 
   // Q^T fragments of this wave's dim quarter (MFMA B operand): k-steps 0..6
   // cover FP8 dims 112 wave + 16 ks .. +15, k-step 7 RoPE dims 448 + 16 wave
@@ -512,24 +512,34 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   S.l_run = 0.0f;
   const float c2 = a.sm_scale * kLog2e;
 
-  stage_store(&tiles[0], st);
-  stage_load(B, src, sh.tbits, 1, n_local, st);
+  // load order tile 0, Q, tile 1, tile 2: at the loop entry, as at every
+  // back edge, the older register set is the one stored next
+  stage_load(B, src, sh.tbits, 1, n_local, st1);
+  stage_store(&tiles[0], st0);
+  stage_load(B, src, sh.tbits, 2, n_local, st0);
   __syncthreads();
 
   // step t: partial logits of tile t | softmax of tile t, tile t+1 into LDS,
-  // the register set refilled with tile t+2 | PV of tile t.  Two barriers
+  // its register set refilled with tile t+3 | PV of tile t.  Two barriers
   // per tile: the partial logits and tile t+1 are read only after the
   // barrier that follows their writes, and every LDS buffer is rewritten
-  // only after a barrier that follows its last read.
-  for (int t = 0; t < n_tiles; t++) {
+  // only after a barrier that follows its last read.  Unrolled by two so
+  // that the register sets alternate statically.
+  auto step = [&](int t, Stage& nxt) {
     qk_partial(&tiles[t & 1], &sh, qf, wave, lane);
     __syncthreads();
     softmax_tile(&tiles[t & 1], &sh, S, c2, wave, lane);
-    stage_store(&tiles[(t + 1) & 1], st);
-    stage_load(B, src, sh.tbits, t + 2, n_local, st);
+    stage_store(&tiles[(t + 1) & 1], nxt);
+    stage_load(B, src, sh.tbits, t + 3, n_local, nxt);
     __syncthreads();
     pv_slice(&tiles[t & 1], &sh, acc, wave, g, li);
+  };
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, st1);
+    step(t + 1, st0);
   }
+  if (t < n_tiles) step(t, st1);
 
   // ---- epilogue: the softmax lanes of entry group 0 publish each head's
   // factor (the denominator summed over the head's 8 lanes)
