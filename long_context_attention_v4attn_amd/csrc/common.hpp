@@ -65,19 +65,16 @@ __device__ __forceinline__ uint32_t enc_e4m3(float x) {
 
 // Encode a value already divided by its block scale to e2m1 (4-bit code),
 // RNE with saturation at +-6.  Grid spacing: 0.5 below 2, 1 in [2,4), 2 in [4,6].
+// Branch-free: the region picks an exact power-of-two step and a code offset
+// (below 2: rint(2a) = codes 0..4; [2,4): rint(a) + 2 = codes 4..6; [4,6):
+// rint(a/2) + 4 = codes 6..7), then saturation.
 __device__ __forceinline__ uint32_t enc_e2m1(float x) {
-  uint32_t sign = (__float_as_uint(x) >> 28) & 0x8u;
-  float a = fabsf(x);
-  uint32_t c;
-  if (a >= 6.0f) {
-    c = 7;
-  } else if (a < 2.0f) {
-    c = (uint32_t)__builtin_rintf(a * 2.0f);               // 0..4 -> codes 0..4
-  } else if (a < 4.0f) {
-    c = (uint32_t)__builtin_rintf(a) + 2;                  // 2..4 -> codes 4..6
-  } else {
-    c = (uint32_t)__builtin_rintf(a * 0.5f) + 4;           // 2..3 -> codes 6..7
-  }
+  const uint32_t sign = (__float_as_uint(x) >> 28) & 0x8u;
+  const float a = fabsf(x);
+  const float step = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+  const uint32_t off = a < 2.0f ? 0u : (a < 4.0f ? 2u : 4u);
+  uint32_t c = (uint32_t)__builtin_rintf(a * step) + off;
+  c = a >= 6.0f ? 7u : c;
   return sign | c;
 }
 

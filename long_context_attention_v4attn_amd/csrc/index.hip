@@ -54,9 +54,39 @@ constexpr int kCtr = 8;                    // counters per query
 __host__ __device__ inline int64_t score_ld(int64_t cap) { return (cap + 63) / 64 * 64; }
 __host__ __device__ inline int64_t n_chunks(int64_t cap) { return (cap + kFilterChunk - 1) / kFilterChunk; }
 
+constexpr int kWaveTiles = 8;              // 8 tiles x 16 blocks per wave and iteration
+constexpr int kScanWaves = 4;              // waves per scan workgroup
+constexpr int kIterBlocks = kScanWaves * kWaveTiles * 16;   // 512 blocks per workgroup iteration
+constexpr int kQT = 8;                     // queries per workgroup of the query-tiled scan
+constexpr int kMaxParts = 128;             // widest partial-histogram row
+
+// Plan of the one-query-per-workgroup FP4 scan: about 512 workgroups of 4
+// waves in all (two per CU), each walking `iters` iterations of kIterBlocks
+// blocks.  With 16
+// index heads, when every workgroup's count fits 16 bits and there are at
+// most kMaxParts workgroups per query, the workgroups write partial
+// first-digit histograms (hp_ld = workgroups per query, else 0).
+struct ScanPlan {
+  int iters, wgs, hp_ld;
+};
+
+static ScanPlan scan_plan(int64_t cap, int64_t R, int H, int Q, int key_mx) {
+  ScanPlan p{0, 0, 0};
+  if (!key_mx || (H == 16 && Q >= kQT)) return p;
+  const int64_t it_total = (cap + kIterBlocks - 1) / kIterBlocks;
+  int64_t iters = (it_total * R + 511) / 512;
+  if (iters < 1) iters = 1;
+  if (iters > it_total) iters = it_total;
+  p.iters = (int)iters;
+  p.wgs = (int)((it_total + iters - 1) / iters);
+  if (H == 16 && iters * kIterBlocks <= 65535 && p.wgs <= kMaxParts) p.hp_ld = p.wgs;
+  return p;
+}
+
 size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx) {
   const size_t R = (size_t)B * Q;
-  size_t n = 0;
+  const ScanPlan sp = scan_plan(cap, (int64_t)R, H, Q, key_mx);
+  size_t n = align256(R * kBins1 * (size_t)sp.hp_ld * sizeof(uint16_t));
   if (key_mx) n += align256(R * H * (d / 2)) + align256(R * H * (d / 32));
   n += align256(R * (size_t)score_ld(cap) * sizeof(float));
   n += align256(R * kBins1 * sizeof(uint32_t)) + align256(R * kBins2 * sizeof(uint32_t));
@@ -68,7 +98,14 @@ size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx
 
 void index_carve(IndexArgs& a, void* ws) {
   const size_t R = (size_t)a.B * a.Q;
+  const ScanPlan sp = scan_plan(a.cap, (int64_t)R, a.H, a.Q, a.key_mx);
+  a.score_iters = sp.iters;
+  a.score_wgs = sp.wgs;
+  // the scan's own query quantisation loads 16-byte vectors
+  a.hp_ld = ((uintptr_t)a.q & 15) ? 0 : sp.hp_ld;
   char* p = (char*)ws;
+  a.hparts = (uint16_t*)p;
+  p += align256(R * kBins1 * (size_t)sp.hp_ld * sizeof(uint16_t));
   a.qmx = nullptr;
   a.qsc = nullptr;
   if (a.key_mx) {
@@ -167,26 +204,102 @@ __device__ __forceinline__ float swap_add16(float x, float y) {
   return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
 }
 
-constexpr int kWaveTiles = 16;             // 16 tiles x 16 blocks per wave and iteration
-constexpr int kIterBlocks = 4 * kWaveTiles * 16;   // 1024 blocks per workgroup iteration
-
+// A wave's key tiles of one iteration: per tile the lane's 16 code bytes;
+// the e8m0 scales as one dword (the 4 group scales of a block) per four
+// tiles -- lane group g holds the dword of block 16 (t4 + g) + li -- which
+// the scoring hands to the right lanes with ds_bpermute.  (A wave keeps its
+// loads in flight under the 63 the load counter tracks.)
 struct KeyTiles {
   u32x4 v[kWaveTiles];
-  int sc[kWaveTiles];
+  uint32_t sd[kWaveTiles / 4];
 };
 
+// The wave's key tiles of one iteration: tile t = blocks blk0 + 16t + li.
+// The addresses do not depend on the query's visible count (blocks past the
+// cache end read its last block), so the loads go out before that count is
+// known; blocks past the visible count are dropped when the scores are
+// stored.  Away from the cache end (the uniform common case) every load is
+// one base address plus an immediate offset.
 __device__ __forceinline__ void load_keys(const uint8_t* kc, const uint8_t* ks, int64_t blk0,
-                                          int64_t nv, int g, int li, KeyTiles& kt) {
+                                          int64_t cap, int g, int li, KeyTiles& kt) {
+  if (blk0 + kWaveTiles * 16 <= cap) {
+    const uint8_t* cp = kc + (blk0 + li) * 64 + g * 16;
+    const uint32_t* sp = (const uint32_t*)(ks + (blk0 + 16 * g + li) * 4);
 #pragma unroll
-  for (int t = 0; t < kWaveTiles; t++) {
-    const int64_t blk = blk0 + t * 16 + li;
-    kt.v[t] = (u32x4){0u, 0u, 0u, 0u};
-    kt.sc[t] = 127;
-    if (blk < nv) {
+    for (int t = 0; t < kWaveTiles; t++)
+      kt.v[t] = __builtin_nontemporal_load((const u32x4*)(cp + t * 1024));
+#pragma unroll
+    for (int q = 0; q < kWaveTiles / 4; q++) kt.sd[q] = sp[q * 64];
+  } else {
+#pragma unroll
+    for (int t = 0; t < kWaveTiles; t++) {
+      int64_t blk = blk0 + t * 16 + li;
+      blk = blk < cap ? blk : cap - 1;
       kt.v[t] = __builtin_nontemporal_load((const u32x4*)(kc + blk * 64 + g * 16));
-      kt.sc[t] = ks[blk * 4 + g];
+    }
+#pragma unroll
+    for (int q = 0; q < kWaveTiles / 4; q++) {
+      int64_t blk = blk0 + 16 * (4 * q + g) + li;
+      blk = blk < cap ? blk : cap - 1;
+      kt.sd[q] = *(const uint32_t*)(ks + blk * 4);
     }
   }
+}
+
+// MXFP4 fragment of the lane's query head, in two steps so that the loads
+// can go out long before the arithmetic: load_q_frag fetches elements
+// 32g .. 32g+31 of head h (bf16: 64 bytes, f32: 128 bytes); quantize_q_frag
+// encodes them as 16 bytes of e2m1 codes (element 2j in the low nibble of
+// byte j) and the group's e8m0 exponent -- the encoding the prep kernel
+// writes (the group's 32 elements are all in this lane).
+struct QRaw {
+  u32x4 v[8];
+};
+
+__device__ __forceinline__ void load_q_frag(const IndexArgs& a, int row, int h, int g, QRaw& r) {
+  const size_t base = ((size_t)row * a.H + h) * a.d + g * 32;
+  if (a.q_bf16) {
+    const u32x4* p = (const u32x4*)((const uint16_t*)a.q + base);
+#pragma unroll
+    for (int i = 0; i < 4; i++) r.v[i] = p[i];
+  } else {
+    const u32x4* p = (const u32x4*)((const float*)a.q + base);
+#pragma unroll
+    for (int i = 0; i < 8; i++) r.v[i] = p[i];
+  }
+}
+
+__device__ __forceinline__ void quantize_q_frag(const IndexArgs& a, const QRaw& r, i32x8* qa,
+                                                int* qs) {
+  float x[32];
+  if (a.q_bf16) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        x[8 * i + 2 * j] = bf16_bits_to_f32(r.v[i][j] & 0xFFFFu);
+        x[8 * i + 2 * j + 1] = bf16_bits_to_f32(r.v[i][j] >> 16);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) x[4 * i + j] = __uint_as_float(r.v[i][j]);
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i++) am = fmaxf(am, fabsf(x[i]));
+  const int e = mx_exponent(am);
+  const float inv = ldexpf(1.0f, -e);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    const uint32_t c0 = am > 0.f ? enc_e2m1(x[2 * j] * inv) : 0u;
+    const uint32_t c1 = am > 0.f ? enc_e2m1(x[2 * j + 1] * inv) : 0u;
+    w[j / 4] |= (c0 | (c1 << 4)) << (8 * (j % 4));
+  }
+  *qa = (i32x8){(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+  *qs = e + 127;
 }
 
 // Scores of the wave's kWaveTiles tiles, four tiles at a time: per tile one
@@ -195,26 +308,42 @@ __device__ __forceinline__ void load_keys(const uint8_t* kc, const uint8_t* ks, 
 // two lane-swap steps, which leave lane group g with the total of tile g --
 // so each lane owns one score: blocks blk0 + 16 t4 + lane, stored and
 // histogrammed by all 64 lanes together.
+template <int kHT>
 __device__ __forceinline__ void score_tiles(const KeyTiles& kt, const i32x8* qa, const int* qs,
                                             float (*wv)[4], int HT, int64_t blk0, int64_t nv,
-                                            int lane, float* out, uint32_t* lh) {
+                                            int64_t sc_ld, int lane, float* out, uint32_t* lh) {
+  // uniform: the iteration's blocks all lie inside the (64-padded) score row,
+  // so every lane stores (scores past the visible count are never read)
+  const bool in_row = blk0 + kWaveTiles * 16 <= sc_ld;
+  float* ob = out + blk0 + lane;
+  const int g = lane >> 4, li = lane & 15;
 #pragma unroll
   for (int t4 = 0; t4 < kWaveTiles; t4 += 4) {
     float part[4];
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       const int t = t4 + u;
+      // scale of (block 16t + li, group g): byte g of lane (li, u)'s dword
+      // (the MFMA reads the scale operand's low byte)
+      const int sc_t = __builtin_amdgcn_ds_bpermute((li + 16 * u) * 4, (int)kt.sd[t4 / 4]) >> (8 * g);
       const i32x8 kb = {(int)kt.v[t][0], (int)kt.v[t][1], (int)kt.v[t][2], (int)kt.v[t][3],
                         0, 0, 0, 0};
       float p = 0.0f;
 #pragma unroll
-      for (int ht = 0; ht < 4; ht++) {
+      for (int ht = 0; ht < kHT; ht++) {
         if (ht < HT) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb, acc, 4, 4, 0, qs[ht],
-                                                                 0, kt.sc[t]);
+                                                                 0, sc_t);
+          // ReLU as one integer max on the bits: a float with the sign bit
+          // set is a negative integer (-0 included) and becomes +0, any
+          // other is unchanged
 #pragma unroll
-          for (int i = 0; i < 4; i++) p += wv[ht][i] * fmaxf(acc[i], 0.0f);
+          for (int i = 0; i < 4; i++) {
+            const float x = acc[i];       // (a vector element as an lvalue does
+            const int bits = __float_as_int(x);   // not bit-cast reliably)
+            p += wv[ht][i] * __builtin_bit_cast(float, bits > 0 ? bits : 0);
+          }
         }
       }
       part[u] = p;
@@ -222,67 +351,122 @@ __device__ __forceinline__ void score_tiles(const KeyTiles& kt, const i32x8* qa,
     // lanes 0..31 / 32..63: tiles 0, 1 / 2, 3 summed over lane groups {0,2}, {1,3}
     const float h0 = swap_add32(part[0], part[2]);
     const float h1 = swap_add32(part[1], part[3]);
-    // lane group g: tile g
+    // lane group g: tile g; block blk0 + 16 t4 + lane
     const float sc = swap_add16(h0, h1);
     const int64_t blk = blk0 + t4 * 16 + lane;
-    if (blk < nv) {
-      out[blk] = sc;
-      atomicAdd(&lh[score_key(sc) >> kSh1], 1u);
-    }
+    if (in_row || blk < sc_ld) ob[t4 * 16] = sc;
+    // counted only when visible (an invisible block adds 0)
+    atomicAdd(&lh[score_key(sc) >> kSh1], blk < nv ? 1u : 0u);
   }
 }
 
-// Workgroup w of a query covers blocks [w * iters * 1024, (w + 1) * iters * 1024).
-__global__ void __launch_bounds__(256) k_score_mx(IndexArgs a) {
+// Workgroup w of a query covers blocks [w * iters * kIterBlocks, (w + 1) * iters * kIterBlocks).
+// kParts (16 index heads, hp_ld > 0): the workgroup quantises its query heads
+// itself, zeroes the query's filter counters and writes a partial histogram,
+// so no kernel runs before it; otherwise the prep kernel has quantised the
+// query and zeroed the global histogram the workgroup adds to.
+// kIters > 0: every workgroup's range is kIters iterations (score_iters ==
+// kIters) and all of them are loaded up front; 0: any count, two iterations
+// in flight.
+template <bool kParts, int kIters>
+__global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
   __shared__ uint32_t lh[kBins1];
   const int row = blockIdx.y;
   const int b = row / a.Q;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
   const int64_t wg0 = (int64_t)blockIdx.x * a.score_iters * kIterBlocks;
-  if (wg0 >= nv) return;                   // uniform across the workgroup
-  for (int i = threadIdx.x; i < kBins1; i += blockDim.x) lh[i] = 0u;
-  int iters = (int)((nv - wg0 + kIterBlocks - 1) / kIterBlocks);
-  if (iters > a.score_iters) iters = a.score_iters;
-
   const uint8_t* kc = (const uint8_t*)a.codes + (size_t)b * a.cap * 64;
   const uint8_t* ks = a.kscales + (size_t)b * a.cap * 4;
   const int64_t wblk = wg0 + wave * (kWaveTiles * 16);
-  KeyTiles k0, k1;
-  load_keys(kc, ks, wblk, nv, g, li, k0);
-  // A operands: q heads (ht*16 + li), elements 32g .. 32g+31; head weights
-  const int HT = a.H / 16;
-  i32x8 qa[4];
-  int qs[4];
-  float wv[4][4];
+  // the query's operands first, quantised before any key load is issued:
+  // a compute unit returns loads in order, so behind the keys the query
+  // would arrive only with them
+  const int64_t p_row = a.pos[row];
+  constexpr int kHT = kParts ? 1 : 4;
+  const int HT = kParts ? 1 : a.H / 16;
+  i32x8 qa[kHT];
+  int qs[kHT];
+  float wv[kHT][4];
+  QRaw qraw;
+  if (kParts) load_q_frag(a, row, li, g, qraw);
 #pragma unroll
-  for (int ht = 0; ht < 4; ht++) {
+  for (int ht = 0; ht < kHT; ht++) {
     qa[ht] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
     qs[ht] = 127;
 #pragma unroll
     for (int i = 0; i < 4; i++) wv[ht][i] = 0.0f;
     if (ht < HT) {
-      const uint8_t* qp = a.qmx + ((size_t)row * a.H + ht * 16 + li) * 64 + g * 16;
-      u32x4 v = *(const u32x4*)qp;
-      qa[ht] = (i32x8){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-      qs[ht] = a.qsc[((size_t)row * a.H + ht * 16 + li) * 4 + g];
+      if (!kParts) {
+        const uint8_t* qp = a.qmx + ((size_t)row * a.H + ht * 16 + li) * 64 + g * 16;
+        u32x4 v = *(const u32x4*)qp;
+        qa[ht] = (i32x8){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        qs[ht] = a.qsc[((size_t)row * a.H + ht * 16 + li) * 4 + g];
+      }
+      const f32x4 w4 = *(const f32x4*)(a.w + (size_t)row * a.H + ht * 16 + g * 4);
 #pragma unroll
-      for (int i = 0; i < 4; i++) wv[ht][i] = a.w[(size_t)row * a.H + ht * 16 + g * 4 + i];
+      for (int i = 0; i < 4; i++) wv[ht][i] = w4[i];
     }
   }
+  if (kParts) quantize_q_frag(a, qraw, &qa[0], &qs[0]);
+  constexpr int kSets = kIters > 0 ? kIters : 2;
+  KeyTiles kt[kSets];
+  // kIters > 0: iterations 0 .. kDepth-2 go out now, iteration j + kDepth - 1
+  // just before iteration j is scored (a wave that issued all its loads at
+  // once would wait at the issue of the later ones -- the compute unit's
+  // load queue fills -- instead of scoring what has arrived)
+  constexpr int kDepth = 2;
+#pragma unroll
+  for (int j = 0; j < kSets; j++)
+    if (kIters > 0 ? j < kDepth - 1 : j < a.score_iters)
+      load_keys(kc, ks, wblk + (int64_t)j * kIterBlocks, a.cap, g, li, kt[j]);
+  if (kParts) {
+    // the filter kernels' counters of this query (they run after this kernel)
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < kBins2 + kCtr; i += gridDim.x * blockDim.x) {
+      if (i < kBins2)
+        a.hist2[(size_t)row * kBins2 + i] = 0u;
+      else
+        a.ctr[(size_t)row * kCtr + i - kBins2] = 0u;
+    }
+  }
+  for (int i = threadIdx.x; i < kBins1; i += blockDim.x) lh[i] = 0u;
+  const int64_t nv = n_visible(p_row, a.m, a.cap);
+  int iters = wg0 < nv ? (int)((nv - wg0 + kIterBlocks - 1) / kIterBlocks) : 0;
+  if (iters > a.score_iters) iters = a.score_iters;
+  iters = __builtin_amdgcn_readfirstlane(iters);
   __syncthreads();                         // lh zeroed
   float* out = a.scores + (size_t)row * a.sc_ld;
-  for (int it = 0; it < iters; it += 2) {
-    const int64_t b0 = wblk + (int64_t)it * kIterBlocks;
-    if (it + 1 < iters) load_keys(kc, ks, b0 + kIterBlocks, nv, g, li, k1);
-    score_tiles(k0, qa, qs, wv, HT, b0, nv, lane, out, lh);
-    if (it + 1 >= iters) break;
-    if (it + 2 < iters) load_keys(kc, ks, b0 + 2 * kIterBlocks, nv, g, li, k0);
-    score_tiles(k1, qa, qs, wv, HT, b0 + kIterBlocks, nv, lane, out, lh);
+  if (kIters > 0) {
+    // every iteration's keys in flight from the start; scored in order
+#pragma unroll
+    for (int j = 0; j < kSets; j++) {
+      if (j + kDepth - 1 < kSets)
+        load_keys(kc, ks, wblk + (int64_t)(j + kDepth - 1) * kIterBlocks, a.cap, g, li,
+                  kt[j + kDepth - 1]);
+      if (j < iters)
+        score_tiles<kHT>(kt[j], qa, qs, wv, HT, wblk + (int64_t)j * kIterBlocks, nv, a.sc_ld, lane,
+                         out, lh);
+    }
+  } else {
+    // two iterations' keys in flight: kt[0] holds even, kt[1] odd iterations
+    for (int it = 0; it < iters; it += 2) {
+      const int64_t b0 = wblk + (int64_t)it * kIterBlocks;
+      score_tiles<kHT>(kt[0], qa, qs, wv, HT, b0, nv, a.sc_ld, lane, out, lh);
+      if (it + 1 >= iters) break;
+      if (it + 2 < iters) load_keys(kc, ks, b0 + 2 * kIterBlocks, a.cap, g, li, kt[0]);
+      score_tiles<kHT>(kt[1], qa, qs, wv, HT, b0 + kIterBlocks, nv, a.sc_ld, lane, out, lh);
+      if (it + 3 < iters) load_keys(kc, ks, b0 + 3 * kIterBlocks, a.cap, g, li, kt[1]);
+    }
   }
-  hist_flush(lh, a.hist + (size_t)row * kBins1, kBins1);
+  if (kParts) {
+    // this workgroup's counts: row blockIdx.x of [query][workgroup][bin]
+    __syncthreads();
+    for (int i = threadIdx.x; i < kBins1; i += blockDim.x)
+      a.hparts[((size_t)row * a.hp_ld + blockIdx.x) * kBins1 + i] = (uint16_t)lh[i];
+  } else {
+    hist_flush(lh, a.hist + (size_t)row * kBins1, kBins1);
+  }
 }
 
 // ---------------------------------------------------------------- FP4 scan, query-tiled
@@ -295,7 +479,6 @@ __global__ void __launch_bounds__(256) k_score_mx(IndexArgs a) {
 // with two lane-swap steps (v_permlane32_swap, v_permlane16_swap), which
 // leaves lane group g with the totals of queries (g & 1) + 4 (g >> 1) and
 // that + 2.  Per-query first-digit histograms in LDS, flushed once.
-constexpr int kQT = 8;
 constexpr int kQRange = 16384;
 
 struct QFrag {
@@ -547,6 +730,48 @@ __device__ __forceinline__ bool filter_head(const IndexArgs& a, int row, uint32_
   return true;
 }
 
+// Partial first-digit histograms of a query: one row of 256 16-bit counts
+// per scan workgroup ([query][workgroup][bin], at most kMaxParts rows).  A
+// load step reads 8 rows with the 256 threads in contiguous 16-byte pieces:
+// thread t takes bins 8 (t % 32) .. +7 of row 8i + t / 32 in step i, so a
+// thread always sums the same 8 bins.
+struct Parts {
+  u32x4 v[kMaxParts / 8];
+};
+
+__device__ __forceinline__ void load_parts(const IndexArgs& a, int row, Parts& p) {
+  const int t = threadIdx.x;
+  const uint16_t* base = a.hparts + (size_t)row * a.hp_ld * kBins1 + 8 * (t % 32);
+#pragma unroll
+  for (int i = 0; i < kMaxParts / 8; i++) {
+    const int slot = 8 * i + t / 32;
+    p.v[i] = slot < a.score_wgs ? *(const u32x4*)(base + (size_t)slot * kBins1)
+                                : (u32x4){0u, 0u, 0u, 0u};
+  }
+}
+
+// The count of bin threadIdx.x over all rows; red = 8 x 256 words of LDS
+// (free again on return).
+__device__ __forceinline__ uint32_t part_sum(const Parts& p, uint32_t* red) {
+  const int t = threadIdx.x;
+  uint32_t acc[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < kMaxParts / 8; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      acc[2 * j] += p.v[i][j] & 0xFFFFu;
+      acc[2 * j + 1] += p.v[i][j] >> 16;
+    }
+#pragma unroll
+  for (int j = 0; j < 8; j++) red[(t / 32) * kBins1 + 8 * (t % 32) + j] = acc[j];
+  __syncthreads();
+  uint32_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < 8; k++) sum += red[k * kBins1 + t];
+  __syncthreads();
+  return sum;
+}
+
 __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
   __shared__ uint32_t lh[kBins2];
   __shared__ uint32_t tmp[kFThreads / 64];
@@ -563,10 +788,22 @@ __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
     return;
   }
   if ((int64_t)blockIdx.x * kFilterChunk >= nv) return;
-  // all global loads first: the first histogram, then this thread's scores
-  const uint32_t h1 = a.hist[(size_t)row * kBins1 + threadIdx.x];   // kBins1 == kFThreads
+  // all global loads first: the first histogram (bin = thread), then this
+  // thread's scores
+  uint32_t h1;
   Group gr;
-  issue_group(a, row, blockIdx.x, gr);
+  if (a.hp_ld) {
+    Parts pt;
+    load_parts(a, row, pt);
+    issue_group(a, row, blockIdx.x, gr);
+    static_assert(8 * kBins1 <= kBins2, "partial-sum scratch fits the histogram buffer");
+    h1 = part_sum(pt, lh);
+    // the total for the kernels that follow
+    if (blockIdx.x == 0) a.hist[(size_t)row * kBins1 + threadIdx.x] = h1;
+  } else {
+    h1 = a.hist[(size_t)row * kBins1 + threadIdx.x];   // kBins1 == kFThreads
+    issue_group(a, row, blockIdx.x, gr);
+  }
   lh[threadIdx.x] = h1;
   __syncthreads();
   find_bin(lh, kBins1, (uint32_t)kk, tmp, &s_bin, &s_above);
@@ -832,7 +1069,7 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEvents* ev) {
   const int R = a.B * a.Q;
   if (R == 0) return hipSuccess;
-  {
+  if (!a.hp_ld) {
     size_t work = (size_t)R * kBins2;
     if (a.key_mx) {
       size_t qthreads = (size_t)R * a.H * 64;
@@ -852,19 +1089,25 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEve
     else
       hipLaunchKernelGGL(k_score_mx_q, grid, dim3(256), 0, st, a);
   } else if (a.key_mx) {
-    // about 512 workgroups in all (two per CU), each walking score_iters
-    // iterations of 1024 blocks: fewer histogram flushes per query
-    IndexArgs b = a;
-    const int64_t it_total = (a.cap + kIterBlocks - 1) / kIterBlocks;
-    int64_t iters = (it_total * R + 511) / 512;
-    if (iters < 1) iters = 1;
-    if (iters > it_total) iters = it_total;
-    b.score_iters = (int)iters;
-    dim3 grid((unsigned)((it_total + iters - 1) / iters), R);
-    if (ev)
-      hipExtLaunchKernelGGL(k_score_mx, grid, dim3(256), 0, st, ev->start, ev->stop, 0, b);
-    else
-      hipLaunchKernelGGL(k_score_mx, grid, dim3(256), 0, st, b);
+    dim3 grid((unsigned)a.score_wgs, R);
+    auto go = [&](auto kern) {
+      if (ev)
+        hipExtLaunchKernelGGL(kern, grid, dim3(64 * kScanWaves), 0, st, ev->start, ev->stop, 0, a);
+      else
+        hipLaunchKernelGGL(kern, grid, dim3(64 * kScanWaves), 0, st, a);
+    };
+    const int it = a.score_iters;
+    if (a.hp_ld) {
+      if (it == 4) go(k_score_mx<true, 4>);
+      else if (it == 2) go(k_score_mx<true, 2>);
+      else if (it == 1) go(k_score_mx<true, 1>);
+      else go(k_score_mx<true, 0>);
+    } else {
+      if (it == 4) go(k_score_mx<false, 4>);
+      else if (it == 2) go(k_score_mx<false, 2>);
+      else if (it == 1) go(k_score_mx<false, 1>);
+      else go(k_score_mx<false, 0>);
+    }
   } else {
     dim3 grid((unsigned)((a.cap + 255) / 256), R);
     size_t smem = sizeof(float) * ((size_t)a.H * a.d + a.H) + sizeof(uint32_t) * kBins1;

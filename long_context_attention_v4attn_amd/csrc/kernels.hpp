@@ -40,18 +40,24 @@ struct IndexArgs {
   int d;
   const int64_t* pos;        // [R]
   int B, Q, H, m, k;
-  int score_iters;           // 1024-block iterations per scan workgroup
   int32_t* topk;             // [R][k]
+  // scan plan (one-query-per-workgroup FP4 scan)
+  int score_iters;           // 1024-block iterations per scan workgroup
+  int score_wgs;             // scan workgroups per query
+  int hp_ld;                 // > 0 (= score_wgs): the scan writes per-workgroup
+                             // first-digit histograms and zeroes the filter
+                             // counters itself (no prep kernel)
   // workspace regions
   uint8_t* qmx;              // [R][H][d/2]
   uint8_t* qsc;              // [R][H][d/32]
   float* scores;             // [R][sc_ld]
   int64_t sc_ld;             // score row stride (cap rounded up to 64)
-  uint32_t* hist;            // [R][2048] first-digit histogram (key bits 31..21)
-  uint32_t* hist2;           // [R][2048] second digit (key bits 20..10) within the first
-  uint32_t* ctr;             // [R][8] candidate / finished-workgroup counters, threshold
+  uint32_t* hist;            // [R][256] first-digit histogram (key bits 31..24)
+  uint32_t* hist2;           // [R][2048] second digit (key bits 23..13) within the first
+  uint32_t* ctr;             // [R][8] candidate count, threshold digits
   uint64_t* cand;            // [R][16384] candidate keys (score key : inverted id)
-  uint32_t* chunk;           // [R][n_chunks] selected per filter chunk, then its output offset
+  uint32_t* chunk;           // [R][n_chunks] per filter chunk: ids above the candidates
+  uint16_t* hparts;          // [R][hp_ld][256] per-scan-workgroup first-digit counts
 };
 size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx);
 void index_carve(IndexArgs& a, void* ws);
