@@ -583,7 +583,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
         if (a.out_bf16) {
           const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
           const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-          *(u32x2*)((uint16_t*)a.out + oi) = (u32x2){lo, hi};
+          __builtin_nontemporal_store((u32x2){lo, hi}, (u32x2*)((uint16_t*)a.out + oi));
         } else {
           *(f32x4*)((float*)a.out + oi) = o;
         }
@@ -599,7 +599,10 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
         const f32x4 o = acc[db][ht] * sh.fin[ht * 16 + li];
         const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
         const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-        *(u32x2*)(po + (((int64_t)(wave * 8 + db) * nht + ht) * 64 + lane) * 4) = (u32x2){lo, hi};
+        // streaming stores: the merge reads them once, and lines that do
+        // not sit dirty in L2 need no write-back when the kernel ends
+        __builtin_nontemporal_store((u32x2){lo, hi},
+                                    (u32x2*)(po + (((int64_t)(wave * 8 + db) * nht + ht) * 64 + lane) * 4));
       }
     }
   }
@@ -855,7 +858,7 @@ __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
   if (a.out_bf16) {
     const uint32_t lo = f32_to_bf16_bits(o[0] * inv) | (f32_to_bf16_bits(o[1] * inv) << 16);
     const uint32_t hi = f32_to_bf16_bits(o[2] * inv) | (f32_to_bf16_bits(o[3] * inv) << 16);
-    *(u32x2*)((uint16_t*)a.out + oi) = (u32x2){lo, hi};
+    __builtin_nontemporal_store((u32x2){lo, hi}, (u32x2*)((uint16_t*)a.out + oi));
   } else {
     *(f32x4*)((float*)a.out + oi) = (f32x4){o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
   }

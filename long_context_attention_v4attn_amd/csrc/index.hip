@@ -354,7 +354,9 @@ __device__ __forceinline__ void score_tiles(const KeyTiles& kt, const i32x8* qa,
     // lane group g: tile g; block blk0 + 16 t4 + lane
     const float sc = swap_add16(h0, h1);
     const int64_t blk = blk0 + t4 * 16 + lane;
-    if (in_row || blk < sc_ld) ob[t4 * 16] = sc;
+    // streaming store: the filters read each score once (and dirty L2 lines
+    // would have to be written back when the kernel ends)
+    if (in_row || blk < sc_ld) __builtin_nontemporal_store(sc, ob + t4 * 16);
     // counted only when visible (an invisible block adds 0)
     atomicAdd(&lh[score_key(sc) >> kSh1], blk < nv ? 1u : 0u);
   }
