@@ -632,7 +632,8 @@ __global__ void __launch_bounds__(256) k_score_f32(IndexArgs a) {
 // ---------------------------------------------------------------- filter + select
 
 // Inclusive block scan of one value per thread.
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp,
+                                                    uint32_t* total = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -641,8 +642,12 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
   }
   if (lane == 63) tmp[wave] = v;
   __syncthreads();
-  uint32_t add = 0;
-  for (int w = 0; w < wave; w++) add += tmp[w];
+  uint32_t add = 0, all = 0;
+  for (int w = 0; w < kFThreads / 64; w++) {
+    add += w < wave ? tmp[w] : 0u;
+    all += tmp[w];
+  }
+  if (total) *total = all;
   __syncthreads();
   return v + add;
 }
@@ -1001,6 +1006,22 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
 }
 
 constexpr int kEmitCand = 4096;            // candidates resolved from LDS
+constexpr int kRankCand = 128;             // candidates resolved by counting ranks
+
+// The threshold when the candidates are few and in LDS: the keys are all
+// distinct (the low word is the inverted id), so the need-th largest is the
+// one candidate that exactly need - 1 others exceed.
+__device__ uint64_t rank_threshold(const uint64_t* cl, uint32_t n, uint32_t need) {
+  __shared__ uint64_t s_T;
+  if (threadIdx.x < n) {
+    const uint64_t c = cl[threadIdx.x];
+    uint32_t r = 0;
+    for (uint32_t j = 0; j < n; j++) r += cl[j] > c ? 1u : 0u;
+    if (r == need - 1) s_T = c;
+  }
+  __syncthreads();
+  return s_T;
+}
 
 // Every workgroup of a query resolves the threshold T from the candidates
 // (few: they share the top 19 key bits with the k-th largest score), finds
@@ -1035,7 +1056,9 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   __syncthreads();
   const CandSrc src{in_lds ? cl : gc, n_cand, a.scores + (size_t)row * a.sc_ld, nv, b12,
                     n_cand <= (uint32_t)kCandCap};
-  const uint64_t T = resolve_threshold(src, need, lh, tmp);
+  const uint64_t T = (src.compact && in_lds && n_cand <= (uint32_t)kRankCand)
+                         ? rank_threshold(cl, n_cand, need)
+                         : resolve_threshold(src, need, lh, tmp);
   // offset of this chunk: ids above the bin in earlier chunks, plus the
   // candidates >= T with lower ids
   const int64_t c0 = (int64_t)blockIdx.x * kFilterChunk;
@@ -1052,13 +1075,18 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   uint32_t k32[kPer];
   const int n_in = finish_group(gr, nv, k32);
   const int64_t i0 = gr.g0;
-  const uint32_t base = block_sum(before, tmp);
   uint32_t sel = 0;
 #pragma unroll
   for (int j = 0; j < kPer; j++)
     if (j < n_in && sel_key(k32[j], i0 + j) >= T) sel |= 1u << j;
   const uint32_t cnt = (uint32_t)__builtin_popcount(sel);
-  uint32_t pos = base + block_incl_scan(cnt, tmp) - cnt;
+  // one scan for both: the chunk's offset (sum of `before`, high half) and
+  // this thread's rank in the chunk (prefix of `cnt`, low half); both sums
+  // stay below 2^16 (k <= 4096)
+  const uint32_t packed = (before << 16) | cnt;
+  uint32_t total;
+  const uint32_t incl = block_incl_scan(packed, tmp, &total);
+  uint32_t pos = (total >> 16) + ((incl - packed) & 0xFFFFu);
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
     if ((sel >> j) & 1u) {
