@@ -382,9 +382,8 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
   const uint8_t* kc = (const uint8_t*)a.codes + (size_t)b * a.cap * 64;
   const uint8_t* ks = a.kscales + (size_t)b * a.cap * 4;
   const int64_t wblk = wg0 + wave * (kWaveTiles * 16);
-  // the query's operands first, quantised before any key load is issued:
-  // a compute unit returns loads in order, so behind the keys the query
-  // would arrive only with them
+  // the query's operands first: loads return in order, so the query must not
+  // queue behind keys
   const int64_t p_row = a.pos[row];
   constexpr int kHT = kParts ? 1 : 4;
   const int HT = kParts ? 1 : a.H / 16;
@@ -411,7 +410,6 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
       for (int i = 0; i < 4; i++) wv[ht][i] = w4[i];
     }
   }
-  if (kParts) quantize_q_frag(a, qraw, &qa[0], &qs[0]);
   constexpr int kSets = kIters > 0 ? kIters : 2;
   KeyTiles kt[kSets];
   // kIters > 0: iterations 0 .. kDepth-2 go out now, iteration j + kDepth - 1
@@ -423,6 +421,9 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
   for (int j = 0; j < kSets; j++)
     if (kIters > 0 ? j < kDepth - 1 : j < a.score_iters)
       load_keys(kc, ks, wblk + (int64_t)j * kIterBlocks, a.cap, g, li, kt[j]);
+  // the query loads went out first, so this waits for them alone and runs
+  // while the first keys are on their way
+  if (kParts) quantize_q_frag(a, qraw, &qa[0], &qs[0]);
   if (kParts) {
     // the filter kernels' counters of this query (they run after this kernel)
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < kBins2 + kCtr; i += gridDim.x * blockDim.x) {
