@@ -877,10 +877,17 @@ void attend_plan(AttendArgs& a, int64_t n_entries_max) {
   a.f32_heads = a.fp8 ? 64 : (a.H < 4096 / D ? a.H : (4096 / D > 0 ? 4096 / D : 1));
   // short lists (CSA: k + window) split finer than long ones (HCA), so that
   // a small batch still spreads over the chip; the size depends on the
-  // per-query bound only
-  int64_t per = n_entries_max <= 4096 ? (n_entries_max + 47) / 48 : (n_entries_max + 15) / 16;
-  if (per < 64) per = 64;
-  per = (per + 63) / 64 * 64;               // whole tile pairs
+  // per-query bound only (short: ~24 splits of whole tiles, at least 64
+  // entries; long: ~16 splits of whole tile pairs)
+  int64_t per;
+  if (n_entries_max <= 4096) {
+    per = (n_entries_max + 23) / 24;
+    if (per < 64) per = 64;
+    per = (per + kTile - 1) / kTile * kTile;
+  } else {
+    per = (n_entries_max + 15) / 16;
+    per = (per + 2 * kTile - 1) / (2 * kTile) * (2 * kTile);
+  }
   if (per > kMaxSplit) per = kMaxSplit;
   a.split_size = (int)per;
   int64_t ns = n_entries_max > 0 ? (n_entries_max + per - 1) / per : 1;
