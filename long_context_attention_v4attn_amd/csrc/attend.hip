@@ -156,14 +156,27 @@ constexpr int kHasComp = 1, kHasWin = 2, kHasAbsent = 4;
 // RoPE dims and scale are all zero, so no loaded value needs masking.
 __device__ __align__(256) uint32_t g_zero_row[(kNope + 2 * kRope + 64) / 4];
 
+// CSA: the top-k id of entry e_beg + threadIdx.x, loaded before the query
+// position is known (the k slots exist whatever the position).
+__device__ __forceinline__ int32_t prefetch_topk(const AttendArgs& a, int row, int e_beg) {
+  const int e = e_beg + (int)threadIdx.x;
+  return (a.csa && e < a.k) ? a.topk[(int64_t)row * a.k + e] : -1;
+}
+
 __device__ __forceinline__ void resolve_sources(const AttendArgs& a, const RowEntries& r, int row,
                                                 int e_beg, int e_end, int n_local, int n_tiles,
-                                                int* src, int* tbits) {
+                                                int32_t pre, int* src, int* tbits) {
   for (int i = threadIdx.x; i < kMaxTiles; i += blockDim.x) tbits[i] = i < n_tiles ? 0 : kHasAbsent;
   __syncthreads();
   for (int e = e_beg + threadIdx.x; e < e_end; e += blockDim.x) {
     bool is_win;
-    int64_t sr = entry_source(a, r, row, e, &is_win);
+    int64_t sr;
+    if (a.csa && e < r.n_c && e == e_beg + (int)threadIdx.x) {
+      is_win = false;                      // the prefetched slot
+      sr = (pre >= 0 && pre < a.c_cap) ? (int64_t)pre : -1;
+    } else {
+      sr = entry_source(a, r, row, e, &is_win);
+    }
     const int code = sr < 0 ? -1 : (is_win ? (int)(-2 - sr) : (int)sr);
     src[e - e_beg] = code;
     atomicOr(&tbits[(e - e_beg) / kTile], code >= 0 ? kHasComp : (code == -1 ? kHasAbsent : kHasWin));
@@ -459,6 +472,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   const int nht = min(2, (a.H - hgrp * kHeads) / 16);   // head tiles present (H % 16 == 0)
   const int D = kNope + kRope;
 
+  const int32_t pre = prefetch_topk(a, row, split * a.split_size);
   const RowEntries r = row_entries(a, row);
   const int n_tot = r.n_c + r.n_w;
   const int e_beg = split * a.split_size;
@@ -468,7 +482,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   const int n_local = __builtin_amdgcn_readfirstlane(e_end > e_beg ? e_end - e_beg : 0);
   const int n_tiles = (n_local + kTile - 1) / kTile;
 
-  resolve_sources(a, r, row, e_beg, e_end, n_local, n_tiles, src, sh.tbits);
+  resolve_sources(a, r, row, e_beg, e_end, n_local, n_tiles, pre, src, sh.tbits);
   __syncthreads();
 
   Bases B;

@@ -806,8 +806,6 @@ __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
     issue_group(a, row, blockIdx.x, gr);
     static_assert(8 * kBins1 <= kBins2, "partial-sum scratch fits the histogram buffer");
     h1 = part_sum(pt, lh);
-    // the total for the kernels that follow
-    if (blockIdx.x == 0) a.hist[(size_t)row * kBins1 + threadIdx.x] = h1;
   } else {
     h1 = a.hist[(size_t)row * kBins1 + threadIdx.x];   // kBins1 == kFThreads
     issue_group(a, row, blockIdx.x, gr);
@@ -816,6 +814,11 @@ __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
   __syncthreads();
   find_bin(lh, kBins1, (uint32_t)kk, tmp, &s_bin, &s_above);
   const uint32_t b1 = (uint32_t)s_bin;
+  // the first digit for the kernels that follow
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.ctr[(size_t)row * kCtr + 4] = b1;
+    a.ctr[(size_t)row * kCtr + 5] = s_above;
+  }
   for (int i = threadIdx.x; i < kBins2; i += blockDim.x) lh[i] = 0u;
   uint32_t k32[kPer];
   const int n_in = finish_group(gr, nv, k32);
@@ -962,18 +965,16 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
   const int kk = (int)(nv < a.k ? nv : a.k);
   if (kk == nv || (int64_t)blockIdx.x * kFilterChunk >= nv) return;
-  // all global loads first: both histograms, then this thread's scores
-  const uint32_t h1 = a.hist[(size_t)row * kBins1 + threadIdx.x];   // kBins1 == kFThreads
+  // all global loads first: the first digit (published by k_filter1), the
+  // second histogram, then this thread's scores
+  uint32_t* ctr = a.ctr + (size_t)row * kCtr;
+  const uint32_t b1 = ctr[4], above1 = ctr[5];
   constexpr int kPer2 = kBins2 / kFThreads;                          // 8
   const u32x4* gh2 = (const u32x4*)(a.hist2 + (size_t)row * kBins2 + threadIdx.x * kPer2);
   const u32x4 h2a = gh2[0], h2b = gh2[1];
   Group gr;
   issue_group(a, row, blockIdx.x, gr);
-  lh[threadIdx.x] = h1;
   if (threadIdx.x == 0) cand_n = 0;
-  __syncthreads();
-  find_bin(lh, kBins1, (uint32_t)kk, tmp, &s_bin, &s_above);
-  const uint32_t b1 = (uint32_t)s_bin, above1 = s_above;
   *(u32x4*)&lh[threadIdx.x * kPer2] = h2a;
   *(u32x4*)&lh[threadIdx.x * kPer2 + 4] = h2b;
   __syncthreads();
@@ -983,7 +984,6 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   const int n_in = finish_group(gr, nv, k32);
   const int64_t i0 = gr.g0;
   FilterRow fr{nv, kk, b1, above1};
-  uint32_t* ctr = a.ctr + (size_t)row * kCtr;
   uint64_t* cand = a.cand + (size_t)row * kCandCap;
   CandList cnd{cand_buf, &cand_n};
   uint32_t above = 0;
