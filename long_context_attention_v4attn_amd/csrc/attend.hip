@@ -164,24 +164,38 @@ __device__ __forceinline__ int32_t prefetch_topk(const AttendArgs& a, int row, i
 }
 
 __device__ __forceinline__ void resolve_sources(const AttendArgs& a, const RowEntries& r, int row,
-                                                int e_beg, int e_end, int n_local, int n_tiles,
-                                                int32_t pre, int* src, int* tbits) {
-  for (int i = threadIdx.x; i < kMaxTiles; i += blockDim.x) tbits[i] = i < n_tiles ? 0 : kHasAbsent;
-  __syncthreads();
-  for (int e = e_beg + threadIdx.x; e < e_end; e += blockDim.x) {
-    bool is_win;
-    int64_t sr;
-    if (a.csa && e < r.n_c && e == e_beg + (int)threadIdx.x) {
-      is_win = false;                      // the prefetched slot
-      sr = (pre >= 0 && pre < a.c_cap) ? (int64_t)pre : -1;
-    } else {
-      sr = entry_source(a, r, row, e, &is_win);
+                                                int e_beg, int n_local, int n_tiles, int32_t pre,
+                                                int* src, int* tbits) {
+  const int lane = threadIdx.x & 63;
+  for (int i = n_tiles + threadIdx.x; i < kMaxTiles; i += blockDim.x) tbits[i] = kHasAbsent;
+  // local entry l = base + thread; splits start on tile boundaries, so each
+  // half-wave covers one tile and its kinds come from three ballots (slots
+  // past the split count as absent)
+  for (int base = 0; base < n_tiles * kTile; base += blockDim.x) {
+    const int l = base + (int)threadIdx.x;
+    int code = -1;
+    if (l < n_local) {
+      const int e = e_beg + l;
+      bool is_win;
+      int64_t sr;
+      if (a.csa && e < r.n_c && base == 0) {
+        is_win = false;                    // the prefetched slot
+        sr = (pre >= 0 && pre < a.c_cap) ? (int64_t)pre : -1;
+      } else {
+        sr = entry_source(a, r, row, e, &is_win);
+      }
+      code = sr < 0 ? -1 : (is_win ? (int)(-2 - sr) : (int)sr);
+      src[l] = code;
     }
-    const int code = sr < 0 ? -1 : (is_win ? (int)(-2 - sr) : (int)sr);
-    src[e - e_beg] = code;
-    atomicOr(&tbits[(e - e_beg) / kTile], code >= 0 ? kHasComp : (code == -1 ? kHasAbsent : kHasWin));
+    const uint64_t mc = __builtin_amdgcn_ballot_w64(code >= 0);
+    const uint64_t mw = __builtin_amdgcn_ballot_w64(code < -1);
+    const uint64_t ma = __builtin_amdgcn_ballot_w64(code == -1);
+    if ((lane & 31) == 0 && l < n_tiles * kTile) {
+      const uint64_t half = lane == 0 ? 0xFFFFFFFFull : 0xFFFFFFFF00000000ull;
+      tbits[l / kTile] = ((mc & half) ? kHasComp : 0) | ((mw & half) ? kHasWin : 0) |
+                         ((ma & half) ? kHasAbsent : 0);
+    }
   }
-  if (threadIdx.x == 0 && (n_local % kTile) != 0) atomicOr(&tbits[n_local / kTile], kHasAbsent);
 }
 
 // Per-sequence bases of the compressed cache and the window ring.
@@ -482,7 +496,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   const int n_local = __builtin_amdgcn_readfirstlane(e_end > e_beg ? e_end - e_beg : 0);
   const int n_tiles = (n_local + kTile - 1) / kTile;
 
-  resolve_sources(a, r, row, e_beg, e_end, n_local, n_tiles, pre, src, sh.tbits);
+  resolve_sources(a, r, row, e_beg, n_local, n_tiles, pre, src, sh.tbits);
   __syncthreads();
 
   Bases B;
