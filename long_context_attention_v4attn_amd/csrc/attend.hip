@@ -212,29 +212,43 @@ struct Bases {
 // the number of loads per tile is fixed and the compiler can keep later
 // tiles' loads in flight when it waits for an earlier one.  The address path
 // branches on the tile's kind, which is uniform across the workgroup.
-__device__ __forceinline__ void stage_load(Bases B, const int* src, const int* tbits,
-                                           int tile, int n_local, Stage& st) {
+// The LDS side of a tile's staging (its kind, this thread's entry source),
+// read a step ahead of the loads so that their addresses do not wait on LDS.
+struct StageSrc {
+  int bits;
+  int sraw;
+};
+
+__device__ __forceinline__ StageSrc stage_src(const int* src, const int* tbits, int tile) {
+  const int le = tile * kTile + ((int)threadIdx.x >> 3);
+  StageSrc r;
+  r.bits = tbits[tile];
+  r.sraw = src[le < kMaxSplit ? le : kMaxSplit - 1];   // always in bounds
+  return r;
+}
+
+__device__ __forceinline__ void stage_load(Bases B, StageSrc ss, int tile, int n_local,
+                                           Stage& st) {
   const int t = threadIdx.x;
   const int q = t & 7;
   const int le = tile * kTile + (t >> 3);
-  const int bits = __builtin_amdgcn_readfirstlane(tbits[tile]);
+  const int bits = __builtin_amdgcn_readfirstlane(ss.bits);
   const uint8_t* nope;
   const uint8_t* rope;
   const float* scp;
   int ok = 1;
   if (bits == kHasComp) {
-    const int64_t rr = src[le];
+    const int64_t rr = ss.sraw;
     nope = B.cn + rr * kNope;
     rope = B.cr + rr * (2 * kRope);
     scp = B.cs + rr;
   } else if (bits == kHasWin) {
-    const int64_t rr = -2 - src[le];
+    const int64_t rr = -2 - ss.sraw;
     nope = B.wn + rr * kNope;
     rope = B.wr + rr * (2 * kRope);
     scp = B.ws + rr;
   } else {
-    const int sraw = src[le < kMaxSplit ? le : kMaxSplit - 1];   // always in bounds
-    const int s = le < n_local ? sraw : -1;
+    const int s = le < n_local ? ss.sraw : -1;
     const bool is_win = s < -1;
     const int64_t rr = is_win ? (int64_t)(-2 - s) : (int64_t)s;
     ok = s != -1;
@@ -344,6 +358,49 @@ __device__ __forceinline__ void qk_partial(const Fp8Tile* tl, Shared* sh, const 
   }
 }
 
+// Reductions over the 8 lanes of a softmax head (lane bits 3..5) without
+// LDS: lane ^ 8 by a DPP rotate of each 16-lane row by 8, lane ^ 16 and
+// lane ^ 32 by v_permlane16_swap / v_permlane32_swap of a value with itself
+// (each lane ends up with its own value and its partner's).  Every lane of a
+// head combines the same values, so all eight hold identical results.
+// (The empty asm statement keeps the compiler from folding the two results
+// of a swap into one value.)
+constexpr int kDppRowRor8 = 0x128;         // row_ror:8
+
+__device__ __forceinline__ float xor8_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               kDppRowRor8, 0xF, 0xF, false));
+}
+
+template <bool kSwap32>
+__device__ __forceinline__ void swap_pair(float v, float& a, float& b) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, v);
+  auto r = kSwap32 ? __builtin_amdgcn_permlane32_swap(x, x, false, false)
+                   : __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  uint32_t lo = r[0], hi = r[1];
+  __asm__ volatile("" : "+v"(lo), "+v"(hi));
+  a = __builtin_bit_cast(float, lo);
+  b = __builtin_bit_cast(float, hi);
+}
+
+__device__ __forceinline__ float head_max(float v) {
+  float a, b;
+  v = fmaxf(v, xor8_f(v));
+  swap_pair<false>(v, a, b);
+  v = fmaxf(a, b);
+  swap_pair<true>(v, a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float head_sum(float v) {
+  float a, b;
+  v += xor8_f(v);
+  swap_pair<false>(v, a, b);
+  v = a + b;
+  swap_pair<true>(v, a, b);
+  return a + b;
+}
+
 // Softmax of wave w's 8 heads: lane = head h (lane & 7) x entry group eg
 // (lane >> 3, entries 4eg .. 4eg+3).  Writes P^T and (P * scale)^T in the
 // PV operand layout: head tile j / 16, lane (j % 16) + 16 (eg % 4), slots
@@ -362,9 +419,7 @@ __device__ __forceinline__ void softmax_tile(const Fp8Tile* tl, Shared* sh, Soft
     s2[i] = (((a0[i] + a1[i]) + a2[i]) + a3[i]) * c2 + bi[i];
     tmax = fmaxf(tmax, s2[i]);
   }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 8, 64));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  tmax = head_max(tmax);
   // lazy rescale: the running max moves only when it grows by more than
   // kRescale (exact: P <= 2^kRescale, and the final normalisation uses the
   // same max); the factor goes to the PV waves through LDS
@@ -510,7 +565,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   // two tiles in flight in registers while another is computed; every
   // stage_load issues the same loads (tiles past the split read the zero row)
   Stage st0, st1;
-  stage_load(B, src, sh.tbits, 0, n_local, st0);
+  stage_load(B, stage_src(src, sh.tbits, 0), 0, n_local, st0);
 
   // Q^T fragments of this wave's dim quarter (MFMA B operand): k-steps 0..6
   // cover FP8 dims 112 wave + 16 ks .. +15, k-step 7 RoPE dims 448 + 16 wave
@@ -542,9 +597,9 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
 
   // load order tile 0, Q, tile 1, tile 2: at the loop entry, as at every
   // back edge, the older register set is the one stored next
-  stage_load(B, src, sh.tbits, 1, n_local, st1);
+  stage_load(B, stage_src(src, sh.tbits, 1), 1, n_local, st1);
   stage_store(&tiles[0], st0);
-  stage_load(B, src, sh.tbits, 2, n_local, st0);
+  stage_load(B, stage_src(src, sh.tbits, 2), 2, n_local, st0);
   __syncthreads();
 
   // step t: partial logits of tile t | softmax of tile t, tile t+1 into LDS,
@@ -554,11 +609,12 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   // only after a barrier that follows its last read.  Unrolled by two so
   // that the register sets alternate statically.
   auto step = [&](int t, Stage& nxt) {
+    const StageSrc ns = stage_src(src, sh.tbits, t + 3);
     qk_partial(&tiles[t & 1], &sh, qf, wave, lane);
     __syncthreads();
     softmax_tile(&tiles[t & 1], &sh, S, c2, wave, lane);
     stage_store(&tiles[(t + 1) & 1], nxt);
-    stage_load(B, src, sh.tbits, t + 3, n_local, nxt);
+    stage_load(B, ns, t + 3, n_local, nxt);
     __syncthreads();
     pv_slice(&tiles[t & 1], &sh, acc, wave, g, li);
   };
@@ -571,9 +627,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
 
   // ---- epilogue: the softmax lanes of entry group 0 publish each head's
   // factor (the denominator summed over the head's 8 lanes)
-  float l_tot = S.l_run + __shfl_xor(S.l_run, 8, 64);
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float l_tot = head_sum(S.l_run);
   if (lane < 8) {
     const int jh = 8 * wave + lane;
     const int head = hgrp * kHeads + jh;
