@@ -874,6 +874,7 @@ __global__ void __launch_bounds__(256) k_merge(AttendArgs a) {
 // s = p, p + 4, ... and the phases combine their maxima, then their weighted
 // sums, through LDS in fixed order (deterministic).
 constexpr int kMergePhases = 4;
+constexpr int kMergeRegs = 8;              // splits per phase held in registers
 
 __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
   __shared__ float red[kMergePhases][64][6];
@@ -892,34 +893,71 @@ __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
   const int head = hgrp * kHeads + ht * 16 + (ln & 15);
   const int d0 = pv_dim0(sb >> 3, sb & 7) + (ln >> 4) * 4;
   const f32x2* ml = (const f32x2*)a.part_ml + (int64_t)row * a.n_split * a.H + head;
-  // ---- the maximum over all splits (and the sink)
-  float M = -INFINITY;
-#pragma unroll 4
-  for (int s = ph; s < a.n_split; s += kMergePhases) M = fmaxf(M, ml[(int64_t)s * a.H][0]);
-  red[ph][vg][0] = M;
-  __syncthreads();
-  const float z2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
-  M = z2;
-#pragma unroll
-  for (int p = 0; p < kMergePhases; p++) M = fmaxf(M, red[p][vg][0]);
-  // ---- this phase's weighted sums
+  // (an inactive thread reads the block's first values: always in bounds)
+  const uint16_t* po = (const uint16_t*)a.part_o + part_block(a, row, 0, hgrp) + (active ? j : 0);
+  const int64_t sstride = (int64_t)a.H * D;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  if (M != -INFINITY) {
-    // (an inactive thread reads the block's first values: always in bounds)
-    const uint16_t* po = (const uint16_t*)a.part_o + part_block(a, row, 0, hgrp) + (active ? j : 0);
-    const int64_t sstride = (int64_t)a.H * D;
-    // an empty split has m = -inf, hence weight 0, and zero partials
+  float M = -INFINITY;
+  const float z2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
+  if (a.n_split <= kMergePhases * kMergeRegs) {
+    // every split of this phase in registers before the first wait: the
+    // maxima and the partials come in one round trip
+    f32x2 mv[kMergeRegs];
+    u32x2 ov[kMergeRegs];
+#pragma unroll
+    for (int i = 0; i < kMergeRegs; i++) {
+      const int sp = ph + kMergePhases * i;
+      mv[i] = (f32x2){-INFINITY, 0.f};
+      ov[i] = (u32x2){0u, 0u};
+      if (sp < a.n_split) {
+        mv[i] = ml[(int64_t)sp * a.H];
+        ov[i] = *(const u32x2*)(po + sp * sstride);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeRegs; i++) M = fmaxf(M, mv[i][0]);
+    red[ph][vg][0] = M;
+    __syncthreads();
+    M = z2;
+#pragma unroll
+    for (int p = 0; p < kMergePhases; p++) M = fmaxf(M, red[p][vg][0]);
+    if (M != -INFINITY) {
+      // an empty split has m = -inf, hence weight 0, and zero partials
+#pragma unroll
+      for (int i = 0; i < kMergeRegs; i++) {
+        if (ph + kMergePhases * i < a.n_split) {
+          const float w = mv[i][1] * exp2f(mv[i][0] - M);
+          den += w;
+          acc[0] += w * bf16_bits_to_f32(ov[i][0] & 0xFFFFu);
+          acc[1] += w * bf16_bits_to_f32(ov[i][0] >> 16);
+          acc[2] += w * bf16_bits_to_f32(ov[i][1] & 0xFFFFu);
+          acc[3] += w * bf16_bits_to_f32(ov[i][1] >> 16);
+        }
+      }
+    }
+  } else {
+    // ---- the maximum over all splits (and the sink)
 #pragma unroll 4
-    for (int s = ph; s < a.n_split; s += kMergePhases) {
-      const f32x2 v_ml = ml[(int64_t)s * a.H];
-      const u32x2 v = *(const u32x2*)(po + s * sstride);
-      const float w = v_ml[1] * exp2f(v_ml[0] - M);
-      den += w;
-      acc[0] += w * bf16_bits_to_f32(v[0] & 0xFFFFu);
-      acc[1] += w * bf16_bits_to_f32(v[0] >> 16);
-      acc[2] += w * bf16_bits_to_f32(v[1] & 0xFFFFu);
-      acc[3] += w * bf16_bits_to_f32(v[1] >> 16);
+    for (int sp = ph; sp < a.n_split; sp += kMergePhases) M = fmaxf(M, ml[(int64_t)sp * a.H][0]);
+    red[ph][vg][0] = M;
+    __syncthreads();
+    M = z2;
+#pragma unroll
+    for (int p = 0; p < kMergePhases; p++) M = fmaxf(M, red[p][vg][0]);
+    // ---- this phase's weighted sums
+    if (M != -INFINITY) {
+#pragma unroll 4
+      for (int sp = ph; sp < a.n_split; sp += kMergePhases) {
+        const f32x2 v_ml = ml[(int64_t)sp * a.H];
+        const u32x2 v = *(const u32x2*)(po + sp * sstride);
+        const float w = v_ml[1] * exp2f(v_ml[0] - M);
+        den += w;
+        acc[0] += w * bf16_bits_to_f32(v[0] & 0xFFFFu);
+        acc[1] += w * bf16_bits_to_f32(v[0] >> 16);
+        acc[2] += w * bf16_bits_to_f32(v[1] & 0xFFFFu);
+        acc[3] += w * bf16_bits_to_f32(v[1] >> 16);
+      }
     }
   }
   red[ph][vg][1] = den;
