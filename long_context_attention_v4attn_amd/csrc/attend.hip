@@ -541,6 +541,25 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   const int nht = min(2, (a.H - hgrp * kHeads) / 16);   // head tiles present (H % 16 == 0)
   const int D = kNope + kRope;
 
+  // Q^T fragments of this wave's dim quarter (MFMA B operand), the first
+  // loads the workgroup issues (they depend on nothing): k-steps 0..6
+  // cover FP8 dims 112 wave + 16 ks .. +15, k-step 7 RoPE dims 448 + 16 wave
+  // .. +15; the lane holds dims +8 (lane >> 5) .. +8 of head lane & 31 (zero
+  // for heads beyond H)
+  bf16x8 qf[8];
+  {
+    const int qh = hgrp * kHeads + (lane & 31);
+    const bool q_ok = qh < a.H;
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.H + (q_ok ? qh : 0)) * D +
+                         8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 8; ks++) {
+      const int d0 = ks < 7 ? 112 * wave + 16 * ks : kNope + 16 * wave;
+      u32x4 v = *(const u32x4*)(qp + d0);
+      if (!q_ok) v = (u32x4){0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
   const int32_t pre = prefetch_topk(a, row, split * a.split_size);
   const RowEntries r = row_entries(a, row);
   const int n_tot = r.n_c + r.n_w;
@@ -567,24 +586,6 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   Stage st0, st1;
   stage_load(B, stage_src(src, sh.tbits, 0), 0, n_local, st0);
 
-  // Q^T fragments of this wave's dim quarter (MFMA B operand): k-steps 0..6
-  // cover FP8 dims 112 wave + 16 ks .. +15, k-step 7 RoPE dims 448 + 16 wave
-  // .. +15; the lane holds dims +8 (lane >> 5) .. +8 of head lane & 31 (zero
-  // for heads beyond H)
-  bf16x8 qf[8];
-  {
-    const int qh = hgrp * kHeads + (lane & 31);
-    const bool q_ok = qh < a.H;
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.H + (q_ok ? qh : 0)) * D +
-                         8 * (lane >> 5);
-#pragma unroll
-    for (int ks = 0; ks < 8; ks++) {
-      const int d0 = ks < 7 ? 112 * wave + 16 * ks : kNope + 16 * wave;
-      u32x4 v = *(const u32x4*)(qp + d0);
-      if (!q_ok) v = (u32x4){0u, 0u, 0u, 0u};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
   f32x4 acc[8][2];
 #pragma unroll
   for (int i = 0; i < 8; i++)
@@ -595,9 +596,10 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   S.l_run = 0.0f;
   const float c2 = a.sm_scale * kLog2e;
 
-  // load order tile 0, Q, tile 1, tile 2: at the loop entry, as at every
+  // load order Q, tile 0, tile 1, tile 2: at the loop entry, as at every
   // back edge, the older register set is the one stored next
   stage_load(B, stage_src(src, sh.tbits, 1), 1, n_local, st1);
+  __builtin_amdgcn_sched_barrier(0);       // tile 1's loads stay ahead of tile 0's wait
   stage_store(&tiles[0], st0);
   stage_load(B, stage_src(src, sh.tbits, 2), 2, n_local, st0);
   __syncthreads();
