@@ -786,6 +786,16 @@ __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
   __shared__ int s_bin;
   __shared__ uint32_t s_above;
   const int row = blockIdx.y;
+  // all global loads first, before the query position arrives (no address
+  // depends on it): the first histogram (bin = thread), this thread's scores
+  Parts pt;
+  uint32_t h1 = 0;
+  Group gr;
+  if (a.hp_ld)
+    load_parts(a, row, pt);
+  else
+    h1 = a.hist[(size_t)row * kBins1 + threadIdx.x];   // kBins1 == kFThreads
+  issue_group(a, row, blockIdx.x, gr);
   const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
   const int kk = (int)(nv < a.k ? nv : a.k);
   if (kk == nv) {                          // everything visible is selected
@@ -796,20 +806,8 @@ __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
     return;
   }
   if ((int64_t)blockIdx.x * kFilterChunk >= nv) return;
-  // all global loads first: the first histogram (bin = thread), then this
-  // thread's scores
-  uint32_t h1;
-  Group gr;
-  if (a.hp_ld) {
-    Parts pt;
-    load_parts(a, row, pt);
-    issue_group(a, row, blockIdx.x, gr);
-    static_assert(8 * kBins1 <= kBins2, "partial-sum scratch fits the histogram buffer");
-    h1 = part_sum(pt, lh);
-  } else {
-    h1 = a.hist[(size_t)row * kBins1 + threadIdx.x];   // kBins1 == kFThreads
-    issue_group(a, row, blockIdx.x, gr);
-  }
+  static_assert(8 * kBins1 <= kBins2, "partial-sum scratch fits the histogram buffer");
+  if (a.hp_ld) h1 = part_sum(pt, lh);
   lh[threadIdx.x] = h1;
   __syncthreads();
   find_bin(lh, kBins1, (uint32_t)kk, tmp, &s_bin, &s_above);
@@ -962,11 +960,8 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   __shared__ int s_bin;
   __shared__ uint32_t s_above, cand_n, s_base;
   const int row = blockIdx.y;
-  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
-  const int kk = (int)(nv < a.k ? nv : a.k);
-  if (kk == nv || (int64_t)blockIdx.x * kFilterChunk >= nv) return;
-  // all global loads first: the first digit (published by k_filter1), the
-  // second histogram, then this thread's scores
+  // all global loads first, before the query position arrives: the first
+  // digit (published by k_filter1), the second histogram, this thread's scores
   uint32_t* ctr = a.ctr + (size_t)row * kCtr;
   const uint32_t b1 = ctr[4], above1 = ctr[5];
   constexpr int kPer2 = kBins2 / kFThreads;                          // 8
@@ -974,6 +969,9 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   const u32x4 h2a = gh2[0], h2b = gh2[1];
   Group gr;
   issue_group(a, row, blockIdx.x, gr);
+  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
+  const int kk = (int)(nv < a.k ? nv : a.k);
+  if (kk == nv || (int64_t)blockIdx.x * kFilterChunk >= nv) return;
   if (threadIdx.x == 0) cand_n = 0;
   *(u32x4*)&lh[threadIdx.x * kPer2] = h2a;
   *(u32x4*)&lh[threadIdx.x * kPer2 + 4] = h2b;
@@ -1032,15 +1030,9 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   __shared__ uint32_t tmp[kFThreads / 64];
   __shared__ uint64_t cl[kEmitCand];
   const int row = blockIdx.y;
-  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
-  const int kk = (int)(nv < a.k ? nv : a.k);
-  if (kk == nv) return;                    // written by k_filter1
-  int32_t* out = a.topk + (size_t)row * a.k;
-  if (blockIdx.x == 0)
-    for (int i = kk + threadIdx.x; i < a.k; i += blockDim.x) out[i] = -1;
-  if ((int64_t)blockIdx.x * kFilterChunk >= nv) return;
-  // all global loads first: counters, the first candidates (speculatively:
-  // the list always has kCandCap slots), the earlier chunks' counts, scores
+  // all global loads first, before the query position arrives: counters, the
+  // first candidates (speculatively: the list always has kCandCap slots), the
+  // earlier chunks' counts, scores
   const uint32_t* ctr = a.ctr + (size_t)row * kCtr;
   const uint32_t n_cand = ctr[0], b12 = ctr[2], need = ctr[3];
   const uint64_t* gc = a.cand + (size_t)row * kCandCap;
@@ -1049,6 +1041,13 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   const uint32_t cc_first = (int)threadIdx.x < (int)blockIdx.x ? cc[threadIdx.x] : 0u;
   Group gr;
   issue_group(a, row, blockIdx.x, gr);
+  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
+  const int kk = (int)(nv < a.k ? nv : a.k);
+  if (kk == nv) return;                    // written by k_filter1
+  int32_t* out = a.topk + (size_t)row * a.k;
+  if (blockIdx.x == 0)
+    for (int i = kk + threadIdx.x; i < a.k; i += blockDim.x) out[i] = -1;
+  if ((int64_t)blockIdx.x * kFilterChunk >= nv) return;
   const bool in_lds = n_cand <= (uint32_t)kEmitCand;
   if (in_lds) {
     if (threadIdx.x < n_cand) cl[threadIdx.x] = c_first;
