@@ -79,16 +79,20 @@ def _gpu_csa(lib, case):
     return topk.cpu().numpy(), out
 
 
-@pytest.mark.parametrize("wid", [2, 4])
-def test_csa_decode_full_size_sampled_rows(lib, wid):
+# (workload, batch): the benchmark batches, then 1M-context batches whose
+# index scan takes the other launch shapes (1, 3 and 6 iterations per
+# workgroup; with and without the per-workgroup partial histograms)
+@pytest.mark.parametrize("wid,B", [(2, None), (4, None), (4, 1), (4, 3), (4, 6)])
+def test_csa_decode_full_size_sampled_rows(lib, wid, B):
     c = synth.WORKLOADS[wid]
-    print(f"workload {wid}: CSA decode B={c['B']} ctx={c['ctx']}", flush=True)
-    last = c["B"] - 1
-    case = _decode_case(lib, wid, distinct=[0, last])
+    B = c["B"] if B is None else B
+    print(f"workload {wid}: CSA decode B={B} ctx={c['ctx']}", flush=True)
+    last = B - 1
+    case = _decode_case(lib, wid, B=B, distinct=sorted({0, last}))
     topk, out = _gpu_csa(lib, case)
     g = case["g"]
     qi = C.bf16_decode(case["qib"]).astype(np.float32)
-    for b in (0, last):                             # sampled rows
+    for b in sorted({0, last}):                     # sampled rows
         sc = index_scores(qi[b:b + 1], g["w"][b:b + 1],
                           C.Idx("mxfp4", 128, case["keys"].codes[b:b + 1], case["keys"].scales[b:b + 1]),
                           g["pos"][b:b + 1], c["m"])
