@@ -66,7 +66,8 @@ typedef int32_t v4a_status;
  * cap.  Entry value (used as both key and value, [Notes §7] shared-KV MQA):
  *   V4A_F32:             nope f32 [B][cap][d_nope] ++ rope f32 [B][cap][d_rope]
  *   V4A_KV_FP8_BF16ROPE: nope u8 e4m3fn [B][cap][d_nope] times scale f32 [B][cap],
- *                        ++ rope bf16 [B][cap][d_rope]
+ *                        ++ rope bf16 [B][cap][d_rope]; scales are finite and
+ *                        >= 0 (v4attn_compress writes amax / 448)
  */
 typedef struct {
   int32_t fmt;      /* V4A_F32 | V4A_KV_FP8_BF16ROPE                          */

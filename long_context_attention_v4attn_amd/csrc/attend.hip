@@ -13,17 +13,20 @@
 //                 one query (two workgroups per compute unit).  The entry
 //                 list is walked in tiles of 32 entries staged (raw FP8 codes
 //                 + BF16 RoPE + fp32 scale) in LDS once per workgroup:
-//                   S = K Q^T   by dim quarter: wave w computes all 32 x 32
-//                         logits over its 112 FP8 + 16 RoPE dims with
-//                         v_mfma_f32_32x32x16_bf16 (K rows read with
-//                         ds_read_b64 and widened e4m3 -> bf16 exactly, Q^T in
-//                         registers); the partials are added through LDS;
-//                   softmax by head: wave w owns heads 8w .. 8w+7;
-//                   O^T += V^T P^T by dim slice: wave w owns the same dims
-//                         for all 32 heads; V^T fragments come straight from
-//                         the row-major tile with ds_read_b64_tr_b8 / _tr_b16
-//                         (transpose loads), are widened once and feed one
-//                         v_mfma_f32_16x16x32_bf16 per 16-head tile.
+//                   S = K Q^T   by (entry half, head tile): wave w computes
+//                         the complete logits of 16 entries x 16 heads over
+//                         all 512 dims with v_mfma_f32_16x16x32_bf16 (K rows
+//                         read with ds_read_b128 and widened e4m3 -> bf16
+//                         exactly, Q^T in registers);
+//                   softmax in those registers (the two waves of a head tile
+//                         share a lazily updated running max);
+//                   O^T += V^T P^T by dim slice: wave w owns 112 FP8 + 16
+//                         RoPE dims for all 32 heads; V^T fragments come
+//                         straight from the row-major tile with
+//                         ds_read_b64_tr_b8 / _tr_b16 (transpose loads), are
+//                         widened once and feed one v_mfma_f32_16x16x32_bf16
+//                         per 16-head tile; P^T comes through LDS.
+//                 One barrier per tile (three tile buffers, two P buffers).
 //                 The per-entry FP8 scale multiplies the non-RoPE logit and
 //                 the non-RoPE probability in fp32, so decoding adds no
 //                 rounding.  Online softmax in base 2 with a lazily updated
@@ -106,7 +109,7 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// 4 fp32 -> 4 bf16 (round to nearest even), packed.
+// 4 fp32 -> 4 bf16 (round to nearest even, v_cvt_pk_bf16_f32), packed.
 __device__ __forceinline__ u32x2 pack4(const float* v) {
   const bf16x2 lo = {(__bf16)v[0], (__bf16)v[1]};
   const bf16x2 hi = {(__bf16)v[2], (__bf16)v[3]};
@@ -135,11 +138,11 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint8_t* p) {
 // Staging: the 8 threads t = 8e .. 8e+7 move entry e of the tile, so a thread
 // resolves one entry's row per tile.  Thread q = t & 7 moves the 16-byte
 // chunks q, 8 + q, 16 + q and 24 + q (q < 4) of the FP8 codes, or RoPE chunk
-// q - 4 (q >= 4), plus RoPE chunk 4 + (q & 3) and the entry's scale.
+// q - 4 (q >= 4), plus RoPE chunk 4 + (q & 3) and the entry's scale (-1 for
+// an absent entry).
 struct Stage {
   u32x4 r[5];
   float sc;
-  int ok;                                  // the entry is present
 };
 
 // Source of every entry of this workgroup's split, resolved once into LDS
@@ -152,15 +155,27 @@ constexpr int kMaxSplit = 2048;
 constexpr int kMaxTiles = kMaxSplit / kTile + 3;   // + the three prefetched past the end
 constexpr int kHasComp = 1, kHasWin = 2, kHasAbsent = 4;
 
-// An absent entry (or a slot past the split) reads this zero row: its codes,
-// RoPE dims and scale are all zero, so no loaded value needs masking.
-__device__ __align__(256) uint32_t g_zero_row[(kNope + 2 * kRope + 64) / 4];
+// An absent entry (or a slot past the split) reads this row: zero codes and
+// RoPE dims, and in place of a scale the marker -1 (cache scales are >= 0),
+// which staging turns into scale 0 and mask -inf.
+struct __align__(256) AbsentRow {
+  uint32_t zero[(kNope + 2 * kRope) / 4];
+  float marker;
+};
+__device__ AbsentRow g_absent = {{}, -1.0f};
 
-// CSA: the top-k id of entry e_beg + threadIdx.x, loaded before the query
-// position is known (the k slots exist whatever the position).
+// CSA: the top-k id of entry e_beg + threadIdx.x, the workgroup's first load
+// (the gather of the first tiles waits on it; the k slots exist whatever the
+// query position).  The load is unconditional (a clamped slot, or the
+// position array when there is no top-k list) and its value is returned
+// as loaded: a load under a branch, or a select on its value, makes the
+// compiler wait for it right away.  Only CSA slots e < k use the value.
 __device__ __forceinline__ int32_t prefetch_topk(const AttendArgs& a, int row, int e_beg) {
   const int e = e_beg + (int)threadIdx.x;
-  return (a.csa && e < a.k) ? a.topk[(int64_t)row * a.k + e] : -1;
+  const bool has = a.csa && a.k > 0;
+  const int32_t* p = has ? a.topk + (int64_t)row * a.k + (e < a.k ? e : a.k - 1)
+                         : (const int32_t*)(a.pos + row);
+  return *p;
 }
 
 __device__ __forceinline__ void resolve_sources(const AttendArgs& a, const RowEntries& r, int row,
@@ -236,7 +251,6 @@ __device__ __forceinline__ void stage_load(Bases B, StageSrc ss, int tile, int n
   const uint8_t* nope;
   const uint8_t* rope;
   const float* scp;
-  int ok = 1;
   if (bits == kHasComp) {
     const int64_t rr = ss.sraw;
     nope = B.cn + rr * kNope;
@@ -251,8 +265,7 @@ __device__ __forceinline__ void stage_load(Bases B, StageSrc ss, int tile, int n
     const int s = le < n_local ? ss.sraw : -1;
     const bool is_win = s < -1;
     const int64_t rr = is_win ? (int64_t)(-2 - s) : (int64_t)s;
-    ok = s != -1;
-    const uint8_t* zero = (const uint8_t*)g_zero_row;
+    const uint8_t* zero = (const uint8_t*)g_absent.zero;
     if (is_win) {
       nope = B.wn + rr * kNope;
       rope = B.wr + rr * (2 * kRope);
@@ -262,10 +275,10 @@ __device__ __forceinline__ void stage_load(Bases B, StageSrc ss, int tile, int n
       rope = B.cr + rr * (2 * kRope);
       scp = B.cs + rr;
     }
-    if (!ok) {
+    if (s == -1) {
       nope = zero;
       rope = zero + kNope;
-      scp = (const float*)zero;
+      scp = &g_absent.marker;
     }
   }
   // the values are stored to LDS one step later: using them now would make
@@ -277,7 +290,6 @@ __device__ __forceinline__ void stage_load(Bases B, StageSrc ss, int tile, int n
       (const u32x4*)(q < 4 ? nope + (24 + q) * 16 : rope + (q - 4) * 16));
   st.r[4] = __builtin_nontemporal_load((const u32x4*)(rope + (4 + (q & 3)) * 16));
   st.sc = *scp;
-  st.ok = ok;
 }
 
 // Every value is stored unconditionally (duplicates write identical values),
@@ -291,87 +303,93 @@ __device__ __forceinline__ void stage_store(Fp8Tile* tl, const Stage& st) {
   *(u32x4*)(dst + (16 + q) * 16) = st.r[2];
   *(u32x4*)(dst + (q < 4 ? (24 + q) * 16 : kNope + (q - 4) * 16)) = st.r[3];
   *(u32x4*)(dst + kNope + (4 + (q & 3)) * 16) = st.r[4];
-  tl->scale[e] = st.sc;
-  tl->bias[e] = st.ok ? 0.0f : -INFINITY;
+  tl->scale[e] = st.sc < 0.0f ? 0.0f : st.sc;
+  tl->bias[e] = st.sc < 0.0f ? -INFINITY : 0.0f;
 }
 
 // Work split of the 4 waves of a workgroup (32 heads of one query):
-//  * logits by dim quarter: wave w computes the partial S = K Q^T of the
-//    tile's 32 entries x 32 heads over FP8 dims 112w .. +111 and RoPE dims
-//    448 + 16w .. +15 with v_mfma_f32_32x32x16_bf16, so each widened K value
-//    feeds 32 heads; the four partials meet in LDS (added in wave order);
-//  * softmax by head: wave w owns heads 8w .. 8w+7, a lane one head and four
-//    entries (entry group eg = lane / 8);
+//  * logits by (entry half, head tile): wave w computes the complete logits
+//    S = K Q^T of entries 16 (w & 1) .. +15 x heads 16 (w >> 1) .. +15 of a
+//    tile over all 512 dims with v_mfma_f32_16x16x32_bf16 (14 FP8 k-steps,
+//    widened exactly, and 2 RoPE k-steps), so no partial logits cross waves;
+//  * softmax in the same registers: a lane holds one head (lane & 15) and
+//    four entries (4 (lane >> 4) + i) of the wave's half; the two waves of a
+//    head tile share the running max through a lazily updated value that
+//    both compute identically;
 //  * PV by output-dim slice: wave w owns FP8 dims 112w .. 112w+111 and RoPE
 //    dims 448 + 16w .. +15 for the 32 heads, so each V^T fragment is widened
 //    from FP8 once and feeds two MFMAs (one per 16-head tile); P^T comes
 //    through LDS.
-// A workgroup is small (4 waves, about 64 KB of LDS) so that two run on
+// Three tile buffers and two P buffers let one barrier per tile order
+// everything: tile t+1 and P(t) are written before it, PV(t) reads after it,
+// and a buffer is rewritten only two barriers after its last read.
+// A workgroup is small (4 waves, under 80 KB of LDS) so that two run on
 // every compute unit and each hides the other's barriers and latencies.
+constexpr int kTileBufs = 3;
+constexpr int kQrStride = kRope + 8;       // Q RoPE row (bf16): 144 B, conflict-free reads
+
 struct __align__(16) Shared {
-  f32x4 xp[4][4][64];                      // partial logits [QK wave][softmax wave][lane]
-  u32x4 pB[2][64];                         // P^T operand (RoPE dims) [head tile][lane]
-  u32x4 pnB[2][64];                        // (P * scale)^T operand (FP8 dims)
-  float alpha[kHeads];                     // per-head rescale of the tile (1 = none)
-  i32x4 flag;                              // softmax wave rescaled this tile
+  u32x4 pB[2][2][64];                      // P^T operand (RoPE dims) [P buffer][head tile][lane]
+  u32x4 pnB[2][2][64];                     // (P * scale)^T operand (FP8 dims)
+  float tmx[2][4][16];                     // tile max per head of each wave's entry half
+  float alpha[2][kHeads];                  // per-head rescale of a tile (1 = none)
+  i32x4 flag[2];                           // a wave's heads outgrew the running max
+  uint16_t qr[kHeads][kQrStride];          // Q RoPE dims (bf16) of the 32 heads
+  float lsum[4][16];                       // epilogue: each wave's denominators
   float fin[kHeads];                       // per-head output factor (epilogue)
   int tbits[kMaxTiles];                    // entry kinds per tile
 };
 
-// Online-softmax state of a softmax lane's head (the 8 lanes of a head agree
-// on the max; the denominator is lane-partial).
+// Online-softmax state of a lane's head: the running max (identical in the
+// 8 lanes x 2 waves that hold a head) and the lane's partial denominator.
 struct SoftState {
   float m_run;
   float l_run;
 };
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// Partial logits of QK wave w.  MFMA operands: A = K (lane: entry lane & 31,
-// dims +8 (lane >> 5) .. +8 of the k-step), B = Q^T (lane: head lane & 31,
-// same dims); the accumulator's value v of a lane is entry
-// 8 (v / 4) + 4 (lane >> 5) + v % 4, head lane & 31.  The FP8 part is scaled
-// per entry in fp32 before the RoPE part is added.
-__device__ __forceinline__ void qk_partial(const Fp8Tile* tl, Shared* sh, const bf16x8* qf, int w,
-                                           int lane) {
-  const int kh = lane >> 5;
-  const uint8_t* er = tl->rows + (lane & 31) * kRowStride;
-  const uint8_t* kp = er + 112 * w + 8 * kh;
-  u32x2 kw[7];
+// Logits of wave (eh, ht) for tile tl.  MFMA operands: A = K (lane: entry
+// 16 eh + (lane & 15), 8 dims of the k-step), B = Q^T (lane: head lane & 15,
+// the same dims): lane group g = lane >> 4 takes FP8 dims
+// 64 (s >> 1) + 16 g + 8 (s & 1) .. +7 at k-step s < 14 (so a lane reads its
+// entry's row in seven 16-byte pieces, and at each k-step the four lane
+// groups of a head touch one 64-dim span of Q) and RoPE dims
+// 448 + 16 g + 8 (s - 14) .. +7 at s = 14, 15.  The FP8 k-steps' Q^T is
+// held in registers, the RoPE k-steps' is read from LDS.  The accumulator value i of a lane is entry 4 (lane >> 4) + i
+// of the half, head lane & 15.
+__device__ __forceinline__ void qk_tile(const Fp8Tile* tl, const Shared* sh, const bf16x8* qf,
+                                        int eh, int ht, int lane, f32x4& sn, f32x4& sr) {
+  const int g = lane >> 4;
+  const uint8_t* er = tl->rows + (16 * eh + (lane & 15)) * kRowStride;
+  // the row is read in two batches (the second in flight under the first
+  // batch's MFMAs) to bound the registers held by raw K
+  u32x4 kw[7];
 #pragma unroll
-  for (int ks = 0; ks < 7; ks++) kw[ks] = *(const u32x2*)(kp + 16 * ks);
-  const u32x4 kr = *(const u32x4*)(er + kNope + (16 * w + 8 * kh) * 2);
-  f32x16 sn = {}, sr = {};
+  for (int j = 0; j < 4; j++) kw[j] = *(const u32x4*)(er + 64 * j + 16 * g);
+  __builtin_amdgcn_sched_barrier(0);
+  sn = (f32x4){0.f, 0.f, 0.f, 0.f};
+  sr = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 7; ks++)
-    sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8(kw[ks][0], kw[ks][1]), qf[ks], sn, 0, 0, 0);
-  sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr), qf[7], sr, 0, 0, 0);
-  const int j = lane & 31;
+  for (int j = 4; j < 7; j++) kw[j] = *(const u32x4*)(er + 64 * j + 16 * g);
+  const u32x4 kr0 = *(const u32x4*)(er + kNope + 32 * g);
+  const u32x4 kr1 = *(const u32x4*)(er + kNope + 32 * g + 16);
+  const uint16_t* qrp = &sh->qr[16 * ht + (lane & 15)][16 * g];
+  const bf16x8 qr0 = __builtin_bit_cast(bf16x8, *(const u32x4*)qrp);
+  const bf16x8 qr1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrp + 8));
 #pragma unroll
-  for (int qd = 0; qd < 4; qd++) {
-    // entries 8qd + 4kh .. +3 = entry group 2qd + kh
-    const f32x4 sc = *(const f32x4*)&tl->scale[8 * qd + 4 * kh];
-    f32x4 v;
-#pragma unroll
-    for (int i = 0; i < 4; i++) v[i] = sn[4 * qd + i] * sc[i] + sr[4 * qd + i];
-    sh->xp[w][j >> 3][(2 * qd + kh) * 8 + (j & 7)] = v;
+  for (int j = 0; j < 7; j++) {
+    sn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(kw[j][0], kw[j][1]), qf[2 * j], sn, 0, 0, 0);
+    sn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(kw[j][2], kw[j][3]), qf[2 * j + 1], sn, 0, 0, 0);
   }
+  sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr0), qr0, sr, 0, 0, 0);
+  sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr1), qr1, sr, 0, 0, 0);
 }
 
-// Reductions over the 8 lanes of a softmax head (lane bits 3..5) without
-// LDS: lane ^ 8 by a DPP rotate of each 16-lane row by 8, lane ^ 16 and
-// lane ^ 32 by v_permlane16_swap / v_permlane32_swap of a value with itself
-// (each lane ends up with its own value and its partner's).  Every lane of a
-// head combines the same values, so all eight hold identical results.
+// Reductions over the 4 lanes of a head (lane bits 4, 5) without LDS:
+// v_permlane16_swap / v_permlane32_swap of a value with itself give each
+// lane its own value and that of lane ^ 16 resp. lane ^ 32.  Every lane of a
+// head combines the same values, so all four hold identical results.
 // (The empty asm statement keeps the compiler from folding the two results
 // of a swap into one value.)
-constexpr int kDppRowRor8 = 0x128;         // row_ror:8
-
-__device__ __forceinline__ float xor8_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               kDppRowRor8, 0xF, 0xF, false));
-}
-
 template <bool kSwap32>
 __device__ __forceinline__ void swap_pair(float v, float& a, float& b) {
   const uint32_t x = __builtin_bit_cast(uint32_t, v);
@@ -385,7 +403,6 @@ __device__ __forceinline__ void swap_pair(float v, float& a, float& b) {
 
 __device__ __forceinline__ float head_max(float v) {
   float a, b;
-  v = fmaxf(v, xor8_f(v));
   swap_pair<false>(v, a, b);
   v = fmaxf(a, b);
   swap_pair<true>(v, a, b);
@@ -394,61 +411,63 @@ __device__ __forceinline__ float head_max(float v) {
 
 __device__ __forceinline__ float head_sum(float v) {
   float a, b;
-  v += xor8_f(v);
   swap_pair<false>(v, a, b);
   v = a + b;
   swap_pair<true>(v, a, b);
   return a + b;
 }
 
-// Softmax of wave w's 8 heads: lane = head h (lane & 7) x entry group eg
-// (lane >> 3, entries 4eg .. 4eg+3).  Writes P^T and (P * scale)^T in the
-// PV operand layout: head tile j / 16, lane (j % 16) + 16 (eg % 4), slots
-// 4 (eg / 4) .. +3 (PV's k-slot order: entries 4g .. 4g+3, 16+4g .. +3).
-__device__ __forceinline__ void softmax_tile(const Fp8Tile* tl, Shared* sh, SoftState& S,
-                                             float c2, int w, int lane) {
-  const int h = lane & 7, eg = lane >> 3;
-  const f32x4 a0 = sh->xp[0][w][lane], a1 = sh->xp[1][w][lane];
-  const f32x4 a2 = sh->xp[2][w][lane], a3 = sh->xp[3][w][lane];
-  const f32x4 bi = *(const f32x4*)&tl->bias[4 * eg];
-  const f32x4 sc = *(const f32x4*)&tl->scale[4 * eg];
-  float s2[4];
-  float tmax = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    s2[i] = (((a0[i] + a1[i]) + a2[i]) + a3[i]) * c2 + bi[i];
-    tmax = fmaxf(tmax, s2[i]);
-  }
-  tmax = head_max(tmax);
-  // lazy rescale: the running max moves only when it grows by more than
-  // kRescale (exact: P <= 2^kRescale, and the final normalisation uses the
-  // same max); the factor goes to the PV waves through LDS
-  const bool need = (S.m_run == -INFINITY) ? (tmax > -INFINITY) : (tmax > S.m_run + kRescale);
-  float alpha = 1.0f;
-  if (need) {
-    alpha = (S.m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(S.m_run - tmax);
-    S.l_run *= alpha;
-    S.m_run = tmax;
-  }
-  const float m_use = (S.m_run == -INFINITY) ? 0.0f : S.m_run;
+// The lazy-rescale rule: the running max moves only when a tile's max
+// exceeds it by more than kRescale (exact: P <= 2^kRescale, and the final
+// normalisation uses the same max).
+__device__ __forceinline__ bool needs_rescale(float m_run, float tmax) {
+  return (m_run == -INFINITY) ? (tmax > -INFINITY) : (tmax > m_run + kRescale);
+}
+
+// P and (P * scale) of the lane's four entries against max m (m = -inf:
+// nothing seen yet, every logit so far is -inf), written in the PV operand
+// layout: head tile ht, lane, slots 4 eh .. +3 (PV's k-slot order: entries
+// 4g .. 4g+3 of half 0, then of half 1).  Returns the lane's sum of P.
+__device__ __forceinline__ float write_p(Shared* sh, int pb, int ht, int eh, int lane,
+                                         const float* s2, f32x4 sc, float m) {
+  const float m_use = (m == -INFINITY) ? 0.0f : m;
   float pv[4], pn[4];
+  float l = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     // 2^(x) for x <= kRescale; an absent entry gives 2^-inf = 0
     const float p = __builtin_amdgcn_exp2f(s2[i] - m_use);
-    S.l_run += p;
+    l += p;
     pv[i] = p;
     pn[i] = p * sc[i];
   }
-  const int j = 8 * w + h;
-  const int pl = (j & 15) + 16 * (eg & 3);
-  uint8_t* pb = (uint8_t*)&sh->pB[j >> 4][pl] + 8 * (eg >> 2);
-  uint8_t* pnb = (uint8_t*)&sh->pnB[j >> 4][pl] + 8 * (eg >> 2);
-  *(u32x2*)pb = pack4(pv);
-  *(u32x2*)pnb = pack4(pn);
-  if (eg == 0) sh->alpha[j] = alpha;
-  const int any = __builtin_amdgcn_ballot_w64(need) != 0;
-  if (lane == 0) sh->flag[w] = any;
+  *(u32x2*)((uint8_t*)&sh->pB[pb][ht][lane] + 8 * eh) = pack4(pv);
+  *(u32x2*)((uint8_t*)&sh->pnB[pb][ht][lane] + 8 * eh) = pack4(pn);
+  return l;
+}
+
+// Softmax of the wave's logits, first pass: P against the running max as it
+// stands (right unless some wave's tile max outgrows it, which the flags
+// report after the barrier; on a split's first tile it always does, so no P
+// is written there).  Publishes the wave's tile max per head.
+__device__ __forceinline__ float softmax_pass(const Fp8Tile* tl, Shared* sh, const SoftState& S,
+                                              f32x4 sn, f32x4 sr, float c2, int pb, int w,
+                                              int lane, bool first, float* s2, float& tmax) {
+  const int eh = w & 1, ht = w >> 1, g = lane >> 4;
+  const f32x4 sc = *(const f32x4*)&tl->scale[16 * eh + 4 * g];
+  const f32x4 bi = *(const f32x4*)&tl->bias[16 * eh + 4 * g];
+  tmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    s2[i] = (sn[i] * sc[i] + sr[i]) * c2 + bi[i];
+    tmax = fmaxf(tmax, s2[i]);
+  }
+  tmax = head_max(tmax);
+  const float l = first ? 0.0f : write_p(sh, pb, ht, eh, lane, s2, sc, S.m_run);
+  if (lane < 16) sh->tmx[pb][w][lane] = tmax;
+  const int any = __builtin_amdgcn_ballot_w64(needs_rescale(S.m_run, tmax)) != 0;
+  if (lane == 0) sh->flag[pb][w] = any;
+  return l;
 }
 
 // Output dims of PV wave w, block db (16 dims): FP8 dims 112w + 16db for
@@ -461,12 +480,12 @@ __device__ __forceinline__ int pv_dim0(int w, int db) { return db < 7 ? 112 * w 
 // reads, widened, times (P * scale)^T; the RoPE block: 16-bit transpose
 // reads times P^T.  All LDS reads are issued before the (rare) rescale.
 __device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f32x4 (*acc)[2],
-                                         int ds, int g, int li) {
+                                         int ds, int g, int li, int pb, bool rescale) {
   const int lane = threadIdx.x & 63;
-  const bf16x8 pn0 = __builtin_bit_cast(bf16x8, sh->pnB[0][lane]);
-  const bf16x8 pn1 = __builtin_bit_cast(bf16x8, sh->pnB[1][lane]);
-  const bf16x8 pb0 = __builtin_bit_cast(bf16x8, sh->pB[0][lane]);
-  const bf16x8 pb1 = __builtin_bit_cast(bf16x8, sh->pB[1][lane]);
+  const bf16x8 pn0 = __builtin_bit_cast(bf16x8, sh->pnB[pb][0][lane]);
+  const bf16x8 pn1 = __builtin_bit_cast(bf16x8, sh->pnB[pb][1][lane]);
+  const bf16x8 pb0 = __builtin_bit_cast(bf16x8, sh->pB[pb][0][lane]);
+  const bf16x8 pb1 = __builtin_bit_cast(bf16x8, sh->pB[pb][1][lane]);
   // lane group g's k-values are entries {4g..4g+3, 16+4g..16+4g+3}; source
   // lane s of the group points at entry k = s/2 (tr8) resp. s/4 (tr16)
   const int s = li;
@@ -481,11 +500,10 @@ __device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f3
   const uint8_t* vhi = tl->rows + (16 + g * 4 + kk16) * kRowStride + kNope + ds * 32 + (s & 3) * 8;
   const u32x2 lo = lds_tr16(vlo);
   const u32x2 hi = lds_tr16(vhi);
-  const i32x4 fl = sh->flag;
-  if ((fl[0] | fl[1]) | (fl[2] | fl[3])) {
+  if (rescale) {
 #pragma unroll
     for (int ht = 0; ht < 2; ht++) {
-      const float al = sh->alpha[ht * 16 + li];
+      const float al = sh->alpha[pb][ht * 16 + li];
 #pragma unroll
       for (int db = 0; db < 8; db++) acc[db][ht] *= al;
     }
@@ -528,39 +546,47 @@ __device__ __forceinline__ int64_t part_block(const AttendArgs& a, int row, int 
 }
 
 __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
-  __shared__ Fp8Tile tiles[2];
+  __shared__ Fp8Tile tiles[kTileBufs];
   __shared__ Shared sh;
   __shared__ int src[kMaxSplit];
   int row, split, hgrp;
   if (!wg_coords(a, &row, &split, &hgrp)) return;
+  const int32_t pre = prefetch_topk(a, row, split * a.split_size);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int eh = wave & 1, wht = wave >> 1;  // logits: entry half, head tile
   const int b = row / a.Q;
   const int g = lane >> 4;                 // PV: lane group 0..3
   const int li = lane & 15;
   const int nht = min(2, (a.H - hgrp * kHeads) / 16);   // head tiles present (H % 16 == 0)
   const int D = kNope + kRope;
 
-  // Q^T fragments of this wave's dim quarter (MFMA B operand), the first
-  // loads the workgroup issues (they depend on nothing): k-steps 0..6
-  // cover FP8 dims 112 wave + 16 ks .. +15, k-step 7 RoPE dims 448 + 16 wave
-  // .. +15; the lane holds dims +8 (lane >> 5) .. +8 of head lane & 31 (zero
-  // for heads beyond H)
-  bf16x8 qf[8];
+  // Q^T fragments of head 16 wht + (lane & 15) (MFMA B operand), loaded
+  // right after the top-k ids (they depend on nothing): k-step s < 14 holds
+  // FP8 dims 64 (s >> 1) + 16 g + 8 (s & 1) .. +7 (zero for heads beyond
+  // H); the RoPE dims go to LDS
+  bf16x8 qf[14];
   {
-    const int qh = hgrp * kHeads + (lane & 31);
+    const int qh = hgrp * kHeads + 16 * wht + li;
     const bool q_ok = qh < a.H;
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.H + (q_ok ? qh : 0)) * D +
-                         8 * (lane >> 5);
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.H + (q_ok ? qh : 0)) * D;
 #pragma unroll
-    for (int ks = 0; ks < 8; ks++) {
-      const int d0 = ks < 7 ? 112 * wave + 16 * ks : kNope + 16 * wave;
-      u32x4 v = *(const u32x4*)(qp + d0);
+    for (int s = 0; s < 14; s++) {
+      u32x4 v = *(const u32x4*)(qp + 64 * (s >> 1) + 16 * g + 8 * (s & 1));
       if (!q_ok) v = (u32x4){0u, 0u, 0u, 0u};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
+      qf[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  const int32_t pre = prefetch_topk(a, row, split * a.split_size);
+  // RoPE dims of the 32 heads, 16 bytes per thread: loaded now, stored to
+  // LDS once the first tiles' loads are out (so that waiting for this load
+  // holds back neither source resolution nor the gather)
+  // (an unconditional load: a conditional one would make the compiler wait
+  // for it, and for the loads before it, where the branches join)
+  const int rh = threadIdx.x >> 3, rc = threadIdx.x & 7;
+  const bool r_ok = hgrp * kHeads + rh < a.H;
+  u32x4 qrv = *(const u32x4*)((const uint16_t*)a.q +
+                              ((int64_t)row * a.H + (r_ok ? hgrp * kHeads + rh : 0)) * D + kNope + 8 * rc);
+  if (!r_ok) qrv = (u32x4){0u, 0u, 0u, 0u};
   const RowEntries r = row_entries(a, row);
   const int n_tot = r.n_c + r.n_w;
   const int e_beg = split * a.split_size;
@@ -602,36 +628,66 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   __builtin_amdgcn_sched_barrier(0);       // tile 1's loads stay ahead of tile 0's wait
   stage_store(&tiles[0], st0);
   stage_load(B, stage_src(src, sh.tbits, 2), 2, n_local, st0);
+  *(u32x4*)&sh.qr[rh][8 * rc] = qrv;
   __syncthreads();
 
-  // step t: partial logits of tile t | softmax of tile t, tile t+1 into LDS,
-  // its register set refilled with tile t+3 | PV of tile t.  Two barriers
-  // per tile: the partial logits and tile t+1 are read only after the
-  // barrier that follows their writes, and every LDS buffer is rewritten
-  // only after a barrier that follows its last read.  Unrolled by two so
-  // that the register sets alternate statically.
-  auto step = [&](int t, Stage& nxt) {
+  // step t (tile t in buffer cb, P buffer pb = t & 1): logits and softmax
+  // of tile t in registers, P(t) and tile t+1 (buffer nb) into LDS, the
+  // register set refilled with tile t+3 | barrier | PV of tile t.  When a
+  // wave's tile max outgrew the running max (and on the first tile), the
+  // two waves of each head tile agree on the tile max through LDS, P(t) is
+  // (re)written against the new max and a second barrier publishes it and
+  // the rescale factors.  Unrolled by two so that the register sets and P
+  // buffers alternate statically.
+  auto step = [&](int t, int cb, int nb, int pb, Stage& nxt) {
     const StageSrc ns = stage_src(src, sh.tbits, t + 3);
-    qk_partial(&tiles[t & 1], &sh, qf, wave, lane);
-    __syncthreads();
-    softmax_tile(&tiles[t & 1], &sh, S, c2, wave, lane);
-    stage_store(&tiles[(t + 1) & 1], nxt);
+    f32x4 sn, sr;
+    float s2[4], tmax;
+    qk_tile(&tiles[cb], &sh, qf, eh, wht, lane, sn, sr);
+    const bool first = t == 0;
+    float l_add = softmax_pass(&tiles[cb], &sh, S, sn, sr, c2, pb, wave, lane, first, s2, tmax);
+    stage_store(&tiles[nb], nxt);
     stage_load(B, ns, t + 3, n_local, nxt);
     __syncthreads();
-    pv_slice(&tiles[t & 1], &sh, acc, wave, g, li);
+    const i32x4 fl = sh.flag[pb];
+    const bool rescale = first || ((fl[0] | fl[1]) | (fl[2] | fl[3])) != 0;
+    if (rescale) {
+      // max over both entry halves, in the same order in both waves
+      const float tp = sh.tmx[pb][wave ^ 1][li];
+      const float tj = eh == 0 ? fmaxf(tmax, tp) : fmaxf(tp, tmax);
+      float alpha = 1.0f;
+      if (needs_rescale(S.m_run, tj)) {
+        alpha = (S.m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(S.m_run - tj);
+        S.l_run *= alpha;
+        S.m_run = tj;
+      }
+      const f32x4 sc = *(const f32x4*)&tiles[cb].scale[16 * eh + 4 * g];
+      l_add = write_p(&sh, pb, wht, eh, lane, s2, sc, S.m_run);
+      if (eh == 0 && lane < 16) sh.alpha[pb][16 * wht + lane] = alpha;
+      __syncthreads();
+    }
+    S.l_run += l_add;
+    pv_slice(&tiles[cb], &sh, acc, wave, g, li, pb, rescale);
   };
-  int t = 0;
+  int t = 0, cb = 0;
   for (; t + 1 < n_tiles; t += 2) {
-    step(t, st1);
-    step(t + 1, st0);
+    const int nb = cb == kTileBufs - 1 ? 0 : cb + 1;
+    const int nb2 = nb == kTileBufs - 1 ? 0 : nb + 1;
+    step(t, cb, nb, 0, st1);
+    step(t + 1, nb, nb2, 1, st0);
+    cb = nb2;
   }
-  if (t < n_tiles) step(t, st1);
+  if (t < n_tiles) step(t, cb, cb == kTileBufs - 1 ? 0 : cb + 1, 0, st1);
 
-  // ---- epilogue: the softmax lanes of entry group 0 publish each head's
-  // factor (the denominator summed over the head's 8 lanes)
-  const float l_tot = head_sum(S.l_run);
-  if (lane < 8) {
-    const int jh = 8 * wave + lane;
+  // ---- epilogue: each wave's denominators per head (summed over its four
+  // lane groups), then the two entry halves added in fixed order by the
+  // lanes of the half-0 wave, which publish each head's factor
+  const float l_w = head_sum(S.l_run);
+  if (lane < 16) sh.lsum[wave][lane] = l_w;
+  __syncthreads();
+  if (eh == 0 && lane < 16) {
+    const float l_tot = sh.lsum[wave][lane] + sh.lsum[wave + 1][lane];
+    const int jh = 16 * wht + lane;
     const int head = hgrp * kHeads + jh;
     const bool head_ok = head < a.H;
     float f;
@@ -665,9 +721,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
         const f32x4 o = acc[db][ht] * f;
         const int64_t oi = ob + pv_dim0(wave, db);
         if (a.out_bf16) {
-          const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-          const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-          __builtin_nontemporal_store((u32x2){lo, hi}, (u32x2*)((uint16_t*)a.out + oi));
+          const float ov[4] = {o[0], o[1], o[2], o[3]};
+          __builtin_nontemporal_store(pack4(ov), (u32x2*)((uint16_t*)a.out + oi));
         } else {
           *(f32x4*)((float*)a.out + oi) = o;
         }
@@ -681,11 +736,10 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
       for (int ht = 0; ht < 2; ht++) {
         if (ht >= nht) break;
         const f32x4 o = acc[db][ht] * sh.fin[ht * 16 + li];
-        const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-        const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+        const float ov[4] = {o[0], o[1], o[2], o[3]};
         // streaming stores: the merge reads them once, and lines that do
         // not sit dirty in L2 need no write-back when the kernel ends
-        __builtin_nontemporal_store((u32x2){lo, hi},
+        __builtin_nontemporal_store(pack4(ov),
                                     (u32x2*)(po + (((int64_t)(wave * 8 + db) * nht + ht) * 64 + lane) * 4));
       }
     }
