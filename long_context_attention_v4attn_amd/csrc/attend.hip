@@ -478,28 +478,40 @@ __device__ __forceinline__ int pv_dim0(int w, int db) { return db < 7 ? 112 * w 
 // PV for wave `ds`, both head groups: acc[db][ht] = O^T block of dims
 // pv_dim0(ds, db) .. +16 x heads 16ht .. +16.  FP8 blocks: 8-bit transpose
 // reads, widened, times (P * scale)^T; the RoPE block: 16-bit transpose
-// reads times P^T.  All LDS reads are issued before the (rare) rescale.
-__device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f32x4 (*acc)[2],
-                                         int ds, int g, int li, int pb, bool rescale) {
-  const int lane = threadIdx.x & 63;
-  const bf16x8 pn0 = __builtin_bit_cast(bf16x8, sh->pnB[pb][0][lane]);
-  const bf16x8 pn1 = __builtin_bit_cast(bf16x8, sh->pnB[pb][1][lane]);
-  const bf16x8 pb0 = __builtin_bit_cast(bf16x8, sh->pB[pb][0][lane]);
-  const bf16x8 pb1 = __builtin_bit_cast(bf16x8, sh->pB[pb][1][lane]);
+// reads times P^T.  The V^T reads depend only on the tile, so they are
+// issued right after the barrier, together with the rescale flags, and
+// their latency covers the flags' (pv_load); P^T is read after the (rare)
+// rescale step has settled it (pv_mma).
+struct VFrag {
+  u32x2 w8[7];                             // FP8 blocks, raw codes
+  u32x2 lo, hi;                            // RoPE block, bf16
+};
+
+__device__ __forceinline__ VFrag pv_load(const Fp8Tile* tl, int ds, int g, int li) {
   // lane group g's k-values are entries {4g..4g+3, 16+4g..16+4g+3}; source
   // lane s of the group points at entry k = s/2 (tr8) resp. s/4 (tr16)
   const int s = li;
   const int kk8 = s >> 1;
   const int ent8 = (kk8 < 4) ? (g * 4 + kk8) : (16 + g * 4 + kk8 - 4);
   const uint8_t* vb8 = tl->rows + ent8 * kRowStride + (s & 1) * 8 + ds * 112;
-  u32x2 w8[7];
+  VFrag v;
 #pragma unroll
-  for (int db = 0; db < 7; db++) w8[db] = lds_tr8(vb8 + db * 16);
+  for (int db = 0; db < 7; db++) v.w8[db] = lds_tr8(vb8 + db * 16);
   const int kk16 = s >> 2;
   const uint8_t* vlo = tl->rows + (g * 4 + kk16) * kRowStride + kNope + ds * 32 + (s & 3) * 8;
   const uint8_t* vhi = tl->rows + (16 + g * 4 + kk16) * kRowStride + kNope + ds * 32 + (s & 3) * 8;
-  const u32x2 lo = lds_tr16(vlo);
-  const u32x2 hi = lds_tr16(vhi);
+  v.lo = lds_tr16(vlo);
+  v.hi = lds_tr16(vhi);
+  return v;
+}
+
+__device__ __forceinline__ void pv_mma(const Shared* sh, f32x4 (*acc)[2], const VFrag& vf, int li,
+                                       int pb, bool rescale) {
+  const int lane = threadIdx.x & 63;
+  const bf16x8 pn0 = __builtin_bit_cast(bf16x8, sh->pnB[pb][0][lane]);
+  const bf16x8 pn1 = __builtin_bit_cast(bf16x8, sh->pnB[pb][1][lane]);
+  const bf16x8 pb0 = __builtin_bit_cast(bf16x8, sh->pB[pb][0][lane]);
+  const bf16x8 pb1 = __builtin_bit_cast(bf16x8, sh->pB[pb][1][lane]);
   if (rescale) {
 #pragma unroll
     for (int ht = 0; ht < 2; ht++) {
@@ -510,11 +522,11 @@ __device__ __forceinline__ void pv_slice(const Fp8Tile* tl, const Shared* sh, f3
   }
 #pragma unroll
   for (int db = 0; db < 7; db++) {
-    const bf16x8 v = widen8(w8[db][0], w8[db][1]);
+    const bf16x8 v = widen8(vf.w8[db][0], vf.w8[db][1]);
     acc[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn0, acc[db][0], 0, 0, 0);
     acc[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pn1, acc[db][1], 0, 0, 0);
   }
-  const bf16x8 vr = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+  const bf16x8 vr = __builtin_bit_cast(bf16x8, (u32x4){vf.lo[0], vf.lo[1], vf.hi[0], vf.hi[1]});
   acc[7][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr, pb0, acc[7][0], 0, 0, 0);
   acc[7][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr, pb1, acc[7][1], 0, 0, 0);
 }
@@ -649,6 +661,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
     stage_store(&tiles[nb], nxt);
     stage_load(B, ns, t + 3, n_local, nxt);
     __syncthreads();
+    VFrag vf = pv_load(&tiles[cb], wave, g, li);
     const i32x4 fl = sh.flag[pb];
     const bool rescale = first || ((fl[0] | fl[1]) | (fl[2] | fl[3])) != 0;
     if (rescale) {
@@ -663,11 +676,14 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
       }
       const f32x4 sc = *(const f32x4*)&tiles[cb].scale[16 * eh + 4 * g];
       l_add = write_p(&sh, pb, wht, eh, lane, s2, sc, S.m_run);
-      if (eh == 0 && lane < 16) sh.alpha[pb][16 * wht + lane] = alpha;
+      // (the four lanes of a head hold the same factor and all store it)
+      if (eh == 0) sh.alpha[pb][16 * wht + li] = alpha;
       __syncthreads();
+      // read again rather than held across this rare path (register room)
+      vf = pv_load(&tiles[cb], wave, g, li);
     }
     S.l_run += l_add;
-    pv_slice(&tiles[cb], &sh, acc, wave, g, li, pb, rescale);
+    pv_mma(&sh, acc, vf, li, pb, rescale);
   };
   int t = 0, cb = 0;
   for (; t + 1 < n_tiles; t += 2) {
