@@ -161,6 +161,21 @@ v4a_status v4attn_index_topk(const void *q_idx, int32_t q_dtype, const float *w,
                              void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * v4attn_index_topk_bf16 -- the selector variant with BF16 index scores
+ * ([Notes §9]: the top-k selector's index scores go from FP32 to BF16).
+ * Same arguments, workspace, supported set and errors as v4attn_index_topk;
+ * each fp32 score is rounded to the nearest bf16 (ties to even) before it is
+ * ranked, so scores that become equal are ordered by id (lower id first).
+ * The workspace's score rows hold the bf16 values (half the traffic of the
+ * fp32 scores through the selector).
+ */
+v4a_status v4attn_index_topk_bf16(const void *q_idx, int32_t q_dtype, const float *w,
+                                  const v4a_idx *keys, const int64_t *pos,
+                                  int32_t B, int32_t Q, int32_t H_I, int32_t m,
+                                  int32_t k, int32_t *topk,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/*
  * v4attn_csa_attend -- CSA core attention ([Notes §7]: shared key-value MQA
  * over the selected compressed entries, plus the sliding-window branch over
  * the most recent n_win uncompressed entries; [Notes §8] table: both sets enter
@@ -225,7 +240,7 @@ int32_t v4attn_last_hip_error(void);
 
 /*
  * Kernel timing (measurement helper).  The calling thread's next call of
- * v4attn_index_topk, v4attn_csa_attend or v4attn_hca_attend records `start`
+ * v4attn_index_topk(_bf16), v4attn_csa_attend or v4attn_hca_attend records `start`
  * and `stop` (hipEvent_t handles created by the caller) on the call's stream
  * immediately before and after its dominant kernel -- the index scan, resp.
  * the attention kernel (not the split merge) -- so hipEventElapsedTime gives

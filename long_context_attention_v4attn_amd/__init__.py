@@ -10,6 +10,7 @@ is not built or no GPU is present.
 from .binding import (  # noqa: F401
     F32, BF16, KV_FP8_BF16ROPE, IDX_MXFP4, OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND,
     KVCache, IdxCache, V4AttnError, load, library_path,
-    v4attn_compress, v4attn_index_topk, v4attn_csa_attend, v4attn_hca_attend,
+    v4attn_compress, v4attn_index_topk, v4attn_index_topk_bf16, v4attn_csa_attend,
+    v4attn_hca_attend,
     v4attn_workspace_bytes, v4attn_status_str, v4attn_time_next_kernel,
 )

@@ -50,6 +50,8 @@ _F = ctypes.c_float
 _SIGS = {
     "v4attn_compress": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I64, _I32, _P, _P]),
     "v4attn_index_topk": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "v4attn_index_topk_bf16": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ,
+                                      _P]),
     "v4attn_csa_attend": (_I32, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32, _I32,
                                  _P, _I32, _P, _SZ, _P]),
     "v4attn_hca_attend": (_I32, [_P, _I32, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32, _I32,
@@ -207,7 +209,7 @@ def v4attn_compress(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, m, t0, out, 
     return out
 
 
-def v4attn_index_topk(q_idx, w, keys, pos, m, k, topk=None, ws=None, stream=None):
+def _index_topk(name, q_idx, w, keys, pos, m, k, topk, ws, stream):
     lib = load()
     _need_cuda(q_idx, w, pos)
     B, Q, H, d = q_idx.shape
@@ -216,10 +218,19 @@ def v4attn_index_topk(q_idx, w, keys, pos, m, k, topk=None, ws=None, stream=None
     nbytes = v4attn_workspace_bytes(OP_INDEX_TOPK, B, Q, H, d, keys.cap, k, 0)
     ws, wsb = _workspace(ws, nbytes, q_idx.device)
     st = keys.c_struct()
-    s = lib.v4attn_index_topk(_ptr(q_idx), _dtype_code(q_idx), _ptr(w), ctypes.byref(st),
-                              _ptr(pos), B, Q, H, m, k, _ptr(topk), _ptr(ws), wsb, _stream(stream))
-    _check(s, "v4attn_index_topk")
+    s = getattr(lib, name)(_ptr(q_idx), _dtype_code(q_idx), _ptr(w), ctypes.byref(st),
+                           _ptr(pos), B, Q, H, m, k, _ptr(topk), _ptr(ws), wsb, _stream(stream))
+    _check(s, name)
     return topk
+
+
+def v4attn_index_topk(q_idx, w, keys, pos, m, k, topk=None, ws=None, stream=None):
+    return _index_topk("v4attn_index_topk", q_idx, w, keys, pos, m, k, topk, ws, stream)
+
+
+def v4attn_index_topk_bf16(q_idx, w, keys, pos, m, k, topk=None, ws=None, stream=None):
+    """The BF16-score selector variant (same arguments as v4attn_index_topk)."""
+    return _index_topk("v4attn_index_topk_bf16", q_idx, w, keys, pos, m, k, topk, ws, stream)
 
 
 def _out(q, out, out_dtype):

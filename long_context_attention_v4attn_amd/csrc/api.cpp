@@ -160,10 +160,10 @@ v4a_status v4attn_compress(const void* kv_cur, const void* gate_cur, const void*
   return hip_status(launch_compress(a, (hipStream_t)stream));
 }
 
-v4a_status v4attn_index_topk(const void* q_idx, int32_t q_dtype, const float* w,
+static v4a_status index_topk(const void* q_idx, int32_t q_dtype, const float* w,
                              const v4a_idx* keys, const int64_t* pos, int32_t B, int32_t Q,
                              int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             size_t ws_bytes, void* stream, int score_bf16) {
   if (!q_idx || !w || !keys || !pos || !topk || B < 0 || Q < 0 || H_I < 1 || k < 1 || m < 1)
     return V4A_ERR_INVALID;
   if (q_dtype != V4A_F32 && q_dtype != V4A_BF16) return V4A_ERR_INVALID;
@@ -195,12 +195,27 @@ v4a_status v4attn_index_topk(const void* q_idx, int32_t q_dtype, const float* w,
   a.m = m;
   a.k = k;
   a.topk = topk;
+  a.score_bf16 = score_bf16;
   size_t need = index_workspace_bytes(B, Q, H_I, keys->d, keys->cap, a.key_mx);
   if (!ws || ws_bytes < need) return V4A_ERR_WORKSPACE;
   index_carve(a, ws);
   if (B == 0 || Q == 0) return V4A_OK;
   KernelEvents ev;
   return hip_status(launch_index_topk(a, (hipStream_t)stream, take_events(&ev)));
+}
+
+v4a_status v4attn_index_topk(const void* q_idx, int32_t q_dtype, const float* w,
+                             const v4a_idx* keys, const int64_t* pos, int32_t B, int32_t Q,
+                             int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return index_topk(q_idx, q_dtype, w, keys, pos, B, Q, H_I, m, k, topk, ws, ws_bytes, stream, 0);
+}
+
+v4a_status v4attn_index_topk_bf16(const void* q_idx, int32_t q_dtype, const float* w,
+                                  const v4a_idx* keys, const int64_t* pos, int32_t B, int32_t Q,
+                                  int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return index_topk(q_idx, q_dtype, w, keys, pos, B, Q, H_I, m, k, topk, ws, ws_bytes, stream, 1);
 }
 
 v4a_status v4attn_csa_attend(const void* q, int32_t q_dtype, const v4a_kv* comp,

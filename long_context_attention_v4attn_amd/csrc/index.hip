@@ -3,7 +3,8 @@
 // Method: [Notes §7] index score I_{t,s} = sum_h w_{t,h} ReLU(q_{t,h} . K_s)
 // over the compressed blocks visible to query t, then Top-k over s;
 // [Notes §9] the indexer's QK path runs in FP4 (keys and queries MXFP4), and
-// the selector ranks fp32 scores.
+// the selector ranks fp32 scores -- or, in the BF16-score variant of the same
+// section, the scores rounded to bf16 (which the score rows then hold).
 //
 // Pipeline of one v4attn_index_topk call (five launches):
 //   k_prep       query heads -> MXFP4 (e2m1 codes + e8m0 scale per 32); zero
@@ -138,6 +139,26 @@ __device__ __forceinline__ int64_t n_visible(int64_t p, int m, int64_t cap) {
 __device__ __forceinline__ uint32_t score_key(float f) {
   if (f == 0.0f) f = 0.0f;
   return order_key(f);
+}
+
+// The selector's score precision.  fp32, or the bf16 variant ([Notes §9]:
+// index scores cut from FP32 to BF16 in the top-k selector): the fp32 score
+// rounded to the nearest bf16 (ties to even, v_cvt_pk_bf16_f32) is what is
+// ranked and what the score rows hold (its 16 high bits).  A bf16 value's
+// key has its low 16 bits zero, so the radix digits below work unchanged.
+__device__ __forceinline__ float ranked(float s, int bf16) {
+  return bf16 ? (float)(__bf16)s : s;
+}
+
+__device__ __forceinline__ void put_score(const IndexArgs& a, size_t i, float r) {
+  if (a.score_bf16)
+    ((uint16_t*)a.scores)[i] = (uint16_t)(__float_as_uint(r) >> 16);
+  else
+    a.scores[i] = r;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
 }
 
 // ---------------------------------------------------------------- prep
@@ -311,11 +332,13 @@ __device__ __forceinline__ void quantize_q_frag(const IndexArgs& a, const QRaw& 
 template <int kHT>
 __device__ __forceinline__ void score_tiles(const KeyTiles& kt, const i32x8* qa, const int* qs,
                                             float (*wv)[4], int HT, int64_t blk0, int64_t nv,
-                                            int64_t sc_ld, int lane, float* out, uint32_t* lh) {
+                                            int64_t sc_ld, int lane, float* out, uint16_t* outh,
+                                            int bf16, uint32_t* lh) {
   // uniform: the iteration's blocks all lie inside the (64-padded) score row,
   // so every lane stores (scores past the visible count are never read)
   const bool in_row = blk0 + kWaveTiles * 16 <= sc_ld;
   float* ob = out + blk0 + lane;
+  uint16_t* obh = outh + blk0 + lane;
   const int g = lane >> 4, li = lane & 15;
 #pragma unroll
   for (int t4 = 0; t4 < kWaveTiles; t4 += 4) {
@@ -352,11 +375,16 @@ __device__ __forceinline__ void score_tiles(const KeyTiles& kt, const i32x8* qa,
     const float h0 = swap_add32(part[0], part[2]);
     const float h1 = swap_add32(part[1], part[3]);
     // lane group g: tile g; block blk0 + 16 t4 + lane
-    const float sc = swap_add16(h0, h1);
+    const float sc = ranked(swap_add16(h0, h1), bf16);
     const int64_t blk = blk0 + t4 * 16 + lane;
     // streaming store: the filters read each score once (and dirty L2 lines
     // would have to be written back when the kernel ends)
-    if (in_row || blk < sc_ld) __builtin_nontemporal_store(sc, ob + t4 * 16);
+    if (in_row || blk < sc_ld) {
+      if (bf16)
+        __builtin_nontemporal_store((uint16_t)(__float_as_uint(sc) >> 16), obh + t4 * 16);
+      else
+        __builtin_nontemporal_store(sc, ob + t4 * 16);
+    }
     // counted only when visible (an invisible block adds 0)
     atomicAdd(&lh[score_key(sc) >> kSh1], blk < nv ? 1u : 0u);
   }
@@ -440,6 +468,8 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
   iters = __builtin_amdgcn_readfirstlane(iters);
   __syncthreads();                         // lh zeroed
   float* out = a.scores + (size_t)row * a.sc_ld;
+  uint16_t* outh = (uint16_t*)a.scores + (size_t)row * a.sc_ld;
+  const int bf16 = a.score_bf16;
   if (kIters > 0) {
     // every iteration's keys in flight from the start; scored in order
 #pragma unroll
@@ -449,16 +479,17 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
                   kt[j + kDepth - 1]);
       if (j < iters)
         score_tiles<kHT>(kt[j], qa, qs, wv, HT, wblk + (int64_t)j * kIterBlocks, nv, a.sc_ld, lane,
-                         out, lh);
+                         out, outh, bf16, lh);
     }
   } else {
     // two iterations' keys in flight: kt[0] holds even, kt[1] odd iterations
     for (int it = 0; it < iters; it += 2) {
       const int64_t b0 = wblk + (int64_t)it * kIterBlocks;
-      score_tiles<kHT>(kt[0], qa, qs, wv, HT, b0, nv, a.sc_ld, lane, out, lh);
+      score_tiles<kHT>(kt[0], qa, qs, wv, HT, b0, nv, a.sc_ld, lane, out, outh, bf16, lh);
       if (it + 1 >= iters) break;
       if (it + 2 < iters) load_keys(kc, ks, b0 + 2 * kIterBlocks, a.cap, g, li, kt[0]);
-      score_tiles<kHT>(kt[1], qa, qs, wv, HT, b0 + kIterBlocks, nv, a.sc_ld, lane, out, lh);
+      score_tiles<kHT>(kt[1], qa, qs, wv, HT, b0 + kIterBlocks, nv, a.sc_ld, lane, out, outh, bf16,
+                       lh);
       if (it + 3 < iters) load_keys(kc, ks, b0 + 3 * kIterBlocks, a.cap, g, li, kt[1]);
     }
   }
@@ -538,8 +569,8 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
     if (q == qa0) nv0 = nv;
     if (q == qa1) nv1 = nv;
   }
-  float* out0 = a.scores + ((int64_t)b * a.Q + t0 + qa0) * a.sc_ld;
-  float* out1 = a.scores + ((int64_t)b * a.Q + t0 + qa1) * a.sc_ld;
+  const size_t o0 = (size_t)((int64_t)b * a.Q + t0 + qa0) * a.sc_ld;   // score row offsets
+  const size_t o1 = (size_t)((int64_t)b * a.Q + t0 + qa1) * a.sc_ld;
   __syncthreads();                         // lh zeroed
 
   const uint8_t* kc = (const uint8_t*)a.codes + (size_t)b * a.cap * 64;
@@ -564,15 +595,15 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
     float h[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) h[j] = swap_add32(part[j], part[4 + j]);
-    const float s0 = swap_add16(h[0], h[1]);    // queries 0, 1, 4, 5 by lane group
-    const float s1 = swap_add16(h[2], h[3]);    // queries 2, 3, 6, 7
+    const float s0 = ranked(swap_add16(h[0], h[1]), a.score_bf16);   // queries 0, 1, 4, 5 by lane group
+    const float s1 = ranked(swap_add16(h[2], h[3]), a.score_bf16);   // queries 2, 3, 6, 7
     const int64_t blk = blk0 + li;
     if (blk < nv0 && t0 + qa0 < a.Q) {
-      out0[blk] = s0;
+      put_score(a, o0 + blk, s0);
       atomicAdd(&lh[qa0][score_key(s0) >> kSh1], 1u);
     }
     if (blk < nv1 && t0 + qa1 < a.Q) {
-      out1[blk] = s1;
+      put_score(a, o1 + blk, s1);
       atomicAdd(&lh[qa1][score_key(s1) >> kSh1], 1u);
     }
   };
@@ -624,8 +655,9 @@ __global__ void __launch_bounds__(256) k_score_f32(IndexArgs a) {
       for (int c = 0; c < a.d; c++) dot += qsm[h * a.d + c] * kr[c];
       s += wsm[h] * fmaxf(dot, 0.0f);
     }
-    a.scores[(size_t)row * a.sc_ld + blk] = s;
-    atomicAdd(&lh[score_key(s) >> kSh1], 1u);
+    const float r = ranked(s, a.score_bf16);
+    put_score(a, (size_t)row * a.sc_ld + blk, r);
+    atomicAdd(&lh[score_key(r) >> kSh1], 1u);
   }
   hist_flush(lh, a.hist + (size_t)row * kBins1, kBins1);
 }
@@ -684,32 +716,47 @@ __device__ __forceinline__ uint64_t sel_key(uint32_t k32, int64_t i) {
   return ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
 }
 
-// This thread's kPer consecutive scores of filter chunk `chunk` as keys; the
-// loads are issued together (the score rows are padded to 64 floats, and a
-// thread whose group starts past nv reads its row's first group instead).
-// Returns the number of the group's ids below nv.
-
 // This thread's kPer consecutive scores of filter chunk `chunk`, in two
 // halves so that the loads can be issued before anything else the kernel
 // waits for: issue_group needs no visible count (the score rows are padded to
-// 64 floats; a group past the padded row reads the row's first group),
+// 64 entries; a group past the padded row reads the row's first group),
 // finish_group converts them to keys and returns how many are below nv.
+// kBf16: the rows hold bf16 scores (32 bytes per group instead of 64).
 struct Group {
-  f32x4 v[kPer / 4];
+  u32x4 v[kPer / 4];
   int64_t g0;
 };
 
+template <bool kBf16>
 __device__ __forceinline__ void issue_group(const IndexArgs& a, int row, int chunk, Group& gr) {
   gr.g0 = (int64_t)chunk * kFilterChunk + threadIdx.x * kPer;
-  const float* sc = a.scores + (size_t)row * a.sc_ld + (gr.g0 < a.sc_ld ? gr.g0 : 0);
+  const size_t off = (size_t)row * a.sc_ld + (gr.g0 < a.sc_ld ? gr.g0 : 0);
+  if (kBf16) {
+    const uint16_t* sc = (const uint16_t*)a.scores + off;
 #pragma unroll
-  for (int j = 0; j < kPer / 4; j++) gr.v[j] = *(const f32x4*)(sc + 4 * j);
+    for (int j = 0; j < kPer / 8; j++) gr.v[j] = *(const u32x4*)(sc + 8 * j);
+  } else {
+    const float* sc = a.scores + off;
+#pragma unroll
+    for (int j = 0; j < kPer / 4; j++) gr.v[j] = *(const u32x4*)(sc + 4 * j);
+  }
 }
 
+template <bool kBf16>
 __device__ __forceinline__ int finish_group(const Group& gr, int64_t nv, uint32_t* k32) {
   const int64_t rem = nv - gr.g0;
 #pragma unroll
-  for (int j = 0; j < kPer; j++) k32[j] = score_key(gr.v[j / 4][j % 4]);
+  for (int j = 0; j < kPer; j++) {
+    float f;
+    if (kBf16) {
+      const uint32_t w = gr.v[j / 8][(j % 8) / 2];
+      f = bf16_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+    } else {
+      const uint32_t w = gr.v[j / 4][j % 4];
+      f = __uint_as_float(w);
+    }
+    k32[j] = score_key(f);
+  }
   return rem <= 0 ? 0 : (rem >= kPer ? kPer : (int)rem);
 }
 
@@ -780,6 +827,7 @@ __device__ __forceinline__ uint32_t part_sum(const Parts& p, uint32_t* red) {
   return sum;
 }
 
+template <bool kBf16>
 __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
   __shared__ uint32_t lh[kBins2];
   __shared__ uint32_t tmp[kFThreads / 64];
@@ -795,7 +843,7 @@ __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
     load_parts(a, row, pt);
   else
     h1 = a.hist[(size_t)row * kBins1 + threadIdx.x];   // kBins1 == kFThreads
-  issue_group(a, row, blockIdx.x, gr);
+  issue_group<kBf16>(a, row, blockIdx.x, gr);
   const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
   const int kk = (int)(nv < a.k ? nv : a.k);
   if (kk == nv) {                          // everything visible is selected
@@ -819,7 +867,7 @@ __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
   }
   for (int i = threadIdx.x; i < kBins2; i += blockDim.x) lh[i] = 0u;
   uint32_t k32[kPer];
-  const int n_in = finish_group(gr, nv, k32);
+  const int n_in = finish_group<kBf16>(gr, nv, k32);
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kPer; j++)
@@ -873,10 +921,11 @@ struct CandList {
 
 // Candidates of the threshold search: the compact list, or (when it
 // overflowed) the query's scores filtered by the first two digits.
+template <bool kBf16>
 struct CandSrc {
   const uint64_t* cand;
   uint32_t n;
-  const float* sc;
+  const void* sc;                          // the query's score row
   int64_t nv;
   uint32_t b12;                            // key bits 31..13 of the candidates
   bool compact;
@@ -886,7 +935,7 @@ struct CandSrc {
       *key = cand[i];
       return true;
     }
-    uint32_t k32 = score_key(sc[i]);
+    const uint32_t k32 = score_key(kBf16 ? bf16_to_f32(((const uint16_t*)sc)[i]) : ((const float*)sc)[i]);
     *key = sel_key(k32, i);
     return (k32 >> kSh2) == b12;
   }
@@ -908,7 +957,8 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* tmp) {
 // The exact 64-bit threshold T: the need-th largest key among the
 // candidates (radix select on the bits below the candidates' common 19-bit
 // prefix).  Exactly `need` candidates have keys >= T.
-__device__ uint64_t resolve_threshold(const CandSrc& src, uint32_t need, uint32_t* lh,
+template <bool kBf16>
+__device__ uint64_t resolve_threshold(const CandSrc<kBf16>& src, uint32_t need, uint32_t* lh,
                                       uint32_t* tmp) {
   __shared__ uint64_t s_prefix, s_mask;
   __shared__ uint32_t s_need, s_above;
@@ -953,6 +1003,7 @@ __device__ uint64_t resolve_threshold(const CandSrc& src, uint32_t need, uint32_
   return T;
 }
 
+template <bool kBf16>
 __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   __shared__ uint32_t lh[kBins2];
   __shared__ uint32_t tmp[kFThreads / 64];
@@ -968,7 +1019,7 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   const u32x4* gh2 = (const u32x4*)(a.hist2 + (size_t)row * kBins2 + threadIdx.x * kPer2);
   const u32x4 h2a = gh2[0], h2b = gh2[1];
   Group gr;
-  issue_group(a, row, blockIdx.x, gr);
+  issue_group<kBf16>(a, row, blockIdx.x, gr);
   const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
   const int kk = (int)(nv < a.k ? nv : a.k);
   if (kk == nv || (int64_t)blockIdx.x * kFilterChunk >= nv) return;
@@ -979,7 +1030,7 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   find_bin(lh, kBins2, (uint32_t)kk - above1, tmp, &s_bin, &s_above);
   const uint32_t b12 = (b1 << 11) | (uint32_t)s_bin;   // key bits 31..13
   uint32_t k32[kPer];
-  const int n_in = finish_group(gr, nv, k32);
+  const int n_in = finish_group<kBf16>(gr, nv, k32);
   const int64_t i0 = gr.g0;
   FilterRow fr{nv, kk, b1, above1};
   uint64_t* cand = a.cand + (size_t)row * kCandCap;
@@ -1025,6 +1076,7 @@ __device__ uint64_t rank_threshold(const uint64_t* cl, uint32_t n, uint32_t need
 // Every workgroup of a query resolves the threshold T from the candidates
 // (few: they share the top 19 key bits with the k-th largest score), finds
 // its chunk's output offset, and writes its chunk's selected ids in order.
+template <bool kBf16>
 __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   __shared__ uint32_t lh[kBinsMax];
   __shared__ uint32_t tmp[kFThreads / 64];
@@ -1040,7 +1092,7 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   const uint32_t* cc = a.chunk + (size_t)row * n_chunks(a.cap);
   const uint32_t cc_first = (int)threadIdx.x < (int)blockIdx.x ? cc[threadIdx.x] : 0u;
   Group gr;
-  issue_group(a, row, blockIdx.x, gr);
+  issue_group<kBf16>(a, row, blockIdx.x, gr);
   const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
   const int kk = (int)(nv < a.k ? nv : a.k);
   if (kk == nv) return;                    // written by k_filter1
@@ -1054,8 +1106,9 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
     for (uint32_t i = threadIdx.x + blockDim.x; i < n_cand; i += blockDim.x) cl[i] = gc[i];
   }
   __syncthreads();
-  const CandSrc src{in_lds ? cl : gc, n_cand, a.scores + (size_t)row * a.sc_ld, nv, b12,
-                    n_cand <= (uint32_t)kCandCap};
+  const void* srow = kBf16 ? (const void*)((const uint16_t*)a.scores + (size_t)row * a.sc_ld)
+                         : (const void*)(a.scores + (size_t)row * a.sc_ld);
+  const CandSrc<kBf16> src{in_lds ? cl : gc, n_cand, srow, nv, b12, n_cand <= (uint32_t)kCandCap};
   const uint64_t T = (src.compact && in_lds && n_cand <= (uint32_t)kRankCand)
                          ? rank_threshold(cl, n_cand, need)
                          : resolve_threshold(src, need, lh, tmp);
@@ -1073,7 +1126,7 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
     }
   }
   uint32_t k32[kPer];
-  const int n_in = finish_group(gr, nv, k32);
+  const int n_in = finish_group<kBf16>(gr, nv, k32);
   const int64_t i0 = gr.g0;
   uint32_t sel = 0;
 #pragma unroll
@@ -1146,13 +1199,22 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEve
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 fgrid((unsigned)n_chunks(a.cap), R);
-  hipLaunchKernelGGL(k_filter1, fgrid, dim3(kFThreads), 0, st, a);
+  if (a.score_bf16)
+    hipLaunchKernelGGL(k_filter1<true>, fgrid, dim3(kFThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_filter1<false>, fgrid, dim3(kFThreads), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_filter2, fgrid, dim3(kFThreads), 0, st, a);
+  if (a.score_bf16)
+    hipLaunchKernelGGL(k_filter2<true>, fgrid, dim3(kFThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_filter2<false>, fgrid, dim3(kFThreads), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_emit, fgrid, dim3(kFThreads), 0, st, a);
+  if (a.score_bf16)
+    hipLaunchKernelGGL(k_emit<true>, fgrid, dim3(kFThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_emit<false>, fgrid, dim3(kFThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -41,6 +41,8 @@ struct IndexArgs {
   const int64_t* pos;        // [R]
   int B, Q, H, m, k;
   int32_t* topk;             // [R][k]
+  int score_bf16;            // 1: scores are cut to bf16 (RNE) and ranked as
+                             // such; the workspace's score rows hold bf16
   // scan plan (one-query-per-workgroup FP4 scan)
   int score_iters;           // 1024-block iterations per scan workgroup
   int score_wgs;             // scan workgroups per query
@@ -50,7 +52,7 @@ struct IndexArgs {
   // workspace regions
   uint8_t* qmx;              // [R][H][d/2]
   uint8_t* qsc;              // [R][H][d/32]
-  float* scores;             // [R][sc_ld]
+  float* scores;             // [R][sc_ld] fp32, or bf16 (score_bf16) in the same space
   int64_t sc_ld;             // score row stride (cap rounded up to 64)
   uint32_t* hist;            // [R][256] first-digit histogram (key bits 31..24)
   uint32_t* hist2;           // [R][2048] second digit (key bits 23..13) within the first

@@ -14,13 +14,16 @@ min(floor((p+1)/m), cap); p < 0 sees none.
 
 Top-k: the k' = min(k, n_vis) largest scores; ties go to the lower block
 index; the result is listed in ascending block order and padded with -1 up to
-k.  Scores are ranked in fp32 (the selector's score precision, [Notes §9]
-"index scores in FP32" before the BF16 variant).
+k.  Scores are ranked in fp32 (the selector's score precision before the
+BF16 variant of [Notes §9]).  The BF16 variant ([Notes §9]: the top-k
+selector's index scores cut from FP32 to BF16): each fp32 score is rounded to
+the nearest bf16 (ties to even) and the bf16 values are ranked, equal values
+again going to the lower block index.
 """
 
 import numpy as np
 
-from .codecs import f32, idx_decode_rows, mxfp4_roundtrip
+from .codecs import bf16_decode, bf16_encode, f32, idx_decode_rows, mxfp4_roundtrip
 
 
 def n_visible(p, m, cap):
@@ -59,23 +62,33 @@ def index_scores(q_idx, w, keys, pos, m):
     return out
 
 
-def topk_from_scores(scores, k):
-    """Ascending block ids of the k' largest fp32 scores (lower id wins ties),
-    padded with -1 to length k."""
-    s32 = f32(scores).astype(np.float64)
-    n = len(s32)
+def ranked_scores(scores, score_dtype="f32"):
+    """The values the selector ranks: the fp32 scores, or ("bf16") those
+    rounded to the nearest bf16 (ties to even)."""
+    s32 = f32(scores)
+    if score_dtype == "bf16":
+        return bf16_decode(bf16_encode(s32)) if len(s32) else s32.astype(np.float64)
+    assert score_dtype == "f32"
+    return s32.astype(np.float64)
+
+
+def topk_from_scores(scores, k, score_dtype="f32"):
+    """Ascending block ids of the k' largest ranked scores (lower id wins
+    ties), padded with -1 to length k."""
+    s = ranked_scores(scores, score_dtype)
+    n = len(s)
     kk = min(k, n)
-    order = sorted(range(n), key=lambda i: (-s32[i], i))
+    order = sorted(range(n), key=lambda i: (-s[i], i))
     sel = sorted(order[:kk])
     return np.array(sel + [-1] * (k - kk), dtype=np.int64)
 
 
-def index_topk(q_idx, w, keys, pos, m, k):
+def index_topk(q_idx, w, keys, pos, m, k, score_dtype="f32"):
     scores = index_scores(q_idx, w, keys, pos, m)
     B = len(scores)
     Q = len(scores[0])
     out = np.full((B, Q, k), -1, dtype=np.int64)
     for b in range(B):
         for t in range(Q):
-            out[b, t] = topk_from_scores(scores[b][t], k)
+            out[b, t] = topk_from_scores(scores[b][t], k, score_dtype)
     return out, scores

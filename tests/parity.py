@@ -21,6 +21,7 @@ import torch
 
 from long_context_attention_v4attn_amd import binding as B
 from oracle import codecs as C
+from oracle.indexer import topk_from_scores
 
 OUT_TOL = 2e-2
 TOPK_REL = 1e-5
@@ -116,6 +117,41 @@ def check_topk_row(gpu_row, scores, k):
     gs = set(sel.tolist())
     assert upper <= gs, "an id clearly above the boundary is missing"
     assert gs <= upper | band, "an id clearly below the boundary was selected"
+    return "band"
+
+
+def check_topk_row_bf16(gpu_row, scores, k):
+    """The BF16-score selector.  Exact against the oracle's bf16 ranking,
+    unless an id's fp32 score lies within TOPK_REL (relative) of a bf16
+    rounding boundary -- the GPU's fp32 sum (another accumulation order) may
+    round it to the neighbouring bf16 value; then ids certainly above the
+    k-th bf16 value must be selected, ids certainly below must not, and ids
+    at (or possibly at) that value may go either way."""
+    n = len(scores)
+    kk = min(k, n)
+    g = np.asarray(gpu_row, np.int64)
+    assert np.all(g[kk:] == -1), "padding must be -1"
+    sel = g[:kk]
+    assert np.all(np.diff(sel) > 0), "ids must be ascending and unique"
+    assert kk == 0 or (sel[0] >= 0 and sel[-1] < n), "ids out of range"
+    ref = topk_from_scores(scores, k, "bf16")[:kk]
+    if kk == n or np.array_equal(sel, ref):
+        return "exact"
+    s32 = C.f32(scores).astype(np.float64)
+    b = C.bf16_decode(C.bf16_encode(s32))
+    lo = C.bf16_decode(C.bf16_encode(C.f32(s32 * (1 - TOPK_REL)))).astype(np.float64)
+    hi = C.bf16_decode(C.bf16_encode(C.f32(s32 * (1 + TOPK_REL)))).astype(np.float64)
+    vmin, vmax = np.minimum(np.minimum(lo, hi), b), np.maximum(np.maximum(lo, hi), b)
+    amb = (vmin != b) | (vmax != b)
+    order = sorted(range(n), key=lambda i: (-b[i], i))
+    T = b[order[kk - 1]]
+    assert np.any(amb & (vmax >= T) & (vmin <= T)), \
+        "bf16 top-k differs with no score near a bf16 rounding boundary at the k-th value"
+    gs = set(sel.tolist())
+    above = set(np.nonzero(vmin > T)[0].tolist())
+    below = set(np.nonzero(vmax < T)[0].tolist())
+    assert above <= gs, "an id certainly above the k-th bf16 value is missing"
+    assert not (gs & below), "an id certainly below the k-th bf16 value was selected"
     return "band"
 
 

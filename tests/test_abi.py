@@ -90,6 +90,11 @@ def test_invalid_arguments_rejected_on_host(clib):
     ix_bad = _Idx(3, 64, 1000, 0x1000, 0x2000)
     assert clib.v4attn_index_topk(FAKE, 1, FAKE, r(ix_bad), FAKE, 1, 1, 16, 4, 8, FAKE, FAKE, 1 << 30, None) == -2
     assert clib.v4attn_index_topk(FAKE, 1, FAKE, r(ix), FAKE, 1, 1, 16, 4, 8, FAKE, None, 0, None) == -3
+    # the BF16-score variant validates the same way
+    assert clib.v4attn_index_topk_bf16(FAKE, 1, FAKE, r(ix), FAKE, 1, 1, 16, 4, 0, FAKE, FAKE, 1 << 30, None) == -1
+    assert clib.v4attn_index_topk_bf16(FAKE, 1, FAKE, r(ix_bad), FAKE, 1, 1, 16, 4, 8, FAKE, FAKE, 1 << 30,
+                                       None) == -2
+    assert clib.v4attn_index_topk_bf16(FAKE, 1, FAKE, r(ix), FAKE, 1, 1, 16, 4, 8, FAKE, None, 0, None) == -3
     # attend: H not a multiple of 16 on the FP8 path, window ring too small, f32 q on FP8
     win = _KV(2, 448, 64, 0, 64, 0x1000, 0x2000, 0x3000)
     assert clib.v4attn_hca_attend(FAKE, 1, r(kv), 128, r(kv), 16, FAKE, None, ctypes.c_float(0.1),

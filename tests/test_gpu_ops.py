@@ -105,7 +105,8 @@ def test_compress_ring_wraps(lib):
 
 # ---------------------------------------------------------------- index + top-k
 
-def _index_case(lib, rng, Bn, Q, cap, H, k, m, pos, key_fmt="mxfp4", d=128, w=None, keys=None):
+def _index_case(lib, rng, Bn, Q, cap, H, k, m, pos, key_fmt="mxfp4", d=128, w=None, keys=None,
+                bf16_scores=False):
     if keys is None:
         y = _f32(rng, (Bn, cap, d), d ** -0.5)
         keys = C.idx_encode(y, key_fmt)
@@ -114,15 +115,17 @@ def _index_case(lib, rng, Bn, Q, cap, H, k, m, pos, key_fmt="mxfp4", d=128, w=No
         w = rng.random((Bn, Q, H)).astype(np.float32)
     qb = C.bf16_encode(q)
     qd = C.bf16_decode(qb).astype(np.float32)
-    topk = lib.v4attn_index_topk(P.dev(qb.view(np.int16)).view(torch.bfloat16), P.dev(w),
-                                 P.idx_to_dev(keys), P.dev(pos), m, k)
+    call = lib.v4attn_index_topk_bf16 if bf16_scores else lib.v4attn_index_topk
+    topk = call(P.dev(qb.view(np.int16)).view(torch.bfloat16), P.dev(w), P.idx_to_dev(keys),
+                P.dev(pos), m, k)
     torch.cuda.synchronize()
     sc = index_scores(qd, w, keys, pos, m)
     g = topk.cpu().numpy()
+    check = P.check_topk_row_bf16 if bf16_scores else P.check_topk_row
     kinds = []
     for b in range(Bn):
         for t in range(Q):
-            kinds.append(P.check_topk_row(g[b, t], sc[b][t], k))
+            kinds.append(check(g[b, t], sc[b][t], k))
     return kinds
 
 
@@ -134,6 +137,33 @@ def test_index_topk_mxfp4(lib, cap, k, H):
     pos = np.array([[4 * cap - 1, 4 * (cap // 2) + 2, 37], [4 * cap + 100, 4 * cap - 5, 3]], np.int64)
     kinds = _index_case(lib, rng, Bn, Q, cap, H, k, m, pos)
     assert kinds.count("exact") >= len(kinds) // 2
+
+
+@pytest.mark.parametrize("cap,k,H", [(1000, 64, 16), (5003, 300, 16), (3000, 100, 64), (777, 1024, 32)])
+def test_index_topk_bf16_scores(lib, cap, k, H):
+    # the BF16-score selector: the oracle's bf16 ranking (ties to the lower id)
+    print(f"index bf16 scores cap={cap} k={k} H={H}", flush=True)
+    rng = _rng(cap + k)
+    Bn, Q, m = 2, 3, 4
+    pos = np.array([[4 * cap - 1, 4 * (cap // 2) + 2, 37], [4 * cap + 100, 4 * cap - 5, 3]], np.int64)
+    kinds = _index_case(lib, rng, Bn, Q, cap, H, k, m, pos, bf16_scores=True)
+    assert kinds.count("exact") >= len(kinds) // 2
+
+
+def test_index_topk_bf16_scores_f32_keys_and_ties(lib):
+    print("index bf16 scores: f32 keys; all-equal scores", flush=True)
+    rng = _rng(11)
+    _index_case(lib, rng, 1, 1, 1024, 4, 64, 4, np.array([[4095]], np.int64), key_fmt="f32", d=64,
+                bf16_scores=True)
+    # all-zero head weights: every score is 0, the k lowest ids win
+    Bn, Q, cap, H, k = 1, 2, 3000, 16, 50
+    pos = np.array([[4 * cap - 1, 4 * 1000 - 1]], np.int64)
+    w = np.zeros((Bn, Q, H), np.float32)
+    keys = C.idx_encode(_f32(rng, (Bn, cap, 128), 0.1), "mxfp4")
+    q = _f32(rng, (Bn, Q, H, 128), 0.1)
+    topk = lib.v4attn_index_topk_bf16(P.dev(q), P.dev(w), P.idx_to_dev(keys), P.dev(pos), 4, k)
+    g = topk.cpu().numpy()
+    assert list(g[0, 0]) == list(range(k)) and list(g[0, 1]) == list(range(k))
 
 
 def test_index_topk_f32_workload1_shape(lib):

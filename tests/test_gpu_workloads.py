@@ -105,6 +105,31 @@ def test_csa_decode_full_size_sampled_rows(lib, wid, B):
         P.check_out(out[b:b + 1], ref, what=f"row {b}")
 
 
+def test_csa_decode_full_size_bf16_selector(lib):
+    # workload 4 through the BF16-score selector, sampled rows against the
+    # oracle's bf16 ranking; the recall of the fp32 selection is reported
+    c = synth.WORKLOADS[4]
+    print(f"workload 4: BF16-score selector B={c['B']} ctx={c['ctx']}", flush=True)
+    last = c["B"] - 1
+    case = _decode_case(lib, 4, distinct=[0, last])
+    g = case["g"]
+    keys = P.idx_to_dev(case["keys"])
+    qi_t = P.dev(case["qib"].view(np.int16)).view(torch.bfloat16)
+    t16 = lib.v4attn_index_topk_bf16(qi_t, P.dev(g["w"]), keys, P.dev(g["pos"]), c["m"], c["k"])
+    t32 = lib.v4attn_index_topk(qi_t, P.dev(g["w"]), keys, P.dev(g["pos"]), c["m"], c["k"])
+    torch.cuda.synchronize()
+    t16, t32 = t16.cpu().numpy(), t32.cpu().numpy()
+    qi = C.bf16_decode(case["qib"]).astype(np.float32)
+    for b in (0, last):
+        sc = index_scores(qi[b:b + 1], g["w"][b:b + 1],
+                          C.Idx("mxfp4", 128, case["keys"].codes[b:b + 1], case["keys"].scales[b:b + 1]),
+                          g["pos"][b:b + 1], c["m"])
+        P.check_topk_row_bf16(t16[b, 0], sc[0][0], c["k"])
+        recall = len(set(t16[b, 0].tolist()) & set(t32[b, 0].tolist())) / c["k"]
+        print(f"  row {b}: recall of the fp32 top-{c['k']} = {recall:.4f}", flush=True)
+        assert recall > 0.9
+
+
 def test_hca_decode_full_size_sampled_rows(lib):
     c = synth.WORKLOADS[3]
     print(f"workload 3: HCA decode B={c['B']} ctx={c['ctx']}", flush=True)

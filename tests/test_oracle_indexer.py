@@ -120,3 +120,60 @@ def test_k_at_least_nvis_selects_all():
     topk, sc = index_topk(q, w, keys, np.array([[4 * 12 + 1]]), 4, 20)   # n_vis = 12
     assert list(topk[0, 0]) == list(range(12)) + [-1] * 8
     assert len(sc[0][0]) == 12
+
+
+# ---------------------------------------------------------------- BF16-score selector
+# [Notes §9]: the selector's index scores cut from FP32 to BF16.
+
+def test_bf16_selector_hand_computed_ties():
+    # 1.0, 1 + 2^-10, 1 + 2^-9 all round to bf16 1.0 (the bf16 step at 1 is
+    # 2^-7), so the fp32 ranking {1, 2} becomes a three-way tie: ids 0, 1 win
+    s = np.array([1.0, 1.0 + 2.0 ** -10, 1.0 + 2.0 ** -9, 0.5])
+    assert list(topk_from_scores(s, 2, "f32")) == [1, 2]
+    assert list(topk_from_scores(s, 2, "bf16")) == [0, 1]
+
+
+def test_bf16_selector_round_half_to_even():
+    # 1 + 2^-8 is halfway between bf16 1.0 (even mantissa) and 1 + 2^-7:
+    # ties to even -> 1.0, equal to id 1; 1 + 3 * 2^-8 is halfway between
+    # 1 + 2^-7 (odd mantissa) and 1 + 2^-6 (even): rounds up, above id 3
+    s = np.array([1.0 + 2.0 ** -8, 1.0, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -7])
+    # bf16 values: [1.0, 1.0, 1 + 2^-6, 1 + 2^-7] -> order 2, 3, 0, 1
+    assert list(topk_from_scores(s, 1, "bf16")) == [2]
+    assert list(topk_from_scores(s, 2, "bf16")) == [2, 3]
+    assert list(topk_from_scores(s, 3, "bf16")) == [0, 2, 3]
+    # fp32 order: 2, 3, 0, 1 as well, but id 0 beats id 1 by value there
+    assert list(topk_from_scores(s, 3, "f32")) == [0, 2, 3]
+    s2 = np.array([1.0, 1.0 + 2.0 ** -8])          # bf16: equal -> lower id
+    assert list(topk_from_scores(s2, 1, "f32")) == [1]
+    assert list(topk_from_scores(s2, 1, "bf16")) == [0]
+
+
+def test_bf16_selector_is_fp32_on_bf16_values():
+    # scores already representable in bf16 rank identically in both modes
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        n = int(rng.integers(1, 300))
+        bits = rng.integers(0x3C00, 0x4400, n).astype(np.uint16)   # positive bf16 values
+        s = C.bf16_decode(bits)
+        k = int(rng.integers(1, 320))
+        assert np.array_equal(topk_from_scores(s, k, "bf16"), topk_from_scores(s, k, "f32"))
+
+
+def test_bf16_selector_order_property():
+    # every selected id's bf16 value >= every other's; at the boundary value
+    # the selected ids are the lowest ones
+    rng = np.random.default_rng(10)
+    for _ in range(20):
+        n = int(rng.integers(2, 400))
+        s = rng.normal(1.0, 0.01, n)
+        k = int(rng.integers(1, n))
+        sel = topk_from_scores(s, k, "bf16")
+        sel = sel[sel >= 0]
+        v = C.bf16_decode(C.bf16_encode(C.f32(s)))
+        rest = np.setdiff1d(np.arange(n), sel)
+        assert v[sel].min() >= v[rest].max()
+        t = v[sel].min()
+        tie_sel = sel[v[sel] == t]
+        tie_rest = rest[v[rest] == t]
+        assert len(tie_rest) == 0 or tie_sel.max() < tie_rest.min()
