@@ -178,6 +178,7 @@ def build_inputs(v4, torch, replicas, log):
         reps.append(r)
     for r in reps:
         r.c_topk = torch.empty(cc["B"], 1, cc["k"], dtype=torch.int32, device=dev)
+        r.c_topk16 = torch.empty_like(r.c_topk)
         r.c_out = torch.empty_like(r.c_q)
         r.h_out = torch.empty_like(r.h_q)
     torch.cuda.synchronize()
@@ -185,7 +186,9 @@ def build_inputs(v4, torch, replicas, log):
 
 
 def make_calls(v4, torch, r, ws, cc, ch):
-    """The three C-ABI calls of a step on replica r (fixed buffers)."""
+    """The three C-ABI calls of a step on replica r (fixed buffers), and the
+    BF16-score selector variant of the first (timed beside it, not in the
+    step)."""
     D = 512
     sc = D ** -0.5
 
@@ -201,7 +204,11 @@ def make_calls(v4, torch, r, ws, cc, ch):
         v4.v4attn_hca_attend(r.h_q, r.h_comp, ch["m"], r.h_win, ch["n_win"], r.h_pos, None, sc,
                              out=r.h_out, ws=ws["hca"])
 
-    return [idx, csa, hca]
+    def idx16():
+        v4.v4attn_index_topk_bf16(r.c_qi, r.c_w, r.c_keys, r.c_pos, cc["m"], cc["k"],
+                                  topk=r.c_topk16, ws=ws["index"])
+
+    return [idx, csa, hca, idx16]
 
 
 # ---------------------------------------------------------------- prefill chunk
@@ -455,12 +462,12 @@ def main():
 
         csa_layer = capture([f for cs in calls for f in cs[:2]])
         hca_layer = capture([cs[2] for cs in calls])
-        per_call_g = [capture([cs[i] for cs in calls]) for i in range(3)]
+        per_call_g = [capture([cs[i] for cs in calls]) for i in range(4)]
         torch.cuda.synchronize()
     else:
         csa_layer = lambda: [f() for cs in calls for f in cs[:2]]
         hca_layer = lambda: [cs[2]() for cs in calls]
-        per_call_g = [(lambda i=i: [cs[i]() for cs in calls]) for i in range(3)]
+        per_call_g = [(lambda i=i: [cs[i]() for cs in calls]) for i in range(4)]
 
     for _ in range(max(1, args.warmup // R)):
         csa_layer()
@@ -500,7 +507,14 @@ def main():
         return e0.elapsed_time(e1) / (n * R) * 1e-3
 
     n_call = max(4, rounds // 4)
-    t_idx, t_csa_att, t_hca_call = (per_call(i, n_call) for i in range(3))
+    t_idx, t_csa_att, t_hca_call, t_idx16 = (per_call(i, n_call) for i in range(4))
+    # recall of the fp32 selection by the BF16-score selector (every replica
+    # ran both in the eager pass; same inputs)
+    recalls = []
+    for r in reps:
+        a32, a16 = r.c_topk.cpu().numpy(), r.c_topk16.cpu().numpy()
+        for b in range(cc["B"]):
+            recalls.append(len(set(a32[b, 0].tolist()) & set(a16[b, 0].tolist())) / cc["k"])
 
     # ---- dominant kernels, timed live with HIP events recorded by the
     # library immediately around each kernel (eager launches)
@@ -590,6 +604,12 @@ def main():
         "replicas": R,
         "graph": not args.no_graph,
         "roofline": roofline,
+        "selector_bf16": {
+            "what": "v4attn_index_topk_bf16 (index scores ranked in bf16) on the CSA decode call",
+            "index_topk_us": round(t_idx16 * 1e6, 3), "index_topk_fp32_us": round(t_idx * 1e6, 3),
+            "speedup": round(t_idx / t_idx16, 3),
+            "recall_vs_fp32": round(float(np.mean(recalls)), 5),
+            "recall_min": round(float(np.min(recalls)), 5)},
     }
     if not args.no_prefill:
         del csa_layer, hca_layer, per_call_g, calls, reps, ws
