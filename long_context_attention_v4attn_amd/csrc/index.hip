@@ -921,11 +921,10 @@ struct CandList {
 
 // Candidates of the threshold search: the compact list, or (when it
 // overflowed) the query's scores filtered by the first two digits.
-template <bool kBf16>
 struct CandSrc {
   const uint64_t* cand;
   uint32_t n;
-  const void* sc;                          // the query's score row
+  const float* sc;
   int64_t nv;
   uint32_t b12;                            // key bits 31..13 of the candidates
   bool compact;
@@ -935,7 +934,7 @@ struct CandSrc {
       *key = cand[i];
       return true;
     }
-    const uint32_t k32 = score_key(kBf16 ? bf16_to_f32(((const uint16_t*)sc)[i]) : ((const float*)sc)[i]);
+    const uint32_t k32 = score_key(sc[i]);
     *key = sel_key(k32, i);
     return (k32 >> kSh2) == b12;
   }
@@ -957,8 +956,7 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* tmp) {
 // The exact 64-bit threshold T: the need-th largest key among the
 // candidates (radix select on the bits below the candidates' common 19-bit
 // prefix).  Exactly `need` candidates have keys >= T.
-template <bool kBf16>
-__device__ uint64_t resolve_threshold(const CandSrc<kBf16>& src, uint32_t need, uint32_t* lh,
+__device__ uint64_t resolve_threshold(const CandSrc& src, uint32_t need, uint32_t* lh,
                                       uint32_t* tmp) {
   __shared__ uint64_t s_prefix, s_mask;
   __shared__ uint32_t s_need, s_above;
@@ -1003,7 +1001,6 @@ __device__ uint64_t resolve_threshold(const CandSrc<kBf16>& src, uint32_t need, 
   return T;
 }
 
-template <bool kBf16>
 __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   __shared__ uint32_t lh[kBins2];
   __shared__ uint32_t tmp[kFThreads / 64];
@@ -1019,7 +1016,7 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   const u32x4* gh2 = (const u32x4*)(a.hist2 + (size_t)row * kBins2 + threadIdx.x * kPer2);
   const u32x4 h2a = gh2[0], h2b = gh2[1];
   Group gr;
-  issue_group<kBf16>(a, row, blockIdx.x, gr);
+  issue_group<false>(a, row, blockIdx.x, gr);
   const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
   const int kk = (int)(nv < a.k ? nv : a.k);
   if (kk == nv || (int64_t)blockIdx.x * kFilterChunk >= nv) return;
@@ -1030,7 +1027,7 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   find_bin(lh, kBins2, (uint32_t)kk - above1, tmp, &s_bin, &s_above);
   const uint32_t b12 = (b1 << 11) | (uint32_t)s_bin;   // key bits 31..13
   uint32_t k32[kPer];
-  const int n_in = finish_group<kBf16>(gr, nv, k32);
+  const int n_in = finish_group<false>(gr, nv, k32);
   const int64_t i0 = gr.g0;
   FilterRow fr{nv, kk, b1, above1};
   uint64_t* cand = a.cand + (size_t)row * kCandCap;
@@ -1076,7 +1073,6 @@ __device__ uint64_t rank_threshold(const uint64_t* cl, uint32_t n, uint32_t need
 // Every workgroup of a query resolves the threshold T from the candidates
 // (few: they share the top 19 key bits with the k-th largest score), finds
 // its chunk's output offset, and writes its chunk's selected ids in order.
-template <bool kBf16>
 __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   __shared__ uint32_t lh[kBinsMax];
   __shared__ uint32_t tmp[kFThreads / 64];
@@ -1092,7 +1088,7 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   const uint32_t* cc = a.chunk + (size_t)row * n_chunks(a.cap);
   const uint32_t cc_first = (int)threadIdx.x < (int)blockIdx.x ? cc[threadIdx.x] : 0u;
   Group gr;
-  issue_group<kBf16>(a, row, blockIdx.x, gr);
+  issue_group<false>(a, row, blockIdx.x, gr);
   const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
   const int kk = (int)(nv < a.k ? nv : a.k);
   if (kk == nv) return;                    // written by k_filter1
@@ -1106,9 +1102,8 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
     for (uint32_t i = threadIdx.x + blockDim.x; i < n_cand; i += blockDim.x) cl[i] = gc[i];
   }
   __syncthreads();
-  const void* srow = kBf16 ? (const void*)((const uint16_t*)a.scores + (size_t)row * a.sc_ld)
-                         : (const void*)(a.scores + (size_t)row * a.sc_ld);
-  const CandSrc<kBf16> src{in_lds ? cl : gc, n_cand, srow, nv, b12, n_cand <= (uint32_t)kCandCap};
+  const CandSrc src{in_lds ? cl : gc, n_cand, a.scores + (size_t)row * a.sc_ld, nv, b12,
+                    n_cand <= (uint32_t)kCandCap};
   const uint64_t T = (src.compact && in_lds && n_cand <= (uint32_t)kRankCand)
                          ? rank_threshold(cl, n_cand, need)
                          : resolve_threshold(src, need, lh, tmp);
@@ -1126,7 +1121,7 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
     }
   }
   uint32_t k32[kPer];
-  const int n_in = finish_group<kBf16>(gr, nv, k32);
+  const int n_in = finish_group<false>(gr, nv, k32);
   const int64_t i0 = gr.g0;
   uint32_t sel = 0;
 #pragma unroll
@@ -1143,6 +1138,114 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
     if ((sel >> j) & 1u) {
+      if (pos < (uint32_t)kk) out[pos] = (int32_t)(i0 + j);
+      pos++;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- BF16-score selector
+// With bf16 scores the two radix digits fix the k-th value T exactly (a bf16
+// value's key has its low 16 bits zero), so the selection needs no
+// candidate list: every id above T is taken, and of the ids at T the
+// lowest-indexed ones, as many as are still needed.
+
+// Second filter: T's digits and, per chunk, its counts above and at T
+// (packed: above in the high half, at T in the low half, each <= 4096).
+__global__ void __launch_bounds__(kFThreads) k_filter2_bf16(IndexArgs a) {
+  __shared__ uint32_t lh[kBins2];
+  __shared__ uint32_t tmp[kFThreads / 64];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above;
+  const int row = blockIdx.y;
+  // all global loads first, before the query position arrives
+  uint32_t* ctr = a.ctr + (size_t)row * kCtr;
+  const uint32_t b1 = ctr[4], above1 = ctr[5];
+  constexpr int kPer2 = kBins2 / kFThreads;                          // 8
+  const u32x4* gh2 = (const u32x4*)(a.hist2 + (size_t)row * kBins2 + threadIdx.x * kPer2);
+  const u32x4 h2a = gh2[0], h2b = gh2[1];
+  Group gr;
+  issue_group<true>(a, row, blockIdx.x, gr);
+  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
+  const int kk = (int)(nv < a.k ? nv : a.k);
+  if (kk == nv || (int64_t)blockIdx.x * kFilterChunk >= nv) return;
+  *(u32x4*)&lh[threadIdx.x * kPer2] = h2a;
+  *(u32x4*)&lh[threadIdx.x * kPer2 + 4] = h2b;
+  __syncthreads();
+  find_bin(lh, kBins2, (uint32_t)kk - above1, tmp, &s_bin, &s_above);
+  const uint32_t b12 = (b1 << 11) | (uint32_t)s_bin;   // key bits 31..13 of T
+  uint32_t k32[kPer];
+  const int n_in = finish_group<true>(gr, nv, k32);
+  uint32_t above = 0, at = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const bool in = j < n_in;
+    const uint32_t d12 = k32[j] >> kSh2;
+    above += (in && d12 > b12) ? 1u : 0u;
+    at += (in && d12 == b12) ? 1u : 0u;
+  }
+  const uint32_t packed = block_sum((above << 16) | at, tmp);
+  if (threadIdx.x == 0) {
+    a.chunk[(size_t)row * n_chunks(a.cap) + blockIdx.x] = packed;
+    if (blockIdx.x == 0) {
+      ctr[2] = b12;
+      ctr[3] = (uint32_t)kk - above1 - s_above;   // ids at T to take
+    }
+  }
+}
+
+// Emit: a workgroup's chunk offset = ids above T in earlier chunks + the ids
+// at T taken there; within the chunk one scan of the packed (above, at T)
+// counts places every thread's ids; output ascending, tail -1.
+__global__ void __launch_bounds__(kFThreads) k_emit_bf16(IndexArgs a) {
+  __shared__ uint32_t tmp[kFThreads / 64];
+  const int row = blockIdx.y;
+  const uint32_t* ctr = a.ctr + (size_t)row * kCtr;
+  const uint32_t b12 = ctr[2], need = ctr[3];
+  const uint32_t* cc = a.chunk + (size_t)row * n_chunks(a.cap);
+  const uint32_t cc_first = (int)threadIdx.x < (int)blockIdx.x ? cc[threadIdx.x] : 0u;
+  Group gr;
+  issue_group<true>(a, row, blockIdx.x, gr);
+  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
+  const int kk = (int)(nv < a.k ? nv : a.k);
+  if (kk == nv) return;                    // written by k_filter1
+  int32_t* out = a.topk + (size_t)row * a.k;
+  if (blockIdx.x == 0)
+    for (int i = kk + threadIdx.x; i < a.k; i += blockDim.x) out[i] = -1;
+  if ((int64_t)blockIdx.x * kFilterChunk >= nv) return;
+  // earlier chunks: ids above T (all taken) and at T (summed separately: the
+  // ties may outnumber 16 bits over many chunks)
+  uint32_t b_above = cc_first >> 16, b_at = cc_first & 0xFFFFu;
+  for (int c = threadIdx.x + blockDim.x; c < (int)blockIdx.x; c += blockDim.x) {
+    b_above += cc[c] >> 16;
+    b_at += cc[c] & 0xFFFFu;
+  }
+  b_above = block_sum(b_above, tmp);
+  b_at = block_sum(b_at, tmp);
+  const uint32_t left = need > b_at ? need - b_at : 0u;   // ties still to take from here on
+  uint32_t k32[kPer];
+  const int n_in = finish_group<true>(gr, nv, k32);
+  const int64_t i0 = gr.g0;
+  uint32_t above = 0, at = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const bool in = j < n_in;
+    const uint32_t d12 = k32[j] >> kSh2;
+    above += (in && d12 > b12) ? 1u : 0u;
+    at += (in && d12 == b12) ? 1u : 0u;
+  }
+  const uint32_t packed = (above << 16) | at;              // chunk sums <= 4096 each
+  const uint32_t ex = block_incl_scan(packed, tmp) - packed;
+  const uint32_t ex_at = ex & 0xFFFFu;
+  uint32_t pos = b_above + (b_at < need ? b_at : need) + (ex >> 16) + (ex_at < left ? ex_at : left);
+  uint32_t tie = ex_at;                    // rank of the next id at T within the chunk
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const uint32_t d12 = k32[j] >> kSh2;
+    const bool is_at = j < n_in && d12 == b12;
+    const bool take = (j < n_in && d12 > b12) || (is_at && tie < left);
+    tie += is_at ? 1u : 0u;
+    if (take) {
       if (pos < (uint32_t)kk) out[pos] = (int32_t)(i0 + j);
       pos++;
     }
@@ -1206,15 +1309,15 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEve
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.score_bf16)
-    hipLaunchKernelGGL(k_filter2<true>, fgrid, dim3(kFThreads), 0, st, a);
+    hipLaunchKernelGGL(k_filter2_bf16, fgrid, dim3(kFThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(k_filter2<false>, fgrid, dim3(kFThreads), 0, st, a);
+    hipLaunchKernelGGL(k_filter2, fgrid, dim3(kFThreads), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.score_bf16)
-    hipLaunchKernelGGL(k_emit<true>, fgrid, dim3(kFThreads), 0, st, a);
+    hipLaunchKernelGGL(k_emit_bf16, fgrid, dim3(kFThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(k_emit<false>, fgrid, dim3(kFThreads), 0, st, a);
+    hipLaunchKernelGGL(k_emit, fgrid, dim3(kFThreads), 0, st, a);
   return hipGetLastError();
 }
 
