@@ -211,6 +211,72 @@ def make_calls(v4, torch, r, ws, cc, ch):
     return [idx, csa, hca, idx16]
 
 
+# ---------------------------------------------------------------- production shapes
+
+def graph_time(torch, fns, n):
+    """Seconds per call: the calls `fns` (one per replica) captured in one
+    graph, replayed n times."""
+    cap_stream = torch.cuda.Stream()
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap_stream):
+        for f in fns:
+            f()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (n * len(fns)) * 1e-3
+
+
+def bench_production(v4, torch, reps, ws, cc, ch, n=8):
+    """The production shapes of the pages' hyper-parameter table on the CSA
+    layer's caches: the indexer with 64 heads, top-512 and top-1024 with their
+    CSA attention; and a window-only (compression-free) layer on the HCA
+    layer's queries and window rings.  Each call over all replicas in one
+    graph (as the step's calls), per-call times."""
+    from long_context_attention_v4attn_amd import synth
+    H_I, D, sc = synth.PRODUCTION["H_I"], 512, 512 ** -0.5
+    B, cap = cc["B"], cc["ctx"] // cc["m"]
+    q64, w64 = synth.index_queries(CSA_WID, B, H_I)
+    qi = torch.from_numpy(q64).cuda().to(torch.bfloat16)
+    w = torch.from_numpy(w64).cuda()
+    wsi = torch.empty(v4.v4attn_workspace_bytes(v4.OP_INDEX_TOPK, B, 1, H_I, 128, cap, 4096, 0),
+                      dtype=torch.uint8, device="cuda")
+    res = {"indexer_heads": H_I}
+    for k in synth.PRODUCTION["ks"]:
+        topk = [torch.empty(B, 1, k, dtype=torch.int32, device="cuda") for _ in reps]
+        wsa = torch.empty(max(1, v4.v4attn_workspace_bytes(v4.OP_CSA_ATTEND, B, 1, 64, D, 0, k, cc["n_win"])),
+                          dtype=torch.uint8, device="cuda")
+        f_i = [(lambda r=r, t=t: v4.v4attn_index_topk(qi, w, r.c_keys, r.c_pos, cc["m"], k, topk=t, ws=wsi))
+               for r, t in zip(reps, topk)]
+        f_a = [(lambda r=r, t=t: v4.v4attn_csa_attend(r.c_q, r.c_comp, t, r.c_win, cc["n_win"], r.c_pos, None,
+                                                      sc, out=r.c_out, ws=wsa))
+               for r, t in zip(reps, topk)]
+        t_i, t_a = graph_time(torch, f_i, n), graph_time(torch, f_a, n)
+        res[f"top{k}"] = {"index_topk_us": round(t_i * 1e6, 3), "csa_attend_us": round(t_a * 1e6, 3),
+                          "csa_queries_per_s": round(B / (t_i + t_a), 1)}
+    # window-only: a one-row compressed cache that no position reaches (the
+    # split plan follows the cache size, so the list bound is the window)
+    none = v4.KVCache.empty(ch["B"], 1, 448, 64, v4.KV_FP8_BF16ROPE)
+    wsw = torch.empty(max(1, v4.v4attn_workspace_bytes(v4.OP_HCA_ATTEND, ch["B"], 1, 64, D, 1, 1 << 30,
+                                                       ch["n_win"])), dtype=torch.uint8, device="cuda")
+    f_w = [(lambda r=r: v4.v4attn_hca_attend(r.h_q, none, 1 << 30, r.h_win, ch["n_win"], r.h_pos, None,
+                                             sc, out=r.h_out, ws=wsw)) for r in reps]
+    t_w = graph_time(torch, f_w, n)
+    res["window_only"] = {"B": ch["B"], "entries": ch["n_win"], "attend_us": round(t_w * 1e6, 3),
+                          "queries_per_s": round(ch["B"] / t_w, 1)}
+    return res
+
+
 # ---------------------------------------------------------------- prefill chunk
 
 PREFILL_WID = 5
@@ -611,6 +677,8 @@ def main():
             "recall_vs_fp32": round(float(np.mean(recalls)), 5),
             "recall_min": round(float(np.min(recalls)), 5)},
     }
+    log("production shapes ...")
+    result["production_shapes"] = bench_production(v4, torch, reps, ws, cc, ch)
     if not args.no_prefill:
         del csa_layer, hca_layer, per_call_g, calls, reps, ws
         torch.cuda.empty_cache()

@@ -34,6 +34,11 @@ T_KV_A, T_KV_B, T_Z_A, T_Z_B, T_BIAS = 1, 2, 3, 4, 5
 T_KI_A, T_KI_B, T_ZI_A, T_ZI_B, T_BIAS_I = 6, 7, 8, 9, 10
 T_Q, T_QI, T_W, T_COMP, T_KEYS, T_WIN, T_SINK = 11, 12, 13, 14, 15, 16, 17
 T_HCA_KV, T_HCA_Z, T_HCA_BIAS, T_HCA_COMP, T_HCA_WIN = 18, 19, 20, 21, 22
+T_QI64, T_W64 = 23, 24
+
+# Production shapes of the pages' hyper-parameter table (the indexer's 64
+# heads, top-512 / top-1024) run on workload 4's caches with these queries.
+PRODUCTION = dict(H_I=64, ks=(512, 1024))
 
 WORKLOADS = {
     1: dict(name="csa_decode_f32_4k", kind="csa", B=1, ctx=4096, m=4, H=8,
@@ -131,6 +136,18 @@ def decode_inputs(wid, B=None, n_comp=None, ctx=None, with_index=None, ring=None
         g["w"] = batched_rows(lambda b: uniform(wid, T_W, b, (1, c["H_I"])))
     g["pos"] = np.full((len(rows), 1), ctx - 1, dtype=np.int64)
     return g
+
+
+def index_queries(wid, B, H_I, rows=None):
+    """Indexer queries with H_I heads for workload wid's decode rows:
+    q_idx [B][1][H_I][d_I] ~ N(0,1)/sqrt(d_I), w [B][1][H_I] ~ U(0,1), drawn
+    from their own streams (the 16-head draws are untouched)."""
+    c = WORKLOADS[wid]
+    dI = c["d_I"]
+    rows = list(range(B)) if rows is None else list(rows)
+    q = np.stack([normal(wid, T_QI64, b, (1, H_I, dI), dI ** -0.5) for b in rows])
+    w = np.stack([uniform(wid, T_W64, b, (1, H_I)) for b in rows])
+    return q, w
 
 
 # ---------------------------------------------------------------- compress inputs

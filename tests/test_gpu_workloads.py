@@ -130,6 +130,59 @@ def test_csa_decode_full_size_bf16_selector(lib):
         assert recall > 0.9
 
 
+@pytest.mark.parametrize("k", list(synth.PRODUCTION["ks"]))
+def test_csa_decode_1m_production_shapes(lib, k):
+    # the pages' production indexer (64 heads x 128) with top-512 / top-1024 on
+    # workload 4's caches: sampled rows of the top-k and of the attention
+    c = synth.WORKLOADS[4]
+    H_I = synth.PRODUCTION["H_I"]
+    print(f"workload 4 caches, indexer {H_I} heads, top-{k}", flush=True)
+    last = c["B"] - 1
+    case = _decode_case(lib, 4, distinct=[0, last])
+    g = case["g"]
+    q64, w64 = synth.index_queries(4, c["B"], H_I)
+    qib = C.bf16_encode(q64)
+    topk = lib.v4attn_index_topk(P.dev(qib.view(np.int16)).view(torch.bfloat16), P.dev(w64),
+                                 P.idx_to_dev(case["keys"]), P.dev(g["pos"]), c["m"], k)
+    out = lib.v4attn_csa_attend(P.dev(case["qb"].view(np.int16)).view(torch.bfloat16),
+                                P.kv_to_dev(case["comp"]), topk, P.kv_to_dev(case["win"]),
+                                c["n_win"], P.dev(g["pos"]), None, 512 ** -0.5)
+    torch.cuda.synchronize()
+    topk = topk.cpu().numpy()
+    qi = C.bf16_decode(qib).astype(np.float32)
+    for b in (0, last):
+        sc = index_scores(qi[b:b + 1], w64[b:b + 1],
+                          C.Idx("mxfp4", 128, case["keys"].codes[b:b + 1], case["keys"].scales[b:b + 1]),
+                          g["pos"][b:b + 1], c["m"])
+        P.check_topk_row(topk[b, 0], sc[0][0], k)
+        sub = lambda kv: C.KV("fp8", kv.d_nope, kv.d_rope, kv.nope[b:b + 1], kv.rope[b:b + 1],
+                              kv.scale[b:b + 1])
+        _, ref = csa_attend(case["qb"][b:b + 1], "bf16", sub(case["comp"]), topk[b:b + 1],
+                            sub(case["win"]), c["n_win"], g["pos"][b:b + 1], None, 512 ** -0.5, "bf16")
+        P.check_out(out[b:b + 1], ref, what=f"row {b}")
+
+
+def test_window_only_layer_full_shape(lib):
+    # a ratio-0 layer (no compressed branch): the HCA call on a one-row
+    # compressed cache with a compression rate no position reaches, so only
+    # the 128-token window is attended
+    c = synth.WORKLOADS[3]
+    print(f"window-only layer: B={c['B']}, 64 heads, window {c['n_win']}", flush=True)
+    case = _decode_case(lib, 3, n_comp=1)
+    g = case["g"]
+    m = 1 << 30
+    out = lib.v4attn_hca_attend(P.dev(case["qb"].view(np.int16)).view(torch.bfloat16),
+                                P.kv_to_dev(case["comp"]), m, P.kv_to_dev(case["win"]),
+                                c["n_win"], P.dev(g["pos"]), None, 512 ** -0.5)
+    torch.cuda.synchronize()
+    for b in (0, c["B"] - 1):
+        sub = lambda kv: C.KV("fp8", kv.d_nope, kv.d_rope, kv.nope[b:b + 1], kv.rope[b:b + 1],
+                              kv.scale[b:b + 1])
+        _, ref = hca_attend(case["qb"][b:b + 1], "bf16", sub(case["comp"]), m, sub(case["win"]),
+                            c["n_win"], g["pos"][b:b + 1], None, 512 ** -0.5, "bf16")
+        P.check_out(out[b:b + 1], ref, what=f"row {b}")
+
+
 def test_hca_decode_full_size_sampled_rows(lib):
     c = synth.WORKLOADS[3]
     print(f"workload 3: HCA decode B={c['B']} ctx={c['ctx']}", flush=True)
