@@ -18,13 +18,18 @@ For a query at absolute position p, head h:
   out_h = sum_e exp(l_e - M) v_e / (sum_e exp(l_e - M) + exp(z_h - M))
   empty E and no sink -> out_h = 0.
 Queries are decoded from bf16 (or taken as fp32); the output is rounded to bf16
-(or fp32).
+(or fp32).  With `nr` (dict gamma, eps, inv_freq; [Notes §9] query RMSNorm and
+partial RoPE, see normrope.py) each query head is RMS-normalised, its last
+2 * len(inv_freq) dims rotated by the query position and the result rounded to
+bf16 (the precision the attention multiplies in), and the output's same dims
+are rotated back by the query position before the final rounding.
 """
 
 import numpy as np
 
 from .codecs import bf16_decode, bf16_encode, f32, kv_decode_rows
 from .indexer import n_visible
+from .normrope import rms_norm, rope
 
 
 def window_positions(p, n_win):
@@ -72,10 +77,25 @@ def _entries(comp, win, b, p, rows_comp, n_win):
     return np.concatenate(parts, axis=0) if parts else np.zeros((0, D))
 
 
-def csa_attend(q, q_fmt, comp, topk, win, n_win, pos, sink, sm_scale, out_fmt):
+def _prep_q(qd, pos, nr):
+    """[Notes §9] query RMSNorm + partial RoPE, rounded to bf16 (see module doc)."""
+    if nr is None:
+        return qd
+    pos = np.asarray(pos, np.int64)
+    qn = rope(rms_norm(qd, nr["gamma"], nr["eps"]), pos[:, :, None], nr["inv_freq"])
+    return bf16_decode(bf16_encode(f32(qn)))
+
+
+def _post_out(out, pos, nr):
+    if nr is None:
+        return out
+    return rope(out, np.asarray(pos, np.int64)[:, :, None], nr["inv_freq"], sign=-1)
+
+
+def csa_attend(q, q_fmt, comp, topk, win, n_win, pos, sink, sm_scale, out_fmt, nr=None):
     """q [B][Q][H][D] (bf16 bits or f32), topk int [B][Q][k] (ids outside
     [0, cap) are skipped), pos int [B][Q], sink None | [H]."""
-    qd = _decode_q(q, q_fmt)
+    qd = _prep_q(_decode_q(q, q_fmt), pos, nr)
     B, Q, H, D = qd.shape
     out = np.zeros((B, Q, H, D))
     sk = None if sink is None else np.asarray(sink, np.float64)
@@ -85,11 +105,12 @@ def csa_attend(q, q_fmt, comp, topk, win, n_win, pos, sink, sm_scale, out_fmt):
             ids = ids[(ids >= 0) & (ids < comp.cap)]
             V = _entries(comp, win, b, int(pos[b][t]), ids, n_win)
             out[b, t] = _attend_one(qd[b, t], V, sm_scale, sk)
+    out = _post_out(out, pos, nr)
     return _round_out(out, out_fmt), out
 
 
-def hca_attend(q, q_fmt, comp, m, win, n_win, pos, sink, sm_scale, out_fmt):
-    qd = _decode_q(q, q_fmt)
+def hca_attend(q, q_fmt, comp, m, win, n_win, pos, sink, sm_scale, out_fmt, nr=None):
+    qd = _prep_q(_decode_q(q, q_fmt), pos, nr)
     B, Q, H, D = qd.shape
     out = np.zeros((B, Q, H, D))
     sk = None if sink is None else np.asarray(sink, np.float64)
@@ -99,4 +120,5 @@ def hca_attend(q, q_fmt, comp, m, win, n_win, pos, sink, sm_scale, out_fmt):
             ids = np.arange(n_visible(p, m, comp.cap), dtype=np.int64)
             V = _entries(comp, win, b, p, ids, n_win)
             out[b, t] = _attend_one(qd[b, t], V, sm_scale, sk)
+    out = _post_out(out, pos, nr)
     return _round_out(out, out_fmt), out

@@ -22,12 +22,17 @@ Inputs of one call cover tokens [t0, t0+T) (t0 and T multiples of m):
   kv_prev, gate_prev [B][T][d]  rows = tokens t0-m .. t0+T-m-1 (stream a), or None
   pos_bias           [slots][d] (slots = 2m with overlap, m without), or None = 0
   gate None means all-zero gate logits.
+With `nr` (dict gamma, eps, inv_freq; [Notes §9] KV entry RMSNorm and
+partial RoPE, see normrope.py) each pooled fp32 row is RMS-normalised and its
+last 2 * len(inv_freq) dims rotated by the entry's position (its block's last
+token), then rounded to fp32 again.
 Output: float64 [B][T/m][d], rounded to fp32 -- compressed entries t0/m ...
 """
 
 import numpy as np
 
 from .codecs import f32
+from .normrope import entry_positions, rms_norm, rope
 
 
 def _softmax_rows(logits):
@@ -37,7 +42,18 @@ def _softmax_rows(logits):
     return e / np.sum(e, axis=-2, keepdims=True)
 
 
-def compress(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, m, t0):
+def compress(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, m, t0, nr=None):
+    y = _pool(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, m, t0)
+    if nr is None:
+        return y
+    nb = y.shape[1]
+    blocks = t0 // m + np.arange(nb)
+    y = rope(rms_norm(y, nr["gamma"], nr["eps"]), entry_positions(blocks, m)[None, :],
+             nr["inv_freq"])
+    return f32(y).astype(np.float64)
+
+
+def _pool(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, m, t0):
     kv_cur = np.asarray(kv_cur, dtype=np.float64)
     B, T, d = kv_cur.shape
     assert T % m == 0 and t0 % m == 0
