@@ -277,6 +277,28 @@ def bench_production(v4, torch, reps, ws, cc, ch, n=8):
     return res
 
 
+def bench_norm_rope(v4, torch, reps, ws, cc, ch, n=8):
+    """The attend calls with the query RMSNorm + partial RoPE and the output's
+    rotation back ([Notes §9], the _nr variants) beside the plain calls, on the
+    benchmark's shapes (per-call times over all replicas)."""
+    D, sc = 512, 512 ** -0.5
+    g = torch.Generator(device="cuda").manual_seed(7)
+    gamma = 0.5 + torch.rand(D, device="cuda", generator=g)
+    inv = (10000.0 ** (-2.0 * torch.arange(32, dtype=torch.float64) / 64)).float().cuda()
+    nr = v4.NormRope(gamma, inv, 1e-6)
+    wsc = torch.empty(v4.v4attn_workspace_bytes(v4.OP_CSA_ATTEND_NR, cc["B"], 1, 64, D, 0, cc["k"],
+                                                cc["n_win"]), dtype=torch.uint8, device="cuda")
+    wsh = torch.empty(v4.v4attn_workspace_bytes(v4.OP_HCA_ATTEND_NR, ch["B"], 1, 64, D,
+                                                ch["ctx"] // ch["m"], ch["m"], ch["n_win"]),
+                      dtype=torch.uint8, device="cuda")
+    f_c = [(lambda r=r: v4.v4attn_csa_attend_nr(r.c_q, r.c_comp, r.c_topk, r.c_win, cc["n_win"], r.c_pos,
+                                                None, sc, nr, out=r.c_out, ws=wsc)) for r in reps]
+    f_h = [(lambda r=r: v4.v4attn_hca_attend_nr(r.h_q, r.h_comp, ch["m"], r.h_win, ch["n_win"], r.h_pos,
+                                                None, sc, nr, out=r.h_out, ws=wsh)) for r in reps]
+    t_c, t_h = graph_time(torch, f_c, n), graph_time(torch, f_h, n)
+    return {"csa_attend_nr_us": round(t_c * 1e6, 3), "hca_attend_nr_us": round(t_h * 1e6, 3)}
+
+
 # ---------------------------------------------------------------- prefill chunk
 
 PREFILL_WID = 5
@@ -679,6 +701,10 @@ def main():
     }
     log("production shapes ...")
     result["production_shapes"] = bench_production(v4, torch, reps, ws, cc, ch)
+    log("norm + RoPE variants ...")
+    result["norm_rope"] = bench_norm_rope(v4, torch, reps, ws, cc, ch)
+    result["norm_rope"]["csa_attend_us"] = round(t_csa_att * 1e6, 3)
+    result["norm_rope"]["hca_attend_us"] = round(t_hca_call * 1e6, 3)
     if not args.no_prefill:
         del csa_layer, hca_layer, per_call_g, calls, reps, ws
         torch.cuda.empty_cache()

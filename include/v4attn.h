@@ -136,6 +136,43 @@ v4a_status v4attn_compress(const void *kv_cur, const void *gate_cur,
                            void *stream);
 
 /*
+ * Query / KV-entry RMSNorm and partial RoPE ([Notes §9]: every query head and
+ * every compressed KV entry is RMS-normalised before core attention; RoPE acts
+ * on the last 64 dims of the query, of the KV entry and of the core-attention
+ * output, which is rotated back by the query's position since an entry is
+ * both key and value).
+ *   RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma over the D dims of a head
+ *   or an entry.  RoPE rotates adjacent pairs (x[2i], x[2i+1]) of the last
+ *   d_rope dims by a = fl32(fl32(pos) * inv_freq[i]) (one fp32 product):
+ *   (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a).
+ * Positions: a query's is pos[b][j]; a compressed entry's the last token of
+ * its block (i * m + m - 1, the first position that sees it); a window
+ * token's (compressed with m = 1) its own index.
+ */
+typedef struct {
+  const float *gamma;     /* device f32 [D] RMSNorm weight, or NULL: no RMSNorm   */
+  const float *inv_freq;  /* device f32 [d_rope / 2] RoPE inverse frequencies, or
+                             NULL: no RoPE                                        */
+  float eps;              /* RMSNorm epsilon, >= 0                                */
+  int32_t _pad;
+} v4a_norm_rope;
+
+/*
+ * v4attn_compress_nr -- v4attn_compress with the KV-entry RMSNorm and RoPE
+ * (v4a_norm_rope, host struct holding device pointers) applied to every pooled
+ * entry, in fp32, before it is stored or quantised (the FP8 scale is taken
+ * after them).  KV outputs only (out_kind V4A_OUT_KV, d_nope even, d_rope
+ * even); nr NULL behaves as v4attn_compress.  Errors as v4attn_compress, plus
+ * V4A_ERR_UNSUPPORTED for indexer-key outputs and V4A_ERR_INVALID for eps < 0.
+ */
+v4a_status v4attn_compress_nr(const void *kv_cur, const void *gate_cur,
+                              const void *kv_prev, const void *gate_prev,
+                              const float *pos_bias, int32_t in_dtype,
+                              int32_t B, int32_t T, int32_t d, int32_t m,
+                              int64_t t0, int32_t out_kind, const void *out,
+                              const v4a_norm_rope *nr, void *stream);
+
+/*
  * v4attn_index_topk -- lightning indexer + top-k selector ([Notes §7]:
  * I_{t,s} = sum_h w_{t,h} ReLU(q_{t,h} . K_s), then Top-k over s).
  * For each query (b, j) at position pos[b][j], scores every visible block
@@ -216,17 +253,44 @@ v4a_status v4attn_hca_attend(const void *q, int32_t q_dtype, const v4a_kv *comp,
                              void *out, int32_t out_dtype,
                              void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * v4attn_csa_attend_nr / v4attn_hca_attend_nr -- the attend calls with the
+ * query RMSNorm and RoPE (v4a_norm_rope; the query's own position) applied
+ * before attention, and the output's last d_rope dims rotated back by the
+ * query position ([Notes §9]).  The normalised, rotated query is rounded to
+ * bf16 (the attention's operand precision) in the workspace, sized by
+ * v4attn_workspace_bytes(V4A_OP_CSA_ATTEND_NR resp. V4A_OP_HCA_ATTEND_NR, ...).
+ * The cache entries are expected to carry their own RMSNorm and RoPE
+ * (v4attn_compress_nr).  FP8 entries only (V4A_KV_FP8_BF16ROPE); nr NULL
+ * behaves as the plain call.  Errors as the plain calls, plus
+ * V4A_ERR_UNSUPPORTED for fp32 entries and V4A_ERR_INVALID for eps < 0.
+ */
+v4a_status v4attn_csa_attend_nr(const void *q, int32_t q_dtype, const v4a_kv *comp,
+                                const int32_t *topk, int32_t k, const v4a_kv *win,
+                                int32_t n_win, const int64_t *pos, const float *sink,
+                                float sm_scale, int32_t B, int32_t Q, int32_t H,
+                                void *out, int32_t out_dtype, const v4a_norm_rope *nr,
+                                void *ws, size_t ws_bytes, void *stream);
+v4a_status v4attn_hca_attend_nr(const void *q, int32_t q_dtype, const v4a_kv *comp,
+                                int32_t m, const v4a_kv *win, int32_t n_win,
+                                const int64_t *pos, const float *sink, float sm_scale,
+                                int32_t B, int32_t Q, int32_t H,
+                                void *out, int32_t out_dtype, const v4a_norm_rope *nr,
+                                void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------- helpers */
 #define V4A_OP_INDEX_TOPK 1
 #define V4A_OP_CSA_ATTEND 2
 #define V4A_OP_HCA_ATTEND 3
+#define V4A_OP_CSA_ATTEND_NR 4   /* the _nr variants: + the normalised queries */
+#define V4A_OP_HCA_ATTEND_NR 5
 
 /*
  * Workspace bytes a call needs (0 = none).  Arguments that do not apply to
  * `op` are ignored:
  *   INDEX_TOPK: B, Q, H (= H_I), d (= key dim), cap (= keys->cap), k
- *   CSA_ATTEND: B, Q, H, d (= D), cap (ignored), k, n_win
- *   HCA_ATTEND: B, Q, H, d (= D), cap (= comp->cap), k (= m), n_win
+ *   CSA_ATTEND(_NR): B, Q, H, d (= D), cap (ignored), k, n_win
+ *   HCA_ATTEND(_NR): B, Q, H, d (= D), cap (= comp->cap), k (= m), n_win
  * Returns (size_t)-1 for an invalid combination.
  */
 size_t v4attn_workspace_bytes(int32_t op, int32_t B, int32_t Q, int32_t H,
@@ -240,7 +304,7 @@ int32_t v4attn_last_hip_error(void);
 
 /*
  * Kernel timing (measurement helper).  The calling thread's next call of
- * v4attn_index_topk(_bf16), v4attn_csa_attend or v4attn_hca_attend records `start`
+ * v4attn_index_topk(_bf16), v4attn_csa_attend(_nr) or v4attn_hca_attend(_nr) records `start`
  * and `stop` (hipEvent_t handles created by the caller) on the call's stream
  * immediately before and after its dominant kernel -- the index scan, resp.
  * the attention kernel (not the split merge) -- so hipEventElapsedTime gives

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     F32, BF16, KV_FP8_BF16ROPE, IDX_MXFP4, OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND,
     KVCache, IdxCache, V4AttnError, load, library_path,
     v4attn_compress, v4attn_index_topk, v4attn_index_topk_bf16, v4attn_csa_attend,
-    v4attn_hca_attend,
+    v4attn_hca_attend, NormRope, OP_CSA_ATTEND_NR, OP_HCA_ATTEND_NR, v4attn_compress_nr,
+    v4attn_csa_attend_nr, v4attn_hca_attend_nr,
     v4attn_workspace_bytes, v4attn_status_str, v4attn_time_next_kernel,
 )

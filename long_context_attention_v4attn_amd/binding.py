@@ -15,6 +15,7 @@ import torch
 F32, BF16, KV_FP8_BF16ROPE, IDX_MXFP4 = 0, 1, 2, 3
 OUT_KV, OUT_IDX = 0, 1
 OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND = 1, 2, 3
+OP_CSA_ATTEND_NR, OP_HCA_ATTEND_NR = 4, 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -33,6 +34,24 @@ class _KV(ctypes.Structure):
                 ("d_rope", ctypes.c_int32), ("_pad", ctypes.c_int32),
                 ("cap", ctypes.c_int64), ("nope", ctypes.c_void_p),
                 ("rope", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class _NormRope(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_void_p), ("inv_freq", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("_pad", ctypes.c_int32)]
+
+
+@dataclass
+class NormRope:
+    """[Notes §9] query / KV-entry RMSNorm and partial RoPE: gamma f32 [D]
+    (None: no RMSNorm), inv_freq f32 [d_rope / 2] (None: no RoPE), eps."""
+    gamma: object = None
+    inv_freq: object = None
+    eps: float = 1e-6
+
+    def c_struct(self):
+        _need_cuda(self.gamma, self.inv_freq)
+        return _NormRope(_ptr(self.gamma), _ptr(self.inv_freq), float(self.eps), 0)
 
 
 class _Idx(ctypes.Structure):
@@ -54,6 +73,12 @@ _SIGS = {
                                       _P]),
     "v4attn_csa_attend": (_I32, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32, _I32,
                                  _P, _I32, _P, _SZ, _P]),
+    "v4attn_csa_attend_nr": (_I32, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32, _I32,
+                                    _P, _I32, _P, _P, _SZ, _P]),
+    "v4attn_hca_attend_nr": (_I32, [_P, _I32, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32, _I32,
+                                    _P, _I32, _P, _P, _SZ, _P]),
+    "v4attn_compress_nr": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I64, _I32, _P,
+                                  _P, _P]),
     "v4attn_hca_attend": (_I32, [_P, _I32, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32, _I32,
                                  _P, _I32, _P, _SZ, _P]),
     "v4attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I64, _I32, _I32]),
@@ -209,6 +234,21 @@ def v4attn_compress(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, m, t0, out, 
     return out
 
 
+def v4attn_compress_nr(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, m, t0, out, nr,
+                       stream=None):
+    """v4attn_compress with the KV-entry RMSNorm and RoPE of `nr` (NormRope)."""
+    lib = load()
+    _need_cuda(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias)
+    B, T, d = kv_cur.shape
+    kind = OUT_KV if isinstance(out, KVCache) else OUT_IDX
+    st, ns = out.c_struct(), nr.c_struct()
+    s = lib.v4attn_compress_nr(_ptr(kv_cur), _ptr(gate_cur), _ptr(kv_prev), _ptr(gate_prev),
+                               _ptr(pos_bias), _dtype_code(kv_cur), B, T, d, m, int(t0), kind,
+                               ctypes.byref(st), ctypes.byref(ns), _stream(stream))
+    _check(s, "v4attn_compress_nr")
+    return out
+
+
 def _index_topk(name, q_idx, w, keys, pos, m, k, topk, ws, stream):
     lib = load()
     _need_cuda(q_idx, w, pos)
@@ -269,4 +309,43 @@ def v4attn_hca_attend(q, comp, m, win, n_win, pos, sink, sm_scale, out=None,
                               n_win, _ptr(pos), _ptr(sink), float(sm_scale), B, Q, H,
                               _ptr(out), _dtype_code(out), _ptr(ws), wsb, _stream(stream))
     _check(s, "v4attn_hca_attend")
+    return out
+
+
+def v4attn_csa_attend_nr(q, comp, topk, win, n_win, pos, sink, sm_scale, nr, out=None,
+                         out_dtype=torch.bfloat16, ws=None, stream=None):
+    """v4attn_csa_attend with the query RMSNorm + RoPE and the output's
+    rotation back of `nr` (NormRope)."""
+    lib = load()
+    _need_cuda(q, topk, pos, sink)
+    B, Q, H, D = q.shape
+    k = topk.shape[-1]
+    out = _out(q, out, out_dtype)
+    nbytes = v4attn_workspace_bytes(OP_CSA_ATTEND_NR, B, Q, H, D, comp.cap, k, n_win)
+    ws, wsb = _workspace(ws, nbytes, q.device)
+    cs, wst, ns = comp.c_struct(), win.c_struct(), nr.c_struct()
+    s = lib.v4attn_csa_attend_nr(_ptr(q), _dtype_code(q), ctypes.byref(cs), _ptr(topk), k,
+                                 ctypes.byref(wst), n_win, _ptr(pos), _ptr(sink), float(sm_scale),
+                                 B, Q, H, _ptr(out), _dtype_code(out), ctypes.byref(ns), _ptr(ws),
+                                 wsb, _stream(stream))
+    _check(s, "v4attn_csa_attend_nr")
+    return out
+
+
+def v4attn_hca_attend_nr(q, comp, m, win, n_win, pos, sink, sm_scale, nr, out=None,
+                         out_dtype=torch.bfloat16, ws=None, stream=None):
+    """v4attn_hca_attend with the query RMSNorm + RoPE and the output's
+    rotation back of `nr` (NormRope)."""
+    lib = load()
+    _need_cuda(q, pos, sink)
+    B, Q, H, D = q.shape
+    out = _out(q, out, out_dtype)
+    nbytes = v4attn_workspace_bytes(OP_HCA_ATTEND_NR, B, Q, H, D, comp.cap, m, n_win)
+    ws, wsb = _workspace(ws, nbytes, q.device)
+    cs, wst, ns = comp.c_struct(), win.c_struct(), nr.c_struct()
+    s = lib.v4attn_hca_attend_nr(_ptr(q), _dtype_code(q), ctypes.byref(cs), m, ctypes.byref(wst),
+                                 n_win, _ptr(pos), _ptr(sink), float(sm_scale), B, Q, H,
+                                 _ptr(out), _dtype_code(out), ctypes.byref(ns), _ptr(ws), wsb,
+                                 _stream(stream))
+    _check(s, "v4attn_hca_attend_nr")
     return out

@@ -90,27 +90,53 @@ void fill_attend(AttendArgs& a, const void* q, int32_t q_dtype, const v4a_kv* co
   a.fp8 = comp->fmt == V4A_KV_FP8_BF16ROPE;
 }
 
+// The normalised, rotated queries of the _nr calls: bf16 [R][H][D] after the
+// attention's own workspace regions.
+size_t qprep_bytes(const AttendArgs& a) {
+  return ((size_t)a.B * a.Q * a.H * (a.d_nope + a.d_rope) * 2 + 255) & ~(size_t)255;
+}
+
 v4a_status run_attend(AttendArgs& a, int64_t n_entries_max, void* ws, size_t ws_bytes,
-                      void* stream) {
+                      void* stream, const v4a_norm_rope* nr = nullptr) {
   attend_plan(a, n_entries_max);
   size_t need = attend_workspace_bytes(a);
+  const size_t base = need;
+  if (nr) need += qprep_bytes(a);
   if (need > 0) {
     if (!ws || ws_bytes < need) return V4A_ERR_WORKSPACE;
     attend_carve(a, ws);
   }
+  if (nr) {
+    a.q_in = a.q;
+    a.nr_gamma = nr->gamma;
+    a.nr_eps = nr->eps;
+    a.nr_inv = a.d_rope > 0 ? nr->inv_freq : nullptr;
+    a.q = (char*)ws + base;
+  }
   KernelEvents ev;
   return hip_status(launch_attend(a, (hipStream_t)stream, take_events(&ev)));
+}
+
+// Extra checks of the _nr attend calls.
+v4a_status check_nr(const v4a_kv* comp, const v4a_norm_rope* nr) {
+  if (!nr) return V4A_OK;
+  if (!(nr->eps >= 0.0f)) return V4A_ERR_INVALID;
+  if (comp->fmt != V4A_KV_FP8_BF16ROPE) return V4A_ERR_UNSUPPORTED;
+  return V4A_OK;
 }
 
 }  // namespace
 
 extern "C" {
 
-v4a_status v4attn_compress(const void* kv_cur, const void* gate_cur, const void* kv_prev,
-                           const void* gate_prev, const float* pos_bias, int32_t in_dtype,
-                           int32_t B, int32_t T, int32_t d, int32_t m, int64_t t0,
-                           int32_t out_kind, const void* out, void* stream) {
+static v4a_status compress_impl(const void* kv_cur, const void* gate_cur, const void* kv_prev,
+                                const void* gate_prev, const float* pos_bias, int32_t in_dtype,
+                                int32_t B, int32_t T, int32_t d, int32_t m, int64_t t0,
+                                int32_t out_kind, const void* out, const v4a_norm_rope* nr,
+                                void* stream) {
   if (!kv_cur || !out || B < 0 || T < 0 || d < 1 || t0 < 0) return V4A_ERR_INVALID;
+  if (nr && !(nr->eps >= 0.0f)) return V4A_ERR_INVALID;
+  if (nr && out_kind != V4A_OUT_KV) return V4A_ERR_UNSUPPORTED;
   if (in_dtype != V4A_F32 && in_dtype != V4A_BF16) return V4A_ERR_INVALID;
   if (!is_pow2_le(m, 128)) return V4A_ERR_UNSUPPORTED;
   if (T % m != 0 || t0 % m != 0) return V4A_ERR_INVALID;
@@ -140,6 +166,12 @@ v4a_status v4attn_compress(const void* kv_cur, const void* gate_cur, const void*
     a.o_a = kv->nope;
     a.o_b = kv->rope;
     a.o_scale = kv->scale;
+    if (nr) {
+      if (kv->d_nope % 2 != 0 || kv->d_rope % 2 != 0) return V4A_ERR_UNSUPPORTED;
+      a.nr_gamma = nr->gamma;
+      a.nr_inv = kv->d_rope > 0 ? nr->inv_freq : nullptr;
+      a.nr_eps = nr->eps;
+    }
   } else if (out_kind == V4A_OUT_IDX) {
     const v4a_idx* ix = (const v4a_idx*)out;
     if (!ix->codes || ix->cap < 1 || ix->d != d) return V4A_ERR_INVALID;
@@ -158,6 +190,23 @@ v4a_status v4attn_compress(const void* kv_cur, const void* gate_cur, const void*
   }
   if (B == 0 || T == 0) return V4A_OK;
   return hip_status(launch_compress(a, (hipStream_t)stream));
+}
+
+v4a_status v4attn_compress(const void* kv_cur, const void* gate_cur, const void* kv_prev,
+                           const void* gate_prev, const float* pos_bias, int32_t in_dtype,
+                           int32_t B, int32_t T, int32_t d, int32_t m, int64_t t0,
+                           int32_t out_kind, const void* out, void* stream) {
+  return compress_impl(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, in_dtype, B, T, d, m, t0,
+                       out_kind, out, nullptr, stream);
+}
+
+v4a_status v4attn_compress_nr(const void* kv_cur, const void* gate_cur, const void* kv_prev,
+                              const void* gate_prev, const float* pos_bias, int32_t in_dtype,
+                              int32_t B, int32_t T, int32_t d, int32_t m, int64_t t0,
+                              int32_t out_kind, const void* out, const v4a_norm_rope* nr,
+                              void* stream) {
+  return compress_impl(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, in_dtype, B, T, d, m, t0,
+                       out_kind, out, nr, stream);
 }
 
 static v4a_status index_topk(const void* q_idx, int32_t q_dtype, const float* w,
@@ -218,13 +267,14 @@ v4a_status v4attn_index_topk_bf16(const void* q_idx, int32_t q_dtype, const floa
   return index_topk(q_idx, q_dtype, w, keys, pos, B, Q, H_I, m, k, topk, ws, ws_bytes, stream, 1);
 }
 
-v4a_status v4attn_csa_attend(const void* q, int32_t q_dtype, const v4a_kv* comp,
-                             const int32_t* topk, int32_t k, const v4a_kv* win, int32_t n_win,
-                             const int64_t* pos, const float* sink, float sm_scale, int32_t B,
-                             int32_t Q, int32_t H, void* out, int32_t out_dtype, void* ws,
-                             size_t ws_bytes, void* stream) {
+v4a_status v4attn_csa_attend_nr(const void* q, int32_t q_dtype, const v4a_kv* comp,
+                                const int32_t* topk, int32_t k, const v4a_kv* win, int32_t n_win,
+                                const int64_t* pos, const float* sink, float sm_scale, int32_t B,
+                                int32_t Q, int32_t H, void* out, int32_t out_dtype,
+                                const v4a_norm_rope* nr, void* ws, size_t ws_bytes, void* stream) {
   v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype);
   if (s != V4A_OK) return s;
+  if ((s = check_nr(comp, nr)) != V4A_OK) return s;
   if (k < 0 || (k > 0 && !topk)) return V4A_ERR_INVALID;
   AttendArgs a;
   fill_attend(a, q, q_dtype, comp, win, n_win, pos, sink, sm_scale, B, Q, H, out, out_dtype);
@@ -233,16 +283,26 @@ v4a_status v4attn_csa_attend(const void* q, int32_t q_dtype, const v4a_kv* comp,
   a.k = k;
   a.m = 1;
   if (B == 0 || Q == 0) return V4A_OK;
-  return run_attend(a, (int64_t)k + n_win, ws, ws_bytes, stream);
+  return run_attend(a, (int64_t)k + n_win, ws, ws_bytes, stream, nr);
 }
 
-v4a_status v4attn_hca_attend(const void* q, int32_t q_dtype, const v4a_kv* comp, int32_t m,
-                             const v4a_kv* win, int32_t n_win, const int64_t* pos,
-                             const float* sink, float sm_scale, int32_t B, int32_t Q, int32_t H,
-                             void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
-                             void* stream) {
+v4a_status v4attn_csa_attend(const void* q, int32_t q_dtype, const v4a_kv* comp,
+                             const int32_t* topk, int32_t k, const v4a_kv* win, int32_t n_win,
+                             const int64_t* pos, const float* sink, float sm_scale, int32_t B,
+                             int32_t Q, int32_t H, void* out, int32_t out_dtype, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return v4attn_csa_attend_nr(q, q_dtype, comp, topk, k, win, n_win, pos, sink, sm_scale, B, Q, H,
+                              out, out_dtype, nullptr, ws, ws_bytes, stream);
+}
+
+v4a_status v4attn_hca_attend_nr(const void* q, int32_t q_dtype, const v4a_kv* comp, int32_t m,
+                                const v4a_kv* win, int32_t n_win, const int64_t* pos,
+                                const float* sink, float sm_scale, int32_t B, int32_t Q, int32_t H,
+                                void* out, int32_t out_dtype, const v4a_norm_rope* nr, void* ws,
+                                size_t ws_bytes, void* stream) {
   v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype);
   if (s != V4A_OK) return s;
+  if ((s = check_nr(comp, nr)) != V4A_OK) return s;
   if (m < 1) return V4A_ERR_INVALID;
   AttendArgs a;
   fill_attend(a, q, q_dtype, comp, win, n_win, pos, sink, sm_scale, B, Q, H, out, out_dtype);
@@ -250,7 +310,16 @@ v4a_status v4attn_hca_attend(const void* q, int32_t q_dtype, const v4a_kv* comp,
   a.topk = nullptr;
   a.m = m;
   if (B == 0 || Q == 0) return V4A_OK;
-  return run_attend(a, comp->cap + n_win, ws, ws_bytes, stream);
+  return run_attend(a, comp->cap + n_win, ws, ws_bytes, stream, nr);
+}
+
+v4a_status v4attn_hca_attend(const void* q, int32_t q_dtype, const v4a_kv* comp, int32_t m,
+                             const v4a_kv* win, int32_t n_win, const int64_t* pos,
+                             const float* sink, float sm_scale, int32_t B, int32_t Q, int32_t H,
+                             void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                             void* stream) {
+  return v4attn_hca_attend_nr(q, q_dtype, comp, m, win, n_win, pos, sink, sm_scale, B, Q, H, out,
+                              out_dtype, nullptr, ws, ws_bytes, stream);
 }
 
 size_t v4attn_workspace_bytes(int32_t op, int32_t B, int32_t Q, int32_t H, int32_t d, int64_t cap,
@@ -260,6 +329,8 @@ size_t v4attn_workspace_bytes(int32_t op, int32_t B, int32_t Q, int32_t H, int32
     if (cap < 1) return (size_t)-1;
     return index_workspace_bytes(B, Q, H, d, cap, d == 128 && H % 16 == 0 ? 1 : 0);
   }
+  const bool nr = op == V4A_OP_CSA_ATTEND_NR || op == V4A_OP_HCA_ATTEND_NR;
+  if (nr) op = op == V4A_OP_CSA_ATTEND_NR ? V4A_OP_CSA_ATTEND : V4A_OP_HCA_ATTEND;
   if (op != V4A_OP_CSA_ATTEND && op != V4A_OP_HCA_ATTEND) return (size_t)-1;
   if (n_win < 0 || k < 0) return (size_t)-1;
   AttendArgs a;
@@ -272,7 +343,9 @@ size_t v4attn_workspace_bytes(int32_t op, int32_t B, int32_t Q, int32_t H, int32
   a.fp8 = 0;                      // fp32 partials: the larger of the two formats
   int64_t n = op == V4A_OP_CSA_ATTEND ? (int64_t)k + n_win : cap + n_win;
   attend_plan(a, n);
-  return attend_workspace_bytes(a);
+  // the plan of the fp32 partials bounds the FP8 one; the _nr calls carve
+  // their queries after the FP8 plan's regions, which this sum also covers
+  return attend_workspace_bytes(a) + (nr ? qprep_bytes(a) : 0);
 }
 
 const char* v4attn_status_str(v4a_status s) {

@@ -135,6 +135,21 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint8_t* p) {
   return o;
 }
 
+// [Notes §9] the output's RoPE dims rotated back by the query position:
+// four consecutive dims d0 .. d0+3 (d0 a multiple of 4, two adjacent pairs)
+// at RoPE offset r0 = d0 - d_nope >= 0, angle fl32(fl32(p) * inv[pair]).
+__device__ __forceinline__ void unrotate4(float* o, const float* inv, int r0, int64_t p) {
+  const float pf = (float)p;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    float sn, cs;
+    sincos_angle(pf * inv[(r0 >> 1) + j], &sn, &cs);
+    const float x0 = o[2 * j], x1 = o[2 * j + 1];
+    o[2 * j] = x0 * cs + x1 * sn;          // rotation by -angle
+    o[2 * j + 1] = x1 * cs - x0 * sn;
+  }
+}
+
 // Staging: the 8 threads t = 8e .. 8e+7 move entry e of the tile, so a thread
 // resolves one entry's row per tile.  Thread q = t & 7 moves the 16-byte
 // chunks q, 8 + q, 16 + q and 24 + q (q < 4) of the FP8 codes, or RoPE chunk
@@ -734,7 +749,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
       const int64_t ob = ((int64_t)row * a.H + hgrp * kHeads + ht * 16 + li) * D + g * 4;
 #pragma unroll
       for (int db = 0; db < 8; db++) {
-        const f32x4 o = acc[db][ht] * f;
+        f32x4 o = acc[db][ht] * f;
+        if (db == 7 && a.nr_inv) {
+          // the RoPE block: dims 448 + 16 wave + 4g .. +3
+          float ov[4] = {o[0], o[1], o[2], o[3]};
+          unrotate4(ov, a.nr_inv, 16 * wave + 4 * g, a.pos[row]);
+          o = (f32x4){ov[0], ov[1], ov[2], ov[3]};
+        }
         const int64_t oi = ob + pv_dim0(wave, db);
         if (a.out_bf16) {
           const float ov[4] = {o[0], o[1], o[2], o[3]};
@@ -972,6 +993,11 @@ __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
   float den = 0.f;
   float M = -INFINITY;
   const float z2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
+  // the output rotation's inputs, loaded with the rest (used when nr_inv is
+  // set and d0 is a RoPE dim; otherwise valid dummy addresses)
+  const bool rot = a.nr_inv != nullptr && d0 >= a.d_nope;
+  const f32x2 inv2 = *(const f32x2*)(rot ? a.nr_inv + ((d0 - a.d_nope) >> 1) : (const float*)a.pos);
+  const int64_t p_row = a.pos[row];
   if (a.n_split <= kMergePhases * kMergeRegs) {
     // every split of this phase in registers before the first wait: the
     // maxima and the partials come in one round trip
@@ -1047,13 +1073,70 @@ __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   const int64_t oi = ((int64_t)row * a.H + head) * D + d0;
-  if (a.out_bf16) {
-    const uint32_t lo = f32_to_bf16_bits(o[0] * inv) | (f32_to_bf16_bits(o[1] * inv) << 16);
-    const uint32_t hi = f32_to_bf16_bits(o[2] * inv) | (f32_to_bf16_bits(o[3] * inv) << 16);
-    __builtin_nontemporal_store((u32x2){lo, hi}, (u32x2*)((uint16_t*)a.out + oi));
-  } else {
-    *(f32x4*)((float*)a.out + oi) = (f32x4){o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+#pragma unroll
+  for (int i = 0; i < 4; i++) o[i] *= inv;
+  if (rot) {
+    const float inv[2] = {inv2[0], inv2[1]};
+    unrotate4(o, inv, 0, p_row);
   }
+  if (a.out_bf16) {
+    __builtin_nontemporal_store(pack4(o), (u32x2*)((uint16_t*)a.out + oi));
+  } else {
+    *(f32x4*)((float*)a.out + oi) = (f32x4){o[0], o[1], o[2], o[3]};
+  }
+}
+
+// ---------------------------------------------------------------- query RMSNorm + RoPE
+// [Notes §9] prologue of the _nr calls: every query head RMS-normalised over
+// its D = 512 dims (weight gamma), its last 64 dims rotated by the query
+// position, rounded to bf16 for the attention kernel.  One wave per (query,
+// head): lane l holds dims 8l .. 8l+7 (RoPE pairs stay inside a lane).
+__global__ void __launch_bounds__(256) k_qprep(AttendArgs a) {
+  const int D = kNope + kRope;
+  const int lane = threadIdx.x & 63;
+  const int64_t gh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // row * H + head
+  if (gh >= (int64_t)a.B * a.Q * a.H) return;
+  const int64_t row = gh / a.H;
+  // every load first (valid dummy addresses where a step is off), then the
+  // arithmetic: one memory round trip
+  const u32x4 raw = *(const u32x4*)((const uint16_t*)a.q_in + gh * D + 8 * lane);
+  const float* gsrc = a.nr_gamma ? a.nr_gamma + 8 * lane : (const float*)a.q_in;
+  const f32x4 g0 = *(const f32x4*)gsrc, g1 = *(const f32x4*)(gsrc + 4);
+  const bool rot = a.nr_inv != nullptr && 8 * lane >= kNope;
+  const f32x4 iv = *(const f32x4*)(rot ? a.nr_inv + ((8 * lane - kNope) >> 1) : (const float*)a.q_in);
+  const int64_t p_row = a.pos[row];
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t w = raw[i];
+    x[2 * i] = bf16_bits_to_f32(w & 0xFFFFu);
+    x[2 * i + 1] = bf16_bits_to_f32(w >> 16);
+  }
+  if (a.nr_gamma) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) ss += x[i] * x[i];
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)D + a.nr_eps);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      x[i] = x[i] * r * g0[i];
+      x[4 + i] = x[4 + i] * r * g1[i];
+    }
+  }
+  if (rot) {
+    const float pf = (float)p_row;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      float sn, cs;
+      sincos_angle(pf * iv[j], &sn, &cs);
+      const float x0 = x[2 * j], x1 = x[2 * j + 1];
+      x[2 * j] = x0 * cs - x1 * sn;
+      x[2 * j + 1] = x0 * sn + x1 * cs;
+    }
+  }
+  const u32x2 lo = pack4(x), hi = pack4(x + 4);
+  *(u32x4*)((uint16_t*)a.q + gh * D + 8 * lane) = (u32x4){lo[0], lo[1], hi[0], hi[1]};
 }
 
 // ---------------------------------------------------------------- plan / launch
@@ -1114,6 +1197,12 @@ size_t attend_f32_smem(const AttendArgs& a) {
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st, const KernelEvents* ev) {
   const int rows = a.B * a.Q;
   if (rows == 0) return hipSuccess;
+  if (a.fp8 && a.q_in) {
+    const int64_t heads = (int64_t)rows * a.H;
+    hipLaunchKernelGGL(k_qprep, dim3((unsigned)((heads + 3) / 4)), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (a.fp8) {
     const int64_t N = (int64_t)rows * a.n_split * ((a.H + kHeads - 1) / kHeads);
     const int64_t per = (N + 7) / 8;

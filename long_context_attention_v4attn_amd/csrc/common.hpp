@@ -112,6 +112,50 @@ __device__ __forceinline__ float load_as_f32(const void* p, int dtype_bf16, size
   return ((const float*)p)[i];
 }
 
+// ------------------------------------------------------------------ rotary angles
+
+// Sine and cosine of an fp32 angle a (any magnitude a RoPE angle reaches, well
+// below 2^40), evaluated in fp64 and rounded to fp32: Cody-Waite reduction
+// by pi/2 with the constant split in two doubles and FMA (r = a - k pi/2 to
+// ~1e-30 absolute for |k| < 2^40), then the Taylor series of sin and cos on
+// |r| <= pi/4 (terms through r^17 / r^16: truncation < 1e-18), then the
+// quadrant's swap and signs.  (fp64 runs at the fp32 VALU rate here; the
+// fp32 library routines take a slow path for large arguments.)
+__device__ __forceinline__ void sincos_angle(float a, float* s, float* c) {
+  constexpr double kTwoOverPi = 0.63661977236758134308;
+  constexpr double kPio2Hi = 1.5707963267948966192;         // nearest double to pi/2
+  constexpr double kPio2Lo = 6.123233995736766036e-17;       // pi/2 - kPio2Hi
+  const double x = (double)a;
+  const double kd = rint(x * kTwoOverPi);
+  double r = fma(-kd, kPio2Hi, x);
+  r = fma(-kd, kPio2Lo, r);
+  const double r2 = r * r;
+  // sin r = r (1 - r2/3! + r2^2/5! - ... + r2^8/17!), cos r = 1 - r2/2! + ... + r2^8/16!
+  double ps = 1.0 / 355687428096000.0;                       // 1/17!
+  ps = fma(ps, r2, -1.0 / 1307674368000.0);                  // 1/15!
+  ps = fma(ps, r2, 1.0 / 6227020800.0);                      // 1/13!
+  ps = fma(ps, r2, -1.0 / 39916800.0);                       // 1/11!
+  ps = fma(ps, r2, 1.0 / 362880.0);                          // 1/9!
+  ps = fma(ps, r2, -1.0 / 5040.0);                           // 1/7!
+  ps = fma(ps, r2, 1.0 / 120.0);                             // 1/5!
+  ps = fma(ps, r2, -1.0 / 6.0);                              // 1/3!
+  const double sr = fma(ps * r2, r, r);
+  double pc = 1.0 / 20922789888000.0;                        // 1/16!
+  pc = fma(pc, r2, -1.0 / 87178291200.0);                    // 1/14!
+  pc = fma(pc, r2, 1.0 / 479001600.0);                       // 1/12!
+  pc = fma(pc, r2, -1.0 / 3628800.0);                        // 1/10!
+  pc = fma(pc, r2, 1.0 / 40320.0);                           // 1/8!
+  pc = fma(pc, r2, -1.0 / 720.0);                            // 1/6!
+  pc = fma(pc, r2, 1.0 / 24.0);                              // 1/4!
+  pc = fma(pc, r2, -0.5);                                    // 1/2!
+  const double cr = fma(pc, r2, 1.0);
+  const int q = (int)((long long)kd & 3);
+  const double sv = (q == 0) ? sr : (q == 1) ? cr : (q == 2) ? -sr : -cr;
+  const double cv = (q == 0) ? cr : (q == 1) ? -sr : (q == 2) ? -cr : sr;
+  *s = (float)sv;
+  *c = (float)cv;
+}
+
 // Monotone map of fp32 to uint32: a < b (as floats) <=> key(a) < key(b).
 // -0.0 and +0.0 map to neighbouring keys (-0 below +0).
 __device__ __forceinline__ uint32_t order_key(float f) {

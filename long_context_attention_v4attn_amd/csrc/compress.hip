@@ -82,6 +82,44 @@ __global__ void __launch_bounds__(kCompThreads) k_compress(CompressArgs a) {
   }
 
   const int64_t orow = (int64_t)b * a.cap + (gblk % a.cap);
+  if (a.out_kind == 0 && (a.nr_gamma || a.nr_inv)) {
+    // [Notes §9] KV-entry RMSNorm over the d channels, then RoPE of the last
+    // d - d_nope channels at the entry's position (its block's last token):
+    // adjacent channels pair up, and since d_nope and 256 are even a pair is
+    // two adjacent lanes of one wave
+    if (a.nr_gamma) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kMaxChan; q++) ss += y[q] * y[q];   // y = 0 past d
+      ss = wave_sum(ss);
+      __syncthreads();                     // red is free
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+      __syncthreads();
+      ss = red[0];
+      for (int w = 1; w < kCompThreads / 64; w++) ss += red[w];
+      __syncthreads();                     // red is reused below
+      const float r = 1.0f / sqrtf(ss / (float)d + a.nr_eps);
+#pragma unroll
+      for (int q = 0; q < kMaxChan; q++) {
+        const int c = threadIdx.x + q * kCompThreads;
+        if (c < d) y[q] = y[q] * r * a.nr_gamma[c];
+      }
+    }
+    if (a.nr_inv) {
+      const float pf = (float)(gblk * m + m - 1);
+#pragma unroll
+      for (int q = 0; q < kMaxChan; q++) {
+        const int c = threadIdx.x + q * kCompThreads;
+        const float other = __shfl_xor(y[q], 1, 64);       // channel c ^ 1
+        if (c < d && c >= a.d_nope) {
+          const float ang = pf * a.nr_inv[(c - a.d_nope) >> 1];
+          float sn, cs;
+          sincos_angle(ang, &sn, &cs);
+          y[q] = ((c - a.d_nope) & 1) ? other * sn + y[q] * cs : y[q] * cs - other * sn;
+        }
+      }
+    }
+  }
   if (a.out_kind == 0) {
     const int dn = a.d_nope, dr = d - a.d_nope;
     if (a.out_fmt == 0) {

@@ -25,6 +25,10 @@ struct CompressArgs {
   void* o_a;                 // KV: nope (f32 | u8 e4m3);  keys: codes (f32 | u8 packed)
   void* o_b;                 // KV: rope (f32 | bf16);     keys: e8m0 scales
   float* o_scale;            // KV FP8: per-entry scale
+  // KV-entry RMSNorm / RoPE before the store (null: off)
+  const float* nr_gamma;     // [d]
+  const float* nr_inv;       // [d_rope / 2] inverse frequencies
+  float nr_eps;
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
 
@@ -99,6 +103,12 @@ struct AttendArgs {
   int part_bf16;             // split partials stored in bf16 (FP8 path) or fp32
   void* part_o;              // [R][n_split][H][D] O / l
   float* part_ml;            // [R][n_split][H][2] (max, denominator)
+  // query RMSNorm / RoPE (q_in non-null: a prologue kernel writes the bf16
+  // result to q) and the output's rotation back (nr_inv non-null)
+  const void* q_in;          // [R][H][D] bf16
+  const float* nr_gamma;     // [D] or null
+  const float* nr_inv;       // [d_rope / 2] or null
+  float nr_eps;
 };
 void attend_plan(AttendArgs& a, int64_t n_entries_max);
 size_t attend_workspace_bytes(const AttendArgs& a);

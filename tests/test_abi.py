@@ -113,6 +113,39 @@ def test_invalid_arguments_rejected_on_host(clib):
                                   1, 1, 64, FAKE, 1, None, 0, None) == -3
 
 
+class _NR(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_void_p), ("inv_freq", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("_pad", ctypes.c_int32)]
+
+
+def test_norm_rope_variants_rejected_on_host(clib):
+    from long_context_attention_v4attn_amd import binding as B
+    r = ctypes.byref
+    nr = _NR(0x4000, 0x5000, 1e-6, 0)
+    bad = _NR(0x4000, 0x5000, -1.0, 0)
+    kv = _KV(2, 448, 64, 0, 100, 0x1000, 0x2000, 0x3000)
+    kv32 = _KV(0, 448, 64, 0, 100, 0x1000, 0x2000, 0)
+    ix = _Idx(3, 128, 1000, 0x1000, 0x2000)
+    # compress: indexer keys take no norm/RoPE; negative eps
+    assert clib.v4attn_compress_nr(FAKE, None, None, None, None, 0, 1, 4, 128, 4, 0, 1, r(ix), r(nr),
+                                   None) == -2
+    assert clib.v4attn_compress_nr(FAKE, None, None, None, None, 0, 1, 4, 512, 4, 0, 0, r(kv), r(bad),
+                                   None) == -1
+    # attend: FP8 entries only; negative eps; the plain-call checks still apply
+    assert clib.v4attn_csa_attend_nr(FAKE, 1, r(kv32), FAKE, 8, r(kv32), 16, FAKE, None,
+                                     ctypes.c_float(0.1), 1, 1, 64, FAKE, 1, r(nr), FAKE, 1 << 30,
+                                     None) == -2
+    assert clib.v4attn_hca_attend_nr(FAKE, 1, r(kv), 128, r(kv), 16, FAKE, None, ctypes.c_float(0.1),
+                                     1, 1, 64, FAKE, 1, r(bad), FAKE, 1 << 30, None) == -1
+    assert clib.v4attn_hca_attend_nr(FAKE, 1, r(kv), 128, r(kv), 16, FAKE, None, ctypes.c_float(0.1),
+                                     1, 1, 24, FAKE, 1, r(nr), FAKE, 1 << 30, None) == -2
+    # the _nr workspace adds the bf16 queries
+    for op, op_nr in ((B.OP_CSA_ATTEND, B.OP_CSA_ATTEND_NR), (B.OP_HCA_ATTEND, B.OP_HCA_ATTEND_NR)):
+        a = B.v4attn_workspace_bytes(op, 4, 1, 64, 512, 8192, 2048, 128)
+        b = B.v4attn_workspace_bytes(op_nr, 4, 1, 64, 512, 8192, 2048, 128)
+        assert b >= a + 4 * 64 * 512 * 2
+
+
 def test_binding_refuses_host_tensors():
     import numpy as np
     import torch

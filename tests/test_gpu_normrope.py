@@ -1,0 +1,137 @@
+"""GPU parity of the query / KV-entry RMSNorm and partial RoPE variants
+([Notes §9]) against the oracle: v4attn_compress_nr (the pooled entries
+normalised and rotated at their blocks' positions, then stored or quantised)
+and v4attn_csa_attend_nr / v4attn_hca_attend_nr (the query normalised and
+rotated at its position, the output rotated back), at small and 1M-scale
+positions, through the direct and the split-merge epilogues."""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_v4attn_amd import synth
+from oracle import codecs as C
+from oracle.attend import csa_attend, hca_attend
+from oracle.compress import compress
+from oracle.normrope import default_inv_freq
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _nr(rng, D=512, d_rope=64):
+    gamma = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    inv = default_inv_freq(d_rope).astype(np.float32)
+    return dict(gamma=gamma.astype(np.float64), eps=1e-6, inv_freq=inv), gamma, inv
+
+
+def _nr_dev(lib, gamma, inv, eps=1e-6):
+    return lib.NormRope(P.dev(gamma), P.dev(inv), eps)
+
+
+@pytest.mark.parametrize("m,overlap,t0,fmt", [
+    (4, True, 0, "fp8"),
+    (128, False, 256, "fp8"),
+    (1, False, 5, "fp8"),                # window tokens: their own positions
+    (4, True, 1 << 20, "fp8"),           # positions near 1M (fp32 angle rule)
+    (4, False, 8, "f32"),
+])
+def test_compress_kv_norm_rope(lib, m, overlap, t0, fmt):
+    print(f"compress_nr m={m} overlap={overlap} t0={t0} fmt={fmt}", flush=True)
+    rng = np.random.default_rng(m + t0 % 977)
+    Bn, d, dn = 2, 512, 448
+    T = 3 * m if m > 1 else 37
+    g = synth.compress_inputs(3, Bn, T, d, m, overlap, t0)
+    nr, gamma, inv = _nr(rng)
+    y = compress(g["kv_cur"], g["gate_cur"], g["kv_prev"], g["gate_prev"], g["bias"], m, t0, nr=nr)
+    cap = T // m + 2
+    out = lib.KVCache.empty(Bn, cap, dn, d - dn, lib.KV_FP8_BF16ROPE if fmt == "fp8" else lib.F32)
+    lib.v4attn_compress_nr(P.dev(g["kv_cur"]), P.dev(g["gate_cur"]),
+                           None if g["kv_prev"] is None else P.dev(g["kv_prev"]),
+                           None if g["gate_prev"] is None else P.dev(g["gate_prev"]),
+                           P.dev(g["bias"]), m, t0, out, _nr_dev(lib, gamma, inv))
+    torch.cuda.synchronize()
+    back = P.kv_from_dev(out)
+    rows = (t0 // m + np.arange(T // m)) % cap
+    if fmt == "fp8":
+        sub = C.KV("fp8", dn, d - dn, back.nope[:, rows], back.rope[:, rows], back.scale[:, rows])
+        P.check_fp8_rows(sub, y, dn)
+    else:
+        full = np.concatenate([back.nope, back.rope], -1)[:, rows]
+        P.check_f32_rows(full, y)
+
+
+def _inputs(rng, Bn, Q, H, n_comp, R):
+    D = 512
+    comp = C.kv_encode((rng.standard_normal((Bn, n_comp, D)) * D ** -0.5 * 3).astype(np.float32), "fp8", 448)
+    win = C.kv_encode((rng.standard_normal((Bn, R, D)) * D ** -0.5 * 3).astype(np.float32), "fp8", 448)
+    q = rng.standard_normal((Bn, Q, H, D)).astype(np.float32)
+    return comp, win, q
+
+
+# (the CSA case with k = 16 and a 32-token window has one split: the attention
+# kernel's own epilogue rotates the output; the others go through the merge)
+@pytest.mark.parametrize("kind,H,n,far,n_win", [("hca", 64, 300, False, 128), ("hca", 32, 2100, True, 128),
+                                                ("csa", 64, 16, False, 32), ("csa", 64, 1000, True, 128)])
+def test_attend_norm_rope(lib, kind, H, n, far, n_win):
+    print(f"attend_nr {kind} H={H} n={n} far={far} n_win={n_win}", flush=True)
+    rng = np.random.default_rng(H + n)
+    Bn, Q, R = 2, 2, 160
+    comp, win, q = _inputs(rng, Bn, Q, H, n, R)
+    nr, gamma, inv = _nr(rng)
+    m = 4
+    base = (1 << 20) if far else 0
+    # the HCA call sees blocks s < n_vis(p); far positions use a larger m so
+    # that n_vis stays within the cache
+    mm = m if not far else (base // n + 1)
+    pos = np.array([[mm * n + 5, mm * (n // 3) + 1], [40 + base, mm * n - 1]], np.int64)
+    qb = C.bf16_encode(q)
+    scale = 512 ** -0.5
+    nd = _nr_dev(lib, gamma, inv)
+    qd = P.dev(qb.view(np.int16)).view(torch.bfloat16)
+    if kind == "hca":
+        _, ref = hca_attend(qb, "bf16", comp, mm, win, n_win, pos, None, scale, "bf16", nr=nr)
+        o = lib.v4attn_hca_attend_nr(qd, P.kv_to_dev(comp), mm, P.kv_to_dev(win), n_win, P.dev(pos),
+                                     None, scale, nd)
+    else:
+        k = min(n, 64)
+        topk = np.full((Bn, Q, k), -1, np.int64)
+        for b in range(Bn):
+            for t in range(Q):
+                topk[b, t] = np.sort(rng.choice(n, k, replace=False))
+        _, ref = csa_attend(qb, "bf16", comp, topk, win, n_win, pos, None, scale, "bf16", nr=nr)
+        o = lib.v4attn_csa_attend_nr(qd, P.kv_to_dev(comp), P.dev(topk.astype(np.int32)),
+                                     P.kv_to_dev(win), n_win, P.dev(pos), None, scale, nd)
+    torch.cuda.synchronize()
+    P.check_out(o, ref)
+
+
+def test_norm_rope_pipeline_end_to_end(lib):
+    # entries compressed with RMSNorm + RoPE, attended with the query's: the
+    # oracle runs the same two steps (its own encode of its own entries)
+    print("compress_nr -> hca_attend_nr", flush=True)
+    rng = np.random.default_rng(31)
+    Bn, m, T, d, dn, H = 1, 4, 512, 512, 448, 64
+    g = synth.compress_inputs(3, Bn, T, d, m, False, 0)
+    nr, gamma, inv = _nr(rng)
+    nd = _nr_dev(lib, gamma, inv)
+    comp = lib.KVCache.empty(Bn, T // m, dn, d - dn, lib.KV_FP8_BF16ROPE)
+    lib.v4attn_compress_nr(P.dev(g["kv_cur"]), P.dev(g["gate_cur"]), None, None, P.dev(g["bias"]), m, 0,
+                           comp, nd)
+    y = compress(g["kv_cur"], g["gate_cur"], None, None, g["bias"], m, 0, nr=nr)
+    # window: the last 128 raw tokens, rotated at their own positions (m = 1)
+    win = lib.KVCache.empty(Bn, 128, dn, d - dn, lib.KV_FP8_BF16ROPE)
+    lib.v4attn_compress_nr(P.dev(g["kv_cur"][:, T - 128:]), None, None, None, None, 1, T - 128, win, nd)
+    yw = compress(g["kv_cur"][:, T - 128:], None, None, None, None, 1, T - 128, nr=nr)
+    torch.cuda.synchronize()
+    ring = np.empty_like(yw)
+    ring[:, (np.arange(T - 128, T)) % 128] = yw
+    comp_o, win_o = C.kv_encode(y, "fp8", dn), C.kv_encode(ring, "fp8", dn)
+    q = rng.standard_normal((Bn, 1, H, d)).astype(np.float32)
+    qb = C.bf16_encode(q)
+    pos = np.array([[T - 1]], np.int64)
+    o = lib.v4attn_hca_attend_nr(P.dev(qb.view(np.int16)).view(torch.bfloat16), comp, m, win, 128,
+                                 P.dev(pos), None, d ** -0.5, nd)
+    torch.cuda.synchronize()
+    _, ref = hca_attend(qb, "bf16", comp_o, m, win_o, 128, pos, None, d ** -0.5, "bf16", nr=nr)
+    P.check_out(o, ref)
