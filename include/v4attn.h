@@ -278,6 +278,133 @@ v4a_status v4attn_hca_attend_nr(const void *q, int32_t q_dtype, const v4a_kv *co
                                 void *out, int32_t out_dtype, const v4a_norm_rope *nr,
                                 void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------- paged cache
+ * [Notes §11] KV cache table: the classical cache holds the compressed
+ * entries in blocks, each covering a span of raw tokens and holding the
+ * entries that span produces; the block size is a multiple of the least
+ * common multiple of the two compression ratios (4 and 128, so 128 tokens),
+ * so one layout serves both kinds of layer.  The state cache is a fixed-size
+ * region per sequence: the sliding-window entries and the uncompressed tail
+ * of the compressor block that is not full yet, updated as the position
+ * advances.
+ *
+ * Here a block of the classical cache is a page of `page_tokens` raw tokens;
+ * a layer of compression rate m keeps P = page_tokens / m entries per page.
+ * A paged cache is a pool of pages, and the v4a_kv / v4a_idx of a paged call
+ * describes the pool: its arrays have no batch axis, [cap][...] with cap =
+ * n_pages * P pool rows.  Logical entry r of sequence b (its compressed block
+ * r) is pool row table[b][r / P] * P + r % P, and a sequence holds at most
+ * max_pages * P entries: that logical capacity takes the place of `cap` in
+ * n_vis.  Page ids outside [0, n_pages) are clamped into it on the device, so
+ * no table content addresses memory outside the pool (such a page reads or
+ * writes the clamped page).  Top-k ids are logical block ids.  The window ring
+ * stays a per-sequence ring (state cache), as in the plain calls.
+ * Supported: page_tokens a power of two, 128 <= page_tokens <= 2^30, m <=
+ * page_tokens; n_pages * P and max_pages * P below 2^31; FP8 entries
+ * (V4A_KV_FP8_BF16ROPE) for attention, MXFP4 keys with P >= 128 for the
+ * indexer (fp32 caches are not paged).
+ */
+typedef struct {
+  const int32_t *table;   /* device int32 [B][max_pages]: pool page of each page */
+  int32_t max_pages;      /* table row length, >= 1                           */
+  int32_t page_tokens;    /* raw tokens per page                              */
+} v4a_pages;
+
+/*
+ * v4attn_compress_paged -- v4attn_compress (and, with nr non-NULL, its _nr
+ * form) writing block t0/m + j of sequence b to its pool row instead of a ring
+ * row; t0/m + T/m must not exceed max_pages * P (V4A_ERR_INVALID).
+ */
+v4a_status v4attn_compress_paged(const void *kv_cur, const void *gate_cur,
+                                 const void *kv_prev, const void *gate_prev,
+                                 const float *pos_bias, int32_t in_dtype,
+                                 int32_t B, int32_t T, int32_t d, int32_t m,
+                                 int64_t t0, int32_t out_kind, const void *out,
+                                 const v4a_pages *pages, const v4a_norm_rope *nr,
+                                 void *stream);
+
+/*
+ * Compressor tails of the state cache: per sequence a ring of `rows` raw
+ * token rows of each stream, token t at row t mod rows, device arrays
+ * [B][rows][d] in the call's in_dtype (the streams as in v4attn_compress;
+ * gate and previous-role rings only where those inputs exist).
+ */
+typedef struct {
+  void *kv_cur;
+  void *gate_cur;
+  void *kv_prev;
+  void *gate_prev;
+  int32_t rows;
+  int32_t _pad;
+} v4a_tail;
+
+/*
+ * v4attn_append -- the decode-time compressor step ([Notes §11] state cache):
+ * one new token per sequence.  For every b with p = pos[b] >= 0, the token's
+ * rows kv_cur[b], gate_cur[b], kv_prev[b], gate_prev[b] ([B][d] each, the
+ * streams of v4attn_compress; gates may be NULL = 0, kv_prev NULL = no
+ * overlap) are written to the tail rings at row p mod rows; if p + 1 is a
+ * multiple of m, the token completes block i = (p + 1) / m - 1, which is
+ * pooled exactly as v4attn_compress would pool it (current rows: tokens
+ * i*m .. p; previous-role rows: tokens (i-1)*m .. i*m - 1, none for block 0)
+ * and stored -- with nr, after the entry RMSNorm and RoPE -- at ring row
+ * i mod cap (pages NULL) or at its pool row (pages non-NULL; a block beyond
+ * the sequence's max_pages * P entries is not stored).  pos[b] < 0 leaves
+ * sequence b untouched.  The tails must hold the block's earlier tokens:
+ * rows >= 2m with overlap, >= m without; with m == 1 and no overlap the tail
+ * may be NULL (the token is the whole block: the window ring is filled so).
+ * Calls for one sequence must come in position order, and every position
+ * must be appended once (the tail rings hold what earlier calls wrote).
+ *
+ *   tail     host v4a_tail (device arrays inside), or NULL as above
+ *   pos      int64 [B]
+ *   out_kind, out, nr  as v4attn_compress_nr / _paged
+ * Errors: as v4attn_compress_paged; V4A_ERR_INVALID for a missing or short
+ * tail (or a gate ring missing where its gate input exists).
+ */
+v4a_status v4attn_append(const void *kv_cur, const void *gate_cur,
+                         const void *kv_prev, const void *gate_prev,
+                         const v4a_tail *tail, const int64_t *pos,
+                         const float *pos_bias, int32_t in_dtype,
+                         int32_t B, int32_t d, int32_t m,
+                         int32_t out_kind, const void *out,
+                         const v4a_pages *pages, const v4a_norm_rope *nr,
+                         void *stream);
+
+/*
+ * v4attn_index_topk_paged -- v4attn_index_topk over paged MXFP4 keys (keys
+ * describes the pool; P = page_tokens / m >= 128).  score_bf16 != 0 selects
+ * the BF16-score ranking of v4attn_index_topk_bf16.  Workspace: as
+ * V4A_OP_INDEX_TOPK with cap = max_pages * P.
+ */
+v4a_status v4attn_index_topk_paged(const void *q_idx, int32_t q_dtype, const float *w,
+                                   const v4a_idx *keys, const v4a_pages *pages,
+                                   const int64_t *pos, int32_t B, int32_t Q, int32_t H_I,
+                                   int32_t m, int32_t k, int32_t score_bf16, int32_t *topk,
+                                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * v4attn_csa_attend_paged / v4attn_hca_attend_paged -- the attend calls (and,
+ * with nr non-NULL, their _nr forms) over a paged compressed cache of
+ * compression rate m (comp describes the pool; FP8 entries).  CSA: top-k ids
+ * are logical block ids; ids outside [0, max_pages * P) are skipped.
+ * Workspace: as the plain (or _nr) op, with cap = max_pages * P for HCA.
+ */
+v4a_status v4attn_csa_attend_paged(const void *q, int32_t q_dtype, const v4a_kv *comp,
+                                   const v4a_pages *pages, int32_t m,
+                                   const int32_t *topk, int32_t k, const v4a_kv *win,
+                                   int32_t n_win, const int64_t *pos, const float *sink,
+                                   float sm_scale, int32_t B, int32_t Q, int32_t H,
+                                   void *out, int32_t out_dtype, const v4a_norm_rope *nr,
+                                   void *ws, size_t ws_bytes, void *stream);
+v4a_status v4attn_hca_attend_paged(const void *q, int32_t q_dtype, const v4a_kv *comp,
+                                   const v4a_pages *pages, int32_t m,
+                                   const v4a_kv *win, int32_t n_win, const int64_t *pos,
+                                   const float *sink, float sm_scale,
+                                   int32_t B, int32_t Q, int32_t H,
+                                   void *out, int32_t out_dtype, const v4a_norm_rope *nr,
+                                   void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------- helpers */
 #define V4A_OP_INDEX_TOPK 1
 #define V4A_OP_CSA_ATTEND 2

@@ -41,6 +41,17 @@ class _NormRope(ctypes.Structure):
                 ("eps", ctypes.c_float), ("_pad", ctypes.c_int32)]
 
 
+class _Pages(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+                ("page_tokens", ctypes.c_int32)]
+
+
+class _Tail(ctypes.Structure):
+    _fields_ = [("kv_cur", ctypes.c_void_p), ("gate_cur", ctypes.c_void_p),
+                ("kv_prev", ctypes.c_void_p), ("gate_prev", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("_pad", ctypes.c_int32)]
+
+
 @dataclass
 class NormRope:
     """[Notes §9] query / KV-entry RMSNorm and partial RoPE: gamma f32 [D]
@@ -81,6 +92,16 @@ _SIGS = {
                                   _P, _P]),
     "v4attn_hca_attend": (_I32, [_P, _I32, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32, _I32,
                                  _P, _I32, _P, _SZ, _P]),
+    "v4attn_compress_paged": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I64, _I32,
+                                     _P, _P, _P, _P]),
+    "v4attn_append": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
+                             _P]),
+    "v4attn_index_topk_paged": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                       _P, _P, _SZ, _P]),
+    "v4attn_csa_attend_paged": (_I32, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _I32, _P, _P, _F, _I32,
+                                       _I32, _I32, _P, _I32, _P, _P, _SZ, _P]),
+    "v4attn_hca_attend_paged": (_I32, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32,
+                                       _I32, _P, _I32, _P, _P, _SZ, _P]),
     "v4attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I64, _I32, _I32]),
     "v4attn_status_str": (ctypes.c_char_p, [_I32]),
     "v4attn_last_hip_error": (_I32, []),
@@ -348,4 +369,150 @@ def v4attn_hca_attend_nr(q, comp, m, win, n_win, pos, sink, sm_scale, nr, out=No
                                  _ptr(out), _dtype_code(out), ctypes.byref(ns), _ptr(ws), wsb,
                                  _stream(stream))
     _check(s, "v4attn_hca_attend_nr")
+    return out
+
+
+# ---------------------------------------------------------------- paged cache
+
+@dataclass
+class Pages:
+    """[Notes §11] block table of a paged cache: table int32 [B][max_pages]
+    (device) naming each sequence's pool pages, page_tokens raw tokens per
+    page.  A paged KVCache / IdxCache is the pool: batch axis 1, n_pages * P
+    rows, P = page_tokens / m."""
+    table: torch.Tensor
+    page_tokens: int
+
+    def entries_per_page(self, m):
+        return self.page_tokens // m
+
+    def logical_cap(self, m):
+        return self.table.shape[1] * self.entries_per_page(m)
+
+    def c_struct(self):
+        _need_cuda(self.table)
+        if self.table.dtype != torch.int32 or self.table.dim() != 2 or not self.table.is_contiguous():
+            raise V4AttnError("page table must be a contiguous int32 [B][max_pages] tensor")
+        return _Pages(self.table.data_ptr(), self.table.shape[1], int(self.page_tokens))
+
+
+@dataclass
+class Tail:
+    """Compressor tails of the state cache: rings [B][rows][d] of raw token
+    rows per stream (token t at row t mod rows), in the tokens' dtype."""
+    kv_cur: torch.Tensor
+    gate_cur: torch.Tensor = None
+    kv_prev: torch.Tensor = None
+    gate_prev: torch.Tensor = None
+
+    @staticmethod
+    def empty(B, rows, d, dtype, gates=True, overlap=False, device="cuda"):
+        z = lambda: torch.zeros(B, rows, d, dtype=dtype, device=device)
+        return Tail(z(), z() if gates else None, z() if overlap else None,
+                    z() if gates and overlap else None)
+
+    @property
+    def rows(self):
+        return self.kv_cur.shape[1]
+
+    def c_struct(self):
+        _need_cuda(self.kv_cur, self.gate_cur, self.kv_prev, self.gate_prev)
+        return _Tail(self.kv_cur.data_ptr(), *[0 if t is None else t.data_ptr()
+                                                 for t in (self.gate_cur, self.kv_prev,
+                                                           self.gate_prev)], self.rows, 0)
+
+
+def _byref(st):
+    return None if st is None else ctypes.byref(st)
+
+
+def v4attn_compress_paged(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, m, t0, out, pages,
+                          nr=None, stream=None):
+    """v4attn_compress (with nr: its _nr form) into the pool pages of `pages`."""
+    lib = load()
+    _need_cuda(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias)
+    B, T, d = kv_cur.shape
+    kind = OUT_KV if isinstance(out, KVCache) else OUT_IDX
+    st, ps = out.c_struct(), pages.c_struct()
+    ns = None if nr is None else nr.c_struct()
+    s = lib.v4attn_compress_paged(_ptr(kv_cur), _ptr(gate_cur), _ptr(kv_prev), _ptr(gate_prev),
+                                  _ptr(pos_bias), _dtype_code(kv_cur), B, T, d, m, int(t0), kind,
+                                  ctypes.byref(st), ctypes.byref(ps), _byref(ns), _stream(stream))
+    _check(s, "v4attn_compress_paged")
+    return out
+
+
+def v4attn_append(kv_cur, gate_cur, kv_prev, gate_prev, tail, pos, pos_bias, m, out, pages=None,
+                  nr=None, stream=None):
+    """One decode step of the compressor: token rows [B][d] at positions pos
+    [B] join the tails (Tail or None); completed blocks go to `out`."""
+    lib = load()
+    _need_cuda(kv_cur, gate_cur, kv_prev, gate_prev, pos, pos_bias)
+    B, d = kv_cur.shape
+    kind = OUT_KV if isinstance(out, KVCache) else OUT_IDX
+    st = out.c_struct()
+    ts = None if tail is None else tail.c_struct()
+    ps = None if pages is None else pages.c_struct()
+    ns = None if nr is None else nr.c_struct()
+    s = lib.v4attn_append(_ptr(kv_cur), _ptr(gate_cur), _ptr(kv_prev), _ptr(gate_prev),
+                          _byref(ts), _ptr(pos), _ptr(pos_bias), _dtype_code(kv_cur), B, d, m,
+                          kind, ctypes.byref(st), _byref(ps), _byref(ns), _stream(stream))
+    _check(s, "v4attn_append")
+    return out
+
+
+def v4attn_index_topk_paged(q_idx, w, keys, pages, pos, m, k, score_bf16=False, topk=None,
+                            ws=None, stream=None):
+    lib = load()
+    _need_cuda(q_idx, w, pos)
+    B, Q, H, d = q_idx.shape
+    if topk is None:
+        topk = torch.empty(B, Q, k, dtype=torch.int32, device=q_idx.device)
+    nbytes = v4attn_workspace_bytes(OP_INDEX_TOPK, B, Q, H, d, pages.logical_cap(m), k, 0)
+    ws, wsb = _workspace(ws, nbytes, q_idx.device)
+    st, ps = keys.c_struct(), pages.c_struct()
+    s = lib.v4attn_index_topk_paged(_ptr(q_idx), _dtype_code(q_idx), _ptr(w), ctypes.byref(st),
+                                    ctypes.byref(ps), _ptr(pos), B, Q, H, m, k,
+                                    1 if score_bf16 else 0, _ptr(topk), _ptr(ws), wsb,
+                                    _stream(stream))
+    _check(s, "v4attn_index_topk_paged")
+    return topk
+
+
+def v4attn_csa_attend_paged(q, comp, pages, m, topk, win, n_win, pos, sink, sm_scale, nr=None,
+                            out=None, out_dtype=torch.bfloat16, ws=None, stream=None):
+    lib = load()
+    _need_cuda(q, topk, pos, sink)
+    B, Q, H, D = q.shape
+    k = topk.shape[-1]
+    out = _out(q, out, out_dtype)
+    op = OP_CSA_ATTEND if nr is None else OP_CSA_ATTEND_NR
+    nbytes = v4attn_workspace_bytes(op, B, Q, H, D, pages.logical_cap(m), k, n_win)
+    ws, wsb = _workspace(ws, nbytes, q.device)
+    cs, wst, ps = comp.c_struct(), win.c_struct(), pages.c_struct()
+    ns = None if nr is None else nr.c_struct()
+    s = lib.v4attn_csa_attend_paged(_ptr(q), _dtype_code(q), ctypes.byref(cs), ctypes.byref(ps), m,
+                                    _ptr(topk), k, ctypes.byref(wst), n_win, _ptr(pos), _ptr(sink),
+                                    float(sm_scale), B, Q, H, _ptr(out), _dtype_code(out),
+                                    _byref(ns), _ptr(ws), wsb, _stream(stream))
+    _check(s, "v4attn_csa_attend_paged")
+    return out
+
+
+def v4attn_hca_attend_paged(q, comp, pages, m, win, n_win, pos, sink, sm_scale, nr=None, out=None,
+                            out_dtype=torch.bfloat16, ws=None, stream=None):
+    lib = load()
+    _need_cuda(q, pos, sink)
+    B, Q, H, D = q.shape
+    out = _out(q, out, out_dtype)
+    op = OP_HCA_ATTEND if nr is None else OP_HCA_ATTEND_NR
+    nbytes = v4attn_workspace_bytes(op, B, Q, H, D, pages.logical_cap(m), m, n_win)
+    ws, wsb = _workspace(ws, nbytes, q.device)
+    cs, wst, ps = comp.c_struct(), win.c_struct(), pages.c_struct()
+    ns = None if nr is None else nr.c_struct()
+    s = lib.v4attn_hca_attend_paged(_ptr(q), _dtype_code(q), ctypes.byref(cs), ctypes.byref(ps), m,
+                                    ctypes.byref(wst), n_win, _ptr(pos), _ptr(sink),
+                                    float(sm_scale), B, Q, H, _ptr(out), _dtype_code(out),
+                                    _byref(ns), _ptr(ws), wsb, _stream(stream))
+    _check(s, "v4attn_hca_attend_paged")
     return out

@@ -125,6 +125,29 @@ v4a_status check_nr(const v4a_kv* comp, const v4a_norm_rope* nr) {
   return V4A_OK;
 }
 
+// Validates a page table for a cache of `pool_rows` rows and rate m; fills
+// the kernel's view and the sequence's logical capacity.
+v4a_status check_pages(const v4a_pages* pg, int m, int64_t pool_rows, int64_t min_per_page,
+                       Pages* out, int64_t* lcap) {
+  if (!pg || !pg->table || pg->max_pages < 1 || m < 1) return V4A_ERR_INVALID;
+  const int64_t pt = pg->page_tokens;
+  if (pt < 128 || pt > ((int64_t)1 << 30) || (pt & (pt - 1)) != 0 || m > pt)
+    return V4A_ERR_UNSUPPORTED;
+  const int64_t P = pt / m;
+  if (P < min_per_page) return V4A_ERR_UNSUPPORTED;
+  if (pool_rows < P || pool_rows % P != 0) return V4A_ERR_INVALID;
+  if (pool_rows >= ((int64_t)1 << 31) || (int64_t)pg->max_pages * P >= ((int64_t)1 << 31))
+    return V4A_ERR_UNSUPPORTED;
+  int sh = 0;
+  while (((int64_t)1 << sh) < P) sh++;
+  out->tab = pg->table;
+  out->tab_ld = pg->max_pages;
+  out->psh = sh;
+  out->n_pages = pool_rows / P;
+  *lcap = (int64_t)pg->max_pages * P;
+  return V4A_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -133,7 +156,8 @@ static v4a_status compress_impl(const void* kv_cur, const void* gate_cur, const 
                                 const void* gate_prev, const float* pos_bias, int32_t in_dtype,
                                 int32_t B, int32_t T, int32_t d, int32_t m, int64_t t0,
                                 int32_t out_kind, const void* out, const v4a_norm_rope* nr,
-                                void* stream) {
+                                void* stream, const v4a_pages* pages = nullptr,
+                                const int64_t* apos = nullptr, const v4a_tail* tail = nullptr) {
   if (!kv_cur || !out || B < 0 || T < 0 || d < 1 || t0 < 0) return V4A_ERR_INVALID;
   if (nr && !(nr->eps >= 0.0f)) return V4A_ERR_INVALID;
   if (nr && out_kind != V4A_OUT_KV) return V4A_ERR_UNSUPPORTED;
@@ -188,8 +212,59 @@ static v4a_status compress_impl(const void* kv_cur, const void* gate_cur, const 
   } else {
     return V4A_ERR_INVALID;
   }
+  if (pages) {
+    int64_t lcap = 0;
+    v4a_status s = check_pages(pages, m, a.cap, 1, &a.pg, &lcap);
+    if (s != V4A_OK) return s;
+    if (!apos && t0 / m + T / m > lcap) return V4A_ERR_INVALID;
+    a.cap = lcap;
+  }
+  if (apos) {
+    // decode-time append: one token per sequence, pooled from the tails
+    const bool need_tail = m > 1 || kv_prev;
+    a.apos = apos;
+    if (tail) {
+      a.t_kv_cur = tail->kv_cur;
+      a.t_gate_cur = tail->gate_cur;
+      a.t_kv_prev = tail->kv_prev;
+      a.t_gate_prev = tail->gate_prev;
+      a.t_rows = tail->rows;
+    }
+    if (need_tail) {
+      if (!tail || tail->rows < (kv_prev ? 2 * m : m) || !tail->kv_cur) return V4A_ERR_INVALID;
+      if ((gate_cur && !tail->gate_cur) || (kv_prev && !tail->kv_prev) ||
+          (gate_prev && !tail->gate_prev))
+        return V4A_ERR_INVALID;
+    } else if (tail && tail->rows < 1) {
+      return V4A_ERR_INVALID;
+    }
+    if (B == 0) return V4A_OK;
+    return hip_status(launch_compress(a, (hipStream_t)stream));
+  }
   if (B == 0 || T == 0) return V4A_OK;
   return hip_status(launch_compress(a, (hipStream_t)stream));
+}
+
+v4a_status v4attn_compress_paged(const void* kv_cur, const void* gate_cur, const void* kv_prev,
+                                 const void* gate_prev, const float* pos_bias, int32_t in_dtype,
+                                 int32_t B, int32_t T, int32_t d, int32_t m, int64_t t0,
+                                 int32_t out_kind, const void* out, const v4a_pages* pages,
+                                 const v4a_norm_rope* nr, void* stream) {
+  if (!pages) return V4A_ERR_INVALID;
+  return compress_impl(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, in_dtype, B, T, d, m, t0,
+                       out_kind, out, nr, stream, pages);
+}
+
+v4a_status v4attn_append(const void* kv_cur, const void* gate_cur, const void* kv_prev,
+                         const void* gate_prev, const v4a_tail* tail, const int64_t* pos,
+                         const float* pos_bias, int32_t in_dtype, int32_t B, int32_t d, int32_t m,
+                         int32_t out_kind, const void* out, const v4a_pages* pages,
+                         const v4a_norm_rope* nr, void* stream) {
+  if (!pos) return V4A_ERR_INVALID;
+  // T = m, t0 = 0 pass the shape checks of the chunked call; the append
+  // kernel takes its blocks from pos
+  return compress_impl(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, in_dtype, B, m, d, m, 0,
+                       out_kind, out, nr, stream, pages, pos, tail);
 }
 
 v4a_status v4attn_compress(const void* kv_cur, const void* gate_cur, const void* kv_prev,
@@ -212,7 +287,8 @@ v4a_status v4attn_compress_nr(const void* kv_cur, const void* gate_cur, const vo
 static v4a_status index_topk(const void* q_idx, int32_t q_dtype, const float* w,
                              const v4a_idx* keys, const int64_t* pos, int32_t B, int32_t Q,
                              int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
-                             size_t ws_bytes, void* stream, int score_bf16) {
+                             size_t ws_bytes, void* stream, int score_bf16,
+                             const v4a_pages* pages = nullptr) {
   if (!q_idx || !w || !keys || !pos || !topk || B < 0 || Q < 0 || H_I < 1 || k < 1 || m < 1)
     return V4A_ERR_INVALID;
   if (q_dtype != V4A_F32 && q_dtype != V4A_BF16) return V4A_ERR_INVALID;
@@ -245,7 +321,12 @@ static v4a_status index_topk(const void* q_idx, int32_t q_dtype, const float* w,
   a.k = k;
   a.topk = topk;
   a.score_bf16 = score_bf16;
-  size_t need = index_workspace_bytes(B, Q, H_I, keys->d, keys->cap, a.key_mx);
+  if (pages) {
+    if (!a.key_mx) return V4A_ERR_UNSUPPORTED;
+    v4a_status s = check_pages(pages, m, keys->cap, 128, &a.pg, &a.cap);
+    if (s != V4A_OK) return s;
+  }
+  size_t need = index_workspace_bytes(B, Q, H_I, keys->d, a.cap, a.key_mx);
   if (!ws || ws_bytes < need) return V4A_ERR_WORKSPACE;
   index_carve(a, ws);
   if (B == 0 || Q == 0) return V4A_OK;
@@ -265,6 +346,60 @@ v4a_status v4attn_index_topk_bf16(const void* q_idx, int32_t q_dtype, const floa
                                   int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
                                   size_t ws_bytes, void* stream) {
   return index_topk(q_idx, q_dtype, w, keys, pos, B, Q, H_I, m, k, topk, ws, ws_bytes, stream, 1);
+}
+
+v4a_status v4attn_index_topk_paged(const void* q_idx, int32_t q_dtype, const float* w,
+                                   const v4a_idx* keys, const v4a_pages* pages,
+                                   const int64_t* pos, int32_t B, int32_t Q, int32_t H_I,
+                                   int32_t m, int32_t k, int32_t score_bf16, int32_t* topk,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (!pages) return V4A_ERR_INVALID;
+  return index_topk(q_idx, q_dtype, w, keys, pos, B, Q, H_I, m, k, topk, ws, ws_bytes, stream,
+                    score_bf16 ? 1 : 0, pages);
+}
+
+v4a_status v4attn_csa_attend_paged(const void* q, int32_t q_dtype, const v4a_kv* comp,
+                                   const v4a_pages* pages, int32_t m, const int32_t* topk,
+                                   int32_t k, const v4a_kv* win, int32_t n_win,
+                                   const int64_t* pos, const float* sink, float sm_scale,
+                                   int32_t B, int32_t Q, int32_t H, void* out, int32_t out_dtype,
+                                   const v4a_norm_rope* nr, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype);
+  if (s != V4A_OK) return s;
+  if ((s = check_nr(comp, nr)) != V4A_OK) return s;
+  if (k < 0 || (k > 0 && !topk)) return V4A_ERR_INVALID;
+  if (comp->fmt != V4A_KV_FP8_BF16ROPE) return V4A_ERR_UNSUPPORTED;
+  AttendArgs a;
+  fill_attend(a, q, q_dtype, comp, win, n_win, pos, sink, sm_scale, B, Q, H, out, out_dtype);
+  if ((s = check_pages(pages, m, comp->cap, 1, &a.c_pg, &a.c_cap)) != V4A_OK) return s;
+  a.csa = 1;
+  a.topk = topk;
+  a.k = k;
+  a.m = 1;
+  if (B == 0 || Q == 0) return V4A_OK;
+  return run_attend(a, (int64_t)k + n_win, ws, ws_bytes, stream, nr);
+}
+
+v4a_status v4attn_hca_attend_paged(const void* q, int32_t q_dtype, const v4a_kv* comp,
+                                   const v4a_pages* pages, int32_t m, const v4a_kv* win,
+                                   int32_t n_win, const int64_t* pos, const float* sink,
+                                   float sm_scale, int32_t B, int32_t Q, int32_t H, void* out,
+                                   int32_t out_dtype, const v4a_norm_rope* nr, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype);
+  if (s != V4A_OK) return s;
+  if ((s = check_nr(comp, nr)) != V4A_OK) return s;
+  if (m < 1) return V4A_ERR_INVALID;
+  if (comp->fmt != V4A_KV_FP8_BF16ROPE) return V4A_ERR_UNSUPPORTED;
+  AttendArgs a;
+  fill_attend(a, q, q_dtype, comp, win, n_win, pos, sink, sm_scale, B, Q, H, out, out_dtype);
+  if ((s = check_pages(pages, m, comp->cap, 1, &a.c_pg, &a.c_cap)) != V4A_OK) return s;
+  a.csa = 0;
+  a.topk = nullptr;
+  a.m = m;
+  if (B == 0 || Q == 0) return V4A_OK;
+  return run_attend(a, a.c_cap + n_win, ws, ws_bytes, stream, nr);
 }
 
 v4a_status v4attn_csa_attend_nr(const void* q, int32_t q_dtype, const v4a_kv* comp,

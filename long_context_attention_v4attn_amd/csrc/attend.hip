@@ -214,6 +214,8 @@ __device__ __forceinline__ void resolve_sources(const AttendArgs& a, const RowEn
       } else {
         sr = entry_source(a, r, row, e, &is_win);
       }
+      // a paged cache: the logical row's pool row ([Notes §11] block table)
+      if (a.c_pg.tab && !is_win && sr >= 0) sr = page_row(a.c_pg, row / a.Q, sr);
       code = sr < 0 ? -1 : (is_win ? (int)(-2 - sr) : (int)sr);
       src[l] = code;
     }
@@ -627,9 +629,10 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   __syncthreads();
 
   Bases B;
-  B.cn = a.c_nope + (int64_t)b * a.c_cap * kNope;
-  B.cr = (const uint8_t*)(a.c_rope + (int64_t)b * a.c_cap * kRope);
-  B.cs = a.c_scale + (int64_t)b * a.c_cap;
+  const int64_t cbase = a.c_pg.tab ? 0 : (int64_t)b * a.c_cap;   // paged: pool rows
+  B.cn = a.c_nope + cbase * kNope;
+  B.cr = (const uint8_t*)(a.c_rope + cbase * kRope);
+  B.cs = a.c_scale + cbase;
   B.wn = a.w_nope + (int64_t)b * a.w_cap * kNope;
   B.wr = (const uint8_t*)(a.w_rope + (int64_t)b * a.w_cap * kRope);
   B.ws = a.w_scale + (int64_t)b * a.w_cap;

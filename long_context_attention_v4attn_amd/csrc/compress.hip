@@ -29,20 +29,61 @@ __device__ __forceinline__ float ld(const void* p, int bf16, size_t i) {
   return load_as_f32(p, bf16, i);
 }
 
+// kAppend: a decode step ([Notes §11] state cache): one workgroup per
+// sequence b and one new token at position p = apos[b].  The token's rows
+// join the compressor tails (ring rows p mod t_rows); when the token completes
+// block i = (p + 1) / m - 1, the block is pooled like any other: its current
+// rows are tail rows except the token itself (read from the input), its
+// previous-role rows (tokens of block i - 1) are tail rows.  With t_rows >= 2m
+// (>= m without overlap) no row read here is the row the token writes.
+template <bool kAppend>
 __global__ void __launch_bounds__(kCompThreads) k_compress(CompressArgs a) {
   __shared__ float red[kCompThreads / 64];
-  const int j = blockIdx.x;                // block within the call
-  const int b = blockIdx.y;
   const int m = a.m;
   const int d = a.d;
   const bool overlap = a.kv_prev != nullptr;
-  const int64_t gblk = a.t0 / m + j;       // global block index
-  // a call that produces more than cap entries keeps the last cap of them:
-  // an earlier block whose ring row a later block of this call also writes
-  // is skipped (concurrent writes to one row would race)
-  if ((int64_t)(a.T / m) - j > a.cap) return;
+  int b, j = 0;
+  int64_t gblk, p = 0;
+  if (kAppend) {
+    b = blockIdx.x;
+    p = a.apos[b];
+    if (p < 0) return;
+    const size_t di = ((size_t)b * a.t_rows + (size_t)(p % a.t_rows)) * d;
+    const size_t si = (size_t)b * d;
+    auto keep = [&](void* dst, const void* src) {
+      if (!dst || !src) return;
+      for (int c = threadIdx.x; c < d; c += kCompThreads) {
+        if (a.in_bf16) ((uint16_t*)dst)[di + c] = ((const uint16_t*)src)[si + c];
+        else ((float*)dst)[di + c] = ((const float*)src)[si + c];
+      }
+    };
+    keep(a.t_kv_cur, a.kv_cur);
+    keep(a.t_gate_cur, a.gate_cur);
+    keep(a.t_kv_prev, a.kv_prev);
+    keep(a.t_gate_prev, a.gate_prev);
+    if ((p + 1) % m != 0) return;          // uniform: the block is not complete
+    gblk = (p + 1) / m - 1;
+    // a block past the sequence's pages is not stored
+    if (a.pg.tab && (gblk >> a.pg.psh) >= a.pg.tab_ld) return;
+  } else {
+    j = blockIdx.x;                        // block within the call
+    b = blockIdx.y;
+    gblk = a.t0 / m + j;                   // global block index
+    // a call that produces more than cap ring entries keeps the last cap of
+    // them: an earlier block whose ring row a later block of this call also
+    // writes is skipped (concurrent writes to one row would race)
+    if (!a.pg.tab && (int64_t)(a.T / m) - j > a.cap) return;
+  }
   const bool has_prev = overlap && gblk > 0;
   const int64_t rbase = ((int64_t)b * a.T + (int64_t)j * m) * d;   // row m*j of this call
+  // slot sources: the call's rows, or (append) tail rows and the token
+  auto prev_idx = [&](int u, int c) -> size_t {
+    if (!kAppend) return rbase + (int64_t)u * d + c;
+    const int64_t t = (gblk - 1) * m + u;
+    return ((size_t)b * a.t_rows + (size_t)(t % a.t_rows)) * d + c;
+  };
+  const void* kv_prev = kAppend ? a.t_kv_prev : a.kv_prev;
+  const void* gate_prev = kAppend ? (a.gate_prev ? a.t_gate_prev : nullptr) : a.gate_prev;
 
   float y[kMaxChan];
 #pragma unroll
@@ -65,23 +106,35 @@ __global__ void __launch_bounds__(kCompThreads) k_compress(CompressArgs a) {
     };
     if (has_prev) {
       for (int u = 0; u < m; u++) {
-        size_t idx = rbase + (int64_t)u * d + c;
-        float z = (a.gate_prev ? ld(a.gate_prev, a.in_bf16, idx) : 0.0f) +
+        size_t idx = prev_idx(u, c);
+        float z = (gate_prev ? ld(gate_prev, a.in_bf16, idx) : 0.0f) +
                   (a.bias ? a.bias[(size_t)u * d + c] : 0.0f);
-        add(z, ld(a.kv_prev, a.in_bf16, idx));
+        add(z, ld(kv_prev, a.in_bf16, idx));
       }
     }
     const int boff = overlap ? m : 0;
     for (int u = 0; u < m; u++) {
+      const void* kvp = a.kv_cur;
+      const void* gp = a.gate_cur;
       size_t idx = rbase + (int64_t)u * d + c;
-      float z = (a.gate_cur ? ld(a.gate_cur, a.in_bf16, idx) : 0.0f) +
+      if (kAppend) {
+        const int64_t t = gblk * m + u;
+        if (t == p) {
+          idx = (size_t)b * d + c;
+        } else {
+          kvp = a.t_kv_cur;
+          gp = a.gate_cur ? a.t_gate_cur : nullptr;
+          idx = ((size_t)b * a.t_rows + (size_t)(t % a.t_rows)) * d + c;
+        }
+      }
+      float z = (gp ? ld(gp, a.in_bf16, idx) : 0.0f) +
                 (a.bias ? a.bias[(size_t)(boff + u) * d + c] : 0.0f);
-      add(z, ld(a.kv_cur, a.in_bf16, idx));
+      add(z, ld(kvp, a.in_bf16, idx));
     }
     y[q] = num / den;
   }
 
-  const int64_t orow = (int64_t)b * a.cap + (gblk % a.cap);
+  const int64_t orow = a.pg.tab ? page_row(a.pg, b, gblk) : (int64_t)b * a.cap + (gblk % a.cap);
   if (a.out_kind == 0 && (a.nr_gamma || a.nr_inv)) {
     // [Notes §9] KV-entry RMSNorm over the d channels, then RoPE of the last
     // d - d_nope channels at the entry's position (its block's last token):
@@ -188,9 +241,14 @@ __global__ void __launch_bounds__(kCompThreads) k_compress(CompressArgs a) {
 }
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  if (a.apos) {
+    hipLaunchKernelGGL(k_compress<true>, dim3(a.B), dim3(kCompThreads), 0, st, a);
+    return hipGetLastError();
+  }
   const int nb = a.T / a.m;
-  if (nb == 0 || a.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_compress, dim3(nb, a.B), dim3(kCompThreads), 0, st, a);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_compress<false>, dim3(nb, a.B), dim3(kCompThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -60,6 +60,7 @@ constexpr int kScanWaves = 4;              // waves per scan workgroup
 constexpr int kIterBlocks = kScanWaves * kWaveTiles * 16;   // 512 blocks per workgroup iteration
 constexpr int kQT = 8;                     // queries per workgroup of the query-tiled scan
 constexpr int kMaxParts = 128;             // widest partial-histogram row
+constexpr int kMaxIters = 32;              // iterations per scan workgroup (<= 16384 blocks)
 
 // Plan of the one-query-per-workgroup FP4 scan: about 512 workgroups of 4
 // waves in all (two per CU), each walking `iters` iterations of kIterBlocks
@@ -78,6 +79,7 @@ static ScanPlan scan_plan(int64_t cap, int64_t R, int H, int Q, int key_mx) {
   int64_t iters = (it_total * R + 511) / 512;
   if (iters < 1) iters = 1;
   if (iters > it_total) iters = it_total;
+  if (iters > kMaxIters) iters = kMaxIters;
   p.iters = (int)iters;
   p.wgs = (int)((it_total + iters - 1) / iters);
   if (H == 16 && iters * kIterBlocks <= 65535 && p.wgs <= kMaxParts) p.hp_ld = p.wgs;
@@ -241,11 +243,17 @@ struct KeyTiles {
 // known; blocks past the visible count are dropped when the scores are
 // stored.  Away from the cache end (the uniform common case) every load is
 // one base address plus an immediate offset.
+// Paged keys: a page holds >= 128 keys and blk0 is a multiple of 128, so the
+// wave's blocks are one contiguous run of pool rows (past the cache end the
+// run of the last 128 blocks stands in).
 __device__ __forceinline__ void load_keys(const uint8_t* kc, const uint8_t* ks, int64_t blk0,
-                                          int64_t cap, int g, int li, KeyTiles& kt) {
-  if (blk0 + kWaveTiles * 16 <= cap) {
-    const uint8_t* cp = kc + (blk0 + li) * 64 + g * 16;
-    const uint32_t* sp = (const uint32_t*)(ks + (blk0 + 16 * g + li) * 4);
+                                          int64_t cap, const Pages& pg, int b, int g, int li,
+                                          KeyTiles& kt) {
+  const bool paged = pg.tab != nullptr;
+  if (paged || blk0 + kWaveTiles * 16 <= cap) {
+    const int64_t r0 = paged ? page_row(pg, b, blk0 < cap ? blk0 : cap - kWaveTiles * 16) : blk0;
+    const uint8_t* cp = kc + (r0 + li) * 64 + g * 16;
+    const uint32_t* sp = (const uint32_t*)(ks + (r0 + 16 * g + li) * 4);
 #pragma unroll
     for (int t = 0; t < kWaveTiles; t++)
       kt.v[t] = __builtin_nontemporal_load((const u32x4*)(cp + t * 1024));
@@ -407,8 +415,9 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int64_t wg0 = (int64_t)blockIdx.x * a.score_iters * kIterBlocks;
-  const uint8_t* kc = (const uint8_t*)a.codes + (size_t)b * a.cap * 64;
-  const uint8_t* ks = a.kscales + (size_t)b * a.cap * 4;
+  const size_t kb = a.pg.tab ? 0 : (size_t)b * a.cap;   // paged: rows are pool rows
+  const uint8_t* kc = (const uint8_t*)a.codes + kb * 64;
+  const uint8_t* ks = a.kscales + kb * 4;
   const int64_t wblk = wg0 + wave * (kWaveTiles * 16);
   // the query's operands first: loads return in order, so the query must not
   // queue behind keys
@@ -448,7 +457,7 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
 #pragma unroll
   for (int j = 0; j < kSets; j++)
     if (kIters > 0 ? j < kDepth - 1 : j < a.score_iters)
-      load_keys(kc, ks, wblk + (int64_t)j * kIterBlocks, a.cap, g, li, kt[j]);
+      load_keys(kc, ks, wblk + (int64_t)j * kIterBlocks, a.cap, a.pg, b, g, li, kt[j]);
   // the query loads went out first, so this waits for them alone and runs
   // while the first keys are on their way
   if (kParts) quantize_q_frag(a, qraw, &qa[0], &qs[0]);
@@ -475,7 +484,7 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
 #pragma unroll
     for (int j = 0; j < kSets; j++) {
       if (j + kDepth - 1 < kSets)
-        load_keys(kc, ks, wblk + (int64_t)(j + kDepth - 1) * kIterBlocks, a.cap, g, li,
+        load_keys(kc, ks, wblk + (int64_t)(j + kDepth - 1) * kIterBlocks, a.cap, a.pg, b, g, li,
                   kt[j + kDepth - 1]);
       if (j < iters)
         score_tiles<kHT>(kt[j], qa, qs, wv, HT, wblk + (int64_t)j * kIterBlocks, nv, a.sc_ld, lane,
@@ -487,10 +496,10 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
       const int64_t b0 = wblk + (int64_t)it * kIterBlocks;
       score_tiles<kHT>(kt[0], qa, qs, wv, HT, b0, nv, a.sc_ld, lane, out, outh, bf16, lh);
       if (it + 1 >= iters) break;
-      if (it + 2 < iters) load_keys(kc, ks, b0 + 2 * kIterBlocks, a.cap, g, li, kt[0]);
+      if (it + 2 < iters) load_keys(kc, ks, b0 + 2 * kIterBlocks, a.cap, a.pg, b, g, li, kt[0]);
       score_tiles<kHT>(kt[1], qa, qs, wv, HT, b0 + kIterBlocks, nv, a.sc_ld, lane, out, outh, bf16,
                        lh);
-      if (it + 3 < iters) load_keys(kc, ks, b0 + 3 * kIterBlocks, a.cap, g, li, kt[1]);
+      if (it + 3 < iters) load_keys(kc, ks, b0 + 3 * kIterBlocks, a.cap, a.pg, b, g, li, kt[1]);
     }
   }
   if (kParts) {
@@ -521,14 +530,17 @@ struct QFrag {
 };
 
 __device__ __forceinline__ void load_qfrag(const uint8_t* kc, const uint8_t* ks, int64_t blk,
-                                           int64_t last, int g, QFrag& f) {
-  const int64_t bb = blk < last ? blk : last;     // clamped: always a real row
+                                           int64_t last, int g, QFrag& f, const int* pgl,
+                                           int64_t r0, int psh) {
+  int64_t bb = blk < last ? blk : last;     // clamped: always a real row
+  if (pgl) bb = ((int64_t)pgl[(bb - r0) >> psh] << psh) | (bb & (((int64_t)1 << psh) - 1));
   f.v = __builtin_nontemporal_load((const u32x4*)(kc + bb * 64 + g * 16));
   f.sc = ks[bb * 4 + g];
 }
 
 __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
   __shared__ uint32_t lh[kQT][kBins1];
+  __shared__ int pg_rows[kQRange / 128];    // paged keys: the range's pool pages
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
@@ -545,6 +557,17 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
   }
   if (r0 >= nv_max) return;                // uniform across the workgroup
   for (int i = threadIdx.x; i < kQT * kBins1; i += blockDim.x) (&lh[0][0])[i] = 0u;
+  if (a.pg.tab) {
+    // (a page longer than the range: the range lies in one page)
+    const int n_pg = (kQRange >> a.pg.psh) > 0 ? (kQRange >> a.pg.psh) : 1;
+    for (int i = threadIdx.x; i < n_pg; i += blockDim.x) {
+      int64_t lp = (r0 >> a.pg.psh) + i;
+      lp = lp < a.pg.tab_ld ? lp : a.pg.tab_ld - 1;
+      int64_t pp = a.pg.tab[(int64_t)b * a.pg.tab_ld + lp];
+      pp = pp < 0 ? 0 : (pp >= a.pg.n_pages ? a.pg.n_pages - 1 : pp);
+      pg_rows[i] = (int)pp;
+    }
+  }
   // A operands (16 heads x 128 elements of each query), scales, head weights
   i32x8 qa[kQT];
   int qs[kQT];
@@ -573,8 +596,11 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
   const size_t o1 = (size_t)((int64_t)b * a.Q + t0 + qa1) * a.sc_ld;
   __syncthreads();                         // lh zeroed
 
-  const uint8_t* kc = (const uint8_t*)a.codes + (size_t)b * a.cap * 64;
-  const uint8_t* ks = a.kscales + (size_t)b * a.cap * 4;
+  const size_t kb = a.pg.tab ? 0 : (size_t)b * a.cap;   // paged: rows are pool rows
+  const uint8_t* kc = (const uint8_t*)a.codes + kb * 64;
+  const uint8_t* ks = a.kscales + kb * 4;
+  const int* pgl = a.pg.tab ? pg_rows : nullptr;
+  const int psh = a.pg.psh;
   const int64_t r1 = r0 + kQRange < nv_max ? r0 + kQRange : nv_max;
   const int64_t last = r1 - 1;
 
@@ -611,12 +637,12 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
   // tiles w, w + 4, ... of 16 blocks; two fragments in flight
   QFrag fa, fb;
   int64_t blk0 = r0 + wave * 16;
-  load_qfrag(kc, ks, blk0 + li, last, g, fa);
+  load_qfrag(kc, ks, blk0 + li, last, g, fa, pgl, r0, psh);
   for (; blk0 < r1; blk0 += 128) {
-    load_qfrag(kc, ks, blk0 + 64 + li, last, g, fb);
+    load_qfrag(kc, ks, blk0 + 64 + li, last, g, fb, pgl, r0, psh);
     tile(fa, blk0);
     if (blk0 + 64 >= r1) break;
-    load_qfrag(kc, ks, blk0 + 128 + li, last, g, fa);
+    load_qfrag(kc, ks, blk0 + 128 + li, last, g, fa, pgl, r0, psh);
     tile(fb, blk0 + 64);
   }
   __syncthreads();

@@ -8,6 +8,23 @@
 
 namespace v4a {
 
+// Paged classical cache ([Notes §11]): logical row r of sequence b lives at
+// pool row tab[b * tab_ld + (r >> psh)] * 2^psh + (r & (2^psh - 1)).  Page
+// ids are clamped into [0, n_pages) on the device, so no table content can
+// address outside the pool.  tab == null: the contiguous [B][cap] layout.
+struct Pages {
+  const int32_t* tab;
+  int tab_ld;                // table row length (pages per sequence)
+  int psh;                   // log2 of the entries per page
+  int64_t n_pages;           // pages in the pool
+};
+
+__device__ __forceinline__ int64_t page_row(const Pages& pg, int b, int64_t r) {
+  int64_t p = pg.tab[(int64_t)b * pg.tab_ld + (r >> pg.psh)];
+  p = p < 0 ? 0 : (p >= pg.n_pages ? pg.n_pages - 1 : p);
+  return (p << pg.psh) | (r & (((int64_t)1 << pg.psh) - 1));
+}
+
 // ---------------------------------------------------------------- compress
 struct CompressArgs {
   const void* kv_cur;
@@ -29,6 +46,17 @@ struct CompressArgs {
   const float* nr_gamma;     // [d]
   const float* nr_inv;       // [d_rope / 2] inverse frequencies
   float nr_eps;
+  Pages pg;                  // paged output: row = page_row(block), no ring
+  // decode-time append (apos non-null): one token per sequence, kv_* / gate_*
+  // are [B][d]; the token's rows go to the tails (t_* [B][t_rows][d], token t
+  // at row t mod t_rows) and a block that the token completes is pooled from
+  // the tails plus the token itself
+  const int64_t* apos;       // [B] the token's position (< 0: sequence idle)
+  void* t_kv_cur;
+  void* t_gate_cur;
+  void* t_kv_prev;
+  void* t_gate_prev;
+  int t_rows;
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
 
@@ -64,6 +92,7 @@ struct IndexArgs {
   uint64_t* cand;            // [R][16384] candidate keys (score key : inverted id)
   uint32_t* chunk;           // [R][n_chunks] per filter chunk: ids above the candidates
   uint16_t* hparts;          // [R][hp_ld][256] per-scan-workgroup first-digit counts
+  Pages pg;                  // paged keys (MXFP4 only; >= 128 keys per page)
 };
 size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx);
 void index_carve(IndexArgs& a, void* ws);
@@ -109,6 +138,7 @@ struct AttendArgs {
   const float* nr_gamma;     // [D] or null
   const float* nr_inv;       // [d_rope / 2] or null
   float nr_eps;
+  Pages c_pg;                // paged compressed cache (FP8 path only)
 };
 void attend_plan(AttendArgs& a, int64_t n_entries_max);
 size_t attend_workspace_bytes(const AttendArgs& a);

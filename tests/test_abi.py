@@ -146,6 +146,68 @@ def test_norm_rope_variants_rejected_on_host(clib):
         assert b >= a + 4 * 64 * 512 * 2
 
 
+class _Pg(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+                ("page_tokens", ctypes.c_int32)]
+
+
+class _Tail(ctypes.Structure):
+    _fields_ = [("kv_cur", ctypes.c_void_p), ("gate_cur", ctypes.c_void_p),
+                ("kv_prev", ctypes.c_void_p), ("gate_prev", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("_pad", ctypes.c_int32)]
+
+
+def test_paged_variants_rejected_on_host(clib):
+    r = ctypes.byref
+    f = ctypes.c_float(0.1)
+    pg = _Pg(0x6000, 8, 512)                     # 128 CSA entries per page
+    kv = _KV(2, 448, 64, 0, 128 * 10, 0x1000, 0x2000, 0x3000)     # a pool of 10 pages
+    kv32 = _KV(0, 448, 64, 0, 128 * 10, 0x1000, 0x2000, 0)
+    ix = _Idx(3, 128, 128 * 10, 0x1000, 0x2000)
+    ix32 = _Idx(0, 128, 128 * 10, 0x1000, 0)
+
+    def csa(comp, pages, m=4):
+        return clib.v4attn_csa_attend_paged(FAKE, 1, r(comp), r(pages) if pages else None, m, FAKE,
+                                            8, r(comp), 16, FAKE, None, f, 1, 1, 64, FAKE, 1, None,
+                                            FAKE, 1 << 30, None)
+
+    def idx(keys, pages, m=4):
+        return clib.v4attn_index_topk_paged(FAKE, 1, FAKE, r(keys), r(pages) if pages else None,
+                                            FAKE, 1, 1, 16, m, 64, 0, FAKE, FAKE, 1 << 30, None)
+    # no table; page sizes that are not powers of two >= 128
+    assert csa(kv, None) == -1
+    for bad in (_Pg(0x6000, 8, 192), _Pg(0x6000, 8, 64), _Pg(0x6000, 0, 512), _Pg(None, 8, 512)):
+        assert csa(kv, bad) in (-1, -2)
+    # fp32 caches are not paged; m above the page
+    assert csa(kv32, pg) == -2
+    assert csa(kv, pg, m=1024) == -2
+    # the pool is not whole pages
+    assert csa(_KV(2, 448, 64, 0, 1000, 0x1000, 0x2000, 0x3000), pg) == -1
+    # indexer: MXFP4 keys with >= 128 keys per page only
+    assert idx(ix, _Pg(0x6000, 8, 256)) == -2
+    assert idx(ix32, pg) == -2
+    assert idx(ix, None) == -1
+    # HCA: rate 128 on 512-token pages is 4 entries per page (accepted shape);
+    # a pool that is not whole pages is still refused
+    assert clib.v4attn_hca_attend_paged(FAKE, 1, r(_KV(2, 448, 64, 0, 6, 0x1000, 0x2000, 0x3000)),
+                                        r(pg), 128, r(kv), 16, FAKE, None, f, 1, 1, 64, FAKE, 1,
+                                        None, FAKE, 1 << 30, None) == -1
+    # compress: the call's blocks past the sequence's pages
+    assert clib.v4attn_compress_paged(FAKE, None, None, None, None, 0, 1, 4 * 1100, 512, 4, 0, 0,
+                                      r(kv), r(pg), None, None) == -1
+    # append: a rate above 1 needs tails of >= m rows (>= 2m with overlap),
+    # with a gate ring where gates are given
+    def app(tail, m=4, kv_prev=None, gate=None):
+        return clib.v4attn_append(FAKE, gate, kv_prev, None, r(tail) if tail else None, FAKE, None,
+                                  0, 2, 512, m, 0, r(kv), r(pg), None, None)
+    assert app(None) == -1
+    assert app(_Tail(0x7000, None, 0x7100, None, 7, 0), kv_prev=FAKE) == -1
+    assert app(_Tail(0x7000, None, None, None, 4, 0), gate=FAKE) == -1
+    assert app(_Tail(0x7000, None, None, None, 4, 0), m=256) == -2   # above the page size
+    assert clib.v4attn_append(FAKE, None, None, None, None, None, None, 0, 2, 512, 1, 0, r(kv),
+                              None, None, None) == -1                 # no positions
+
+
 def test_binding_refuses_host_tensors():
     import numpy as np
     import torch

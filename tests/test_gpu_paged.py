@@ -1,0 +1,317 @@
+"""GPU parity of the paged classical cache and the decode-time compressor
+append ([Notes §11] KV cache table) against the oracle: the indexer and both
+attention calls over pools whose pages are shuffled (results against the
+oracle on the table's logical view, and bit-equal to the contiguous calls on
+the same entries), the chunked compressor writing through the table, and
+decode steps that fill the compressor tails and the window ring."""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_v4attn_amd import synth
+from oracle import codecs as C
+from oracle.attend import csa_attend, hca_attend
+from oracle.compress import compress
+from oracle.indexer import index_scores
+from oracle.normrope import default_inv_freq
+from oracle.paged import append_entry, logical_view, pool_rows
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _perm(rng, Bn, n_pg, spare=3):
+    """A block table naming distinct, shuffled pool pages (plus unused ones)."""
+    n_pool = Bn * n_pg + spare
+    return rng.permutation(n_pool)[:Bn * n_pg].reshape(Bn, n_pg).astype(np.int32), n_pool
+
+
+def _to_pool(a, table, P_, n_pool):
+    """Host array [B][n_pg * P][...] -> pool [1][n_pool * P][...] through the table."""
+    out = np.zeros((1, n_pool * P_) + a.shape[2:], a.dtype)
+    for b in range(table.shape[0]):
+        out[0, pool_rows(table[b], P_, np.arange(table.shape[1] * P_))] = a[b]
+    return out
+
+
+def _pool_kv(kv, table, P_, n_pool):
+    return C.KV(kv.fmt, kv.d_nope, kv.d_rope, _to_pool(kv.nope, table, P_, n_pool),
+                _to_pool(kv.rope, table, P_, n_pool), _to_pool(kv.scale, table, P_, n_pool))
+
+
+def _pool_idx(ix, table, P_, n_pool):
+    return C.Idx(ix.fmt, ix.d, _to_pool(ix.codes, table, P_, n_pool),
+                 _to_pool(ix.scales, table, P_, n_pool))
+
+
+def _dev_pool(t, table, P_, n_pool):
+    """Device tensor [B][n_pg * P][...] -> device pool [1][n_pool * P][...]."""
+    Bn, n_pg = table.shape
+    out = torch.zeros((n_pool, P_) + tuple(t.shape[2:]), dtype=t.dtype, device=t.device)
+    out[torch.from_numpy(table.reshape(-1).astype(np.int64)).cuda()] = t.reshape(
+        (Bn * n_pg, P_) + tuple(t.shape[2:]))
+    return out.reshape((1, n_pool * P_) + tuple(t.shape[2:]))
+
+
+def _pages(lib, table, page_tokens):
+    return lib.Pages(P.dev(table), page_tokens)
+
+
+@pytest.mark.parametrize("Q,page_tokens,n_pg,bf16", [(1, 512, 7, False), (1, 2048, 5, True),
+                                                      (16, 512, 6, False), (3, 4096, 3, False)])
+def test_index_topk_paged(lib, Q, page_tokens, n_pg, bf16):
+    print(f"index paged Q={Q} page_tokens={page_tokens} pages={n_pg} bf16={bf16}", flush=True)
+    rng = np.random.default_rng(page_tokens + Q)
+    Bn, H, d, m, k = 2, 16, 128, 4, 100
+    P_ = page_tokens // m
+    table, n_pool = _perm(rng, Bn, n_pg)
+    keys = C.idx_encode((rng.standard_normal((Bn, n_pg * P_, d)) * d ** -0.5).astype(np.float32),
+                        "mxfp4")
+    pool = _pool_idx(keys, table, P_, n_pool)
+    lv = logical_view(pool, table, P_)
+    lcap = n_pg * P_
+    # ragged visible counts: mid-page, page ends, the whole table, beyond it
+    base = [4 * lcap + 50, 4 * P_ - 1, 4 * (lcap // 2) + 3, 4 * lcap - 1, 37, 4 * P_ + 7]
+    pos = np.array([[base[(b * Q + t) % len(base)] - 4 * t * (t % 3) for t in range(Q)]
+                    for b in range(Bn)], np.int64)
+    q = (rng.standard_normal((Bn, Q, H, d)) * d ** -0.5).astype(np.float32)
+    w = rng.random((Bn, Q, H)).astype(np.float32)
+    qb = C.bf16_encode(q)
+    topk = lib.v4attn_index_topk_paged(P.dev(qb.view(np.int16)).view(torch.bfloat16), P.dev(w),
+                                       P.idx_to_dev(pool), _pages(lib, table, page_tokens),
+                                       P.dev(pos), m, k, score_bf16=bf16)
+    torch.cuda.synchronize()
+    sc = index_scores(C.bf16_decode(qb).astype(np.float32), w, lv, pos, m)
+    g = topk.cpu().numpy()
+    check = P.check_topk_row_bf16 if bf16 else P.check_topk_row
+    for b in range(Bn):
+        for t in range(Q):
+            check(g[b, t], sc[b][t], k)
+
+
+def _nr(lib, rng, D=512):
+    gamma = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    inv = default_inv_freq(64).astype(np.float32)
+    return (dict(gamma=gamma.astype(np.float64), eps=1e-6, inv_freq=inv),
+            lib.NormRope(P.dev(gamma), P.dev(inv), 1e-6))
+
+
+@pytest.mark.parametrize("kind,page_tokens,n_pg,with_nr", [("csa", 512, 9, False),
+                                                            ("csa", 1024, 3, True),
+                                                            ("hca", 512, 300, False),
+                                                            ("hca", 8192, 20, True)])
+def test_attend_paged(lib, kind, page_tokens, n_pg, with_nr):
+    print(f"attend paged {kind} page_tokens={page_tokens} pages={n_pg} nr={with_nr}", flush=True)
+    rng = np.random.default_rng(page_tokens + n_pg)
+    Bn, Q, H, D, R, n_win = 2, 2, 64, 512, 160, 128
+    m = 4 if kind == "csa" else 128
+    P_ = page_tokens // m
+    table, n_pool = _perm(rng, Bn, n_pg)
+    lcap = n_pg * P_
+    comp = C.kv_encode((rng.standard_normal((Bn, lcap, D)) * D ** -0.5 * 3).astype(np.float32),
+                       "fp8", 448)
+    win = C.kv_encode((rng.standard_normal((Bn, R, D)) * D ** -0.5 * 3).astype(np.float32), "fp8",
+                      448)
+    pool = _pool_kv(comp, table, P_, n_pool)
+    lv = logical_view(pool, table, P_)
+    qb = C.bf16_encode(rng.standard_normal((Bn, Q, H, D)).astype(np.float32))
+    qd = P.dev(qb.view(np.int16)).view(torch.bfloat16)
+    pos = np.array([[m * lcap + 9, m * (lcap // 3) + 1], [40, m * lcap - 1]], np.int64)
+    nr, nd = _nr(lib, rng) if with_nr else (None, None)
+    pages = _pages(lib, table, page_tokens)
+    scale = D ** -0.5
+    if kind == "hca":
+        _, ref = hca_attend(qb, "bf16", lv, m, win, n_win, pos, None, scale, "bf16", nr=nr)
+        o = lib.v4attn_hca_attend_paged(qd, P.kv_to_dev(pool), pages, m, P.kv_to_dev(win), n_win,
+                                        P.dev(pos), None, scale, nr=nd)
+    else:
+        k = min(lcap, 600)
+        topk = np.full((Bn, Q, k), -1, np.int64)
+        for b in range(Bn):
+            for t in range(Q):
+                nv = min((pos[b, t] + 1) // m, lcap)
+                kk = min(k, nv) - 3
+                topk[b, t, :kk] = np.sort(rng.choice(nv, kk, replace=False))
+                topk[b, t, kk] = lcap + 5           # out of range: skipped
+        _, ref = csa_attend(qb, "bf16", lv, topk, win, n_win, pos, None, scale, "bf16", nr=nr)
+        o = lib.v4attn_csa_attend_paged(qd, P.kv_to_dev(pool), pages, m,
+                                        P.dev(topk.astype(np.int32)), P.kv_to_dev(win), n_win,
+                                        P.dev(pos), None, scale, nr=nd)
+    torch.cuda.synchronize()
+    P.check_out(o, ref)
+
+
+@pytest.mark.parametrize("m,overlap,out", [(4, True, "kv"), (4, True, "idx"), (128, False, "kv")])
+def test_compress_paged(lib, m, overlap, out):
+    print(f"compress paged m={m} overlap={overlap} out={out}", flush=True)
+    rng = np.random.default_rng(m + overlap)
+    Bn, page_tokens, n_pg = 2, 1024, 4
+    d = 512 if out == "kv" else 128
+    P_ = page_tokens // m
+    table, n_pool = _perm(rng, Bn, n_pg)
+    t0 = page_tokens - 2 * m                   # the chunk crosses a page boundary
+    T = page_tokens + 4 * m
+    g = synth.compress_inputs(6, Bn, T, d, m, overlap, t0)
+    y = compress(g["kv_cur"], g["gate_cur"], g["kv_prev"], g["gate_prev"], g["bias"], m, t0)
+    pages = _pages(lib, table, page_tokens)
+    if out == "kv":
+        pool = lib.KVCache.empty(1, n_pool * P_, 448, 64, lib.KV_FP8_BF16ROPE)
+    else:
+        pool = lib.IdxCache.empty(1, n_pool * P_, d, lib.IDX_MXFP4)
+    lib.v4attn_compress_paged(P.dev(g["kv_cur"]), P.dev(g["gate_cur"]),
+                              None if g["kv_prev"] is None else P.dev(g["kv_prev"]),
+                              None if g["gate_prev"] is None else P.dev(g["gate_prev"]),
+                              P.dev(g["bias"]), m, t0, pool, pages)
+    torch.cuda.synchronize()
+    rows = t0 // m + np.arange(T // m)
+    if out == "kv":
+        lv = logical_view(P.kv_from_dev(pool), table, P_)
+        sub = C.KV("fp8", 448, 64, lv.nope[:, rows], lv.rope[:, rows], lv.scale[:, rows])
+        P.check_fp8_rows(sub, y, 448)
+    else:
+        lv = logical_view(P.idx_from_dev(pool), table, P_)
+        P.check_mxfp4_rows(C.Idx("mxfp4", d, lv.codes[:, rows], lv.scales[:, rows]), y)
+
+
+@pytest.mark.parametrize("m,overlap,paged,with_nr,dtype", [(4, True, True, False, "f32"),
+                                                           (4, True, False, True, "bf16"),
+                                                           (16, False, True, False, "f32"),
+                                                           (1, False, False, False, "bf16")])
+def test_append_decode_steps(lib, m, overlap, paged, with_nr, dtype):
+    # sequences start at different steps (idle before: position -1), so blocks
+    # complete at different calls; every completed block is compared with the
+    # compressor's definition over the same token stream
+    print(f"append m={m} overlap={overlap} paged={paged} nr={with_nr} {dtype}", flush=True)
+    rng = np.random.default_rng(3 * m + paged)
+    Bn, d, steps = 3, 512, 70
+    start = [0, 5, 11]
+    T = steps
+    st = synth.compress_inputs(7, Bn, T, d, max(m, 1), overlap, 0)
+    to_in = (lambda a: C.bf16_decode(C.bf16_encode(a)).astype(np.float32)) if dtype == "bf16" \
+        else (lambda a: a)
+    streams = {k: (None if v is None else to_in(v)) for k, v in st.items() if k != "bias"}
+    if m == 1:
+        streams["gate_cur"] = None
+    bias = None if m == 1 else st["bias"]
+    nr, nd = _nr(lib, rng) if with_nr else (None, None)
+    dev_in = (lambda a: P.bf16_dev(a)) if dtype == "bf16" else (lambda a: P.dev(a))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tail = None if m == 1 else lib.Tail.empty(Bn, 2 * m if overlap else m, d, tdt,
+                                              gates=True, overlap=overlap)
+    page_tokens = 512
+    P_ = page_tokens // m
+    n_blocks = steps // m + 1
+    if paged:
+        n_pg = (n_blocks + P_ - 1) // P_ + 1
+        table, n_pool = _perm(rng, Bn, n_pg)
+        out = lib.KVCache.empty(1, n_pool * P_, 448, 64, lib.KV_FP8_BF16ROPE)
+        pages = _pages(lib, table, page_tokens)
+    else:
+        out = lib.KVCache.empty(Bn, n_blocks + 2, 448, 64, lib.KV_FP8_BF16ROPE)
+        pages = None
+    dev = {k: (None if v is None else dev_in(v)) for k, v in streams.items()}
+    bias_d = None if bias is None else P.dev(bias)
+    for s in range(steps):
+        pos = np.array([s - start[b] for b in range(Bn)], np.int64)
+        tok = np.clip(pos, 0, None)
+        rows = lambda a: None if a is None else a[torch.arange(Bn), torch.from_numpy(tok).cuda()]
+        lib.v4attn_append(rows(dev["kv_cur"]), rows(dev["gate_cur"]), rows(dev["kv_prev"]),
+                          rows(dev["gate_prev"]), tail, P.dev(np.where(pos >= 0, pos, -1)),
+                          bias_d, m, out, pages=pages, nr=nd)
+    torch.cuda.synchronize()
+    back = P.kv_from_dev(out)
+    if paged:
+        back = logical_view(back, table, P_)
+    for b in range(Bn):
+        seq = {k: (None if v is None else v[b]) for k, v in streams.items()}
+        last = steps - 1 - start[b]
+        done = [(p + 1) // m - 1 for p in range(last + 1) if (p + 1) % m == 0]
+        y = np.stack([append_entry(seq, (i + 1) * m - 1, m, bias, nr=nr) for i in done])[None]
+        r = np.array(done) % back.cap
+        sub = C.KV("fp8", 448, 64, back.nope[b:b + 1, r], back.rope[b:b + 1, r],
+                   back.scale[b:b + 1, r])
+        P.check_fp8_rows(sub, y, 448)
+
+
+def test_csa_decode_1m_paged_full_size(lib):
+    # the CSA decode benchmark shape (4 sequences, 1M tokens: 262144 blocks,
+    # top-2048, 128-token window) on 8192-token pages in shuffled order:
+    # bit-equal to the contiguous calls, sampled rows against the oracle
+    c = synth.WORKLOADS[4]
+    print(f"workload 4 paged: B={c['B']} ctx={c['ctx']} pages of 8192 tokens", flush=True)
+    gd = synth.decode_inputs(4, rows=[0, c["B"] - 1])
+    Bn = c["B"]
+    src = [0] * (Bn - 1) + [1]
+    g = {k: v[src] for k, v in gd.items()}
+    cd = C.kv_encode(gd["comp"], "fp8", c["d_nope"])
+    kd = C.idx_encode(gd["keys"], "mxfp4")
+    comp = C.KV("fp8", cd.d_nope, cd.d_rope, cd.nope[src], cd.rope[src], cd.scale[src])
+    keys = C.Idx("mxfp4", 128, kd.codes[src], kd.scales[src])
+    win = C.kv_encode(g["win"], "fp8", c["d_nope"])
+    page_tokens, m = 8192, c["m"]
+    P_ = page_tokens // m
+    n_pg = comp.cap // P_
+    table, n_pool = _perm(np.random.default_rng(11), Bn, n_pg)
+    comp_d, keys_d = P.kv_to_dev(comp), P.idx_to_dev(keys)
+    pool_c = lib.KVCache(lib.KV_FP8_BF16ROPE, 448, 64, _dev_pool(comp_d.nope, table, P_, n_pool),
+                         _dev_pool(comp_d.rope, table, P_, n_pool),
+                         _dev_pool(comp_d.scale, table, P_, n_pool))
+    pool_k = lib.IdxCache(lib.IDX_MXFP4, 128, _dev_pool(keys_d.codes, table, P_, n_pool),
+                          _dev_pool(keys_d.scales, table, P_, n_pool))
+    pages = _pages(lib, table, page_tokens)
+    qi = P.dev(C.bf16_encode(g["q_idx"]).view(np.int16)).view(torch.bfloat16)
+    qb = C.bf16_encode(g["q"])
+    q = P.dev(qb.view(np.int16)).view(torch.bfloat16)
+    pos_d, w_d, win_d = P.dev(g["pos"]), P.dev(g["w"]), P.kv_to_dev(win)
+    t_pg = lib.v4attn_index_topk_paged(qi, w_d, pool_k, pages, pos_d, m, c["k"])
+    t_ct = lib.v4attn_index_topk(qi, w_d, keys_d, pos_d, m, c["k"])
+    o_pg = lib.v4attn_csa_attend_paged(q, pool_c, pages, m, t_pg, win_d, c["n_win"], pos_d, None,
+                                       512 ** -0.5)
+    o_ct = lib.v4attn_csa_attend(q, comp_d, t_ct, win_d, c["n_win"], pos_d, None, 512 ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(t_pg, t_ct), "paged top-k differs from the contiguous call"
+    assert torch.equal(o_pg, o_ct), "paged attention differs from the contiguous call"
+    tk = t_pg.cpu().numpy()
+    qi_h = C.bf16_decode(C.bf16_encode(g["q_idx"])).astype(np.float32)
+    b = Bn - 1
+    sc = index_scores(qi_h[b:b + 1], g["w"][b:b + 1],
+                      C.Idx("mxfp4", 128, keys.codes[b:b + 1], keys.scales[b:b + 1]),
+                      g["pos"][b:b + 1], m)
+    P.check_topk_row(tk[b, 0], sc[0][0], c["k"])
+    sub = lambda kv: C.KV("fp8", kv.d_nope, kv.d_rope, kv.nope[b:b + 1], kv.rope[b:b + 1],
+                          kv.scale[b:b + 1])
+    _, ref = csa_attend(qb[b:b + 1], "bf16", sub(comp), tk[b:b + 1], sub(win), c["n_win"],
+                        g["pos"][b:b + 1], None, 512 ** -0.5, "bf16")
+    P.check_out(o_pg[b:b + 1], ref)
+
+
+def test_hca_decode_1m_paged_full_size(lib):
+    # the HCA decode benchmark shape (16 sequences, 8192 entries of 128
+    # tokens) on 8192-token pages (64 entries each) in shuffled order
+    c = synth.WORKLOADS[3]
+    print(f"workload 3 paged: B={c['B']} ctx={c['ctx']} pages of 8192 tokens", flush=True)
+    gd = synth.decode_inputs(3)
+    comp = C.kv_encode(gd["comp"], "fp8", c["d_nope"])
+    win = C.kv_encode(gd["win"], "fp8", c["d_nope"])
+    page_tokens, m, Bn = 8192, c["m"], c["B"]
+    P_ = page_tokens // m
+    table, n_pool = _perm(np.random.default_rng(12), Bn, comp.cap // P_)
+    comp_d = P.kv_to_dev(comp)
+    pool_c = lib.KVCache(lib.KV_FP8_BF16ROPE, 448, 64, _dev_pool(comp_d.nope, table, P_, n_pool),
+                         _dev_pool(comp_d.rope, table, P_, n_pool),
+                         _dev_pool(comp_d.scale, table, P_, n_pool))
+    qb = C.bf16_encode(gd["q"])
+    q = P.dev(qb.view(np.int16)).view(torch.bfloat16)
+    pos_d, win_d = P.dev(gd["pos"]), P.kv_to_dev(win)
+    o_pg = lib.v4attn_hca_attend_paged(q, pool_c, _pages(lib, table, page_tokens), m, win_d,
+                                       c["n_win"], pos_d, None, 512 ** -0.5)
+    o_ct = lib.v4attn_hca_attend(q, comp_d, m, win_d, c["n_win"], pos_d, None, 512 ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(o_pg, o_ct), "paged attention differs from the contiguous call"
+    for b in (0, Bn - 1):
+        sub = lambda kv: C.KV("fp8", kv.d_nope, kv.d_rope, kv.nope[b:b + 1], kv.rope[b:b + 1],
+                              kv.scale[b:b + 1])
+        _, ref = hca_attend(qb[b:b + 1], "bf16", sub(comp), m, sub(win), c["n_win"],
+                            gd["pos"][b:b + 1], None, 512 ** -0.5, "bf16")
+        P.check_out(o_pg[b:b + 1], ref, what=f"row {b}")
