@@ -299,6 +299,90 @@ def bench_norm_rope(v4, torch, reps, ws, cc, ch, n=8):
     return {"csa_attend_nr_us": round(t_c * 1e6, 3), "hca_attend_nr_us": round(t_h * 1e6, 3)}
 
 
+def bench_paged(v4, torch, reps, ws, cc, ch, n=8, page_tokens=8192):
+    """The decode calls over paged caches ([Notes §11] classical cache in
+    blocks of raw tokens): every replica's CSA entries, indexer keys and HCA
+    entries copied into a pool whose pages are shuffled, called through the
+    block table (per-call times over all replicas, as the plain calls); and
+    one decode step of the compressor appends (CSA entries, indexer keys and
+    window token at B = 4; HCA entry and window token at B = 16), at a
+    position that completes a block of every layer."""
+    dev = "cuda"
+    gen = torch.Generator(device="cpu").manual_seed(5)
+
+    def pool_of(t, P_, perm, n_pool):
+        B, n_pg = perm.shape
+        out = torch.empty((n_pool, P_) + tuple(t.shape[2:]), dtype=t.dtype, device=dev)
+        out[perm.reshape(-1).to(dev)] = t.reshape((B * n_pg, P_) + tuple(t.shape[2:]))
+        return out.reshape((1, n_pool * P_) + tuple(t.shape[2:]))
+
+    def paged(kv, m):
+        P_ = page_tokens // m
+        B, n_pg = kv.nope.shape[0], kv.nope.shape[1] // P_
+        n_pool = B * n_pg
+        perm = torch.randperm(n_pool, generator=gen).reshape(B, n_pg)
+        tab = v4.Pages(perm.to(torch.int32).to(dev).contiguous(), page_tokens)
+        if isinstance(kv, v4.KVCache):
+            return v4.KVCache(kv.fmt, kv.d_nope, kv.d_rope, pool_of(kv.nope, P_, perm, n_pool),
+                              pool_of(kv.rope, P_, perm, n_pool),
+                              pool_of(kv.scale, P_, perm, n_pool)), tab, perm, n_pool
+        return v4.IdxCache(kv.fmt, kv.d, pool_of(kv.codes, P_, perm, n_pool),
+                           pool_of(kv.scales, P_, perm, n_pool)), tab, perm, n_pool
+
+    sc = 512 ** -0.5
+    for r in reps:
+        r.pc_comp, r.pc_tab, perm, n_pool = paged(r.c_comp, cc["m"])
+        P_ = page_tokens // cc["m"]
+        # the keys share the entries' table ([Notes §11]: one block layout)
+        r.pc_keys = v4.IdxCache(r.c_keys.fmt, 128, pool_of(r.c_keys.codes, P_, perm, n_pool),
+                                pool_of(r.c_keys.scales, P_, perm, n_pool))
+        r.ph_comp, r.ph_tab, _, _ = paged(r.h_comp, ch["m"])
+        r.pc_topk = torch.empty_like(r.c_topk)
+    torch.cuda.synchronize()
+    f_i = [(lambda r=r: v4.v4attn_index_topk_paged(r.c_qi, r.c_w, r.pc_keys, r.pc_tab, r.c_pos,
+                                                   cc["m"], cc["k"], topk=r.pc_topk,
+                                                   ws=ws["index"])) for r in reps]
+    f_c = [(lambda r=r: v4.v4attn_csa_attend_paged(r.c_q, r.pc_comp, r.pc_tab, cc["m"], r.pc_topk,
+                                                   r.c_win, cc["n_win"], r.c_pos, None, sc,
+                                                   out=r.c_out, ws=ws["csa"])) for r in reps]
+    f_h = [(lambda r=r: v4.v4attn_hca_attend_paged(r.h_q, r.ph_comp, r.ph_tab, ch["m"], r.h_win,
+                                                   ch["n_win"], r.h_pos, None, sc,
+                                                   out=r.h_out, ws=ws["hca"])) for r in reps]
+    t_i, t_c, t_h = graph_time(torch, f_i, n), graph_time(torch, f_c, n), graph_time(torch, f_h, n)
+    same = all(torch.equal(r.pc_topk, r.c_topk) for r in reps)
+    # one decode step of the compressor appends, on replica 0's paged caches
+    r = reps[0]
+    g = torch.Generator(device=dev).manual_seed(9)
+    rows = lambda B, d, s=1.0: (torch.randn(B, d, device=dev, generator=g) * s).to(torch.bfloat16)
+    D, dI = 512, 128
+    Bc, Bh = cc["B"], ch["B"]
+    c_tok = [rows(Bc, D, D ** -0.5), rows(Bc, D), rows(Bc, D, D ** -0.5), rows(Bc, D)]
+    k_tok = [rows(Bc, dI, dI ** -0.5), rows(Bc, dI), rows(Bc, dI, dI ** -0.5), rows(Bc, dI)]
+    h_tok = [rows(Bh, D, D ** -0.5), rows(Bh, D)]
+    c_state, k_state = v4.append_state(Bc, D), v4.append_state(Bc, dI)
+    h_state = v4.append_state(Bh, D)
+    c_bias = torch.randn(2 * cc["m"], D, device=dev, generator=g) * 0.5
+    k_bias = torch.randn(2 * cc["m"], dI, device=dev, generator=g) * 0.5
+    h_bias = torch.randn(ch["m"], D, device=dev, generator=g) * 0.5
+    c_pos, h_pos = r.c_pos.reshape(-1).contiguous(), r.h_pos.reshape(-1).contiguous()
+    f_a = [lambda: v4.v4attn_append(*c_tok, c_state, c_pos, c_bias, cc["m"], r.pc_comp, r.pc_tab),
+           lambda: v4.v4attn_append(*k_tok, k_state, c_pos, k_bias, cc["m"], r.pc_keys, r.pc_tab),
+           lambda: v4.v4attn_append(c_tok[0], None, None, None, None, c_pos, None, 1, r.c_win),
+           lambda: v4.v4attn_append(*h_tok, None, None, h_state, h_pos, h_bias, ch["m"], r.ph_comp,
+                                    r.ph_tab),
+           lambda: v4.v4attn_append(h_tok[0], None, None, None, None, h_pos, None, 1, r.h_win)]
+    t_a = graph_time(torch, f_a, n) * len(f_a)
+    for r in reps:
+        del r.pc_comp, r.pc_keys, r.ph_comp
+    torch.cuda.empty_cache()
+    return {"page_tokens": page_tokens, "index_topk_us": round(t_i * 1e6, 3),
+            "csa_attend_us": round(t_c * 1e6, 3), "hca_attend_us": round(t_h * 1e6, 3),
+            "topk_equal_to_contiguous": bool(same),
+            "append_step_us": round(t_a * 1e6, 3),
+            "append_step": "CSA entry + indexer key + window token at B = 4, HCA entry + "
+                           "window token at B = 16, every sequence completing a block"}
+
+
 # ---------------------------------------------------------------- prefill chunk
 
 PREFILL_WID = 5
@@ -705,6 +789,11 @@ def main():
     result["norm_rope"] = bench_norm_rope(v4, torch, reps, ws, cc, ch)
     result["norm_rope"]["csa_attend_us"] = round(t_csa_att * 1e6, 3)
     result["norm_rope"]["hca_attend_us"] = round(t_hca_call * 1e6, 3)
+    log("paged caches ...")
+    result["paged"] = bench_paged(v4, torch, reps, ws, cc, ch)
+    result["paged"]["contiguous"] = {"index_topk_us": round(t_idx * 1e6, 3),
+                                     "csa_attend_us": round(t_csa_att * 1e6, 3),
+                                     "hca_attend_us": round(t_hca_call * 1e6, 3)}
     if not args.no_prefill:
         del csa_layer, hca_layer, per_call_g, calls, reps, ws
         torch.cuda.empty_cache()

@@ -324,47 +324,43 @@ v4a_status v4attn_compress_paged(const void *kv_cur, const void *gate_cur,
                                  void *stream);
 
 /*
- * Compressor tails of the state cache: per sequence a ring of `rows` raw
- * token rows of each stream, token t at row t mod rows, device arrays
- * [B][rows][d] in the call's in_dtype (the streams as in v4attn_compress;
- * gate and previous-role rings only where those inputs exist).
- */
-typedef struct {
-  void *kv_cur;
-  void *gate_cur;
-  void *kv_prev;
-  void *gate_prev;
-  int32_t rows;
-  int32_t _pad;
-} v4a_tail;
-
-/*
  * v4attn_append -- the decode-time compressor step ([Notes §11] state cache):
  * one new token per sequence.  For every b with p = pos[b] >= 0, the token's
  * rows kv_cur[b], gate_cur[b], kv_prev[b], gate_prev[b] ([B][d] each, the
  * streams of v4attn_compress; gates may be NULL = 0, kv_prev NULL = no
- * overlap) are written to the tail rings at row p mod rows; if p + 1 is a
- * multiple of m, the token completes block i = (p + 1) / m - 1, which is
- * pooled exactly as v4attn_compress would pool it (current rows: tokens
- * i*m .. p; previous-role rows: tokens (i-1)*m .. i*m - 1, none for block 0)
- * and stored -- with nr, after the entry RMSNorm and RoPE -- at ring row
- * i mod cap (pages NULL) or at its pool row (pages non-NULL; a block beyond
- * the sequence's max_pages * P entries is not stored).  pos[b] < 0 leaves
- * sequence b untouched.  The tails must hold the block's earlier tokens:
- * rows >= 2m with overlap, >= m without; with m == 1 and no overlap the tail
- * may be NULL (the token is the whole block: the window ring is filled so).
- * Calls for one sequence must come in position order, and every position
- * must be appended once (the tail rings hold what earlier calls wrote).
+ * overlap) are folded into the sequence's pooling state; if p + 1 is a
+ * multiple of m, the token completes block i = (p + 1) / m - 1, whose entry --
+ * the value v4attn_compress gives that block (current rows: tokens i*m .. p;
+ * previous-role rows: tokens (i-1)*m .. i*m - 1, none for block 0) -- is
+ * stored, with nr after the entry RMSNorm and RoPE, at ring row i mod cap
+ * (pages NULL) or at its pool row (pages non-NULL; a block beyond the
+ * sequence's max_pages * P entries is not stored).  pos[b] < 0 leaves
+ * sequence b untouched.
  *
- *   tail     host v4a_tail (device arrays inside), or NULL as above
+ * The state cache of the compressor holds, instead of the raw rows of the
+ * unfinished block, their running softmax pooling: state is device f32
+ * [B][2][3][d] -- for the block of the current token and for the
+ * previous-role part of the next block, per channel the running maximum of
+ * the logits, the denominator and the numerator.  A step folds one token in,
+ * and a block completes with one division (O(1) work per token).  The state
+ * needs no initialisation: a token at slot 0 of its block resets the parts
+ * it starts.  Calls for one sequence must come in position order with every
+ * position once, and a sequence's first call must be at slot 0 of a block.
+ * With out NULL the call only updates the state (nothing is stored; out_kind,
+ * pages and nr are ignored): to continue after a chunked prefill of tokens
+ * 0 .. P-1 (v4attn_compress over its complete blocks), first append tokens
+ * max(0, m * (floor(P / m) - 1)) .. m * floor(P / m) - 1 with out NULL, then
+ * every later token normally.  state may be NULL only for m == 1 without
+ * overlap (the token is the whole block: the window ring is filled so).
+ *
+ *   state    device f32 [B][2][3][d], or NULL as above
  *   pos      int64 [B]
- *   out_kind, out, nr  as v4attn_compress_nr / _paged
- * Errors: as v4attn_compress_paged; V4A_ERR_INVALID for a missing or short
- * tail (or a gate ring missing where its gate input exists).
+ *   out_kind, out, nr  as v4attn_compress_nr / _paged; out may be NULL
+ * Errors: as v4attn_compress_paged; V4A_ERR_INVALID for a missing state.
  */
 v4a_status v4attn_append(const void *kv_cur, const void *gate_cur,
                          const void *kv_prev, const void *gate_prev,
-                         const v4a_tail *tail, const int64_t *pos,
+                         float *state, const int64_t *pos,
                          const float *pos_bias, int32_t in_dtype,
                          int32_t B, int32_t d, int32_t m,
                          int32_t out_kind, const void *out,

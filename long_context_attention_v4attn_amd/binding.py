@@ -46,12 +46,6 @@ class _Pages(ctypes.Structure):
                 ("page_tokens", ctypes.c_int32)]
 
 
-class _Tail(ctypes.Structure):
-    _fields_ = [("kv_cur", ctypes.c_void_p), ("gate_cur", ctypes.c_void_p),
-                ("kv_prev", ctypes.c_void_p), ("gate_prev", ctypes.c_void_p),
-                ("rows", ctypes.c_int32), ("_pad", ctypes.c_int32)]
-
-
 @dataclass
 class NormRope:
     """[Notes §9] query / KV-entry RMSNorm and partial RoPE: gamma f32 [D]
@@ -396,30 +390,10 @@ class Pages:
         return _Pages(self.table.data_ptr(), self.table.shape[1], int(self.page_tokens))
 
 
-@dataclass
-class Tail:
-    """Compressor tails of the state cache: rings [B][rows][d] of raw token
-    rows per stream (token t at row t mod rows), in the tokens' dtype."""
-    kv_cur: torch.Tensor
-    gate_cur: torch.Tensor = None
-    kv_prev: torch.Tensor = None
-    gate_prev: torch.Tensor = None
-
-    @staticmethod
-    def empty(B, rows, d, dtype, gates=True, overlap=False, device="cuda"):
-        z = lambda: torch.zeros(B, rows, d, dtype=dtype, device=device)
-        return Tail(z(), z() if gates else None, z() if overlap else None,
-                    z() if gates and overlap else None)
-
-    @property
-    def rows(self):
-        return self.kv_cur.shape[1]
-
-    def c_struct(self):
-        _need_cuda(self.kv_cur, self.gate_cur, self.kv_prev, self.gate_prev)
-        return _Tail(self.kv_cur.data_ptr(), *[0 if t is None else t.data_ptr()
-                                                 for t in (self.gate_cur, self.kv_prev,
-                                                           self.gate_prev)], self.rows, 0)
+def append_state(B, d, device="cuda"):
+    """Pooling state of v4attn_append: f32 [B][2][3][d] (no initialisation
+    needed: a sequence's first token at slot 0 of a block resets it)."""
+    return torch.empty(B, 2, 3, d, dtype=torch.float32, device=device)
 
 
 def _byref(st):
@@ -442,21 +416,23 @@ def v4attn_compress_paged(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, m, t0,
     return out
 
 
-def v4attn_append(kv_cur, gate_cur, kv_prev, gate_prev, tail, pos, pos_bias, m, out, pages=None,
+def v4attn_append(kv_cur, gate_cur, kv_prev, gate_prev, state, pos, pos_bias, m, out, pages=None,
                   nr=None, stream=None):
     """One decode step of the compressor: token rows [B][d] at positions pos
-    [B] join the tails (Tail or None); completed blocks go to `out`."""
+    [B] fold into `state` (append_state, or None for m = 1 without overlap);
+    completed blocks go to `out` (None: the state alone is updated)."""
     lib = load()
-    _need_cuda(kv_cur, gate_cur, kv_prev, gate_prev, pos, pos_bias)
+    _need_cuda(kv_cur, gate_cur, kv_prev, gate_prev, state, pos, pos_bias)
     B, d = kv_cur.shape
+    if state is not None and (state.dtype != torch.float32 or state.numel() < B * 6 * d):
+        raise V4AttnError("append state must be f32 [B][2][3][d]")
     kind = OUT_KV if isinstance(out, KVCache) else OUT_IDX
-    st = out.c_struct()
-    ts = None if tail is None else tail.c_struct()
+    st = None if out is None else out.c_struct()
     ps = None if pages is None else pages.c_struct()
     ns = None if nr is None else nr.c_struct()
     s = lib.v4attn_append(_ptr(kv_cur), _ptr(gate_cur), _ptr(kv_prev), _ptr(gate_prev),
-                          _byref(ts), _ptr(pos), _ptr(pos_bias), _dtype_code(kv_cur), B, d, m,
-                          kind, ctypes.byref(st), _byref(ps), _byref(ns), _stream(stream))
+                          _ptr(state), _ptr(pos), _ptr(pos_bias), _dtype_code(kv_cur), B, d, m,
+                          kind, _byref(st), _byref(ps), _byref(ns), _stream(stream))
     _check(s, "v4attn_append")
     return out
 

@@ -157,8 +157,9 @@ static v4a_status compress_impl(const void* kv_cur, const void* gate_cur, const 
                                 int32_t B, int32_t T, int32_t d, int32_t m, int64_t t0,
                                 int32_t out_kind, const void* out, const v4a_norm_rope* nr,
                                 void* stream, const v4a_pages* pages = nullptr,
-                                const int64_t* apos = nullptr, const v4a_tail* tail = nullptr) {
-  if (!kv_cur || !out || B < 0 || T < 0 || d < 1 || t0 < 0) return V4A_ERR_INVALID;
+                                const int64_t* apos = nullptr, float* state = nullptr) {
+  if (!kv_cur || B < 0 || T < 0 || d < 1 || t0 < 0) return V4A_ERR_INVALID;
+  if (!out && !apos) return V4A_ERR_INVALID;
   if (nr && !(nr->eps >= 0.0f)) return V4A_ERR_INVALID;
   if (nr && out_kind != V4A_OUT_KV) return V4A_ERR_UNSUPPORTED;
   if (in_dtype != V4A_F32 && in_dtype != V4A_BF16) return V4A_ERR_INVALID;
@@ -180,7 +181,11 @@ static v4a_status compress_impl(const void* kv_cur, const void* gate_cur, const 
   a.m = m;
   a.t0 = t0;
   a.out_kind = out_kind;
-  if (out_kind == V4A_OUT_KV) {
+  if (!out) {
+    // a state-only append: nothing is stored
+    a.no_store = 1;
+    a.d_nope = d;
+  } else if (out_kind == V4A_OUT_KV) {
     const v4a_kv* kv = (const v4a_kv*)out;
     if (!valid_kv(kv) || kv->d_nope + kv->d_rope != d) return V4A_ERR_INVALID;
     if (kv->fmt == V4A_KV_FP8_BF16ROPE && kv->d_nope % 32 != 0) return V4A_ERR_UNSUPPORTED;
@@ -212,7 +217,7 @@ static v4a_status compress_impl(const void* kv_cur, const void* gate_cur, const 
   } else {
     return V4A_ERR_INVALID;
   }
-  if (pages) {
+  if (pages && out) {
     int64_t lcap = 0;
     v4a_status s = check_pages(pages, m, a.cap, 1, &a.pg, &lcap);
     if (s != V4A_OK) return s;
@@ -220,24 +225,10 @@ static v4a_status compress_impl(const void* kv_cur, const void* gate_cur, const 
     a.cap = lcap;
   }
   if (apos) {
-    // decode-time append: one token per sequence, pooled from the tails
-    const bool need_tail = m > 1 || kv_prev;
+    // decode-time append: one token per sequence folded into the state
+    if (!state && (m > 1 || kv_prev)) return V4A_ERR_INVALID;
     a.apos = apos;
-    if (tail) {
-      a.t_kv_cur = tail->kv_cur;
-      a.t_gate_cur = tail->gate_cur;
-      a.t_kv_prev = tail->kv_prev;
-      a.t_gate_prev = tail->gate_prev;
-      a.t_rows = tail->rows;
-    }
-    if (need_tail) {
-      if (!tail || tail->rows < (kv_prev ? 2 * m : m) || !tail->kv_cur) return V4A_ERR_INVALID;
-      if ((gate_cur && !tail->gate_cur) || (kv_prev && !tail->kv_prev) ||
-          (gate_prev && !tail->gate_prev))
-        return V4A_ERR_INVALID;
-    } else if (tail && tail->rows < 1) {
-      return V4A_ERR_INVALID;
-    }
+    a.state = state;
     if (B == 0) return V4A_OK;
     return hip_status(launch_compress(a, (hipStream_t)stream));
   }
@@ -256,7 +247,7 @@ v4a_status v4attn_compress_paged(const void* kv_cur, const void* gate_cur, const
 }
 
 v4a_status v4attn_append(const void* kv_cur, const void* gate_cur, const void* kv_prev,
-                         const void* gate_prev, const v4a_tail* tail, const int64_t* pos,
+                         const void* gate_prev, float* state, const int64_t* pos,
                          const float* pos_bias, int32_t in_dtype, int32_t B, int32_t d, int32_t m,
                          int32_t out_kind, const void* out, const v4a_pages* pages,
                          const v4a_norm_rope* nr, void* stream) {
@@ -264,7 +255,7 @@ v4a_status v4attn_append(const void* kv_cur, const void* gate_cur, const void* k
   // T = m, t0 = 0 pass the shape checks of the chunked call; the append
   // kernel takes its blocks from pos
   return compress_impl(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, in_dtype, B, m, d, m, 0,
-                       out_kind, out, nr, stream, pages, pos, tail);
+                       out_kind, out, nr, stream, pages, pos, state);
 }
 
 v4a_status v4attn_compress(const void* kv_cur, const void* gate_cur, const void* kv_prev,

@@ -17,6 +17,13 @@
 //              (correctly rounded), e4m3 = RNE(clamp(y/s)); RoPE tail -> bf16.
 //   MXFP4 key: 32 consecutive channels = 32 consecutive lanes; lane-shuffle
 //              max -> e8m0 exponent, e2m1 = RNE(y * 2^-e); two nibbles a byte.
+// k_append: a decode step ([Notes §11] state cache), one workgroup per
+//   sequence.  The state holds, per channel, the running online-softmax
+//   triple (max, denominator, numerator) of the block being pooled and of the
+//   previous-role part of the next block, so a step folds in one token's rows
+//   and a block completes with one divide: O(1) work per step, and the same
+//   sequence of operations as k_compress (previous-role slots in order, then
+//   current ones), hence the same values.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,111 +36,39 @@ __device__ __forceinline__ float ld(const void* p, int bf16, size_t i) {
   return load_as_f32(p, bf16, i);
 }
 
-// kAppend: a decode step ([Notes §11] state cache): one workgroup per
-// sequence b and one new token at position p = apos[b].  The token's rows
-// join the compressor tails (ring rows p mod t_rows); when the token completes
-// block i = (p + 1) / m - 1, the block is pooled like any other: its current
-// rows are tail rows except the token itself (read from the input), its
-// previous-role rows (tokens of block i - 1) are tail rows.  With t_rows >= 2m
-// (>= m without overlap) no row read here is the row the token writes.
-template <bool kAppend>
-__global__ void __launch_bounds__(kCompThreads) k_compress(CompressArgs a) {
-  __shared__ float red[kCompThreads / 64];
+// The input dtype as a template parameter: no branch around the load.
+template <bool kBf16>
+__device__ __forceinline__ float ldt(const void* p, size_t i) {
+  if (kBf16) return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+  return ((const float*)p)[i];
+}
+
+// Stands in for an absent gate, bias or state row (zeros; any dtype, d <= 1024).
+__device__ float g_zero_row[kMaxChan * kCompThreads];
+
+// Online softmax step: fold slot (logit z, value v) into (mx, den, num).
+// Branch-free; exp(0) = 1 exactly, so this is the same arithmetic as
+// rescaling only when the maximum moves.
+struct Acc {
+  float mx, den, num;
+};
+__device__ __forceinline__ void acc_add(Acc& s, float z, float v) {
+  const float mn = fmaxf(s.mx, z);
+  const float sc = expf(s.mx - mn);        // mx = -inf -> 0
+  const float e = expf(z - mn);
+  s.den = s.den * sc + e;
+  s.num = s.num * sc + e * v;
+  s.mx = mn;
+}
+
+// Epilogue shared by both kernels: the pooled row y (channels tid + 256 q) of
+// block gblk of sequence b -> optional entry RMSNorm / RoPE -> the cache
+// format, at the block's ring row or pool row.  Every thread of the
+// workgroup calls it (it synchronises).
+__device__ __forceinline__ void finish_entry(const CompressArgs& a, float (&y)[kMaxChan], int b,
+                                             int64_t gblk, float* red) {
   const int m = a.m;
   const int d = a.d;
-  const bool overlap = a.kv_prev != nullptr;
-  int b, j = 0;
-  int64_t gblk, p = 0;
-  if (kAppend) {
-    b = blockIdx.x;
-    p = a.apos[b];
-    if (p < 0) return;
-    const size_t di = ((size_t)b * a.t_rows + (size_t)(p % a.t_rows)) * d;
-    const size_t si = (size_t)b * d;
-    auto keep = [&](void* dst, const void* src) {
-      if (!dst || !src) return;
-      for (int c = threadIdx.x; c < d; c += kCompThreads) {
-        if (a.in_bf16) ((uint16_t*)dst)[di + c] = ((const uint16_t*)src)[si + c];
-        else ((float*)dst)[di + c] = ((const float*)src)[si + c];
-      }
-    };
-    keep(a.t_kv_cur, a.kv_cur);
-    keep(a.t_gate_cur, a.gate_cur);
-    keep(a.t_kv_prev, a.kv_prev);
-    keep(a.t_gate_prev, a.gate_prev);
-    if ((p + 1) % m != 0) return;          // uniform: the block is not complete
-    gblk = (p + 1) / m - 1;
-    // a block past the sequence's pages is not stored
-    if (a.pg.tab && (gblk >> a.pg.psh) >= a.pg.tab_ld) return;
-  } else {
-    j = blockIdx.x;                        // block within the call
-    b = blockIdx.y;
-    gblk = a.t0 / m + j;                   // global block index
-    // a call that produces more than cap ring entries keeps the last cap of
-    // them: an earlier block whose ring row a later block of this call also
-    // writes is skipped (concurrent writes to one row would race)
-    if (!a.pg.tab && (int64_t)(a.T / m) - j > a.cap) return;
-  }
-  const bool has_prev = overlap && gblk > 0;
-  const int64_t rbase = ((int64_t)b * a.T + (int64_t)j * m) * d;   // row m*j of this call
-  // slot sources: the call's rows, or (append) tail rows and the token
-  auto prev_idx = [&](int u, int c) -> size_t {
-    if (!kAppend) return rbase + (int64_t)u * d + c;
-    const int64_t t = (gblk - 1) * m + u;
-    return ((size_t)b * a.t_rows + (size_t)(t % a.t_rows)) * d + c;
-  };
-  const void* kv_prev = kAppend ? a.t_kv_prev : a.kv_prev;
-  const void* gate_prev = kAppend ? (a.gate_prev ? a.t_gate_prev : nullptr) : a.gate_prev;
-
-  float y[kMaxChan];
-#pragma unroll
-  for (int q = 0; q < kMaxChan; q++) {
-    const int c = threadIdx.x + q * kCompThreads;
-    y[q] = 0.0f;
-    if (c >= d) continue;
-    float mx = -INFINITY, den = 0.0f, num = 0.0f;
-    auto add = [&](float z, float v) {
-      if (z > mx) {
-        float sc = expf(mx - z);           // mx = -inf -> 0
-        den = den * sc + 1.0f;
-        num = num * sc + v;
-        mx = z;
-      } else {
-        float e = expf(z - mx);
-        den += e;
-        num += e * v;
-      }
-    };
-    if (has_prev) {
-      for (int u = 0; u < m; u++) {
-        size_t idx = prev_idx(u, c);
-        float z = (gate_prev ? ld(gate_prev, a.in_bf16, idx) : 0.0f) +
-                  (a.bias ? a.bias[(size_t)u * d + c] : 0.0f);
-        add(z, ld(kv_prev, a.in_bf16, idx));
-      }
-    }
-    const int boff = overlap ? m : 0;
-    for (int u = 0; u < m; u++) {
-      const void* kvp = a.kv_cur;
-      const void* gp = a.gate_cur;
-      size_t idx = rbase + (int64_t)u * d + c;
-      if (kAppend) {
-        const int64_t t = gblk * m + u;
-        if (t == p) {
-          idx = (size_t)b * d + c;
-        } else {
-          kvp = a.t_kv_cur;
-          gp = a.gate_cur ? a.t_gate_cur : nullptr;
-          idx = ((size_t)b * a.t_rows + (size_t)(t % a.t_rows)) * d + c;
-        }
-      }
-      float z = (gp ? ld(gp, a.in_bf16, idx) : 0.0f) +
-                (a.bias ? a.bias[(size_t)(boff + u) * d + c] : 0.0f);
-      add(z, ld(kvp, a.in_bf16, idx));
-    }
-    y[q] = num / den;
-  }
-
   const int64_t orow = a.pg.tab ? page_row(a.pg, b, gblk) : (int64_t)b * a.cap + (gblk % a.cap);
   if (a.out_kind == 0 && (a.nr_gamma || a.nr_inv)) {
     // [Notes §9] KV-entry RMSNorm over the d channels, then RoPE of the last
@@ -240,15 +175,120 @@ __global__ void __launch_bounds__(kCompThreads) k_compress(CompressArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(kCompThreads) k_compress(CompressArgs a) {
+  __shared__ float red[kCompThreads / 64];
+  const int j = blockIdx.x;                // block within the call
+  const int b = blockIdx.y;
+  const int m = a.m;
+  const int d = a.d;
+  const bool overlap = a.kv_prev != nullptr;
+  const int64_t gblk = a.t0 / m + j;       // global block index
+  // a call that produces more than cap ring entries keeps the last cap of
+  // them: an earlier block whose ring row a later block of this call also
+  // writes is skipped (concurrent writes to one row would race)
+  if (!a.pg.tab && (int64_t)(a.T / m) - j > a.cap) return;
+  const bool has_prev = overlap && gblk > 0;
+  const int64_t rbase = ((int64_t)b * a.T + (int64_t)j * m) * d;   // row m*j of this call
+
+  float y[kMaxChan];
+#pragma unroll
+  for (int q = 0; q < kMaxChan; q++) {
+    const int c = threadIdx.x + q * kCompThreads;
+    y[q] = 0.0f;
+    if (c >= d) continue;
+    Acc s{-INFINITY, 0.0f, 0.0f};
+    if (has_prev) {
+      for (int u = 0; u < m; u++) {
+        size_t idx = rbase + (int64_t)u * d + c;
+        float z = (a.gate_prev ? ld(a.gate_prev, a.in_bf16, idx) : 0.0f) +
+                  (a.bias ? a.bias[(size_t)u * d + c] : 0.0f);
+        acc_add(s, z, ld(a.kv_prev, a.in_bf16, idx));
+      }
+    }
+    const int boff = overlap ? m : 0;
+    for (int u = 0; u < m; u++) {
+      size_t idx = rbase + (int64_t)u * d + c;
+      float z = (a.gate_cur ? ld(a.gate_cur, a.in_bf16, idx) : 0.0f) +
+                (a.bias ? a.bias[(size_t)(boff + u) * d + c] : 0.0f);
+      acc_add(s, z, ld(a.kv_cur, a.in_bf16, idx));
+    }
+    y[q] = s.num / s.den;
+  }
+  finish_entry(a, y, b, gblk, red);
+}
+
+// State of sequence b: float [2][3][d] = (accumulator k, field: max,
+// denominator, numerator, channel); accumulator 0 pools the block of the
+// current token, accumulator 1 the previous-role rows of that block (they
+// belong to the next block's entry).
+template <bool kBf16>
+__global__ void __launch_bounds__(kCompThreads) k_append(CompressArgs a) {
+  __shared__ float red[kCompThreads / 64];
+  const int b = blockIdx.x;
+  const int64_t p = a.apos[b];
+  if (p < 0) return;                       // uniform: the sequence is idle
+  const int m = a.m;
+  const int d = a.d;
+  const bool overlap = a.kv_prev != nullptr;
+  const int u = (int)(p & (m - 1));        // slot of the token in its block (m = 2^k)
+  const int64_t blk = p / m;
+  const int boff = overlap ? m : 0;
+  float* st = a.state ? a.state + (size_t)b * 6 * d : nullptr;
+  const float* sr = st ? st : g_zero_row;  // read side (zeros without a state)
+  const int sd = st ? d : 0;
+  float y[kMaxChan];
+#pragma unroll
+  for (int q = 0; q < kMaxChan; q++) {
+    const int c = threadIdx.x + q * kCompThreads;
+    y[q] = 0.0f;
+    if (c >= d) continue;
+    // every load first, unconditionally (absent inputs read the zero row)
+    const size_t ti = (size_t)b * d + c;
+    const float kv = ldt<kBf16>(a.kv_cur, ti);
+    const float g = a.gate_cur ? ldt<kBf16>(a.gate_cur, ti) : ldt<kBf16>(g_zero_row, c);
+    const float bc = (a.bias ? a.bias + (size_t)(boff + u) * d : g_zero_row)[c];
+    const float kvp = ldt<kBf16>(overlap ? a.kv_prev : g_zero_row, overlap ? ti : (size_t)c);
+    const float gpv = ldt<kBf16>(a.gate_prev ? a.gate_prev : g_zero_row, a.gate_prev ? ti : (size_t)c);
+    const float bp = (a.bias && overlap ? a.bias + (size_t)u * d : g_zero_row)[c];
+    Acc s0{sr[c], sr[sd + c], sr[2 * sd + c]};
+    Acc s1{sr[3 * sd + c], sr[4 * sd + c], sr[5 * sd + c]};
+    if (u == 0) {
+      // a new block: its entry starts from the previous-role rows pooled
+      // during the block before (block 0 has none)
+      if (!(overlap && blk > 0)) s1 = Acc{-INFINITY, 0.0f, 0.0f};
+      s0 = s1;
+      s1 = Acc{-INFINITY, 0.0f, 0.0f};
+    }
+    acc_add(s0, g + bc, kv);
+    if (overlap) acc_add(s1, gpv + bp, kvp);
+    y[q] = s0.num / s0.den;
+    if (st) {
+      st[c] = s0.mx;
+      st[d + c] = s0.den;
+      st[2 * d + c] = s0.num;
+      st[3 * d + c] = s1.mx;
+      st[4 * d + c] = s1.den;
+      st[5 * d + c] = s1.num;
+    }
+  }
+  if (u != m - 1 || a.no_store) return;    // uniform: no entry to store
+  // a block past the sequence's pages is not stored
+  if (a.pg.tab && (blk >> a.pg.psh) >= a.pg.tab_ld) return;
+  finish_entry(a, y, b, blk, red);
+}
+
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   if (a.apos) {
-    hipLaunchKernelGGL(k_compress<true>, dim3(a.B), dim3(kCompThreads), 0, st, a);
+    if (a.in_bf16)
+      hipLaunchKernelGGL(k_append<true>, dim3(a.B), dim3(kCompThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_append<false>, dim3(a.B), dim3(kCompThreads), 0, st, a);
     return hipGetLastError();
   }
   const int nb = a.T / a.m;
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_compress<false>, dim3(nb, a.B), dim3(kCompThreads), 0, st, a);
+  hipLaunchKernelGGL(k_compress, dim3(nb, a.B), dim3(kCompThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -48,15 +48,10 @@ struct CompressArgs {
   float nr_eps;
   Pages pg;                  // paged output: row = page_row(block), no ring
   // decode-time append (apos non-null): one token per sequence, kv_* / gate_*
-  // are [B][d]; the token's rows go to the tails (t_* [B][t_rows][d], token t
-  // at row t mod t_rows) and a block that the token completes is pooled from
-  // the tails plus the token itself
+  // are [B][d]; state [B][2][3][d] holds the running pooling of each sequence
   const int64_t* apos;       // [B] the token's position (< 0: sequence idle)
-  void* t_kv_cur;
-  void* t_gate_cur;
-  void* t_kv_prev;
-  void* t_gate_prev;
-  int t_rows;
+  float* state;              // null only for m == 1 without overlap
+  int no_store;              // 1: update the state only (no output cache)
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
 

@@ -22,12 +22,12 @@ Readings (the pages give no layout; each is listed in the design notes):
     use the same table as its entries;
   * everything the attention and the indexer compute is unchanged: they act
     on the logical cache read through the table;
-  * the compressor tail of a sequence is a ring of S raw-token rows per
-    stream (token t at row t mod S); at a decode step of position p the
-    token's rows join the tail and, when p + 1 is a multiple of m, block
-    (p + 1) / m - 1 is complete and is pooled by the compressor's own
-    definition over its slots (its previous-role rows are those of block
-    i - 1, still in the tail when S >= 2m);
+  * what the compressor keeps of the unfinished block is not fixed by the
+    pages (they name the uncompressed tail); the result is: at a decode step
+    of position p, when p + 1 is a multiple of m, block (p + 1) / m - 1 is
+    complete and its entry is the compressor's own definition over its slots
+    (its previous-role rows are those of block i - 1), whatever the state
+    holds in between;
   * the sliding-window part of the state cache is the window ring itself
     (token t at row t mod cap), written at each step as a rate-1 compressor.
 """

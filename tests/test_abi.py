@@ -151,12 +151,6 @@ class _Pg(ctypes.Structure):
                 ("page_tokens", ctypes.c_int32)]
 
 
-class _Tail(ctypes.Structure):
-    _fields_ = [("kv_cur", ctypes.c_void_p), ("gate_cur", ctypes.c_void_p),
-                ("kv_prev", ctypes.c_void_p), ("gate_prev", ctypes.c_void_p),
-                ("rows", ctypes.c_int32), ("_pad", ctypes.c_int32)]
-
-
 def test_paged_variants_rejected_on_host(clib):
     r = ctypes.byref
     f = ctypes.c_float(0.1)
@@ -195,15 +189,13 @@ def test_paged_variants_rejected_on_host(clib):
     # compress: the call's blocks past the sequence's pages
     assert clib.v4attn_compress_paged(FAKE, None, None, None, None, 0, 1, 4 * 1100, 512, 4, 0, 0,
                                       r(kv), r(pg), None, None) == -1
-    # append: a rate above 1 needs tails of >= m rows (>= 2m with overlap),
-    # with a gate ring where gates are given
-    def app(tail, m=4, kv_prev=None, gate=None):
-        return clib.v4attn_append(FAKE, gate, kv_prev, None, r(tail) if tail else None, FAKE, None,
-                                  0, 2, 512, m, 0, r(kv), r(pg), None, None)
+    # append: a rate above 1 (or overlap) needs the pooling state
+    def app(state, m=4, kv_prev=None):
+        return clib.v4attn_append(FAKE, None, kv_prev, None, state, FAKE, None, 0, 2, 512, m, 0,
+                                  r(kv), r(pg), None, None)
     assert app(None) == -1
-    assert app(_Tail(0x7000, None, 0x7100, None, 7, 0), kv_prev=FAKE) == -1
-    assert app(_Tail(0x7000, None, None, None, 4, 0), gate=FAKE) == -1
-    assert app(_Tail(0x7000, None, None, None, 4, 0), m=256) == -2   # above the page size
+    assert app(None, m=1, kv_prev=FAKE) == -1
+    assert app(FAKE, m=256) == -2                                   # above the page size
     assert clib.v4attn_append(FAKE, None, None, None, None, None, None, 0, 2, 512, 1, 0, r(kv),
                               None, None, None) == -1                 # no positions
 

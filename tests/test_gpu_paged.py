@@ -3,7 +3,8 @@ append ([Notes §11] KV cache table) against the oracle: the indexer and both
 attention calls over pools whose pages are shuffled (results against the
 oracle on the table's logical view, and bit-equal to the contiguous calls on
 the same entries), the chunked compressor writing through the table, and
-decode steps that fill the compressor tails and the window ring."""
+decode steps that fold tokens into the compressor's pooling state and fill
+the window ring."""
 
 import numpy as np
 import pytest
@@ -174,18 +175,23 @@ def test_compress_paged(lib, m, overlap, out):
         P.check_mxfp4_rows(C.Idx("mxfp4", d, lv.codes[:, rows], lv.scales[:, rows]), y)
 
 
-@pytest.mark.parametrize("m,overlap,paged,with_nr,dtype", [(4, True, True, False, "f32"),
-                                                           (4, True, False, True, "bf16"),
-                                                           (16, False, True, False, "f32"),
-                                                           (1, False, False, False, "bf16")])
-def test_append_decode_steps(lib, m, overlap, paged, with_nr, dtype):
+@pytest.mark.parametrize("m,overlap,paged,with_nr,dtype,prefill", [
+    (4, True, True, False, "f32", 0), (4, True, False, True, "bf16", 0),
+    (16, False, True, False, "f32", 0), (1, False, False, False, "bf16", 0),
+    (128, False, True, False, "bf16", 0), (4, True, True, False, "bf16", 24),
+    (16, False, False, False, "f32", 40)])
+def test_append_decode_steps(lib, m, overlap, paged, with_nr, dtype, prefill):
     # sequences start at different steps (idle before: position -1), so blocks
     # complete at different calls; every completed block is compared with the
-    # compressor's definition over the same token stream
-    print(f"append m={m} overlap={overlap} paged={paged} nr={with_nr} {dtype}", flush=True)
-    rng = np.random.default_rng(3 * m + paged)
-    Bn, d, steps = 3, 512, 70
-    start = [0, 5, 11]
+    # compressor's definition over the same token stream.  With `prefill`, the
+    # first tokens go through the chunked compressor, then the last complete
+    # block's tokens are appended again, state only, before the decode steps.
+    print(f"append m={m} overlap={overlap} paged={paged} nr={with_nr} {dtype} prefill={prefill}",
+          flush=True)
+    rng = np.random.default_rng(3 * m + paged + prefill)
+    Bn, d = 3, 512
+    steps = 300 if m == 128 else 70
+    start = [0, 5, 11] if not prefill else [0, 0, 0]
     T = steps
     st = synth.compress_inputs(7, Bn, T, d, max(m, 1), overlap, 0)
     to_in = (lambda a: C.bf16_decode(C.bf16_encode(a)).astype(np.float32)) if dtype == "bf16" \
@@ -196,9 +202,7 @@ def test_append_decode_steps(lib, m, overlap, paged, with_nr, dtype):
     bias = None if m == 1 else st["bias"]
     nr, nd = _nr(lib, rng) if with_nr else (None, None)
     dev_in = (lambda a: P.bf16_dev(a)) if dtype == "bf16" else (lambda a: P.dev(a))
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    tail = None if m == 1 else lib.Tail.empty(Bn, 2 * m if overlap else m, d, tdt,
-                                              gates=True, overlap=overlap)
+    state = None if (m == 1 and not overlap) else lib.append_state(Bn, d)
     page_tokens = 512
     P_ = page_tokens // m
     n_blocks = steps // m + 1
@@ -212,12 +216,38 @@ def test_append_decode_steps(lib, m, overlap, paged, with_nr, dtype):
         pages = None
     dev = {k: (None if v is None else dev_in(v)) for k, v in streams.items()}
     bias_d = None if bias is None else P.dev(bias)
-    for s in range(steps):
+    first = 0
+    if prefill:
+        # the chunked call: tokens 0 .. prefill-1 (previous-role rows shifted
+        # by m, as that call takes them), into the same cache
+        # (its complete blocks; a partial last block is appended below)
+        P0 = m * (prefill // m)
+        pv = lambda a: None if a is None else torch.cat(
+            [torch.zeros_like(a[:, :m]), a[:, :P0 - m]], 1).contiguous()
+        cut = lambda a: None if a is None else a[:, :P0].contiguous()
+        args = (cut(dev["kv_cur"]), cut(dev["gate_cur"]), pv(dev["kv_prev"]), pv(dev["gate_prev"]),
+                bias_d, m, 0, out)
+        if paged:
+            lib.v4attn_compress_paged(*args, pages, nr=nd)
+        elif nd is not None:
+            lib.v4attn_compress_nr(*args, nd)
+        else:
+            lib.v4attn_compress(*args)
+        # rebuild the state from the last complete block: state only
+        for s in range(max(0, m * (prefill // m - 1)), m * (prefill // m)):
+            pos = torch.full((Bn,), s, dtype=torch.int64, device="cuda")
+            lib.v4attn_append(dev["kv_cur"][:, s].contiguous(),
+                              None if dev["gate_cur"] is None else dev["gate_cur"][:, s].contiguous(),
+                              None if dev["kv_prev"] is None else dev["kv_prev"][:, s].contiguous(),
+                              None if dev["gate_prev"] is None else dev["gate_prev"][:, s].contiguous(),
+                              state, pos, bias_d, m, None)
+        first = m * (prefill // m)
+    for s in range(first, steps):
         pos = np.array([s - start[b] for b in range(Bn)], np.int64)
         tok = np.clip(pos, 0, None)
         rows = lambda a: None if a is None else a[torch.arange(Bn), torch.from_numpy(tok).cuda()]
         lib.v4attn_append(rows(dev["kv_cur"]), rows(dev["gate_cur"]), rows(dev["kv_prev"]),
-                          rows(dev["gate_prev"]), tail, P.dev(np.where(pos >= 0, pos, -1)),
+                          rows(dev["gate_prev"]), state, P.dev(np.where(pos >= 0, pos, -1)),
                           bias_d, m, out, pages=pages, nr=nd)
     torch.cuda.synchronize()
     back = P.kv_from_dev(out)
