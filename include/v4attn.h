@@ -19,7 +19,9 @@
  *    `stream` (a hipStream_t; NULL = the null stream) and the call returns
  *    without synchronising.  Device faults surface at the caller's next sync.
  *  - Arguments are validated on the host before anything is enqueued; an
- *    error return leaves no side effects.
+ *    error return leaves no side effects.  A call with nothing to do (B == 0
+ *    or Q == 0; T == 0 for the chunked compressor) returns V4A_OK without
+ *    looking at its data pointers, which may then be NULL.
  *  - Positions are absolute 0-based token indices.  Compressed block i covers
  *    tokens [m*i, m*(i+1)).  A query at position p sees the n_vis(p) =
  *    min(floor((p+1)/m), cap) blocks whose tokens are all at or before p, and

@@ -40,9 +40,16 @@ bool valid_kv(const v4a_kv* kv) {
 }
 
 // Shared validation of the two attend calls.
+// V4A_OK with *empty set: B == 0 or Q == 0, nothing to read or write.
 v4a_status check_attend(const void* q, int32_t q_dtype, const v4a_kv* comp, const v4a_kv* win,
                         int32_t n_win, const int64_t* pos, int32_t B, int32_t Q, int32_t H,
-                        void* out, int32_t out_dtype) {
+                        void* out, int32_t out_dtype, bool* empty) {
+  *empty = false;
+  if (B < 0 || Q < 0) return V4A_ERR_INVALID;
+  if (B == 0 || Q == 0) {
+    *empty = true;
+    return V4A_OK;
+  }
   if (!q || !pos || !out || !comp || !win || B < 0 || Q < 0 || H < 1 || n_win < 0)
     return V4A_ERR_INVALID;
   if (!valid_kv(comp) || !valid_kv(win)) return V4A_ERR_INVALID;
@@ -158,7 +165,9 @@ static v4a_status compress_impl(const void* kv_cur, const void* gate_cur, const 
                                 int32_t out_kind, const void* out, const v4a_norm_rope* nr,
                                 void* stream, const v4a_pages* pages = nullptr,
                                 const int64_t* apos = nullptr, float* state = nullptr) {
-  if (!kv_cur || B < 0 || T < 0 || d < 1 || t0 < 0) return V4A_ERR_INVALID;
+  if (B < 0 || T < 0 || d < 1 || t0 < 0) return V4A_ERR_INVALID;
+  if (B == 0 || (!apos && T == 0)) return V4A_OK;   // nothing to read or write
+  if (!kv_cur) return V4A_ERR_INVALID;
   if (!out && !apos) return V4A_ERR_INVALID;
   if (nr && !(nr->eps >= 0.0f)) return V4A_ERR_INVALID;
   if (nr && out_kind != V4A_OUT_KV) return V4A_ERR_UNSUPPORTED;
@@ -241,7 +250,7 @@ v4a_status v4attn_compress_paged(const void* kv_cur, const void* gate_cur, const
                                  int32_t B, int32_t T, int32_t d, int32_t m, int64_t t0,
                                  int32_t out_kind, const void* out, const v4a_pages* pages,
                                  const v4a_norm_rope* nr, void* stream) {
-  if (!pages) return V4A_ERR_INVALID;
+  if (!pages && B > 0 && T > 0) return V4A_ERR_INVALID;
   return compress_impl(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, in_dtype, B, T, d, m, t0,
                        out_kind, out, nr, stream, pages);
 }
@@ -251,7 +260,7 @@ v4a_status v4attn_append(const void* kv_cur, const void* gate_cur, const void* k
                          const float* pos_bias, int32_t in_dtype, int32_t B, int32_t d, int32_t m,
                          int32_t out_kind, const void* out, const v4a_pages* pages,
                          const v4a_norm_rope* nr, void* stream) {
-  if (!pos) return V4A_ERR_INVALID;
+  if (!pos && B > 0) return V4A_ERR_INVALID;
   // T = m, t0 = 0 pass the shape checks of the chunked call; the append
   // kernel takes its blocks from pos
   return compress_impl(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, in_dtype, B, m, d, m, 0,
@@ -280,7 +289,9 @@ static v4a_status index_topk(const void* q_idx, int32_t q_dtype, const float* w,
                              int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
                              size_t ws_bytes, void* stream, int score_bf16,
                              const v4a_pages* pages = nullptr) {
-  if (!q_idx || !w || !keys || !pos || !topk || B < 0 || Q < 0 || H_I < 1 || k < 1 || m < 1)
+  if (B < 0 || Q < 0) return V4A_ERR_INVALID;
+  if (B == 0 || Q == 0) return V4A_OK;     // nothing to read or write
+  if (!q_idx || !w || !keys || !pos || !topk || H_I < 1 || k < 1 || m < 1)
     return V4A_ERR_INVALID;
   if (q_dtype != V4A_F32 && q_dtype != V4A_BF16) return V4A_ERR_INVALID;
   if (!keys->codes || keys->cap < 1 || keys->d < 1) return V4A_ERR_INVALID;
@@ -344,7 +355,7 @@ v4a_status v4attn_index_topk_paged(const void* q_idx, int32_t q_dtype, const flo
                                    const int64_t* pos, int32_t B, int32_t Q, int32_t H_I,
                                    int32_t m, int32_t k, int32_t score_bf16, int32_t* topk,
                                    void* ws, size_t ws_bytes, void* stream) {
-  if (!pages) return V4A_ERR_INVALID;
+  if (!pages && B > 0 && Q > 0) return V4A_ERR_INVALID;
   return index_topk(q_idx, q_dtype, w, keys, pos, B, Q, H_I, m, k, topk, ws, ws_bytes, stream,
                     score_bf16 ? 1 : 0, pages);
 }
@@ -356,8 +367,9 @@ v4a_status v4attn_csa_attend_paged(const void* q, int32_t q_dtype, const v4a_kv*
                                    int32_t B, int32_t Q, int32_t H, void* out, int32_t out_dtype,
                                    const v4a_norm_rope* nr, void* ws, size_t ws_bytes,
                                    void* stream) {
-  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype);
-  if (s != V4A_OK) return s;
+  bool empty;
+  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype, &empty);
+  if (s != V4A_OK || empty) return s;
   if ((s = check_nr(comp, nr)) != V4A_OK) return s;
   if (k < 0 || (k > 0 && !topk)) return V4A_ERR_INVALID;
   if (comp->fmt != V4A_KV_FP8_BF16ROPE) return V4A_ERR_UNSUPPORTED;
@@ -378,8 +390,9 @@ v4a_status v4attn_hca_attend_paged(const void* q, int32_t q_dtype, const v4a_kv*
                                    float sm_scale, int32_t B, int32_t Q, int32_t H, void* out,
                                    int32_t out_dtype, const v4a_norm_rope* nr, void* ws,
                                    size_t ws_bytes, void* stream) {
-  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype);
-  if (s != V4A_OK) return s;
+  bool empty;
+  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype, &empty);
+  if (s != V4A_OK || empty) return s;
   if ((s = check_nr(comp, nr)) != V4A_OK) return s;
   if (m < 1) return V4A_ERR_INVALID;
   if (comp->fmt != V4A_KV_FP8_BF16ROPE) return V4A_ERR_UNSUPPORTED;
@@ -398,8 +411,9 @@ v4a_status v4attn_csa_attend_nr(const void* q, int32_t q_dtype, const v4a_kv* co
                                 const int64_t* pos, const float* sink, float sm_scale, int32_t B,
                                 int32_t Q, int32_t H, void* out, int32_t out_dtype,
                                 const v4a_norm_rope* nr, void* ws, size_t ws_bytes, void* stream) {
-  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype);
-  if (s != V4A_OK) return s;
+  bool empty;
+  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype, &empty);
+  if (s != V4A_OK || empty) return s;
   if ((s = check_nr(comp, nr)) != V4A_OK) return s;
   if (k < 0 || (k > 0 && !topk)) return V4A_ERR_INVALID;
   AttendArgs a;
@@ -426,8 +440,9 @@ v4a_status v4attn_hca_attend_nr(const void* q, int32_t q_dtype, const v4a_kv* co
                                 const float* sink, float sm_scale, int32_t B, int32_t Q, int32_t H,
                                 void* out, int32_t out_dtype, const v4a_norm_rope* nr, void* ws,
                                 size_t ws_bytes, void* stream) {
-  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype);
-  if (s != V4A_OK) return s;
+  bool empty;
+  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype, &empty);
+  if (s != V4A_OK || empty) return s;
   if ((s = check_nr(comp, nr)) != V4A_OK) return s;
   if (m < 1) return V4A_ERR_INVALID;
   AttendArgs a;

@@ -200,6 +200,27 @@ def test_paged_variants_rejected_on_host(clib):
                               None, None, None) == -1                 # no positions
 
 
+def test_empty_calls_need_no_pointers(clib):
+    # B == 0 (or Q == 0, or T == 0 for the chunked compressor): V4A_OK without
+    # reading any data pointer (torch hands out NULL for empty tensors)
+    f = ctypes.c_float(0.1)
+    assert clib.v4attn_compress(None, None, None, None, None, 0, 0, 4, 512, 4, 0, 0, None, None) == 0
+    assert clib.v4attn_compress(None, None, None, None, None, 0, 2, 0, 512, 4, 0, 0, None, None) == 0
+    assert clib.v4attn_append(None, None, None, None, None, None, None, 0, 0, 512, 4, 0, None, None,
+                              None, None) == 0
+    assert clib.v4attn_index_topk(None, 1, None, None, None, 0, 1, 16, 4, 64, None, None, 0,
+                                  None) == 0
+    assert clib.v4attn_index_topk_paged(None, 1, None, None, None, None, 2, 0, 16, 4, 64, 0, None,
+                                        None, 0, None) == 0
+    assert clib.v4attn_csa_attend(None, 1, None, None, 8, None, 16, None, None, f, 0, 1, 64, None, 1,
+                                  None, 0, None) == 0
+    assert clib.v4attn_hca_attend_paged(None, 1, None, None, 128, None, 16, None, None, f, 3, 0, 64,
+                                        None, 1, None, None, 0, None) == 0
+    # negative sizes stay invalid
+    assert clib.v4attn_index_topk(None, 1, None, None, None, -1, 1, 16, 4, 64, None, None, 0,
+                                  None) == -1
+
+
 def test_binding_refuses_host_tensors():
     import numpy as np
     import torch

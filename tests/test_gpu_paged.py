@@ -345,3 +345,67 @@ def test_hca_decode_1m_paged_full_size(lib):
         _, ref = hca_attend(qb[b:b + 1], "bf16", sub(comp), m, sub(win), c["n_win"],
                             gd["pos"][b:b + 1], None, 512 ** -0.5, "bf16")
         P.check_out(o_pg[b:b + 1], ref, what=f"row {b}")
+
+
+def test_paged_edge_cases(lib):
+    # table slots past a sequence's pages hold garbage (negative, past the
+    # pool): the kernels clamp them, so reads stay in the pool and results
+    # only depend on the pages the visible entries use; an empty batch and
+    # idle sequences (position -1) touch nothing
+    print("paged edge cases: garbage table slots, empty batch, idle sequences", flush=True)
+    rng = np.random.default_rng(77)
+    Bn, H, d, m, k, page_tokens, n_pg = 2, 16, 128, 4, 64, 512, 6
+    P_ = page_tokens // m
+    table, n_pool = _perm(rng, Bn, n_pg)
+    keys = C.idx_encode((rng.standard_normal((Bn, n_pg * P_, d)) * d ** -0.5).astype(np.float32),
+                        "mxfp4")
+    pool = _pool_idx(keys, table, P_, n_pool)
+    lv = logical_view(pool, table, P_)
+    used = 2                                    # pages the positions below can see
+    bad = table.copy()
+    bad[0, used:] = [-7, 1 << 30, -1, 99999][:n_pg - used]
+    bad[1, used:] = n_pool + 5
+    pos = np.array([[4 * used * P_ - 1], [4 * P_ + 9]], np.int64)
+    q = (rng.standard_normal((Bn, 1, H, d)) * d ** -0.5).astype(np.float32)
+    w = rng.random((Bn, 1, H)).astype(np.float32)
+    qb = C.bf16_encode(q)
+    qd = P.dev(qb.view(np.int16)).view(torch.bfloat16)
+    t_bad = lib.v4attn_index_topk_paged(qd, P.dev(w), P.idx_to_dev(pool),
+                                        _pages(lib, bad, page_tokens), P.dev(pos), m, k)
+    t_ok = lib.v4attn_index_topk_paged(qd, P.dev(w), P.idx_to_dev(pool),
+                                       _pages(lib, table, page_tokens), P.dev(pos), m, k)
+    torch.cuda.synchronize()
+    assert torch.equal(t_bad, t_ok)
+    sc = index_scores(C.bf16_decode(qb).astype(np.float32), w, lv, pos, m)
+    for b in range(Bn):
+        P.check_topk_row(t_bad.cpu().numpy()[b, 0], sc[b][0], k)
+    # HCA attention through the garbage slots: rows past n_vis never count
+    comp = C.kv_encode((rng.standard_normal((Bn, n_pg * 4, 512)) * 512 ** -0.5).astype(np.float32),
+                       "fp8", 448)
+    tab_h, n_pool_h = _perm(rng, Bn, n_pg)
+    pool_h = _pool_kv(comp, tab_h, 4, n_pool_h)
+    bad_h = tab_h.copy()
+    bad_h[:, used:] = -3
+    win = C.kv_encode((rng.standard_normal((Bn, 128, 512)) * 512 ** -0.5).astype(np.float32), "fp8",
+                      448)
+    qh = C.bf16_encode(rng.standard_normal((Bn, 1, 64, 512)).astype(np.float32))
+    ph = np.array([[128 * 4 * used - 1], [128 * 5 + 3]], np.int64)
+    o = lib.v4attn_hca_attend_paged(P.dev(qh.view(np.int16)).view(torch.bfloat16),
+                                    P.kv_to_dev(pool_h), _pages(lib, bad_h, page_tokens), 128,
+                                    P.kv_to_dev(win), 128, P.dev(ph), None, 512 ** -0.5)
+    torch.cuda.synchronize()
+    _, ref = hca_attend(qh, "bf16", logical_view(pool_h, tab_h, 4), 128, win, 128, ph, None,
+                        512 ** -0.5, "bf16")
+    P.check_out(o, ref)
+    # an empty batch, and a batch of idle sequences, leave the cache as it was
+    out = lib.KVCache.empty(1, n_pool * P_, 448, 64, lib.KV_FP8_BF16ROPE)
+    before = out.nope.clone()
+    state = lib.append_state(Bn, 512)
+    tok = P.dev(rng.standard_normal((Bn, 512)).astype(np.float32))
+    pos0 = P.dev(np.zeros(1, np.int64))[:0]      # views: valid pointers, no rows
+    lib.v4attn_append(tok[:0], None, None, None, state[:0], pos0, None, m, out,
+                      pages=lib.Pages(P.dev(table)[:0], page_tokens))
+    lib.v4attn_append(tok, None, None, None, state, P.dev(np.full(Bn, -1, np.int64)), None, m, out,
+                      pages=_pages(lib, table, page_tokens))
+    torch.cuda.synchronize()
+    assert torch.equal(out.nope, before)
