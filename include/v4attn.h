@@ -260,8 +260,9 @@ v4a_status v4attn_hca_attend(const void *q, int32_t q_dtype, const v4a_kv *comp,
  * query RMSNorm and RoPE (v4a_norm_rope; the query's own position) applied
  * before attention, and the output's last d_rope dims rotated back by the
  * query position ([Notes §9]).  The normalised, rotated query is rounded to
- * bf16 (the attention's operand precision) in the workspace, sized by
- * v4attn_workspace_bytes(V4A_OP_CSA_ATTEND_NR resp. V4A_OP_HCA_ATTEND_NR, ...).
+ * bf16 (the attention's operand precision) inside the attention kernel; the
+ * workspace is the plain call's (V4A_OP_CSA_ATTEND_NR / _HCA_ATTEND_NR size it
+ * the same).
  * The cache entries are expected to carry their own RMSNorm and RoPE
  * (v4attn_compress_nr).  FP8 entries only (V4A_KV_FP8_BF16ROPE); nr NULL
  * behaves as the plain call.  Errors as the plain calls, plus
@@ -407,7 +408,7 @@ v4a_status v4attn_hca_attend_paged(const void *q, int32_t q_dtype, const v4a_kv 
 #define V4A_OP_INDEX_TOPK 1
 #define V4A_OP_CSA_ATTEND 2
 #define V4A_OP_HCA_ATTEND 3
-#define V4A_OP_CSA_ATTEND_NR 4   /* the _nr variants: + the normalised queries */
+#define V4A_OP_CSA_ATTEND_NR 4   /* the _nr variants (same sizes as the plain ops) */
 #define V4A_OP_HCA_ATTEND_NR 5
 
 /*

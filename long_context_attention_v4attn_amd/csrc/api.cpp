@@ -97,28 +97,18 @@ void fill_attend(AttendArgs& a, const void* q, int32_t q_dtype, const v4a_kv* co
   a.fp8 = comp->fmt == V4A_KV_FP8_BF16ROPE;
 }
 
-// The normalised, rotated queries of the _nr calls: bf16 [R][H][D] after the
-// attention's own workspace regions.
-size_t qprep_bytes(const AttendArgs& a) {
-  return ((size_t)a.B * a.Q * a.H * (a.d_nope + a.d_rope) * 2 + 255) & ~(size_t)255;
-}
-
 v4a_status run_attend(AttendArgs& a, int64_t n_entries_max, void* ws, size_t ws_bytes,
                       void* stream, const v4a_norm_rope* nr = nullptr) {
   attend_plan(a, n_entries_max);
-  size_t need = attend_workspace_bytes(a);
-  const size_t base = need;
-  if (nr) need += qprep_bytes(a);
+  const size_t need = attend_workspace_bytes(a);
   if (need > 0) {
     if (!ws || ws_bytes < need) return V4A_ERR_WORKSPACE;
     attend_carve(a, ws);
   }
   if (nr) {
-    a.q_in = a.q;
     a.nr_gamma = nr->gamma;
     a.nr_eps = nr->eps;
     a.nr_inv = a.d_rope > 0 ? nr->inv_freq : nullptr;
-    a.q = (char*)ws + base;
   }
   KernelEvents ev;
   return hip_status(launch_attend(a, (hipStream_t)stream, take_events(&ev)));
@@ -470,8 +460,8 @@ size_t v4attn_workspace_bytes(int32_t op, int32_t B, int32_t Q, int32_t H, int32
     if (cap < 1) return (size_t)-1;
     return index_workspace_bytes(B, Q, H, d, cap, d == 128 && H % 16 == 0 ? 1 : 0);
   }
-  const bool nr = op == V4A_OP_CSA_ATTEND_NR || op == V4A_OP_HCA_ATTEND_NR;
-  if (nr) op = op == V4A_OP_CSA_ATTEND_NR ? V4A_OP_CSA_ATTEND : V4A_OP_HCA_ATTEND;
+  if (op == V4A_OP_CSA_ATTEND_NR) op = V4A_OP_CSA_ATTEND;
+  if (op == V4A_OP_HCA_ATTEND_NR) op = V4A_OP_HCA_ATTEND;
   if (op != V4A_OP_CSA_ATTEND && op != V4A_OP_HCA_ATTEND) return (size_t)-1;
   if (n_win < 0 || k < 0) return (size_t)-1;
   AttendArgs a;
@@ -484,9 +474,9 @@ size_t v4attn_workspace_bytes(int32_t op, int32_t B, int32_t Q, int32_t H, int32
   a.fp8 = 0;                      // fp32 partials: the larger of the two formats
   int64_t n = op == V4A_OP_CSA_ATTEND ? (int64_t)k + n_win : cap + n_win;
   attend_plan(a, n);
-  // the plan of the fp32 partials bounds the FP8 one; the _nr calls carve
-  // their queries after the FP8 plan's regions, which this sum also covers
-  return attend_workspace_bytes(a) + (nr ? qprep_bytes(a) : 0);
+  // the plan of the fp32 partials bounds the FP8 one (the _nr calls need no
+  // more: their queries are normalised inside the attention kernel)
+  return attend_workspace_bytes(a);
 }
 
 const char* v4attn_status_str(v4a_status s) {

@@ -31,6 +31,13 @@
 //                 the non-RoPE probability in fp32, so decoding adds no
 //                 rounding.  Online softmax in base 2 with a lazily updated
 //                 running max (rescale only when the max grows by > 8).
+//   k_attend_fp8_nr  the same with the query RMSNorm + RoPE of the _nr calls
+//                 ([Notes §9]) in its prologue: each workgroup normalises and
+//                 rotates its 32 heads in registers while its first tiles
+//                 load (the per-head sums of squares meet in LDS at the
+//                 prologue's first barrier) before the RoPE dims go to LDS;
+//                 the output's RoPE dims are rotated back in the epilogue or
+//                 the merge.
 //   k_attend_f32  fp32 VALU path for unquantised entries (any D <= 512).
 //   k_merge_tiled / k_merge  combine split partials in fixed split order.
 #include "common.hpp"
@@ -574,7 +581,10 @@ __device__ __forceinline__ int64_t part_block(const AttendArgs& a, int row, int 
   return (((int64_t)row * a.n_split + split) * a.H + hgrp * kHeads) * (kNope + kRope);
 }
 
-__global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
+// kNr: the _nr calls' query RMSNorm + RoPE ([Notes §9]) fused into the
+// prologue (see below); the output's rotation back is in the epilogues.
+template <bool kNr>
+__device__ __forceinline__ void attend_fp8(AttendArgs a) {
   __shared__ Fp8Tile tiles[kTileBufs];
   __shared__ Shared sh;
   __shared__ int src[kMaxSplit];
@@ -616,6 +626,17 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   u32x4 qrv = *(const u32x4*)((const uint16_t*)a.q +
                               ((int64_t)row * a.H + (r_ok ? hgrp * kHeads + rh : 0)) * D + kNope + 8 * rc);
   if (!r_ok) qrv = (u32x4){0u, 0u, 0u, 0u};
+  // _nr: the norm weights (two per thread), the RoPE inverse frequencies of
+  // this thread's four pairs and the query position, loaded with the query
+  // (unconditional loads; a missing weight or table reads the query instead)
+  float2 gam = {1.0f, 1.0f};
+  f32x4 ivf = {0.0f, 0.0f, 0.0f, 0.0f};
+  int64_t p_q = 0;
+  if (kNr) {
+    gam = *(const float2*)(a.nr_gamma ? a.nr_gamma + 2 * threadIdx.x : (const float*)a.q);
+    ivf = *(const f32x4*)(a.nr_inv ? a.nr_inv + 4 * rc : (const float*)a.q);
+    p_q = a.pos[row];
+  }
   const RowEntries r = row_entries(a, row);
   const int n_tot = r.n_c + r.n_w;
   const int e_beg = split * a.split_size;
@@ -626,6 +647,36 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   const int n_tiles = (n_local + kTile - 1) / kTile;
 
   resolve_sources(a, r, row, e_beg, n_local, n_tiles, pre, src, sh.tbits);
+  if (kNr) {
+    // the weights go to the third tile buffer (first written after the
+    // loop's first barrier); each head's sum of squares in two parts: its
+    // FP8 dims over the four lane groups that hold them (fin), its RoPE dims
+    // over the eight threads that hold them (lsum; both are epilogue slots)
+    *(float2*)((float*)tiles[2].rows + 2 * threadIdx.x) = gam;
+    float sq = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 14; s++) {
+      const u32x4 w = __builtin_bit_cast(u32x4, qf[s]);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float x0 = bf16_bits_to_f32(w[i] & 0xFFFFu), x1 = bf16_bits_to_f32(w[i] >> 16);
+        sq += x0 * x0 + x1 * x1;
+      }
+    }
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    if (eh == 0 && g == 0) sh.fin[16 * wht + li] = sq;
+    float rq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float x0 = bf16_bits_to_f32(qrv[i] & 0xFFFFu), x1 = bf16_bits_to_f32(qrv[i] >> 16);
+      rq += x0 * x0 + x1 * x1;
+    }
+    rq += __shfl_xor(rq, 1, 64);
+    rq += __shfl_xor(rq, 2, 64);
+    rq += __shfl_xor(rq, 4, 64);
+    if (rc == 0) (&sh.lsum[0][0])[rh] = rq;
+  }
   __syncthreads();
 
   Bases B;
@@ -656,6 +707,55 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
   // back edge, the older register set is the one stored next
   stage_load(B, stage_src(src, sh.tbits, 1), 1, n_local, st1);
   __builtin_amdgcn_sched_barrier(0);       // tile 1's loads stay ahead of tile 0's wait
+  // (_nr: the query's norm and rotation run while the first tiles load)
+  if (kNr) {
+    // x * r * gamma with r = 1 / sqrt(mean(x^2) + eps) over the head's 512
+    // dims, then the RoPE dims' adjacent pairs rotated by the query
+    // position; the results are rounded to bf16 once, as the operands
+    const float* gl = (const float*)tiles[2].rows;
+    const float* sql = &sh.lsum[0][0];
+    if (a.nr_gamma) {
+      const int hq = 16 * wht + li;
+      const float rn = 1.0f / sqrtf((sh.fin[hq] + sql[hq]) / (float)D + a.nr_eps);
+#pragma unroll
+      for (int s = 0; s < 14; s++) {
+        const u32x4 w = __builtin_bit_cast(u32x4, qf[s]);
+        const float* gd = gl + 64 * (s >> 1) + 16 * g + 8 * (s & 1);
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          x[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu) * rn * gd[2 * i];
+          x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16) * rn * gd[2 * i + 1];
+        }
+        const u32x2 lo = pack4(x), hi = pack4(x + 4);
+        qf[s] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+      }
+    }
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      x[2 * i] = bf16_bits_to_f32(qrv[i] & 0xFFFFu);
+      x[2 * i + 1] = bf16_bits_to_f32(qrv[i] >> 16);
+    }
+    if (a.nr_gamma) {
+      const float rr = 1.0f / sqrtf((sh.fin[rh] + sql[rh]) / (float)D + a.nr_eps);
+#pragma unroll
+      for (int i = 0; i < 8; i++) x[i] = x[i] * rr * gl[kNope + 8 * rc + i];
+    }
+    if (a.nr_inv) {
+      const float pf = (float)p_q;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        float sn, cs;
+        sincos_angle(pf * ivf[j], &sn, &cs);
+        const float x0 = x[2 * j], x1 = x[2 * j + 1];
+        x[2 * j] = x0 * cs - x1 * sn;
+        x[2 * j + 1] = x0 * sn + x1 * cs;
+      }
+    }
+    const u32x2 lo = pack4(x), hi = pack4(x + 4);
+    qrv = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+  }
   stage_store(&tiles[0], st0);
   stage_load(B, stage_src(src, sh.tbits, 2), 2, n_local, st0);
   *(u32x4*)&sh.qr[rh][8 * rc] = qrv;
@@ -785,6 +885,9 @@ __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) {
     }
   }
 }
+
+__global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) { attend_fp8<false>(a); }
+__global__ void __launch_bounds__(kThreads, 2) k_attend_fp8_nr(AttendArgs a) { attend_fp8<true>(a); }
 
 // ---------------------------------------------------------------- fp32 VALU path
 // One workgroup per (query, split, head group of kF32Heads); entries are
@@ -1089,59 +1192,6 @@ __global__ void __launch_bounds__(256) k_merge_tiled(AttendArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- query RMSNorm + RoPE
-// [Notes §9] prologue of the _nr calls: every query head RMS-normalised over
-// its D = 512 dims (weight gamma), its last 64 dims rotated by the query
-// position, rounded to bf16 for the attention kernel.  One wave per (query,
-// head): lane l holds dims 8l .. 8l+7 (RoPE pairs stay inside a lane).
-__global__ void __launch_bounds__(256) k_qprep(AttendArgs a) {
-  const int D = kNope + kRope;
-  const int lane = threadIdx.x & 63;
-  const int64_t gh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // row * H + head
-  if (gh >= (int64_t)a.B * a.Q * a.H) return;
-  const int64_t row = gh / a.H;
-  // every load first (valid dummy addresses where a step is off), then the
-  // arithmetic: one memory round trip
-  const u32x4 raw = *(const u32x4*)((const uint16_t*)a.q_in + gh * D + 8 * lane);
-  const float* gsrc = a.nr_gamma ? a.nr_gamma + 8 * lane : (const float*)a.q_in;
-  const f32x4 g0 = *(const f32x4*)gsrc, g1 = *(const f32x4*)(gsrc + 4);
-  const bool rot = a.nr_inv != nullptr && 8 * lane >= kNope;
-  const f32x4 iv = *(const f32x4*)(rot ? a.nr_inv + ((8 * lane - kNope) >> 1) : (const float*)a.q_in);
-  const int64_t p_row = a.pos[row];
-  float x[8];
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const uint32_t w = raw[i];
-    x[2 * i] = bf16_bits_to_f32(w & 0xFFFFu);
-    x[2 * i + 1] = bf16_bits_to_f32(w >> 16);
-  }
-  if (a.nr_gamma) {
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) ss += x[i] * x[i];
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)D + a.nr_eps);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      x[i] = x[i] * r * g0[i];
-      x[4 + i] = x[4 + i] * r * g1[i];
-    }
-  }
-  if (rot) {
-    const float pf = (float)p_row;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      float sn, cs;
-      sincos_angle(pf * iv[j], &sn, &cs);
-      const float x0 = x[2 * j], x1 = x[2 * j + 1];
-      x[2 * j] = x0 * cs - x1 * sn;
-      x[2 * j + 1] = x0 * sn + x1 * cs;
-    }
-  }
-  const u32x2 lo = pack4(x), hi = pack4(x + 4);
-  *(u32x4*)((uint16_t*)a.q + gh * D + 8 * lane) = (u32x4){lo[0], lo[1], hi[0], hi[1]};
-}
-
 // ---------------------------------------------------------------- plan / launch
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1200,18 +1250,18 @@ size_t attend_f32_smem(const AttendArgs& a) {
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st, const KernelEvents* ev) {
   const int rows = a.B * a.Q;
   if (rows == 0) return hipSuccess;
-  if (a.fp8 && a.q_in) {
-    const int64_t heads = (int64_t)rows * a.H;
-    hipLaunchKernelGGL(k_qprep, dim3((unsigned)((heads + 3) / 4)), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   if (a.fp8) {
     const int64_t N = (int64_t)rows * a.n_split * ((a.H + kHeads - 1) / kHeads);
     const int64_t per = (N + 7) / 8;
-    if (ev)
+    const bool nr = a.nr_gamma || a.nr_inv;
+    if (ev && nr)
+      hipExtLaunchKernelGGL(k_attend_fp8_nr, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st,
+                            ev->start, ev->stop, 0, a);
+    else if (ev)
       hipExtLaunchKernelGGL(k_attend_fp8, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st, ev->start,
                             ev->stop, 0, a);
+    else if (nr)
+      hipLaunchKernelGGL(k_attend_fp8_nr, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st, a);
     else
       hipLaunchKernelGGL(k_attend_fp8, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st, a);
   } else {

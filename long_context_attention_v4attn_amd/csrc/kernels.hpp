@@ -127,9 +127,8 @@ struct AttendArgs {
   int part_bf16;             // split partials stored in bf16 (FP8 path) or fp32
   void* part_o;              // [R][n_split][H][D] O / l
   float* part_ml;            // [R][n_split][H][2] (max, denominator)
-  // query RMSNorm / RoPE (q_in non-null: a prologue kernel writes the bf16
-  // result to q) and the output's rotation back (nr_inv non-null)
-  const void* q_in;          // [R][H][D] bf16
+  // query RMSNorm / RoPE in the attention prologue and the output's rotation
+  // back (k_attend_fp8_nr when either is set)
   const float* nr_gamma;     // [D] or null
   const float* nr_inv;       // [d_rope / 2] or null
   float nr_eps;
