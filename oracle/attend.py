@@ -29,7 +29,7 @@ import numpy as np
 
 from .codecs import bf16_decode, bf16_encode, f32, kv_decode_rows
 from .indexer import n_visible
-from .normrope import rms_norm, rope
+from .normrope import norm_rope, rope
 
 
 def window_positions(p, n_win):
@@ -82,12 +82,12 @@ def _prep_q(qd, pos, nr):
     if nr is None:
         return qd
     pos = np.asarray(pos, np.int64)
-    qn = rope(rms_norm(qd, nr["gamma"], nr["eps"]), pos[:, :, None], nr["inv_freq"])
+    qn = norm_rope(qd, pos[:, :, None], nr)
     return bf16_decode(bf16_encode(f32(qn)))
 
 
 def _post_out(out, pos, nr):
-    if nr is None:
+    if nr is None or nr.get("inv_freq") is None:
         return out
     return rope(out, np.asarray(pos, np.int64)[:, :, None], nr["inv_freq"], sign=-1)
 

@@ -32,7 +32,7 @@ Output: float64 [B][T/m][d], rounded to fp32 -- compressed entries t0/m ...
 import numpy as np
 
 from .codecs import f32
-from .normrope import entry_positions, rms_norm, rope
+from .normrope import entry_positions, norm_rope
 
 
 def _softmax_rows(logits):
@@ -48,8 +48,7 @@ def compress(kv_cur, gate_cur, kv_prev, gate_prev, pos_bias, m, t0, nr=None):
         return y
     nb = y.shape[1]
     blocks = t0 // m + np.arange(nb)
-    y = rope(rms_norm(y, nr["gamma"], nr["eps"]), entry_positions(blocks, m)[None, :],
-             nr["inv_freq"])
+    y = norm_rope(y, entry_positions(blocks, m)[None, :], nr)
     return f32(y).astype(np.float64)
 
 

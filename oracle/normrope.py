@@ -66,3 +66,16 @@ def default_inv_freq(d_rope, base=10000.0):
     """The usual table fl32(base^(-2i/d_rope)); callers may pass any table."""
     i = np.arange(d_rope // 2, dtype=np.float64)
     return f32(base ** (-2.0 * i / d_rope))
+
+
+def norm_rope(x, pos, nr):
+    """The [Notes §9] steps of an `nr` option on rows x [..., D] at positions
+    pos (broadcast against x's leading axes): RMSNorm when nr["gamma"] is not
+    None, then RoPE when nr["inv_freq"] is not None (either step may be off,
+    as in the library's calls)."""
+    y = np.asarray(x, np.float64)
+    if nr.get("gamma") is not None:
+        y = rms_norm(y, nr["gamma"], nr["eps"])
+    if nr.get("inv_freq") is not None:
+        y = rope(y, pos, nr["inv_freq"])
+    return y

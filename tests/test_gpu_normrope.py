@@ -135,3 +135,47 @@ def test_norm_rope_pipeline_end_to_end(lib):
     torch.cuda.synchronize()
     _, ref = hca_attend(qb, "bf16", comp_o, m, win_o, 128, pos, None, d ** -0.5, "bf16", nr=nr)
     P.check_out(o, ref)
+
+
+@pytest.mark.parametrize("mode", ["rope_only", "norm_only"])
+def test_partial_norm_rope(lib, mode):
+    # one of the two steps off (gamma or inv_freq NULL), in the compressor
+    # epilogue and in the attention prologue / output rotation
+    print(f"partial norm/rope: {mode}", flush=True)
+    rng = np.random.default_rng(41 if mode == "rope_only" else 43)
+    nr, gamma, inv = _nr(rng)
+    if mode == "rope_only":
+        nr["gamma"] = None
+        nd = lib.NormRope(None, P.dev(inv), 1e-6)
+    else:
+        nr["inv_freq"] = None
+        nd = lib.NormRope(P.dev(gamma), None, 1e-6)
+    Bn, d, dn, m, T, t0 = 2, 512, 448, 4, 24, 1 << 19
+    g = synth.compress_inputs(3, Bn, T, d, m, True, t0)
+    y = compress(g["kv_cur"], g["gate_cur"], g["kv_prev"], g["gate_prev"], g["bias"], m, t0, nr=nr)
+    out = lib.KVCache.empty(Bn, T // m, dn, d - dn, lib.KV_FP8_BF16ROPE)
+    lib.v4attn_compress_nr(P.dev(g["kv_cur"]), P.dev(g["gate_cur"]), P.dev(g["kv_prev"]),
+                           P.dev(g["gate_prev"]), P.dev(g["bias"]), m, t0, out, nd)
+    torch.cuda.synchronize()
+    back = P.kv_from_dev(out)
+    rows = (t0 // m + np.arange(T // m)) % (T // m)
+    P.check_fp8_rows(C.KV("fp8", dn, d - dn, back.nope[:, rows], back.rope[:, rows],
+                          back.scale[:, rows]), y, dn)
+    H, Q, n, R = 64, 2, 700, 160
+    comp, win, q = _inputs(rng, Bn, Q, H, n, R)
+    qb = C.bf16_encode(q)
+    qd = P.dev(qb.view(np.int16)).view(torch.bfloat16)
+    pos = np.array([[4 * n + 5, 1 << 20], [37, 4 * n - 1]], np.int64)
+    scale = 512 ** -0.5
+    _, ref = hca_attend(qb, "bf16", comp, 4, win, 128, pos, None, scale, "bf16", nr=nr)
+    o = lib.v4attn_hca_attend_nr(qd, P.kv_to_dev(comp), 4, P.kv_to_dev(win), 128, P.dev(pos), None,
+                                 scale, nd)
+    k = 200
+    topk = np.stack([np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(Q)])
+                     for _ in range(Bn)])
+    _, ref_c = csa_attend(qb, "bf16", comp, topk, win, 128, pos, None, scale, "bf16", nr=nr)
+    oc = lib.v4attn_csa_attend_nr(qd, P.kv_to_dev(comp), P.dev(topk.astype(np.int32)),
+                                  P.kv_to_dev(win), 128, P.dev(pos), None, scale, nd)
+    torch.cuda.synchronize()
+    P.check_out(o, ref)
+    P.check_out(oc, ref_c)

@@ -115,3 +115,21 @@ def test_output_rotation_undoes_the_entry_rotation():
         assert np.allclose(out[0, 0, h], want, atol=1e-12)
     # the RoPE dims come back to the unrotated entry up to the bf16 storage
     assert np.allclose(out[0, 0, 0, 448:], v[448:], atol=2e-2 * np.abs(v[448:]).max())
+
+
+def test_partial_options_switch_single_steps_off():
+    # gamma None: RoPE alone (norms of the rotated pairs kept); inv_freq None:
+    # RMSNorm alone (mean square 1 with unit weights); both: the identity
+    from oracle.normrope import norm_rope
+    x = np.random.default_rng(5).normal(size=(3, 512)) * 4
+    inv = default_inv_freq(64)
+    only_rope = norm_rope(x, np.array([7, 8, 9]), dict(gamma=None, eps=0.0, inv_freq=inv))
+    assert np.array_equal(only_rope[:, :448], x[:, :448])
+    pair = lambda a: np.hypot(a[:, 448::2], a[:, 449::2])
+    assert np.allclose(pair(only_rope), pair(x))
+    assert not np.allclose(only_rope[:, 448:], x[:, 448:])
+    only_norm = norm_rope(x, np.array([7, 8, 9]), dict(gamma=np.ones(512), eps=0.0, inv_freq=None))
+    assert np.allclose(np.mean(only_norm ** 2, axis=-1), 1.0)
+    assert np.allclose(only_norm * np.sqrt(np.mean(x ** 2, axis=-1, keepdims=True)), x)
+    none = norm_rope(x, 0, dict(gamma=None, eps=0.0, inv_freq=None))
+    assert np.array_equal(none, x)
