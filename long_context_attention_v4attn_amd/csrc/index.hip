@@ -246,12 +246,17 @@ struct KeyTiles {
 // Paged keys: a page holds >= 128 keys and blk0 is a multiple of 128, so the
 // wave's blocks are one contiguous run of pool rows (past the cache end the
 // run of the last 128 blocks stands in).
+// prow >= 0: that pool row, looked up in advance (paged); -1: look it up here.
+__device__ __forceinline__ int64_t paged_run(const Pages& pg, int b, int64_t blk0, int64_t cap) {
+  return page_row(pg, b, blk0 < cap ? blk0 : cap - kWaveTiles * 16);
+}
+
 __device__ __forceinline__ void load_keys(const uint8_t* kc, const uint8_t* ks, int64_t blk0,
                                           int64_t cap, const Pages& pg, int b, int g, int li,
-                                          KeyTiles& kt) {
+                                          KeyTiles& kt, int64_t prow = -1) {
   const bool paged = pg.tab != nullptr;
   if (paged || blk0 + kWaveTiles * 16 <= cap) {
-    const int64_t r0 = paged ? page_row(pg, b, blk0 < cap ? blk0 : cap - kWaveTiles * 16) : blk0;
+    const int64_t r0 = paged ? (prow >= 0 ? prow : paged_run(pg, b, blk0, cap)) : blk0;
     const uint8_t* cp = kc + (r0 + li) * 64 + g * 16;
     const uint32_t* sp = (const uint32_t*)(ks + (r0 + 16 * g + li) * 4);
 #pragma unroll
@@ -449,6 +454,13 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
   }
   constexpr int kSets = kIters > 0 ? kIters : 2;
   KeyTiles kt[kSets];
+  // paged keys, fixed iteration count: every iteration's pool row looked up
+  // now, with the query loads (not one lookup wait per iteration)
+  int64_t prow[kSets];
+#pragma unroll
+  for (int j = 0; j < kSets; j++)
+    prow[j] = (kIters > 0 && a.pg.tab) ? paged_run(a.pg, b, wblk + (int64_t)j * kIterBlocks, a.cap)
+                                       : -1;
   // kIters > 0: iterations 0 .. kDepth-2 go out now, iteration j + kDepth - 1
   // just before iteration j is scored (a wave that issued all its loads at
   // once would wait at the issue of the later ones -- the compute unit's
@@ -457,7 +469,7 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
 #pragma unroll
   for (int j = 0; j < kSets; j++)
     if (kIters > 0 ? j < kDepth - 1 : j < a.score_iters)
-      load_keys(kc, ks, wblk + (int64_t)j * kIterBlocks, a.cap, a.pg, b, g, li, kt[j]);
+      load_keys(kc, ks, wblk + (int64_t)j * kIterBlocks, a.cap, a.pg, b, g, li, kt[j], prow[j]);
   // the query loads went out first, so this waits for them alone and runs
   // while the first keys are on their way
   if (kParts) quantize_q_frag(a, qraw, &qa[0], &qs[0]);
@@ -485,7 +497,7 @@ __global__ void __launch_bounds__(64 * kScanWaves) k_score_mx(IndexArgs a) {
     for (int j = 0; j < kSets; j++) {
       if (j + kDepth - 1 < kSets)
         load_keys(kc, ks, wblk + (int64_t)(j + kDepth - 1) * kIterBlocks, a.cap, a.pg, b, g, li,
-                  kt[j + kDepth - 1]);
+                  kt[j + kDepth - 1], prow[j + kDepth - 1]);
       if (j < iters)
         score_tiles<kHT>(kt[j], qa, qs, wv, HT, wblk + (int64_t)j * kIterBlocks, nv, a.sc_ld, lane,
                          out, outh, bf16, lh);
