@@ -371,6 +371,29 @@ v4a_status v4attn_append(const void *kv_cur, const void *gate_cur,
                          void *stream);
 
 /*
+ * v4attn_append_batch -- up to V4A_MAX_APPEND v4attn_append calls in one
+ * launch (a decode step's appends of several caches: a layer's entries,
+ * indexer keys and window ring, or several layers).  calls[j] holds the
+ * arguments of one v4attn_append (host struct; out, pages and nr are host
+ * pointers as there).  The result is that of the calls made one after the
+ * other, provided no two of them write the same state or the same cache
+ * rows (they run concurrently).  Every call is validated before anything
+ * is launched; the first invalid one's status is returned.
+ */
+#define V4A_MAX_APPEND 8
+typedef struct {
+  const void *kv_cur, *gate_cur, *kv_prev, *gate_prev;   /* [B][d] token rows */
+  float *state;                 /* f32 [B][2][3][d], or NULL (m == 1, no overlap) */
+  const int64_t *pos;           /* int64 [B] */
+  const float *pos_bias;        /* f32 [slots][d] or NULL */
+  const void *out;              /* host v4a_kv / v4a_idx, or NULL: state only */
+  const v4a_pages *pages;       /* or NULL: ring rows */
+  const v4a_norm_rope *nr;      /* or NULL */
+  int32_t in_dtype, B, d, m, out_kind, _pad;
+} v4a_append;
+v4a_status v4attn_append_batch(int32_t n, const v4a_append *calls, void *stream);
+
+/*
  * v4attn_index_topk_paged -- v4attn_index_topk over paged MXFP4 keys (keys
  * describes the pool; P = page_tokens / m >= 128).  score_bf16 != 0 selects
  * the BF16-score ranking of v4attn_index_topk_bf16.  Workspace: as

@@ -13,7 +13,7 @@ from .binding import (  # noqa: F401
     v4attn_compress, v4attn_index_topk, v4attn_index_topk_bf16, v4attn_csa_attend,
     v4attn_hca_attend, NormRope, OP_CSA_ATTEND_NR, OP_HCA_ATTEND_NR, v4attn_compress_nr,
     v4attn_csa_attend_nr, v4attn_hca_attend_nr,
-    Pages, append_state, v4attn_compress_paged, v4attn_append, v4attn_index_topk_paged,
+    Pages, append_state, v4attn_compress_paged, v4attn_append, v4attn_append_batch, v4attn_index_topk_paged,
     v4attn_csa_attend_paged, v4attn_hca_attend_paged,
     v4attn_workspace_bytes, v4attn_status_str, v4attn_time_next_kernel,
 )

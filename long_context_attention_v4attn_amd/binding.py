@@ -46,6 +46,15 @@ class _Pages(ctypes.Structure):
                 ("page_tokens", ctypes.c_int32)]
 
 
+class _Append(ctypes.Structure):
+    _fields_ = [("kv_cur", ctypes.c_void_p), ("gate_cur", ctypes.c_void_p),
+                ("kv_prev", ctypes.c_void_p), ("gate_prev", ctypes.c_void_p),
+                ("state", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("pos_bias", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("pages", ctypes.c_void_p), ("nr", ctypes.c_void_p),
+                ("in_dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("m", ctypes.c_int32), ("out_kind", ctypes.c_int32), ("_pad", ctypes.c_int32)]
+
+
 @dataclass
 class NormRope:
     """[Notes §9] query / KV-entry RMSNorm and partial RoPE: gamma f32 [D]
@@ -90,6 +99,7 @@ _SIGS = {
                                      _P, _P, _P, _P]),
     "v4attn_append": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
                              _P]),
+    "v4attn_append_batch": (_I32, [_I32, _P, _P]),
     "v4attn_index_topk_paged": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                        _P, _P, _SZ, _P]),
     "v4attn_csa_attend_paged": (_I32, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _I32, _P, _P, _F, _I32,
@@ -435,6 +445,39 @@ def v4attn_append(kv_cur, gate_cur, kv_prev, gate_prev, state, pos, pos_bias, m,
                           kind, _byref(st), _byref(ps), _byref(ns), _stream(stream))
     _check(s, "v4attn_append")
     return out
+
+
+def v4attn_append_batch(calls, stream=None):
+    """Several v4attn_append calls in one launch.  `calls`: dicts with the
+    keyword arguments of v4attn_append (kv_cur, gate_cur, kv_prev, gate_prev,
+    state, pos, pos_bias, m, out, pages, nr); no two may write the same state
+    or cache rows."""
+    lib = load()
+    keep = []                                   # host structs the call points to
+
+    def ref(st):
+        if st is None:
+            return None
+        keep.append(st)
+        return ctypes.cast(ctypes.pointer(st), ctypes.c_void_p)
+
+    arr = (_Append * max(1, len(calls)))()
+    for j, c in enumerate(calls):
+        kv = c["kv_cur"]
+        _need_cuda(kv, c.get("gate_cur"), c.get("kv_prev"), c.get("gate_prev"), c.get("state"),
+                   c["pos"], c.get("pos_bias"))
+        B, d = kv.shape
+        out = c.get("out")
+        kind = OUT_KV if isinstance(out, KVCache) else OUT_IDX
+        pg, nr = c.get("pages"), c.get("nr")
+        arr[j] = _Append(_ptr(kv), _ptr(c.get("gate_cur")), _ptr(c.get("kv_prev")),
+                         _ptr(c.get("gate_prev")), _ptr(c.get("state")), _ptr(c["pos"]),
+                         _ptr(c.get("pos_bias")), ref(None if out is None else out.c_struct()),
+                         ref(None if pg is None else pg.c_struct()),
+                         ref(None if nr is None else nr.c_struct()), _dtype_code(kv), B, d,
+                         int(c["m"]), kind, 0)
+    s = lib.v4attn_append_batch(len(calls), arr, _stream(stream))
+    _check(s, "v4attn_append_batch")
 
 
 def v4attn_index_topk_paged(q_idx, w, keys, pages, pos, m, k, score_bf16=False, topk=None,

@@ -154,7 +154,13 @@ static v4a_status compress_impl(const void* kv_cur, const void* gate_cur, const 
                                 int32_t B, int32_t T, int32_t d, int32_t m, int64_t t0,
                                 int32_t out_kind, const void* out, const v4a_norm_rope* nr,
                                 void* stream, const v4a_pages* pages = nullptr,
-                                const int64_t* apos = nullptr, float* state = nullptr) {
+                                const int64_t* apos = nullptr, float* state = nullptr,
+                                CompressArgs* built = nullptr) {
+  // built: validate and fill the kernel arguments only (no launch)
+  if (built) {
+    memset(built, 0, sizeof(*built));
+    built->B = 0;
+  }
   if (B < 0 || T < 0 || d < 1 || t0 < 0) return V4A_ERR_INVALID;
   if (B == 0 || (!apos && T == 0)) return V4A_OK;   // nothing to read or write
   if (!kv_cur) return V4A_ERR_INVALID;
@@ -228,7 +234,10 @@ static v4a_status compress_impl(const void* kv_cur, const void* gate_cur, const 
     if (!state && (m > 1 || kv_prev)) return V4A_ERR_INVALID;
     a.apos = apos;
     a.state = state;
-    if (B == 0) return V4A_OK;
+    if (built) {
+      *built = a;
+      return V4A_OK;
+    }
     return hip_status(launch_compress(a, (hipStream_t)stream));
   }
   if (B == 0 || T == 0) return V4A_OK;
@@ -338,6 +347,23 @@ v4a_status v4attn_index_topk_bf16(const void* q_idx, int32_t q_dtype, const floa
                                   int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
                                   size_t ws_bytes, void* stream) {
   return index_topk(q_idx, q_dtype, w, keys, pos, B, Q, H_I, m, k, topk, ws, ws_bytes, stream, 1);
+}
+
+v4a_status v4attn_append_batch(int32_t n, const v4a_append* calls, void* stream) {
+  if (n < 0 || (n > 0 && !calls)) return V4A_ERR_INVALID;
+  if (n > V4A_MAX_APPEND) return V4A_ERR_UNSUPPORTED;
+  AppendBatch ab;
+  memset(&ab, 0, sizeof(ab));
+  ab.n = n;
+  for (int j = 0; j < n; j++) {
+    const v4a_append& c = calls[j];
+    if (!c.pos && c.B > 0) return V4A_ERR_INVALID;
+    const v4a_status s = compress_impl(c.kv_cur, c.gate_cur, c.kv_prev, c.gate_prev, c.pos_bias,
+                                       c.in_dtype, c.B, c.m, c.d, c.m, 0, c.out_kind, c.out, c.nr,
+                                       stream, c.pages, c.pos, c.state, &ab.c[j]);
+    if (s != V4A_OK) return s;
+  }
+  return hip_status(launch_append_batch(ab, (hipStream_t)stream));
 }
 
 v4a_status v4attn_index_topk_paged(const void* q_idx, int32_t q_dtype, const float* w,

@@ -222,9 +222,8 @@ __global__ void __launch_bounds__(kCompThreads) k_compress(CompressArgs a) {
 // current token, accumulator 1 the previous-role rows of that block (they
 // belong to the next block's entry).
 template <bool kBf16>
-__global__ void __launch_bounds__(kCompThreads) k_append(CompressArgs a) {
+__device__ __forceinline__ void append_one(const CompressArgs& a, int b) {
   __shared__ float red[kCompThreads / 64];
-  const int b = blockIdx.x;
   const int64_t p = a.apos[b];
   if (p < 0) return;                       // uniform: the sequence is idle
   const int m = a.m;
@@ -275,6 +274,31 @@ __global__ void __launch_bounds__(kCompThreads) k_append(CompressArgs a) {
   // a block past the sequence's pages is not stored
   if (a.pg.tab && (blk >> a.pg.psh) >= a.pg.tab_ld) return;
   finish_entry(a, y, b, blk, red);
+}
+
+template <bool kBf16>
+__global__ void __launch_bounds__(kCompThreads) k_append(CompressArgs a) {
+  append_one<kBf16>(a, blockIdx.x);
+}
+
+// Several appends in one launch: workgroup (b, j) runs sequence b of append
+// j (the appends touch disjoint states and cache rows).
+__global__ void __launch_bounds__(kCompThreads) k_append_batch(AppendBatch ab) {
+  const int j = blockIdx.y;
+  const CompressArgs& a = ab.c[j];
+  if ((int)blockIdx.x >= a.B) return;
+  if (a.in_bf16)
+    append_one<true>(a, blockIdx.x);
+  else
+    append_one<false>(a, blockIdx.x);
+}
+
+hipError_t launch_append_batch(const AppendBatch& ab, hipStream_t st) {
+  int bmax = 0;
+  for (int j = 0; j < ab.n; j++) bmax = ab.c[j].B > bmax ? ab.c[j].B : bmax;
+  if (ab.n == 0 || bmax == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_append_batch, dim3(bmax, ab.n), dim3(kCompThreads), 0, st, ab);
+  return hipGetLastError();
 }
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {

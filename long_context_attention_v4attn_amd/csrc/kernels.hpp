@@ -54,6 +54,13 @@ struct CompressArgs {
   int no_store;              // 1: update the state only (no output cache)
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
+// up to kMaxAppend decode-time appends in one launch
+constexpr int kMaxAppend = 8;
+struct AppendBatch {
+  CompressArgs c[kMaxAppend];
+  int n;
+};
+hipError_t launch_append_batch(const AppendBatch& ab, hipStream_t st);
 
 // ---------------------------------------------------------------- indexer + top-k
 struct IndexArgs {

@@ -201,6 +201,24 @@ def test_paged_variants_rejected_on_host(clib):
                               None, None, None) == -1                 # no positions
 
 
+def test_append_batch_rejected_on_host(clib):
+    from long_context_attention_v4attn_amd.binding import _Append
+    r = ctypes.byref
+    kv = _KV(2, 448, 64, 0, 100, 0x1000, 0x2000, 0x3000)
+    assert clib.v4attn_append_batch(0, None, None) == 0
+    assert clib.v4attn_append_batch(1, None, None) == -1
+    assert clib.v4attn_append_batch(-1, None, None) == -1
+    arr = (_Append * 9)()
+    assert clib.v4attn_append_batch(9, arr, None) == -2          # more than V4A_MAX_APPEND
+    # one bad call (rate 4 without a state) refuses the whole batch
+    good = _Append(0x1000, None, None, None, None, 0x5000, None, ctypes.cast(ctypes.pointer(kv), ctypes.c_void_p),
+                   None, None, 0, 2, 512, 1, 0, 0)
+    bad = _Append(0x1000, None, None, None, None, 0x5000, None, ctypes.cast(ctypes.pointer(kv), ctypes.c_void_p),
+                  None, None, 0, 2, 512, 4, 0, 0)
+    two = (_Append * 2)(good, bad)
+    assert clib.v4attn_append_batch(2, two, None) == -1
+
+
 def test_empty_calls_need_no_pointers(clib):
     # B == 0 (or Q == 0, or T == 0 for the chunked compressor): V4A_OK without
     # reading any data pointer (torch hands out NULL for empty tensors)

@@ -409,3 +409,57 @@ def test_paged_edge_cases(lib):
                       pages=_pages(lib, table, page_tokens))
     torch.cuda.synchronize()
     assert torch.equal(out.nope, before)
+
+
+def test_append_batch_matches_separate_calls(lib):
+    # a CSA layer's decode step in one launch: the entry (m = 4 overlap, paged),
+    # the indexer key (m = 4 overlap, 128 dims, paged) and the window token
+    # (m = 1 ring); the caches equal those of the separate calls bit for bit,
+    # and the entries the compressor's definition
+    print("append batch: CSA entry + indexer key + window token", flush=True)
+    rng = np.random.default_rng(91)
+    Bn, m, steps, page_tokens = 3, 4, 40, 512
+    P_ = page_tokens // m
+    table, n_pool = _perm(rng, Bn, 2)
+    pages = _pages(lib, table, page_tokens)
+    se = synth.compress_inputs(9, Bn, steps, 512, m, True, 0)
+    sk = synth.compress_inputs(10, Bn, steps, 128, m, True, 0)
+    dv = lambda a: P.dev(a)
+
+    def caches():
+        return (lib.KVCache.empty(1, n_pool * P_, 448, 64, lib.KV_FP8_BF16ROPE),
+                lib.IdxCache.empty(1, n_pool * P_, 128, lib.IDX_MXFP4),
+                lib.KVCache.empty(Bn, 64, 448, 64, lib.KV_FP8_BF16ROPE),
+                lib.append_state(Bn, 512), lib.append_state(Bn, 128))
+    one, sep = caches(), caches()
+    ge = {k: (None if v is None else dv(v)) for k, v in se.items()}
+    gk = {k: (None if v is None else dv(v)) for k, v in sk.items()}
+    start = [0, 3, 9]
+    for s in range(steps):
+        pos = np.array([s - start[b] for b in range(Bn)], np.int64)
+        tok = torch.from_numpy(np.clip(pos, 0, None)).cuda()
+        row = lambda a: a[torch.arange(Bn), tok].contiguous()
+        pd = P.dev(np.where(pos >= 0, pos, -1))
+        ent = dict(kv_cur=row(ge["kv_cur"]), gate_cur=row(ge["gate_cur"]), kv_prev=row(ge["kv_prev"]),
+                   gate_prev=row(ge["gate_prev"]), pos=pd, pos_bias=ge["bias"], m=m, pages=pages)
+        key = dict(kv_cur=row(gk["kv_cur"]), gate_cur=row(gk["gate_cur"]), kv_prev=row(gk["kv_prev"]),
+                   gate_prev=row(gk["gate_prev"]), pos=pd, pos_bias=gk["bias"], m=m, pages=pages)
+        win = dict(kv_cur=ent["kv_cur"], pos=pd, m=1)
+        lib.v4attn_append_batch([dict(ent, out=one[0], state=one[3]), dict(key, out=one[1], state=one[4]),
+                                 dict(win, out=one[2])])
+        for c, o, st in ((ent, sep[0], sep[3]), (key, sep[1], sep[4]), (win, sep[2], None)):
+            lib.v4attn_append(c["kv_cur"], c.get("gate_cur"), c.get("kv_prev"), c.get("gate_prev"), st,
+                              c["pos"], c.get("pos_bias"), c["m"], o, pages=c.get("pages"))
+    torch.cuda.synchronize()
+    for a, b in ((one[0].nope, sep[0].nope), (one[0].rope, sep[0].rope), (one[0].scale, sep[0].scale),
+                 (one[1].codes, sep[1].codes), (one[1].scales, sep[1].scales),
+                 (one[2].nope, sep[2].nope), (one[2].scale, sep[2].scale)):
+        assert torch.equal(a, b)
+    back = logical_view(P.kv_from_dev(one[0]), table, P_)
+    for b in range(Bn):
+        seq = {k: se[k][b] for k in ("kv_cur", "gate_cur", "kv_prev", "gate_prev")}
+        last = steps - 1 - start[b]
+        done = [i for i in range((last + 1) // m)]
+        y = np.stack([append_entry(seq, (i + 1) * m - 1, m, se["bias"]) for i in done])[None]
+        P.check_fp8_rows(C.KV("fp8", 448, 64, back.nope[b:b + 1, done], back.rope[b:b + 1, done],
+                              back.scale[b:b + 1, done]), y, 448)
