@@ -24,6 +24,8 @@
 //   and a block completes with one divide: O(1) work per step, and the same
 //   sequence of operations as k_compress (previous-role slots in order, then
 //   current ones), hence the same values.
+// k_append_batch: several appends (up to 8, each its own argument block) in
+//   one launch, workgroup (b, j) = sequence b of append j.
 #include "common.hpp"
 #include "kernels.hpp"
 
