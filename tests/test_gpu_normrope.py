@@ -179,3 +179,33 @@ def test_partial_norm_rope(lib, mode):
     torch.cuda.synchronize()
     P.check_out(o, ref)
     P.check_out(oc, ref_c)
+
+
+@pytest.mark.parametrize("kind,n,n_win", [("csa", 16, 32), ("hca", 900, 128)])
+def test_attend_norm_rope_f32_out(lib, kind, n, n_win):
+    # fp32 outputs through both epilogues (the kernel's own for one split, the
+    # merge for several): the output's RoPE dims rotated back before the store
+    print(f"attend_nr f32 out {kind} n={n}", flush=True)
+    rng = np.random.default_rng(n + 7)
+    Bn, Q, H, R, m = 2, 2, 64, 160, 4
+    comp, win, q = _inputs(rng, Bn, Q, H, n, R)
+    nr, gamma, inv = _nr(rng)
+    nd = _nr_dev(lib, gamma, inv)
+    pos = np.array([[m * n + 5, 3000], [40, m * n - 1]], np.int64)
+    qb = C.bf16_encode(q)
+    qd = P.dev(qb.view(np.int16)).view(torch.bfloat16)
+    scale = 512 ** -0.5
+    if kind == "hca":
+        _, ref = hca_attend(qb, "bf16", comp, m, win, n_win, pos, None, scale, "f32", nr=nr)
+        o = lib.v4attn_hca_attend_nr(qd, P.kv_to_dev(comp), m, P.kv_to_dev(win), n_win, P.dev(pos),
+                                     None, scale, nd, out_dtype=torch.float32)
+    else:
+        topk = np.stack([np.stack([np.sort(rng.choice(n, n, replace=False)) for _ in range(Q)])
+                         for _ in range(Bn)])
+        _, ref = csa_attend(qb, "bf16", comp, topk, win, n_win, pos, None, scale, "f32", nr=nr)
+        o = lib.v4attn_csa_attend_nr(qd, P.kv_to_dev(comp), P.dev(topk.astype(np.int32)),
+                                     P.kv_to_dev(win), n_win, P.dev(pos), None, scale, nd,
+                                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float32
+    P.check_out(o, ref)
