@@ -184,3 +184,31 @@ def test_fp8_entry_scale_and_error_bound():
     assert np.all(np.abs(dec - x) <= bound * (1 + 1e-6))
     assert np.array_equal(rope, torch.from_numpy(y[:, 448:]).to(torch.bfloat16)
                           .view(torch.int16).numpy().view(np.uint16))
+
+
+def test_kv_decode_rows_fp8_against_library_decode():
+    # the FP8 branch of the cache-row decoder against an independent decode:
+    # torch's float8_e4m3fn cast of the stored codes times the stored fp32
+    # scale, and the RoPE dims through torch's bfloat16; the decoded rows lie
+    # within the e4m3 half-spacing of the encoded values (a dropped, inverted
+    # or misplaced scale fails both)
+    rng = np.random.default_rng(17)
+    y = (rng.standard_normal((2, 40, 512)) / np.sqrt(512)).astype(np.float32)
+    y[1, 3] *= 1e3
+    y[0, 5, :448] = 0.0
+    kv = C.kv_encode(y, "fp8", 448)
+    rows = np.array([0, 3, 5, 39, 7, 3])
+    for b in range(2):
+        got = C.kv_decode_rows(kv, b, rows)
+        codes = torch.from_numpy(kv.nope[b, rows].copy()).view(torch.float8_e4m3fn)
+        lib_nope = codes.to(torch.float64).numpy() * kv.scale[b, rows].astype(np.float64)[:, None]
+        lib_rope = (torch.from_numpy(kv.rope[b, rows].copy().view(np.int16)).view(torch.bfloat16)
+                    .to(torch.float64).numpy())
+        assert np.array_equal(got[:, :448], lib_nope)
+        assert np.array_equal(got[:, 448:], lib_rope)
+        x = y[b, rows].astype(np.float64)
+        s = kv.scale[b, rows].astype(np.float64)[:, None]
+        bound = np.maximum(np.abs(x[:, :448]) * 2.0 ** -4, 2.0 ** -10 * s)
+        assert np.all(np.abs(got[:, :448] - x[:, :448]) <= bound * (1 + 1e-6))
+        assert np.all(np.abs(got[:, 448:] - x[:, 448:]) <= np.abs(x[:, 448:]) * 2.0 ** -8)
+    assert np.all(C.kv_decode_rows(kv, 0, [5])[0, :448] == 0.0)
