@@ -50,6 +50,8 @@ typedef int32_t v4a_status;
 #define V4A_ERR_UNSUPPORTED (-2)  /* outside the supported shape/format set   */
 #define V4A_ERR_WORKSPACE   (-3)  /* workspace missing or too small           */
 #define V4A_ERR_HIP         (-4)  /* HIP runtime / launch error (see below)   */
+#define V4A_ERR_SCRATCH     (-5)  /* beyond the fixed scratch of the          */
+                                  /* allocation-free entry point              */
 
 /* ---------------------------------------------------------------- formats */
 #define V4A_F32              0  /* fp32                                        */
@@ -198,6 +200,31 @@ v4a_status v4attn_index_topk(const void *q_idx, int32_t q_dtype, const float *w,
                              int32_t B, int32_t Q, int32_t H_I, int32_t m,
                              int32_t k, int32_t *topk,
                              void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * v4attn_index_topk_noalloc -- v4attn_index_topk for callers that cannot
+ * allocate device memory or own a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments
+ * (minus ws / ws_bytes), results, supported set and errors as
+ * v4attn_index_topk; the call's scratch (scores, histograms, candidates)
+ * lives in a fixed device array of the library, 32 MiB on every GPU the
+ * library runs on, held until the process ends.  The call allocates nothing
+ * (no hipMalloc / hipFree); its first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress, once per device).
+ *   V4A_ERR_SCRATCH  the call needs more than 32 MiB, i.e. more than
+ *                    v4attn_workspace_bytes(V4A_OP_INDEX_TOPK, ...) allows
+ *                    (about 1.15 MiB per query row at 262144 MXFP4
+ *                    blocks: up to 27 rows B * Q at a 1M-token context);
+ *                    nothing is enqueued.
+ * Every call on a GPU shares that GPU's array and leaves its contents
+ * behind; the kernels clear what must start at zero.  Calls that overlap on
+ * one GPU (on different streams, or from different threads) race on the
+ * array: the caller orders them (one stream, or events).
+ */
+v4a_status v4attn_index_topk_noalloc(const void *q_idx, int32_t q_dtype, const float *w,
+                                     const v4a_idx *keys, const int64_t *pos,
+                                     int32_t B, int32_t Q, int32_t H_I, int32_t m,
+                                     int32_t k, int32_t *topk, void *stream);
 
 /*
  * v4attn_index_topk_bf16 -- the selector variant with BF16 index scores

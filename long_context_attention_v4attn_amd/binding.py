@@ -85,6 +85,7 @@ _SIGS = {
     "v4attn_index_topk": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "v4attn_index_topk_bf16": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ,
                                       _P]),
+    "v4attn_index_topk_noalloc": (_I32, [_P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]),
     "v4attn_csa_attend": (_I32, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32, _I32,
                                  _P, _I32, _P, _SZ, _P]),
     "v4attn_csa_attend_nr": (_I32, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32, _I32,
@@ -291,6 +292,19 @@ def _index_topk(name, q_idx, w, keys, pos, m, k, topk, ws, stream):
 
 def v4attn_index_topk(q_idx, w, keys, pos, m, k, topk=None, ws=None, stream=None):
     return _index_topk("v4attn_index_topk", q_idx, w, keys, pos, m, k, topk, ws, stream)
+
+
+def v4attn_index_topk_noalloc(q_idx, w, keys, pos, m, k, topk, stream=None):
+    """v4attn_index_topk on the library's fixed device scratch: the caller
+    passes the output `topk` (int32 [B][Q][k]); nothing is allocated."""
+    lib = load()
+    _need_cuda(q_idx, w, pos, topk)
+    B, Q, H, d = q_idx.shape
+    st = keys.c_struct()
+    s = lib.v4attn_index_topk_noalloc(_ptr(q_idx), _dtype_code(q_idx), _ptr(w), ctypes.byref(st),
+                                      _ptr(pos), B, Q, H, m, k, _ptr(topk), _stream(stream))
+    _check(s, "v4attn_index_topk_noalloc")
+    return topk
 
 
 def v4attn_index_topk_bf16(q_idx, w, keys, pos, m, k, topk=None, ws=None, stream=None):

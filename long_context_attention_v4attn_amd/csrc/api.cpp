@@ -287,7 +287,7 @@ static v4a_status index_topk(const void* q_idx, int32_t q_dtype, const float* w,
                              const v4a_idx* keys, const int64_t* pos, int32_t B, int32_t Q,
                              int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
                              size_t ws_bytes, void* stream, int score_bf16,
-                             const v4a_pages* pages = nullptr) {
+                             const v4a_pages* pages = nullptr, bool fixed_scratch = false) {
   if (B < 0 || Q < 0) return V4A_ERR_INVALID;
   if (B == 0 || Q == 0) return V4A_OK;     // nothing to read or write
   if (!q_idx || !w || !keys || !pos || !topk || H_I < 1 || k < 1 || m < 1)
@@ -328,7 +328,15 @@ static v4a_status index_topk(const void* q_idx, int32_t q_dtype, const float* w,
     if (s != V4A_OK) return s;
   }
   size_t need = index_workspace_bytes(B, Q, H_I, keys->d, a.cap, a.key_mx);
-  if (!ws || ws_bytes < need) return V4A_ERR_WORKSPACE;
+  if (fixed_scratch) {
+    // the library's own device array (no allocation): the call's scratch
+    // must fit it
+    if (need > kIndexScratchBytes) return V4A_ERR_SCRATCH;
+    hipError_t e = index_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e);
+  } else if (!ws || ws_bytes < need) {
+    return V4A_ERR_WORKSPACE;
+  }
   index_carve(a, ws);
   if (B == 0 || Q == 0) return V4A_OK;
   KernelEvents ev;
@@ -340,6 +348,14 @@ v4a_status v4attn_index_topk(const void* q_idx, int32_t q_dtype, const float* w,
                              int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
                              size_t ws_bytes, void* stream) {
   return index_topk(q_idx, q_dtype, w, keys, pos, B, Q, H_I, m, k, topk, ws, ws_bytes, stream, 0);
+}
+
+v4a_status v4attn_index_topk_noalloc(const void* q_idx, int32_t q_dtype, const float* w,
+                                     const v4a_idx* keys, const int64_t* pos, int32_t B,
+                                     int32_t Q, int32_t H_I, int32_t m, int32_t k, int32_t* topk,
+                                     void* stream) {
+  return index_topk(q_idx, q_dtype, w, keys, pos, B, Q, H_I, m, k, topk, nullptr, 0, stream, 0,
+                    nullptr, true);
 }
 
 v4a_status v4attn_index_topk_bf16(const void* q_idx, int32_t q_dtype, const float* w,
@@ -512,6 +528,8 @@ const char* v4attn_status_str(v4a_status s) {
     case V4A_ERR_UNSUPPORTED: return "unsupported shape or format";
     case V4A_ERR_WORKSPACE: return "workspace missing or too small";
     case V4A_ERR_HIP: return "HIP runtime error";
+    case V4A_ERR_SCRATCH:
+      return "the call needs more scratch than the allocation-free entry point's fixed 32 MiB";
     default: return "unknown status";
   }
 }

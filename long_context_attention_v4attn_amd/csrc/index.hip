@@ -34,6 +34,8 @@
 //                come out ascending with no sort; the tail is -1.  No
 //                workgroup waits for another, and the output is
 //                deterministic.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -1288,6 +1290,38 @@ __global__ void __launch_bounds__(kFThreads) k_emit_bf16(IndexArgs a) {
       pos++;
     }
   }
+}
+
+// ---------------------------------------------------------------- fixed scratch
+// The allocation-free index call carves its workspace out of this array
+// instead of a caller's buffer.  Every GPU the library runs on holds its own
+// copy (loaded with the code object, kept until the process ends).  Host
+// code never passes the array's name to a kernel (on the host it stands for
+// a host-side shadow, not a device address): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[kIndexScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t index_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEvents* ev) {

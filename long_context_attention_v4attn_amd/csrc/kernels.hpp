@@ -104,6 +104,10 @@ struct KernelEvents {
   hipEvent_t start, stop;
 };
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEvents* ev);
+// Fixed device scratch of the allocation-free index call: its size, and its
+// device address on the current device (looked up once per device).
+constexpr size_t kIndexScratchBytes = (size_t)32 << 20;
+hipError_t index_scratch(void** ptr);
 
 // ---------------------------------------------------------------- attend
 struct AttendArgs {

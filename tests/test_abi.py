@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(clib):
 
 def test_status_strings_and_version(clib):
     from long_context_attention_v4attn_amd import binding as B
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert B.v4attn_status_str(s)
     assert clib.v4attn_version() >= 100
     assert clib.v4attn_last_hip_error() == 0
@@ -95,6 +95,13 @@ def test_invalid_arguments_rejected_on_host(clib):
     assert clib.v4attn_index_topk_bf16(FAKE, 1, FAKE, r(ix_bad), FAKE, 1, 1, 16, 4, 8, FAKE, FAKE, 1 << 30,
                                        None) == -2
     assert clib.v4attn_index_topk_bf16(FAKE, 1, FAKE, r(ix), FAKE, 1, 1, 16, 4, 8, FAKE, None, 0, None) == -3
+    # the allocation-free variant: the same validation, and a call that needs
+    # more than its fixed scratch (28 rows over 262144 blocks) -> -5, all on
+    # the host (nothing is read or enqueued)
+    assert clib.v4attn_index_topk_noalloc(FAKE, 1, FAKE, r(ix), FAKE, 1, 1, 16, 4, 0, FAKE, None) == -1
+    assert clib.v4attn_index_topk_noalloc(FAKE, 1, FAKE, r(ix_bad), FAKE, 1, 1, 16, 4, 8, FAKE, None) == -2
+    ix_1m = _Idx(3, 128, 262144, 0x1000, 0x2000)
+    assert clib.v4attn_index_topk_noalloc(FAKE, 1, FAKE, r(ix_1m), FAKE, 28, 1, 16, 4, 2048, FAKE, None) == -5
     # attend: H not a multiple of 16 on the FP8 path, window ring too small, f32 q on FP8
     win = _KV(2, 448, 64, 0, 64, 0x1000, 0x2000, 0x3000)
     assert clib.v4attn_hca_attend(FAKE, 1, r(kv), 128, r(kv), 16, FAKE, None, ctypes.c_float(0.1),
