@@ -577,6 +577,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk leg")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="run one leg alone (for profiling): the decode step and its kernels, "
+                         "or the prefill chunk")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (the reference kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -610,6 +613,9 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     cc, ch = synth.WORKLOADS[CSA_WID], synth.WORKLOADS[HCA_WID]
+    if args.only == "prefill":
+        print(json.dumps({"prefill": bench_prefill(v4, torch, log)}))
+        return
 
     reps, gc, gh = build_inputs(v4, torch, args.replicas, log)
     ws = {
@@ -797,6 +803,9 @@ def main():
             "recall_vs_fp32": round(float(np.mean(recalls)), 5),
             "recall_min": round(float(np.min(recalls)), 5)},
     }
+    if args.only == "decode":
+        print(json.dumps(result))
+        return
     log("production shapes ...")
     result["production_shapes"] = bench_production(v4, torch, reps, ws, cc, ch)
     log("norm + RoPE variants ...")
