@@ -118,6 +118,58 @@ class Replica:
     pass
 
 
+def copy_bandwidth(torch, nbytes=1 << 30, n=10):
+    """Measured HBM streaming rate: a plain device-to-device copy of `nbytes`
+    (read + written), n launches timed with events; GB/s of read + write."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / n
+    del x, y
+    torch.cuda.empty_cache()
+    return 2 * nbytes / t / 1e9
+
+
+def upload(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def quant_kv(v4, torch, x, d_nope=448, d_rope=64, fmt=None):
+    """Rows x [B][n][D] (fp32, host) stored as a cache by the library
+    (v4attn_compress with m = 1)."""
+    B, n = x.shape[:2]
+    kv = v4.KVCache.empty(B, n, d_nope, d_rope, v4.KV_FP8_BF16ROPE if fmt is None else fmt)
+    xs = upload(torch, x)
+    v4.v4attn_compress(xs, None, None, None, None, 1, 0, kv)
+    del xs
+    return kv
+
+
+def quant_keys(v4, torch, x, fmt=None):
+    B, n, d = x.shape
+    ix = v4.IdxCache.empty(B, n, d, v4.IDX_MXFP4 if fmt is None else fmt)
+    xs = upload(torch, x)
+    v4.v4attn_compress(xs, None, None, None, None, 1, 0, ix)
+    del xs
+    return ix
+
+
+def clone_kv(v4, kv):
+    return v4.KVCache(kv.fmt, kv.d_nope, kv.d_rope, kv.nope.clone(), kv.rope.clone(),
+                      None if kv.scale is None else kv.scale.clone())
+
+
+def clone_keys(v4, ix):
+    return v4.IdxCache(ix.fmt, ix.d, ix.codes.clone(), None if ix.scales is None else ix.scales.clone())
+
+
 def build_inputs(v4, torch, replicas, log):
     from long_context_attention_v4attn_amd import synth
     dev = "cuda"
@@ -127,32 +179,17 @@ def build_inputs(v4, torch, replicas, log):
     gh = synth.decode_inputs(HCA_WID)
     log(f"synthetic inputs drawn in {time.time() - t0:.1f}s")
 
-    def up(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    def quant_kv(x, B, n):
-        kv = v4.KVCache.empty(B, n, 448, 64, v4.KV_FP8_BF16ROPE)
-        xs = up(x)
-        v4.v4attn_compress(xs, None, None, None, None, 1, 0, kv)
-        del xs
-        return kv
-
-    def quant_keys(x, B, n):
-        ix = v4.IdxCache.empty(B, n, 128, v4.IDX_MXFP4)
-        xs = up(x)
-        v4.v4attn_compress(xs, None, None, None, None, 1, 0, ix)
-        del xs
-        return ix
+    up = lambda a: upload(torch, a)
+    qkv = lambda x: quant_kv(v4, torch, x)
+    qkeys = lambda x: quant_keys(v4, torch, x)
 
     t0 = time.time()
     base = Replica()
-    nc = cc["ctx"] // cc["m"]
-    nh = ch["ctx"] // ch["m"]
-    base.c_comp = quant_kv(gc["comp"], cc["B"], nc)
-    base.c_keys = quant_keys(gc["keys"], cc["B"], nc)
-    base.c_win = quant_kv(gc["win"], cc["B"], cc["n_win"])
-    base.h_comp = quant_kv(gh["comp"], ch["B"], nh)
-    base.h_win = quant_kv(gh["win"], ch["B"], ch["n_win"])
+    base.c_comp = qkv(gc["comp"])
+    base.c_keys = qkeys(gc["keys"])
+    base.c_win = qkv(gc["win"])
+    base.h_comp = qkv(gh["comp"])
+    base.h_win = qkv(gh["win"])
     base.c_q = up(gc["q"]).to(torch.bfloat16)
     base.c_qi = up(gc["q_idx"]).to(torch.bfloat16)
     base.c_w = up(gc["w"])
@@ -162,17 +199,12 @@ def build_inputs(v4, torch, replicas, log):
     torch.cuda.synchronize()
     log(f"caches quantised on the GPU in {time.time() - t0:.1f}s")
 
-    def clone_kv(kv):
-        return v4.KVCache(kv.fmt, kv.d_nope, kv.d_rope, kv.nope.clone(), kv.rope.clone(),
-                          None if kv.scale is None else kv.scale.clone())
-
     reps = [base]
     for _ in range(replicas - 1):
         r = Replica()
-        r.c_comp, r.c_win, r.h_comp, r.h_win = (clone_kv(base.c_comp), clone_kv(base.c_win),
-                                                clone_kv(base.h_comp), clone_kv(base.h_win))
-        r.c_keys = v4.IdxCache(base.c_keys.fmt, 128, base.c_keys.codes.clone(),
-                               base.c_keys.scales.clone())
+        r.c_comp, r.c_win, r.h_comp, r.h_win = (clone_kv(v4, base.c_comp), clone_kv(v4, base.c_win),
+                                                clone_kv(v4, base.h_comp), clone_kv(v4, base.h_win))
+        r.c_keys = clone_keys(v4, base.c_keys)
         for name in ("c_q", "c_qi", "c_w", "c_pos", "h_q", "h_pos"):
             setattr(r, name, getattr(base, name).clone())
         reps.append(r)
@@ -397,6 +429,188 @@ def bench_paged(v4, torch, reps, ws, cc, ch, n=8, page_tokens=8192):
                            "v4attn_append_batch launch (and as five v4attn_append calls)"}
 
 
+def bench_append(v4, torch, r, cc, ch, n):
+    """Seconds per launch of one decode step's cache appends per layer, each
+    layer one v4attn_append_batch: CSA entry (overlapped pooling, m = 4),
+    indexer key and window token at B = 4; HCA entry (m = 128) and window
+    token at B = 16.  Position ctx - 1 completes a block of both layers, so
+    every append pools its block and stores it.  Into copies of replica r's
+    caches (the appended rows would otherwise change its last blocks)."""
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(11)
+    rows = lambda B, d, s=1.0: (torch.randn(B, d, device=dev, generator=g) * s).to(torch.bfloat16)
+    D, dI, Bc, Bh = 512, 128, cc["B"], ch["B"]
+    c_tok = [rows(Bc, D, D ** -0.5), rows(Bc, D), rows(Bc, D, D ** -0.5), rows(Bc, D)]
+    k_tok = [rows(Bc, dI, dI ** -0.5), rows(Bc, dI), rows(Bc, dI, dI ** -0.5), rows(Bc, dI)]
+    h_tok = [rows(Bh, D, D ** -0.5), rows(Bh, D)]
+    c_bias = torch.randn(2 * cc["m"], D, device=dev, generator=g) * 0.5
+    k_bias = torch.randn(2 * cc["m"], dI, device=dev, generator=g) * 0.5
+    h_bias = torch.randn(ch["m"], D, device=dev, generator=g) * 0.5
+    c_pos, h_pos = r.c_pos.reshape(-1).contiguous(), r.h_pos.reshape(-1).contiguous()
+    comp, keys, win = clone_kv(v4, r.c_comp), clone_keys(v4, r.c_keys), clone_kv(v4, r.c_win)
+    hcomp, hwin = clone_kv(v4, r.h_comp), clone_kv(v4, r.h_win)
+    csa_batch = [dict(kv_cur=c_tok[0], gate_cur=c_tok[1], kv_prev=c_tok[2], gate_prev=c_tok[3],
+                      state=v4.append_state(Bc, D), pos=c_pos, pos_bias=c_bias, m=cc["m"], out=comp),
+                 dict(kv_cur=k_tok[0], gate_cur=k_tok[1], kv_prev=k_tok[2], gate_prev=k_tok[3],
+                      state=v4.append_state(Bc, dI), pos=c_pos, pos_bias=k_bias, m=cc["m"], out=keys),
+                 dict(kv_cur=c_tok[0], pos=c_pos, m=1, out=win)]
+    hca_batch = [dict(kv_cur=h_tok[0], gate_cur=h_tok[1], state=v4.append_state(Bh, D), pos=h_pos,
+                      pos_bias=h_bias, m=ch["m"], out=hcomp),
+                 dict(kv_cur=h_tok[0], pos=h_pos, m=1, out=hwin)]
+    t_c = graph_time(torch, [lambda: v4.v4attn_append_batch(csa_batch)] * 8, n)
+    t_h = graph_time(torch, [lambda: v4.v4attn_append_batch(hca_batch)] * 8, n)
+    del comp, keys, win, hcomp, hwin
+    torch.cuda.empty_cache()
+    return t_c, t_h
+
+
+# ---------------------------------------------------------------- the other decode configurations
+
+def bench_csa_128k(v4, torch, log, replicas=8, n=25):
+    """csa_decode_128k: B = 8 sequences of 131072 tokens (32768 blocks),
+    top-1024, window 128, 64 heads x D = 512, indexer 16 x 128 MXFP4.  A step
+    is v4attn_index_topk then v4attn_csa_attend for the batch; `replicas`
+    address-distinct cache copies (8 x 170 MB) cycled in one graph, as in the
+    headline; the index scan kernel timed live."""
+    from long_context_attention_v4attn_amd import synth
+    wid = 2
+    c = synth.WORKLOADS[wid]
+    B, cap, k, nw = c["B"], c["ctx"] // c["m"], c["k"], c["n_win"]
+    t0 = time.time()
+    g = synth.decode_inputs(wid)
+    base = Replica()
+    base.comp, base.keys, base.win = (quant_kv(v4, torch, g["comp"]), quant_keys(v4, torch, g["keys"]),
+                                      quant_kv(v4, torch, g["win"]))
+    base.q = upload(torch, g["q"]).to(torch.bfloat16)
+    base.qi = upload(torch, g["q_idx"]).to(torch.bfloat16)
+    base.w, base.pos = upload(torch, g["w"]), upload(torch, g["pos"])
+    del g
+    reps = [base]
+    for _ in range(replicas - 1):
+        r = Replica()
+        r.comp, r.keys, r.win = clone_kv(v4, base.comp), clone_keys(v4, base.keys), clone_kv(v4, base.win)
+        r.q, r.qi, r.w, r.pos = base.q.clone(), base.qi.clone(), base.w.clone(), base.pos.clone()
+        reps.append(r)
+    for r in reps:
+        r.topk = torch.empty(B, 1, k, dtype=torch.int32, device="cuda")
+        r.out = torch.empty_like(r.q)
+    wsi = torch.empty(v4.v4attn_workspace_bytes(v4.OP_INDEX_TOPK, B, 1, c["H_I"], c["d_I"], cap, k, 0),
+                      dtype=torch.uint8, device="cuda")
+    wsa = torch.empty(max(1, v4.v4attn_workspace_bytes(v4.OP_CSA_ATTEND, B, 1, c["H"], 512, 0, k, nw)),
+                      dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"csa_decode_128k inputs on the GPU in {time.time() - t0:.1f}s")
+    sc = 512 ** -0.5
+    f_i = [(lambda r=r: v4.v4attn_index_topk(r.qi, r.w, r.keys, r.pos, c["m"], k, topk=r.topk, ws=wsi))
+           for r in reps]
+    f_a = [(lambda r=r: v4.v4attn_csa_attend(r.q, r.comp, r.topk, r.win, nw, r.pos, None, sc,
+                                             out=r.out, ws=wsa)) for r in reps]
+    t_step = graph_time(torch, [f for pair in zip(f_i, f_a) for f in pair], n) * 2
+    t_i, t_a = graph_time(torch, f_i, n), graph_time(torch, f_a, n)
+    t_scan = kernel_time_of(v4, torch, f_i, 4 * replicas)
+    ab = algorithmic_bytes(c, c)
+    step_bytes = B * (ab["index"] + ab["csa_attend"])
+    scan_bytes = B * (cap * (c["d_I"] // 2 + c["d_I"] // 32) + c["H_I"] * c["d_I"] * 2 + c["H_I"] * 4)
+    for r in reps:
+        del r.comp, r.keys, r.win
+    del reps, wsi, wsa
+    torch.cuda.empty_cache()
+    return {
+        "workload": "csa_decode_128k (B=8, 32768 blocks, top-1024, window 128; 64 heads x D=512; "
+                    "indexer 16 x 128 MXFP4)",
+        "queries_per_s": round(B / t_step, 1), "us_per_step": round(t_step * 1e6, 3),
+        "calls_us": {"index_topk": round(t_i * 1e6, 3), "csa_attend": round(t_a * 1e6, 3)},
+        "step_bytes": step_bytes,
+        "step_GBps": round(step_bytes / t_step / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / t_step / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "k_score_mx [index_topk]", "t_us": round(t_scan * 1e6, 3),
+                     "algorithmic_bytes": scan_bytes,
+                     "achieved": round(scan_bytes / t_scan / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(scan_bytes / t_scan / 1e9 / HBM_PEAK_GBPS, 4)},
+    }
+
+
+def bench_csa_f32_4k(v4, torch, log, n=50):
+    """csa_decode_f32_4k: the fp32 CSA pipeline of one sequence, a step being
+    the full pipeline: pool 4096 raw tokens into 1024 entries (D = 128) and
+    1024 indexer keys (d = 64), store the last 128 tokens in the window ring,
+    then top-64 selection and attention for the decode query (8 heads).  A
+    correctness configuration, launch-bound: 8 steps per graph on one set of
+    buffers (about 13 MB, resident in the caches)."""
+    from long_context_attention_v4attn_amd import synth
+    m, T, D, dI, k, nw = 4, 4096, 128, 64, 64, 128
+    g = synth.workload1_inputs()
+    prev = lambda x: np.concatenate([np.zeros_like(x[:, :m]), x[:, :T - m]], axis=1)
+    up = lambda a: upload(torch, a)
+    kv_b, z_b, kv_a, z_a, bias = (up(g["kv_b"]), up(g["z_b"]), up(prev(g["kv_a"])), up(prev(g["z_a"])),
+                                  up(g["bias"]))
+    ki_b, zi_b, ki_a, zi_a, bias_i = (up(g["ki_b"]), up(g["zi_b"]), up(prev(g["ki_a"])),
+                                      up(prev(g["zi_a"])), up(g["bias_i"]))
+    tail = up(g["kv_b"][:, T - nw:])
+    q, qi, w, pos = up(g["q"]), up(g["q_idx"]), up(g["w"]), up(g["pos"])
+    comp = v4.KVCache.empty(1, T // m, 64, 64, v4.F32)
+    keys = v4.IdxCache.empty(1, T // m, dI, v4.F32)
+    win = v4.KVCache.empty(1, nw, 64, 64, v4.F32)
+    topk = torch.empty(1, 1, k, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    wsi = torch.empty(v4.v4attn_workspace_bytes(v4.OP_INDEX_TOPK, 1, 1, 4, dI, T // m, k, 0),
+                      dtype=torch.uint8, device="cuda")
+    wsa = torch.empty(max(1, v4.v4attn_workspace_bytes(v4.OP_CSA_ATTEND, 1, 1, 8, D, 0, k, nw)),
+                      dtype=torch.uint8, device="cuda")
+
+    def compress():
+        v4.v4attn_compress(kv_b, z_b, kv_a, z_a, bias, m, 0, comp)
+        v4.v4attn_compress(ki_b, zi_b, ki_a, zi_a, bias_i, m, 0, keys)
+        v4.v4attn_compress(tail, None, None, None, None, 1, T - nw, win)
+
+    def decode():
+        v4.v4attn_index_topk(qi, w, keys, pos, m, k, topk=topk, ws=wsi)
+        v4.v4attn_csa_attend(q, comp, topk, win, nw, pos, None, D ** -0.5, out=out, ws=wsa)
+
+    step = lambda: (compress(), decode())
+    t_step = graph_time(torch, [step] * 8, n)
+    t_dec = graph_time(torch, [decode] * 8, n)
+    f32b = 4
+    comp_bytes = (4 * T * D + 4 * T * dI) * f32b + (T // m) * (D + dI) * f32b + 2 * nw * D * f32b
+    dec_bytes = ((T // m) * dI + (k + nw) * D + 2 * 8 * D + 4 * dI + 4 + k) * f32b
+    return {
+        "workload": "csa_decode_f32_4k (B=1, 4096 raw tokens pooled to 1024 blocks, top-64, window 128; "
+                    "8 heads x D=128, indexer 4 x 64; fp32)",
+        "queries_per_s": round(1.0 / t_step, 1), "us_per_step": round(t_step * 1e6, 3),
+        "decode_only_us": round(t_dec * 1e6, 3),
+        "step_bytes": comp_bytes + dec_bytes, "decode_bytes": dec_bytes,
+        "roofline": {"bound": "hbm", "what": "whole step (launch-bound: 5 launches of a few us)",
+                     "achieved": round((comp_bytes + dec_bytes) / t_step / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round((comp_bytes + dec_bytes) / t_step / 1e9 / HBM_PEAK_GBPS, 4)},
+    }
+
+
+def kernel_time_of(v4, torch, fns, n):
+    """Mean duration of the dominant kernel of the calls `fns` (cycled, n
+    eager launches), from HIP events the library records around it."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    evs = []
+    for _ in range(2 * n):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        evs.append(e)
+    torch.cuda.synchronize()
+    for s in range(n):
+        v4.v4attn_time_next_kernel(evs[2 * s].value, evs[2 * s + 1].value)
+        fns[s % len(fns)]()
+    torch.cuda.synchronize()
+    tot, ms = 0.0, ctypes.c_float()
+    for s in range(n):
+        if hip.hipEventElapsedTime(ctypes.byref(ms), evs[2 * s], evs[2 * s + 1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        tot += ms.value
+    for e in evs:
+        hip.hipEventDestroy(e)
+    return tot / n * 1e-3
+
+
 # ---------------------------------------------------------------- prefill chunk
 
 PREFILL_WID = 5
@@ -550,6 +764,30 @@ def cpu_baseline(gc, gh, log):
         hca_attend(qb, "bf16", hcomp, ch["m"], hwin, ch["n_win"], gh["pos"][b:b + 1], None, sc, "bf16")
     t_hca = (time.time() - t0) / ch["B"]
     value = 1.0 / (t_csa + t_hca)
+    # the prefill chunk (4096 tokens after 1048576 cached, one sequence): its
+    # compress is run in full; each chunk query does a decode query's work
+    # (index scores over 262145..263168 blocks, top-2048, CSA over 2176
+    # entries; HCA over 8192..8224 entries + 128), so the query part is the
+    # per-query times above x 4096: a fraction run, stated as such
+    from oracle.compress import compress
+    c5 = synth.WORKLOADS[PREFILL_WID]
+    g5 = synth.prefill_inputs(n_csa=4, n_hca=1, H=1)
+    ctx5, T5 = c5["ctx"], c5["chunk"]
+    t0 = time.time()
+    compress(g5["csa_kv_cur"], g5["csa_z_cur"], g5["csa_kv_prev"], g5["csa_z_prev"], g5["csa_bias"],
+             c5["m_csa"], ctx5)
+    compress(g5["idx_kv_cur"], g5["idx_z_cur"], g5["idx_kv_prev"], g5["idx_z_prev"], g5["idx_bias"],
+             c5["m_csa"], ctx5)
+    compress(g5["hca_kv"], g5["hca_z"], None, None, g5["hca_bias"], c5["m_hca"], ctx5)
+    t_comp5 = time.time() - t0
+    del g5
+    est5 = t_comp5 + T5 * (t_csa + t_hca)
+    prefill = {"workload": "prefill_pair_1m chunk (4096 tokens after 1048576 cached, B = 1)",
+               "compress_s": round(t_comp5, 3), "compress_fraction_run": 1.0,
+               "query_fraction_run": {"csa": round(cc["B"] / T5, 6), "hca": round(ch["B"] / T5, 6)},
+               "est_chunk_s": round(est5, 1), "tokens_per_s": round(T5 / est5, 4),
+               "how": "compress of the whole chunk timed; the query part = 4096 x the per-query "
+                      "oracle times measured on the decode queries (the same work per query)"}
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -562,7 +800,8 @@ def cpu_baseline(gc, gh, log):
             "sample": (f"{cc['B']} CSA queries over one 1M-context cache row (index scores over "
                        f"262144 blocks, top-2048, attend 2176 entries) + {ch['B']} HCA queries over "
                        f"one 8192-entry row; oracle s/query: csa {t_csa:.3f}, hca {t_hca:.3f}"),
-            "cpu_model": cpu, "s_per_csa_query": t_csa, "s_per_hca_query": t_hca}
+            "cpu_model": cpu, "s_per_csa_query": t_csa, "s_per_hca_query": t_hca,
+            "prefill_chunk": prefill}
 
 
 # ---------------------------------------------------------------- main
@@ -599,11 +838,19 @@ def main():
     if args.calibrate_copy:
         x = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         for _ in range(10):
             y.copy_(x)
+        e1.record()
         torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 10
         print(json.dumps({"calibration": "device copy", "bytes_read": x.numel() * 4,
-                          "bytes_written": y.numel() * 4, "launches": 10}))
+                          "bytes_written": y.numel() * 4, "launches": 11,
+                          "copy_GBps": round(2 * x.numel() * 4 / t / 1e9, 1),
+                          "peak_GBps": HBM_PEAK_GBPS}))
         return
     import long_context_attention_v4attn_amd as v4
     from long_context_attention_v4attn_amd import synth
@@ -661,7 +908,8 @@ def main():
         hca_layer = lambda: [cs[2]() for cs in calls]
         per_call_g = [(lambda i=i: [cs[i]() for cs in calls]) for i in range(4)]
 
-    for _ in range(max(1, args.warmup // R)):
+    warm_rounds = max(1, -(-args.warmup // R))
+    for _ in range(warm_rounds):
         csa_layer()
         hca_layer()
     torch.cuda.synchronize()
@@ -710,37 +958,32 @@ def main():
 
     # ---- dominant kernels, timed live with HIP events recorded by the
     # library immediately around each kernel (eager launches)
-    hip = ctypes.CDLL("libamdhip64.so")
-
-    def kernel_time(i, n):
-        evs = []
-        for _ in range(2 * n):
-            e = ctypes.c_void_p()
-            if hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
-            evs.append(e)
-        torch.cuda.synchronize()
-        for s in range(n):
-            v4.v4attn_time_next_kernel(evs[2 * s].value, evs[2 * s + 1].value)
-            calls[s % R][i]()
-        torch.cuda.synchronize()
-        tot = 0.0
-        ms = ctypes.c_float()
-        for s in range(n):
-            if hip.hipEventElapsedTime(ctypes.byref(ms), evs[2 * s], evs[2 * s + 1]) != 0:
-                raise RuntimeError("hipEventElapsedTime failed")
-            tot += ms.value
-        for e in evs:
-            hip.hipEventDestroy(e)
-        return tot / n * 1e-3
-
     n_k = max(20, K // 8)
     kern = {
-        "k_score_mx [index_topk]": kernel_time(0, n_k),
-        "k_attend_fp8 [csa_attend]": kernel_time(1, n_k),
-        "k_attend_fp8 [hca_attend]": kernel_time(2, n_k),
+        "k_score_mx [index_topk]": kernel_time_of(v4, torch, [cs[0] for cs in calls], n_k),
+        "k_attend_fp8 [csa_attend]": kernel_time_of(v4, torch, [cs[1] for cs in calls], n_k),
+        "k_attend_fp8 [hca_attend]": kernel_time_of(v4, torch, [cs[2] for cs in calls], n_k),
     }
 
+    # ---- the pair figure at a common B = 4: the HCA call on the first four
+    # sequences of each replica, beside the CSA layer's B = 4
+    def first4(kv):
+        return v4.KVCache(kv.fmt, kv.d_nope, kv.d_rope, kv.nope[:4], kv.rope[:4], kv.scale[:4])
+
+    sc = 512 ** -0.5
+    f_h4 = [(lambda r=r, hc=first4(r.h_comp), hw=first4(r.h_win):
+             v4.v4attn_hca_attend(r.h_q[:4], hc, ch["m"], hw, ch["n_win"], r.h_pos[:4], None, sc,
+                                  out=r.h_out[:4], ws=ws["hca"])) for r in reps]
+    t_hca4 = graph_time(torch, f_h4, n_call)
+
+    # ---- the decode-time cache appends of one step (timed separately, not
+    # in `value`): the CSA layer's entry, indexer key and window token at
+    # B = 4, the HCA layer's entry and window token at B = 16, each layer one
+    # v4attn_append_batch launch, on replica 0 at a position that completes
+    # a block of every layer
+    t_app_c, t_app_h = bench_append(v4, torch, reps[0], cc, ch, n_call)
+
+    copy_gbps = copy_bandwidth(torch)
     ab = algorithmic_bytes(cc, ch)
     af = algorithmic_flops(cc, ch)
     kb = kernel_bytes(cc, ch)
@@ -765,7 +1008,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": dm["GBps"], "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(dm["GBps"] / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(dom), "kernel": dom, "t_us": dm["t_us"],
-                "algorithmic_bytes": dm["bytes"]}
+                "algorithmic_bytes": dm["bytes"], "measured_copy_GBps": round(copy_gbps, 1)}
 
     result = {
         "metric": "CSA+HCA decode queries/sec at 1M ctx; achieved HBM GB/s vs peak",
@@ -773,7 +1016,7 @@ def main():
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warm_rounds * R,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -791,6 +1034,17 @@ def main():
         "t_hca_layer_us": round(t_hca * 1e6, 3),
         "csa_qps": round(cc["B"] / t_csa, 1),
         "hca_qps": round(ch["B"] / t_hca, 1),
+        "value_derivation": "value = 1 / (t_csa_layer / 4 + t_hca_layer / 16): the step time per "
+                            "query of each layer at its own batch (CSA B = 4, HCA B = 16), summed",
+        "pair_common_b4": {"what": "both layers at B = 4: 4 / (t_csa_layer + t_hca_attend(B = 4))",
+                           "queries_per_s": round(cc["B"] / (t_csa + t_hca4), 1),
+                           "t_hca_attend_b4_us": round(t_hca4 * 1e6, 3)},
+        "append": {"what": "the step's decode-time cache appends, not in value: one "
+                           "v4attn_append_batch per layer (CSA entry + indexer key + window token "
+                           "at B = 4; HCA entry + window token at B = 16)",
+                   "csa_layer_us": round(t_app_c * 1e6, 3), "hca_layer_us": round(t_app_h * 1e6, 3),
+                   "value_with_append": round(1.0 / ((t_csa + t_app_c) / cc["B"]
+                                                     + (t_hca + t_app_h) / ch["B"]), 1)},
         "calls": {k_: {kk: round(vv, 3) for kk, vv in m_.items()} for k_, m_ in calls_meta.items()},
         "kernels": kernels_meta,
         "replicas": R,
@@ -817,9 +1071,13 @@ def main():
     result["paged"]["contiguous"] = {"index_topk_us": round(t_idx * 1e6, 3),
                                      "csa_attend_us": round(t_csa_att * 1e6, 3),
                                      "hca_attend_us": round(t_hca_call * 1e6, 3)}
+    del csa_layer, hca_layer, per_call_g, calls, reps, ws, f_h4
+    torch.cuda.empty_cache()
+    log("csa_decode_128k ...")
+    result["csa_decode_128k"] = bench_csa_128k(v4, torch, log)
+    log("csa_decode_f32_4k ...")
+    result["csa_decode_f32_4k"] = bench_csa_f32_4k(v4, torch, log)
     if not args.no_prefill:
-        del csa_layer, hca_layer, per_call_g, calls, reps, ws
-        torch.cuda.empty_cache()
         log("prefill chunk ...")
         result["prefill"] = bench_prefill(v4, torch, log)
     if not args.no_cpu:

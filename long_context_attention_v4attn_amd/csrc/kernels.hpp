@@ -2,7 +2,6 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
-#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 

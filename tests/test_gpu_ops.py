@@ -268,6 +268,54 @@ def test_csa_attend_fp8(lib, H, k, n_comp):
     P.check_out(o32, ref)
 
 
+@pytest.mark.parametrize("kind", ["hca", "csa"])
+def test_attend_fp8_error_within_operand_rounding_bound(lib, kind):
+    """The FP8 path's arithmetic: probabilities enter the PV product as bf16
+    MFMA operands and each split's normalised partial O/l is stored in bf16;
+    everything else is fp32 on exactly widened entries.  Per output element
+    (h, d) that bounds the error by 2^-9 (A + 2 M): A = sum_e P_e |v_e,d|
+    (probability rounding), M = max_e |v_e,d| (a partial and the output are
+    means of the v_e,d, each rounded once).  Checked on fp32 outputs against
+    the oracle's exact float64 result, on lists long enough for many splits."""
+    from oracle.attend import window_positions
+    print(f"{kind} fp8 operand-rounding bound", flush=True)
+    rng = _rng(41 if kind == "hca" else 42)
+    Bn, Q, H, R, n_win, m = 2, 1, 64, 160, 128, 4
+    n_comp = 8000 if kind == "hca" else 3000
+    comp, win, q = _attend_inputs(rng, Bn, Q, H, n_comp, R)
+    pos = np.array([[m * n_comp - 1], [m * 5000 + 2]], np.int64)
+    scale = 512 ** -0.5
+    qb = C.bf16_encode(q)
+    if kind == "hca":
+        _, ref = hca_attend(qb, "bf16", comp, m, win, n_win, pos, None, scale, "f32")
+        o = _run_attend(lib, "hca", q, True, comp, win, n_win, pos, None, scale, m=m,
+                        out_dtype=torch.float32)
+        ids = [np.arange(min((p + 1) // m, n_comp)) for p in pos[:, 0]]
+    else:
+        k = 1024
+        ids = [np.sort(rng.choice(min((p + 1) // m, n_comp), k, replace=False)) for p in pos[:, 0]]
+        topk = np.stack(ids)[:, None, :]
+        _, ref = csa_attend(qb, "bf16", comp, topk, win, n_win, pos, None, scale, "f32")
+        o = _run_attend(lib, "csa", q, True, comp, win, n_win, pos, None, scale, topk=topk,
+                        out_dtype=torch.float32)
+    g = o.cpu().numpy().astype(np.float64)
+    qd = C.bf16_decode(qb).astype(np.float64)
+    worst = 0.0
+    for b in range(Bn):
+        p = int(pos[b, 0])
+        V = np.concatenate([C.kv_decode_rows(comp, b, ids[b]),
+                            C.kv_decode_rows(win, b, window_positions(p, n_win) % R)])
+        s = scale * (qd[b, 0] @ V.T)
+        Pm = np.exp(s - s.max(axis=1, keepdims=True))
+        Pm /= Pm.sum(axis=1, keepdims=True)
+        A = Pm @ np.abs(V)                       # [H][D]
+        M = np.abs(V).max(axis=0)[None, :]
+        bound = 2.0 ** -9 * (A + 2 * M) * 1.01 + 1e-7
+        err = np.abs(g[b, 0] - ref[b, 0])
+        worst = max(worst, float((err / bound).max()))
+    assert worst <= 1.0, f"error reaches {worst:.3f} of the operand-rounding bound"
+
+
 def test_attend_fp8_edge_cases(lib):
     rng = _rng(21)
     Bn, Q, H, n_comp, R = 1, 4, 16, 50, 130
