@@ -63,12 +63,14 @@ __device__ __forceinline__ void acc_add(Acc& s, float z, float v) {
   s.mx = mn;
 }
 
-// Epilogue shared by both kernels: the pooled row y (channels tid + 256 q) of
+// Epilogue shared by the kernels: the pooled row y (channels tid + NT q) of
 // block gblk of sequence b -> optional entry RMSNorm / RoPE -> the cache
 // format, at the block's ring row or pool row.  Every thread of the
 // workgroup calls it (it synchronises).
-__device__ __forceinline__ void finish_entry(const CompressArgs& a, float (&y)[kMaxChan], int b,
+template <int NT>
+__device__ __forceinline__ void finish_entry(const CompressArgs& a, float (&y)[1024 / NT], int b,
                                              int64_t gblk, float* red) {
+  constexpr int kCh = 1024 / NT;           // channels per thread (d <= 1024)
   const int m = a.m;
   const int d = a.d;
   const int64_t orow = a.pg.tab ? page_row(a.pg, b, gblk) : (int64_t)b * a.cap + (gblk % a.cap);
@@ -80,26 +82,26 @@ __device__ __forceinline__ void finish_entry(const CompressArgs& a, float (&y)[k
     if (a.nr_gamma) {
       float ss = 0.0f;
 #pragma unroll
-      for (int q = 0; q < kMaxChan; q++) ss += y[q] * y[q];   // y = 0 past d
+      for (int q = 0; q < kCh; q++) ss += y[q] * y[q];   // y = 0 past d
       ss = wave_sum(ss);
       __syncthreads();                     // red is free
       if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
       __syncthreads();
       ss = red[0];
-      for (int w = 1; w < kCompThreads / 64; w++) ss += red[w];
+      for (int w = 1; w < NT / 64; w++) ss += red[w];
       __syncthreads();                     // red is reused below
       const float r = 1.0f / sqrtf(ss / (float)d + a.nr_eps);
 #pragma unroll
-      for (int q = 0; q < kMaxChan; q++) {
-        const int c = threadIdx.x + q * kCompThreads;
+      for (int q = 0; q < kCh; q++) {
+        const int c = threadIdx.x + q * NT;
         if (c < d) y[q] = y[q] * r * a.nr_gamma[c];
       }
     }
     if (a.nr_inv) {
       const float pf = (float)(gblk * m + m - 1);
 #pragma unroll
-      for (int q = 0; q < kMaxChan; q++) {
-        const int c = threadIdx.x + q * kCompThreads;
+      for (int q = 0; q < kCh; q++) {
+        const int c = threadIdx.x + q * NT;
         const float other = __shfl_xor(y[q], 1, 64);       // channel c ^ 1
         if (c < d && c >= a.d_nope) {
           const float ang = pf * a.nr_inv[(c - a.d_nope) >> 1];
@@ -114,8 +116,8 @@ __device__ __forceinline__ void finish_entry(const CompressArgs& a, float (&y)[k
     const int dn = a.d_nope, dr = d - a.d_nope;
     if (a.out_fmt == 0) {
 #pragma unroll
-      for (int q = 0; q < kMaxChan; q++) {
-        const int c = threadIdx.x + q * kCompThreads;
+      for (int q = 0; q < kCh; q++) {
+        const int c = threadIdx.x + q * NT;
         if (c >= d) continue;
         if (c < dn) ((float*)a.o_a)[orow * dn + c] = y[q];
         else ((float*)a.o_b)[orow * dr + (c - dn)] = y[q];
@@ -125,19 +127,19 @@ __device__ __forceinline__ void finish_entry(const CompressArgs& a, float (&y)[k
     // FP8 entry: amax over the non-RoPE channels
     float am = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kMaxChan; q++) {
-      const int c = threadIdx.x + q * kCompThreads;
+    for (int q = 0; q < kCh; q++) {
+      const int c = threadIdx.x + q * NT;
       if (c < dn) am = fmaxf(am, fabsf(y[q]));
     }
     am = wave_max(am);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
     __syncthreads();
     am = red[0];
-    for (int w = 1; w < kCompThreads / 64; w++) am = fmaxf(am, red[w]);
+    for (int w = 1; w < NT / 64; w++) am = fmaxf(am, red[w]);
     const float s = am > 0.0f ? __fdiv_rn(am, kE4M3Max) : 1.0f;
 #pragma unroll
-    for (int q = 0; q < kMaxChan; q++) {
-      const int c = threadIdx.x + q * kCompThreads;
+    for (int q = 0; q < kCh; q++) {
+      const int c = threadIdx.x + q * NT;
       if (c >= d) continue;
       if (c < dn) {
         float u = __fdiv_rn(y[q], s);
@@ -153,16 +155,16 @@ __device__ __forceinline__ void finish_entry(const CompressArgs& a, float (&y)[k
   // indexer keys
   if (a.out_fmt == 0) {
 #pragma unroll
-    for (int q = 0; q < kMaxChan; q++) {
-      const int c = threadIdx.x + q * kCompThreads;
+    for (int q = 0; q < kCh; q++) {
+      const int c = threadIdx.x + q * NT;
       if (c < d) ((float*)a.o_a)[orow * d + c] = y[q];
     }
     return;
   }
   // MXFP4: d % 32 == 0, so a group of 32 channels is 32 consecutive lanes
 #pragma unroll
-  for (int q = 0; q < kMaxChan; q++) {
-    const int c = threadIdx.x + q * kCompThreads;
+  for (int q = 0; q < kCh; q++) {
+    const int c = threadIdx.x + q * NT;
     float v = c < d ? y[q] : 0.0f;
     float am = fabsf(v);
 #pragma unroll
@@ -216,7 +218,157 @@ __global__ void __launch_bounds__(kCompThreads) k_compress(CompressArgs a) {
     }
     y[q] = s.num / s.den;
   }
-  finish_entry(a, y, b, gblk, red);
+  finish_entry<kCompThreads>(a, y, b, gblk, red);
+}
+
+// Large blocks (HCA, m' = 128 slots): one workgroup of kWideThreads per
+// (block, sequence) with the slots spread over it.  A lane moves 16 bytes of
+// a token row (VW channels); the d / VW lanes of a slot group cover the row,
+// and the kWideThreads / (d / VW) groups take consecutive slot ranges (in
+// slot order, eight slots' loads in flight per lane).  A chunk of eight
+// slots is folded at once: the running max moves once per chunk and each
+// slot costs one base-2 exponential (v_exp_f32).  Each group's
+// (max, denominator, numerator) per channel goes to LDS and the groups are
+// combined in group order (deterministic), then the shared epilogue.
+constexpr int kWideThreads = 512;
+constexpr int kWideUnroll = 8;
+constexpr float kLog2eC = 1.4426950408889634f;
+
+// (mx, den, num) of a later slot range folded into an earlier one.
+__device__ __forceinline__ void acc_merge(Acc& r, const Acc& o) {
+  if (o.mx == -INFINITY) return;           // an empty range
+  if (r.mx == -INFINITY) {
+    r = o;
+    return;
+  }
+  const float mn = fmaxf(r.mx, o.mx);
+  const float sa = expf(r.mx - mn), sb = expf(o.mx - mn);
+  r.den = r.den * sa + o.den * sb;
+  r.num = r.num * sa + o.num * sb;
+  r.mx = mn;
+}
+
+template <bool kBf16>
+__global__ void __launch_bounds__(kWideThreads) k_compress_wide(CompressArgs a) {
+  constexpr int VW = kBf16 ? 8 : 4;        // channels per 16-byte load
+  __shared__ float part[kWideThreads * VW * 3];   // [group][field][d]
+  __shared__ float red[kWideThreads / 64];
+  const int j = blockIdx.x;
+  const int b = blockIdx.y;
+  const int m = a.m;
+  const int d = a.d;
+  const bool overlap = a.kv_prev != nullptr;
+  const int64_t gblk = a.t0 / m + j;
+  if (!a.pg.tab && (int64_t)(a.T / m) - j > a.cap) return;   // as k_compress
+  const bool has_prev = overlap && gblk > 0;
+  const int L = d / VW;                    // lanes per slot group
+  const int G = kWideThreads / L;          // slot groups
+  const int t = threadIdx.x;
+  const int grp = t / L;
+  const int c0 = (t % L) * VW;
+  // slot index space: overlap = previous-role rows 0..m-1 then current rows
+  // 0..m-1 (the bias rows' order); no overlap = current rows 0..m-1
+  const int nsl = overlap ? 2 * m : m;
+  const int spg = (nsl + G - 1) / G;
+  const int s_beg = grp * spg;
+  const int s_end = min(nsl, s_beg + spg);
+  const int64_t rbase = ((int64_t)b * a.T + (int64_t)j * m) * d + c0;
+  Acc acc[VW];
+#pragma unroll
+  for (int v = 0; v < VW; v++) acc[v] = Acc{-INFINITY, 0.0f, 0.0f};
+  for (int s0 = s_beg; s0 < s_end; s0 += kWideUnroll) {
+    u32x4 kv[kWideUnroll], gt[kWideUnroll];
+    f32x4 bs[kWideUnroll][VW / 4];
+#pragma unroll
+    for (int u = 0; u < kWideUnroll; u++) {
+      const int sl = s0 + u < s_end ? s0 + u : s_end - 1;   // clamped: a real slot
+      const bool prev = overlap && sl < m;
+      const int tok = prev ? sl : (overlap ? sl - m : sl);
+      const size_t idx = (size_t)(rbase + (int64_t)tok * d);
+      const void* kvp = prev ? a.kv_prev : a.kv_cur;
+      const void* gp = prev ? a.gate_prev : a.gate_cur;
+      kv[u] = kBf16 ? *(const u32x4*)((const uint16_t*)kvp + idx) : *(const u32x4*)((const float*)kvp + idx);
+      gt[u] = gp ? (kBf16 ? *(const u32x4*)((const uint16_t*)gp + idx) : *(const u32x4*)((const float*)gp + idx))
+                 : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int h = 0; h < VW / 4; h++)
+        bs[u][h] = a.bias ? *(const f32x4*)(a.bias + (size_t)sl * d + c0 + 4 * h)
+                          : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    // the chunk's slots folded at once: its max first, then one exponential
+    // per slot (base 2) against the new running max, one rescale per chunk
+    bool ok[kWideUnroll];
+#pragma unroll
+    for (int u = 0; u < kWideUnroll; u++) {
+      const int sl = s0 + u;
+      ok[u] = sl < s_end && !(overlap && sl < m && !has_prev);   // block 0: no previous rows
+    }
+#pragma unroll
+    for (int v = 0; v < VW; v++) {
+      float x[kWideUnroll], z[kWideUnroll];
+      float mc = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kWideUnroll; u++) {
+        if (kBf16) {
+          const uint32_t wk = kv[u][v / 2], wg = gt[u][v / 2];
+          x[u] = bf16_bits_to_f32((v & 1) ? (wk >> 16) : (wk & 0xFFFFu));
+          z[u] = bf16_bits_to_f32((v & 1) ? (wg >> 16) : (wg & 0xFFFFu));
+        } else {
+          x[u] = __uint_as_float(kv[u][v]);
+          z[u] = __uint_as_float(gt[u][v]);
+        }
+        z[u] += bs[u][v / 4][v % 4];
+        mc = ok[u] ? fmaxf(mc, z[u]) : mc;
+      }
+      if (mc == -INFINITY) continue;       // no slot of this chunk
+      Acc& s = acc[v];
+      const float mn = fmaxf(s.mx, mc);
+      const float mn2 = mn * kLog2eC;
+      const float r = s.mx == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(s.mx, kLog2eC, -mn2));
+      float se = 0.0f, sev = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kWideUnroll; u++) {
+        const float e = ok[u] ? __builtin_amdgcn_exp2f(fmaf(z[u], kLog2eC, -mn2)) : 0.0f;
+        se += e;
+        sev = fmaf(e, x[u], sev);
+      }
+      s.den = fmaf(s.den, r, se);
+      s.num = fmaf(s.num, r, sev);
+      s.mx = mn;
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < VW; v++) {
+    part[(grp * 3 + 0) * d + c0 + v] = acc[v].mx;
+    part[(grp * 3 + 1) * d + c0 + v] = acc[v].den;
+    part[(grp * 3 + 2) * d + c0 + v] = acc[v].num;
+  }
+  __syncthreads();
+  float y[1024 / kWideThreads];
+#pragma unroll
+  for (int q = 0; q < 1024 / kWideThreads; q++) {
+    const int c = t + q * kWideThreads;
+    y[q] = 0.0f;
+    if (c >= d) continue;
+    Acc r{part[c], part[d + c], part[2 * d + c]};
+    for (int gg = 1; gg < G; gg++)
+      acc_merge(r, Acc{part[(gg * 3) * d + c], part[(gg * 3 + 1) * d + c], part[(gg * 3 + 2) * d + c]});
+    y[q] = r.num / r.den;
+  }
+  finish_entry<kWideThreads>(a, y, b, gblk, red);
+}
+
+// Whether the wide kernel takes a call: blocks of at least 32 slots, rows
+// that split into 16-byte lanes evenly over a power-of-two lane count.
+static bool compress_wide(const CompressArgs& a) {
+  const int vw = a.in_bf16 ? 8 : 4;
+  if (a.m < 32 || a.d % vw != 0 || a.d > 1024) return false;
+  // 16-byte loads: every input must start on a 16-byte boundary
+  const uintptr_t any = (uintptr_t)a.kv_cur | (uintptr_t)a.gate_cur | (uintptr_t)a.kv_prev |
+                        (uintptr_t)a.gate_prev | (uintptr_t)a.bias;
+  if (any & 15) return false;
+  const int L = a.d / vw;
+  return L <= kWideThreads && (L & (L - 1)) == 0;
 }
 
 // State of sequence b: float [2][3][d] = (accumulator k, field: max,
@@ -275,7 +427,7 @@ __device__ __forceinline__ void append_one(const CompressArgs& a, int b) {
   if (u != m - 1 || a.no_store) return;    // uniform: no entry to store
   // a block past the sequence's pages is not stored
   if (a.pg.tab && (blk >> a.pg.psh) >= a.pg.tab_ld) return;
-  finish_entry(a, y, b, blk, red);
+  finish_entry<kCompThreads>(a, y, b, blk, red);
 }
 
 template <bool kBf16>
@@ -314,6 +466,13 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   }
   const int nb = a.T / a.m;
   if (nb == 0) return hipSuccess;
+  if (compress_wide(a)) {
+    if (a.in_bf16)
+      hipLaunchKernelGGL(k_compress_wide<true>, dim3(nb, a.B), dim3(kWideThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_compress_wide<false>, dim3(nb, a.B), dim3(kWideThreads), 0, st, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_compress, dim3(nb, a.B), dim3(kCompThreads), 0, st, a);
   return hipGetLastError();
 }

@@ -27,6 +27,9 @@ def _f32(rng, shape, std=1.0):
 # ---------------------------------------------------------------- compress
 
 @pytest.mark.parametrize("m,overlap,t0,fmt,in_bf16", [
+    (32, True, 0, "fp8", True),
+    (64, True, 128, "f32", False),
+    (128, False, 0, "f32", True),
     (4, True, 0, "fp8", False),
     (4, True, 64, "fp8", True),
     (128, False, 0, "fp8", False),
@@ -65,14 +68,15 @@ def test_compress_kv(lib, m, overlap, t0, fmt, in_bf16):
         P.check_f32_rows(full, y)
 
 
-@pytest.mark.parametrize("fmt,overlap,d", [("mxfp4", True, 128), ("mxfp4", False, 128),
-                                           ("f32", True, 64), ("mxfp4", True, 256)])
-def test_compress_index_keys(lib, fmt, overlap, d):
-    print(f"compress keys fmt={fmt} overlap={overlap} d={d}", flush=True)
-    m, Bn, T, t0 = 4, 3, 64, 16
+@pytest.mark.parametrize("fmt,overlap,d,m", [("mxfp4", True, 128, 4), ("mxfp4", False, 128, 4),
+                                             ("f32", True, 64, 4), ("mxfp4", True, 256, 4),
+                                             ("mxfp4", False, 128, 128), ("mxfp4", True, 128, 32)])
+def test_compress_index_keys(lib, fmt, overlap, d, m):
+    print(f"compress keys fmt={fmt} overlap={overlap} d={d} m={m}", flush=True)
+    Bn, T, t0 = 3, 16 * m, 4 * m
     g = synth.compress_inputs(2, Bn, T, d, m, overlap, t0)
     y = compress(g["kv_cur"], g["gate_cur"], g["kv_prev"], g["gate_prev"], g["bias"], m, t0)
-    cap = 40
+    cap = (t0 + T) // m + 4
     out = lib.IdxCache.empty(Bn, cap, d, lib.IDX_MXFP4 if fmt == "mxfp4" else lib.F32)
     lib.v4attn_compress(P.dev(g["kv_cur"]), P.dev(g["gate_cur"]),
                         None if g["kv_prev"] is None else P.dev(g["kv_prev"]),
