@@ -27,9 +27,15 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
+# per-source device flags: the index scans consume each MFMA result at once
+# in the VALU epilogue, so their accumulators are taken in VGPRs (no
+# accumulator-register reads)
+EXTRA = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc()] + HIPFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + HIPFLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc(), "-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__",
                "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]

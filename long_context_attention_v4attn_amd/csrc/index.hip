@@ -54,8 +54,25 @@ constexpr int kPer = 16;                   // consecutive scores per filter thre
 constexpr int kFilterChunk = kFThreads * kPer;   // scores per filter workgroup
 static_assert(kBins1 == kFThreads, "one first-digit bin per filter thread");
 constexpr int kCtr = 8;                    // counters per query
+constexpr int kFbSlot = 1;                 // counter slot: the row takes the full-score path
+constexpr int kCntSlot = 6;                // counter slot: candidates above the sampled threshold
+constexpr int kThrSlot = 7;                // counter slot: the sampled threshold key
 __host__ __device__ inline int64_t score_ld(int64_t cap) { return (cap + 63) / 64 * 64; }
 __host__ __device__ inline int64_t n_chunks(int64_t cap) { return (cap + kFilterChunk - 1) / kFilterChunk; }
+// Sampled-threshold selection of query-tiled scans (prefill chunks): the
+// sample is every 16th tile of 16 blocks (blocks 256 j .. 256 j + 15).
+__host__ __device__ inline int64_t n_sampled(int64_t nv) {
+  return (nv >> 8) * 16 + ((nv & 255) < 16 ? (nv & 255) : 16);
+}
+__host__ __device__ inline int64_t samp_ld(int64_t cap) { return (n_sampled(cap) + 63) / 64 * 64; }
+constexpr int kFbRows = 32;                // rows the full-score filters take at a time
+constexpr int kThrPer = 68;                // sample keys per k_thresh thread (n_sampled <= 17408)
+constexpr int kPfBmWords = 8448;           // its id bitmap in LDS: up to 270336 blocks
+// The query-tiled scan (16 index heads, MXFP4 keys, >= 8 queries per
+// sequence) takes the sampled-threshold path when the id bitmap fits.
+__host__ __device__ inline bool pf_sampled(int64_t cap, int H, int Q, int key_mx) {
+  return key_mx && H == 16 && Q >= 8 && cap <= (int64_t)kPfBmWords * 32;
+}
 
 constexpr int kWaveTiles = 8;              // 8 tiles x 16 blocks per wave and iteration
 constexpr int kScanWaves = 4;              // waves per scan workgroup
@@ -98,6 +115,8 @@ size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx
   n += align256(R * kCtr * sizeof(uint32_t));
   n += align256(R * kCandCap * sizeof(uint64_t));
   n += align256(R * (size_t)n_chunks(cap) * sizeof(uint32_t));
+  if (pf_sampled(cap, H, Q, key_mx))
+    n += align256(R * (size_t)samp_ld(cap) * sizeof(float)) + align256((R + 1) * sizeof(uint32_t));
   return n;
 }
 
@@ -131,6 +150,16 @@ void index_carve(IndexArgs& a, void* ws) {
   a.cand = (uint64_t*)p;
   p += align256(R * kCandCap * sizeof(uint64_t));
   a.chunk = (uint32_t*)p;
+  p += align256(R * (size_t)n_chunks(a.cap) * sizeof(uint32_t));
+  a.samp = nullptr;
+  a.samp_ld = samp_ld(a.cap);
+  a.fb_only = 0;
+  a.fbl = nullptr;
+  if (pf_sampled(a.cap, a.H, a.Q, a.key_mx)) {
+    a.samp = (float*)p;
+    p += align256(R * (size_t)a.samp_ld * sizeof(float));
+    a.fbl = (uint32_t*)p;
+  }
 }
 
 __device__ __forceinline__ int64_t n_visible(int64_t p, int m, int64_t cap) {
@@ -143,6 +172,12 @@ __device__ __forceinline__ int64_t n_visible(int64_t p, int m, int64_t cap) {
 __device__ __forceinline__ uint32_t score_key(float f) {
   if (f == 0.0f) f = 0.0f;
   return order_key(f);
+}
+
+// The 64-bit selection key of id i: score key above, inverted id below, so
+// that of two equal scores the lower id ranks higher.
+__device__ __forceinline__ uint64_t sel_key(uint32_t k32, int64_t i) {
+  return ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
 }
 
 // The selector's score precision.  fp32, or the bf16 variant ([Notes §9]:
@@ -173,6 +208,7 @@ __global__ void __launch_bounds__(256) k_prep(IndexArgs a) {
   for (size_t i = tid; i < (size_t)R * kBins1; i += nthr) a.hist[i] = 0u;
   for (size_t i = tid; i < (size_t)R * kBins2; i += nthr) a.hist2[i] = 0u;
   for (size_t i = tid; i < (size_t)R * kCtr; i += nthr) a.ctr[i] = 0u;
+  if (a.fbl && tid == 0) a.fbl[0] = 0u;    // rows handed to the full-score path
   if (!a.key_mx) return;
   // one wave per (row, head): 128 elements, 2 per lane; a group of 32 is 16 lanes
   const int lane = threadIdx.x & 63;
@@ -552,9 +588,33 @@ __device__ __forceinline__ void load_qfrag(const uint8_t* kc, const uint8_t* ks,
   f.sc = ks[bb * 4 + g];
 }
 
+// kMode: kModeStore writes every score and the first-digit histogram (the
+// full-score path; with fb_only only for workgroups holding a row that the
+// sampled selection handed over); kModeSample scores the sample tiles into
+// the sample rows; kModeCollect scores every block and appends those at or
+// above the row's sampled threshold to its candidate list.
+constexpr int kModeStore = 0, kModeSample = 1, kModeCollect = 2;
+constexpr int kCollectPer = 8;             // LDS candidate slots per lane and query
+
+__device__ __forceinline__ void load_qfrag_s(const IndexArgs& a, const uint8_t* kc, const uint8_t* ks,
+                                             int b, int64_t sb, int64_t last, int g, QFrag& f) {
+  const int64_t s = sb < last ? sb : last;  // clamped: always a real sample block
+  int64_t bb = ((s >> 4) << 8) | (s & 15);
+  if (a.pg.tab) bb = page_row(a.pg, b, bb);
+  f.v = __builtin_nontemporal_load((const u32x4*)(kc + bb * 64 + g * 16));
+  f.sc = ks[bb * 4 + g];
+}
+
+template <int kMode>
 __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
   __shared__ uint32_t lh[kQT][kBins1];
   __shared__ int pg_rows[kQRange / 128];    // paged keys: the range's pool pages
+  // collect: each lane's candidates of its two queries in slots of its own
+  // (counted in registers: no atomic in the scoring loop), gathered per
+  // query at the end with one global reservation
+  __shared__ uint64_t cbuf[kMode == kModeCollect ? 256 * 2 * kCollectPer : 1];
+  __shared__ uint32_t lcnt[kMode == kModeCollect ? 512 : 1], loff[kMode == kModeCollect ? 512 : 1];
+  __shared__ uint32_t cbase[kQT];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
@@ -563,15 +623,20 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
   const int t0 = (blockIdx.x % qtiles) * kQT;
   const int64_t r0 = (int64_t)blockIdx.y * kQRange;
   int64_t nv_max = 0;
+  bool any_fb = false;
 #pragma unroll
   for (int q = 0; q < kQT; q++) {
     const int t = t0 + q;
-    const int64_t nv = t < a.Q ? n_visible(a.pos[(int64_t)b * a.Q + t], a.m, a.cap) : 0;
+    int64_t nv = t < a.Q ? n_visible(a.pos[(int64_t)b * a.Q + t], a.m, a.cap) : 0;
+    if (kMode == kModeSample) nv = n_sampled(nv);
     nv_max = nv > nv_max ? nv : nv_max;
+    if (kMode == kModeStore && a.fb_only && t < a.Q)
+      any_fb = any_fb || a.ctr[((int64_t)b * a.Q + t) * kCtr + kFbSlot] != 0u;
   }
+  if (kMode == kModeStore && a.fb_only && !any_fb) return;   // uniform
   if (r0 >= nv_max) return;                // uniform across the workgroup
   for (int i = threadIdx.x; i < kQT * kBins1; i += blockDim.x) (&lh[0][0])[i] = 0u;
-  if (a.pg.tab) {
+  if (a.pg.tab && kMode != kModeSample) {
     // (a page longer than the range: the range lies in one page)
     const int n_pg = (kQRange >> a.pg.psh) > 0 ? (kQRange >> a.pg.psh) : 1;
     for (int i = threadIdx.x; i < n_pg; i += blockDim.x) {
@@ -602,10 +667,30 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
 #pragma unroll
   for (int q = 0; q < kQT; q++) {
     const int t = t0 + q;
-    const int64_t nv = t < a.Q ? n_visible(a.pos[(int64_t)b * a.Q + t], a.m, a.cap) : 0;
+    int64_t nv = t < a.Q ? n_visible(a.pos[(int64_t)b * a.Q + t], a.m, a.cap) : 0;
+    if (kMode == kModeSample) nv = n_sampled(nv);
     if (q == qa0) nv0 = nv;
     if (q == qa1) nv1 = nv;
   }
+  // collect: the two rows' thresholds and counters
+  const int64_t row0 = (int64_t)b * a.Q + t0 + qa0, row1 = (int64_t)b * a.Q + t0 + qa1;
+  uint32_t thr0 = 0xFFFFFFFFu, thr1 = 0xFFFFFFFFu;
+  if (kMode == kModeCollect) {
+    if (t0 + qa0 < a.Q) thr0 = a.ctr[row0 * kCtr + kThrSlot];
+    if (t0 + qa1 < a.Q) thr1 = a.ctr[row1 * kCtr + kThrSlot];
+  }
+  // a candidate of this lane's query `which` (0: qa0, 1: qa1): its next own
+  // slot, or (its slots full) a global one
+  uint32_t cn[2] = {0u, 0u};
+  auto put_cand = [&](int which, int64_t row, uint64_t key) {
+    if (cn[which] < (uint32_t)kCollectPer) {
+      cbuf[(threadIdx.x * 2 + which) * kCollectPer + cn[which]] = key;
+      cn[which]++;
+    } else {
+      const uint32_t gs = atomicAdd(&a.ctr[row * kCtr + kCntSlot], 1u);
+      if (gs < (uint32_t)kCandCap) a.cand[row * kCandCap + gs] = key;
+    }
+  };
   const size_t o0 = (size_t)((int64_t)b * a.Q + t0 + qa0) * a.sc_ld;   // score row offsets
   const size_t o1 = (size_t)((int64_t)b * a.Q + t0 + qa1) * a.sc_ld;
   __syncthreads();                         // lh zeroed
@@ -620,15 +705,29 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
 
   auto tile = [&](const QFrag& f, int64_t blk0) {
     const i32x8 kb = {(int)f.v[0], (int)f.v[1], (int)f.v[2], (int)f.v[3], 0, 0, 0, 0};
+    // the eight queries' products first, each into its own accumulator, so
+    // that the MFMAs issue back to back and the epilogue reads finished ones
+    f32x4 acc[kQT];
+#pragma unroll
+    for (int q = 0; q < kQT; q++)
+      acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          qa[q], kb, (f32x4){0.f, 0.f, 0.f, 0.f}, 4, 4, 0, qs[q], 0, f.sc);
     float part[kQT];
 #pragma unroll
     for (int q = 0; q < kQT; q++) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[q], kb, acc, 4, 4, 0, qs[q], 0,
-                                                             f.sc);
-      float p = wv[q][0] * fmaxf(acc[0], 0.0f);
+      // ReLU as one integer max on the bits (a float with the sign bit set
+      // is a negative integer and becomes +0); w-weighted sum of the lane's
+      // four heads
+      float r[4];
 #pragma unroll
-      for (int i = 1; i < 4; i++) p += wv[q][i] * fmaxf(acc[i], 0.0f);
+      for (int i = 0; i < 4; i++) {
+        const float x = acc[q][i];
+        const int bits = __float_as_int(x);
+        r[i] = __int_as_float(bits > 0 ? bits : 0);
+      }
+      float p = wv[q][0] * r[0];
+#pragma unroll
+      for (int i = 1; i < 4; i++) p = fmaf(wv[q][i], r[i], p);
       part[q] = p;
     }
     // sum over the four lane groups, all queries at once
@@ -638,27 +737,75 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
     const float s0 = ranked(swap_add16(h[0], h[1]), a.score_bf16);   // queries 0, 1, 4, 5 by lane group
     const float s1 = ranked(swap_add16(h[2], h[3]), a.score_bf16);   // queries 2, 3, 6, 7
     const int64_t blk = blk0 + li;
-    if (blk < nv0 && t0 + qa0 < a.Q) {
-      put_score(a, o0 + blk, s0);
-      atomicAdd(&lh[qa0][score_key(s0) >> kSh1], 1u);
-    }
-    if (blk < nv1 && t0 + qa1 < a.Q) {
-      put_score(a, o1 + blk, s1);
-      atomicAdd(&lh[qa1][score_key(s1) >> kSh1], 1u);
+    if (kMode == kModeStore) {
+      if (blk < nv0 && t0 + qa0 < a.Q) {
+        put_score(a, o0 + blk, s0);
+        atomicAdd(&lh[qa0][score_key(s0) >> kSh1], 1u);
+      }
+      if (blk < nv1 && t0 + qa1 < a.Q) {
+        put_score(a, o1 + blk, s1);
+        atomicAdd(&lh[qa1][score_key(s1) >> kSh1], 1u);
+      }
+    } else if (kMode == kModeSample) {
+      if (blk < nv0 && t0 + qa0 < a.Q) a.samp[row0 * a.samp_ld + blk] = s0;
+      if (blk < nv1 && t0 + qa1 < a.Q) a.samp[row1 * a.samp_ld + blk] = s1;
+    } else {
+      // (few pass: about 1.3 % of the scores at the benchmark's shape)
+      const uint32_t k0 = score_key(s0), k1 = score_key(s1);
+      if (blk < nv0 && t0 + qa0 < a.Q && k0 >= thr0) put_cand(0, row0, sel_key(k0, blk));
+      if (blk < nv1 && t0 + qa1 < a.Q && k1 >= thr1) put_cand(1, row1, sel_key(k1, blk));
     }
   };
 
   // tiles w, w + 4, ... of 16 blocks; two fragments in flight
+  auto ld = [&](int64_t blk, QFrag& f) {
+    if (kMode == kModeSample)
+      load_qfrag_s(a, kc, ks, b, blk, last, g, f);
+    else
+      load_qfrag(kc, ks, blk, last, g, f, pgl, r0, psh);
+  };
   QFrag fa, fb;
   int64_t blk0 = r0 + wave * 16;
-  load_qfrag(kc, ks, blk0 + li, last, g, fa, pgl, r0, psh);
+  ld(blk0 + li, fa);
   for (; blk0 < r1; blk0 += 128) {
-    load_qfrag(kc, ks, blk0 + 64 + li, last, g, fb, pgl, r0, psh);
+    ld(blk0 + 64 + li, fb);
     tile(fa, blk0);
     if (blk0 + 64 >= r1) break;
-    load_qfrag(kc, ks, blk0 + 128 + li, last, g, fa, pgl, r0, psh);
+    ld(blk0 + 128 + li, fa);
     tile(fb, blk0 + 64);
   }
+  if (kMode == kModeCollect) {
+    const int t = threadIdx.x;
+    lcnt[2 * t] = cn[0] < (uint32_t)kCollectPer ? cn[0] : (uint32_t)kCollectPer;
+    lcnt[2 * t + 1] = cn[1] < (uint32_t)kCollectPer ? cn[1] : (uint32_t)kCollectPer;
+    __syncthreads();
+    if (t < kQT) {
+      // query q is held by lane group g of every wave as its query `which`
+      const int q = t, which = (q >> 1) & 1, qb = q - 2 * which;
+      const int gq = (qb & 1) + 2 * (qb >> 2);
+      uint32_t tot = 0;
+      for (int w = 0; w < 4; w++)
+        for (int l = 0; l < 16; l++) {
+          const int idx = 2 * (w * 64 + gq * 16 + l) + which;
+          loff[idx] = tot;
+          tot += lcnt[idx];
+        }
+      cbase[q] = (tot && t0 + q < a.Q) ? atomicAdd(&a.ctr[((int64_t)b * a.Q + t0 + q) * kCtr + kCntSlot], tot)
+                                       : 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int which = 0; which < 2; which++) {
+      const int q = which ? qa1 : qa0;
+      if (t0 + q >= a.Q) continue;
+      const int idx = 2 * t + which;
+      const uint32_t base = cbase[q] + loff[idx];
+      uint64_t* dst = a.cand + ((int64_t)b * a.Q + t0 + q) * kCandCap;
+      for (uint32_t j = 0; j < lcnt[idx]; j++)
+        if (base + j < (uint32_t)kCandCap) dst[base + j] = cbuf[idx * kCollectPer + j];
+    }
+  }
+  if (kMode != kModeStore) return;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < kQT; q++) {
@@ -727,18 +874,22 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp,
 
 // Find the bin (scanning from the top) where the cumulative count reaches
 // `need` (1 <= need <= total); writes (bin, count strictly above) to shared
-// memory.  All threads must call it; nb is a multiple of kFThreads.
+// memory.  All threads must call it; nb is a power of two (a multiple of
+// kFThreads, or below it: one bin per thread, the rest empty).
 __device__ void find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* tmp,
                          int* s_bin, uint32_t* s_above) {
-  const int per = nb / kFThreads;
+  const int per = nb >= kFThreads ? nb / kFThreads : 1;
   uint32_t cnt = 0;
-  for (int j = 0; j < per; j++) cnt += h[nb - 1 - (threadIdx.x * per + j)];
+  for (int j = 0; j < per; j++) {
+    const int i = threadIdx.x * per + j;
+    cnt += i < nb ? h[nb - 1 - i] : 0u;
+  }
   uint32_t incl = block_incl_scan(cnt, tmp);
   uint32_t excl = incl - cnt;
   if (excl < need && incl >= need) {
     uint32_t above = excl;
     for (int j = 0; j < per; j++) {
-      int bin = nb - 1 - (threadIdx.x * per + j);
+      int bin = nb - 1 - (threadIdx.x * per + j);      // >= 0: this thread's count is not empty
       if (above + h[bin] >= need) {
         *s_bin = bin;
         *s_above = above;
@@ -750,11 +901,6 @@ __device__ void find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* tmp
   __syncthreads();
 }
 
-// The 64-bit selection key of id i: score key above, inverted id below, so
-// that of two equal scores the lower id ranks higher.
-__device__ __forceinline__ uint64_t sel_key(uint32_t k32, int64_t i) {
-  return ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-}
 
 // This thread's kPer consecutive scores of filter chunk `chunk`, in two
 // halves so that the loads can be issued before anything else the kernel
@@ -868,12 +1014,11 @@ __device__ __forceinline__ uint32_t part_sum(const Parts& p, uint32_t* red) {
 }
 
 template <bool kBf16>
-__global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
+__device__ __forceinline__ void filter1_row(const IndexArgs& a, const int row) {
   __shared__ uint32_t lh[kBins2];
   __shared__ uint32_t tmp[kFThreads / 64];
   __shared__ int s_bin;
   __shared__ uint32_t s_above;
-  const int row = blockIdx.y;
   // all global loads first, before the query position arrives (no address
   // depends on it): the first histogram (bin = thread), this thread's scores
   Parts pt;
@@ -913,6 +1058,20 @@ __global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
   for (int j = 0; j < kPer; j++)
     if (j < n_in && (k32[j] >> kSh1) == b1) atomicAdd(&lh[(k32[j] >> kSh2) & (kBins2 - 1)], 1u);
   hist_flush(lh, a.hist2 + (size_t)row * kBins2, kBins2);
+}
+
+template <bool kBf16>
+__global__ void __launch_bounds__(kFThreads) k_filter1(IndexArgs a) {
+  if (!a.fb_only) {
+    filter1_row<kBf16>(a, (int)blockIdx.y);
+    return;
+  }
+  // the rows the sampled selection handed over, gridDim.y at a time
+  const uint32_t n_fb = a.fbl[0];
+  for (uint32_t r = blockIdx.y; r < n_fb; r += gridDim.y) {
+    filter1_row<kBf16>(a, (int)a.fbl[1 + r]);
+    __syncthreads();
+  }
 }
 
 // Candidate appends go to an LDS buffer first (wave-aggregated LDS atomics);
@@ -959,24 +1118,28 @@ struct CandList {
   }
 };
 
-// Candidates of the threshold search: the compact list, or (when it
-// overflowed) the query's scores filtered by the first two digits.
+// Candidates of the threshold search: the compact list (in LDS, or the
+// query's global list), or (when it overflowed) the query's scores filtered
+// by the candidates' common key prefix (the top pbits bits of the score key;
+// pbits = 0: no common prefix).
 struct CandSrc {
-  const uint64_t* cand;
+  const uint64_t* lds;                     // the list in LDS, or null
+  const uint64_t* glob;                    // the query's global list
   uint32_t n;
-  const float* sc;
+  const float* sc;                         // the query's score row
   int64_t nv;
-  uint32_t b12;                            // key bits 31..13 of the candidates
+  uint32_t pfx;
+  int pbits;
   bool compact;
   __device__ __forceinline__ int64_t size() const { return compact ? (int64_t)n : nv; }
   __device__ __forceinline__ bool get(int64_t i, uint64_t* key) const {
     if (compact) {
-      *key = cand[i];
+      *key = lds ? lds[i] : glob[i];
       return true;
     }
     const uint32_t k32 = score_key(sc[i]);
     *key = sel_key(k32, i);
-    return (k32 >> kSh2) == b12;
+    return pbits == 0 || (k32 >> (32 - pbits)) == pfx;
   }
 };
 
@@ -994,7 +1157,7 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* tmp) {
 }
 
 // The exact 64-bit threshold T: the need-th largest key among the
-// candidates (radix select on the bits below the candidates' common 19-bit
+// candidates (radix select on the bits below the candidates' common key
 // prefix).  Exactly `need` candidates have keys >= T.
 __device__ uint64_t resolve_threshold(const CandSrc& src, uint32_t need, uint32_t* lh,
                                       uint32_t* tmp) {
@@ -1002,19 +1165,21 @@ __device__ uint64_t resolve_threshold(const CandSrc& src, uint32_t need, uint32_
   __shared__ uint32_t s_need, s_above;
   __shared__ int s_bin, s_done;
   if (threadIdx.x == 0) {
-    s_prefix = (uint64_t)src.b12 << (32 + kSh2);
-    s_mask = (uint64_t)0x7FFFF << (32 + kSh2);
+    s_prefix = src.pbits ? (uint64_t)src.pfx << (64 - src.pbits) : 0ull;
+    s_mask = src.pbits ? (((uint64_t)1 << src.pbits) - 1) << (64 - src.pbits) : 0ull;
     s_need = need;
     s_done = 0;
   }
   __syncthreads();
-  // remaining digits: score key bits 12..0, then the inverted id
-  const int shifts[4] = {34, 23, 12, 0};
-  const int widths[4] = {11, 11, 11, 12};
+  // remaining digits: the score key bits below the prefix, then the
+  // inverted id, 11 bits a pass from the top (all that is left once 12 or
+  // fewer remain)
   const int64_t n = src.size();
-  for (int pass = 0; pass < 4; pass++) {
+  for (int lo = 64 - src.pbits; lo > 0;) {
     if (s_done) break;
-    const int sh = shifts[pass], wd = widths[pass];
+    const int wd = lo > 12 ? 11 : lo;
+    const int sh = lo - wd;
+    lo = sh;
     const uint32_t nb = 1u << wd;
     for (int i = threadIdx.x; i < (int)nb; i += blockDim.x) lh[i] = 0u;
     __syncthreads();
@@ -1041,13 +1206,12 @@ __device__ uint64_t resolve_threshold(const CandSrc& src, uint32_t need, uint32_
   return T;
 }
 
-__global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
+__device__ __forceinline__ void filter2_row(const IndexArgs& a, const int row) {
   __shared__ uint32_t lh[kBins2];
   __shared__ uint32_t tmp[kFThreads / 64];
   __shared__ uint64_t cand_buf[kCandLds];
   __shared__ int s_bin;
   __shared__ uint32_t s_above, cand_n, s_base;
-  const int row = blockIdx.y;
   // all global loads first, before the query position arrives: the first
   // digit (published by k_filter1), the second histogram, this thread's scores
   uint32_t* ctr = a.ctr + (size_t)row * kCtr;
@@ -1092,6 +1256,19 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
+  if (!a.fb_only) {
+    filter2_row(a, (int)blockIdx.y);
+    return;
+  }
+  // the rows the sampled selection handed over, gridDim.y at a time
+  const uint32_t n_fb = a.fbl[0];
+  for (uint32_t r = blockIdx.y; r < n_fb; r += gridDim.y) {
+    filter2_row(a, (int)a.fbl[1 + r]);
+    __syncthreads();
+  }
+}
+
 constexpr int kEmitCand = 4096;            // candidates resolved from LDS
 constexpr int kRankCand = 128;             // candidates resolved by counting ranks
 
@@ -1113,11 +1290,10 @@ __device__ uint64_t rank_threshold(const uint64_t* cl, uint32_t n, uint32_t need
 // Every workgroup of a query resolves the threshold T from the candidates
 // (few: they share the top 19 key bits with the k-th largest score), finds
 // its chunk's output offset, and writes its chunk's selected ids in order.
-__global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
+__device__ __forceinline__ void emit_row(const IndexArgs& a, const int row) {
   __shared__ uint32_t lh[kBinsMax];
   __shared__ uint32_t tmp[kFThreads / 64];
   __shared__ uint64_t cl[kEmitCand];
-  const int row = blockIdx.y;
   // all global loads first, before the query position arrives: counters, the
   // first candidates (speculatively: the list always has kCandCap slots), the
   // earlier chunks' counts, scores
@@ -1142,8 +1318,8 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
     for (uint32_t i = threadIdx.x + blockDim.x; i < n_cand; i += blockDim.x) cl[i] = gc[i];
   }
   __syncthreads();
-  const CandSrc src{in_lds ? cl : gc, n_cand, a.scores + (size_t)row * a.sc_ld, nv, b12,
-                    n_cand <= (uint32_t)kCandCap};
+  const CandSrc src{in_lds ? cl : nullptr, gc, n_cand, a.scores + (size_t)row * a.sc_ld, nv, b12,
+                    32 - kSh2, n_cand <= (uint32_t)kCandCap};
   const uint64_t T = (src.compact && in_lds && n_cand <= (uint32_t)kRankCand)
                          ? rank_threshold(cl, n_cand, need)
                          : resolve_threshold(src, need, lh, tmp);
@@ -1184,6 +1360,165 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
+  if (!a.fb_only) {
+    emit_row(a, (int)blockIdx.y);
+    return;
+  }
+  // the rows the sampled selection handed over, gridDim.y at a time
+  const uint32_t n_fb = a.fbl[0];
+  for (uint32_t r = blockIdx.y; r < n_fb; r += gridDim.y) {
+    emit_row(a, (int)a.fbl[1 + r]);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- sampled-threshold selection
+// Query-tiled scans (prefill chunks) do not materialise the score matrix
+// (4 bytes per query and block, written once and read three times by the
+// filters above).  A sample pass scores every 16th tile of 16 blocks; for
+// each query k_thresh takes the r-th largest sample key as a lower bound L,
+// with r = k s/n + 6 sqrt(k s/n) + 16 for s samples of n visible blocks
+// (about 6 standard deviations above the expected sample count of the top
+// k), so that at least k of all keys are >= L with near certainty and
+// about r n / s are; the collect pass scores every block and appends those
+// >= L to the query's candidate list; k_select_pf takes the exact top k of
+// the candidates (the same 64-bit keys and tie rule as the filters) and
+// emits them in ascending id order from an id bitmap.  A query whose
+// candidates are fewer than k or more than the list holds (ties, or a
+// sample unlike the rest) is flagged and runs through the full-score path
+// (store scan + the three filters, each skipping unflagged rows), so the
+// result is exact whatever the scores.
+__global__ void __launch_bounds__(kFThreads) k_thresh(IndexArgs a) {
+  __shared__ uint32_t lh[kBins2];
+  __shared__ uint32_t tmp[kFThreads / 64];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above;
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
+  const int kk = (int)(nv < a.k ? nv : a.k);
+  uint32_t* ctr = a.ctr + (size_t)row * kCtr;
+  const int64_t ns = n_sampled(nv);
+  const float ksf = nv > 0 ? (float)kk * (float)ns / (float)nv : 0.0f;
+  const int64_t r = (int64_t)ceilf(ksf + 6.0f * sqrtf(ksf) + 16.0f);
+  if (kk == nv || r >= ns) {               // every visible block is a candidate
+    if (t == 0) ctr[kThrSlot] = 0u;
+    return;
+  }
+  // this thread's sample keys in registers (ns <= kThrPer * 256 on this path)
+  const float* sp = a.samp + (size_t)row * a.samp_ld;
+  uint32_t kv[kThrPer];
+#pragma unroll
+  for (int j = 0; j < kThrPer; j++) {
+    const int64_t i = t + (int64_t)j * kFThreads;
+    kv[j] = i < ns ? score_key(sp[i]) : 0u;
+  }
+  uint32_t prefix = 0u, mask = 0u, need = (uint32_t)r;
+  const int shs[3] = {21, 10, 0}, wds[3] = {11, 11, 10};
+  for (int pass = 0; pass < 3; pass++) {
+    const int sh = shs[pass];
+    const uint32_t nb = 1u << wds[pass];
+    for (int i = t; i < (int)nb; i += blockDim.x) lh[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kThrPer; j++) {
+      const int64_t i = t + (int64_t)j * kFThreads;
+      if (i < ns && (kv[j] & mask) == prefix) atomicAdd(&lh[(kv[j] >> sh) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    find_bin(lh, (int)nb, need, tmp, &s_bin, &s_above);
+    prefix |= (uint32_t)s_bin << sh;
+    mask |= (nb - 1) << sh;
+    need -= s_above;
+    __syncthreads();                       // s_bin, s_above read by all
+  }
+  if (t == 0) ctr[kThrSlot] = prefix;      // the r-th largest sample key
+}
+
+__global__ void __launch_bounds__(kFThreads) k_select_pf(IndexArgs a) {
+  __shared__ uint64_t cl[kEmitCand];
+  __shared__ uint32_t bmh[kPfBmWords];     // radix histogram, then the id bitmap
+  __shared__ uint32_t tmp[kFThreads / 64];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t nv = n_visible(a.pos[row], a.m, a.cap);
+  const int kk = (int)(nv < a.k ? nv : a.k);
+  int32_t* out = a.topk + (size_t)row * a.k;
+  if (kk == nv) {                          // everything visible is selected
+    for (int64_t i = t; i < a.k; i += blockDim.x) out[i] = i < nv ? (int32_t)i : -1;
+    return;
+  }
+  uint32_t* ctr = a.ctr + (size_t)row * kCtr;
+  const uint32_t n = ctr[kCntSlot];
+  const int nw = (int)((nv + 31) / 32);
+  if (n < (uint32_t)kk || n > (uint32_t)kCandCap || nw > kPfBmWords) {
+    if (t == 0) {                          // the full-score path takes this row
+      ctr[kFbSlot] = 1u;
+      a.fbl[1 + atomicAdd(&a.fbl[0], 1u)] = (uint32_t)row;
+    }
+    return;
+  }
+  for (int i = kk + t; i < a.k; i += blockDim.x) out[i] = -1;
+  const uint64_t* cand = a.cand + (size_t)row * kCandCap;
+  const bool in_lds = n <= (uint32_t)kEmitCand;
+  if (in_lds)
+    for (uint32_t i = t; i < n; i += blockDim.x) cl[i] = cand[i];
+  // the candidates' common score-key prefix (all are >= the threshold, so
+  // usually many top bits agree): the radix passes start below it
+  uint32_t k_and = 0xFFFFFFFFu, k_or = 0u;
+  for (uint32_t i = t; i < n; i += blockDim.x) {
+    const uint32_t k32 = (uint32_t)((in_lds ? cl[i] : cand[i]) >> 32);
+    k_and &= k32;
+    k_or |= k32;
+  }
+  __shared__ uint32_t s_and[kFThreads / 64], s_or[kFThreads / 64];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    k_and &= __shfl_xor(k_and, o, 64);
+    k_or |= __shfl_xor(k_or, o, 64);
+  }
+  if ((t & 63) == 0) {
+    s_and[t >> 6] = k_and;
+    s_or[t >> 6] = k_or;
+  }
+  __syncthreads();
+  k_and = s_and[0] & s_and[1] & s_and[2] & s_and[3];
+  k_or = s_or[0] | s_or[1] | s_or[2] | s_or[3];
+  const uint32_t diff = k_and ^ k_or;      // bits that differ among the candidates
+  const int pbits = diff ? __builtin_clz(diff) : 32;
+  const CandSrc src{in_lds ? cl : nullptr, cand, n, nullptr, nv,
+                    pbits ? (k_and >> (32 - pbits)) : 0u, pbits, true};
+  const uint64_t T = (in_lds && n <= (uint32_t)kRankCand) ? rank_threshold(cl, n, (uint32_t)kk)
+                                                          : resolve_threshold(src, (uint32_t)kk, bmh, tmp);
+  __syncthreads();                         // the histogram space is free
+  for (int i = t; i < nw; i += blockDim.x) bmh[i] = 0u;
+  __syncthreads();
+  for (uint32_t i = t; i < n; i += blockDim.x) {
+    const uint64_t key = in_lds ? cl[i] : cand[i];
+    if (key >= T) {
+      const uint32_t id = 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu);
+      atomicOr(&bmh[id >> 5], 1u << (id & 31));
+    }
+  }
+  __syncthreads();
+  // thread t emits bitmap words [t per, (t + 1) per) at its prefix count
+  const int per = (nw + kFThreads - 1) / kFThreads;
+  const int w0 = t * per, w1 = w0 + per < nw ? w0 + per : nw;
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; w++) cnt += (uint32_t)__builtin_popcount(bmh[w]);
+  uint32_t pos = block_incl_scan(cnt, tmp) - cnt;
+  for (int w = w0; w < w1; w++) {
+    uint32_t m = bmh[w];
+    while (m) {
+      const int bit = __builtin_ctz(m);
+      m &= m - 1;
+      if (pos < (uint32_t)kk) out[pos] = w * 32 + bit;
+      pos++;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- BF16-score selector
 // With bf16 scores the two radix digits fix the k-th value T exactly (a bf16
 // value's key has its low 16 bits zero), so the selection needs no
@@ -1192,12 +1527,11 @@ __global__ void __launch_bounds__(kFThreads) k_emit(IndexArgs a) {
 
 // Second filter: T's digits and, per chunk, its counts above and at T
 // (packed: above in the high half, at T in the low half, each <= 4096).
-__global__ void __launch_bounds__(kFThreads) k_filter2_bf16(IndexArgs a) {
+__device__ __forceinline__ void filter2_bf16_row(const IndexArgs& a, const int row) {
   __shared__ uint32_t lh[kBins2];
   __shared__ uint32_t tmp[kFThreads / 64];
   __shared__ int s_bin;
   __shared__ uint32_t s_above;
-  const int row = blockIdx.y;
   // all global loads first, before the query position arrives
   uint32_t* ctr = a.ctr + (size_t)row * kCtr;
   const uint32_t b1 = ctr[4], above1 = ctr[5];
@@ -1234,12 +1568,24 @@ __global__ void __launch_bounds__(kFThreads) k_filter2_bf16(IndexArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(kFThreads) k_filter2_bf16(IndexArgs a) {
+  if (!a.fb_only) {
+    filter2_bf16_row(a, (int)blockIdx.y);
+    return;
+  }
+  // the rows the sampled selection handed over, gridDim.y at a time
+  const uint32_t n_fb = a.fbl[0];
+  for (uint32_t r = blockIdx.y; r < n_fb; r += gridDim.y) {
+    filter2_bf16_row(a, (int)a.fbl[1 + r]);
+    __syncthreads();
+  }
+}
+
 // Emit: a workgroup's chunk offset = ids above T in earlier chunks + the ids
 // at T taken there; within the chunk one scan of the packed (above, at T)
 // counts places every thread's ids; output ascending, tail -1.
-__global__ void __launch_bounds__(kFThreads) k_emit_bf16(IndexArgs a) {
+__device__ __forceinline__ void emit_bf16_row(const IndexArgs& a, const int row) {
   __shared__ uint32_t tmp[kFThreads / 64];
-  const int row = blockIdx.y;
   const uint32_t* ctr = a.ctr + (size_t)row * kCtr;
   const uint32_t b12 = ctr[2], need = ctr[3];
   const uint32_t* cc = a.chunk + (size_t)row * n_chunks(a.cap);
@@ -1292,6 +1638,19 @@ __global__ void __launch_bounds__(kFThreads) k_emit_bf16(IndexArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(kFThreads) k_emit_bf16(IndexArgs a) {
+  if (!a.fb_only) {
+    emit_bf16_row(a, (int)blockIdx.y);
+    return;
+  }
+  // the rows the sampled selection handed over, gridDim.y at a time
+  const uint32_t n_fb = a.fbl[0];
+  for (uint32_t r = blockIdx.y; r < n_fb; r += gridDim.y) {
+    emit_bf16_row(a, (int)a.fbl[1 + r]);
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- fixed scratch
 // The allocation-free index call carves its workspace out of this array
 // instead of a caller's buffer.  Every GPU the library runs on holds its own
@@ -1339,13 +1698,42 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEve
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.key_mx && a.H == 16 && a.Q >= kQT) {
+  if (a.samp) {
+    // sampled-threshold path: sample scan, thresholds, collect scan, exact
+    // selection; then the full-score path for the rows it hands over
+    const unsigned qt = (unsigned)(a.B * ((a.Q + kQT - 1) / kQT));
+    dim3 sgrid(qt, (unsigned)((n_sampled(a.cap) + kQRange - 1) / kQRange));
+    dim3 grid(qt, (unsigned)((a.cap + kQRange - 1) / kQRange));
+    hipLaunchKernelGGL(k_score_mx_q<kModeSample>, sgrid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_thresh, dim3(R), dim3(kFThreads), 0, st, a);
+    if (ev)
+      hipExtLaunchKernelGGL(k_score_mx_q<kModeCollect>, grid, dim3(256), 0, st, ev->start, ev->stop, 0,
+                            a);
+    else
+      hipLaunchKernelGGL(k_score_mx_q<kModeCollect>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_select_pf, dim3(R), dim3(kFThreads), 0, st, a);
+    IndexArgs f = a;
+    f.fb_only = 1;
+    hipLaunchKernelGGL(k_score_mx_q<kModeStore>, grid, dim3(256), 0, st, f);
+    // the handed-over rows, kFbRows at a time
+    dim3 fgrid((unsigned)n_chunks(a.cap), (unsigned)(R < kFbRows ? R : kFbRows));
+    if (a.score_bf16) {
+      hipLaunchKernelGGL(k_filter1<true>, fgrid, dim3(kFThreads), 0, st, f);
+      hipLaunchKernelGGL(k_filter2_bf16, fgrid, dim3(kFThreads), 0, st, f);
+      hipLaunchKernelGGL(k_emit_bf16, fgrid, dim3(kFThreads), 0, st, f);
+    } else {
+      hipLaunchKernelGGL(k_filter1<false>, fgrid, dim3(kFThreads), 0, st, f);
+      hipLaunchKernelGGL(k_filter2, fgrid, dim3(kFThreads), 0, st, f);
+      hipLaunchKernelGGL(k_emit, fgrid, dim3(kFThreads), 0, st, f);
+    }
+    return hipGetLastError();
+  } else if (a.key_mx && a.H == 16 && a.Q >= kQT) {
     dim3 grid((unsigned)(a.B * ((a.Q + kQT - 1) / kQT)),
               (unsigned)((a.cap + kQRange - 1) / kQRange));
     if (ev)
-      hipExtLaunchKernelGGL(k_score_mx_q, grid, dim3(256), 0, st, ev->start, ev->stop, 0, a);
+      hipExtLaunchKernelGGL(k_score_mx_q<kModeStore>, grid, dim3(256), 0, st, ev->start, ev->stop, 0, a);
     else
-      hipLaunchKernelGGL(k_score_mx_q, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(k_score_mx_q<kModeStore>, grid, dim3(256), 0, st, a);
   } else if (a.key_mx) {
     dim3 grid((unsigned)a.score_wgs, R);
     auto go = [&](auto kern) {

@@ -93,6 +93,10 @@ struct IndexArgs {
   uint64_t* cand;            // [R][16384] candidate keys (score key : inverted id)
   uint32_t* chunk;           // [R][n_chunks] per filter chunk: ids above the candidates
   uint16_t* hparts;          // [R][hp_ld][256] per-scan-workgroup first-digit counts
+  float* samp;               // [R][samp_ld] sample-tile scores (query-tiled scans), or null
+  int64_t samp_ld;
+  int fb_only;               // 1: the full-score kernels take only the rows handed over
+  uint32_t* fbl;             // [1 + R]: count, then the rows handed over (sampled path)
   Pages pg;                  // paged keys (MXFP4 only; >= 128 keys per page)
 };
 size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx);

@@ -160,3 +160,91 @@ def test_prefill_pair_full_size_sampled(lib):
     P.check_out(P.out_to_f64(out)[:, rows], r, what="csa prefill 1M")
     _, rh = hca_attend(qs, "bf16", ref["hcomp"], 128, ref["hwin"], n_win, ps, None, x["sc"], "bf16")
     P.check_out(P.out_to_f64(hout)[:, rows], rh, what="hca prefill 1M")
+
+
+# ---------------------------------------------------------------- sampled-threshold selection
+
+def _planted_keys(n, sampled_score_shift, other_shift, seed):
+    """MXFP4 keys that are all one random key r with every e8m0 scale byte
+    raised by a shift: blocks of the sample tiles (block % 256 < 16) by
+    `sampled_score_shift`, the others by `other_shift`.  A shift j multiplies
+    the score by exactly 2^j (exact FP4 products, positively homogeneous
+    ReLU), so each class holds identical scores."""
+    rng = np.random.default_rng(seed)
+    r = (rng.standard_normal((1, 1, 128)) * 128 ** -0.5).astype(np.float32)
+    rk = C.idx_encode(r, "mxfp4")
+    codes = np.repeat(rk.codes, n, axis=1)
+    scales = np.repeat(rk.scales, n, axis=1).astype(np.int64)
+    blk = np.arange(n)
+    samp = (blk % 256) < 16
+    scales[0, samp] += sampled_score_shift
+    scales[0, ~samp] += other_shift
+    assert scales.min() >= 1 and scales.max() <= 254
+    return C.Idx("mxfp4", 128, codes, scales.astype(np.uint8)), samp
+
+
+@pytest.mark.parametrize("bf16_scores", [False, True])
+def test_sampled_select_hands_over_when_too_few_candidates(lib, bf16_scores):
+    """The sample tiles score 16 times higher than every other block: the
+    sampled threshold lands on the sample scores, fewer than k blocks reach
+    it, and the rows go through the full-score path: the k' - |sample| extra
+    ids are the lowest-indexed of the tied rest."""
+    cap, Q, k, m = 20000, 8, 2048, 4
+    keys, samp = _planted_keys(cap, 2, -2, 41)
+    rng = _rng(41)
+    q = (rng.standard_normal((1, Q, 16, 128)) * 128 ** -0.5).astype(np.float32)
+    w = rng.random((1, Q, 16)).astype(np.float32)
+    pos = (4 * cap - 1 - np.arange(Q)[::-1] * 4).reshape(1, Q).astype(np.int64)
+    qb = C.bf16_encode(q)
+    qd = C.bf16_decode(qb).astype(np.float32)
+    print(f"sampled select: too few candidates, bf16={bf16_scores}", flush=True)
+    call = lib.v4attn_index_topk_bf16 if bf16_scores else lib.v4attn_index_topk
+    topk = call(P.dev(qb.view(np.int16)).view(torch.bfloat16), P.dev(w), P.idx_to_dev(keys),
+                P.dev(pos), m, k)
+    torch.cuda.synchronize()
+    got = topk.cpu().numpy()
+    sc = index_scores(qd, w, keys, pos, m)
+    for t in range(Q):
+        nv = int((pos[0, t] + 1) // m)
+        s = sc[0][t]
+        ids = np.arange(nv)
+        assert np.sum(samp[:nv]) < k
+        # expected: every sample block, then the lowest other ids (all tied)
+        exp = np.sort(np.concatenate([ids[samp[:nv]], ids[~samp[:nv]][:k - int(np.sum(samp[:nv]))]]))
+        assert np.all(s[samp[:nv]] > s[~samp[:nv]].max())
+        assert np.array_equal(got[0, t], exp), f"query {t}"
+
+
+@pytest.mark.parametrize("bf16_scores", [False, True])
+def test_sampled_select_hands_over_on_ties(lib, bf16_scores):
+    """All head weights zero: every score is 0, so every visible block is at
+    the sampled threshold, more than the candidate list holds: the full-score
+    path selects the k lowest ids."""
+    cap, Q, k, m = 20000, 9, 1000, 4
+    rng = _rng(43)
+    y = (rng.standard_normal((1, cap, 128)) * 128 ** -0.5).astype(np.float32)
+    keys = C.idx_encode(y, "mxfp4")
+    q = (rng.standard_normal((1, Q, 16, 128)) * 128 ** -0.5).astype(np.float32)
+    w = np.zeros((1, Q, 16), np.float32)
+    pos = (4 * cap - 1 - np.arange(Q)[::-1] * 7).reshape(1, Q).astype(np.int64)
+    print(f"sampled select: ties, bf16={bf16_scores}", flush=True)
+    call = lib.v4attn_index_topk_bf16 if bf16_scores else lib.v4attn_index_topk
+    topk = call(P.bf16_dev(q), P.dev(w), P.idx_to_dev(keys), P.dev(pos), m, k)
+    torch.cuda.synchronize()
+    got = topk.cpu().numpy()
+    for t in range(Q):
+        assert list(got[0, t]) == list(range(k)), f"query {t}"
+
+
+def test_sampled_select_bf16_scores_query_tiled(lib):
+    """The bf16-score ranking on the sampled path (ordinary scores: the
+    selection is exact from the candidates) against the oracle's bf16
+    ranking."""
+    rng = _rng(47)
+    Bn, Q, cap, k, m = 2, 16, 12000, 700, 4
+    pos = np.empty((Bn, Q), np.int64)
+    for b in range(Bn):
+        pos[b] = 4 * (cap - 8) + b * 3 + np.arange(Q)
+    print("sampled select: bf16 scores", flush=True)
+    kinds = _index_case(lib, rng, Bn, Q, cap, 16, k, m, pos, bf16_scores=True)
+    assert kinds.count("exact") >= len(kinds) // 2
