@@ -174,7 +174,7 @@ struct Stage {
 // holds (bit set), so that a tile of only compressed (only window) rows takes
 // a branch-free address path.
 constexpr int kMaxSplit = 2048;
-constexpr int kMaxTiles = kMaxSplit / kTile + 3;   // + the three prefetched past the end
+constexpr int kMaxTiles = kMaxSplit / kTile + 3;   // + the tiles prefetched past the end
 constexpr int kHasComp = 1, kHasWin = 2, kHasAbsent = 4;
 
 // An absent entry (or a slot past the split) reads this row: zero codes and
@@ -688,10 +688,11 @@ __device__ __forceinline__ void attend_fp8(AttendArgs a) {
   B.wr = (const uint8_t*)(a.w_rope + (int64_t)b * a.w_cap * kRope);
   B.ws = a.w_scale + (int64_t)b * a.w_cap;
 
-  // two tiles in flight in registers while another is computed; every
+  // one tile in flight in registers while another is computed (a second
+  // register set would push the kernel past 256 VGPRs into scratch); every
   // stage_load issues the same loads (tiles past the split read the zero row)
-  Stage st0, st1;
-  stage_load(B, stage_src(src, sh.tbits, 0), 0, n_local, st0);
+  Stage st;
+  stage_load(B, stage_src(src, sh.tbits, 0), 0, n_local, st);
 
   f32x4 acc[8][2];
 #pragma unroll
@@ -703,10 +704,6 @@ __device__ __forceinline__ void attend_fp8(AttendArgs a) {
   S.l_run = 0.0f;
   const float c2 = a.sm_scale * kLog2e;
 
-  // load order Q, tile 0, tile 1, tile 2: at the loop entry, as at every
-  // back edge, the older register set is the one stored next
-  stage_load(B, stage_src(src, sh.tbits, 1), 1, n_local, st1);
-  __builtin_amdgcn_sched_barrier(0);       // tile 1's loads stay ahead of tile 0's wait
   // (_nr: the query's norm and rotation run while the first tiles load)
   if (kNr) {
     // x * r * gamma with r = 1 / sqrt(mean(x^2) + eps) over the head's 512
@@ -756,28 +753,28 @@ __device__ __forceinline__ void attend_fp8(AttendArgs a) {
     const u32x2 lo = pack4(x), hi = pack4(x + 4);
     qrv = (u32x4){lo[0], lo[1], hi[0], hi[1]};
   }
-  stage_store(&tiles[0], st0);
-  stage_load(B, stage_src(src, sh.tbits, 2), 2, n_local, st0);
+  stage_store(&tiles[0], st);
+  stage_load(B, stage_src(src, sh.tbits, 1), 1, n_local, st);
   *(u32x4*)&sh.qr[rh][8 * rc] = qrv;
   __syncthreads();
 
   // step t (tile t in buffer cb, P buffer pb = t & 1): logits and softmax
   // of tile t in registers, P(t) and tile t+1 (buffer nb) into LDS, the
-  // register set refilled with tile t+3 | barrier | PV of tile t.  When a
+  // register set refilled with tile t+2 | barrier | PV of tile t.  When a
   // wave's tile max outgrew the running max (and on the first tile), the
   // two waves of each head tile agree on the tile max through LDS, P(t) is
   // (re)written against the new max and a second barrier publishes it and
-  // the rescale factors.  Unrolled by two so that the register sets and P
-  // buffers alternate statically.
+  // the rescale factors.  Unrolled by two so that the P buffers alternate
+  // statically.
   auto step = [&](int t, int cb, int nb, int pb, Stage& nxt) {
-    const StageSrc ns = stage_src(src, sh.tbits, t + 3);
+    const StageSrc ns = stage_src(src, sh.tbits, t + 2);
     f32x4 sn, sr;
     float s2[4], tmax;
     qk_tile(&tiles[cb], &sh, qf, eh, wht, lane, sn, sr);
     const bool first = t == 0;
     float l_add = softmax_pass(&tiles[cb], &sh, S, sn, sr, c2, pb, wave, lane, first, s2, tmax);
     stage_store(&tiles[nb], nxt);
-    stage_load(B, ns, t + 3, n_local, nxt);
+    stage_load(B, ns, t + 2, n_local, nxt);
     __syncthreads();
     VFrag vf = pv_load(&tiles[cb], wave, g, li);
     const i32x4 fl = sh.flag[pb];
@@ -807,11 +804,11 @@ __device__ __forceinline__ void attend_fp8(AttendArgs a) {
   for (; t + 1 < n_tiles; t += 2) {
     const int nb = cb == kTileBufs - 1 ? 0 : cb + 1;
     const int nb2 = nb == kTileBufs - 1 ? 0 : nb + 1;
-    step(t, cb, nb, 0, st1);
-    step(t + 1, nb, nb2, 1, st0);
+    step(t, cb, nb, 0, st);
+    step(t + 1, nb, nb2, 1, st);
     cb = nb2;
   }
-  if (t < n_tiles) step(t, cb, cb == kTileBufs - 1 ? 0 : cb + 1, 0, st1);
+  if (t < n_tiles) step(t, cb, cb == kTileBufs - 1 ? 0 : cb + 1, 0, st);
 
   // ---- epilogue: each wave's denominators per head (summed over its four
   // lane groups), then the two entry halves added in fixed order by the
