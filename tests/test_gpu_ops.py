@@ -345,6 +345,32 @@ def test_attend_fp8_edge_cases(lib):
     P.check_out(o, ref)
 
 
+@pytest.mark.parametrize("H,n_comp,m,n_win,with_sink,f32_out", [
+    (64, 30, 1, 16, True, False),      # one split: the kernel writes the output itself
+    (64, 3000, 1, 128, False, True),   # 17 splits of 6 tiles, fp32 output
+    (128, 700, 4, 128, True, False),   # two groups of 64 heads
+    (64, 9000, 1, 128, False, False),  # 16 splits of 18 tiles
+])
+def test_hca_attend_64_head_groups(lib, H, n_comp, m, n_win, with_sink, f32_out):
+    """HCA lists at H % 64 == 0 (the 64-head workgroups): rows whose splits
+    hold every tile count from full down to none (positions spread over the
+    list), a window-only row, an empty row (negative position), a sink."""
+    print(f"hca 64-head groups H={H} n_comp={n_comp} m={m} n_win={n_win}", flush=True)
+    rng = _rng(H + n_comp + n_win)
+    Bn, Q, R = 2, 4, 160
+    comp, win, q = _attend_inputs(rng, Bn, Q, H, n_comp, R)
+    last = m * n_comp - 1
+    pos = np.array([[last, m * (n_comp // 2) + 3, m * 33 + 1, m - 2],
+                    [last + 77, m * (n_comp // 7), 5, -3]], np.int64)
+    sink = rng.standard_normal(H) if with_sink else None
+    qb = C.bf16_encode(q)
+    scale = 512 ** -0.5
+    _, ref = hca_attend(qb, "bf16", comp, m, win, n_win, pos, sink, scale, "bf16")
+    o = _run_attend(lib, "hca", q, True, comp, win, n_win, pos, sink, scale, m=m,
+                    out_dtype=torch.float32 if f32_out else torch.bfloat16)
+    P.check_out(o, ref)
+
+
 @pytest.mark.parametrize("kind,q_bf16", [("csa", False), ("hca", True)])
 def test_attend_f32_entries(lib, kind, q_bf16):
     rng = _rng(31)
