@@ -1205,7 +1205,9 @@ void attend_plan(AttendArgs& a, int64_t n_entries_max) {
   // per-query bound only (short: ~17 splits of whole tiles, at least 64
   // entries -- 4-tile splits at top-2048 cost the B = 4 decode call 1 % and
   // save the 4096-query prefill 14 % of its CSA attention against 3-tile
-  // splits; long: ~16 splits of whole tile pairs)
+  // splits; long: ~16 splits of whole tiles -- 544 entries for the
+  // 8320-entry HCA list, 16 splits, so that B = 16 x 2 head groups fill
+  // 512 workgroup slots, two per CU, in one round)
   int64_t per;
   if (n_entries_max <= 4096) {
     per = (n_entries_max + 16) / 17;
@@ -1213,7 +1215,7 @@ void attend_plan(AttendArgs& a, int64_t n_entries_max) {
     per = (per + kTile - 1) / kTile * kTile;
   } else {
     per = (n_entries_max + 15) / 16;
-    per = (per + 2 * kTile - 1) / (2 * kTile) * (2 * kTile);
+    per = (per + kTile - 1) / kTile * kTile;
   }
   if (per > kMaxSplit) per = kMaxSplit;
   a.split_size = (int)per;
