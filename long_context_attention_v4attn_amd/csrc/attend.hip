@@ -307,12 +307,11 @@ __device__ __forceinline__ void stage_load(Bases B, StageSrc ss, int tile, int n
   }
   // the values are stored to LDS one step later: using them now would make
   // the compiler wait for these loads immediately
-  st.r[0] = __builtin_nontemporal_load((const u32x4*)(nope + q * 16));
-  st.r[1] = __builtin_nontemporal_load((const u32x4*)(nope + (8 + q) * 16));
-  st.r[2] = __builtin_nontemporal_load((const u32x4*)(nope + (16 + q) * 16));
-  st.r[3] = __builtin_nontemporal_load(
-      (const u32x4*)(q < 4 ? nope + (24 + q) * 16 : rope + (q - 4) * 16));
-  st.r[4] = __builtin_nontemporal_load((const u32x4*)(rope + (4 + (q & 3)) * 16));
+  st.r[0] = *(const u32x4*)(nope + q * 16);
+  st.r[1] = *(const u32x4*)(nope + (8 + q) * 16);
+  st.r[2] = *(const u32x4*)(nope + (16 + q) * 16);
+  st.r[3] = *(const u32x4*)(q < 4 ? nope + (24 + q) * 16 : rope + (q - 4) * 16);
+  st.r[4] = *(const u32x4*)(rope + (4 + (q & 3)) * 16);
   st.sc = *scp;
 }
 

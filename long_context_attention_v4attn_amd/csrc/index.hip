@@ -584,7 +584,8 @@ __device__ __forceinline__ void load_qfrag(const uint8_t* kc, const uint8_t* ks,
                                            int64_t r0, int psh) {
   int64_t bb = blk < last ? blk : last;     // clamped: always a real row
   if (pgl) bb = ((int64_t)pgl[(bb - r0) >> psh] << psh) | (bb & (((int64_t)1 << psh) - 1));
-  f.v = __builtin_nontemporal_load((const u32x4*)(kc + bb * 64 + g * 16));
+  // a plain load: every query tile of the sequence reads these keys again
+  f.v = *(const u32x4*)(kc + bb * 64 + g * 16);
   f.sc = ks[bb * 4 + g];
 }
 
@@ -601,7 +602,7 @@ __device__ __forceinline__ void load_qfrag_s(const IndexArgs& a, const uint8_t* 
   const int64_t s = sb < last ? sb : last;  // clamped: always a real sample block
   int64_t bb = ((s >> 4) << 8) | (s & 15);
   if (a.pg.tab) bb = page_row(a.pg, b, bb);
-  f.v = __builtin_nontemporal_load((const u32x4*)(kc + bb * 64 + g * 16));
+  f.v = *(const u32x4*)(kc + bb * 64 + g * 16);
   f.sc = ks[bb * 4 + g];
 }
 
