@@ -189,6 +189,16 @@ __device__ __forceinline__ float ranked(float s, int bf16) {
   return bf16 ? (float)(__bf16)s : s;
 }
 
+// The smallest score whose key is >= k: for every non-NaN score s,
+// score_key(s) >= k exactly when s >= key_floor(k) (a float compare in place
+// of the key; keys below that of -inf admit every score, keys above that of
+// +inf none).
+__device__ __forceinline__ float key_floor(uint32_t k) {
+  if (k <= 0x007FFFFFu) return -INFINITY;
+  if (k > 0xFF800000u) return __uint_as_float(0x7FC00000u);   // NaN: no score compares >=
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 __device__ __forceinline__ void put_score(const IndexArgs& a, size_t i, float r) {
   if (a.score_bf16)
     ((uint16_t*)a.scores)[i] = (uint16_t)(__float_as_uint(r) >> 16);
@@ -606,7 +616,7 @@ __device__ __forceinline__ void load_qfrag_s(const IndexArgs& a, const uint8_t* 
   f.sc = ks[bb * 4 + g];
 }
 
-template <int kMode>
+template <int kMode, bool kBf16>
 __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
   __shared__ uint32_t lh[kQT][kBins1];
   __shared__ int pg_rows[kQRange / 128];    // paged keys: the range's pool pages
@@ -676,10 +686,13 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
   // collect: the two rows' thresholds and counters
   const int64_t row0 = (int64_t)b * a.Q + t0 + qa0, row1 = (int64_t)b * a.Q + t0 + qa1;
   uint32_t thr0 = 0xFFFFFFFFu, thr1 = 0xFFFFFFFFu;
+  float thf0, thf1;                        // the thresholds as scores (one compare per score)
   if (kMode == kModeCollect) {
     if (t0 + qa0 < a.Q) thr0 = a.ctr[row0 * kCtr + kThrSlot];
     if (t0 + qa1 < a.Q) thr1 = a.ctr[row1 * kCtr + kThrSlot];
   }
+  thf0 = key_floor(thr0);
+  thf1 = key_floor(thr1);
   // a candidate of this lane's query `which` (0: qa0, 1: qa1): its next own
   // slot, or (its slots full) a global one
   uint32_t cn[2] = {0u, 0u};
@@ -735,8 +748,8 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
     float h[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) h[j] = swap_add32(part[j], part[4 + j]);
-    const float s0 = ranked(swap_add16(h[0], h[1]), a.score_bf16);   // queries 0, 1, 4, 5 by lane group
-    const float s1 = ranked(swap_add16(h[2], h[3]), a.score_bf16);   // queries 2, 3, 6, 7
+    const float s0 = ranked(swap_add16(h[0], h[1]), kBf16);   // queries 0, 1, 4, 5 by lane group
+    const float s1 = ranked(swap_add16(h[2], h[3]), kBf16);   // queries 2, 3, 6, 7
     const int64_t blk = blk0 + li;
     if (kMode == kModeStore) {
       if (blk < nv0 && t0 + qa0 < a.Q) {
@@ -752,9 +765,8 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
       if (blk < nv1 && t0 + qa1 < a.Q) a.samp[row1 * a.samp_ld + blk] = s1;
     } else {
       // (few pass: about 1.3 % of the scores at the benchmark's shape)
-      const uint32_t k0 = score_key(s0), k1 = score_key(s1);
-      if (blk < nv0 && t0 + qa0 < a.Q && k0 >= thr0) put_cand(0, row0, sel_key(k0, blk));
-      if (blk < nv1 && t0 + qa1 < a.Q && k1 >= thr1) put_cand(1, row1, sel_key(k1, blk));
+      if (blk < nv0 && t0 + qa0 < a.Q && s0 >= thf0) put_cand(0, row0, sel_key(score_key(s0), blk));
+      if (blk < nv1 && t0 + qa1 < a.Q && s1 >= thf1) put_cand(1, row1, sel_key(score_key(s1), blk));
     }
   };
 
@@ -1705,17 +1717,28 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEve
     const unsigned qt = (unsigned)(a.B * ((a.Q + kQT - 1) / kQT));
     dim3 sgrid(qt, (unsigned)((n_sampled(a.cap) + kQRange - 1) / kQRange));
     dim3 grid(qt, (unsigned)((a.cap + kQRange - 1) / kQRange));
-    hipLaunchKernelGGL(k_score_mx_q<kModeSample>, sgrid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_thresh, dim3(R), dim3(kFThreads), 0, st, a);
-    if (ev)
-      hipExtLaunchKernelGGL(k_score_mx_q<kModeCollect>, grid, dim3(256), 0, st, ev->start, ev->stop, 0,
-                            a);
+    if (a.score_bf16)
+      hipLaunchKernelGGL((k_score_mx_q<kModeSample, true>), sgrid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL(k_score_mx_q<kModeCollect>, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_score_mx_q<kModeSample, false>), sgrid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_thresh, dim3(R), dim3(kFThreads), 0, st, a);
+    auto collect = [&](auto kern) {
+      if (ev)
+        hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, st, ev->start, ev->stop, 0, a);
+      else
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a);
+    };
+    if (a.score_bf16)
+      collect(k_score_mx_q<kModeCollect, true>);
+    else
+      collect(k_score_mx_q<kModeCollect, false>);
     hipLaunchKernelGGL(k_select_pf, dim3(R), dim3(kFThreads), 0, st, a);
     IndexArgs f = a;
     f.fb_only = 1;
-    hipLaunchKernelGGL(k_score_mx_q<kModeStore>, grid, dim3(256), 0, st, f);
+    if (a.score_bf16)
+      hipLaunchKernelGGL((k_score_mx_q<kModeStore, true>), grid, dim3(256), 0, st, f);
+    else
+      hipLaunchKernelGGL((k_score_mx_q<kModeStore, false>), grid, dim3(256), 0, st, f);
     // the handed-over rows, kFbRows at a time
     dim3 fgrid((unsigned)n_chunks(a.cap), (unsigned)(R < kFbRows ? R : kFbRows));
     if (a.score_bf16) {
@@ -1731,10 +1754,16 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEve
   } else if (a.key_mx && a.H == 16 && a.Q >= kQT) {
     dim3 grid((unsigned)(a.B * ((a.Q + kQT - 1) / kQT)),
               (unsigned)((a.cap + kQRange - 1) / kQRange));
-    if (ev)
-      hipExtLaunchKernelGGL(k_score_mx_q<kModeStore>, grid, dim3(256), 0, st, ev->start, ev->stop, 0, a);
+    auto store = [&](auto kern) {
+      if (ev)
+        hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, st, ev->start, ev->stop, 0, a);
+      else
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a);
+    };
+    if (a.score_bf16)
+      store(k_score_mx_q<kModeStore, true>);
     else
-      hipLaunchKernelGGL(k_score_mx_q<kModeStore>, grid, dim3(256), 0, st, a);
+      store(k_score_mx_q<kModeStore, false>);
   } else if (a.key_mx) {
     dim3 grid((unsigned)a.score_wgs, R);
     auto go = [&](auto kern) {
