@@ -248,3 +248,33 @@ def test_sampled_select_bf16_scores_query_tiled(lib):
     print("sampled select: bf16 scores", flush=True)
     kinds = _index_case(lib, rng, Bn, Q, cap, 16, k, m, pos, bf16_scores=True)
     assert kinds.count("exact") >= len(kinds) // 2
+
+
+def test_prefill_rows_match_single_query_calls(lib):
+    """A chunk query's result does not depend on the chunk it is computed
+    in: rows of a 256-query prefill call (query-tiled index scan and
+    sampled selection; attention split by the per-query bound only) against
+    the same queries called one at a time (Q = 1: the decode scan and the
+    three-launch selector): identical top-k ids and bit-identical CSA and HCA
+    outputs."""
+    c, g, bits, ref = _prefill_case(8192, 256)
+    k, n_win = 512, c["n_win"]
+    x = _attend_inputs(lib, c, g, ref)
+    qi = C.bf16_encode(g["q_idx"])
+    topk = lib.v4attn_index_topk(_bf16_t(qi), P.dev(g["w"]), x["keys"], x["pos"], 4, k)
+    out = lib.v4attn_csa_attend(x["q"], x["comp"], topk, x["win"], n_win, x["pos"], None, x["sc"])
+    hout = lib.v4attn_hca_attend(x["q"], x["hcomp"], 128, x["hwin"], n_win, x["pos"], None, x["sc"])
+    torch.cuda.synchronize()
+    for t in (0, 7, 8, 131, 255):
+        print(f"prefill row {t} alone", flush=True)
+        one = lambda a: a[:, t:t + 1].contiguous()
+        tk1 = lib.v4attn_index_topk(one(_bf16_t(qi)), one(P.dev(g["w"])), x["keys"], one(x["pos"]), 4,
+                                    k)
+        o1 = lib.v4attn_csa_attend(one(x["q"]), x["comp"], one(topk), x["win"], n_win, one(x["pos"]),
+                                   None, x["sc"])
+        h1 = lib.v4attn_hca_attend(one(x["q"]), x["hcomp"], 128, x["hwin"], n_win, one(x["pos"]),
+                                   None, x["sc"])
+        torch.cuda.synchronize()
+        assert torch.equal(tk1[:, 0], topk[:, t]), f"row {t}: top-k ids differ"
+        assert torch.equal(o1[:, 0], out[:, t]), f"row {t}: CSA output differs"
+        assert torch.equal(h1[:, 0], hout[:, t]), f"row {t}: HCA output differs"
