@@ -199,6 +199,47 @@ def test_index_topk_ties_lower_index_wins(lib):
         P.check_topk_row(g[0, t], sc[0][t], 5)
 
 
+@pytest.mark.parametrize("Q,kind", [(3, "nonpositive"), (3, "mixed"), (16, "nonpositive"), (16, "mixed")])
+def test_index_topk_signed_weights(lib, Q, kind):
+    """Head weights of any sign (w is any real): "nonpositive" -- w < 0 and
+    one query direction for all heads, so about half the blocks score
+    exactly 0 (every ReLU term zero, the products -0) and the rest below 0:
+    the top k are the k lowest ids among the zeros, with -0 ranked equal to
+    +0; "mixed" -- weights of both signs, scores of both signs.  Q = 3 takes
+    the decode scan and the three-launch selector, Q = 16 the query-tiled
+    scan with the sampled-threshold selection."""
+    print(f"index signed weights Q={Q} {kind}", flush=True)
+    rng = _rng(97 + Q + len(kind))
+    Bn, cap, H, k, m, d = 1, 5000, 16, 300, 4, 128
+    y = _f32(rng, (Bn, cap, d), d ** -0.5)
+    keys = C.idx_encode(y, "mxfp4")
+    if kind == "nonpositive":
+        q1 = _f32(rng, (Bn, Q, 1, d), d ** -0.5)
+        q = np.repeat(q1, H, axis=2)
+        w = -(rng.random((Bn, Q, H)).astype(np.float32) + 0.1)
+    else:
+        q = _f32(rng, (Bn, Q, H, d), d ** -0.5)
+        w = rng.standard_normal((Bn, Q, H)).astype(np.float32)
+    pos = np.full((Bn, Q), m * cap - 1, np.int64)
+    pos[0, 1] = m * (cap // 3) + 1
+    qb = C.bf16_encode(q)
+    qd = C.bf16_decode(qb).astype(np.float32)
+    topk = lib.v4attn_index_topk(P.dev(qb.view(np.int16)).view(torch.bfloat16), P.dev(w),
+                                 P.idx_to_dev(keys), P.dev(pos), m, k)
+    torch.cuda.synchronize()
+    sc = index_scores(qd, w, keys, pos, m)
+    g = topk.cpu().numpy()
+    for t in range(Q):
+        s = sc[0][t]
+        if kind == "nonpositive":
+            assert np.all(s <= 0) and np.sum(s == 0) > k, "the planted zero scores"
+            expect = np.nonzero(s == 0)[0][:k]
+            assert np.array_equal(g[0, t], expect), f"query {t}: not the k lowest ids of the zeros"
+        else:
+            assert (s > 0).any() and (s < 0).any()
+            P.check_topk_row(g[0, t], s, k)
+
+
 def test_index_topk_small_and_empty_visibility(lib):
     rng = _rng(7)
     cap, k = 64, 16
