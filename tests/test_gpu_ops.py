@@ -386,6 +386,41 @@ def test_attend_fp8_edge_cases(lib):
     P.check_out(o, ref)
 
 
+@pytest.mark.parametrize("kind,H", [("hca", 64), ("hca", 32), ("csa", 64)])
+def test_attend_fp8_running_max_jumps(lib, kind, H):
+    """Entries whose logits jump by ~9.5 (base-2) units part-way through a
+    split: the running max moves after the split's first tile, so the rare
+    rescale step runs (joint tile max, P rewritten, accumulators and
+    denominators scaled) -- and the planted entries carry about half of the
+    softmax mass, so a wrong rescale factor shows.  Two jumps sit in
+    different splits, so the merge combines splits of different maxima."""
+    print(f"attend running-max jumps {kind} H={H}", flush=True)
+    rng = _rng(401 + H + len(kind))
+    Bn, Q, R, n_win, D = 1, 2, 160, 128, 512
+    n_comp = 2048 if kind == "csa" else 3000
+    scale = D ** -0.5
+    rows = _f32(rng, (Bn, n_comp, D), D ** -0.5 * 0.5)
+    base = _f32(rng, (Bn, 1, 1, D), 1.0)
+    q = base + _f32(rng, (Bn, Q, H, D), 0.02)
+    u = base[0, 0, 0] / float(base[0, 0, 0] @ base[0, 0, 0])
+    hot = [100, 101, 1000, 1001]
+    for e in hot:                      # logit ln(750) ~ 6.6 nats above the rest
+        rows[0, e] = np.log(750.0) / scale * u
+    comp = C.kv_encode(rows, "fp8", 448)
+    win = C.kv_encode(_f32(rng, (Bn, R, D), D ** -0.5 * 0.5), "fp8", 448)
+    qb = C.bf16_encode(q)
+    pos = np.array([[n_comp * (4 if kind == "csa" else 1) + 40, n_comp * (4 if kind == "csa" else 1) - 1]],
+                   np.int64)
+    if kind == "csa":
+        topk = np.broadcast_to(np.arange(n_comp, dtype=np.int64), (Bn, Q, n_comp)).copy()
+        _, ref = csa_attend(qb, "bf16", comp, topk, win, n_win, pos, None, scale, "bf16")
+        o = _run_attend(lib, "csa", q, True, comp, win, n_win, pos, None, scale, topk=topk)
+    else:
+        _, ref = hca_attend(qb, "bf16", comp, 1, win, n_win, pos, None, scale, "bf16")
+        o = _run_attend(lib, "hca", q, True, comp, win, n_win, pos, None, scale, m=1)
+    P.check_out(o, ref)
+
+
 @pytest.mark.parametrize("H,n_comp,m,n_win,with_sink,f32_out", [
     (64, 30, 1, 16, True, False),      # one split: the kernel writes the output itself
     (64, 3000, 1, 128, False, True),   # 17 splits of 6 tiles, fp32 output
