@@ -31,6 +31,9 @@
 //                 the non-RoPE probability in fp32, so decoding adds no
 //                 rounding.  Online softmax in base 2 with a lazily updated
 //                 running max (rescale only when the max grows by > 8).
+//                 Instantiated with streaming tile loads (one-query CSA
+//                 calls: no other reader of the gathered rows) or plain ones
+//                 (rows shared by head groups or by a chunk's queries).
 //   k_attend_fp8_nr  the same with the query RMSNorm + RoPE of the _nr calls
 //                 ([Notes §9]) in its prologue: each workgroup normalises and
 //                 rotates its 32 heads in registers while its first tiles
@@ -266,6 +269,16 @@ __device__ __forceinline__ StageSrc stage_src(const int* src, const int* tbits, 
   return r;
 }
 
+// kStream: streaming (non-temporal) loads, for calls whose rows no other
+// workgroup reads again soon (CSA decode: gathered top-k rows of one query);
+// otherwise plain loads keep the rows in L2 for the head-group partner and
+// the other queries of a chunk.
+template <bool kStream>
+__device__ __forceinline__ u32x4 tile_load(const uint8_t* p) {
+  return kStream ? __builtin_nontemporal_load((const u32x4*)p) : *(const u32x4*)p;
+}
+
+template <bool kStream>
 __device__ __forceinline__ void stage_load(Bases B, StageSrc ss, int tile, int n_local,
                                            Stage& st) {
   const int t = threadIdx.x;
@@ -307,11 +320,11 @@ __device__ __forceinline__ void stage_load(Bases B, StageSrc ss, int tile, int n
   }
   // the values are stored to LDS one step later: using them now would make
   // the compiler wait for these loads immediately
-  st.r[0] = *(const u32x4*)(nope + q * 16);
-  st.r[1] = *(const u32x4*)(nope + (8 + q) * 16);
-  st.r[2] = *(const u32x4*)(nope + (16 + q) * 16);
-  st.r[3] = *(const u32x4*)(q < 4 ? nope + (24 + q) * 16 : rope + (q - 4) * 16);
-  st.r[4] = *(const u32x4*)(rope + (4 + (q & 3)) * 16);
+  st.r[0] = tile_load<kStream>(nope + q * 16);
+  st.r[1] = tile_load<kStream>(nope + (8 + q) * 16);
+  st.r[2] = tile_load<kStream>(nope + (16 + q) * 16);
+  st.r[3] = tile_load<kStream>(q < 4 ? nope + (24 + q) * 16 : rope + (q - 4) * 16);
+  st.r[4] = tile_load<kStream>(rope + (4 + (q & 3)) * 16);
   st.sc = *scp;
 }
 
@@ -582,7 +595,7 @@ __device__ __forceinline__ int64_t part_block(const AttendArgs& a, int row, int 
 
 // kNr: the _nr calls' query RMSNorm + RoPE ([Notes §9]) fused into the
 // prologue (see below); the output's rotation back is in the epilogues.
-template <bool kNr>
+template <bool kNr, bool kStream>
 __device__ __forceinline__ void attend_fp8(AttendArgs a) {
   __shared__ Fp8Tile tiles[kTileBufs];
   __shared__ Shared sh;
@@ -691,7 +704,7 @@ __device__ __forceinline__ void attend_fp8(AttendArgs a) {
   // register set would push the kernel past 256 VGPRs into scratch); every
   // stage_load issues the same loads (tiles past the split read the zero row)
   Stage st;
-  stage_load(B, stage_src(src, sh.tbits, 0), 0, n_local, st);
+  stage_load<kStream>(B, stage_src(src, sh.tbits, 0), 0, n_local, st);
 
   f32x4 acc[8][2];
 #pragma unroll
@@ -753,7 +766,7 @@ __device__ __forceinline__ void attend_fp8(AttendArgs a) {
     qrv = (u32x4){lo[0], lo[1], hi[0], hi[1]};
   }
   stage_store(&tiles[0], st);
-  stage_load(B, stage_src(src, sh.tbits, 1), 1, n_local, st);
+  stage_load<kStream>(B, stage_src(src, sh.tbits, 1), 1, n_local, st);
   *(u32x4*)&sh.qr[rh][8 * rc] = qrv;
   __syncthreads();
 
@@ -773,7 +786,7 @@ __device__ __forceinline__ void attend_fp8(AttendArgs a) {
     const bool first = t == 0;
     float l_add = softmax_pass(&tiles[cb], &sh, S, sn, sr, c2, pb, wave, lane, first, s2, tmax);
     stage_store(&tiles[nb], nxt);
-    stage_load(B, ns, t + 2, n_local, nxt);
+    stage_load<kStream>(B, ns, t + 2, n_local, nxt);
     __syncthreads();
     VFrag vf = pv_load(&tiles[cb], wave, g, li);
     const i32x4 fl = sh.flag[pb];
@@ -882,8 +895,10 @@ __device__ __forceinline__ void attend_fp8(AttendArgs a) {
   }
 }
 
-__global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) { attend_fp8<false>(a); }
-__global__ void __launch_bounds__(kThreads, 2) k_attend_fp8_nr(AttendArgs a) { attend_fp8<true>(a); }
+template <bool kStream>
+__global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) { attend_fp8<false, kStream>(a); }
+template <bool kStream>
+__global__ void __launch_bounds__(kThreads, 2) k_attend_fp8_nr(AttendArgs a) { attend_fp8<true, kStream>(a); }
 
 // ---------------------------------------------------------------- fp32 VALU path
 // One workgroup per (query, split, head group of kF32Heads); entries are
@@ -1254,16 +1269,25 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st, const KernelEvents
     const int64_t N = (int64_t)rows * a.n_split * ((a.H + kHeads - 1) / kHeads);
     const int64_t per = (N + 7) / 8;
     const bool nr = a.nr_gamma || a.nr_inv;
-    if (ev && nr)
-      hipExtLaunchKernelGGL(k_attend_fp8_nr, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st,
-                            ev->start, ev->stop, 0, a);
-    else if (ev)
-      hipExtLaunchKernelGGL(k_attend_fp8, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st, ev->start,
-                            ev->stop, 0, a);
-    else if (nr)
-      hipLaunchKernelGGL(k_attend_fp8_nr, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st, a);
+    // streaming loads for one-query CSA calls (decode: a query's gathered
+    // rows are read by its two head groups only, and keeping them in L2
+    // costs the calls that follow more than it saves: a 51.5 against
+    // 54.1 us CSA layer); plain loads everywhere else (HCA rows are shared
+    // by the head groups, a chunk's queries share rows: 44.6 against 46.9 us
+    // HCA layer, and the prefill chunk 17.9 -> 16.0 ms).  The choice changes
+    // no result.
+    const bool stream = a.csa && a.Q == 1;
+    const dim3 grid((unsigned)(8 * per)), block(kThreads);
+    auto go = [&](auto kern) {
+      if (ev)
+        hipExtLaunchKernelGGL(kern, grid, block, 0, st, ev->start, ev->stop, 0, a);
+      else
+        hipLaunchKernelGGL(kern, grid, block, 0, st, a);
+    };
+    if (nr)
+      stream ? go(k_attend_fp8_nr<true>) : go(k_attend_fp8_nr<false>);
     else
-      hipLaunchKernelGGL(k_attend_fp8, dim3((unsigned)(8 * per)), dim3(kThreads), 0, st, a);
+      stream ? go(k_attend_fp8<true>) : go(k_attend_fp8<false>);
   } else {
     dim3 grid(rows, a.n_split, (a.H + a.f32_heads - 1) / a.f32_heads);
     if (ev)
