@@ -271,6 +271,40 @@ v4a_status v4attn_csa_attend(const void *q, int32_t q_dtype, const v4a_kv *comp,
                              void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * v4attn_csa_index_attend -- one CSA layer's indexer, top-k selector and
+ * core attention in one call ([Notes §7]: lightning indexer, Top-k selector,
+ * shared key-value MQA over the selected entries plus the sliding window;
+ * [Notes §9] FP4 indexer QK, FP8 entries).  Same results as
+ * v4attn_index_topk followed by v4attn_csa_attend on the same arguments
+ * (bit for bit: topk and out are what the two calls write): topk is filled
+ * and out is the attention over comp rows topk[b][j][:] plus the window.
+ * When every row takes the three-filter selection (not the sampled one of
+ * query-tiled scans) and the entries are FP8, the selector's last step
+ * (ordering the selected ids) runs inside the attention kernel, one launch
+ * fewer; otherwise the two calls run in sequence.
+ *
+ *   q_idx, q_idx_dtype, w, keys, H_I, m, k, topk   as v4attn_index_topk
+ *   q, q_dtype, comp, win, n_win, sink, sm_scale, H, out, out_dtype
+ *                                                  as v4attn_csa_attend
+ *   pos    int64 [B][Q], the positions of both
+ *   ws_index   at least v4attn_workspace_bytes(V4A_OP_CSA_INDEX, B, Q, H_I,
+ *              keys->d, keys->cap, k, 0) bytes (the index workspace plus the
+ *              selector's per-chunk lists, 8 bytes per key row and query)
+ *   ws_attend  at least v4attn_workspace_bytes(V4A_OP_CSA_ATTEND, B, Q, H, D,
+ *              0, k, n_win) bytes
+ * Supported set and errors: those of the two calls; the timing events of
+ * v4attn_time_next_kernel are not consumed.
+ */
+v4a_status v4attn_csa_index_attend(const void *q_idx, int32_t q_idx_dtype, const float *w,
+                                   const v4a_idx *keys, int32_t H_I, int32_t m, int32_t k,
+                                   int32_t *topk, const void *q, int32_t q_dtype,
+                                   const v4a_kv *comp, const v4a_kv *win, int32_t n_win,
+                                   const int64_t *pos, const float *sink, float sm_scale,
+                                   int32_t B, int32_t Q, int32_t H, void *out, int32_t out_dtype,
+                                   void *ws_index, size_t ws_index_bytes, void *ws_attend,
+                                   size_t ws_attend_bytes, void *stream);
+
+/*
  * v4attn_hca_attend -- HCA core attention ([Notes §8]: no top-k; dense over
  * every visible compressed entry, plus the same window branch).  As
  * v4attn_csa_attend with E = { comp rows s < n_vis(p) } ++ window tokens of p.
@@ -460,11 +494,12 @@ v4a_status v4attn_hca_attend_paged(const void *q, int32_t q_dtype, const v4a_kv 
 #define V4A_OP_HCA_ATTEND 3
 #define V4A_OP_CSA_ATTEND_NR 4   /* the _nr variants (same sizes as the plain ops) */
 #define V4A_OP_HCA_ATTEND_NR 5
+#define V4A_OP_CSA_INDEX 6       /* the index workspace of v4attn_csa_index_attend */
 
 /*
  * Workspace bytes a call needs (0 = none).  Arguments that do not apply to
  * `op` are ignored:
- *   INDEX_TOPK: B, Q, H (= H_I), d (= key dim), cap (= keys->cap), k
+ *   INDEX_TOPK, CSA_INDEX: B, Q, H (= H_I), d (= key dim), cap (= keys->cap), k
  *   CSA_ATTEND(_NR): B, Q, H, d (= D), cap (ignored), k, n_win
  *   HCA_ATTEND(_NR): B, Q, H, d (= D), cap (= comp->cap), k (= m), n_win
  * Returns (size_t)-1 for an invalid combination.

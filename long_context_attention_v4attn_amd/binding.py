@@ -16,6 +16,7 @@ F32, BF16, KV_FP8_BF16ROPE, IDX_MXFP4 = 0, 1, 2, 3
 OUT_KV, OUT_IDX = 0, 1
 OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND = 1, 2, 3
 OP_CSA_ATTEND_NR, OP_HCA_ATTEND_NR = 4, 5
+OP_CSA_INDEX = 6
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -107,6 +108,9 @@ _SIGS = {
                                        _I32, _I32, _P, _I32, _P, _P, _SZ, _P]),
     "v4attn_hca_attend_paged": (_I32, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _F, _I32, _I32,
                                        _I32, _P, _I32, _P, _P, _SZ, _P]),
+    "v4attn_csa_index_attend": (_I32, [_P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I32, _P, _P,
+                                       _I32, _P, _P, _F, _I32, _I32, _I32, _P, _I32, _P, _SZ, _P,
+                                       _SZ, _P]),
     "v4attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I64, _I32, _I32]),
     "v4attn_status_str": (ctypes.c_char_p, [_I32]),
     "v4attn_last_hip_error": (_I32, []),
@@ -333,6 +337,34 @@ def v4attn_csa_attend(q, comp, topk, win, n_win, pos, sink, sm_scale, out=None,
                               B, Q, H, _ptr(out), _dtype_code(out), _ptr(ws), wsb, _stream(stream))
     _check(s, "v4attn_csa_attend")
     return out
+
+
+def v4attn_csa_index_attend(q_idx, w, keys, m, k, q, comp, win, n_win, pos, sink, sm_scale,
+                            topk=None, out=None, out_dtype=torch.bfloat16, ws_index=None,
+                            ws_attend=None, stream=None):
+    """v4attn_index_topk followed by v4attn_csa_attend in one call (the
+    selector's ordering step inside the attention kernel); returns
+    (topk, out)."""
+    lib = load()
+    _need_cuda(q_idx, w, q, pos, sink)
+    B, Q, H_I, d = q_idx.shape
+    H, D = q.shape[2], q.shape[3]
+    if topk is None:
+        topk = torch.empty(B, Q, k, dtype=torch.int32, device=q.device)
+    out = _out(q, out, out_dtype)
+    ws_index, wib = _workspace(ws_index, v4attn_workspace_bytes(OP_CSA_INDEX, B, Q, H_I, d,
+                                                                keys.cap, k, 0), q.device)
+    ws_attend, wab = _workspace(ws_attend, v4attn_workspace_bytes(OP_CSA_ATTEND, B, Q, H, D,
+                                                                  comp.cap, k, n_win), q.device)
+    ks, cs, wst = keys.c_struct(), comp.c_struct(), win.c_struct()
+    s = lib.v4attn_csa_index_attend(_ptr(q_idx), _dtype_code(q_idx), _ptr(w), ctypes.byref(ks),
+                                    H_I, m, k, _ptr(topk), _ptr(q), _dtype_code(q),
+                                    ctypes.byref(cs), ctypes.byref(wst), n_win, _ptr(pos),
+                                    _ptr(sink), float(sm_scale), B, Q, H, _ptr(out),
+                                    _dtype_code(out), _ptr(ws_index), wib, _ptr(ws_attend), wab,
+                                    _stream(stream))
+    _check(s, "v4attn_csa_index_attend")
+    return topk, out
 
 
 def v4attn_hca_attend(q, comp, m, win, n_win, pos, sink, sm_scale, out=None,

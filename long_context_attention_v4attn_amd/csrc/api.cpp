@@ -283,20 +283,18 @@ v4a_status v4attn_compress_nr(const void* kv_cur, const void* gate_cur, const vo
                        out_kind, out, nr, stream);
 }
 
-static v4a_status index_topk(const void* q_idx, int32_t q_dtype, const float* w,
-                             const v4a_idx* keys, const int64_t* pos, int32_t B, int32_t Q,
-                             int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
-                             size_t ws_bytes, void* stream, int score_bf16,
-                             const v4a_pages* pages = nullptr, bool fixed_scratch = false) {
-  if (B < 0 || Q < 0) return V4A_ERR_INVALID;
-  if (B == 0 || Q == 0) return V4A_OK;     // nothing to read or write
+// Validates an index call (B, Q >= 1) and fills its kernel arguments; the
+// workspace is carved by the caller.
+static v4a_status index_prepare(IndexArgs& a, const void* q_idx, int32_t q_dtype, const float* w,
+                                const v4a_idx* keys, const int64_t* pos, int32_t B, int32_t Q,
+                                int32_t H_I, int32_t m, int32_t k, int32_t* topk, int score_bf16,
+                                const v4a_pages* pages) {
   if (!q_idx || !w || !keys || !pos || !topk || H_I < 1 || k < 1 || m < 1)
     return V4A_ERR_INVALID;
   if (q_dtype != V4A_F32 && q_dtype != V4A_BF16) return V4A_ERR_INVALID;
   if (!keys->codes || keys->cap < 1 || keys->d < 1) return V4A_ERR_INVALID;
   if (k > 4096 || H_I > 64) return V4A_ERR_UNSUPPORTED;
   if (keys->cap >= ((int64_t)1 << 31)) return V4A_ERR_UNSUPPORTED;
-  IndexArgs a;
   memset(&a, 0, sizeof(a));
   if (keys->fmt == V4A_IDX_MXFP4) {
     if (!keys->scales) return V4A_ERR_INVALID;
@@ -327,6 +325,20 @@ static v4a_status index_topk(const void* q_idx, int32_t q_dtype, const float* w,
     v4a_status s = check_pages(pages, m, keys->cap, 128, &a.pg, &a.cap);
     if (s != V4A_OK) return s;
   }
+  return V4A_OK;
+}
+
+static v4a_status index_topk(const void* q_idx, int32_t q_dtype, const float* w,
+                             const v4a_idx* keys, const int64_t* pos, int32_t B, int32_t Q,
+                             int32_t H_I, int32_t m, int32_t k, int32_t* topk, void* ws,
+                             size_t ws_bytes, void* stream, int score_bf16,
+                             const v4a_pages* pages = nullptr, bool fixed_scratch = false) {
+  if (B < 0 || Q < 0) return V4A_ERR_INVALID;
+  if (B == 0 || Q == 0) return V4A_OK;     // nothing to read or write
+  IndexArgs a;
+  v4a_status s = index_prepare(a, q_idx, q_dtype, w, keys, pos, B, Q, H_I, m, k, topk, score_bf16,
+                               pages);
+  if (s != V4A_OK) return s;
   size_t need = index_workspace_bytes(B, Q, H_I, keys->d, a.cap, a.key_mx);
   if (fixed_scratch) {
     // the library's own device array (no allocation): the call's scratch
@@ -467,6 +479,56 @@ v4a_status v4attn_csa_attend(const void* q, int32_t q_dtype, const v4a_kv* comp,
                               out, out_dtype, nullptr, ws, ws_bytes, stream);
 }
 
+v4a_status v4attn_csa_index_attend(const void* q_idx, int32_t q_idx_dtype, const float* w,
+                                   const v4a_idx* keys, int32_t H_I, int32_t m, int32_t k,
+                                   int32_t* topk, const void* q, int32_t q_dtype,
+                                   const v4a_kv* comp, const v4a_kv* win, int32_t n_win,
+                                   const int64_t* pos, const float* sink, float sm_scale,
+                                   int32_t B, int32_t Q, int32_t H, void* out, int32_t out_dtype,
+                                   void* ws_index, size_t ws_index_bytes, void* ws_attend,
+                                   size_t ws_attend_bytes, void* stream) {
+  bool empty;
+  v4a_status s = check_attend(q, q_dtype, comp, win, n_win, pos, B, Q, H, out, out_dtype, &empty);
+  if (s != V4A_OK || empty) return s;
+  IndexArgs ia;
+  s = index_prepare(ia, q_idx, q_idx_dtype, w, keys, pos, B, Q, H_I, m, k, topk, 0, nullptr);
+  if (s != V4A_OK) return s;
+  AttendArgs aa;
+  fill_attend(aa, q, q_dtype, comp, win, n_win, pos, sink, sm_scale, B, Q, H, out, out_dtype);
+  aa.csa = 1;
+  aa.topk = topk;
+  aa.k = k;
+  aa.m = 1;
+  attend_plan(aa, (int64_t)k + n_win);
+  // the emit step moves into the attention when the rows take the
+  // three-filter selection and the attention is the FP8 kernel with splits
+  // of at most 256 entries; otherwise the two calls run as they are
+  const int fused = aa.fp8 && index_filter_path(ia) &&
+                    aa.split_size <= 256;
+  const size_t need_i = index_workspace_bytes(B, Q, H_I, keys->d, ia.cap, ia.key_mx, fused);
+  if (!ws_index || ws_index_bytes < need_i) return V4A_ERR_WORKSPACE;
+  const size_t need_a = attend_workspace_bytes(aa);
+  if (need_a > 0) {
+    if (!ws_attend || ws_attend_bytes < need_a) return V4A_ERR_WORKSPACE;
+    attend_carve(aa, ws_attend);
+  }
+  index_carve(ia, ws_index, fused);
+  hipError_t e = launch_index_topk(ia, (hipStream_t)stream, nullptr);
+  if (e != hipSuccess) return hip_status(e);
+  if (fused) {
+    aa.sel_ctr = ia.ctr;
+    aa.sel_cand = ia.cand;
+    aa.sel_elist = ia.elist;
+    aa.sel_elen = ia.elen;
+    aa.sel_scores = ia.scores;
+    aa.sel_sc_ld = ia.sc_ld;
+    aa.sel_cap = ia.cap;
+    aa.sel_m = m;
+    aa.sel_topk = topk;
+  }
+  return hip_status(launch_attend(aa, (hipStream_t)stream, nullptr));
+}
+
 v4a_status v4attn_hca_attend_nr(const void* q, int32_t q_dtype, const v4a_kv* comp, int32_t m,
                                 const v4a_kv* win, int32_t n_win, const int64_t* pos,
                                 const float* sink, float sm_scale, int32_t B, int32_t Q, int32_t H,
@@ -498,9 +560,10 @@ v4a_status v4attn_hca_attend(const void* q, int32_t q_dtype, const v4a_kv* comp,
 size_t v4attn_workspace_bytes(int32_t op, int32_t B, int32_t Q, int32_t H, int32_t d, int64_t cap,
                               int32_t k, int32_t n_win) {
   if (B < 0 || Q < 0 || H < 1 || d < 1) return (size_t)-1;
-  if (op == V4A_OP_INDEX_TOPK) {
+  if (op == V4A_OP_INDEX_TOPK || op == V4A_OP_CSA_INDEX) {
     if (cap < 1) return (size_t)-1;
-    return index_workspace_bytes(B, Q, H, d, cap, d == 128 && H % 16 == 0 ? 1 : 0);
+    return index_workspace_bytes(B, Q, H, d, cap, d == 128 && H % 16 == 0 ? 1 : 0,
+                                 op == V4A_OP_CSA_INDEX);
   }
   if (op == V4A_OP_CSA_ATTEND_NR) op = V4A_OP_CSA_ATTEND;
   if (op == V4A_OP_HCA_ATTEND_NR) op = V4A_OP_HCA_ATTEND;

@@ -34,6 +34,10 @@
 //                 Instantiated with streaming tile loads (one-query CSA
 //                 calls: no other reader of the gathered rows) or plain ones
 //                 (rows shared by head groups or by a chunk's queries).
+//   k_attend_fp8_sel  the same for the fused index + CSA call: the prologue
+//                 derives the split's top-k ids from the selector's filter
+//                 results (the emit step; see derive_topk) instead of
+//                 reading the emitted list.
 //   k_attend_fp8_nr  the same with the query RMSNorm + RoPE of the _nr calls
 //                 ([Notes §9]) in its prologue: each workgroup normalises and
 //                 rotates its 32 heads in registers while its first tiles
@@ -45,6 +49,7 @@
 //   k_merge_tiled / k_merge  combine split partials in fixed split order.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace v4a {
 
@@ -201,6 +206,151 @@ __device__ __forceinline__ int32_t prefetch_topk(const AttendArgs& a, int row, i
   const int32_t* p = has ? a.topk + (int64_t)row * a.k + (e < a.k ? e : a.k - 1)
                          : (const int32_t*)(a.pos + row);
   return *p;
+}
+
+// Fused selection ([Notes §7] Top-k; the emit step of the selector moved
+// into the attention): the ids of top-k slots e_beg .. e_beg + 255 of the
+// row, one per thread, exactly as the emit kernel writes them -- ascending
+// ids, lower id first among equal scores, -1 past k' = min(k, n_vis).  The
+// threshold T is the need-th largest selection key among the filters'
+// candidates (the emit's own resolution); the filters' per-chunk lists hold
+// the selection keys of every id at or above the candidates' bin in id
+// order, so the ids with key >= T, in list order, are the top-k list.  Head
+// group 0 writes its slots to sel_topk (every slot below k belongs to one
+// split).  Scratch: the tile buffers' LDS, before the first tile.
+constexpr size_t kSelLds = (size_t)kEmitCand * 8 + (size_t)kBinsMax * 4 +
+                           (size_t)(kSelMaxChunks + 4) * 4 + (size_t)kThreads * 4 + 16;
+constexpr int kSelPer = 16;                  // list entries per thread and step
+
+__device__ int32_t derive_topk(const AttendArgs& a, int row, int hgrp, int e_beg, uint8_t* lds) {
+  const int t = threadIdx.x;
+  uint64_t* cl = (uint64_t*)lds;                          // candidate keys
+  uint32_t* lh = (uint32_t*)(cl + kEmitCand);             // radix histogram
+  uint32_t* cstart = lh + kBinsMax;                       // list starts, kSelMaxChunks + 1
+  int32_t* slot = (int32_t*)(cstart + kSelMaxChunks + 4);
+  uint32_t* tmp = (uint32_t*)(slot + kThreads);
+  // Everything that depends on nothing else goes out first, unconditionally
+  // (a load under a branch would be waited for at the branch): the query
+  // position, the counters, this thread's candidate slot (the list always
+  // has kCandCap slots), and the head of one chunk's list: the row's nch
+  // chunks (nch <= 256) share the 256 threads, tpc = 256 / nch rounded down
+  // to a power of two a chunk, kSelPer entries each (entries past the list
+  // are masked below).  When no list is longer than tpc * kSelPer (the
+  // 1M-context decode: 64 chunks of about k / 64 entries, 64 loaded each)
+  // these are all the entries the selection needs.
+  const int64_t p = a.pos[row];
+  const uint32_t* ctr = a.sel_ctr + (size_t)row * kCtr;
+  const uint32_t n_cand = ctr[0], b12 = ctr[2], need = ctr[3];
+  const int64_t nch = n_chunks(a.sel_cap);
+  const uint32_t* elen = a.sel_elen + (size_t)row * nch;
+  const uint64_t* elist = a.sel_elist + (size_t)row * nch * kFilterChunk;
+  const uint64_t* gc = a.sel_cand + (size_t)row * kCandCap;
+  const uint64_t c_first = gc[t];
+  const int lg = nch <= kThreads ? 32 - __builtin_clz((uint32_t)nch - 1u | 1u) : 0;
+  const int tpc = nch <= 1 ? kThreads : (nch <= kThreads ? kThreads >> lg : 1);   // threads a chunk
+  const int fc = t / tpc, fq = t % tpc;                   // fast path: chunk, part
+  const int64_t fcc = fc < nch ? fc : nch - 1;
+  const uint32_t flen = elen[fcc];
+  uint64_t key[kSelPer];
+  {
+    const u32x4* ep = (const u32x4*)(elist + (size_t)fcc * kFilterChunk + fq * kSelPer);
+#pragma unroll
+    for (int j = 0; j < kSelPer / 2; j++) {
+      const u32x4 v = ep[j];
+      key[2 * j] = ((uint64_t)v[1] << 32) | v[0];
+      key[2 * j + 1] = ((uint64_t)v[3] << 32) | v[2];
+    }
+  }
+  const int64_t nv = n_visible(p, a.sel_m, a.sel_cap);
+  const int kk = (int)(nv < a.k ? nv : a.k);
+  // every visible block is selected (k_filter1 has written topk)
+  if (kk == nv) return e_beg + t < nv ? e_beg + t : -1;
+  const int nchv = (int)((nv + kFilterChunk - 1) / kFilterChunk);   // <= kSelMaxChunks
+  const bool in_lds = n_cand <= (uint32_t)kEmitCand;
+  if (in_lds) {
+    if ((uint32_t)t < n_cand) cl[t] = c_first;
+    for (uint32_t i = t + kThreads; i < n_cand; i += kThreads) cl[i] = gc[i];
+  }
+  slot[t] = -1;
+  const bool fast = __syncthreads_and(nch <= kThreads &&
+                                      (fc >= nchv || flen <= (uint32_t)(tpc * kSelPer)));
+  const CandSrc src{in_lds ? cl : nullptr, gc, n_cand, a.sel_scores + (size_t)row * a.sel_sc_ld,
+                    nv, b12, 32 - kSh2, n_cand <= (uint32_t)kCandCap};
+  const uint64_t T = (src.compact && in_lds && n_cand <= (uint32_t)kRankCand)
+                         ? rank_threshold(cl, n_cand, need)
+                         : resolve_threshold(src, need, lh, tmp);
+  const int r_end = min(e_beg + kThreads, kk);
+  if (fast) {
+    // the threads in order hold the concatenated lists in order: one scan
+    // of the counts of keys >= T places every selected id
+    const int nval = fc < nchv ? max(0, min((int)flen - fq * kSelPer, kSelPer)) : 0;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kSelPer; j++) cnt += (j < nval && key[j] >= T) ? 1u : 0u;
+    uint32_t pos = block_incl_scan(cnt, tmp) - cnt;
+#pragma unroll
+    for (int j = 0; j < kSelPer; j++) {
+      if (j < nval && key[j] >= T) {
+        if (pos >= (uint32_t)e_beg && pos < (uint32_t)r_end)
+          slot[pos - e_beg] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key[j] & 0xFFFFFFFFu));
+        pos++;
+      }
+    }
+  } else {
+    // general: list starts from the lengths, then walk the concatenated
+    // lists kSelPer consecutive entries per thread a step, until this
+    // split's slots are placed
+    constexpr int kCpt = kSelMaxChunks / kThreads;        // chunks per thread
+    uint32_t len[kCpt];
+    uint32_t lsum = 0;
+#pragma unroll
+    for (int j = 0; j < kCpt; j++) {
+      const int c = t * kCpt + j;
+      len[j] = c < nchv ? elen[c] : 0u;
+      lsum += len[j];
+    }
+    uint32_t n_e;
+    uint32_t st = block_incl_scan(lsum, tmp, &n_e) - lsum;
+#pragma unroll
+    for (int j = 0; j < kCpt; j++) {
+      cstart[t * kCpt + j] = st;
+      st += len[j];
+    }
+    if (t == 0) cstart[kSelMaxChunks] = n_e;
+    __syncthreads();
+    uint32_t done = 0;                     // entries >= T before this step
+    for (uint32_t base = 0; base < n_e && done < (uint32_t)r_end; base += kThreads * kSelPer) {
+      const uint32_t i0 = base + (uint32_t)t * kSelPer;
+      // the chunk of entry i0: the last c < nchv with cstart[c] <= i0
+      int c = 0;
+      for (int w = kSelMaxChunks / 2; w >= 1; w >>= 1)
+        if (c + w < nchv && cstart[c + w] <= i0) c += w;
+#pragma unroll
+      for (int j = 0; j < kSelPer; j++) {
+        const uint32_t i = i0 + j;
+        while (c + 1 < nchv && cstart[c + 1] <= i) c++;
+        key[j] = i < n_e ? elist[(size_t)c * kFilterChunk + (i - cstart[c])] : 0ull;
+      }
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kSelPer; j++) cnt += (i0 + j < n_e && key[j] >= T) ? 1u : 0u;
+      uint32_t tot;
+      uint32_t pos = done + block_incl_scan(cnt, tmp, &tot) - cnt;
+#pragma unroll
+      for (int j = 0; j < kSelPer; j++) {
+        if (i0 + j < n_e && key[j] >= T) {
+          if (pos >= (uint32_t)e_beg && pos < (uint32_t)r_end)
+            slot[pos - e_beg] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key[j] & 0xFFFFFFFFu));
+          pos++;
+        }
+      }
+      done += tot;
+    }
+  }
+  __syncthreads();
+  const int32_t id = slot[t];
+  if (hgrp == 0 && e_beg + t < a.k) a.sel_topk[(size_t)row * a.k + e_beg + t] = id;
+  return id;
 }
 
 __device__ __forceinline__ void resolve_sources(const AttendArgs& a, const RowEntries& r, int row,
@@ -595,14 +745,14 @@ __device__ __forceinline__ int64_t part_block(const AttendArgs& a, int row, int 
 
 // kNr: the _nr calls' query RMSNorm + RoPE ([Notes §9]) fused into the
 // prologue (see below); the output's rotation back is in the epilogues.
-template <bool kNr, bool kStream>
+template <bool kNr, bool kStream, bool kSel = false>
 __device__ __forceinline__ void attend_fp8(AttendArgs a) {
   __shared__ Fp8Tile tiles[kTileBufs];
   __shared__ Shared sh;
   __shared__ int src[kMaxSplit];
   int row, split, hgrp;
   if (!wg_coords(a, &row, &split, &hgrp)) return;
-  const int32_t pre = prefetch_topk(a, row, split * a.split_size);
+  int32_t pre = kSel ? -1 : prefetch_topk(a, row, split * a.split_size);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int eh = wave & 1, wht = wave >> 1;  // logits: entry half, head tile
@@ -658,6 +808,9 @@ __device__ __forceinline__ void attend_fp8(AttendArgs a) {
   const int n_local = __builtin_amdgcn_readfirstlane(e_end > e_beg ? e_end - e_beg : 0);
   const int n_tiles = (n_local + kTile - 1) / kTile;
 
+  // fused selection: the split's top-k ids (the tile buffers are free
+  // until the first tile is staged, after the barrier below)
+  if (kSel && e_beg < a.k) pre = derive_topk(a, row, hgrp, e_beg, (uint8_t*)tiles);
   resolve_sources(a, r, row, e_beg, n_local, n_tiles, pre, src, sh.tbits);
   if (kNr) {
     // the weights go to the third tile buffer (first written after the
@@ -899,6 +1052,11 @@ template <bool kStream>
 __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8(AttendArgs a) { attend_fp8<false, kStream>(a); }
 template <bool kStream>
 __global__ void __launch_bounds__(kThreads, 2) k_attend_fp8_nr(AttendArgs a) { attend_fp8<true, kStream>(a); }
+template <bool kStream>
+__global__ void __launch_bounds__(kThreads, 2) k_attend_fp8_sel(AttendArgs a) {
+  attend_fp8<false, kStream, true>(a);
+}
+static_assert(kSelLds <= sizeof(Fp8Tile) * kTileBufs, "the fused selection's scratch fits the tile buffers");
 
 // ---------------------------------------------------------------- fp32 VALU path
 // One workgroup per (query, split, head group of kF32Heads); entries are
@@ -1284,7 +1442,9 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st, const KernelEvents
       else
         hipLaunchKernelGGL(kern, grid, block, 0, st, a);
     };
-    if (nr)
+    if (a.sel_ctr)
+      stream ? go(k_attend_fp8_sel<true>) : go(k_attend_fp8_sel<false>);
+    else if (nr)
       stream ? go(k_attend_fp8_nr<true>) : go(k_attend_fp8_nr<false>);
     else
       stream ? go(k_attend_fp8<true>) : go(k_attend_fp8<false>);

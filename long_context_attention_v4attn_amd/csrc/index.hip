@@ -38,27 +38,12 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace v4a {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr int kBins1 = 256;                // first radix digit: key bits 31..24
-constexpr int kSh1 = 24;
-constexpr int kBins2 = 2048;               // second digit: key bits 23..13
-constexpr int kSh2 = 13;
-constexpr int kBinsMax = 4096;             // widest digit of the final select
-constexpr int kCandCap = 16384;            // candidate slots per query
-constexpr int kFThreads = 256;
-constexpr int kPer = 16;                   // consecutive scores per filter thread
-constexpr int kFilterChunk = kFThreads * kPer;   // scores per filter workgroup
-static_assert(kBins1 == kFThreads, "one first-digit bin per filter thread");
-constexpr int kCtr = 8;                    // counters per query
-constexpr int kFbSlot = 1;                 // counter slot: the row takes the full-score path
-constexpr int kCntSlot = 6;                // counter slot: candidates above the sampled threshold
-constexpr int kThrSlot = 7;                // counter slot: the sampled threshold key
-__host__ __device__ inline int64_t score_ld(int64_t cap) { return (cap + 63) / 64 * 64; }
-__host__ __device__ inline int64_t n_chunks(int64_t cap) { return (cap + kFilterChunk - 1) / kFilterChunk; }
 // Sampled-threshold selection of query-tiled scans (prefill chunks): the
 // sample is every 16th tile of 16 blocks (blocks 256 j .. 256 j + 15).
 __host__ __device__ inline int64_t n_sampled(int64_t nv) {
@@ -105,7 +90,7 @@ static ScanPlan scan_plan(int64_t cap, int64_t R, int H, int Q, int key_mx) {
   return p;
 }
 
-size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx) {
+size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx, int fused) {
   const size_t R = (size_t)B * Q;
   const ScanPlan sp = scan_plan(cap, (int64_t)R, H, Q, key_mx);
   size_t n = align256(R * kBins1 * (size_t)sp.hp_ld * sizeof(uint16_t));
@@ -117,10 +102,18 @@ size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx
   n += align256(R * (size_t)n_chunks(cap) * sizeof(uint32_t));
   if (pf_sampled(cap, H, Q, key_mx))
     n += align256(R * (size_t)samp_ld(cap) * sizeof(float)) + align256((R + 1) * sizeof(uint32_t));
+  if (fused)
+    n += align256(R * (size_t)n_chunks(cap) * kFilterChunk * sizeof(uint64_t)) +
+         align256(R * (size_t)n_chunks(cap) * sizeof(uint32_t));
   return n;
 }
 
-void index_carve(IndexArgs& a, void* ws) {
+bool index_filter_path(const IndexArgs& a) {
+  return !pf_sampled(a.cap, a.H, a.Q, a.key_mx) && !a.score_bf16 &&
+         n_chunks(a.cap) <= kSelMaxChunks;
+}
+
+void index_carve(IndexArgs& a, void* ws, int fused) {
   const size_t R = (size_t)a.B * a.Q;
   const ScanPlan sp = scan_plan(a.cap, (int64_t)R, a.H, a.Q, a.key_mx);
   a.score_iters = sp.iters;
@@ -159,25 +152,15 @@ void index_carve(IndexArgs& a, void* ws) {
     a.samp = (float*)p;
     p += align256(R * (size_t)a.samp_ld * sizeof(float));
     a.fbl = (uint32_t*)p;
+    p += align256((R + 1) * sizeof(uint32_t));
   }
-}
-
-__device__ __forceinline__ int64_t n_visible(int64_t p, int m, int64_t cap) {
-  if (p < 0) return 0;
-  int64_t nv = (p + 1) / m;
-  return nv < cap ? nv : cap;
-}
-
-// Order-preserving key of a score; -0 is ranked equal to +0.
-__device__ __forceinline__ uint32_t score_key(float f) {
-  if (f == 0.0f) f = 0.0f;
-  return order_key(f);
-}
-
-// The 64-bit selection key of id i: score key above, inverted id below, so
-// that of two equal scores the lower id ranks higher.
-__device__ __forceinline__ uint64_t sel_key(uint32_t k32, int64_t i) {
-  return ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+  a.elist = nullptr;
+  a.elen = nullptr;
+  if (fused) {
+    a.elist = (uint64_t*)p;
+    p += align256(R * (size_t)n_chunks(a.cap) * kFilterChunk * sizeof(uint64_t));
+    a.elen = (uint32_t*)p;
+  }
 }
 
 // The selector's score precision.  fp32, or the bf16 variant ([Notes §9]:
@@ -864,57 +847,6 @@ __global__ void __launch_bounds__(256) k_score_f32(IndexArgs a) {
 
 // ---------------------------------------------------------------- filter + select
 
-// Inclusive block scan of one value per thread.
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp,
-                                                    uint32_t* total = nullptr) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  if (lane == 63) tmp[wave] = v;
-  __syncthreads();
-  uint32_t add = 0, all = 0;
-  for (int w = 0; w < kFThreads / 64; w++) {
-    add += w < wave ? tmp[w] : 0u;
-    all += tmp[w];
-  }
-  if (total) *total = all;
-  __syncthreads();
-  return v + add;
-}
-
-// Find the bin (scanning from the top) where the cumulative count reaches
-// `need` (1 <= need <= total); writes (bin, count strictly above) to shared
-// memory.  All threads must call it; nb is a power of two (a multiple of
-// kFThreads, or below it: one bin per thread, the rest empty).
-__device__ void find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* tmp,
-                         int* s_bin, uint32_t* s_above) {
-  const int per = nb >= kFThreads ? nb / kFThreads : 1;
-  uint32_t cnt = 0;
-  for (int j = 0; j < per; j++) {
-    const int i = threadIdx.x * per + j;
-    cnt += i < nb ? h[nb - 1 - i] : 0u;
-  }
-  uint32_t incl = block_incl_scan(cnt, tmp);
-  uint32_t excl = incl - cnt;
-  if (excl < need && incl >= need) {
-    uint32_t above = excl;
-    for (int j = 0; j < per; j++) {
-      int bin = nb - 1 - (threadIdx.x * per + j);      // >= 0: this thread's count is not empty
-      if (above + h[bin] >= need) {
-        *s_bin = bin;
-        *s_above = above;
-        break;
-      }
-      above += h[bin];
-    }
-  }
-  __syncthreads();
-}
-
-
 // This thread's kPer consecutive scores of filter chunk `chunk`, in two
 // halves so that the loads can be issued before anything else the kernel
 // waits for: issue_group needs no visible count (the score rows are padded to
@@ -1131,94 +1063,6 @@ struct CandList {
   }
 };
 
-// Candidates of the threshold search: the compact list (in LDS, or the
-// query's global list), or (when it overflowed) the query's scores filtered
-// by the candidates' common key prefix (the top pbits bits of the score key;
-// pbits = 0: no common prefix).
-struct CandSrc {
-  const uint64_t* lds;                     // the list in LDS, or null
-  const uint64_t* glob;                    // the query's global list
-  uint32_t n;
-  const float* sc;                         // the query's score row
-  int64_t nv;
-  uint32_t pfx;
-  int pbits;
-  bool compact;
-  __device__ __forceinline__ int64_t size() const { return compact ? (int64_t)n : nv; }
-  __device__ __forceinline__ bool get(int64_t i, uint64_t* key) const {
-    if (compact) {
-      *key = lds ? lds[i] : glob[i];
-      return true;
-    }
-    const uint32_t k32 = score_key(sc[i]);
-    *key = sel_key(k32, i);
-    return pbits == 0 || (k32 >> (32 - pbits)) == pfx;
-  }
-};
-
-// Sum of one value per thread over the workgroup.
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* tmp) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint32_t t = 0;
-  for (int w = 0; w < kFThreads / 64; w++) t += tmp[w];
-  __syncthreads();
-  return t;
-}
-
-// The exact 64-bit threshold T: the need-th largest key among the
-// candidates (radix select on the bits below the candidates' common key
-// prefix).  Exactly `need` candidates have keys >= T.
-__device__ uint64_t resolve_threshold(const CandSrc& src, uint32_t need, uint32_t* lh,
-                                      uint32_t* tmp) {
-  __shared__ uint64_t s_prefix, s_mask;
-  __shared__ uint32_t s_need, s_above;
-  __shared__ int s_bin, s_done;
-  if (threadIdx.x == 0) {
-    s_prefix = src.pbits ? (uint64_t)src.pfx << (64 - src.pbits) : 0ull;
-    s_mask = src.pbits ? (((uint64_t)1 << src.pbits) - 1) << (64 - src.pbits) : 0ull;
-    s_need = need;
-    s_done = 0;
-  }
-  __syncthreads();
-  // remaining digits: the score key bits below the prefix, then the
-  // inverted id, 11 bits a pass from the top (all that is left once 12 or
-  // fewer remain)
-  const int64_t n = src.size();
-  for (int lo = 64 - src.pbits; lo > 0;) {
-    if (s_done) break;
-    const int wd = lo > 12 ? 11 : lo;
-    const int sh = lo - wd;
-    lo = sh;
-    const uint32_t nb = 1u << wd;
-    for (int i = threadIdx.x; i < (int)nb; i += blockDim.x) lh[i] = 0u;
-    __syncthreads();
-    const uint64_t pm = s_mask, pp = s_prefix;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-      uint64_t key;
-      if (src.get(i, &key) && (key & pm) == pp) atomicAdd(&lh[(uint32_t)(key >> sh) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    find_bin(lh, (int)nb, s_need, tmp, &s_bin, &s_above);
-    if (threadIdx.x == 0) {
-      const uint32_t rem = s_need - s_above;
-      s_prefix = pp | ((uint64_t)s_bin << sh);
-      s_mask = pm | ((uint64_t)(nb - 1) << sh);
-      // the whole bin is taken: the prefix with the remaining bits zero is
-      // a threshold every key of the bin meets
-      if (lh[s_bin] == rem) s_done = 1;
-      s_need = rem;
-    }
-    __syncthreads();
-  }
-  const uint64_t T = s_prefix;
-  __syncthreads();
-  return T;
-}
-
 __device__ __forceinline__ void filter2_row(const IndexArgs& a, const int row) {
   __shared__ uint32_t lh[kBins2];
   __shared__ uint32_t tmp[kFThreads / 64];
@@ -1258,8 +1102,31 @@ __device__ __forceinline__ void filter2_row(const IndexArgs& a, const int row) {
     cnd.append(in && d12 == b12, sel_key(k32[j], i0 + j), ctr + 0, cand);
   }
   cnd.flush(ctr + 0, cand, &s_base);
-  // the chunk's count of ids above the candidates' bin; the threshold digits
-  above = block_sum(above, tmp);
+  if (a.elist) {
+    // fused with the CSA attention: the chunk's selection keys of every id
+    // at or above the candidates' bin (the ids above it and the
+    // candidates), in id order; the attention filters them by the exact
+    // threshold in place of the emit step.  One scan gives both the list
+    // positions (low half) and the count above the bin (high half); both
+    // stay below 2^16 (4096 ids a chunk).
+    uint32_t ecnt = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; j++) ecnt += (j < n_in && (k32[j] >> kSh2) >= b12) ? 1u : 0u;
+    const uint32_t packed = (above << 16) | ecnt;
+    uint32_t tot;
+    uint32_t epos = (block_incl_scan(packed, tmp, &tot) - packed) & 0xFFFFu;
+    const size_t ci = (size_t)row * n_chunks(a.cap) + blockIdx.x;
+    uint64_t* el = a.elist + ci * kFilterChunk;
+#pragma unroll
+    for (int j = 0; j < kPer; j++)
+      if (j < n_in && (k32[j] >> kSh2) >= b12) el[epos++] = sel_key(k32[j], i0 + j);
+    if (threadIdx.x == 0) a.elen[ci] = tot & 0xFFFFu;
+    above = tot >> 16;
+  } else {
+    // the chunk's count of ids above the candidates' bin
+    above = block_sum(above, tmp);
+  }
+  // the threshold digits
   if (threadIdx.x == 0) {
     a.chunk[(size_t)row * n_chunks(a.cap) + blockIdx.x] = above;
     if (blockIdx.x == 0) {
@@ -1280,24 +1147,6 @@ __global__ void __launch_bounds__(kFThreads) k_filter2(IndexArgs a) {
     filter2_row(a, (int)a.fbl[1 + r]);
     __syncthreads();
   }
-}
-
-constexpr int kEmitCand = 4096;            // candidates resolved from LDS
-constexpr int kRankCand = 128;             // candidates resolved by counting ranks
-
-// The threshold when the candidates are few and in LDS: the keys are all
-// distinct (the low word is the inverted id), so the need-th largest is the
-// one candidate that exactly need - 1 others exceed.
-__device__ uint64_t rank_threshold(const uint64_t* cl, uint32_t n, uint32_t need) {
-  __shared__ uint64_t s_T;
-  if (threadIdx.x < n) {
-    const uint64_t c = cl[threadIdx.x];
-    uint32_t r = 0;
-    for (uint32_t j = 0; j < n; j++) r += cl[j] > c ? 1u : 0u;
-    if (r == need - 1) s_T = c;
-  }
-  __syncthreads();
-  return s_T;
 }
 
 // Every workgroup of a query resolves the threshold T from the candidates
@@ -1804,6 +1653,7 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t st, const KernelEve
     hipLaunchKernelGGL(k_filter2, fgrid, dim3(kFThreads), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.elist) return hipSuccess;          // the CSA attention takes the emit step
   if (a.score_bf16)
     hipLaunchKernelGGL(k_emit_bf16, fgrid, dim3(kFThreads), 0, st, a);
   else

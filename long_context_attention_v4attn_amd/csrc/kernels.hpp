@@ -98,9 +98,19 @@ struct IndexArgs {
   int fb_only;               // 1: the full-score kernels take only the rows handed over
   uint32_t* fbl;             // [1 + R]: count, then the rows handed over (sampled path)
   Pages pg;                  // paged keys (MXFP4 only; >= 128 keys per page)
+  // selection fused with the CSA attention (null: the emit kernel writes
+  // topk): k_filter2 writes, per chunk, the selection keys of every id at
+  // or above the candidates' bin in id order, and no emit kernel runs
+  uint64_t* elist;           // [R][n_chunks][4096]
+  uint32_t* elen;            // [R][n_chunks] list lengths
 };
-size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx);
-void index_carve(IndexArgs& a, void* ws);
+// fused = 1: with the per-chunk lists of the fused selection
+size_t index_workspace_bytes(int B, int Q, int H, int d, int64_t cap, int key_mx, int fused = 0);
+void index_carve(IndexArgs& a, void* ws, int fused = 0);
+// The call takes the three-filter selection (k_filter1, k_filter2, k_emit)
+// for every row, with at most kSelMaxChunks filter chunks per row, so that
+// its emit step can move into the CSA attention.
+bool index_filter_path(const IndexArgs& a);
 // `ev` (may be null): a start / stop event pair recorded around the call's
 // dominant kernel (hipExtLaunchKernelGGL), for kernel-level timing.
 struct KernelEvents {
@@ -147,7 +157,23 @@ struct AttendArgs {
   const float* nr_inv;       // [d_rope / 2] or null
   float nr_eps;
   Pages c_pg;                // paged compressed cache (FP8 path only)
+  // fused selection (FP8 CSA only; sel_ctr null: the ids are read from
+  // topk): each workgroup derives the ids of its split's top-k slots from
+  // the selector's filter results (IndexArgs ctr / cand / elist / elen /
+  // scores of the same rows) and head group 0 writes them to sel_topk
+  const uint32_t* sel_ctr;
+  const uint64_t* sel_cand;
+  const uint64_t* sel_elist;
+  const uint32_t* sel_elen;
+  const float* sel_scores;
+  int64_t sel_sc_ld;
+  int64_t sel_cap;           // the indexer keys' capacity
+  int sel_m;                 // their compression rate
+  int32_t* sel_topk;         // [R][k]
 };
+// The fused selection handles at most this many filter chunks per row and
+// splits of at most 256 entries.
+constexpr int kSelMaxChunks = 1024;
 void attend_plan(AttendArgs& a, int64_t n_entries_max);
 size_t attend_workspace_bytes(const AttendArgs& a);
 void attend_carve(AttendArgs& a, void* ws);

@@ -57,6 +57,10 @@ def test_workspace_sizes(clib):
     a = B.v4attn_workspace_bytes(B.OP_HCA_ATTEND, 1, 1, 64, 512, 8192, 128, 128)
     b = B.v4attn_workspace_bytes(B.OP_HCA_ATTEND, 16, 1, 64, 512, 8192, 128, 128)
     assert a > 0 and b >= 16 * a - 16 * 512
+    # the fused call's index workspace adds the selector's per-chunk lists
+    # (8 bytes per key row and query)
+    f = B.v4attn_workspace_bytes(B.OP_CSA_INDEX, 4, 1, 16, 128, 262144, 2048, 0)
+    assert f >= n + 4 * 262144 * 8
     with pytest.raises(B.V4AttnError):
         B.v4attn_workspace_bytes(99, 1, 1, 1, 1, 1, 1, 1)
 
@@ -118,6 +122,15 @@ def test_invalid_arguments_rejected_on_host(clib):
     big = _KV(2, 448, 64, 0, 10000, 0x1000, 0x2000, 0x3000)
     assert clib.v4attn_hca_attend(FAKE, 1, r(big), 4, r(kv), 16, FAKE, None, ctypes.c_float(0.1),
                                   1, 1, 64, FAKE, 1, None, 0, None) == -3
+    # the fused index + CSA call: the index call's checks (k = 0), the
+    # attend call's (f32 q on FP8 entries), a missing index workspace
+    fused = clib.v4attn_csa_index_attend
+    assert fused(FAKE, 1, FAKE, r(ix), 16, 4, 0, FAKE, FAKE, 1, r(kv), r(kv), 16, FAKE, None,
+                 ctypes.c_float(0.1), 1, 1, 64, FAKE, 1, FAKE, 1 << 30, FAKE, 1 << 30, None) == -1
+    assert fused(FAKE, 1, FAKE, r(ix), 16, 4, 8, FAKE, FAKE, 0, r(kv), r(kv), 16, FAKE, None,
+                 ctypes.c_float(0.1), 1, 1, 64, FAKE, 1, FAKE, 1 << 30, FAKE, 1 << 30, None) == -2
+    assert fused(FAKE, 1, FAKE, r(ix), 16, 4, 8, FAKE, FAKE, 1, r(kv), r(kv), 16, FAKE, None,
+                 ctypes.c_float(0.1), 1, 1, 64, FAKE, 1, None, 0, FAKE, 1 << 30, None) == -3
 
 
 class _NR(ctypes.Structure):
