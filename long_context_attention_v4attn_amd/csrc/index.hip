@@ -588,7 +588,7 @@ __device__ __forceinline__ void load_qfrag(const uint8_t* kc, const uint8_t* ks,
 // the sample rows; kModeCollect scores every block and appends those at or
 // above the row's sampled threshold to its candidate list.
 constexpr int kModeStore = 0, kModeSample = 1, kModeCollect = 2;
-constexpr int kCollectPer = 8;             // LDS candidate slots per lane and query
+constexpr int kCollectPer = 6;             // LDS candidate slots per lane and query
 
 __device__ __forceinline__ void load_qfrag_s(const IndexArgs& a, const uint8_t* kc, const uint8_t* ks,
                                              int b, int64_t sb, int64_t last, int g, QFrag& f) {
@@ -599,8 +599,25 @@ __device__ __forceinline__ void load_qfrag_s(const IndexArgs& a, const uint8_t* 
   f.sc = ks[bb * 4 + g];
 }
 
+// One query's 16-head x 16-block MXFP4 product; the query scale is byte
+// `sel` of the register sa (four queries' scales share a register).
+template <int kSel>
+__device__ __forceinline__ f32x4 mfma_q_sel(const i32x8& a, const i32x8& b, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, (f32x4){0.f, 0.f, 0.f, 0.f}, 4, 4,
+                                                          kSel, sa, 0, sb);
+}
+__device__ __forceinline__ f32x4 mfma_q_scaled(int sel, const i32x8& a, const i32x8& b, int sa, int sb) {
+  switch (sel) {
+    case 0: return mfma_q_sel<0>(a, b, sa, sb);
+    case 1: return mfma_q_sel<1>(a, b, sa, sb);
+    case 2: return mfma_q_sel<2>(a, b, sa, sb);
+    default: return mfma_q_sel<3>(a, b, sa, sb);
+  }
+}
+
 template <int kMode, bool kBf16>
-__global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
+k_score_mx_q(IndexArgs a) {
   __shared__ uint32_t lh[kQT][kBins1];
   __shared__ int pg_rows[kQRange / 128];    // paged keys: the range's pool pages
   // collect: each lane's candidates of its two queries in slots of its own
@@ -643,17 +660,23 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
   }
   // A operands (16 heads x 128 elements of each query), scales, head weights
   i32x8 qa[kQT];
-  int qs[kQT];
-  float wv[kQT][4];
+  int qs[kQT / 4];                         // the queries' scale bytes, four per register
+  // head weights in LDS (read per tile, four heads of one query per lane:
+  // the lanes of a group read one address), not in 32 registers
+  __shared__ float lw[kQT][16];
+  if (threadIdx.x < kQT * 16) {
+    const int q = threadIdx.x >> 4, h = threadIdx.x & 15, t = t0 + q;
+    lw[q][h] = t < a.Q ? a.w[((int64_t)b * a.Q + t) * 16 + h] : 0.0f;
+  }
 #pragma unroll
   for (int q = 0; q < kQT; q++) {
     const int t = t0 + q;
     const int64_t row = (int64_t)b * a.Q + (t < a.Q ? t : a.Q - 1);
     u32x4 v = *(const u32x4*)(a.qmx + (row * 16 + li) * 64 + g * 16);
     qa[q] = (i32x8){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-    qs[q] = a.qsc[(row * 16 + li) * 4 + g];
-#pragma unroll
-    for (int i = 0; i < 4; i++) wv[q][i] = t < a.Q ? a.w[row * 16 + g * 4 + i] : 0.0f;
+    const int sb = a.qsc[(row * 16 + li) * 4 + g];
+    if (q % 4 == 0) qs[q / 4] = sb;
+    else qs[q / 4] |= sb << (8 * (q % 4));
   }
   // the two queries this lane stores: (g & 1) + 4 (g >> 1) and that + 2
   const int qa0 = (g & 1) + 4 * (g >> 1), qa1 = qa0 + 2;
@@ -704,14 +727,16 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
     const i32x8 kb = {(int)f.v[0], (int)f.v[1], (int)f.v[2], (int)f.v[3], 0, 0, 0, 0};
     // the eight queries' products first, each into its own accumulator, so
     // that the MFMAs issue back to back and the epilogue reads finished ones
-    f32x4 acc[kQT];
-#pragma unroll
-    for (int q = 0; q < kQT; q++)
-      acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          qa[q], kb, (f32x4){0.f, 0.f, 0.f, 0.f}, 4, 4, 0, qs[q], 0, f.sc);
+    // in two batches of four queries (register room for four waves per SIMD)
     float part[kQT];
 #pragma unroll
-    for (int q = 0; q < kQT; q++) {
+    for (int hq = 0; hq < kQT; hq += 4) {
+    f32x4 acc[kQT];
+#pragma unroll
+    for (int q = hq; q < hq + 4; q++)
+      acc[q] = mfma_q_scaled(q % 4, qa[q], kb, qs[q / 4], f.sc);
+#pragma unroll
+    for (int q = hq; q < hq + 4; q++) {
       // ReLU as one integer max on the bits (a float with the sign bit set
       // is a negative integer and becomes +0); w-weighted sum of the lane's
       // four heads
@@ -722,10 +747,12 @@ __global__ void __launch_bounds__(256) k_score_mx_q(IndexArgs a) {
         const int bits = __float_as_int(x);
         r[i] = __int_as_float(bits > 0 ? bits : 0);
       }
-      float p = wv[q][0] * r[0];
+      const f32x4 wq = *(const f32x4*)&lw[q][g * 4];
+      float p = wq[0] * r[0];
 #pragma unroll
-      for (int i = 1; i < 4; i++) p = fmaf(wv[q][i], r[i], p);
+      for (int i = 1; i < 4; i++) p = fmaf(wq[i], r[i], p);
       part[q] = p;
+    }
     }
     // sum over the four lane groups, all queries at once
     float h[4];
