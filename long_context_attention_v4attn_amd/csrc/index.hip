@@ -588,6 +588,17 @@ __device__ __forceinline__ void load_qfrag(const uint8_t* kc, const uint8_t* ks,
 // the sample rows; kModeCollect scores every block and appends those at or
 // above the row's sampled threshold to its candidate list.
 constexpr int kModeStore = 0, kModeSample = 1, kModeCollect = 2;
+// Word 3 of a raw (untyped, byte-addressed) buffer resource on this
+// architecture: 32-bit data format, no swizzle, no index stride.
+constexpr int kBufDword3 = 0x00020000;
+
+// A pointer whose value is the same in every lane, held in scalar registers.
+__device__ __forceinline__ void* wg_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (void*)(((uint64_t)hi << 32) | lo);
+}
 constexpr int kCollectPer = 6;             // LDS candidate slots per lane and query
 
 __device__ __forceinline__ void load_qfrag_s(const IndexArgs& a, const uint8_t* kc, const uint8_t* ks,
@@ -622,7 +633,9 @@ k_score_mx_q(IndexArgs a) {
   __shared__ int pg_rows[kQRange / 128];    // paged keys: the range's pool pages
   // collect: each lane's candidates of its two queries in slots of its own
   // (counted in registers: no atomic in the scoring loop), gathered per
-  // query at the end with one global reservation
+  // query at the end with one global reservation.  A slot holds the raw
+  // pair (score bits, block offset within the range); the 64-bit selection
+  // key is built when the slots are gathered, off the scoring loop.
   __shared__ uint64_t cbuf[kMode == kModeCollect ? 256 * 2 * kCollectPer : 1];
   __shared__ uint32_t lcnt[kMode == kModeCollect ? 512 : 1], loff[kMode == kModeCollect ? 512 : 1];
   __shared__ uint32_t cbase[kQT];
@@ -702,13 +715,14 @@ k_score_mx_q(IndexArgs a) {
   // a candidate of this lane's query `which` (0: qa0, 1: qa1): its next own
   // slot, or (its slots full) a global one
   uint32_t cn[2] = {0u, 0u};
-  auto put_cand = [&](int which, int64_t row, uint64_t key) {
+  auto put_cand = [&](int which, int64_t row, float sc, int rel) {
     if (cn[which] < (uint32_t)kCollectPer) {
-      cbuf[(threadIdx.x * 2 + which) * kCollectPer + cn[which]] = key;
+      cbuf[(threadIdx.x * 2 + which) * kCollectPer + cn[which]] =
+          ((uint64_t)(uint32_t)rel << 32) | __float_as_uint(sc);
       cn[which]++;
     } else {
       const uint32_t gs = atomicAdd(&a.ctr[row * kCtr + kCntSlot], 1u);
-      if (gs < (uint32_t)kCandCap) a.cand[row * kCandCap + gs] = key;
+      if (gs < (uint32_t)kCandCap) a.cand[row * kCandCap + gs] = sel_key(score_key(sc), r0 + rel);
     }
   };
   const size_t o0 = (size_t)((int64_t)b * a.Q + t0 + qa0) * a.sc_ld;   // score row offsets
@@ -722,8 +736,27 @@ k_score_mx_q(IndexArgs a) {
   const int psh = a.pg.psh;
   const int64_t r1 = r0 + kQRange < nv_max ? r0 + kQRange : nv_max;
   const int64_t last = r1 - 1;
+  // Blocks are counted from r0 in 32 bits inside the loop: the range's
+  // length, and per stored row its visible blocks past r0 (0 for a row
+  // past Q), so a bounds test is one 32-bit compare and an unpaged key
+  // load one 32-bit offset from the range's base.
+  const int nrel = (int)(r1 - r0), lastr = nrel - 1;
+  auto rel_bound = [&](int64_t nv, bool ok) -> int {
+    const int64_t v = ok ? nv - r0 : 0;
+    return v <= 0 ? 0 : (v > kQRange ? kQRange : (int)v);
+  };
+  const int nb0 = rel_bound(nv0, t0 + qa0 < a.Q), nb1 = rel_bound(nv1, t0 + qa1 < a.Q);
+  // unpaged: the range's keys and scales as two buffer resources (base in
+  // scalar registers -- the values are the workgroup's, readfirstlane tells
+  // the compiler so -- and the lane's 32-bit byte offset the only address
+  // work; every offset used is below the range's length)
+  const int nrel_s = __builtin_amdgcn_readfirstlane(nrel);
+  const __amdgpu_buffer_rsrc_t kcr =
+      __builtin_amdgcn_make_buffer_rsrc(wg_ptr(kc + (size_t)r0 * 64), 0, nrel_s * 64, kBufDword3);
+  const __amdgpu_buffer_rsrc_t ksr =
+      __builtin_amdgcn_make_buffer_rsrc(wg_ptr(ks + (size_t)r0 * 4), 0, nrel_s * 4, kBufDword3);
 
-  auto tile = [&](const QFrag& f, int64_t blk0) {
+  auto tile = [&](const QFrag& f, int rel0) {
     const i32x8 kb = {(int)f.v[0], (int)f.v[1], (int)f.v[2], (int)f.v[3], 0, 0, 0, 0};
     // the eight queries' products first, each into its own accumulator, so
     // that the MFMAs issue back to back and the epilogue reads finished ones
@@ -760,42 +793,50 @@ k_score_mx_q(IndexArgs a) {
     for (int j = 0; j < 4; j++) h[j] = swap_add32(part[j], part[4 + j]);
     const float s0 = ranked(swap_add16(h[0], h[1]), kBf16);   // queries 0, 1, 4, 5 by lane group
     const float s1 = ranked(swap_add16(h[2], h[3]), kBf16);   // queries 2, 3, 6, 7
-    const int64_t blk = blk0 + li;
+    const int rel = rel0 + li;
+    const int64_t blk = r0 + rel;
     if (kMode == kModeStore) {
-      if (blk < nv0 && t0 + qa0 < a.Q) {
+      if (rel < nb0) {
         put_score(a, o0 + blk, s0);
         atomicAdd(&lh[qa0][score_key(s0) >> kSh1], 1u);
       }
-      if (blk < nv1 && t0 + qa1 < a.Q) {
+      if (rel < nb1) {
         put_score(a, o1 + blk, s1);
         atomicAdd(&lh[qa1][score_key(s1) >> kSh1], 1u);
       }
     } else if (kMode == kModeSample) {
-      if (blk < nv0 && t0 + qa0 < a.Q) a.samp[row0 * a.samp_ld + blk] = s0;
-      if (blk < nv1 && t0 + qa1 < a.Q) a.samp[row1 * a.samp_ld + blk] = s1;
+      if (rel < nb0) a.samp[row0 * a.samp_ld + blk] = s0;
+      if (rel < nb1) a.samp[row1 * a.samp_ld + blk] = s1;
     } else {
       // (few pass: about 1.3 % of the scores at the benchmark's shape)
-      if (blk < nv0 && t0 + qa0 < a.Q && s0 >= thf0) put_cand(0, row0, sel_key(score_key(s0), blk));
-      if (blk < nv1 && t0 + qa1 < a.Q && s1 >= thf1) put_cand(1, row1, sel_key(score_key(s1), blk));
+      if (rel < nb0 && s0 >= thf0) put_cand(0, row0, s0, rel);
+      if (rel < nb1 && s1 >= thf1) put_cand(1, row1, s1, rel);
     }
   };
 
   // tiles w, w + 4, ... of 16 blocks; two fragments in flight
-  auto ld = [&](int64_t blk, QFrag& f) {
-    if (kMode == kModeSample)
-      load_qfrag_s(a, kc, ks, b, blk, last, g, f);
-    else
-      load_qfrag(kc, ks, blk, last, g, f, pgl, r0, psh);
+  auto ld = [&](int rel, QFrag& f) {
+    if (kMode == kModeSample) {
+      load_qfrag_s(a, kc, ks, b, r0 + rel, last, g, f);
+    } else if (pgl) {
+      load_qfrag(kc, ks, r0 + rel, last, g, f, pgl, r0, psh);
+    } else {
+      // clamped: always a real row; a plain load (every query tile of the
+      // sequence reads these keys again)
+      const int o = rel < lastr ? rel : lastr;
+      f.v = __builtin_amdgcn_raw_buffer_load_b128(kcr, o * 64 + g * 16, 0, 0);
+      f.sc = __builtin_amdgcn_raw_buffer_load_b8(ksr, o * 4 + g, 0, 0);
+    }
   };
   QFrag fa, fb;
-  int64_t blk0 = r0 + wave * 16;
-  ld(blk0 + li, fa);
-  for (; blk0 < r1; blk0 += 128) {
-    ld(blk0 + 64 + li, fb);
-    tile(fa, blk0);
-    if (blk0 + 64 >= r1) break;
-    ld(blk0 + 128 + li, fa);
-    tile(fb, blk0 + 64);
+  int rel0 = wave * 16;
+  ld(rel0 + li, fa);
+  for (; rel0 < nrel; rel0 += 128) {
+    ld(rel0 + 64 + li, fb);
+    tile(fa, rel0);
+    if (rel0 + 64 >= nrel) break;
+    ld(rel0 + 128 + li, fa);
+    tile(fb, rel0 + 64);
   }
   if (kMode == kModeCollect) {
     const int t = threadIdx.x;
@@ -825,7 +866,10 @@ k_score_mx_q(IndexArgs a) {
       const uint32_t base = cbase[q] + loff[idx];
       uint64_t* dst = a.cand + ((int64_t)b * a.Q + t0 + q) * kCandCap;
       for (uint32_t j = 0; j < lcnt[idx]; j++)
-        if (base + j < (uint32_t)kCandCap) dst[base + j] = cbuf[idx * kCollectPer + j];
+        if (base + j < (uint32_t)kCandCap) {
+          const uint64_t raw = cbuf[idx * kCollectPer + j];
+          dst[base + j] = sel_key(score_key(__uint_as_float((uint32_t)raw)), r0 + (int64_t)(raw >> 32));
+        }
     }
   }
   if (kMode != kModeStore) return;
