@@ -6,9 +6,10 @@
 // the selector ranks fp32 scores -- or, in the BF16-score variant of the same
 // section, the scores rounded to bf16 (which the score rows then hold).
 //
-// Pipeline of one v4attn_index_topk call (five launches):
-//   k_prep       query heads -> MXFP4 (e2m1 codes + e8m0 scale per 32); zero
-//                the per-query histogram and counters.
+// Pipeline of one v4attn_index_topk call, one query per sequence (decode:
+// four launches with 16 index heads, five otherwise):
+//   k_prep       (other head counts) query heads -> MXFP4 (e2m1 codes + e8m0
+//                scale per 32); zero the per-query histogram and counters.
 //   k_score_mx   FP4 scan: one v_mfma_scale_f32_16x16x128_f8f6f4 per
 //                (16 index heads, 16 blocks): M = heads, N = blocks, K = 128
 //                dims; the e8m0 scales feed the MFMA's scale operands, so the
@@ -17,8 +18,12 @@
 //                lane groups).  A wave streams 256 blocks per iteration (16 KB
 //                of keys in coalesced 1 KB loads); the next iteration's loads
 //                are in flight while the current one computes.  The
-//                workgroup histograms the top 11 bits of its scores'
-//                order-preserving keys in LDS and flushes once (global atomics).
+//                workgroup histograms the first radix digit (key bits
+//                31..24) of its scores' order-preserving keys in LDS and
+//                writes it as one partial row (16 index heads: it also
+//                quantises its query heads and zeroes the counters, so no
+//                kernel runs before it) or adds it to the query's global
+//                histogram.
 //   k_score_f32  fp32 VALU variant for unquantised keys (same histogram).
 //   k_filter1    per query, many workgroups (4096 scores each): the
 //                histogram gives the bin b1 (key bits 31..24) that holds the
@@ -34,6 +39,11 @@
 //                come out ascending with no sort; the tail is -1.  No
 //                workgroup waits for another, and the output is
 //                deterministic.
+// In the fused CSA call (v4attn_csa_index_attend) k_filter2 also writes each
+// chunk's selection keys at or above the candidates' bin in id order, and
+// the attention kernel takes the emit step (no k_emit launch).
+// Query-tiled scans (many queries per sequence: prefill chunks) take the
+// sampled-threshold selection described at k_thresh below.
 #include <mutex>
 
 #include "common.hpp"
