@@ -200,6 +200,18 @@ def test_hca_decode_full_size_sampled_rows(lib):
         P.check_out(out[b:b + 1], ref, what=f"row {b}")
 
 
+def _gpu_csa_fused(lib, case):
+    """The same CSA layer through v4attn_csa_index_attend (one call)."""
+    c, g = case["c"], case["g"]
+    topk, out = lib.v4attn_csa_index_attend(
+        P.dev(case["qib"].view(np.int16)).view(torch.bfloat16), P.dev(g["w"]),
+        P.idx_to_dev(case["keys"]), c["m"], c["k"],
+        P.dev(case["qb"].view(np.int16)).view(torch.bfloat16), P.kv_to_dev(case["comp"]),
+        P.kv_to_dev(case["win"]), c["n_win"], P.dev(g["pos"]), None, 512 ** -0.5)
+    torch.cuda.synchronize()
+    return topk.cpu().numpy(), out
+
+
 def test_determinism_and_batch_invariance(lib):
     print("determinism / batch invariance (workload 2 shapes, 8192 blocks)", flush=True)
     case = _decode_case(lib, 2, B=4, n_comp=8192, ctx=8192 * 4)
@@ -219,3 +231,8 @@ def test_determinism_and_batch_invariance(lib):
     t3, o3 = _gpu_csa(lib, one)
     assert np.array_equal(t3[0], t1[2])
     assert torch.equal(o3[0].view(torch.int16), o1[2].view(torch.int16))
+    # the fused call: the same bits, run twice, and for the row alone
+    for cs, ref_t, ref_o in ((case, t1, o1), (case, t1, o1), (one, t1[2:3], o1[2:3])):
+        tf, of = _gpu_csa_fused(lib, cs)
+        assert np.array_equal(tf, ref_t)
+        assert torch.equal(of.view(torch.int16), ref_o.view(torch.int16))
