@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/v4attn.h"
@@ -14,6 +16,47 @@ using namespace v4a;
 namespace {
 
 thread_local int32_t g_last_hip = 0;
+
+// Launch-plan log: with V4ATTN_LOG=1 in the environment (read on every call)
+// each call prints the plan it enqueues, one line on stderr.
+bool plan_log() {
+  const char* e = getenv("V4ATTN_LOG");
+  return e && e[0] == '1';
+}
+
+void log_compress(const char* what, const CompressArgs& a) {
+  if (!plan_log()) return;
+  fprintf(stderr,
+          "v4attn: %s B=%d T=%d d=%d m=%d t0=%lld out=%s fmt=%d overlap=%d paged=%d append=%d "
+          "norm_rope=%d\n",
+          what, a.B, a.T, a.d, a.m, (long long)a.t0, a.out_kind ? "keys" : "kv", a.out_fmt,
+          a.kv_prev ? 1 : 0, a.pg.tab ? 1 : 0, a.apos ? 1 : 0, (a.nr_gamma || a.nr_inv) ? 1 : 0);
+}
+
+void log_index(const char* what, const IndexArgs& a) {
+  if (!plan_log()) return;
+  const char* path = a.samp ? "sampled (sample scan, thresholds, collect scan, select)"
+                     : a.elist ? "filters, emit in the attention"
+                               : "filters + emit";
+  fprintf(stderr,
+          "v4attn: %s B=%d Q=%d H_I=%d d=%d cap=%lld m=%d k=%d keys=%s scores=%s path=%s "
+          "scan_wgs=%d scan_iters=%d partial_rows=%d paged=%d\n",
+          what, a.B, a.Q, a.H, a.d, (long long)a.cap, a.m, a.k, a.key_mx ? "mxfp4" : "f32",
+          a.score_bf16 ? "bf16" : "f32", path, a.score_wgs, a.score_iters, a.hp_ld,
+          a.pg.tab ? 1 : 0);
+}
+
+void log_attend(const char* what, const AttendArgs& a) {
+  if (!plan_log()) return;
+  fprintf(stderr,
+          "v4attn: %s B=%d Q=%d H=%d D=%d %s entries=%s splits=%d x %d partials=%s path=%s "
+          "loads=%s norm_rope=%d paged=%d fused_select=%d\n",
+          what, a.B, a.Q, a.H, a.d_nope + a.d_rope, a.csa ? "csa" : "hca",
+          a.csa ? "top-k + window" : "all visible + window", a.n_split, a.split_size,
+          a.n_split > 1 ? (a.part_bf16 ? "bf16" : "f32") : "none", a.fp8 ? "fp8 mfma" : "f32 valu",
+          a.fp8 ? (a.csa && a.Q == 1 ? "streaming" : "plain") : "plain",
+          (a.nr_gamma || a.nr_inv) ? 1 : 0, a.c_pg.tab ? 1 : 0, a.sel_ctr ? 1 : 0);
+}
 // events for the calling thread's next index / attend call (kernel timing)
 thread_local KernelEvents g_time_next = {nullptr, nullptr};
 
@@ -110,6 +153,7 @@ v4a_status run_attend(AttendArgs& a, int64_t n_entries_max, void* ws, size_t ws_
     a.nr_eps = nr->eps;
     a.nr_inv = a.d_rope > 0 ? nr->inv_freq : nullptr;
   }
+  log_attend(a.csa ? "csa_attend" : "hca_attend", a);
   KernelEvents ev;
   return hip_status(launch_attend(a, (hipStream_t)stream, take_events(&ev)));
 }
@@ -238,9 +282,11 @@ static v4a_status compress_impl(const void* kv_cur, const void* gate_cur, const 
       *built = a;
       return V4A_OK;
     }
+    log_compress("append", a);
     return hip_status(launch_compress(a, (hipStream_t)stream));
   }
   if (B == 0 || T == 0) return V4A_OK;
+  log_compress("compress", a);
   return hip_status(launch_compress(a, (hipStream_t)stream));
 }
 
@@ -351,6 +397,7 @@ static v4a_status index_topk(const void* q_idx, int32_t q_dtype, const float* w,
   }
   index_carve(a, ws);
   if (B == 0 || Q == 0) return V4A_OK;
+  log_index(score_bf16 ? "index_topk_bf16" : "index_topk", a);
   KernelEvents ev;
   return hip_status(launch_index_topk(a, (hipStream_t)stream, take_events(&ev)));
 }
@@ -391,6 +438,7 @@ v4a_status v4attn_append_batch(int32_t n, const v4a_append* calls, void* stream)
                                        stream, c.pages, c.pos, c.state, &ab.c[j]);
     if (s != V4A_OK) return s;
   }
+  for (int j = 0; j < n; j++) log_compress("append_batch", ab.c[j]);
   return hip_status(launch_append_batch(ab, (hipStream_t)stream));
 }
 
@@ -513,6 +561,7 @@ v4a_status v4attn_csa_index_attend(const void* q_idx, int32_t q_idx_dtype, const
     attend_carve(aa, ws_attend);
   }
   index_carve(ia, ws_index, fused);
+  log_index("csa_index_attend: index", ia);
   hipError_t e = launch_index_topk(ia, (hipStream_t)stream, nullptr);
   if (e != hipSuccess) return hip_status(e);
   if (fused) {
@@ -526,6 +575,7 @@ v4a_status v4attn_csa_index_attend(const void* q_idx, int32_t q_idx_dtype, const
     aa.sel_m = m;
     aa.sel_topk = topk;
   }
+  log_attend("csa_index_attend: attend", aa);
   return hip_status(launch_attend(aa, (hipStream_t)stream, nullptr));
 }
 

@@ -173,3 +173,30 @@ def test_fused_falls_back_to_two_steps(lib):
     q1 = P.dev(rng.standard_normal((Bn, 1, 16, D)).astype(np.float32))
     _compare(lib, qi1, w1, keys, P.dev(np.array([[m * cap - 1]], np.int64)), m, k, q1, comp, win,
              128, out_dtype=torch.float32)
+
+
+def test_launch_plan_log(lib, capfd, monkeypatch):
+    """V4ATTN_LOG=1: every call prints the plan it enqueues on stderr (read
+    per call); unset, nothing is printed."""
+    print("launch-plan log", flush=True)
+    rng = np.random.default_rng(46)
+    Bn, cap, m, k = 2, 5000, 4, 512
+    qi, w, keys = _idx_inputs(rng, Bn, 1, cap)
+    comp, win = _fp8_cache(rng, Bn, cap), _fp8_cache(rng, Bn, 256)
+    q = P.bf16_dev(rng.standard_normal((Bn, 1, 64, 512)).astype(np.float32))
+    pos = P.dev(np.array([[m * cap - 1], [m * 3000 + 1]], np.int64))
+    monkeypatch.setenv("V4ATTN_LOG", "1")
+    capfd.readouterr()
+    lib.v4attn_csa_index_attend(qi, w, keys, m, k, q, comp, win, 128, pos, None, SCALE)
+    lib.v4attn_hca_attend(q, comp, m, win, 128, pos, None, SCALE)
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    assert "v4attn: csa_index_attend: index B=2 Q=1 H_I=16" in err
+    assert "path=filters, emit in the attention" in err
+    assert "v4attn: csa_index_attend: attend B=2 Q=1 H=64 D=512 csa" in err
+    assert "fused_select=1" in err and "loads=streaming" in err
+    assert "v4attn: hca_attend B=2 Q=1 H=64 D=512 hca" in err and "loads=plain" in err
+    monkeypatch.delenv("V4ATTN_LOG")
+    lib.v4attn_hca_attend(q, comp, m, win, 128, pos, None, SCALE)
+    torch.cuda.synchronize()
+    assert "v4attn:" not in capfd.readouterr().err
