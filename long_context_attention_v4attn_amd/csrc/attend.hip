@@ -935,9 +935,16 @@ __device__ __forceinline__ void attend_fp8(AttendArgs a) {
     const StageSrc ns = stage_src(src, sh.tbits, t + 2);
     f32x4 sn, sr;
     float s2[4], tmax;
+    // A wave's logits and softmax run at raised issue priority, so that the
+    // MFMA chain and the softmax that waits on it are not interleaved with
+    // the other wave's staging and PV on the same SIMD (HCA decode attention
+    // 40.4 -> 39.0 us); one-query CSA calls (streaming loads) showed no gain
+    // and keep the default.
+    if (!kStream) __builtin_amdgcn_s_setprio(1);
     qk_tile(&tiles[cb], &sh, qf, eh, wht, lane, sn, sr);
     const bool first = t == 0;
     float l_add = softmax_pass(&tiles[cb], &sh, S, sn, sr, c2, pb, wave, lane, first, s2, tmax);
+    if (!kStream) __builtin_amdgcn_s_setprio(0);
     stage_store(&tiles[nb], nxt);
     stage_load<kStream>(B, ns, t + 2, n_local, nxt);
     __syncthreads();
