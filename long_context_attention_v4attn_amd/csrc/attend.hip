@@ -799,18 +799,19 @@ __device__ __forceinline__ void attend_fp8(AttendArgs a) {
     ivf = *(const f32x4*)(a.nr_inv ? a.nr_inv + 4 * rc : (const float*)a.q);
     p_q = a.pos[row];
   }
+  const int e_beg = split * a.split_size;
+  // fused selection: the split's top-k ids (the tile buffers are free
+  // until the first tile is staged, after the barrier below); called before
+  // the entry list's sizes are read, so that its loads go out with the
+  // query position's rather than one round trip after it
+  if (kSel && e_beg < a.k) pre = derive_topk(a, row, hgrp, e_beg, (uint8_t*)tiles);
   const RowEntries r = row_entries(a, row);
   const int n_tot = r.n_c + r.n_w;
-  const int e_beg = split * a.split_size;
   const int e_end = min(e_beg + a.split_size, n_tot);
   // uniform across the workgroup: kept in scalar registers so that the tile
   // loop's branches are scalar
   const int n_local = __builtin_amdgcn_readfirstlane(e_end > e_beg ? e_end - e_beg : 0);
   const int n_tiles = (n_local + kTile - 1) / kTile;
-
-  // fused selection: the split's top-k ids (the tile buffers are free
-  // until the first tile is staged, after the barrier below)
-  if (kSel && e_beg < a.k) pre = derive_topk(a, row, hgrp, e_beg, (uint8_t*)tiles);
   resolve_sources(a, r, row, e_beg, n_local, n_tiles, pre, src, sh.tbits);
   if (kNr) {
     // the weights go to the third tile buffer (first written after the

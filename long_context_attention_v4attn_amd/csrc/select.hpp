@@ -44,15 +44,26 @@ __device__ __forceinline__ uint64_t sel_key(uint32_t k32, int64_t i) {
   return ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
 }
 
+// Inclusive scan over the 64 lanes of a wave with DPP moves (no LDS round
+// trips): row_shr 1, 2, 4, 8 scan each row of 16 lanes, then row_bcast15
+// adds row 0's total to row 1 and row 2's to row 3, and row_bcast31 adds
+// lane 31's (rows 0-1) to rows 2 and 3.  A lane whose source lies outside
+// its row, or whose row is masked off, receives the old value 0.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
 // Inclusive block scan of one value per thread.
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp,
                                                     uint32_t* total = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
+  v = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = v;
   __syncthreads();
   uint32_t add = 0, all = 0;
