@@ -151,3 +151,71 @@ def test_storage_ratios_from_pages():
     assert abs(mean / gqa8 - g["kv_vs_bf16_gqa8_hd128"]) <= g["kv_vs_bf16_gqa8_hd128_tolerance"]
     swa_vs = entry / ((entry / 4 + entry / 128) / 2)
     assert abs(swa_vs - g["swa_vs_compressed"]) <= g["swa_vs_compressed_tolerance"]
+
+
+def _pooled_row_from_streams(cur_v, cur_z, prev_v, prev_z, bias, m, j):
+    """Pure-Python pooled row of block j read straight from the raw streams:
+    the m tokens of block j in the current role and (j > 0) the m tokens of
+    block j - 1 in the previous role, a softmax over the 2m gate logits per
+    channel ([Notes §8] overlapped compressor)."""
+    d = len(cur_v[0])
+    row = []
+    for c in range(d):
+        terms = []
+        if j > 0:
+            for u in range(m):
+                t = m * (j - 1) + u
+                terms.append((float(prev_z[t][c]) + float(bias[u][c]), float(prev_v[t][c])))
+        for u in range(m):
+            t = m * j + u
+            terms.append((float(cur_z[t][c]) + float(bias[m + u][c]), float(cur_v[t][c])))
+        mx = max(z for z, _ in terms)
+        den = sum(math.exp(z - mx) for z, _ in terms)
+        row.append(sum(math.exp(z - mx) * v for z, v in terms) / den)
+    return row
+
+
+def test_workload1_pipeline_against_raw_streams():
+    """Workload 1 (fp32, 4096 tokens, top-64, window 128) recomputed from the
+    raw token streams apart from the oracle's layer functions: pooled entry and
+    index-key rows at sampled blocks (pure Python, previous role read at block
+    j - 1, within one fp32 step of the fp32 rows), the stored cache rows equal to the pooled rows in fp32, the top-64
+    of the index scores of the stored keys (float64, ranked in fp32, lower id
+    first), and the attention over the selected rows plus the last 128 raw
+    tokens read straight from kv_b rather than from the window ring."""
+    g = synth.workload1_inputs()
+    res = workload1(g)
+    m, k, n_win = 4, 64, 128
+    p = int(g["pos"][0, 0])
+    nv = (p + 1) // m
+    for j in (0, 1, 2, 511, nv - 1):
+        y = _pooled_row_from_streams(g["kv_b"][0], g["z_b"][0], g["kv_a"][0], g["z_a"][0],
+                                     g["bias"], m, j)
+        # the compressor's rows are fp32 values ([Notes §9] workload 1 keeps fp32)
+        assert np.allclose(res["y"][0, j], np.float32(y), rtol=2.0 ** -23, atol=1e-30)
+        yi = _pooled_row_from_streams(g["ki_b"][0], g["zi_b"][0], g["ki_a"][0], g["zi_a"][0],
+                                      g["bias_i"], m, j)
+        assert np.allclose(res["yi"][0, j], np.float32(yi), rtol=2.0 ** -23, atol=1e-30)
+    comp = np.concatenate([res["comp"].nope[0], res["comp"].rope[0]], 1)
+    assert np.array_equal(comp[:nv], res["y"][0, :nv].astype(np.float32))
+    keys = res["keys"].codes[0, :nv].astype(np.float64)
+    assert np.array_equal(res["keys"].codes[0, :nv], res["yi"][0, :nv].astype(np.float32))
+    # index scores of every visible block, ranked as fp32 (lower id first on ties)
+    qi = g["q_idx"][0, 0].astype(np.float64)
+    w = g["w"][0, 0].astype(np.float64)
+    s = np.zeros(nv)
+    for h in range(qi.shape[0]):
+        s += w[h] * np.maximum(keys @ qi[h], 0.0)
+    s32 = s.astype(np.float32)
+    order = sorted(range(nv), key=lambda i: (-float(s32[i]), i))
+    assert list(res["topk"][0, 0]) == sorted(order[:k])
+    # attention over the selected rows and the last n_win raw tokens
+    ent = np.concatenate([comp[sorted(order[:k])],
+                          g["kv_b"][0, p - n_win + 1:p + 1]], 0).astype(np.float64)
+    q = g["q"][0, 0].astype(np.float64)
+    scale = q.shape[1] ** -0.5
+    for h in range(q.shape[0]):
+        lg = scale * (ent @ q[h])
+        e = np.exp(lg - lg.max())
+        ref = (e @ ent) / e.sum()
+        assert np.allclose(res["out_f64"][0, 0, h], ref, rtol=1e-9, atol=1e-12)
