@@ -951,6 +951,11 @@ def main():
     t_gpu = ev[0][0].elapsed_time(ev[rounds][0]) / K * 1e-3
     ms_per_step = max(wall / K, t_gpu) * 1e3
     pair_qps = 1.0 / (t_csa / cc["B"] + t_hca / ch["B"])
+    # the same figure per round of R steps (the events between the rounds),
+    # for its spread over the timed region
+    round_qps = sorted(R / (ev[s][0].elapsed_time(ev[s][1]) * 1e-3 / cc["B"]
+                            + ev[s][1].elapsed_time(ev[s + 1][0]) * 1e-3 / ch["B"])
+                       for s in range(rounds))
 
     # ---- per-call breakdown (each call's graph replayed back to back)
     def per_call(i, n):
@@ -1054,6 +1059,9 @@ def main():
         "hca_qps": round(ch["B"] / t_hca, 1),
         "value_derivation": "value = 1 / (t_csa_layer / 4 + t_hca_layer / 16): the step time per "
                             "query of each layer at its own batch (CSA B = 4, HCA B = 16), summed",
+        "value_over_rounds": {"what": "the value of each timed round of `replicas` steps",
+                              "rounds": rounds, "median": round(float(np.median(round_qps)), 1),
+                              "min": round(round_qps[0], 1), "max": round(round_qps[-1], 1)},
         "pair_common_b4": {"what": "both layers at B = 4: 4 / (t_csa_layer + t_hca_attend(B = 4))",
                            "queries_per_s": round(cc["B"] / (t_csa + t_hca4), 1),
                            "t_hca_attend_b4_us": round(t_hca4 * 1e6, 3)},
