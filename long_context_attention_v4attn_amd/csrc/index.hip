@@ -775,9 +775,13 @@ k_score_mx_q(IndexArgs a) {
 #pragma unroll
     for (int hq = 0; hq < kQT; hq += 4) {
     f32x4 acc[kQT];
+    // (the batch's MFMAs issue at raised wave priority, ahead of the other
+    // waves' VALU epilogues: collect scan 1.77 -> 1.75 ms)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int q = hq; q < hq + 4; q++)
       acc[q] = mfma_q_scaled(q % 4, qa[q], kb, qs[q / 4], f.sc);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int q = hq; q < hq + 4; q++) {
       // ReLU as one integer max on the bits (a float with the sign bit set
