@@ -776,7 +776,8 @@ k_score_mx_q(IndexArgs a) {
     for (int hq = 0; hq < kQT; hq += 4) {
     f32x4 acc[kQT];
     // (the batch's MFMAs issue at raised wave priority, ahead of the other
-    // waves' VALU epilogues: collect scan 1.77 -> 1.75 ms)
+    // waves' VALU epilogues: collect scan 1.77 -> 1.74-1.78 ms, a gain within
+    // the spread between runs)
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int q = hq; q < hq + 4; q++)
